@@ -1,0 +1,1 @@
+"""DashAttention forward pass for MI355X (gfx950): HIP kernels behind a C ABI."""

@@ -1,0 +1,362 @@
+"""Pins of the CPU oracle against what the DashAttention pages and mathematics fix.
+
+None of these re-types an oracle formula: each checks the oracle against an
+independent definition (variational form of entmax, brute-force KKT search,
+library SDPA, a second formulation of Stage 2) or a closed-form special case.
+Citations name the xllm-io paper review, section 三 (technical architecture).
+"""
+import itertools
+
+import numpy as np
+import pytest
+import scipy.optimize
+import scipy.special
+import torch
+
+from oracle import dash_oracle as O
+from long_context_amd import inputs
+
+
+# ----------------------------------------------------------------------------------
+# α-entmax (background formula, section 三): outputs on the simplex, unique τ,
+# α -> 1 softmax, α = 2 sparsemax, sparsity grows with α.
+# ----------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("alpha", [1.1, 1.25, 1.5, 2.0, 3.0])
+def test_entmax_on_simplex(alpha):
+    rng = np.random.default_rng(0)
+    s = rng.standard_normal((400, 33)) * 3
+    valid = np.arange(33)[None] < rng.integers(1, 34, size=(400, 1))
+    p, tau, x = O.entmax(s, alpha, valid)
+    assert np.all(p >= 0)
+    assert np.all(p[~valid] == 0)
+    np.testing.assert_allclose(p.sum(-1), 1.0, atol=1e-12)
+
+
+@pytest.mark.parametrize("alpha", [1.25, 1.5, 2.0])
+def test_entmax_shift_invariance(alpha):
+    rng = np.random.default_rng(1)
+    s = rng.standard_normal((50, 20))
+    p1, _, _ = O.entmax(s, alpha)
+    p2, _, _ = O.entmax(s + 7.25, alpha)
+    np.testing.assert_allclose(p1, p2, atol=1e-12)
+
+
+def _tsallis_objective(p, s, alpha):
+    # maximise p.s + H_alpha(p) with Tsallis entropy H = sum(p - p^alpha)/(alpha(alpha-1))
+    p = np.clip(p, 0, None)
+    return -(p @ s + np.sum(p - p ** alpha) / (alpha * (alpha - 1)))
+
+
+@pytest.mark.parametrize("alpha", [1.25, 1.5, 2.0, 3.0])
+def test_entmax_matches_variational_definition(alpha):
+    """α-entmax is the maximiser of p.s + Tsallis entropy over the simplex; its
+    closed form [(α-1)s - τ]_+^{1/(α-1)} must agree with a generic optimiser."""
+    rng = np.random.default_rng(2)
+    for _ in range(6):
+        T = int(rng.integers(2, 7))
+        s = rng.standard_normal(T) * 1.5
+        res = scipy.optimize.minimize(
+            _tsallis_objective, np.full(T, 1.0 / T), args=(s, alpha), method="SLSQP",
+            bounds=[(0, 1)] * T, constraints=[{"type": "eq", "fun": lambda p: p.sum() - 1}],
+            options={"ftol": 1e-15, "maxiter": 500})
+        p, _, _ = O.entmax(s[None], alpha)
+        np.testing.assert_allclose(p[0], res.x, atol=2e-5)
+
+
+def test_sparsemax_is_simplex_projection():
+    """α = 2 is sparsemax: the Euclidean projection of s onto the simplex."""
+    rng = np.random.default_rng(3)
+    for _ in range(10):
+        T = int(rng.integers(2, 9))
+        s = rng.standard_normal(T)
+        res = scipy.optimize.minimize(
+            lambda p: 0.5 * np.sum((p - s) ** 2), np.full(T, 1.0 / T), method="SLSQP",
+            bounds=[(0, None)] * T, constraints=[{"type": "eq", "fun": lambda p: p.sum() - 1}],
+            options={"ftol": 1e-15, "maxiter": 500})
+        p, _, _ = O.entmax(s[None], 2.0)
+        np.testing.assert_allclose(p[0], res.x, atol=1e-6)
+
+
+def test_entmax_alpha_to_one_is_softmax():
+    rng = np.random.default_rng(4)
+    s = rng.standard_normal((20, 15))
+    p1, _, _ = O.entmax(s, 1.0)
+    np.testing.assert_allclose(p1, scipy.special.softmax(s, axis=-1), atol=1e-14)
+    p, _, _ = O.entmax(s, 1.0 + 1e-4)
+    assert np.abs(p - scipy.special.softmax(s, axis=-1)).max() < 2e-4
+
+
+def _brute_force_tau(x, alpha):
+    """Enumerate every support S, solve sum_S (x-τ)^p = 1 on it, keep the KKT-valid ones."""
+    p = 1.0 / (alpha - 1.0)
+    T = x.size
+    found = []
+    for k in range(1, T + 1):
+        for S in itertools.combinations(range(T), k):
+            xs = x[list(S)]
+            lo, hi = xs.min() - 2.0, xs.min()
+            for _ in range(200):           # on S the sum is decreasing in τ < min(xs)
+                mid = 0.5 * (lo + hi)
+                if np.sum((xs - mid) ** p) >= 1:
+                    lo = mid
+                else:
+                    hi = mid
+            tau = 0.5 * (lo + hi)
+            off = np.setdiff1d(np.arange(T), S)
+            solved = abs(np.sum((xs - tau) ** p) - 1.0) < 1e-9
+            if solved and np.all(xs > tau) and np.all(x[off] <= tau):
+                found.append((S, tau))
+    return found
+
+
+@pytest.mark.parametrize("alpha", [1.25, 1.5, 2.0])
+def test_entmax_brute_force_support(alpha):
+    """Exactly one support satisfies the KKT conditions (τ is unique) and it is the
+    oracle's."""
+    rng = np.random.default_rng(5)
+    for _ in range(8):
+        T = int(rng.integers(1, 9))
+        s = rng.standard_normal(T) * 2
+        x = (alpha - 1) * s
+        found = _brute_force_tau(x, alpha)
+        assert len(found) == 1
+        S, tau = found[0]
+        p, t, _ = O.entmax(s[None], alpha)
+        assert set(np.nonzero(p[0] > 0)[0]) == set(S)
+        assert abs(t[0] - tau) < 1e-12
+
+
+@pytest.mark.parametrize("alpha", [1.5, 2.0])
+def test_sorted_threshold_matches_bisection(alpha):
+    rng = np.random.default_rng(6)
+    x = rng.standard_normal((2000, 64))
+    valid = np.arange(64)[None] < rng.integers(1, 65, size=(2000, 1))
+    a = O.entmax_tau_sorted(x, valid, alpha)
+    b = O.entmax_tau_bisect(x, valid, alpha)
+    assert np.abs(a - b).max() < 1e-13
+
+
+def test_entmax_gamma_limits():
+    rng = np.random.default_rng(7)
+    s = rng.standard_normal((10, 12))
+    p, _, _ = O.entmax(1e-9 * s, 1.5)
+    np.testing.assert_allclose(p, 1.0 / 12, atol=1e-6)
+    p, _, _ = O.entmax(1e4 * s, 1.5)
+    np.testing.assert_array_equal(p, np.eye(12)[s.argmax(-1)])
+
+
+def test_sparsity_grows_with_alpha():
+    rng = np.random.default_rng(8)
+    s = rng.standard_normal((500, 64)) * 2
+    nnz = [np.count_nonzero(O.entmax(s, a)[0]) for a in (1.25, 1.5, 2.0, 3.0)]
+    assert nnz[0] >= nnz[1] >= nnz[2] >= nnz[3]
+    assert nnz[0] > nnz[3]
+
+
+# ----------------------------------------------------------------------------------
+# Stage 0 (Eq. 4): local SDPA under q̄ with keys as values.
+# ----------------------------------------------------------------------------------
+
+def test_stage0_is_local_sdpa():
+    rng = np.random.default_rng(9)
+    K = rng.standard_normal((2, 3, 100, 16))
+    qbar = rng.standard_normal((3, 16))
+    B = 8
+    kb = O.stage0_summaries(K, qbar, B)
+    assert kb.shape == (2, 3, 12, 16)          # trailing partial chunk has no summary
+    Kt = torch.from_numpy(K[:, :, :96].reshape(2, 3, 12, 8, 16))
+    q = torch.from_numpy(qbar)[None, :, None, None, :].expand(2, 3, 12, 1, 16)
+    ref = torch.nn.functional.scaled_dot_product_attention(q, Kt, Kt)[..., 0, :]
+    np.testing.assert_allclose(kb, ref.numpy(), atol=1e-13)
+
+
+def test_stage0_zero_query_is_mean_pooling():
+    rng = np.random.default_rng(10)
+    K = rng.standard_normal((1, 2, 64, 8))
+    kb = O.stage0_summaries(K, np.zeros((2, 8)), 16)
+    np.testing.assert_allclose(kb, K.reshape(1, 2, 4, 16, 8).mean(3), atol=1e-14)
+
+
+def test_stage0_chunk_of_one_is_the_key():
+    rng = np.random.default_rng(11)
+    K = rng.standard_normal((1, 1, 10, 4))
+    kb = O.stage0_summaries(K, rng.standard_normal((1, 4)), 1)
+    np.testing.assert_allclose(kb, K, atol=1e-15)
+
+
+def test_stage0_permutation_invariant_within_chunk():
+    rng = np.random.default_rng(12)
+    K = rng.standard_normal((1, 1, 32, 8))
+    qbar = rng.standard_normal((1, 8))
+    perm = np.concatenate([rng.permutation(16), 16 + rng.permutation(16)])
+    np.testing.assert_allclose(O.stage0_summaries(K, qbar, 16),
+                               O.stage0_summaries(K[:, :, perm], qbar, 16), atol=1e-14)
+
+
+# ----------------------------------------------------------------------------------
+# Stage 1: GQA average and union (Eq. 6 and the GQA paragraph).
+# ----------------------------------------------------------------------------------
+
+def _small(seed=0, **kw):
+    args = dict(b=2, h_q=4, h_kv=2, d=16, n=160, B=16, alphas=(1.5,), gamma=2.0,
+                sigma=1.0, causal=True, dtype="f32", seed=seed)
+    args.update(kw)
+    return inputs.make_prefill(**args)
+
+
+def test_group_weights_simplex_and_union():
+    w = _small()
+    kb = O.stage0_summaries(w.K, w.qbar, w.B)
+    rows = np.arange(w.n)
+    rt = O.route(w.Q, rows[None], kb, w.B, 1.5, 3.0, 1.0, True, w.n, keep_heads=True)
+    has = rt["vis"][:, None, :] >= 1
+    sums = rt["w"].sum(-1)
+    np.testing.assert_allclose(sums[np.broadcast_to(has, sums.shape)], 1.0, atol=1e-12)
+    heads_sup = (rt["what"] > 0).reshape(2, 2, 2, w.n, -1).any(2)
+    np.testing.assert_array_equal(heads_sup, rt["support"])
+
+
+def test_group_of_one_head_is_the_head():
+    w = _small(h_q=2, h_kv=2)
+    kb = O.stage0_summaries(w.K, w.qbar, w.B)
+    rows = np.arange(w.n)
+    rt = O.route(w.Q, rows[None], kb, w.B, 1.5, 3.0, 1.0, True, w.n, keep_heads=True)
+    np.testing.assert_allclose(rt["w"], rt["what"], atol=0)
+
+
+def test_query_head_to_kv_group_map():
+    """r = floor(h/g): with identical heads inside each group, the group weight equals
+    the single-head entmax of that group's query against that group's summaries."""
+    w = _small(h_q=6, h_kv=2)
+    Q = w.Q.copy()
+    Q[:, 1:3] = Q[:, 0:1]
+    Q[:, 4:6] = Q[:, 3:4]
+    kb = O.stage0_summaries(w.K, w.qbar, w.B)
+    rows = np.arange(w.n)
+    rt = O.route(Q, rows[None], kb, w.B, 1.5, 3.0, 1.0, True, w.n)
+    for r in range(2):
+        single = O.route(Q[:, 3 * r:3 * r + 1], rows[None], kb[:, r:r + 1], w.B, 1.5, 3.0, 1.0,
+                         True, w.n)
+        np.testing.assert_allclose(rt["w"][:, r], single["w"][:, 0], atol=1e-14)
+
+
+def test_single_visible_chunk_has_unit_weight_and_zero_bias():
+    w = _small()
+    kb = O.stage0_summaries(w.K, w.qbar, w.B)
+    rows = np.arange(w.B, 2 * w.B)                       # exactly one visible chunk
+    rt = O.route(w.Q[:, :, rows], rows[None], kb, w.B, 1.5, 3.0, 1.0, True, w.n)
+    np.testing.assert_allclose(rt["w"][..., 0], 1.0, atol=1e-15)
+    np.testing.assert_array_equal(rt["cnt"], 1)
+    np.testing.assert_allclose(rt["bias"], 0.0, atol=1e-15)
+
+
+# ----------------------------------------------------------------------------------
+# Stage 2: Eq. 9 / 11 / 12 versus Proposition 4.1, and library SDPA special cases.
+# ----------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("sigma", [1.0, 0.5, 3.0, np.inf])
+@pytest.mark.parametrize("causal,n", [(True, 160), (False, 160), (False, 168)])
+def test_bias_form_equals_prior_form(sigma, causal, n):
+    """Prop. 4.1: the additive bias d = (log w - μ)/σ on R and 0 on D reproduces the
+    prior-induced softmax of Eq. 9 built from Eq. 11 and Eq. 12."""
+    w = _small(n=n, causal=causal, sigma=sigma)
+    kb = O.stage0_summaries(w.K, w.qbar, w.B)
+    rows = np.array([0, 5, 16, 17, 40, 63, 64, 100, n - 1])
+    rt = O.route(w.Q[:, :, rows], rows[None], kb, w.B, 1.5, 3.0, sigma, causal, n)
+    a = O.attend(w.Q[:, :, rows], rows[None], w.K, w.V, rt, w.B, causal, n)
+    b = O.attend_eq9(w.Q[:, :, rows], rows[None], w.K, w.V, rt, w.B, sigma, causal, n)
+    np.testing.assert_allclose(a, b, atol=1e-12)
+
+
+def test_uniform_router_gives_zero_bias_and_size_split():
+    """Identical summaries make the router uniform: d = 0 and λ = |R|/(|R|+|D|)."""
+    w = _small()
+    kb = np.broadcast_to(O.stage0_summaries(w.K, w.qbar, w.B)[:, :, :1], (2, 2, 10, 16)).copy()
+    rows = np.arange(w.n)
+    rt = O.route(w.Q, rows[None], kb, w.B, 1.5, 3.0, 1.0, True, w.n)
+    np.testing.assert_allclose(rt["bias"], 0.0, atol=1e-12)
+    vis = rt["vis"][0]
+    assert np.all(rt["cnt"][0, 0] == vis)
+
+
+def _sdpa(q, k, v, mask):
+    return torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v),
+        attn_mask=torch.from_numpy(mask)).numpy()
+
+
+def test_sigma_inf_is_masked_softmax():
+    """σ = inf: the prior is uniform on the support, so Stage 2 is plain SDPA with the
+    boolean mask of R ∪ D (checked against the library routine)."""
+    w = _small(sigma=np.inf)
+    kb = O.stage0_summaries(w.K, w.qbar, w.B)
+    rows = np.arange(w.n)
+    rt = O.route(w.Q, rows[None], kb, w.B, 2.0, 6.0, np.inf, True, w.n)
+    Oa = O.attend(w.Q, rows[None], w.K, w.V, rt, w.B, True, w.n)
+    T = w.n // w.B
+    tok = np.arange(w.n)
+    for bi in range(2):
+        for r in range(2):
+            mask = np.zeros((w.n, w.n), bool)
+            sup = rt["support"][bi, r]                        # [rows, T]
+            mask[:, :T * w.B] = sup[:, tok[:T * w.B] // w.B]
+            own = (rows[:, None] // w.B == tok[None] // w.B) & (tok[None] <= rows[:, None])
+            mask |= own
+            for h in range(2 * r, 2 * r + 2):
+                ref = _sdpa(np.asarray(w.Q[bi, h], np.float64), np.asarray(w.K[bi, r], np.float64),
+                            np.asarray(w.V[bi, r], np.float64), mask)
+                np.testing.assert_allclose(Oa[bi, h], ref, atol=1e-12)
+
+
+def test_full_support_is_dense_causal_attention():
+    """γ -> 0 routes every visible chunk with equal weight; with σ = inf Stage 2 is
+    dense causal SDPA."""
+    w = _small(sigma=np.inf)
+    res = O.prefill(w.Q, w.K, w.V, w.qbar, w.B, 1.5, 1e-9, np.inf, True)
+    assert O.group_sparsity(res["route"]) == 0.0
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(np.asarray(w.Q, np.float64)),
+        torch.from_numpy(np.asarray(np.repeat(w.K, 2, axis=1), np.float64)),
+        torch.from_numpy(np.asarray(np.repeat(w.V, 2, axis=1), np.float64)), is_causal=True)
+    np.testing.assert_allclose(res["O"], ref.numpy(), atol=1e-12)
+
+
+def test_no_visible_chunk_is_causal_softmax_over_own_chunk():
+    w = _small()
+    res = O.prefill(w.Q, w.K, w.V, w.qbar, w.B, 1.5, 3.0, 1.0, True, rows=np.arange(w.B))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(np.asarray(w.Q[:, :, :w.B], np.float64)),
+        torch.from_numpy(np.asarray(np.repeat(w.K[:, :, :w.B], 2, axis=1), np.float64)),
+        torch.from_numpy(np.asarray(np.repeat(w.V[:, :, :w.B], 2, axis=1), np.float64)),
+        is_causal=True)
+    np.testing.assert_allclose(res["O"], ref.numpy(), atol=1e-13)
+
+
+@pytest.mark.parametrize("L", [160, 161, 175, 176])
+def test_decode_equals_last_prefill_row(L):
+    w = _small(n=L)
+    kb = O.stage0_summaries(w.K, w.qbar, w.B)
+    pre = O.prefill(w.Q, w.K, w.V, w.qbar, w.B, 1.5, 3.0, 1.0, True, rows=np.array([L - 1]))
+    dec = O.decode(w.Q[:, :, L - 1:L], w.K, w.V, kb, np.full(2, L), w.B, 1.5, 3.0, 1.0)
+    np.testing.assert_allclose(dec["O"], pre["O"], atol=1e-14)
+
+
+def test_group_sparsity_monotone_in_alpha_on_clusters():
+    """Aggregate sparsity grows with α on a small clustered workload."""
+    rng = np.random.default_rng(13)
+    w = _small(n=512, B=16, h_q=8, h_kv=2, d=32)
+    K = w.K.copy()
+    for r in range(2):
+        for c0 in (4, 12, 20):
+            u = rng.standard_normal(32)
+            u /= np.linalg.norm(u)
+            K[:, r, c0 * 16:(c0 + 4) * 16] = 0.8 * np.linalg.norm(
+                K[:, r, c0 * 16:(c0 + 4) * 16], axis=-1, keepdims=True) * u + \
+                0.6 * K[:, r, c0 * 16:(c0 + 4) * 16] / np.sqrt(32)
+    kb = O.stage0_summaries(K, w.qbar, 16)
+    rows = np.arange(0, 512, 3)
+    sp = [O.group_sparsity(O.route(w.Q[:, :, rows], rows[None], kb, 16, a, 1.0, 1.0, True, 512))
+          for a in (1.25, 1.5, 2.0)]
+    assert sp[0] <= sp[1] <= sp[2]
+    assert sp[2] > sp[0]
