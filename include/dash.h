@@ -1,0 +1,147 @@
+/*
+ * dash.h -- C ABI of the DashAttention forward pass on MI355X (gfx950).
+ *
+ * The method is the one of "DashAttention: Differentiable and Adaptive Sparse
+ * Hierarchical Attention" as summarised on the xllm-io paper review, section 三
+ * (technical architecture):
+ *   Stage 0 (Eq. 4)   chunk summaries k̄_c = local SDPA of the learned query q̄
+ *                      over the keys of chunk c (keys are also the values);
+ *   Stage 1 (Eq. 6)   chunk logits z̄ = <q, k̄>/sqrt(d), per-head α-entmax of γz̄,
+ *                      GQA average w within each KV group, support = union;
+ *   Stage 2 (Eq. 9-12 via Prop. 4.1)  softmax over the routed chunks' tokens and
+ *                      the query's own diagonal chunk, with the additive bias
+ *                      d = (log w - μ)/σ on routed tokens (μ = mean of log w over
+ *                      the support) and 0 on the diagonal.
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *     keeps no pointer after returning and allocates no device memory.
+ *   - Tensors are contiguous, batch-head-sequence-dim (BHSD):
+ *       Q [b, h_q, n, d], K and V [b, h_kv, n, d], q̄ [h_kv, d] (fp32),
+ *       k̄ [b, h_kv, kbar_cap, d] (fp32).
+ *   - Query head h belongs to KV group r = floor(h / g) with g = h_q / h_kv.
+ *   - Chunk c holds tokens [c*B, (c+1)*B). Only complete chunks have a summary
+ *     (T_c = floor(n / B)).
+ *   - Causal routing: the query at position p may route to chunks c < floor(p/B);
+ *     its own chunk (tokens floor(p/B)*B .. p) is the diagonal branch and is
+ *     always attended with bias 0. Non-causal: every complete chunk is routable
+ *     and the trailing n mod B tokens form the diagonal branch.
+ *   - Routed lists are ascending chunk ids per (b, r, query row), with the bias
+ *     of each listed chunk alongside.
+ *   - `stream` is a hipStream_t (NULL = the null stream). Calls only enqueue
+ *     work; they never synchronise.
+ *   - Every argument is validated on the host before anything is enqueued; on
+ *     error nothing is launched, outputs are untouched, and a detail string is
+ *     available from dash_last_error() (per thread). The library never aborts.
+ *     Device faults surface at the caller's next synchronisation.
+ *   - Supported: d in {64, 128}; B a multiple of 16 (the prefill attention
+ *     kernel needs B a multiple of 32); g = h_q/h_kv a power of two <= 16;
+ *     Q/K/V both fp32 or all bf16; α > 1, γ > 0, σ > 0 (σ = +inf allowed).
+ */
+#ifndef DASH_H
+#define DASH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DASH_OK = 0,
+    DASH_ERR_NULL = 1,         /* a required pointer is NULL                    */
+    DASH_ERR_SHAPE = 2,        /* inconsistent or non-positive sizes            */
+    DASH_ERR_PARAM = 3,        /* α, γ, σ out of range, bad dtype or flag       */
+    DASH_ERR_UNSUPPORTED = 4,  /* valid but outside the supported set above     */
+    DASH_ERR_WORKSPACE = 5,    /* workspace missing or smaller than required    */
+    DASH_ERR_LAUNCH = 6        /* the HIP runtime refused a launch              */
+} dash_status;
+
+typedef enum { DASH_F32 = 0, DASH_BF16 = 1 } dash_dtype;
+
+typedef enum { DASH_OP_ROUTE = 0, DASH_OP_PREFILL = 1, DASH_OP_DECODE = 2 } dash_op;
+
+/*
+ * Stage 0 (Eq. 4): for every (b, r) and every chunk c in [chunk_begin, chunk_end):
+ *   k̄[b,r,c,:] = sum_{t in chunk c} softmax_t(<q̄[r], K[b,r,t]>/sqrt(d)) K[b,r,t,:].
+ * K: [b, h_kv, n_kv, d] of k_dtype; qbar: [h_kv, d] fp32; kbar: [b, h_kv, kbar_cap, d]
+ * fp32 (only rows chunk_begin..chunk_end-1 are written). Requires
+ * 0 <= chunk_begin <= chunk_end <= min(floor(n_kv/B), kbar_cap). During decode,
+ * call it for a chunk once the chunk is complete (the summary is then fixed).
+ */
+dash_status dash_summarize(const void* K, int k_dtype, const float* qbar, float* kbar,
+                           int b, int h_kv, int n_kv, int kbar_cap, int d, int B,
+                           int chunk_begin, int chunk_end, void* stream);
+
+/*
+ * Stage 1 for a prefill (Eq. 6, the GQA paragraph, Prop. 4.1's μ and d): every
+ * query row i (position i) of Q [b, h_q, n, d] (q_dtype) is routed against
+ * k̄ [b, h_kv, kbar_cap, d] (chunks 0..floor(n/B)-1 must be summarised).
+ * Outputs per (b, r, i):
+ *   cnt [b, h_kv, n] int32      number of routed chunks |S_i|
+ *   idx [b, h_kv, n, list_cap]  int32 ascending routed chunk ids (first cnt valid)
+ *   bias[b, h_kv, n, list_cap]  fp32  d = (ln w - μ)/σ of each listed chunk
+ *   w_out (nullable) [b, h_kv, n, kbar_cap] fp32 dense group weights w (0 off
+ *          the visible set); meant for verification.
+ * list_cap >= floor(n/B) and kbar_cap >= floor(n/B). The workspace may be NULL
+ * when dash_workspace_bytes(DASH_OP_ROUTE, ...) is 0.
+ */
+dash_status dash_route(const void* Q, int q_dtype, const float* kbar,
+                       int b, int h_q, int h_kv, int n, int kbar_cap, int d, int B,
+                       float alpha, float gamma, float sigma, int causal,
+                       int32_t* idx, float* bias, int32_t* cnt, int list_cap,
+                       float* w_out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Stage 2 for a prefill (Eq. 10 in the bias form of Prop. 4.1): for every query
+ * head and row, softmax over the tokens of the routed chunks (logit
+ * <q,k>/sqrt(d) + bias of the chunk) and of the diagonal branch (bias 0, causal
+ * mask inside the own chunk), times V. Q, K, V share in_dtype; O
+ * [b, h_q, n, d] is written in out_dtype. idx/bias/cnt are dash_route's outputs
+ * (same list_cap). Requires B % 32 == 0.
+ */
+dash_status dash_attend_prefill(const void* Q, const void* K, const void* V, int in_dtype,
+                                const int32_t* idx, const float* bias, const int32_t* cnt,
+                                int list_cap, void* O, int out_dtype,
+                                int b, int h_q, int h_kv, int n, int d, int B, int causal,
+                                void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * One decode step (Stages 1-2 for one new query per sequence, split-KV Stage 2):
+ *   Q [b, h_q, 1, d]; Kc, Vc [b, h_kv, L_cap, d] hold the KV cache including the
+ *   new token; seq_len [b] (device int32) = KV length L incl. the new token, so
+ *   the query sits at position L-1; kbar [b, h_kv, kbar_cap, d] must hold the
+ *   summaries of chunks 0..floor((L-1)/B)-1. Device-side lengths are clamped to
+ *   [1, L_cap] and the routable chunks to kbar_cap.
+ *   O [b, h_q, 1, d] in out_dtype.
+ *   Optional outputs (NULL to skip): idx_out/bias_out [b, h_kv, list_cap],
+ *   cnt_out [b, h_kv], w_out [b, h_kv, kbar_cap] dense group weights.
+ * ws: at least dash_workspace_bytes(DASH_OP_DECODE, b, h_q, h_kv, L_cap, d, B)
+ * bytes of device memory (scores, routed lists and split-KV partials). Calls that
+ * share one workspace must not overlap.
+ */
+dash_status dash_attend_decode(const void* Q, const void* Kc, const void* Vc, int in_dtype,
+                               const float* kbar, const int32_t* seq_len,
+                               int b, int h_q, int h_kv, int L_cap, int kbar_cap, int d, int B,
+                               float alpha, float gamma, float sigma,
+                               void* O, int out_dtype,
+                               int32_t* idx_out, float* bias_out, int32_t* cnt_out,
+                               float* w_out, int list_cap,
+                               void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes an operation needs (n_or_Lcap: n for prefill ops, L_cap for
+ * decode). Returns 0 when no workspace is needed, (size_t)-1 on invalid sizes. */
+size_t dash_workspace_bytes(int op, int b, int h_q, int h_kv, int n_or_Lcap, int d, int B);
+
+/* Static English name of a status code. */
+const char* dash_status_string(int status);
+
+/* Detail of the last failed call on this thread ("" if none). */
+const char* dash_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DASH_H */

@@ -1,0 +1,68 @@
+"""Build libdash.so (the HIP kernels and the C ABI) for gfx950 with hipcc.
+
+Every .hip file under csrc/ is compiled to an object in parallel, then linked into
+long_context_amd/libdash.so next to this file. Usage: python -m long_context_amd.build
+"""
+from __future__ import annotations
+
+import concurrent.futures
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+OUT = os.path.join(HERE, "libdash.so")
+BUILD = os.path.join(os.path.dirname(HERE), "_build")
+
+ARCH = "gfx950"
+# Packed fp32 instructions are disabled for the device code; hipcc's host pass does
+# not know the feature and says so, which is harmless.
+HIPFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-Wno-unused-result"]
+
+
+def _hipcc() -> str:
+    for cand in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found; the ROCm toolchain is required to build libdash.so")
+
+
+def _compile(src: str, obj: str) -> None:
+    cmd = [_hipcc(), *HIPFLAGS, "-c", src, "-o", obj]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        msg = "\n".join(l for l in res.stderr.splitlines() if "not a recognized feature" not in l)
+        raise RuntimeError(f"hipcc failed for {os.path.basename(src)}:\n{msg}")
+
+
+def build(jobs: int | None = None, verbose: bool = True) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = sorted(f for f in os.listdir(CSRC) if f.endswith(".hip"))
+    jobs = jobs or min(len(srcs), os.cpu_count() or 4, 16)
+    objs = []
+    with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
+        futs = []
+        for f in srcs:
+            obj = os.path.join(BUILD, f[:-4] + ".o")
+            objs.append(obj)
+            futs.append(ex.submit(_compile, os.path.join(CSRC, f), obj))
+        for fut in futs:
+            fut.result()
+    tmp = OUT + ".tmp"
+    cmd = [_hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"link failed:\n{res.stderr}")
+    os.replace(tmp, OUT)
+    if verbose:
+        print(f"built {OUT} from {len(srcs)} sources")
+    return OUT
+
+
+if __name__ == "__main__":
+    build()
+    sys.exit(0)

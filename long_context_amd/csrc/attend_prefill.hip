@@ -1,0 +1,304 @@
+// Stage 2 of DashAttention for a prefill (paper review section 三, Eq. 9-12 through
+// the additive-bias form of Proposition 4.1):
+//   o_i = sum_{j in R_i ∪ D_i} softmax_j(<q_i, k_j>/sqrt(d) + d_ij) v_j,
+// with d_ij = bias of chunk c(j) on the routed tokens R_i and 0 on the diagonal
+// branch D_i (the query's own chunk up to itself, causal).
+//
+// sparse_prior_attn_kernel: one workgroup per (query tile, KV group, batch). The
+// tile is R_t consecutive rows inside one chunk times all g query heads of the
+// group (M = g*R_t pairs, 32 per wavefront); the heads of a group share one routed
+// list, so packing them costs no extra work. The workgroup first merges its rows'
+// lists into the union of routed chunks (ascending) and a per-(row, chunk) bias
+// table in LDS, then walks the union and finally the diagonal chunk:
+//   * K/V tiles of TT tokens are prefetched into registers while the previous tile
+//     is being used, then written to LDS (V transposed for the P·V product);
+//   * a wavefront skips a chunk none of its rows routes to;
+//   * S^T = K Q^T on MFMA, logits in log2 units with the bias folded in, online
+//     softmax per (row, head) lane, O^T += V^T P^T on MFMA; the division by the
+//     softmax denominator happens once at the end.
+#include "attn_common.h"
+#include "kernels.h"
+
+#include <math.h>
+
+namespace dash {
+
+struct PrefillParams {
+    const void* Q; const void* K; const void* V;
+    const int32_t* idx; const float* bias; const int32_t* cnt;
+    void* O;
+    int out_bf16, h_q, h_kv, n, B, T_c, list_cap, causal, g, log2g, R_t;
+    float scale_log2;    // log2(e)/sqrt(d)
+};
+
+template <typename T, int D, int TT>
+__global__ __launch_bounds__(256, 2) void sparse_prior_attn_kernel(PrefillParams p) {
+    typedef TileGeom<T, D, TT> G;
+    typedef Mfma<T> MM;
+    typedef typename MM::Op Op;
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    char* tile = smem;
+    float* btab = reinterpret_cast<float*>(smem + G::BYTES);
+    int* uflag = reinterpret_cast<int*>(btab + p.R_t * p.T_c);
+    int* ulist = uflag + p.T_c;
+    int* s_U = ulist + p.T_c;
+
+    const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
+    const int l32 = lane & 31, hl = lane >> 5;
+    const int r = blockIdx.y, bi = blockIdx.z;
+    const int g = p.g, lg = p.log2g, R_t = p.R_t;
+    const int row0 = blockIdx.x * R_t;
+    const int cq = row0 / p.B;
+    const int nvis = p.causal ? min(cq, p.T_c) : p.T_c;
+    const int last_row = min(row0 + R_t, p.n) - 1;
+    const size_t bhkv = (size_t)bi * p.h_kv + r;
+    const T* Kg = static_cast<const T*>(p.K) + bhkv * (size_t)p.n * D;
+    const T* Vg = static_cast<const T*>(p.V) + bhkv * (size_t)p.n * D;
+
+    // ---- union of the tile rows' routed chunks and the (row, chunk) bias table ----
+    for (int i = tid; i < R_t * nvis; i += 256) btab[(i / nvis) * p.T_c + i % nvis] = -INFINITY;
+    for (int c = tid; c < nvis; c += 256) uflag[c] = 0;
+    __syncthreads();
+    for (int j = 0; j < R_t; ++j) {
+        const int row = row0 + j;
+        if (row >= p.n) break;
+        const size_t rb = bhkv * p.n + row;
+        const int cn = p.cnt[rb];
+        for (int e = tid; e < cn; e += 256) {
+            const int c = p.idx[rb * p.list_cap + e];
+            if (c >= 0 && c < nvis) {
+                btab[j * p.T_c + c] = p.bias[rb * p.list_cap + e];
+                uflag[c] = 1;
+            }
+        }
+    }
+    __syncthreads();
+    if (wid == 0) {
+        int base = 0;
+        for (int c0 = 0; c0 < nvis; c0 += 64) {
+            const int c = c0 + lane;
+            const bool f = c < nvis && uflag[c] != 0;
+            const uint64_t m = ballot(f);
+            if (f) ulist[base + __builtin_popcountll(m & ((1ull << lane) - 1ull))] = c;
+            base += __builtin_popcountll(m);
+        }
+        if (lane == 0) *s_U = base;
+    }
+    __syncthreads();
+    const int U = *s_U;
+
+    // ---- this lane's (row, head) pair ----
+    const int M = g * R_t;
+    const bool wave_active = wid * 32 < M;
+    const int pair = wid * 32 + l32;
+    const int j = pair >> lg;
+    const int hh = r * g + (pair & (g - 1));
+    const int my_row = row0 + j;
+    const bool pair_ok = wave_active && j < R_t && my_row < p.n;
+    Op qf[D / 16];
+    if (pair_ok) {
+        const T* qrow = static_cast<const T*>(p.Q) + (((size_t)bi * p.h_q + hh) * p.n + my_row) * D + 8 * hl;
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) qf[s] = MM::load(qrow + 16 * s);
+    } else {
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) qf[s] = MM::zero();
+    }
+
+    float m_run = -INFINITY, l_run = 0.f;
+    f32x16 o_acc[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o_acc[db][i] = 0.f;
+
+    const int SPC = p.B / TT;
+    int diag_base, ndiag;
+    if (p.causal) {
+        diag_base = cq * p.B;
+        ndiag = (last_row - diag_base) / TT + 1;
+    } else {
+        diag_base = p.T_c * p.B;
+        ndiag = (p.n - diag_base + TT - 1) / TT;
+    }
+    const int nrouted = U * SPC;
+    const int nsteps = nrouted + ndiag;
+    const int nmax = p.n - 1;
+
+    TileRegs<T, D, TT, 256> regs;
+    auto tile_base = [&](int k) -> int {
+        return k < nrouted ? ulist[k / SPC] * p.B + (k % SPC) * TT : diag_base + (k - nrouted) * TT;
+    };
+    if (nsteps > 0) {
+        const int tb = tile_base(0);
+        regs.load(Kg, Vg, [&](int t) { return min(tb + t, nmax); }, tid);
+    }
+    for (int k = 0; k < nsteps; ++k) {
+        __syncthreads();
+        regs.store(tile, tid);
+        __syncthreads();
+        if (k + 1 < nsteps) {
+            const int tb1 = tile_base(k + 1);
+            regs.load(Kg, Vg, [&](int t) { return min(tb1 + t, nmax); }, tid);
+        }
+        if (!wave_active) continue;
+        const bool routed = k < nrouted;
+        const int tb = tile_base(k);
+        float bias2 = 0.f;
+        if (routed) {
+            const int c = ulist[k / SPC];
+            bias2 = pair_ok ? btab[j * p.T_c + c] * kLog2e : -INFINITY;
+            if (ballot(bias2 > -INFINITY) == 0) continue;   // no row of this wave routes c
+        }
+        // S^T = K Q^T: accumulator column = this lane's pair, rows = tokens
+        f32x16 sacc[TT / 32];
+#pragma unroll
+        for (int blk = 0; blk < TT / 32; ++blk) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sacc[blk][i] = 0.f;
+            const T* krow = reinterpret_cast<const T*>(tile + (32 * blk + l32) * G::KROW) + 8 * hl;
+#pragma unroll
+            for (int s = 0; s < D / 16; ++s) sacc[blk] = MM::mma(MM::load(krow + 16 * s), qf[s], sacc[blk]);
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int blk = 0; blk < TT / 32; ++blk)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                float v = fmaf(sacc[blk][i], p.scale_log2, bias2);
+                if (!routed) {
+                    const int tk = tb + 32 * blk + 8 * (i >> 2) + 4 * hl + (i & 3);
+                    if (p.causal ? (tk > my_row) : (tk >= p.n)) v = -INFINITY;
+                }
+                sacc[blk][i] = v;
+                mx = fmaxf(mx, v);
+            }
+        mx = fmaxf(mx, shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_run, mx);
+        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+        const float alpha = fast_exp2(m_run - m_use);
+        float ps = 0.f;
+#pragma unroll
+        for (int blk = 0; blk < TT / 32; ++blk)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float pv = fast_exp2(sacc[blk][i] - m_use);
+                sacc[blk][i] = pv;
+                ps += pv;
+            }
+        l_run = fmaf(l_run, alpha, ps);
+        m_run = m_new;
+        if (ballot(alpha != 1.f) != 0) {
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) o_acc[db][i] *= alpha;
+        }
+        // O^T += V^T P^T
+#pragma unroll
+        for (int s = 0; s < TT / 16; ++s) {
+            float pv8[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pv8[e] = sacc[s >> 1][8 * (s & 1) + e];
+            const Op pb = MM::pack(pv8);
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) {
+                const T* vrow = reinterpret_cast<const T*>(tile + G::KBYTES + (32 * db + l32) * G::VROW) + 16 * s + 8 * hl;
+                o_acc[db] = MM::mma(MM::load(vrow), pb, o_acc[db]);
+            }
+        }
+    }
+
+    const float l_tot = l_run + shfl_xor(l_run, 32);
+    if (pair_ok) {
+        const float inv = 1.f / l_tot;
+        const size_t obase = (((size_t)bi * p.h_q + hh) * p.n + my_row) * D;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                const int d0 = 32 * db + 8 * a + 4 * hl;
+                if (p.out_bf16) {
+                    u32x2 o;
+                    o[0] = (uint32_t)f32_to_bf16_bits(o_acc[db][4 * a] * inv) |
+                           ((uint32_t)f32_to_bf16_bits(o_acc[db][4 * a + 1] * inv) << 16);
+                    o[1] = (uint32_t)f32_to_bf16_bits(o_acc[db][4 * a + 2] * inv) |
+                           ((uint32_t)f32_to_bf16_bits(o_acc[db][4 * a + 3] * inv) << 16);
+                    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.O) + obase + d0) = o;
+                } else {
+                    f32x4 o;
+                    o[0] = o_acc[db][4 * a] * inv; o[1] = o_acc[db][4 * a + 1] * inv;
+                    o[2] = o_acc[db][4 * a + 2] * inv; o[3] = o_acc[db][4 * a + 3] * inv;
+                    *reinterpret_cast<f32x4*>(static_cast<float*>(p.O) + obase + d0) = o;
+                }
+            }
+    }
+}
+
+static size_t prefill_lds(int R_t, int T_c, int tile_bytes) {
+    return (size_t)tile_bytes + (size_t)R_t * T_c * 4 + (size_t)2 * T_c * 4 + 16;
+}
+
+static int tile_bytes_of(int d, bool bf16, int TT) {
+    if (bf16) return d == 64 ? TileGeom<uint16_t, 64, 64>::BYTES * (TT == 64) + TileGeom<uint16_t, 64, 32>::BYTES * (TT == 32)
+                             : TileGeom<uint16_t, 128, 64>::BYTES * (TT == 64) + TileGeom<uint16_t, 128, 32>::BYTES * (TT == 32);
+    return d == 64 ? TileGeom<float, 64, 64>::BYTES * (TT == 64) + TileGeom<float, 64, 32>::BYTES * (TT == 32)
+                   : TileGeom<float, 128, 64>::BYTES * (TT == 64) + TileGeom<float, 128, 32>::BYTES * (TT == 32);
+}
+
+static constexpr size_t kMaxLds = 160 * 1024;
+
+void prefill_tiling(int g, int B, int T_c, int d, bool bf16, int* rows, size_t* lds_bytes) {
+    *rows = 0;
+    *lds_bytes = 0;
+    if (B % 32 != 0 || g < 1 || g > 16) return;
+    const int TT = (B % 64 == 0) ? 64 : 32;
+    const int tb = tile_bytes_of(d, bf16, TT);
+    for (int m = 128; m >= 32; m >>= 1) {
+        const int R_t = m / g;
+        if (R_t < 1 || B % R_t != 0) continue;
+        const size_t lds = prefill_lds(R_t, T_c, tb);
+        if (lds <= kMaxLds) {
+            *rows = R_t;
+            *lds_bytes = lds;
+            return;
+        }
+    }
+}
+
+template <typename T, int D, int TT>
+static hipError_t launch_prefill_t(const PrefillParams& p, int b, size_t lds, hipStream_t s) {
+    static bool configured = false;
+    if (!configured) {
+        hipFuncSetAttribute(reinterpret_cast<const void*>(&sparse_prior_attn_kernel<T, D, TT>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
+        configured = true;
+    }
+    dim3 grid((p.n + p.R_t - 1) / p.R_t, p.h_kv, b), block(256);
+    hipLaunchKernelGGL((sparse_prior_attn_kernel<T, D, TT>), grid, block, lds, s, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_attend_prefill(const PrefillArgs& a, hipStream_t s) {
+    PrefillParams p;
+    p.Q = a.Q; p.K = a.K; p.V = a.V; p.idx = a.idx; p.bias = a.bias; p.cnt = a.cnt; p.O = a.O;
+    p.out_bf16 = a.out_bf16; p.h_q = a.h_q; p.h_kv = a.h_kv; p.n = a.n; p.B = a.B;
+    p.T_c = a.n / a.B; p.list_cap = a.list_cap; p.causal = a.causal;
+    p.g = a.h_q / a.h_kv;
+    p.log2g = 0;
+    while ((1 << p.log2g) < p.g) ++p.log2g;
+    p.scale_log2 = (float)(1.4426950408889634 / sqrt((double)a.d));
+    size_t lds = 0;
+    prefill_tiling(p.g, a.B, p.T_c, a.d, a.in_bf16, &p.R_t, &lds);
+    if (p.R_t == 0) return hipErrorInvalidValue;
+    if (a.n == 0) return hipSuccess;
+    const bool t64 = (a.B % 64 == 0);
+    if (a.in_bf16) {
+        if (a.d == 64) return t64 ? launch_prefill_t<uint16_t, 64, 64>(p, a.b, lds, s) : launch_prefill_t<uint16_t, 64, 32>(p, a.b, lds, s);
+        return t64 ? launch_prefill_t<uint16_t, 128, 64>(p, a.b, lds, s) : launch_prefill_t<uint16_t, 128, 32>(p, a.b, lds, s);
+    }
+    if (a.d == 64) return t64 ? launch_prefill_t<float, 64, 64>(p, a.b, lds, s) : launch_prefill_t<float, 64, 32>(p, a.b, lds, s);
+    return t64 ? launch_prefill_t<float, 128, 64>(p, a.b, lds, s) : launch_prefill_t<float, 128, 32>(p, a.b, lds, s);
+}
+
+}  // namespace dash

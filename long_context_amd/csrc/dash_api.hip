@@ -1,0 +1,217 @@
+// C ABI of the DashAttention forward pass (declared in include/dash.h).
+// Every entry point validates all of its arguments on the host before it enqueues
+// anything; on error it returns a status, leaves the outputs untouched and records
+// a detail string for dash_last_error(). Nothing here synchronises the stream.
+#include "../../include/dash.h"
+#include "kernels.h"
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+dash_status fail(dash_status st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+dash_status ok() {
+    g_err[0] = '\0';
+    return DASH_OK;
+}
+
+dash_status from_hip(hipError_t e, const char* what) {
+    if (e == hipSuccess) return ok();
+    return fail(DASH_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+bool valid_dtype(int t) { return t == DASH_F32 || t == DASH_BF16; }
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+dash_status check_common(int b, int h_q, int h_kv, int d, int B) {
+    if (b < 1 || h_q < 1 || h_kv < 1) return fail(DASH_ERR_SHAPE, "b, h_q, h_kv must be >= 1");
+    if (h_q % h_kv != 0) return fail(DASH_ERR_SHAPE, "h_q (%d) must be a multiple of h_kv (%d)", h_q, h_kv);
+    if (d != 64 && d != 128) return fail(DASH_ERR_UNSUPPORTED, "head dim %d not in {64, 128}", d);
+    if (B < 16 || B % 16 != 0) return fail(DASH_ERR_UNSUPPORTED, "chunk size %d must be a positive multiple of 16", B);
+    const int g = h_q / h_kv;
+    if (!is_pow2(g) || g > 16) return fail(DASH_ERR_UNSUPPORTED, "GQA group size %d must be a power of two <= 16", g);
+    return DASH_OK;
+}
+
+dash_status check_params(float alpha, float gamma, float sigma) {
+    if (!(alpha > 1.0f) || isinf(alpha)) return fail(DASH_ERR_PARAM, "alpha must be finite and > 1 (got %g)", alpha);
+    if (!(gamma > 0.0f) || isinf(gamma)) return fail(DASH_ERR_PARAM, "gamma must be finite and > 0 (got %g)", gamma);
+    if (!(sigma > 0.0f)) return fail(DASH_ERR_PARAM, "sigma must be > 0 or +inf (got %g)", sigma);
+    return DASH_OK;
+}
+
+struct DecodeLayout {
+    int T_ws, T_route, slice_tokens, max_slices;
+    size_t off_scores, off_idx, off_bias, off_cnt, off_part, total;
+};
+
+DecodeLayout decode_layout(int b, int h_q, int h_kv, int L_cap, int kbar_cap, int d, int B) {
+    DecodeLayout L;
+    const int g = h_q / h_kv;
+    L.T_ws = (L_cap - 1) / B;                       // upper bound of the routable chunks
+    int tr_dummy = 0;
+    dash::decode_geometry(L_cap, L.T_ws, B, &tr_dummy, &L.slice_tokens, &L.max_slices);
+    L.T_route = kbar_cap < L.T_ws ? kbar_cap : L.T_ws;
+    const size_t nT = (size_t)(L.T_ws > 0 ? L.T_ws : 1);
+    L.off_scores = 0;
+    L.off_idx = align256(L.off_scores + (size_t)b * h_q * nT * 4);
+    L.off_bias = align256(L.off_idx + (size_t)b * h_kv * nT * 4);
+    L.off_cnt = align256(L.off_bias + (size_t)b * h_kv * nT * 4);
+    L.off_part = align256(L.off_cnt + (size_t)b * h_kv * 4);
+    L.total = align256(L.off_part + (size_t)b * h_kv * L.max_slices * g * (d + 2) * 4);
+    return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dash_status_string(int status) {
+    switch (status) {
+        case DASH_OK: return "ok";
+        case DASH_ERR_NULL: return "null pointer";
+        case DASH_ERR_SHAPE: return "invalid shape";
+        case DASH_ERR_PARAM: return "invalid parameter";
+        case DASH_ERR_UNSUPPORTED: return "unsupported configuration";
+        case DASH_ERR_WORKSPACE: return "workspace too small";
+        case DASH_ERR_LAUNCH: return "kernel launch failed";
+        default: return "unknown status";
+    }
+}
+
+const char* dash_last_error(void) { return g_err; }
+
+dash_status dash_summarize(const void* K, int k_dtype, const float* qbar, float* kbar,
+                           int b, int h_kv, int n_kv, int kbar_cap, int d, int B,
+                           int chunk_begin, int chunk_end, void* stream) {
+    if (!K || !qbar || !kbar) return fail(DASH_ERR_NULL, "K, qbar and kbar must be non-null");
+    if (!valid_dtype(k_dtype)) return fail(DASH_ERR_PARAM, "bad K dtype %d", k_dtype);
+    dash_status st = check_common(b, h_kv, h_kv, d, B);
+    if (st != DASH_OK) return st;
+    if (n_kv < 0 || kbar_cap < 0) return fail(DASH_ERR_SHAPE, "n_kv and kbar_cap must be >= 0");
+    const int T = n_kv / B;
+    const int lim = T < kbar_cap ? T : kbar_cap;
+    if (chunk_begin < 0 || chunk_begin > chunk_end || chunk_end > lim)
+        return fail(DASH_ERR_SHAPE, "chunk range [%d, %d) outside [0, %d]", chunk_begin, chunk_end, lim);
+    dash::SummaryArgs a{K, k_dtype == DASH_BF16, qbar, kbar, b, h_kv, n_kv, kbar_cap, d, B,
+                        chunk_begin, chunk_end};
+    return from_hip(dash::launch_summary(a, (hipStream_t)stream), "chunk_summary_kernel");
+}
+
+dash_status dash_route(const void* Q, int q_dtype, const float* kbar,
+                       int b, int h_q, int h_kv, int n, int kbar_cap, int d, int B,
+                       float alpha, float gamma, float sigma, int causal,
+                       int32_t* idx, float* bias, int32_t* cnt, int list_cap,
+                       float* w_out, void* ws, size_t ws_bytes, void* stream) {
+    (void)ws; (void)ws_bytes;
+    if (!Q || !kbar || !idx || !bias || !cnt) return fail(DASH_ERR_NULL, "Q, kbar, idx, bias and cnt must be non-null");
+    if (!valid_dtype(q_dtype)) return fail(DASH_ERR_PARAM, "bad Q dtype %d", q_dtype);
+    if (causal != 0 && causal != 1) return fail(DASH_ERR_PARAM, "causal must be 0 or 1");
+    dash_status st = check_common(b, h_q, h_kv, d, B);
+    if (st != DASH_OK) return st;
+    if ((st = check_params(alpha, gamma, sigma)) != DASH_OK) return st;
+    if (n < 0) return fail(DASH_ERR_SHAPE, "n must be >= 0");
+    const int T = n / B;
+    if (kbar_cap < T) return fail(DASH_ERR_SHAPE, "kbar_cap %d < floor(n/B) = %d", kbar_cap, T);
+    if (list_cap < T) return fail(DASH_ERR_SHAPE, "list_cap %d < floor(n/B) = %d", list_cap, T);
+    if (dash::route_tiles_bucket(T) == 0) return fail(DASH_ERR_UNSUPPORTED, "%d chunks exceed the router's 1024", T);
+    dash::RouteArgs a{Q, q_dtype == DASH_BF16, kbar, b, h_q, h_kv, n, kbar_cap, d, B, causal, list_cap,
+                      alpha, gamma, sigma, idx, bias, cnt, w_out};
+    return from_hip(dash::launch_route(a, (hipStream_t)stream), "entmax_route_kernel");
+}
+
+dash_status dash_attend_prefill(const void* Q, const void* K, const void* V, int in_dtype,
+                                const int32_t* idx, const float* bias, const int32_t* cnt,
+                                int list_cap, void* O, int out_dtype,
+                                int b, int h_q, int h_kv, int n, int d, int B, int causal,
+                                void* ws, size_t ws_bytes, void* stream) {
+    (void)ws; (void)ws_bytes;
+    if (!Q || !K || !V || !idx || !bias || !cnt || !O) return fail(DASH_ERR_NULL, "Q, K, V, idx, bias, cnt and O must be non-null");
+    if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return fail(DASH_ERR_PARAM, "bad dtype");
+    if (causal != 0 && causal != 1) return fail(DASH_ERR_PARAM, "causal must be 0 or 1");
+    dash_status st = check_common(b, h_q, h_kv, d, B);
+    if (st != DASH_OK) return st;
+    if (B % 32 != 0) return fail(DASH_ERR_UNSUPPORTED, "prefill attention needs B %% 32 == 0 (B = %d)", B);
+    if (n < 0) return fail(DASH_ERR_SHAPE, "n must be >= 0");
+    const int T = n / B;
+    if (list_cap < T) return fail(DASH_ERR_SHAPE, "list_cap %d < floor(n/B) = %d", list_cap, T);
+    int rows = 0;
+    size_t lds = 0;
+    dash::prefill_tiling(h_q / h_kv, B, T, d, in_dtype == DASH_BF16, &rows, &lds);
+    if (rows == 0) return fail(DASH_ERR_UNSUPPORTED, "no query tiling fits LDS (g=%d, B=%d, T_c=%d)", h_q / h_kv, B, T);
+    dash::PrefillArgs a{Q, K, V, in_dtype == DASH_BF16, idx, bias, cnt, list_cap, O, out_dtype == DASH_BF16,
+                        b, h_q, h_kv, n, d, B, causal};
+    return from_hip(dash::launch_attend_prefill(a, (hipStream_t)stream), "sparse_prior_attn_kernel");
+}
+
+size_t dash_workspace_bytes(int op, int b, int h_q, int h_kv, int n_or_Lcap, int d, int B) {
+    if (b < 1 || h_q < 1 || h_kv < 1 || h_q % h_kv != 0 || n_or_Lcap < 0 || d < 1 || B < 1) return (size_t)-1;
+    switch (op) {
+        case DASH_OP_ROUTE: return 0;
+        case DASH_OP_PREFILL: return 0;
+        case DASH_OP_DECODE: {
+            if (n_or_Lcap < 1) return (size_t)-1;
+            return decode_layout(b, h_q, h_kv, n_or_Lcap, 1 << 30, d, B).total;
+        }
+        default: return (size_t)-1;
+    }
+}
+
+dash_status dash_attend_decode(const void* Q, const void* Kc, const void* Vc, int in_dtype,
+                               const float* kbar, const int32_t* seq_len,
+                               int b, int h_q, int h_kv, int L_cap, int kbar_cap, int d, int B,
+                               float alpha, float gamma, float sigma,
+                               void* O, int out_dtype,
+                               int32_t* idx_out, float* bias_out, int32_t* cnt_out,
+                               float* w_out, int list_cap,
+                               void* ws, size_t ws_bytes, void* stream) {
+    if (!Q || !Kc || !Vc || !kbar || !seq_len || !O) return fail(DASH_ERR_NULL, "Q, Kc, Vc, kbar, seq_len and O must be non-null");
+    const int given = (idx_out != nullptr) + (bias_out != nullptr) + (cnt_out != nullptr);
+    if (given != 0 && given != 3) return fail(DASH_ERR_NULL, "idx_out, bias_out and cnt_out must be all NULL or all non-null");
+    if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return fail(DASH_ERR_PARAM, "bad dtype");
+    dash_status st = check_common(b, h_q, h_kv, d, B);
+    if (st != DASH_OK) return st;
+    if ((st = check_params(alpha, gamma, sigma)) != DASH_OK) return st;
+    if (B % 32 != 0) return fail(DASH_ERR_UNSUPPORTED, "decode attention needs B %% 32 == 0 (B = %d)", B);
+    if (L_cap < 1 || kbar_cap < 0) return fail(DASH_ERR_SHAPE, "L_cap must be >= 1 and kbar_cap >= 0");
+    const DecodeLayout Lo = decode_layout(b, h_q, h_kv, L_cap, kbar_cap, d, B);
+    if (Lo.T_ws > 1024) return fail(DASH_ERR_UNSUPPORTED, "%d routable chunks exceed the decode router's 1024", Lo.T_ws);
+    if (given == 3 && list_cap < Lo.T_route) return fail(DASH_ERR_SHAPE, "list_cap %d < routable chunks %d", list_cap, Lo.T_route);
+    if (!ws || ws_bytes < Lo.total) return fail(DASH_ERR_WORKSPACE, "decode needs %zu workspace bytes, got %zu", Lo.total, ws ? ws_bytes : (size_t)0);
+    char* w = static_cast<char*>(ws);
+    dash::DecodeArgs a;
+    a.Q = Q; a.Kc = Kc; a.Vc = Vc; a.in_bf16 = in_dtype == DASH_BF16; a.kbar = kbar; a.seq_len = seq_len;
+    a.b = b; a.h_q = h_q; a.h_kv = h_kv; a.L_cap = L_cap; a.kbar_cap = kbar_cap; a.d = d; a.B = B;
+    a.alpha = alpha; a.gamma = gamma; a.sigma = sigma; a.O = O; a.out_bf16 = out_dtype == DASH_BF16;
+    if (given == 3) {
+        a.idx = idx_out; a.bias = bias_out; a.cnt = cnt_out; a.list_cap = list_cap;
+    } else {
+        a.idx = reinterpret_cast<int32_t*>(w + Lo.off_idx);
+        a.bias = reinterpret_cast<float*>(w + Lo.off_bias);
+        a.cnt = reinterpret_cast<int32_t*>(w + Lo.off_cnt);
+        a.list_cap = Lo.T_ws > 0 ? Lo.T_ws : 1;
+    }
+    a.w_out = w_out;
+    a.scores = reinterpret_cast<float*>(w + Lo.off_scores);
+    a.partials = reinterpret_cast<float*>(w + Lo.off_part);
+    a.T_route = Lo.T_route;
+    a.max_slices = Lo.max_slices;
+    a.slice_tokens = Lo.slice_tokens;
+    return from_hip(dash::launch_decode(a, (hipStream_t)stream), "decode kernels");
+}
+
+}  // extern "C"

@@ -1,0 +1,57 @@
+// Internal launchers of the DashAttention kernels (called by the C ABI layer).
+// Each returns hipSuccess or the launch error; arguments are already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dash {
+
+struct SummaryArgs {
+    const void* K; bool k_bf16; const float* qbar; float* kbar;
+    int b, h_kv, n_kv, kbar_cap, d, B, chunk_begin, chunk_end;
+};
+hipError_t launch_summary(const SummaryArgs& a, hipStream_t s);
+
+struct RouteArgs {
+    const void* Q; bool q_bf16; const float* kbar;
+    int b, h_q, h_kv, n, kbar_cap, d, B, causal, list_cap;
+    float alpha, gamma, sigma;
+    int32_t* idx; float* bias; int32_t* cnt; float* w_out;
+};
+hipError_t launch_route(const RouteArgs& a, hipStream_t s);
+// Number of 16-chunk tiles the routing kernels keep in registers for T chunks
+// (0 if T is beyond the supported range).
+int route_tiles_bucket(int T);
+
+struct PrefillArgs {
+    const void* Q; const void* K; const void* V; bool in_bf16;
+    const int32_t* idx; const float* bias; const int32_t* cnt; int list_cap;
+    void* O; bool out_bf16;
+    int b, h_q, h_kv, n, d, B, causal;
+};
+hipError_t launch_attend_prefill(const PrefillArgs& a, hipStream_t s);
+// Rows per query tile and dynamic LDS bytes of the prefill attention kernel
+// (rows = 0 when the shape is not supported).
+void prefill_tiling(int g, int B, int T_c, int d, bool bf16, int* rows, size_t* lds_bytes);
+
+struct DecodeArgs {
+    const void* Q; const void* Kc; const void* Vc; bool in_bf16;
+    const float* kbar; const int32_t* seq_len;
+    int b, h_q, h_kv, L_cap, kbar_cap, d, B;
+    float alpha, gamma, sigma;
+    void* O; bool out_bf16;
+    int32_t* idx; float* bias; int32_t* cnt; float* w_out; int list_cap;
+    float* scores;       // [b, h_q, T_route] workspace
+    float* partials;     // [b, h_kv, max_slices, g, d + 2] workspace
+    int T_route;         // routable chunk capacity: min(floor((L_cap-1)/B), kbar_cap)
+    int max_slices;
+    int slice_tokens;
+};
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+// Split-KV geometry of the decode kernels for a given cache capacity.
+void decode_geometry(int L_cap, int kbar_cap, int B, int* T_route, int* slice_tokens,
+                     int* max_slices);
+
+}  // namespace dash

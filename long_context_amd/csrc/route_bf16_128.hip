@@ -1,0 +1,8 @@
+// Instantiation of the prefill routing kernel for bf16 queries, head dim 128.
+#include "route_impl.h"
+
+namespace dash {
+hipError_t launch_route_bf16_128(const RouteParams& p, int b, hipStream_t s) {
+    return launch_route_d<uint16_t, 128>(p, b, s);
+}
+}  // namespace dash

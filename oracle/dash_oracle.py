@@ -58,6 +58,8 @@ def entmax_tau_bisect(x, valid=None, alpha=1.5, iters=200):
     x = _f64(x)
     if valid is None:
         valid = np.ones(x.shape, bool)
+    if x.shape[-1] == 0:
+        return np.full(x.shape[:-1], np.nan)
     p = 1.0 / (alpha - 1.0)
     cnt = valid.sum(-1)
     xm = np.where(valid, x, -np.inf)
@@ -92,6 +94,8 @@ def entmax_tau_sorted(x, valid=None, alpha=1.5):
     x = _f64(x)
     if valid is None:
         valid = np.ones(x.shape, bool)
+    if x.shape[-1] == 0:
+        return np.full(x.shape[:-1], np.nan)
     cnt = valid.sum(-1)
     xm = np.where(valid, x, -np.inf)
     mx = np.where(cnt > 0, xm.max(-1), 0.0)
@@ -226,7 +230,8 @@ def route(Qr, pos, kbar, B, alpha, gamma, sigma, causal, n_kv, keep_heads=False,
                     tau[bi, h, r0:r1] = t
                     with np.errstate(invalid="ignore"):
                         gap = np.where(valid, np.abs(x - t[:, None]), np.inf)
-                    margin[bi, r, r0:r1] = np.minimum(margin[bi, r, r0:r1], gap.min(-1))
+                    if T > 0:
+                        margin[bi, r, r0:r1] = np.minimum(margin[bi, r, r0:r1], gap.min(-1))
                     if keep_heads:
                         what_all[bi, h, r0:r1] = p
                         x_all[bi, h, r0:r1] = np.where(valid, x, 0.0)

@@ -1,0 +1,139 @@
+"""The C ABI without a GPU: exported symbols and host-side validation.
+
+Every call here fails validation on the host, which returns before any HIP call,
+so nothing is launched. Fake non-null pointers are never dereferenced.
+"""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "long_context_amd", "libdash.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libdash.so not built")
+
+
+@pytest.fixture(scope="module")
+def dash():
+    from long_context_amd import dash as d
+    return d
+
+
+P = ctypes.c_void_p(4096)        # a non-null pointer that validation never touches
+NUL = None
+
+
+def declared_symbols():
+    text = open(os.path.join(ROOT, "include", "dash.h")).read()
+    return sorted(set(re.findall(r"\b(dash_[a-z_]+)\s*\(", text)))
+
+
+def test_header_symbols_are_exported(dash):
+    syms = declared_symbols()
+    assert set(syms) == set(dash.SYMBOLS)
+    for s in syms:
+        assert hasattr(dash.lib, s), s
+
+
+def test_status_strings(dash):
+    assert dash.dash_status_string(0) == "ok"
+    assert dash.dash_status_string(5) == "workspace too small"
+    assert dash.dash_status_string(99) == "unknown status"
+
+
+def _route(dash, **kw):
+    a = dict(Q=P, qdt=1, kbar=P, b=1, h_q=4, h_kv=2, n=256, cap=4, d=128, B=64, alpha=1.5,
+             gamma=1.0, sigma=1.0, causal=1, idx=P, bias=P, cnt=P, list_cap=4, w=NUL)
+    a.update(kw)
+    return dash.lib.dash_route(a["Q"], a["qdt"], a["kbar"], a["b"], a["h_q"], a["h_kv"], a["n"],
+                               a["cap"], a["d"], a["B"], a["alpha"], a["gamma"], a["sigma"],
+                               a["causal"], a["idx"], a["bias"], a["cnt"], a["list_cap"], a["w"],
+                               NUL, 0, NUL)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Q=NUL), 1), (dict(idx=NUL), 1), (dict(cnt=NUL), 1),
+    (dict(h_q=3), 2), (dict(b=0), 2), (dict(n=-1), 2), (dict(cap=3), 2), (dict(list_cap=2), 2),
+    (dict(alpha=1.0), 3), (dict(alpha=float("nan")), 3), (dict(gamma=0.0), 3),
+    (dict(gamma=float("inf")), 3), (dict(sigma=0.0), 3), (dict(sigma=float("nan")), 3),
+    (dict(qdt=7), 3), (dict(causal=2), 3),
+    (dict(d=96), 4), (dict(B=24), 4), (dict(h_q=64, h_kv=2), 4), (dict(h_q=6, h_kv=2), 4),
+    (dict(n=65 * 1024, cap=1040, list_cap=1040), 4),
+])
+def test_route_validation(dash, kw, status):
+    assert _route(dash, **kw) == status
+    assert dash.lib.dash_last_error().decode() != ""
+
+
+def test_route_accepts_infinite_sigma_in_validation(dash):
+    # sigma = +inf passes validation; a NULL Q then still fails with DASH_ERR_NULL first
+    assert _route(dash, Q=NUL, sigma=math.inf) == 1
+
+
+def _summ(dash, **kw):
+    a = dict(K=P, kdt=1, qbar=P, kbar=P, b=1, h_kv=2, n=256, cap=4, d=128, B=64, c0=0, c1=4)
+    a.update(kw)
+    return dash.lib.dash_summarize(a["K"], a["kdt"], a["qbar"], a["kbar"], a["b"], a["h_kv"],
+                                   a["n"], a["cap"], a["d"], a["B"], a["c0"], a["c1"], NUL)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(K=NUL), 1), (dict(kbar=NUL), 1), (dict(kdt=2), 3), (dict(c1=5), 2),
+    (dict(c0=3, c1=2), 2), (dict(cap=3), 2), (dict(c0=-1), 2), (dict(d=32), 4), (dict(B=8), 4),
+])
+def test_summarize_validation(dash, kw, status):
+    assert _summ(dash, **kw) == status
+
+
+def _prefill(dash, **kw):
+    a = dict(Q=P, K=P, V=P, dt=1, idx=P, bias=P, cnt=P, cap=4, O=P, odt=0, b=1, h_q=4, h_kv=2,
+             n=256, d=128, B=64, causal=1)
+    a.update(kw)
+    return dash.lib.dash_attend_prefill(a["Q"], a["K"], a["V"], a["dt"], a["idx"], a["bias"],
+                                        a["cnt"], a["cap"], a["O"], a["odt"], a["b"], a["h_q"],
+                                        a["h_kv"], a["n"], a["d"], a["B"], a["causal"], NUL, 0, NUL)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(O=NUL), 1), (dict(V=NUL), 1), (dict(odt=3), 3), (dict(cap=3), 2), (dict(B=48), 4),
+    (dict(h_q=5, h_kv=2), 2),
+])
+def test_prefill_validation(dash, kw, status):
+    assert _prefill(dash, **kw) == status
+
+
+def _decode(dash, ws_bytes, **kw):
+    a = dict(Q=P, Kc=P, Vc=P, dt=1, kbar=P, sl=P, b=4, h_q=32, h_kv=2, L=131072, cap=1024,
+             d=128, B=128, alpha=1.5, gamma=1.0, sigma=1.0, O=P, odt=0, idx=NUL, bias=NUL,
+             cnt=NUL, w=NUL, list_cap=0, ws=P)
+    a.update(kw)
+    return dash.lib.dash_attend_decode(a["Q"], a["Kc"], a["Vc"], a["dt"], a["kbar"], a["sl"],
+                                       a["b"], a["h_q"], a["h_kv"], a["L"], a["cap"], a["d"],
+                                       a["B"], a["alpha"], a["gamma"], a["sigma"], a["O"],
+                                       a["odt"], a["idx"], a["bias"], a["cnt"], a["w"],
+                                       a["list_cap"], a["ws"], ws_bytes, NUL)
+
+
+def test_decode_workspace_checks(dash):
+    need = dash.dash_workspace_bytes(dash.DASH_OP_DECODE, 4, 32, 2, 131072, 128, 128)
+    assert 0 < need < (1 << 30)
+    assert _decode(dash, need - 1) == dash.DASH_ERR_WORKSPACE
+    assert _decode(dash, need, ws=NUL) == dash.DASH_ERR_WORKSPACE
+    assert _decode(dash, need, idx=P) == dash.DASH_ERR_NULL          # partial list outputs
+    assert _decode(dash, need, idx=P, bias=P, cnt=P, list_cap=10) == dash.DASH_ERR_SHAPE
+    assert _decode(dash, need, alpha=0.5) == dash.DASH_ERR_PARAM
+    assert _decode(dash, need, B=48) == dash.DASH_ERR_UNSUPPORTED
+    assert _decode(dash, need, L=300000) == dash.DASH_ERR_UNSUPPORTED
+
+
+def test_workspace_sizes(dash):
+    assert dash.dash_workspace_bytes(dash.DASH_OP_ROUTE, 1, 32, 2, 32768, 128, 64) == 0
+    assert dash.dash_workspace_bytes(dash.DASH_OP_PREFILL, 1, 32, 2, 32768, 128, 64) == 0
+    big = dash.dash_workspace_bytes(dash.DASH_OP_DECODE, 16, 32, 2, 32768, 128, 64)
+    small = dash.dash_workspace_bytes(dash.DASH_OP_DECODE, 16, 32, 2, 4096, 128, 64)
+    assert big > small > 0
+    assert dash.dash_workspace_bytes(9, 1, 1, 1, 1, 64, 64) == 2 ** 64 - 1
+    assert dash.dash_workspace_bytes(0, 1, 3, 2, 1, 64, 64) == 2 ** 64 - 1

@@ -360,3 +360,16 @@ def test_group_sparsity_monotone_in_alpha_on_clusters():
           for a in (1.25, 1.5, 2.0)]
     assert sp[0] <= sp[1] <= sp[2]
     assert sp[2] > sp[0]
+
+
+def test_sequence_shorter_than_a_chunk_routes_nothing():
+    """n < B: no complete chunk, so no row routes anywhere and Stage 2 is causal
+    softmax over the row's own (partial) chunk."""
+    w = _small(n=12)
+    res = O.prefill(w.Q, w.K, w.V, w.qbar, w.B, 1.5, 3.0, 1.0, True)
+    assert res["kbar"].shape[2] == 0 and res["route"]["cnt"].sum() == 0
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(np.asarray(w.Q, np.float64)),
+        torch.from_numpy(np.asarray(np.repeat(w.K, 2, axis=1), np.float64)),
+        torch.from_numpy(np.asarray(np.repeat(w.V, 2, axis=1), np.float64)), is_causal=True)
+    np.testing.assert_allclose(res["O"], ref.numpy(), atol=1e-13)

@@ -1,0 +1,284 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle.
+
+Small shapes span several query tiles, chunks and a ragged tail so the oracle checks
+every row; the five reference workloads run at full size with the launch
+configuration the benchmark uses and are checked on sampled rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+from long_context_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+def _gu():
+    from tests import gpu_util
+    return gpu_util
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu(gpu_lib):
+    yield
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+# ------------------------------------------------------------------------------------
+# Stage 0
+# ------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype,d,B,n", [("f32", 64, 64, 1024), ("bf16", 128, 64, 1000),
+                                         ("bf16", 64, 16, 200), ("f32", 128, 128, 640),
+                                         ("bf16", 128, 32, 96)])
+def test_summaries_match_oracle(dtype, d, B, n):
+    G = _gu()
+    from oracle import dash_oracle as O
+    w = inputs.make_prefill(b=2, h_q=4, h_kv=2, d=d, n=n, B=B, dtype=dtype, seed=1)
+    K = G.to_dev(w.K, dtype)
+    kbar = torch.full((2, 2, n // B + 3, d), float("nan"), device="cuda")
+    from long_context_amd import dash
+    dash.dash_summarize(K, torch.from_numpy(w.qbar).cuda(), kbar, B)
+    torch.cuda.synchronize()
+    ref = O.stage0_summaries(w.K, w.qbar, B)
+    got = kbar[:, :, :n // B].cpu().numpy()
+    assert np.abs(got - ref).max() <= G.TOL_KBAR
+    assert torch.isnan(kbar[:, :, n // B:]).all()          # rows beyond the range untouched
+
+
+def test_summary_of_chunk_range_and_zero_query():
+    G = _gu()
+    from oracle import dash_oracle as O
+    from long_context_amd import dash
+    w = inputs.make_prefill(b=1, h_q=2, h_kv=2, d=128, n=512, B=64, dtype="bf16", seed=2)
+    K = G.to_dev(w.K, "bf16")
+    kbar = torch.zeros((1, 2, 8, 128), device="cuda")
+    dash.dash_summarize(K, torch.zeros((2, 128), device="cuda"), kbar, 64, 3, 6)
+    torch.cuda.synchronize()
+    got = kbar.cpu().numpy()
+    mean = w.K.astype(np.float64).reshape(1, 2, 8, 64, 128).mean(3)
+    assert np.abs(got[:, :, 3:6] - mean[:, :, 3:6]).max() <= 1e-5
+    assert np.all(got[:, :, :3] == 0) and np.all(got[:, :, 6:] == 0)
+
+
+# ------------------------------------------------------------------------------------
+# Prefill: routing and attention on small shapes (all rows checked)
+# ------------------------------------------------------------------------------------
+
+SMALL = [
+    # dtype, b, h_q, h_kv, d, n, B, alpha, gamma, sigma, causal
+    ("f32", 1, 1, 1, 64, 1024, 64, 1.5, 1.0, 1.0, True),        # the fp32 workload's shape
+    ("f32", 1, 1, 1, 64, 1024, 64, 1.5, 30.0, 1.0, True),       # sparse fp32 routing
+    ("bf16", 2, 16, 2, 128, 1000, 64, 1.5, 8.0, 1.0, True),     # GQA 8, ragged tail
+    ("bf16", 1, 32, 2, 128, 768, 64, 2.0, 3.0, 1.0, True),      # GQA 16, sparsemax
+    ("bf16", 1, 32, 2, 128, 640, 64, 1.25, 4.0, 1.0, True),     # α = 1.25
+    ("bf16", 1, 8, 2, 128, 512, 64, 1.75, 6.0, 1.0, True),      # non-integer exponent
+    ("bf16", 2, 4, 2, 64, 600, 32, 1.5, 6.0, 0.5, True),        # B = 32, d = 64, σ = 0.5
+    ("bf16", 1, 4, 1, 128, 700, 128, 1.5, 6.0, float("inf"), True),   # B = 128, σ = inf
+    ("bf16", 1, 8, 2, 128, 520, 64, 1.5, 6.0, 1.0, False),      # non-causal with a tail
+    ("f32", 1, 2, 1, 128, 300, 32, 1.5, 5.0, 1.0, True),        # fp32, d = 128
+    ("bf16", 1, 16, 8, 128, 48, 64, 1.5, 5.0, 1.0, True),       # n < B: no routable chunk
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[f"{c[0]}-g{c[2] // c[3]}-d{c[4]}-n{c[5]}-B{c[6]}-a{c[7]}-s{c[9]}-c{int(c[10])}" for c in SMALL])
+def test_prefill_small_matches_oracle(case):
+    G = _gu()
+    dtype, b, h_q, h_kv, d, n, B, alpha, gamma, sigma, causal = case
+    w = inputs.make_prefill(b=b, h_q=h_q, h_kv=h_kv, d=d, n=n, B=B, alphas=(alpha,), gamma=gamma,
+                            sigma=sigma, causal=causal, dtype=dtype, seed=3)
+    _log(f"prefill case {case}")
+    g = G.gpu_prefill(w)
+    rows = np.arange(n)
+    kb, rt, Oref = G.oracle_prefill_rows(w, rows)
+    assert np.abs(g["kbar"][:, :, :n // B].cpu().numpy() - kb).max() <= G.TOL_KBAR
+    nex, tot = G.compare_route(g, rt, rows, n // B)
+    err = G.compare_out(g["O"].cpu().numpy(), Oref, rt["margin"] <= G.MARGIN, h_q // h_kv, dtype)
+    _log(f"  exempt rows {nex}/{tot}, output error {err:.3e}")
+
+
+def test_prefill_bf16_output_dtype():
+    G = _gu()
+    w = inputs.make_prefill(b=1, h_q=16, h_kv=2, d=128, n=512, B=64, gamma=6.0, dtype="bf16", seed=4)
+    g32 = G.gpu_prefill(w)
+    g16 = G.gpu_prefill(w, out_dtype=torch.bfloat16)
+    ref = g32["O"].to(torch.bfloat16).float()
+    assert torch.equal(g16["O"].float(), ref)
+
+
+def test_prefill_is_deterministic():
+    G = _gu()
+    w = inputs.make_prefill(b=1, h_q=32, h_kv=2, d=128, n=1024, B=64, gamma=3.0, dtype="bf16", seed=5)
+    a = G.gpu_prefill(w)
+    b = G.gpu_prefill(w)
+    for k in ("kbar", "cnt", "w", "O"):
+        assert torch.equal(a[k], b[k]), k
+    assert torch.equal(a["idx"][a["cnt"] > 0], b["idx"][b["cnt"] > 0])
+
+
+# ------------------------------------------------------------------------------------
+# Decode on small shapes
+# ------------------------------------------------------------------------------------
+
+def gpu_decode(w, seq_len, kbar=None, with_lists=True):
+    G = _gu()
+    from long_context_amd import dash
+    Q, K, V = G.to_dev(w.Q, w.dtype), G.to_dev(w.K, w.dtype), G.to_dev(w.V, w.dtype)
+    b, h_q, _, d = w.Q.shape
+    L_cap = w.K.shape[2]
+    T = L_cap // w.B
+    if kbar is None:
+        kbar = dash.alloc_kbar(b, w.h_kv, T, d)
+        dash.dash_summarize(K, torch.from_numpy(w.qbar).cuda(), kbar, w.B)
+    sl = torch.from_numpy(np.asarray(seq_len, np.int32)).cuda()
+    ws = dash.alloc_decode_ws(b, h_q, w.h_kv, L_cap, d, w.B)
+    Oo = torch.empty((b, h_q, 1, d), device="cuda")
+    cap = max((L_cap - 1) // w.B, 1)
+    idx = torch.full((b, w.h_kv, cap), -1, dtype=torch.int32, device="cuda")
+    bias = torch.zeros((b, w.h_kv, cap), device="cuda")
+    cnt = torch.zeros((b, w.h_kv), dtype=torch.int32, device="cuda")
+    wo = torch.zeros((b, w.h_kv, kbar.shape[2]), device="cuda")
+    if with_lists:
+        dash.dash_attend_decode(Q, K, V, kbar, sl, w.B, w.alpha, w.gamma, w.sigma, Oo, ws,
+                                idx, bias, cnt, wo)
+    else:
+        dash.dash_attend_decode(Q, K, V, kbar, sl, w.B, w.alpha, w.gamma, w.sigma, Oo, ws)
+    torch.cuda.synchronize()
+    return dict(O=Oo, idx=idx, bias=bias, cnt=cnt, w=wo, kbar=kbar)
+
+
+def check_decode(w, seq_len, g):
+    G = _gu()
+    from oracle import dash_oracle as O
+    kb = O.stage0_summaries(w.K, w.qbar, w.B)
+    res = O.decode(w.Q, w.K, w.V, kb, seq_len, w.B, w.alpha, w.gamma, w.sigma)
+    nex = 0
+    errs = []
+    for bi, rt in enumerate(res["routes"]):
+        L = int(seq_len[bi])
+        T = (L - 1) // w.B
+        ex = rt["margin"][0, :, 0] <= G.MARGIN              # [h_kv]
+        nex += int(ex.sum())
+        if T > 0:
+            dw = np.abs(g["w"][bi, :, :T].cpu().numpy() - rt["w"][0, :, 0, :T]).max()
+            assert dw <= G.TOL_W, f"b={bi}: weights differ by {dw}"
+        for r in range(w.h_kv):
+            if ex[r]:
+                continue
+            ref = np.nonzero(rt["support"][0, r, 0])[0]
+            c = int(g["cnt"][bi, r])
+            assert c == ref.size, f"b={bi} r={r}: cnt {c} != {ref.size}"
+            assert np.array_equal(g["idx"][bi, r, :c].cpu().numpy(), ref)
+        errs.append(G.compare_out(g["O"][bi:bi + 1].cpu().numpy(), res["O"][bi:bi + 1],
+                                  ex[None, :, None], w.g, w.dtype))
+    return nex, max(errs)
+
+
+DEC = [
+    # dtype, b, h_q, h_kv, d, L, B, alpha, gamma, seq_len
+    ("bf16", 3, 32, 2, 128, 4096, 64, 1.5, 1.0, [4096, 4000, 65]),
+    ("bf16", 2, 16, 2, 128, 5000, 128, 1.5, 6.0, [5000, 4097]),
+    ("bf16", 2, 8, 2, 64, 3000, 32, 2.0, 4.0, [3000, 33]),
+    ("bf16", 2, 32, 2, 128, 2048, 64, 1.25, 2.0, [2048, 64]),
+    ("f32", 2, 4, 2, 64, 1500, 64, 1.5, 3.0, [1500, 1]),
+]
+
+
+@pytest.mark.parametrize("case", DEC, ids=[f"{c[0]}-g{c[2] // c[3]}-L{c[5]}-B{c[6]}-a{c[7]}" for c in DEC])
+def test_decode_small_matches_oracle(case):
+    dtype, b, h_q, h_kv, d, L, B, alpha, gamma, seq_len = case
+    _log(f"decode case {case}")
+    w = inputs.make_decode(b=b, h_q=h_q, h_kv=h_kv, d=d, L=L, B=B, alphas=(alpha,), gamma=gamma,
+                           dtype=dtype, seed=6, seq_len=seq_len)
+    g = gpu_decode(w, seq_len)
+    nex, err = check_decode(w, np.asarray(seq_len), g)
+    _log(f"  exempt groups {nex}, output error {err:.3e}")
+    g2 = gpu_decode(w, seq_len, kbar=g["kbar"], with_lists=False)
+    assert torch.equal(g["O"], g2["O"])
+
+
+def test_decode_equals_last_prefill_row():
+    G = _gu()
+    w = inputs.make_prefill(b=1, h_q=16, h_kv=2, d=128, n=1000, B=64, gamma=4.0, dtype="bf16", seed=7)
+    pre = G.gpu_prefill(w)
+    wd = inputs.make_decode(b=1, h_q=16, h_kv=2, d=128, L=1000, B=64, gamma=4.0, dtype="bf16", seed=7)
+    wd.Q = np.ascontiguousarray(w.Q[:, :, -1:])
+    wd.K, wd.V, wd.qbar = w.K, w.V, w.qbar
+    dec = gpu_decode(wd, [1000], kbar=pre["kbar"])
+    r = pre["cnt"][0, :, -1]
+    assert torch.equal(dec["cnt"][0], r)
+    o1 = pre["O"][:, :, -1:].cpu().numpy()
+    o2 = dec["O"].cpu().numpy()
+    assert np.abs(o1 - o2).max() <= 1e-5
+
+
+# ------------------------------------------------------------------------------------
+# The five reference workloads at full size (sampled rows)
+# ------------------------------------------------------------------------------------
+
+def _sample_rows(n, B, k, seed):
+    rng = np.random.default_rng(seed)
+    fixed = np.array([0, 1, B - 1, B, B + 1, 2 * B - 1, n // 2, n - B - 1, n - B, n - 2, n - 1])
+    return np.unique(np.concatenate([fixed, rng.choice(n, size=k, replace=False)]))
+
+
+def test_workload_prefill_1k_fp32_all_rows():
+    G = _gu()
+    w = inputs.prefill_1k_fp32()
+    g = G.gpu_prefill(w)
+    rows = np.arange(w.n)
+    kb, rt, Oref = G.oracle_prefill_rows(w, rows)
+    nex, tot = G.compare_route(g, rt, rows, w.n // w.B)
+    err = G.compare_out(g["O"].cpu().numpy(), Oref, rt["margin"] <= G.MARGIN, 1, "f32")
+    _log(f"prefill_1k_fp32: exempt {nex}/{tot}, max |dO| {err:.3e}")
+
+
+def test_workload_prefill_8k_needles():
+    G = _gu()
+    w = inputs.prefill_8k_gqa8_needles()
+    g = G.gpu_prefill(w)
+    rows = _sample_rows(w.n, w.B, 600, 11)
+    kb, rt, Oref = G.oracle_prefill_rows(w, rows)
+    assert np.abs(g["kbar"].cpu().numpy() - kb).max() <= G.TOL_KBAR
+    nex, tot = G.compare_route(g, rt, rows, w.n // w.B)
+    err = G.compare_out(g["O"][:, :, rows].cpu().numpy(), Oref, rt["margin"] <= G.MARGIN, w.g, "bf16")
+    _log(f"prefill_8k_gqa8_needles: exempt {nex}/{tot}, row error {err:.3e}")
+
+
+@pytest.mark.parametrize("alpha", [1.25, 1.5, 2.0])
+def test_workload_prefill_32k_clusters(alpha):
+    G = _gu()
+    w = _cached_32k()
+    g = G.gpu_prefill(w, alpha=alpha)
+    rows = _sample_rows(w.n, w.B, 150, 12)
+    kb, rt, Oref = G.oracle_prefill_rows(w, rows, kbar_or=_cached_32k_kbar(), alpha=alpha)
+    nex, tot = G.compare_route(g, rt, rows, w.n // w.B)
+    err = G.compare_out(g["O"][:, :, rows].cpu().numpy(), Oref, rt["margin"] <= G.MARGIN, w.g, "bf16")
+    _log(f"prefill_32k_clusters alpha={alpha}: exempt {nex}/{tot}, row error {err:.3e}")
+
+
+_C32 = {}
+
+
+def _cached_32k():
+    if "w" not in _C32:
+        _C32["w"] = inputs.prefill_32k_clusters()
+    return _C32["w"]
+
+
+def _cached_32k_kbar():
+    from oracle import dash_oracle as O
+    if "kb" not in _C32:
+        w = _cached_32k()
+        _C32["kb"] = O.stage0_summaries(w.K, w.qbar, w.B)
+    return _C32["kb"]
+
+
+@pytest.mark.parametrize("name", ["decode_32k_b16", "decode_128k_b4"])
+def test_workload_decode(name):
+    w = inputs.make(name)
+    g = gpu_decode(w, w.seq_len)
+    nex, err = check_decode(w, w.seq_len, g)
+    _log(f"{name}: exempt groups {nex}, row error {err:.3e}, routed {g['cnt'].cpu().numpy().ravel().tolist()}")
