@@ -1,0 +1,309 @@
+"""Benchmark of the DashAttention forward pass on one MI355X.
+
+One step = one pass of the whole hot path over synthetic inputs:
+  * prefill of the 32K clustered workload (b=1, 32 query / 2 KV heads, d=128,
+    n=32768, B=64, γ=1): Stage 0 summaries, Stage 1 routing, Stage 2 attention;
+  * one decode step of the 128K workload (b=4, 32 / 2 heads, d=128, L=131072,
+    B=128): routing against the cached summaries and split-KV attention.
+`value` is the prefill throughput in tokens/s at α=1.5; the decode latency, the
+α sweep {1.25, 1.5, 2.0}, per-stage times, the dense (0%-sparsity) baseline and
+the roofline fractions ride along in the same JSON line.
+
+Timing: HIP events recorded on the stream the kernels are launched on (torch's
+current stream, which the binding passes to every entry point), W untimed warm-up
+steps, then exactly K timed steps bracketed by device synchronisation.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "DashAttention fwd: prefill tok/s @32k, decode µs/step @128k; % of roofline"
+PEAK_BF16_TFLOPS = 2500.0          # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0              # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--alpha", type=float, default=1.5)
+    ap.add_argument("--no-sweep", action="store_true", help="skip the alpha sweep")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--no-dense", action="store_true", help="skip the dense baseline")
+    ap.add_argument("--cpu-rows", type=int, default=3072, help="query rows of the oracle sample")
+    ap.add_argument("--only", choices=["prefill", "decode", "both"], default="both")
+    return ap.parse_args()
+
+
+class Prefill:
+    """Device buffers of the 32K prefill and the three ABI calls of one pass."""
+
+    def __init__(self, w, torch, dash):
+        self.w, self.torch, self.dash = w, torch, dash
+        self.Q = torch.from_numpy(w.Q).to("cuda", torch.bfloat16)
+        self.K = torch.from_numpy(w.K).to("cuda", torch.bfloat16)
+        self.V = torch.from_numpy(w.V).to("cuda", torch.bfloat16)
+        self.qbar = torch.from_numpy(w.qbar).cuda()
+        b, h_q, n, d = w.Q.shape
+        self.T = n // w.B
+        self.kbar = dash.alloc_kbar(b, w.h_kv, self.T, d)
+        self.idx, self.bias, self.cnt, _ = dash.alloc_route(b, w.h_kv, n, self.T)
+        self.O = torch.empty((b, h_q, n, d), dtype=torch.bfloat16, device="cuda")
+
+    def run(self, alpha, ev=None):
+        d, w = self.dash, self.w
+        if ev: ev[0].record()
+        d.dash_summarize(self.K, self.qbar, self.kbar, w.B)
+        if ev: ev[1].record()
+        d.dash_route(self.Q, self.kbar, w.B, alpha, w.gamma, w.sigma, True, self.idx, self.bias,
+                     self.cnt)
+        if ev: ev[2].record()
+        d.dash_attend_prefill(self.Q, self.K, self.V, self.idx, self.bias, self.cnt, self.O, w.B, True)
+        if ev: ev[3].record()
+
+    def stats(self):
+        """Work of the last routing (bookkeeping outside the timed region).
+
+        flops_row:  per-row algorithmic Stage-2 flops, 4 d g (B |S_i| + |D_i|) summed
+                    over rows and KV groups (what the method must compute);
+        flops_wave: flops the MFMAs execute: a wavefront (32 (row, head) pairs =
+                    32/g rows) runs a chunk when any of its rows routes it, and the
+                    diagonal in 64-token tiles;
+        flops_tile: the same at workgroup-tile granularity (128 pairs).
+        """
+        torch, w = self.torch, self.w
+        n, B, d, g = w.n, w.B, w.d, w.g
+        cnt = self.cnt.to(torch.int64)                     # [b, h_kv, n]
+        pos = torch.arange(n, device="cuda")
+        vis = torch.clamp(pos // B, max=self.T)
+        diag = pos - (pos // B) * B + 1
+        rows_sup = cnt.sum().item()
+        rows_vis = (vis.sum() * w.h_kv * w.b).item()
+        diag_tok = (diag.sum() * w.h_kv * w.b).item()
+        flops_row = 4.0 * d * g * (B * rows_sup + diag_tok)
+
+        def union_and_diag(rows_per_group):
+            uni = 0
+            for r in range(w.h_kv):
+                for i0 in range(0, n, 2048):
+                    c = cnt[0, r, i0:i0 + 2048]
+                    ids = self.idx[0, r, i0:i0 + 2048, :self.T].to(torch.int64)
+                    valid = torch.arange(self.T, device="cuda")[None, :] < c[:, None]
+                    mask = torch.zeros((ids.shape[0], self.T), dtype=torch.bool, device="cuda")
+                    mask.scatter_(1, torch.where(valid, ids, torch.zeros_like(ids)), valid)
+                    uni += mask.view(-1, rows_per_group, self.T).any(1).sum().item()
+            dt = 0
+            for t0 in range(0, n, rows_per_group):
+                last = min(t0 + rows_per_group, n) - 1
+                dt += ((last - (t0 // B) * B) // 64 + 1) * 64
+            return uni, dt * w.h_kv * w.b
+
+        uw, dw = union_and_diag(max(32 // g, 1))
+        ut, dtk = union_and_diag(max(128 // g, 1))
+        flops_wave = 4.0 * d * 32 * (B * uw + dw)
+        flops_tile = 4.0 * d * 128 * (B * ut + dtk)
+        return dict(flops_row=flops_row, flops_wave=flops_wave, flops_tile=flops_tile,
+                    sparsity=1.0 - rows_sup / max(rows_vis, 1),
+                    inflation_wave=flops_wave / flops_row, inflation_tile=flops_tile / flops_row)
+
+
+class Decode:
+    def __init__(self, w, torch, dash):
+        self.w, self.torch, self.dash = w, torch, dash
+        self.Q = torch.from_numpy(w.Q).to("cuda", torch.bfloat16)
+        self.K = torch.from_numpy(w.K).to("cuda", torch.bfloat16)
+        self.V = torch.from_numpy(w.V).to("cuda", torch.bfloat16)
+        b, h_q, _, d = w.Q.shape
+        self.T = w.n // w.B
+        self.kbar = dash.alloc_kbar(b, w.h_kv, self.T, d)
+        dash.dash_summarize(self.K, torch.from_numpy(w.qbar).cuda(), self.kbar, w.B)
+        self.sl = torch.from_numpy(w.seq_len).cuda()
+        self.ws = dash.alloc_decode_ws(b, h_q, w.h_kv, w.n, d, w.B)
+        cap = (w.n - 1) // w.B
+        self.idx = torch.empty((b, w.h_kv, cap), dtype=torch.int32, device="cuda")
+        self.bias = torch.empty((b, w.h_kv, cap), device="cuda")
+        self.cnt = torch.empty((b, w.h_kv), dtype=torch.int32, device="cuda")
+        self.O = torch.empty((b, h_q, 1, d), dtype=torch.bfloat16, device="cuda")
+
+    def run(self, ev=None):
+        w = self.w
+        if ev: ev[0].record()
+        self.dash.dash_attend_decode(self.Q, self.K, self.V, self.kbar, self.sl, w.B, w.alpha,
+                                     w.gamma, w.sigma, self.O, self.ws, self.idx, self.bias,
+                                     self.cnt)
+        if ev: ev[1].record()
+
+    def bytes_per_step(self):
+        w = self.w
+        cnt = self.cnt.cpu().numpy().astype(np.int64)
+        L = w.seq_len.astype(np.int64)
+        vis = (L - 1) // w.B
+        diag = L - vis * w.B
+        total = 0
+        for bi in range(w.b):
+            for r in range(w.h_kv):
+                total += vis[bi] * w.d * 4                                  # summaries
+                total += (w.B * cnt[bi, r] + diag[bi]) * w.d * 2 * 2        # K + V bf16
+        total += w.Q.size * 2 + w.Q.size * 2 + cnt.size * 4 + cnt.sum() * 8
+        return int(total), cnt
+
+
+def dense_lists(pre, torch):
+    """Full routed lists (every visible chunk, bias 0): dense causal attention."""
+    w = pre.w
+    T = pre.T
+    pos = torch.arange(w.n, device="cuda")
+    idx = torch.arange(T, dtype=torch.int32, device="cuda").expand(w.b, w.h_kv, w.n, T).contiguous()
+    cnt = torch.clamp(pos // w.B, max=T).to(torch.int32).expand(w.b, w.h_kv, w.n).contiguous()
+    bias = torch.zeros((w.b, w.h_kv, w.n, T), device="cuda")
+    return idx, bias, cnt
+
+
+def time_events(torch, fn, nev, steps, warmup):
+    for _ in range(warmup):
+        fn(None)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for k in range(steps):
+        fn(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    seg = np.array([[evs[k][j].elapsed_time(evs[k][j + 1]) for j in range(nev - 1)]
+                    for k in range(steps)])
+    return seg, wall
+
+
+def cpu_baseline(w, rows_n):
+    from oracle import dash_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    rows = np.unique(np.linspace(0, w.n - 1, rows_n).astype(np.int64))
+    t0 = time.perf_counter()
+    O.prefill(w.Q, w.K, w.V, w.qbar, w.B, 1.5, w.gamma, w.sigma, True, rows=rows)
+    dt = time.perf_counter() - t0
+    return {"value": rows.size / dt, "unit": "tok/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{rows.size} evenly spaced query rows (all 32 heads) of the 32K prefill at "
+                      f"alpha=1.5, Stage 0 over the whole K; {dt:.1f} s on {os.cpu_count()} host "
+                      f"CPUs; tok/s = rows / time"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+    import torch
+    from long_context_amd import dash, inputs
+
+    out = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic"}
+    print(f"[bench] generating workloads", file=sys.stderr, flush=True)
+    wp = inputs.prefill_32k_clusters()
+    pre = Prefill(wp, torch, dash)
+    res = {}
+
+    # --- prefill at the headline α, timed per stage ------------------------------
+    seg, wall = time_events(torch, lambda ev: pre.run(args.alpha, ev), 4, args.steps, args.warmup)
+    st = pre.stats()
+    t_sum, t_route, t_att = (float(np.mean(seg[:, j])) for j in range(3))
+    t_pre = t_sum + t_route + t_att
+    res["prefill"] = dict(ms=t_pre, stage0_ms=t_sum, stage1_ms=t_route, stage2_ms=t_att,
+                          tok_s=wp.n / (t_pre * 1e-3), sparsity=st["sparsity"],
+                          stage2_row_tflops=st["flops_row"] / (t_att * 1e-3) / 1e12,
+                          stage2_wave_tflops=st["flops_wave"] / (t_att * 1e-3) / 1e12,
+                          stage2_tile_tflops=st["flops_tile"] / (t_att * 1e-3) / 1e12,
+                          inflation_wave=st["inflation_wave"], inflation_tile=st["inflation_tile"],
+                          wall_s=wall)
+    print(f"[bench] prefill alpha={args.alpha}: {res['prefill']}", file=sys.stderr, flush=True)
+
+    sweep = {}
+    if not args.no_sweep:
+        for a in (1.25, 1.5, 2.0):
+            s2, _ = time_events(torch, lambda ev: pre.run(a, ev), 4, max(3, args.steps // 2), 1)
+            sta = pre.stats()
+            tt = float(s2.sum(1).mean())
+            sweep[str(a)] = dict(tok_s=wp.n / (tt * 1e-3), ms=tt, sparsity=sta["sparsity"],
+                                 stage2_ms=float(s2[:, 2].mean()),
+                                 stage2_row_tflops=sta["flops_row"] / (float(s2[:, 2].mean()) * 1e-3) / 1e12)
+            print(f"[bench] sweep alpha={a}: {sweep[str(a)]}", file=sys.stderr, flush=True)
+        pre.run(args.alpha)
+        torch.cuda.synchronize()
+
+    # --- dense (0% sparsity) baseline of the same Stage-2 kernel ------------------
+    dense = None
+    if not args.no_dense:
+        di, db, dc = dense_lists(pre, torch)
+        Od = torch.empty_like(pre.O)
+        fn = lambda ev: (ev and ev[0].record(),
+                         dash.dash_attend_prefill(pre.Q, pre.K, pre.V, di, db, dc, Od, wp.B, True),
+                         ev and ev[1].record())
+        sd, _ = time_events(torch, fn, 2, max(3, args.steps // 2), 1)
+        td = float(sd.mean())
+        dense_flops = 4.0 * wp.d * wp.h_q * (wp.n * (wp.n + 1) / 2)
+        dense = dict(stage2_ms=td, tflops=dense_flops / (td * 1e-3) / 1e12,
+                     speedup_vs_dense=td / t_pre)
+        del di, db, dc, Od
+        print(f"[bench] dense: {dense}", file=sys.stderr, flush=True)
+
+    # --- decode at 128K ------------------------------------------------------------
+    dec = None
+    if args.only in ("decode", "both"):
+        wd = inputs.decode_128k_b4()
+        dd = Decode(wd, torch, dash)
+        sdec, _ = time_events(torch, dd.run, 2, args.steps, args.warmup)
+        tdec = float(sdec.mean())
+        nbytes, cnt = dd.bytes_per_step()
+        dec = dict(us_per_step=tdec * 1e3, gbs=nbytes / (tdec * 1e-3) / 1e9,
+                   hbm_frac=nbytes / (tdec * 1e-3) / 1e9 / PEAK_HBM_GBS, bytes=nbytes,
+                   routed=cnt.ravel().tolist())
+        print(f"[bench] decode: {dec}", file=sys.stderr, flush=True)
+        del dd
+
+    t_step = t_pre + (dec["us_per_step"] * 1e-3 if dec else 0.0)
+    out.update({"value": res["prefill"]["tok_s"], "unit": "tok/s", "ms_per_step": t_step,
+                "config": {"workload": "prefill_32k_clusters + decode_128k_b4",
+                           "prefill": "b=1 h_q=32 h_kv=2 d=128 n=32768 B=64 gamma=1 sigma=1 "
+                                      f"alpha={args.alpha}, 32 clusters x 4 chunks per KV head",
+                           "decode": "b=4 h_q=32 h_kv=2 d=128 L=131072 B=128 alpha=1.5, "
+                                     "4 flat + 4 sharp groups, 8 needles per group"}})
+    att = res["prefill"]
+    out["roofline"] = {"bound": "mfma", "kernel": "sparse_prior_attn_kernel",
+                       "achieved": att["stage2_row_tflops"], "peak": PEAK_BF16_TFLOPS,
+                       "unit": "TFLOP/s", "frac": att["stage2_row_tflops"] / PEAK_BF16_TFLOPS,
+                       "traffic": None,
+                       "routed_block_tflops": att["stage2_wave_tflops"],
+                       "routed_block_frac": att["stage2_wave_tflops"] / PEAK_BF16_TFLOPS}
+    out["prefill"] = att
+    out["alpha_sweep"] = sweep
+    out["dense_baseline"] = dense
+    if dec:
+        out["decode"] = dec
+        out["decode_roofline"] = {"bound": "hbm", "kernel": "decode (route + split-KV + combine)",
+                                  "achieved": dec["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                  "frac": dec["hbm_frac"], "traffic": None}
+    del pre
+    torch.cuda.empty_cache()
+    if not args.no_cpu:
+        print(f"[bench] timing the oracle on the host", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(wp, args.cpu_rows)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

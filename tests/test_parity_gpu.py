@@ -93,7 +93,8 @@ def test_prefill_small_matches_oracle(case):
     g = G.gpu_prefill(w)
     rows = np.arange(n)
     kb, rt, Oref = G.oracle_prefill_rows(w, rows)
-    assert np.abs(g["kbar"][:, :, :n // B].cpu().numpy() - kb).max() <= G.TOL_KBAR
+    if n // B > 0:
+        assert np.abs(g["kbar"][:, :, :n // B].cpu().numpy() - kb).max() <= G.TOL_KBAR
     nex, tot = G.compare_route(g, rt, rows, n // B)
     err = G.compare_out(g["O"].cpu().numpy(), Oref, rt["margin"] <= G.MARGIN, h_q // h_kv, dtype)
     _log(f"  exempt rows {nex}/{tot}, output error {err:.3e}")
@@ -115,7 +116,9 @@ def test_prefill_is_deterministic():
     b = G.gpu_prefill(w)
     for k in ("kbar", "cnt", "w", "O"):
         assert torch.equal(a[k], b[k]), k
-    assert torch.equal(a["idx"][a["cnt"] > 0], b["idx"][b["cnt"] > 0])
+    listed = torch.arange(a["idx"].shape[-1], device="cuda") < a["cnt"][..., None]
+    assert torch.equal(a["idx"][listed], b["idx"][listed])
+    assert torch.equal(a["bias"][listed], b["bias"][listed])
 
 
 # ------------------------------------------------------------------------------------
@@ -209,9 +212,14 @@ def test_decode_equals_last_prefill_row():
     dec = gpu_decode(wd, [1000], kbar=pre["kbar"])
     r = pre["cnt"][0, :, -1]
     assert torch.equal(dec["cnt"][0], r)
-    o1 = pre["O"][:, :, -1:].cpu().numpy()
-    o2 = dec["O"].cpu().numpy()
-    assert np.abs(o1 - o2).max() <= 1e-5
+    assert torch.equal(dec["idx"][0][:, :int(r.max())], pre["idx"][0, :, -1, :int(r.max())]) or \
+        int(r.min()) != int(r.max())
+    # both paths round P to bf16 (in different tile orders), so they agree to the
+    # bf16 output tolerance rather than bit for bit
+    o1 = pre["O"][:, :, -1:].cpu().numpy().astype(np.float64)
+    o2 = dec["O"].cpu().numpy().astype(np.float64)
+    rel = np.abs(o1 - o2).max(-1) / np.sqrt((o1 ** 2).mean(-1))
+    assert rel.max() <= 2e-2
 
 
 # ------------------------------------------------------------------------------------
