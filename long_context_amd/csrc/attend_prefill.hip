@@ -47,7 +47,8 @@ __global__ __launch_bounds__(256, 2) void sparse_prior_attn_kernel(PrefillParams
     const int l32 = lane & 31, hl = lane >> 5;
     const int r = blockIdx.y, bi = blockIdx.z;
     const int g = p.g, lg = p.log2g, R_t = p.R_t;
-    const int row0 = blockIdx.x * R_t;
+    // causal tiles near the end of the sequence carry the most work: launch them first
+    const int row0 = (gridDim.x - 1 - blockIdx.x) * R_t;
     const int cq = row0 / p.B;
     const int nvis = p.causal ? min(cq, p.T_c) : p.T_c;
     const int last_row = min(row0 + R_t, p.n) - 1;
@@ -160,35 +161,44 @@ __global__ __launch_bounds__(256, 2) void sparse_prior_attn_kernel(PrefillParams
 #pragma unroll
             for (int s = 0; s < D / 16; ++s) sacc[blk] = MM::mma(MM::load(krow + 16 * s), qf[s], sacc[blk]);
         }
+        // mask the diagonal tile on the raw scores, then the tile maximum; the scale
+        // c1 = log2(e)/sqrt(d) > 0 commutes with the maximum
+        if (!routed) {
+#pragma unroll
+            for (int blk = 0; blk < TT / 32; ++blk)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int tk = tb + 32 * blk + 8 * (i >> 2) + 4 * hl + (i & 3);
+                    if (p.causal ? (tk > my_row) : (tk >= p.n)) sacc[blk][i] = -INFINITY;
+                }
+        }
         float mx = -INFINITY;
 #pragma unroll
         for (int blk = 0; blk < TT / 32; ++blk)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                float v = fmaf(sacc[blk][i], p.scale_log2, bias2);
-                if (!routed) {
-                    const int tk = tb + 32 * blk + 8 * (i >> 2) + 4 * hl + (i & 3);
-                    if (p.causal ? (tk > my_row) : (tk >= p.n)) v = -INFINITY;
-                }
-                sacc[blk][i] = v;
-                mx = fmaxf(mx, v);
-            }
+            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[blk][i]);
         mx = fmaxf(mx, shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx);
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = fast_exp2(m_run - m_use);
+        const float tmax = fmaf(mx, p.scale_log2, bias2);     // -inf when nothing is visible
+        // lazy rescaling: the reference maximum only moves when the tile maximum exceeds
+        // it by more than 8 (probabilities stay <= 2^8 in between)
+        const bool grow = tmax > m_run + 8.f;
+        float alpha = 1.f;
+        if (grow) {
+            alpha = fast_exp2(m_run - tmax);
+            m_run = tmax;
+        }
+        const float off = bias2 - ((m_run == -INFINITY) ? 0.f : m_run);
         float ps = 0.f;
 #pragma unroll
         for (int blk = 0; blk < TT / 32; ++blk)
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const float pv = fast_exp2(sacc[blk][i] - m_use);
+                const float pv = fast_exp2(fmaf(sacc[blk][i], p.scale_log2, off));
                 sacc[blk][i] = pv;
                 ps += pv;
             }
         l_run = fmaf(l_run, alpha, ps);
-        m_run = m_new;
-        if (ballot(alpha != 1.f) != 0) {
+        if (ballot(grow) != 0) {
 #pragma unroll
             for (int db = 0; db < D / 32; ++db)
 #pragma unroll

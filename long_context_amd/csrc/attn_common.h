@@ -86,8 +86,6 @@ struct TileGeom {
     static constexpr int VBYTES = D * VROW;
     static constexpr int BYTES = KBYTES + VBYTES;
     static constexpr int KPIECES = TT * D * ES / 16;   // 16-byte pieces of the K tile
-    static constexpr int EPD = 4 / ES;                 // elements per dword (2 bf16, 1 f32)
-    static constexpr int VBLOCKS = (TT / 8) * (D / EPD);   // (8 tokens x 1 dword) blocks of V
 };
 
 // slot of token t (0..TT-1) in the V^T tile: swap bits 2 and 3 within each 16-group
@@ -95,14 +93,21 @@ __device__ __forceinline__ int v_slot(int t) {
     return (t & ~15) | ((t & 4) << 1) | ((t & 8) >> 1) | (t & 3);
 }
 
-// Registers holding one K/V tile in flight from global memory.
+// Registers holding one K/V tile in flight from global memory. K is copied as
+// 16-byte pieces of its rows; V is read as blocks of 4 consecutive tokens x 16 bytes
+// (8 bf16 or 4 fp32 of d) and transposed in registers, so every global load is 16
+// bytes wide. Consecutive lanes take consecutive 4-token groups of one d-block: the
+// transposed stores of a wavefront then fill whole V^T rows (every LDS bank once
+// per pass), while each load instruction still reads 64-byte row segments.
 template <typename T, int D, int TT, int NTHR>
 struct TileRegs {
     typedef TileGeom<T, D, TT> G;
+    static constexpr int VE = 16 / G::ES;                  // elements of d per V block
+    static constexpr int VBLK = (TT / 4) * (D / VE);       // V blocks per tile
     static constexpr int KP = (G::KPIECES + NTHR - 1) / NTHR;
-    static constexpr int VB = (G::VBLOCKS + NTHR - 1) / NTHR;
+    static constexpr int VB = (VBLK + NTHR - 1) / NTHR;
     u32x4 k[KP];
-    uint32_t v[VB][8];
+    u32x4 v[VB][4];
 
     // row_of(t) gives the global row index (element offset / D) of tile token t.
     template <typename RowFn>
@@ -117,15 +122,15 @@ struct TileRegs {
                     reinterpret_cast<const char*>(Kg + (size_t)row_of(t) * D) + 16 * c);
             }
         }
-        constexpr int DW = D / G::EPD;                   // dwords per V row
+        constexpr int TQ = TT / 4;                        // 4-token groups per tile
 #pragma unroll
         for (int i = 0; i < VB; ++i) {
             const int q = tid + i * NTHR;
-            if (q < G::VBLOCKS) {
-                const int dw = q % DW, tg = q / DW;
+            if (q < VBLK) {
+                const int tq = q % TQ, dg = q / TQ;
 #pragma unroll
-                for (int x = 0; x < 8; ++x)
-                    v[i][x] = reinterpret_cast<const uint32_t*>(Vg + (size_t)row_of(8 * tg + x) * D)[dw];
+                for (int x = 0; x < 4; ++x)
+                    v[i][x] = *reinterpret_cast<const u32x4*>(Vg + (size_t)row_of(4 * tq + x) * D + dg * VE);
             }
         }
     }
@@ -141,37 +146,32 @@ struct TileRegs {
             }
         }
         char* vt = lds + G::KBYTES;
-        constexpr int DW = D / G::EPD;
+        constexpr int TQ = TT / 4;
 #pragma unroll
         for (int i = 0; i < VB; ++i) {
             const int q = tid + i * NTHR;
-            if (q < G::VBLOCKS) {
-                const int dw = q % DW, tg = q / DW;
-                const int t0 = 8 * tg;
-                // tokens t0..t0+3 and t0+4..t0+7 land on two runs of 4 consecutive slots
-                const int s0 = v_slot(t0), s1 = v_slot(t0 + 4);
+            if (q < VBLK) {
+                const int tq = q % TQ, dg = q / TQ;
+                const int sl = v_slot(4 * tq);            // 4 tokens -> 4 consecutive slots
                 if (G::ES == 2) {
-                    // dword x holds (d = 2dw, 2dw+1) of token t0+x
+                    // token x holds d = dg*8 + 2j (low half) and + 2j + 1 (high half) in dword j
 #pragma unroll
-                    for (int half = 0; half < 2; ++half) {
-                        const uint32_t* w = &v[i][4 * half];
-                        const int sl = half ? s1 : s0;
+                    for (int j = 0; j < 4; ++j) {
                         u32x2 lo, hi;
-                        lo[0] = (w[0] & 0xFFFFu) | (w[1] << 16);
-                        lo[1] = (w[2] & 0xFFFFu) | (w[3] << 16);
-                        hi[0] = (w[0] >> 16) | (w[1] & 0xFFFF0000u);
-                        hi[1] = (w[2] >> 16) | (w[3] & 0xFFFF0000u);
-                        *reinterpret_cast<u32x2*>(vt + (2 * dw) * G::VROW + sl * 2) = lo;
-                        *reinterpret_cast<u32x2*>(vt + (2 * dw + 1) * G::VROW + sl * 2) = hi;
+                        lo[0] = __builtin_amdgcn_perm(v[i][1][j], v[i][0][j], 0x05040100u);
+                        lo[1] = __builtin_amdgcn_perm(v[i][3][j], v[i][2][j], 0x05040100u);
+                        hi[0] = __builtin_amdgcn_perm(v[i][1][j], v[i][0][j], 0x07060302u);
+                        hi[1] = __builtin_amdgcn_perm(v[i][3][j], v[i][2][j], 0x07060302u);
+                        const int d0 = dg * 8 + 2 * j;
+                        *reinterpret_cast<u32x2*>(vt + d0 * G::VROW + sl * 2) = lo;
+                        *reinterpret_cast<u32x2*>(vt + (d0 + 1) * G::VROW + sl * 2) = hi;
                     }
                 } else {
 #pragma unroll
-                    for (int half = 0; half < 2; ++half) {
-                        const uint32_t* w = &v[i][4 * half];
-                        const int sl = half ? s1 : s0;
+                    for (int j = 0; j < 4; ++j) {
                         u32x4 o;
-                        o[0] = w[0]; o[1] = w[1]; o[2] = w[2]; o[3] = w[3];
-                        *reinterpret_cast<u32x4*>(vt + dw * G::VROW + sl * 4) = o;
+                        o[0] = v[i][0][j]; o[1] = v[i][1][j]; o[2] = v[i][2][j]; o[3] = v[i][3][j];
+                        *reinterpret_cast<u32x4*>(vt + (dg * 4 + j) * G::VROW + sl * 4) = o;
                     }
                 }
             }

@@ -259,21 +259,34 @@ __global__ __launch_bounds__(256, 2) void decode_attn_kernel(DecodeParams p) {
         for (int i = 0; i < 16; ++i) o_acc[db][i] = 0.f;
 
     const int ntiles = (t_end - t_begin + kDecTT - 1) / kDecTT;
-    auto row_of = [&](int tt0, int t) -> int {
-        const int tau = tt0 + t;
-        if (tau >= t_end) return 0;
-        const int e = tau / B;
-        const int row = s_chunk[e - e_first] * B + tau % B;
-        return min(row, pos);
+    // KV row of the first token of each 32-token group of a tile (a group never
+    // straddles two chunks because B % 32 == 0); -1 past the slice end
+    auto group_base = [&](int tau) -> int {
+        if (tau >= t_end) return -1;
+        return s_chunk[tau / B - e_first] * B + tau % B;
+    };
+    int rb0, rb1, rb2, rb3;
+    auto set_bases = [&](int tt0) {
+        rb0 = group_base(tt0); rb1 = group_base(tt0 + 32);
+        rb2 = group_base(tt0 + 64); rb3 = group_base(tt0 + 96);
+    };
+    auto row_of = [&](int t) -> int {
+        const int g4 = t >> 5;
+        const int base = g4 == 0 ? rb0 : g4 == 1 ? rb1 : g4 == 2 ? rb2 : rb3;
+        return base < 0 ? 0 : min(base + (t & 31), pos);
     };
     TileRegs<T, D, kDecTT, 256> regs;
-    regs.load(Kg, Vg, [&](int t) { return row_of(t_begin, t); }, tid);
+    set_bases(t_begin);
+    regs.load(Kg, Vg, row_of, tid);
     for (int k = 0; k < ntiles; ++k) {
         const int tt0 = t_begin + k * kDecTT;
         __syncthreads();
         regs.store(smem, tid);
         __syncthreads();
-        if (k + 1 < ntiles) regs.load(Kg, Vg, [&](int t) { return row_of(tt0 + kDecTT, t); }, tid);
+        if (k + 1 < ntiles) {
+            set_bases(tt0 + kDecTT);
+            regs.load(Kg, Vg, row_of, tid);
+        }
         const int wt0 = tt0 + 32 * wid;            // this wavefront's 32 stream tokens
         if (wt0 >= t_end) continue;
         const int e = wt0 / B;
@@ -360,8 +373,12 @@ __global__ __launch_bounds__(256, 2) void decode_attn_kernel(DecodeParams p) {
 
 // ---------------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(D) void decode_combine_kernel(DecodeParams p) {
-    const int d = threadIdx.x;
+__global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p) {
+    constexpr int NG = 256 / D;                     // thread groups splitting the slices
+    extern __shared__ float s_f[];                  // [max_slices] slice factors
+    __shared__ float red[2][4];
+    __shared__ float s_acc[NG][D];
+    const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
     const int hh = blockIdx.x, bi = blockIdx.y;
     const int g = p.g, r = hh / g, pr = hh % g;
     const size_t grp = (size_t)bi * p.h_kv + r;
@@ -369,20 +386,38 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeParams p) {
     const int nsl = (E * p.B + p.slice_tokens - 1) / p.slice_tokens;
     const float* base = p.partials + (grp * p.max_slices * (size_t)g + pr) * (D + 2);
     const size_t sstride = (size_t)g * (D + 2);
-    float mstar = -INFINITY;
-    for (int s = 0; s < nsl; ++s) mstar = fmaxf(mstar, base[s * sstride]);
+    float mx = -INFINITY;
+    for (int s = tid; s < nsl; s += 256) mx = fmaxf(mx, base[s * sstride]);
+    mx = wave_max(mx);
+    if (lane == 0) red[0][wid] = mx;
+    __syncthreads();
+    const float mstar = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
     const float mu = (mstar == -INFINITY) ? 0.f : mstar;
-    float o = 0.f, l = 0.f;
-    for (int s = 0; s < nsl; ++s) {
-        const float* pp = base + s * sstride;
-        const float f = fast_exp2(pp[0] - mu);
-        o += f * pp[2 + d];
-        l += f * pp[1];
+    float ls = 0.f;
+    for (int s = tid; s < nsl; s += 256) {
+        const float f = fast_exp2(base[s * sstride] - mu);
+        s_f[s] = f;
+        ls += f * base[s * sstride + 1];
     }
-    const float val = o / l;
-    const size_t oi = ((size_t)bi * p.h_q + hh) * D + d;
-    if (p.out_bf16) static_cast<uint16_t*>(p.O)[oi] = f32_to_bf16_bits(val);
-    else static_cast<float*>(p.O)[oi] = val;
+    ls = wave_sum(ls);
+    if (lane == 0) red[1][wid] = ls;
+    __syncthreads();
+    const float l = red[1][0] + red[1][1] + red[1][2] + red[1][3];
+    const int gq = tid / D, d = tid % D;
+    float acc = 0.f;
+#pragma unroll 8
+    for (int s = gq; s < nsl; s += NG) acc += s_f[s] * base[s * sstride + 2 + d];
+    s_acc[gq][d] = acc;
+    __syncthreads();
+    if (gq == 0) {
+        float o = 0.f;
+#pragma unroll
+        for (int k = 0; k < NG; ++k) o += s_acc[k][d];
+        const float val = o / l;
+        const size_t oi = ((size_t)bi * p.h_q + hh) * D + d;
+        if (p.out_bf16) static_cast<uint16_t*>(p.O)[oi] = f32_to_bf16_bits(val);
+        else static_cast<float*>(p.O)[oi] = val;
+    }
 }
 
 // ---------------------------------------------------------------------------------
@@ -423,7 +458,8 @@ static hipError_t launch_decode_t(const DecodeParams& p, const DecodeArgs& a, hi
     if (p.T_route <= 256) launch_dec_route<4>(p, a.b, s);
     else launch_dec_route<16>(p, a.b, s);
     hipLaunchKernelGGL((decode_attn_kernel<T, D>), dim3(p.max_slices, p.h_kv, a.b), dim3(256), lds, s, p);
-    hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(p.h_q, a.b), dim3(D), 0, s, p);
+    hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(p.h_q, a.b), dim3(256),
+                       (size_t)p.max_slices * sizeof(float), s, p);
     return hipGetLastError();
 }
 
