@@ -6,16 +6,19 @@
 //
 // sparse_prior_attn_kernel: one workgroup per (query tile, KV group, batch). The
 // tile is R_t consecutive rows inside one chunk times all g query heads of the
-// group (M = g*R_t pairs, 32 per wavefront); the heads of a group share one routed
-// list, so packing them costs no extra work. The workgroup first merges its rows'
-// lists into the union of routed chunks (ascending) and a per-(row, chunk) bias
-// table in LDS, then walks the union and finally the diagonal chunk:
-//   * K/V tiles of TT tokens are prefetched into registers while the previous tile
-//     is being used, then written to LDS (V transposed for the P·V product);
+// group (M = g*R_t pairs, 32 per wavefront, up to 8 wavefronts); the heads of a
+// group share one routed list, so packing them costs no extra work. The workgroup
+// first merges its rows' lists into the union of routed chunks (ascending) and a
+// per-(row, chunk) bias table in LDS, then walks the union and finally the
+// diagonal chunk in TT-token tiles:
+//   * tiles are copied global->LDS asynchronously (global_load_lds_dwordx4) into a
+//     two-stage ring; the copy of tile k+1 runs while tile k is computed, and one
+//     barrier per tile separates the stages;
 //   * a wavefront skips a chunk none of its rows routes to;
-//   * S^T = K Q^T on MFMA, logits in log2 units with the bias folded in, online
-//     softmax per (row, head) lane, O^T += V^T P^T on MFMA; the division by the
-//     softmax denominator happens once at the end.
+//   * S^T = K Q^T on MFMA (lane = one (row, head) column), logits in log2 units
+//     with the bias folded into the exp2 argument, online softmax per lane with
+//     lazy rescaling, O^T += V^T P^T on MFMA with V read through the transposing
+//     LDS load; the division by the softmax denominator happens once at the end.
 #include "attn_common.h"
 #include "kernels.h"
 
@@ -27,22 +30,25 @@ struct PrefillParams {
     const void* Q; const void* K; const void* V;
     const int32_t* idx; const float* bias; const int32_t* cnt;
     void* O;
-    int out_bf16, h_q, h_kv, n, B, T_c, list_cap, causal, g, log2g, R_t;
+    int out_bf16, h_q, h_kv, n, B, T_c, list_cap, causal, g, log2g, R_t, nw;
     float scale_log2;    // log2(e)/sqrt(d)
 };
 
+constexpr int kWaves = 8;                 // wavefronts per workgroup (256 pairs)
+
 template <typename T, int D, int TT>
-__global__ __launch_bounds__(256, 2) void sparse_prior_attn_kernel(PrefillParams p) {
-    typedef TileGeom<T, D, TT> G;
+__global__ __launch_bounds__(64 * kWaves) void sparse_prior_attn_kernel(PrefillParams p) {
+    typedef SwzTile<T, D, TT> S;
     typedef Mfma<T> MM;
     typedef typename MM::Op Op;
     extern __shared__ __attribute__((aligned(16))) char smem[];
-    char* tile = smem;
-    float* btab = reinterpret_cast<float*>(smem + G::BYTES);
+    char* ring = smem;                                             // 2 stages
+    float* btab = reinterpret_cast<float*>(smem + 2 * S::STAGE);
     int* uflag = reinterpret_cast<int*>(btab + p.R_t * p.T_c);
     int* ulist = uflag + p.T_c;
     int* s_U = ulist + p.T_c;
 
+    constexpr int nthr = 64 * kWaves;
     const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
     const int l32 = lane & 31, hl = lane >> 5;
     const int r = blockIdx.y, bi = blockIdx.z;
@@ -57,15 +63,15 @@ __global__ __launch_bounds__(256, 2) void sparse_prior_attn_kernel(PrefillParams
     const T* Vg = static_cast<const T*>(p.V) + bhkv * (size_t)p.n * D;
 
     // ---- union of the tile rows' routed chunks and the (row, chunk) bias table ----
-    for (int i = tid; i < R_t * nvis; i += 256) btab[(i / nvis) * p.T_c + i % nvis] = -INFINITY;
-    for (int c = tid; c < nvis; c += 256) uflag[c] = 0;
+    for (int i = tid; i < R_t * nvis; i += nthr) btab[(i / nvis) * p.T_c + i % nvis] = -INFINITY;
+    for (int c = tid; c < nvis; c += nthr) uflag[c] = 0;
     __syncthreads();
     for (int j = 0; j < R_t; ++j) {
         const int row = row0 + j;
         if (row >= p.n) break;
         const size_t rb = bhkv * p.n + row;
         const int cn = p.cnt[rb];
-        for (int e = tid; e < cn; e += 256) {
+        for (int e = tid; e < cn; e += nthr) {
             const int c = p.idx[rb * p.list_cap + e];
             if (c >= 0 && c < nvis) {
                 btab[j * p.T_c + c] = p.bias[rb * p.list_cap + e];
@@ -89,9 +95,8 @@ __global__ __launch_bounds__(256, 2) void sparse_prior_attn_kernel(PrefillParams
     const int U = *s_U;
 
     // ---- this lane's (row, head) pair ----
-    const int M = g * R_t;
-    const bool wave_active = wid * 32 < M;
     const int pair = wid * 32 + l32;
+    const bool wave_active = wid * 32 < g * R_t;
     const int j = pair >> lg;
     const int hh = r * g + (pair & (g - 1));
     const int my_row = row0 + j;
@@ -125,98 +130,112 @@ __global__ __launch_bounds__(256, 2) void sparse_prior_attn_kernel(PrefillParams
     const int nrouted = U * SPC;
     const int nsteps = nrouted + ndiag;
     const int nmax = p.n - 1;
-
-    TileRegs<T, D, TT, 256> regs;
     auto tile_base = [&](int k) -> int {
         return k < nrouted ? ulist[k / SPC] * p.B + (k % SPC) * TT : diag_base + (k - nrouted) * TT;
     };
-    if (nsteps > 0) {
-        const int tb = tile_base(0);
-        regs.load(Kg, Vg, [&](int t) { return min(tb + t, nmax); }, tid);
-    }
+    TileCopier<T, D, TT, kWaves> copier;
+    copier.init(wid, lane);
+    auto issue = [&](int k) { copier.issue(ring + (k & 1) * S::STAGE, Kg, Vg, tile_base(k), nmax, wid); };
+
+    if (nsteps > 0) issue(0);
+    wait_tile_copies();
+    __syncthreads();
     for (int k = 0; k < nsteps; ++k) {
-        __syncthreads();
-        regs.store(tile, tid);
-        __syncthreads();
-        if (k + 1 < nsteps) {
-            const int tb1 = tile_base(k + 1);
-            regs.load(Kg, Vg, [&](int t) { return min(tb1 + t, nmax); }, tid);
-        }
-        if (!wave_active) continue;
+        if (k + 1 < nsteps) issue(k + 1);
+        const char* ktile = ring + (k & 1) * S::STAGE;
+        const char* vtile = ktile + S::BYTES;
         const bool routed = k < nrouted;
-        const int tb = tile_base(k);
         float bias2 = 0.f;
-        if (routed) {
+        bool run = wave_active;
+        if (routed && run) {
             const int c = ulist[k / SPC];
             bias2 = pair_ok ? btab[j * p.T_c + c] * kLog2e : -INFINITY;
-            if (ballot(bias2 > -INFINITY) == 0) continue;   // no row of this wave routes c
+            run = ballot(bias2 > -INFINITY) != 0;          // some row of this wave routes c
         }
-        // S^T = K Q^T: accumulator column = this lane's pair, rows = tokens
-        f32x16 sacc[TT / 32];
+        if (run) {
+            const int tb = tile_base(k);
+            // S^T = K Q^T: accumulator column = this lane's pair, rows = tokens
+            f32x16 sacc[TT / 32];
 #pragma unroll
-        for (int blk = 0; blk < TT / 32; ++blk) {
+            for (int blk = 0; blk < TT / 32; ++blk)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) sacc[blk][i] = 0.f;
-            const T* krow = reinterpret_cast<const T*>(tile + (32 * blk + l32) * G::KROW) + 8 * hl;
+                for (int i = 0; i < 16; ++i) sacc[blk][i] = 0.f;
+            constexpr int NB = sizeof(T) == 2 ? 4 : 2;
 #pragma unroll
-            for (int s = 0; s < D / 16; ++s) sacc[blk] = MM::mma(MM::load(krow + 16 * s), qf[s], sacc[blk]);
-        }
-        // mask the diagonal tile on the raw scores, then the tile maximum; the scale
-        // c1 = log2(e)/sqrt(d) > 0 commutes with the maximum
-        if (!routed) {
+            for (int s0 = 0; s0 < D / 16; s0 += NB) {
+                Op ka[TT / 32][NB];
+#pragma unroll
+                for (int blk = 0; blk < TT / 32; ++blk)
+#pragma unroll
+                    for (int s = 0; s < NB; ++s)
+                        ka[blk][s] = load_k_op<T, D, TT>(ktile, 32 * blk + l32, 16 * (s0 + s) + 8 * hl);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int s = 0; s < NB; ++s)
+#pragma unroll
+                    for (int blk = 0; blk < TT / 32; ++blk) sacc[blk] = MM::mma(ka[blk][s], qf[s0 + s], sacc[blk]);
+            }
+            // mask the diagonal tile on the raw scores (selects, no branches)
+            if (!routed) {
+                const int lim = p.causal ? my_row : p.n - 1;
+                const int tk0 = tb + 4 * hl;
+#pragma unroll
+                for (int blk = 0; blk < TT / 32; ++blk)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int tk = tk0 + 32 * blk + 8 * (i >> 2) + (i & 3);
+                        sacc[blk][i] = tk > lim ? -INFINITY : sacc[blk][i];
+                    }
+            }
+            // tile maximum; c1 = log2(e)/sqrt(d) > 0 commutes with the maximum
+            float mx = -INFINITY;
+#pragma unroll
+            for (int blk = 0; blk < TT / 32; ++blk)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[blk][i]);
+            mx = fmaxf(mx, shfl_xor(mx, 32));
+            const float tmax = fmaf(mx, p.scale_log2, bias2);     // -inf when nothing is visible
+            // lazy rescaling: the reference maximum only moves when the tile maximum
+            // exceeds it by more than 8 (probabilities stay <= 2^8 in between)
+            const bool grow = tmax > m_run + 8.f;
+            float alpha = 1.f;
+            if (grow) {
+                alpha = fast_exp2(m_run - tmax);
+                m_run = tmax;
+            }
+            const float off = bias2 - ((m_run == -INFINITY) ? 0.f : m_run);
+            float ps = 0.f;
 #pragma unroll
             for (int blk = 0; blk < TT / 32; ++blk)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    const int tk = tb + 32 * blk + 8 * (i >> 2) + 4 * hl + (i & 3);
-                    if (p.causal ? (tk > my_row) : (tk >= p.n)) sacc[blk][i] = -INFINITY;
+                    sacc[blk][i] = fast_exp2(fmaf(sacc[blk][i], p.scale_log2, off));
                 }
-        }
-        float mx = -INFINITY;
+            if (ballot(grow) != 0) {
 #pragma unroll
-        for (int blk = 0; blk < TT / 32; ++blk)
+                for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[blk][i]);
-        mx = fmaxf(mx, shfl_xor(mx, 32));
-        const float tmax = fmaf(mx, p.scale_log2, bias2);     // -inf when nothing is visible
-        // lazy rescaling: the reference maximum only moves when the tile maximum exceeds
-        // it by more than 8 (probabilities stay <= 2^8 in between)
-        const bool grow = tmax > m_run + 8.f;
-        float alpha = 1.f;
-        if (grow) {
-            alpha = fast_exp2(m_run - tmax);
-            m_run = tmax;
-        }
-        const float off = bias2 - ((m_run == -INFINITY) ? 0.f : m_run);
-        float ps = 0.f;
-#pragma unroll
-        for (int blk = 0; blk < TT / 32; ++blk)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float pv = fast_exp2(fmaf(sacc[blk][i], p.scale_log2, off));
-                sacc[blk][i] = pv;
-                ps += pv;
+                    for (int i = 0; i < 16; ++i) o_acc[db][i] *= alpha;
             }
-        l_run = fmaf(l_run, alpha, ps);
-        if (ballot(grow) != 0) {
+            // O^T += V^T P^T
 #pragma unroll
-            for (int db = 0; db < D / 32; ++db)
+            for (int s = 0; s < TT / 16; ++s) {
+                float pv8[8];
 #pragma unroll
-                for (int i = 0; i < 16; ++i) o_acc[db][i] *= alpha;
-        }
-        // O^T += V^T P^T
+                for (int e = 0; e < 8; ++e) pv8[e] = sacc[s >> 1][8 * (s & 1) + e];
+                const Op pb = MM::pack(pv8);
+                ps = MM::sum(pb, pv8, ps);        // the denominator sums the P fed to the MFMA
+                Op va[D / 32];
 #pragma unroll
-        for (int s = 0; s < TT / 16; ++s) {
-            float pv8[8];
+                for (int db = 0; db < D / 32; ++db) va[db] = load_vt_op<T, D, TT>(vtile, s, db, lane);
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) pv8[e] = sacc[s >> 1][8 * (s & 1) + e];
-            const Op pb = MM::pack(pv8);
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db) {
-                const T* vrow = reinterpret_cast<const T*>(tile + G::KBYTES + (32 * db + l32) * G::VROW) + 16 * s + 8 * hl;
-                o_acc[db] = MM::mma(MM::load(vrow), pb, o_acc[db]);
+                for (int db = 0; db < D / 32; ++db) o_acc[db] = MM::mma(va[db], pb, o_acc[db]);
             }
+            l_run = fmaf(l_run, alpha, ps);
         }
+        wait_tile_copies();
+        __syncthreads();
     }
 
     const float l_tot = l_run + shfl_xor(l_run, 32);
@@ -245,29 +264,24 @@ __global__ __launch_bounds__(256, 2) void sparse_prior_attn_kernel(PrefillParams
     }
 }
 
-static size_t prefill_lds(int R_t, int T_c, int tile_bytes) {
-    return (size_t)tile_bytes + (size_t)R_t * T_c * 4 + (size_t)2 * T_c * 4 + 16;
-}
-
-static int tile_bytes_of(int d, bool bf16, int TT) {
-    if (bf16) return d == 64 ? TileGeom<uint16_t, 64, 64>::BYTES * (TT == 64) + TileGeom<uint16_t, 64, 32>::BYTES * (TT == 32)
-                             : TileGeom<uint16_t, 128, 64>::BYTES * (TT == 64) + TileGeom<uint16_t, 128, 32>::BYTES * (TT == 32);
-    return d == 64 ? TileGeom<float, 64, 64>::BYTES * (TT == 64) + TileGeom<float, 64, 32>::BYTES * (TT == 32)
-                   : TileGeom<float, 128, 64>::BYTES * (TT == 64) + TileGeom<float, 128, 32>::BYTES * (TT == 32);
-}
-
 static constexpr size_t kMaxLds = 160 * 1024;
+
+static int stage_bytes(int d, bool bf16, int TT) { return 2 * TT * d * (bf16 ? 2 : 4); }
+
+static size_t prefill_lds(int R_t, int T_c, int stage) {
+    return (size_t)2 * stage + (size_t)R_t * T_c * 4 + (size_t)2 * T_c * 4 + 16;
+}
 
 void prefill_tiling(int g, int B, int T_c, int d, bool bf16, int* rows, size_t* lds_bytes) {
     *rows = 0;
     *lds_bytes = 0;
     if (B % 32 != 0 || g < 1 || g > 16) return;
     const int TT = (B % 64 == 0) ? 64 : 32;
-    const int tb = tile_bytes_of(d, bf16, TT);
-    for (int m = 128; m >= 32; m >>= 1) {
+    const int st = stage_bytes(d, bf16, TT);
+    for (int m = 32 * kWaves; m >= 32; m >>= 1) {
         const int R_t = m / g;
         if (R_t < 1 || B % R_t != 0) continue;
-        const size_t lds = prefill_lds(R_t, T_c, tb);
+        const size_t lds = prefill_lds(R_t, T_c, st);
         if (lds <= kMaxLds) {
             *rows = R_t;
             *lds_bytes = lds;
@@ -280,11 +294,11 @@ template <typename T, int D, int TT>
 static hipError_t launch_prefill_t(const PrefillParams& p, int b, size_t lds, hipStream_t s) {
     static bool configured = false;
     if (!configured) {
-        hipFuncSetAttribute(reinterpret_cast<const void*>(&sparse_prior_attn_kernel<T, D, TT>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&sparse_prior_attn_kernel<T, D, TT>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
         configured = true;
     }
-    dim3 grid((p.n + p.R_t - 1) / p.R_t, p.h_kv, b), block(256);
+    dim3 grid((p.n + p.R_t - 1) / p.R_t, p.h_kv, b), block(64 * kWaves);
     hipLaunchKernelGGL((sparse_prior_attn_kernel<T, D, TT>), grid, block, lds, s, p);
     return hipGetLastError();
 }
@@ -301,6 +315,7 @@ hipError_t launch_attend_prefill(const PrefillArgs& a, hipStream_t s) {
     size_t lds = 0;
     prefill_tiling(p.g, a.B, p.T_c, a.d, a.in_bf16, &p.R_t, &lds);
     if (p.R_t == 0) return hipErrorInvalidValue;
+    p.nw = (p.g * p.R_t + 31) / 32;
     if (a.n == 0) return hipSuccess;
     const bool t64 = (a.B % 64 == 0);
     if (a.in_bf16) {

@@ -43,9 +43,23 @@ template <> struct Mfma<uint16_t> {       // bf16 inputs
         for (int e = 0; e < 8; ++e) o[e] = (__bf16)0.f;
         return o;
     }
+    // acc + sum of the 8 (already rounded) values of a packed operand
+    __device__ __forceinline__ static float sum(const Op& o, const float*, float acc) {
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+            const bf16x2 pr = {o[e], o[e + 1]};
+            acc = __builtin_amdgcn_fdot2_f32_bf16(pr, one, acc, false);
+        }
+        return acc;
+    }
 };
 
 struct F32x8 { float v[8]; };
+
+template <typename Op>
+__device__ __forceinline__ Op pack_f32x8(Op r, const f32x4& a, const f32x4& b);
 
 template <> struct Mfma<float> {          // fp32 inputs
     typedef F32x8 Op;
@@ -74,7 +88,174 @@ template <> struct Mfma<float> {          // fp32 inputs
         for (int e = 0; e < 8; ++e) o.v[e] = 0.f;
         return o;
     }
+    __device__ __forceinline__ static float sum(const Op&, const float* v, float acc) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc += v[e];
+        return acc;
+    }
 };
+
+template <>
+__device__ __forceinline__ F32x8 pack_f32x8<F32x8>(F32x8 r, const f32x4& a, const f32x4& b) {
+    r.v[0] = a[0]; r.v[1] = a[1]; r.v[2] = a[2]; r.v[3] = a[3];
+    r.v[4] = b[0]; r.v[5] = b[1]; r.v[6] = b[2]; r.v[7] = b[3];
+    return r;
+}
+template <>
+__device__ __forceinline__ bf16x8 pack_f32x8<bf16x8>(bf16x8 r, const f32x4&, const f32x4&) { return r; }
+
+// S^T blocks (NBLK x 32 tokens x 32 pairs) = K rows [32 tokens][D] (LDS, row
+// stride KROW bytes, block stride 32 rows) times the lane's q fragments. The K
+// fragments of a group of k16 steps are read from LDS before the MFMAs start, and
+// the NBLK independent accumulation chains are interleaved so that consecutive
+// MFMAs never depend on each other.
+template <typename T, int D, int NBLK, int KROW>
+__device__ __forceinline__ void score_blocks(f32x16 (&acc)[NBLK], const char* krow_lds,
+                                             const typename Mfma<T>::Op* qf) {
+    typedef Mfma<T> MM;
+    constexpr int NB = sizeof(T) == 2 ? (NBLK == 1 ? D / 16 : 4) : 2;   // k16 steps per group
+#pragma unroll
+    for (int b = 0; b < NBLK; ++b)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[b][i] = 0.f;
+#pragma unroll
+    for (int s0 = 0; s0 < D / 16; s0 += NB) {
+        typename MM::Op ka[NBLK][NB];
+#pragma unroll
+        for (int b = 0; b < NBLK; ++b)
+#pragma unroll
+            for (int s = 0; s < NB; ++s)
+                ka[b][s] = MM::load(reinterpret_cast<const T*>(krow_lds + 32 * b * KROW) + 16 * (s0 + s));
+        __builtin_amdgcn_sched_barrier(0);     // keep the reads ahead of the MFMAs
+#pragma unroll
+        for (int s = 0; s < NB; ++s)
+#pragma unroll
+            for (int b = 0; b < NBLK; ++b) acc[b] = MM::mma(ka[b][s], qf[s0 + s], acc[b]);
+    }
+}
+
+// ---------------------------------------------------------------------------------
+// Swizzled tiles filled by asynchronous global->LDS copies (global_load_lds_dwordx4:
+// a wavefront instruction writes 64 x 16 bytes contiguously, lane l at +16l).
+// Rows are unpadded (D*ES bytes) and split into PPR 16-byte pieces; piece c of row t
+// is stored at piece slot c ^ swz(t):
+//   K:  swz(t) = t mod PPR            (16 consecutive rows read one column: all banks)
+//   V:  swz(t) = 4 (t mod 4) mod PPR  (bf16; the transposing reads of a k16 step
+//                                      touch 4 rows x 4 pieces: all distinct)
+// ---------------------------------------------------------------------------------
+template <typename T, int D, int TT>
+struct SwzTile {
+    static constexpr int ES = sizeof(T);
+    static constexpr int ROWB = D * ES;              // bytes per row
+    static constexpr int PPR = ROWB / 16;            // 16-byte pieces per row
+    static constexpr int BYTES = TT * ROWB;          // one K (or V) tile
+    static constexpr int STAGE = 2 * BYTES;          // K tile then V tile
+    static constexpr int INSTS = TT * PPR / 64;      // wavefront copies per K (or V) tile
+    __device__ __forceinline__ static int kslot(int t, int c) { return c ^ (t & (PPR - 1)); }
+    __device__ __forceinline__ static int vslot(int t, int c) {
+        return ES == 2 ? (c ^ ((4 * (t & 3)) & (PPR - 1))) : c;
+    }
+};
+
+// The copies of one K/V tile, split over NW wavefronts: wavefront `wid` issues copy
+// instructions wid, wid + NW, ... (CPW of them). Each lane's tile row and source
+// element offset per copy depend only on (wid, lane), so they are computed once.
+template <typename T, int D, int TT, int NW>
+struct TileCopier {
+    typedef SwzTile<T, D, TT> S;
+    static constexpr int CPW = 2 * S::INSTS / NW;   // copies per wavefront per tile
+    static_assert(CPW * NW == 2 * S::INSTS, "copies must divide evenly over the wavefronts");
+    int row[CPW];      // tile row (token) of this lane's piece
+    int off[CPW];      // element offset of the piece inside its row
+    int dst[CPW];      // byte offset of the wavefront's 1 KiB block inside a stage
+
+    __device__ __forceinline__ void init(int wid, int lane) {
+#pragma unroll
+        for (int i = 0; i < CPW; ++i) {
+            const int j = wid + i * NW;
+            const bool isv = j >= S::INSTS;
+            const int jj = isv ? j - S::INSTS : j;
+            const int slot = jj * 64 + lane;
+            const int t = slot / S::PPR, cs = slot % S::PPR;
+            const int c = isv ? S::vslot(t, cs) : S::kslot(t, cs);   // the swizzle is an involution
+            row[i] = t;
+            off[i] = c * (16 / S::ES);
+            dst[i] = (isv ? S::BYTES : 0) + jj * 1024;
+        }
+    }
+    // Copy the tile whose token t lives in row min(tb + t, nmax) of K and V.
+    __device__ __forceinline__ void issue(char* stage, const T* Kg, const T* Vg, int tb, int nmax,
+                                          int wid) const {
+#pragma unroll
+        for (int i = 0; i < CPW; ++i) {
+            const int j = wid + i * NW;
+            const T* base = (j >= S::INSTS) ? Vg : Kg;            // wavefront-uniform
+            const T* src = base + (size_t)min(tb + row[i], nmax) * D + off[i];
+            __builtin_amdgcn_global_load_lds(src, stage + dst[i], 16, 0, 0);
+        }
+    }
+};
+
+__device__ __forceinline__ void wait_tile_copies() {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// 8 consecutive elements (one k16-step operand) of row t starting at element e0 of
+// a K tile stored with the K swizzle.
+template <typename T, int D, int TT>
+__device__ __forceinline__ typename Mfma<T>::Op load_k_op(const char* ktile, int t, int e0) {
+    typedef SwzTile<T, D, TT> S;
+    typedef Mfma<T> MM;
+    constexpr int EPP = 16 / S::ES;                  // elements per piece
+    const char* row = ktile + t * S::ROWB;
+    if constexpr (S::ES == 2) {
+        return MM::load(reinterpret_cast<const T*>(row + S::kslot(t, e0 / EPP) * 16));
+    } else {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(row + S::kslot(t, e0 / EPP) * 16);
+        const f32x4 b = *reinterpret_cast<const f32x4*>(row + S::kslot(t, e0 / EPP + 1) * 16);
+        return pack_f32x8(MM::zero(), a, b);
+    }
+}
+
+// A operand of O^T += V^T P^T for k16 step s and d-block db (rows d = 32db + lane%32,
+// k-slot (h = lane/32, e) = token 16s + 8(e/4) + 4h + e%4) from a V tile stored
+// row-major with the V swizzle.
+//  * bf16: two transposing reads. In a 16-lane group, lane 4k+c addresses the 4
+//    elements of row t_k at d0 + 4c and lane i receives element d0 + i of rows
+//    t_0..t_3; the two reads cover e = 0..3 and e = 4..7.
+//  * fp32: no transpose is needed for one element per MFMA: 8 scalar reads.
+template <typename T, int D, int TT>
+__device__ __forceinline__ typename Mfma<T>::Op load_vt_op(const char* vtile, int s, int db, int lane) {
+    typedef SwzTile<T, D, TT> S;
+    if constexpr (S::ES == 2) {
+        const int G = lane >> 4, i = lane & 15, k = i >> 2, c = i & 3;
+        const int h = G >> 1, dh = G & 1;
+        const int cp = 4 * db + 2 * dh + (c >> 1);
+        const int boff = (c & 1) * 8;
+        s16x4 r[2];
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr) {
+            const int t = 16 * s + 8 * rr + 4 * h + k;
+            const char* a = vtile + t * S::ROWB + S::vslot(t, cp) * 16 + boff;
+            r[rr] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4*)(a));
+        }
+        typename Mfma<T>::Op o;
+        o = __builtin_bit_cast(bf16x8, __builtin_shufflevector(r[0], r[1], 0, 1, 2, 3, 4, 5, 6, 7));
+        return o;
+    } else {
+        const int d = 32 * db + (lane & 31), h = lane >> 5;
+        typename Mfma<T>::Op o;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int t = 16 * s + 8 * (e >> 2) + 4 * h + (e & 3);
+            o.v[e] = *reinterpret_cast<const float*>(vtile + t * S::ROWB + S::vslot(t, d >> 2) * 16 + (d & 3) * 4);
+        }
+        return o;
+    }
+}
 
 // LDS geometry of one token tile of TT tokens.
 template <typename T, int D, int TT>
@@ -116,7 +297,7 @@ struct TileRegs {
 #pragma unroll
         for (int i = 0; i < KP; ++i) {
             const int q = tid + i * NTHR;
-            if (q < G::KPIECES) {
+            if (G::KPIECES % NTHR == 0 || q < G::KPIECES) {
                 const int t = q / PPR, c = q % PPR;
                 k[i] = *reinterpret_cast<const u32x4*>(
                     reinterpret_cast<const char*>(Kg + (size_t)row_of(t) * D) + 16 * c);
@@ -126,7 +307,7 @@ struct TileRegs {
 #pragma unroll
         for (int i = 0; i < VB; ++i) {
             const int q = tid + i * NTHR;
-            if (q < VBLK) {
+            if (VBLK % NTHR == 0 || q < VBLK) {
                 const int tq = q % TQ, dg = q / TQ;
 #pragma unroll
                 for (int x = 0; x < 4; ++x)
@@ -140,7 +321,7 @@ struct TileRegs {
 #pragma unroll
         for (int i = 0; i < KP; ++i) {
             const int q = tid + i * NTHR;
-            if (q < G::KPIECES) {
+            if (G::KPIECES % NTHR == 0 || q < G::KPIECES) {
                 const int t = q / PPR, c = q % PPR;
                 *reinterpret_cast<u32x4*>(lds + t * G::KROW + 16 * c) = k[i];
             }
@@ -150,7 +331,7 @@ struct TileRegs {
 #pragma unroll
         for (int i = 0; i < VB; ++i) {
             const int q = tid + i * NTHR;
-            if (q < VBLK) {
+            if (VBLK % NTHR == 0 || q < VBLK) {
                 const int tq = q % TQ, dg = q / TQ;
                 const int sl = v_slot(4 * tq);            // 4 tokens -> 4 consecutive slots
                 if (G::ES == 2) {

@@ -293,12 +293,9 @@ __global__ __launch_bounds__(256, 2) void decode_attn_kernel(DecodeParams p) {
         const bool diag = e >= cnt;
         const float bias2 = s_bias[e - e_first];
         const int kv0 = s_chunk[e - e_first] * B + wt0 % B;   // KV position of token 0
-        f32x16 sacc;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
-        const T* krow = reinterpret_cast<const T*>(smem + (32 * wid + l32) * G::KROW) + 8 * hl;
-#pragma unroll
-        for (int s = 0; s < D / 16; ++s) sacc = MM::mma(MM::load(krow + 16 * s), qf[s], sacc);
+        f32x16 sacc1[1];
+        score_blocks<T, D, 1, G::KROW>(sacc1, smem + (32 * wid + l32) * G::KROW + 8 * hl * G::ES, qf);
+        f32x16 sacc = sacc1[0];
         float mx = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -331,11 +328,13 @@ __global__ __launch_bounds__(256, 2) void decode_attn_kernel(DecodeParams p) {
 #pragma unroll
             for (int e8 = 0; e8 < 8; ++e8) pv8[e8] = sacc[8 * s + e8];
             const Op pb = MM::pack(pv8);
+            Op va[D / 32];
 #pragma unroll
-            for (int db = 0; db < D / 32; ++db) {
-                const T* vrow = reinterpret_cast<const T*>(smem + G::KBYTES + (32 * db + l32) * G::VROW) + 32 * wid + 16 * s + 8 * hl;
-                o_acc[db] = MM::mma(MM::load(vrow), pb, o_acc[db]);
-            }
+            for (int db = 0; db < D / 32; ++db)
+                va[db] = MM::load(reinterpret_cast<const T*>(smem + G::KBYTES + (32 * db + l32) * G::VROW) + 32 * wid + 16 * s + 8 * hl);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) o_acc[db] = MM::mma(va[db], pb, o_acc[db]);
         }
     }
     // merge the 4 wavefronts' partial softmax states in LDS
