@@ -111,20 +111,42 @@ __device__ __forceinline__ void load4(const uint16_t* p, float* o) {
     o[2] = __uint_as_float(v[1] << 16); o[3] = __uint_as_float(v[1] & 0xFFFF0000u);
 }
 
+// Shared summaries of one stage (32 chunks) for bf16 queries: per chunk three rows
+// (hi, mid, lo) of D bf16, i.e. 3*D/8 16-byte pieces; piece c of split h sits at
+// h*(D/8) + (c ^ (chunk mod D/8)) so that the 16 lanes reading 16 consecutive chunks
+// at one column hit distinct banks.
+template <int D>
+struct KSplitStage {
+    static constexpr int CH = 32;                     // chunks per stage
+    static constexpr int PPS = D / 8;                 // pieces per split row
+    static constexpr int ROWB = 3 * D * 2;            // bytes per chunk
+    static constexpr int BYTES = CH * ROWB;
+    static constexpr int PIECES = CH * PPS;           // fp32 groups of 8 to split per stage
+    __device__ __forceinline__ static int off(int c, int h, int piece) {
+        return c * ROWB + (h * PPS + (piece ^ (c & (PPS - 1)))) * 16;
+    }
+};
+
 template <typename T, int D, int NT, int PM>
-__global__ __launch_bounds__(256) void entmax_route_kernel(RouteParams p) {
+__global__ __launch_bounds__(512) void entmax_route_kernel(RouteParams p) {
     constexpr int WS = NT * 16;                       // LDS floats per row of weights
-    extern __shared__ float wl_all[];
+    typedef KSplitStage<D> KS;
+    typedef __bf16 b8 __attribute__((ext_vector_type(8)));
+    extern __shared__ __attribute__((aligned(16))) char rsm[];
+    const int W = blockDim.x >> 6;
     const int wid = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int n16 = lane & 15, kg = lane >> 4;
     const int g = p.g, lg = p.log2g;
     const int R = 16 >> lg;                           // rows per wave
     const int r = blockIdx.y, bi = blockIdx.z;
-    const int row0 = (blockIdx.x * (blockDim.x >> 6) + wid) * R;
-    if (row0 >= p.n) return;                          // wave-uniform
-    float* wl = wl_all + wid * R * WS;
-    const int nvis = p.causal ? min(row0 / p.B, p.T_c) : p.T_c;
+    // all rows of the workgroup lie in one chunk (W*R divides B): one visible range
+    const int wg_row0 = blockIdx.x * W * R;
+    const int row0 = wg_row0 + wid * R;
+    const bool wave_live = row0 < p.n;
+    char* kstage = rsm;                                              // 2 stages (bf16 path)
+    float* wl = reinterpret_cast<float*>(rsm + (sizeof(T) == 2 ? 2 * KS::BYTES : 0)) + wid * R * WS;
+    const int nvis = p.causal ? min(wg_row0 / p.B, p.T_c) : p.T_c;
     const int my_row = row0 + (n16 >> lg);
     const int my_head = r * g + (n16 & (g - 1));
     const bool row_ok = my_row < p.n;
@@ -132,44 +154,159 @@ __global__ __launch_bounds__(256) void entmax_route_kernel(RouteParams p) {
 
     float sv[NT][4];
     if (nvis > 0) {
-        // q fragment: the MFMA k-slot kg of step (s, j) carries dimension 16s + 4kg + j,
-        // for both operands, so every dimension is summed exactly once.
-        float qv[D / 4];
-        {
-            const T* qrow = static_cast<const T*>(p.Q) +
-                (((size_t)bi * p.h_q + my_head) * p.n + (row_ok ? my_row : 0)) * D + 4 * kg;
-#pragma unroll
-            for (int s = 0; s < D / 16; ++s) load4(qrow + 16 * s, &qv[4 * s]);
-            if (!row_ok) {
-#pragma unroll
-                for (int e = 0; e < D / 4; ++e) qv[e] = 0.f;
-            }
-        }
-        const float* kb = p.kbar + ((size_t)bi * p.h_kv + r) * (size_t)p.kbar_cap * D + 4 * kg;
         float smax = -INFINITY;
+        if constexpr (sizeof(T) == 2) {
+            // bf16 queries are exact in bf16; k̄ = hi + mid + lo (three bf16 terms, exact up
+            // to the last bits of fp32), so every product is exact in fp32 and three bf16
+            // MFMAs 16x16x32 per k step reproduce the fp32 dot product; the three partial
+            // sums are kept apart and added once. k-slot (kg, e) of step s carries
+            // dimension 32s + 8kg + e for both operands.
+            b8 qb[D / 32];
+            {
+                const T* qrow = static_cast<const T*>(p.Q) +
+                    (((size_t)bi * p.h_q + my_head) * p.n + (row_ok ? my_row : 0)) * D + 8 * kg;
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            if (t < nt) {
-                const int c = min(t * 16 + n16, nvis - 1);   // A row = chunk
-                const float* krow = kb + (size_t)c * D;
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int s = 0; s < D / 16; ++s) {
-                    float a[4];
-                    load4(krow + 16 * s, a);
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], qv[4 * s + j], acc, 0, 0, 0);
+                for (int s = 0; s < D / 32; ++s) {
+                    qb[s] = *reinterpret_cast<const b8*>(qrow + 32 * s);
+                    if (!row_ok) qb[s] = b8{};
                 }
+            }
+            // the workgroup loads each stage of 32 summaries once (fp32, coalesced),
+            // splits it in registers and stores it to LDS; the next stage is prefetched
+            const float* kb = p.kbar + ((size_t)bi * p.h_kv + r) * (size_t)p.kbar_cap * D;
+            const int nst = (nvis + KS::CH - 1) / KS::CH;
+            // one piece = 8 consecutive fp32 of one chunk; a workgroup of 8 waves covers a
+            // stage in one round (prefetched), smaller workgroups take extra rounds
+            constexpr int PPT = (KS::PIECES + 511) / 512;
+            f32x4 pre[PPT][2];
+            auto piece_src = [&](int st, int q) {
+                const int c = min(st * KS::CH + q / KS::PPS, nvis - 1);
+                return reinterpret_cast<const f32x4*>(kb + (size_t)c * D + (q % KS::PPS) * 8);
+            };
+            auto split_store = [&](char* dst, int q, f32x4 lo4, f32x4 hi4) {
+                const int c = q / KS::PPS, pc = q % KS::PPS;
+                b8 hv, mv, lv;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int ch = t * 16 + 4 * kg + i;
-                    sv[t][i] = (ch < nvis) ? acc[i] : -INFINITY;
-                    smax = fmaxf(smax, sv[t][i]);
+                for (int e = 0; e < 8; ++e) {
+                    const float x = e < 4 ? lo4[e] : hi4[e - 4];
+                    const __bf16 h = (__bf16)x;
+                    const float r1 = x - (float)h;
+                    const __bf16 m = (__bf16)r1;
+                    hv[e] = h; mv[e] = m; lv[e] = (__bf16)(r1 - (float)m);
                 }
-            } else {
+                *reinterpret_cast<b8*>(dst + KS::off(c, 0, pc)) = hv;
+                *reinterpret_cast<b8*>(dst + KS::off(c, 1, pc)) = mv;
+                *reinterpret_cast<b8*>(dst + KS::off(c, 2, pc)) = lv;
+            };
+            auto load_stage = [&](int st) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) sv[t][i] = -INFINITY;
+                for (int i = 0; i < PPT; ++i) {
+                    const int q = threadIdx.x + i * blockDim.x;
+                    if (q < KS::PIECES) {
+                        const f32x4* src = piece_src(st, q);
+                        pre[i][0] = src[0];
+                        pre[i][1] = src[1];
+                    }
+                }
+            };
+            auto store_stage = [&](int st) {
+                char* dst = kstage + (st & 1) * KS::BYTES;
+#pragma unroll
+                for (int i = 0; i < PPT; ++i) {
+                    const int q = threadIdx.x + i * blockDim.x;
+                    if (q < KS::PIECES) split_store(dst, q, pre[i][0], pre[i][1]);
+                }
+                for (int q = threadIdx.x + PPT * blockDim.x; q < KS::PIECES; q += blockDim.x) {
+                    const f32x4* src = piece_src(st, q);
+                    split_store(dst, q, src[0], src[1]);
+                }
+            };
+            load_stage(0);
+#pragma unroll
+            for (int st = 0; st < (NT + 1) / 2; ++st) {
+                if (st < nst) {
+                    store_stage(st);
+                    __syncthreads();
+                    if (st + 1 < nst) load_stage(st + 1);
+                    const char* stg = kstage + (st & 1) * KS::BYTES;
+#pragma unroll
+                    for (int tt = 0; tt < 2; ++tt) {
+                        const int t = 2 * st + tt;
+                        if (t < NT) {
+                            if (t < nt) {
+                                const int cl = 16 * tt + n16;            // chunk inside the stage
+                                f32x4 acc[3];
+#pragma unroll
+                                for (int h = 0; h < 3; ++h) {
+                                    acc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                                    for (int s = 0; s < D / 32; ++s) {
+                                        const b8 a = *reinterpret_cast<const b8*>(stg + KS::off(cl, h, 4 * s + kg));
+                                        acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[s], acc[h], 0, 0, 0);
+                                    }
+                                }
+#pragma unroll
+                                for (int i = 0; i < 4; ++i) {
+                                    const int ch = t * 16 + 4 * kg + i;
+                                    const float v = acc[0][i] + (acc[1][i] + acc[2][i]);
+                                    sv[t][i] = (ch < nvis) ? v : -INFINITY;
+                                    smax = fmaxf(smax, sv[t][i]);
+                                }
+                            } else {
+#pragma unroll
+                                for (int i = 0; i < 4; ++i) sv[t][i] = -INFINITY;
+                            }
+                        }
+                    }
+                    // no trailing barrier: stage st+1 fills the other buffer, and the barrier
+                    // of stage st+1 orders this stage's reads before stage st+2 refills it
+                } else {
+#pragma unroll
+                    for (int tt = 0; tt < 2; ++tt)
+                        if (2 * st + tt < NT)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) sv[2 * st + tt][i] = -INFINITY;
+                }
+            }
+        } else {
+            // fp32 queries: the MFMA k-slot kg of step (s, j) carries dimension 16s + 4kg + j
+            // for both operands, so every dimension is summed exactly once.
+            float qv[D / 4];
+            {
+                const T* qrow = static_cast<const T*>(p.Q) +
+                    (((size_t)bi * p.h_q + my_head) * p.n + (row_ok ? my_row : 0)) * D + 4 * kg;
+#pragma unroll
+                for (int s = 0; s < D / 16; ++s) load4(qrow + 16 * s, &qv[4 * s]);
+                if (!row_ok) {
+#pragma unroll
+                    for (int e = 0; e < D / 4; ++e) qv[e] = 0.f;
+                }
+            }
+            const float* kb = p.kbar + ((size_t)bi * p.h_kv + r) * (size_t)p.kbar_cap * D + 4 * kg;
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                if (t < nt) {
+                    const int c = min(t * 16 + n16, nvis - 1);   // A row = chunk
+                    const float* krow = kb + (size_t)c * D;
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int s = 0; s < D / 16; ++s) {
+                        float a[4];
+                        load4(krow + 16 * s, a);
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], qv[4 * s + j], acc, 0, 0, 0);
+                    }
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int ch = t * 16 + 4 * kg + i;
+                        sv[t][i] = (ch < nvis) ? acc[i] : -INFINITY;
+                        smax = fmaxf(smax, sv[t][i]);
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) sv[t][i] = -INFINITY;
+                }
             }
         }
         smax = fmaxf(smax, shfl_xor(smax, 16));
@@ -180,22 +317,29 @@ __global__ __launch_bounds__(256) void entmax_route_kernel(RouteParams p) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) sv[t][i] = p.cs * (sv[t][i] - smax);
 
-        const float tau = solve_tau<NT, PM>(sv, nt, p.pexp, row_ok);
+        const float tau = solve_tau<NT, PM>(sv, nt, p.pexp, row_ok && wave_live);
         // per-head weights, then the group average across the g lanes of each row
         const float inv_g = 1.f / (float)g;
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
+        for (int t = 0; t < NT; ++t) {
+            if (t < nt) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float wv = (t < nt && row_ok) ? pow_p<PM>(fmaxf(sv[t][i] - tau, 0.f), p.pexp) : 0.f;
-                sv[t][i] = row_group_sum(wv, lg) * inv_g;
+                for (int i = 0; i < 4; ++i) {
+                    const float wv = row_ok ? pow_p<PM>(fmaxf(sv[t][i] - tau, 0.f), p.pexp) : 0.f;
+                    sv[t][i] = row_group_sum(wv, lg) * inv_g;
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sv[t][i] = 0.f;
             }
+        }
     } else {
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
             for (int i = 0; i < 4; ++i) sv[t][i] = 0.f;
     }
+    if (!wave_live) return;                           // no barrier follows
     // group weights to LDS: the first lane of each row writes its chunks
     if ((n16 & (g - 1)) == 0) {
         float* wr = wl + (n16 >> lg) * WS;
@@ -244,20 +388,24 @@ __global__ __launch_bounds__(256) void entmax_route_kernel(RouteParams p) {
     }
 }
 
-// Waves per workgroup: 4, fewer when a wave's LDS rows would exceed 64 KiB in total.
-inline int route_waves_per_block(int R, int NT) {
-    const int per_wave = R * NT * 16 * 4;
-    int w = 65536 / per_wave;
-    return w >= 4 ? 4 : (w < 1 ? 1 : w);
+// Waves per workgroup: up to 8; all rows of a workgroup must share one chunk, and
+// the LDS (two summary stages for bf16 queries plus the rows' weights) must fit.
+template <typename T, int D, int NT>
+inline int route_waves_per_block(int R, int B, size_t* lds) {
+    const size_t stage = sizeof(T) == 2 ? 2 * (size_t)KSplitStage<D>::BYTES : 0;
+    int w = 8;
+    while (w > 1 && (B % (w * R) != 0 || stage + (size_t)w * R * NT * 16 * 4 > 64 * 1024)) w >>= 1;
+    *lds = stage + (size_t)w * R * NT * 16 * 4;
+    return w;
 }
 
 template <typename T, int D, int NT>
 static hipError_t launch_route_nt(const RouteParams& p, int b, hipStream_t s) {
     const int R = 16 / p.g;
-    const int W = route_waves_per_block(R, NT);
+    size_t lds = 0;
+    const int W = route_waves_per_block<T, D, NT>(R, p.B, &lds);
     const int waves = (p.n + R - 1) / R;
     dim3 grid((waves + W - 1) / W, p.h_kv, b), block(64 * W);
-    const size_t lds = (size_t)W * R * NT * 16 * sizeof(float);
     switch (p.pmode) {
         case 1: hipLaunchKernelGGL((entmax_route_kernel<T, D, NT, 1>), grid, block, lds, s, p); break;
         case 2: hipLaunchKernelGGL((entmax_route_kernel<T, D, NT, 2>), grid, block, lds, s, p); break;
