@@ -59,6 +59,7 @@ class Prefill:
         self.kbar = dash.alloc_kbar(b, w.h_kv, self.T, d)
         self.idx, self.bias, self.cnt, _ = dash.alloc_route(b, w.h_kv, n, self.T)
         self.O = torch.empty((b, h_q, n, d), dtype=torch.bfloat16, device="cuda")
+        self.ws = dash.alloc_prefill_ws(b, h_q, w.h_kv, n, d, w.B)
 
     def run(self, alpha, ev=None):
         d, w = self.dash, self.w
@@ -68,7 +69,8 @@ class Prefill:
         d.dash_route(self.Q, self.kbar, w.B, alpha, w.gamma, w.sigma, True, self.idx, self.bias,
                      self.cnt)
         if ev: ev[2].record()
-        d.dash_attend_prefill(self.Q, self.K, self.V, self.idx, self.bias, self.cnt, self.O, w.B, True)
+        d.dash_attend_prefill(self.Q, self.K, self.V, self.idx, self.bias, self.cnt, self.O, w.B, True,
+                              ws=self.ws)
         if ev: ev[3].record()
 
     def stats(self):
@@ -251,7 +253,7 @@ def main():
         di, db, dc = dense_lists(pre, torch)
         Od = torch.empty_like(pre.O)
         fn = lambda ev: (ev and ev[0].record(),
-                         dash.dash_attend_prefill(pre.Q, pre.K, pre.V, di, db, dc, Od, wp.B, True),
+                         dash.dash_attend_prefill(pre.Q, pre.K, pre.V, di, db, dc, Od, wp.B, True, ws=pre.ws),
                          ev and ev[1].record())
         sd, _ = time_events(torch, fn, 2, max(3, args.steps // 2), 1)
         td = float(sd.mean())

@@ -15,7 +15,8 @@
  *
  * Conventions shared by every entry point
  *   - All tensor pointers are DEVICE pointers owned by the caller; the library
- *     keeps no pointer after returning and allocates no device memory.
+ *     keeps no pointer after returning and allocates no device memory (scratch
+ *     memory comes in through the workspace arguments).
  *   - Tensors are contiguous, batch-head-sequence-dim (BHSD):
  *       Q [b, h_q, n, d], K and V [b, h_kv, n, d], q̄ [h_kv, d] (fp32),
  *       k̄ [b, h_kv, kbar_cap, d] (fp32).
@@ -99,7 +100,10 @@ dash_status dash_route(const void* Q, int q_dtype, const float* kbar,
  * <q,k>/sqrt(d) + bias of the chunk) and of the diagonal branch (bias 0, causal
  * mask inside the own chunk), times V. Q, K, V share in_dtype; O
  * [b, h_q, n, d] is written in out_dtype. idx/bias/cnt are dash_route's outputs
- * (same list_cap). Requires B % 32 == 0.
+ * (same list_cap). Requires B % 32 == 0. bf16 inputs need a device workspace of at
+ * least dash_workspace_bytes(DASH_OP_PREFILL, ...) bytes (V transposed to
+ * [b, h_kv, d, n rounded up to 64]); fp32 inputs need none (ws may be NULL). Calls
+ * that share one workspace must not overlap.
  */
 dash_status dash_attend_prefill(const void* Q, const void* K, const void* V, int in_dtype,
                                 const int32_t* idx, const float* bias, const int32_t* cnt,
@@ -131,7 +135,8 @@ dash_status dash_attend_decode(const void* Q, const void* Kc, const void* Vc, in
                                void* ws, size_t ws_bytes, void* stream);
 
 /* Workspace bytes an operation needs (n_or_Lcap: n for prefill ops, L_cap for
- * decode). Returns 0 when no workspace is needed, (size_t)-1 on invalid sizes. */
+ * decode; DASH_OP_PREFILL gives the size for bf16 inputs). Returns 0 when no
+ * workspace is needed, (size_t)-1 on invalid sizes. */
 size_t dash_workspace_bytes(int op, int b, int h_q, int h_kv, int n_or_Lcap, int d, int B);
 
 /* Static English name of a status code. */

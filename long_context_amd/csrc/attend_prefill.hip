@@ -1,38 +1,23 @@
-// Stage 2 of DashAttention for a prefill (paper review section 三, Eq. 9-12 through
-// the additive-bias form of Proposition 4.1):
-//   o_i = sum_{j in R_i ∪ D_i} softmax_j(<q_i, k_j>/sqrt(d) + d_ij) v_j,
-// with d_ij = bias of chunk c(j) on the routed tokens R_i and 0 on the diagonal
-// branch D_i (the query's own chunk up to itself, causal).
+// Stage 2 prefill kernel for fp32 inputs (see prefill_common.h for the method).
 //
-// sparse_prior_attn_kernel: one workgroup per (query tile, KV group, batch). The
-// tile is R_t consecutive rows inside one chunk times all g query heads of the
-// group (M = g*R_t pairs, 32 per wavefront, up to 8 wavefronts); the heads of a
-// group share one routed list, so packing them costs no extra work. The workgroup
-// first merges its rows' lists into the union of routed chunks (ascending) and a
-// per-(row, chunk) bias table in LDS, then walks the union and finally the
-// diagonal chunk in TT-token tiles:
+// sparse_prior_attn_kernel: the tile is R_t rows times the g heads of a KV group
+// (M = g*R_t pairs, 32 per wavefront, up to 8 wavefronts):
 //   * tiles are copied global->LDS asynchronously (global_load_lds_dwordx4) into a
 //     two-stage ring; the copy of tile k+1 runs while tile k is computed, and one
 //     barrier per tile separates the stages;
 //   * a wavefront skips a chunk none of its rows routes to;
 //   * S^T = K Q^T on MFMA (lane = one (row, head) column), logits in log2 units
 //     with the bias folded into the exp2 argument, online softmax per lane with
-//     lazy rescaling, O^T += V^T P^T on MFMA with V read through the transposing
-//     LDS load; the division by the softmax denominator happens once at the end.
-#include "attn_common.h"
+//     lazy rescaling, O^T += V^T P^T on MFMA; the division by the softmax
+//     denominator happens once at the end.
+// The kernel is generic in the element type; bf16 inputs take the kernel of
+// attend_prefill_bf16.hip.
 #include "kernels.h"
+#include "prefill_common.h"
 
 #include <math.h>
 
 namespace dash {
-
-struct PrefillParams {
-    const void* Q; const void* K; const void* V;
-    const int32_t* idx; const float* bias; const int32_t* cnt;
-    void* O;
-    int out_bf16, h_q, h_kv, n, B, T_c, list_cap, causal, g, log2g, R_t, nw;
-    float scale_log2;    // log2(e)/sqrt(d)
-};
 
 constexpr int kWaves = 8;                 // wavefronts per workgroup (256 pairs)
 
@@ -43,10 +28,8 @@ __global__ __launch_bounds__(64 * kWaves) void sparse_prior_attn_kernel(PrefillP
     typedef typename MM::Op Op;
     extern __shared__ __attribute__((aligned(16))) char smem[];
     char* ring = smem;                                             // 2 stages
-    float* btab = reinterpret_cast<float*>(smem + 2 * S::STAGE);
-    int* uflag = reinterpret_cast<int*>(btab + p.R_t * p.T_c);
-    int* ulist = uflag + p.T_c;
-    int* s_U = ulist + p.T_c;
+    TileTables tabs;
+    tabs.carve(smem + 2 * S::STAGE, p.R_t, p.T_c);
 
     constexpr int nthr = 64 * kWaves;
     const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
@@ -61,38 +44,9 @@ __global__ __launch_bounds__(64 * kWaves) void sparse_prior_attn_kernel(PrefillP
     const size_t bhkv = (size_t)bi * p.h_kv + r;
     const T* Kg = static_cast<const T*>(p.K) + bhkv * (size_t)p.n * D;
     const T* Vg = static_cast<const T*>(p.V) + bhkv * (size_t)p.n * D;
-
-    // ---- union of the tile rows' routed chunks and the (row, chunk) bias table ----
-    for (int i = tid; i < R_t * nvis; i += nthr) btab[(i / nvis) * p.T_c + i % nvis] = -INFINITY;
-    for (int c = tid; c < nvis; c += nthr) uflag[c] = 0;
-    __syncthreads();
-    for (int j = 0; j < R_t; ++j) {
-        const int row = row0 + j;
-        if (row >= p.n) break;
-        const size_t rb = bhkv * p.n + row;
-        const int cn = p.cnt[rb];
-        for (int e = tid; e < cn; e += nthr) {
-            const int c = p.idx[rb * p.list_cap + e];
-            if (c >= 0 && c < nvis) {
-                btab[j * p.T_c + c] = p.bias[rb * p.list_cap + e];
-                uflag[c] = 1;
-            }
-        }
-    }
-    __syncthreads();
-    if (wid == 0) {
-        int base = 0;
-        for (int c0 = 0; c0 < nvis; c0 += 64) {
-            const int c = c0 + lane;
-            const bool f = c < nvis && uflag[c] != 0;
-            const uint64_t m = ballot(f);
-            if (f) ulist[base + __builtin_popcountll(m & ((1ull << lane) - 1ull))] = c;
-            base += __builtin_popcountll(m);
-        }
-        if (lane == 0) *s_U = base;
-    }
-    __syncthreads();
-    const int U = *s_U;
+    const int U = tabs.build(p, bhkv, row0, nvis, tid, nthr);
+    const float* btab = tabs.btab;
+    const int* ulist = tabs.ulist;
 
     // ---- this lane's (row, head) pair ----
     const int pair = wid * 32 + l32;
@@ -118,21 +72,11 @@ __global__ __launch_bounds__(64 * kWaves) void sparse_prior_attn_kernel(PrefillP
 #pragma unroll
         for (int i = 0; i < 16; ++i) o_acc[db][i] = 0.f;
 
-    const int SPC = p.B / TT;
-    int diag_base, ndiag;
-    if (p.causal) {
-        diag_base = cq * p.B;
-        ndiag = (last_row - diag_base) / TT + 1;
-    } else {
-        diag_base = p.T_c * p.B;
-        ndiag = (p.n - diag_base + TT - 1) / TT;
-    }
-    const int nrouted = U * SPC;
-    const int nsteps = nrouted + ndiag;
+    TileSteps st;
+    st.init(p, U, cq, last_row, TT);
+    const int nrouted = st.nrouted, nsteps = st.nsteps, SPC = st.SPC;
     const int nmax = p.n - 1;
-    auto tile_base = [&](int k) -> int {
-        return k < nrouted ? ulist[k / SPC] * p.B + (k % SPC) * TT : diag_base + (k - nrouted) * TT;
-    };
+    auto tile_base = [&](int k) -> int { return st.base(ulist, k); };
     TileCopier<T, D, TT, kWaves> copier;
     copier.init(wid, lane);
     auto issue = [&](int k) { copier.issue(ring + (k & 1) * S::STAGE, Kg, Vg, tile_base(k), nmax, wid); };
@@ -268,20 +212,16 @@ static constexpr size_t kMaxLds = 160 * 1024;
 
 static int stage_bytes(int d, bool bf16, int TT) { return 2 * TT * d * (bf16 ? 2 : 4); }
 
-static size_t prefill_lds(int R_t, int T_c, int stage) {
-    return (size_t)2 * stage + (size_t)R_t * T_c * 4 + (size_t)2 * T_c * 4 + 16;
-}
-
 void prefill_tiling(int g, int B, int T_c, int d, bool bf16, int* rows, size_t* lds_bytes) {
     *rows = 0;
     *lds_bytes = 0;
     if (B % 32 != 0 || g < 1 || g > 16) return;
     const int TT = (B % 64 == 0) ? 64 : 32;
     const int st = stage_bytes(d, bf16, TT);
-    for (int m = 32 * kWaves; m >= 32; m >>= 1) {
+    for (int m = 256; m >= 32; m >>= 1) {
         const int R_t = m / g;
         if (R_t < 1 || B % R_t != 0) continue;
-        const size_t lds = prefill_lds(R_t, T_c, st);
+        const size_t lds = (size_t)2 * st + TileTables::bytes(R_t, T_c);
         if (lds <= kMaxLds) {
             *rows = R_t;
             *lds_bytes = lds;
@@ -290,23 +230,31 @@ void prefill_tiling(int g, int B, int T_c, int d, bool bf16, int* rows, size_t* 
     }
 }
 
-template <typename T, int D, int TT>
+template <int D, int TT>
 static hipError_t launch_prefill_t(const PrefillParams& p, int b, size_t lds, hipStream_t s) {
     static bool configured = false;
     if (!configured) {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&sparse_prior_attn_kernel<T, D, TT>),
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&sparse_prior_attn_kernel<float, D, TT>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
         configured = true;
     }
     dim3 grid((p.n + p.R_t - 1) / p.R_t, p.h_kv, b), block(64 * kWaves);
-    hipLaunchKernelGGL((sparse_prior_attn_kernel<T, D, TT>), grid, block, lds, s, p);
+    hipLaunchKernelGGL((sparse_prior_attn_kernel<float, D, TT>), grid, block, lds, s, p);
     return hipGetLastError();
+}
+
+hipError_t launch_prefill_f32(const PrefillParams& p, int b, int d, size_t lds, hipStream_t s) {
+    const bool t64 = (p.B % 64 == 0);
+    if (d == 64) return t64 ? launch_prefill_t<64, 64>(p, b, lds, s) : launch_prefill_t<64, 32>(p, b, lds, s);
+    return t64 ? launch_prefill_t<128, 64>(p, b, lds, s) : launch_prefill_t<128, 32>(p, b, lds, s);
 }
 
 hipError_t launch_attend_prefill(const PrefillArgs& a, hipStream_t s) {
     PrefillParams p;
     p.Q = a.Q; p.K = a.K; p.V = a.V; p.idx = a.idx; p.bias = a.bias; p.cnt = a.cnt; p.O = a.O;
+    p.Vt = static_cast<const uint16_t*>(a.ws);
     p.out_bf16 = a.out_bf16; p.h_q = a.h_q; p.h_kv = a.h_kv; p.n = a.n; p.B = a.B;
+    p.n_pad = prefill_n_pad(a.n);
     p.T_c = a.n / a.B; p.list_cap = a.list_cap; p.causal = a.causal;
     p.g = a.h_q / a.h_kv;
     p.log2g = 0;
@@ -317,13 +265,7 @@ hipError_t launch_attend_prefill(const PrefillArgs& a, hipStream_t s) {
     if (p.R_t == 0) return hipErrorInvalidValue;
     p.nw = (p.g * p.R_t + 31) / 32;
     if (a.n == 0) return hipSuccess;
-    const bool t64 = (a.B % 64 == 0);
-    if (a.in_bf16) {
-        if (a.d == 64) return t64 ? launch_prefill_t<uint16_t, 64, 64>(p, a.b, lds, s) : launch_prefill_t<uint16_t, 64, 32>(p, a.b, lds, s);
-        return t64 ? launch_prefill_t<uint16_t, 128, 64>(p, a.b, lds, s) : launch_prefill_t<uint16_t, 128, 32>(p, a.b, lds, s);
-    }
-    if (a.d == 64) return t64 ? launch_prefill_t<float, 64, 64>(p, a.b, lds, s) : launch_prefill_t<float, 64, 32>(p, a.b, lds, s);
-    return t64 ? launch_prefill_t<float, 128, 64>(p, a.b, lds, s) : launch_prefill_t<float, 128, 32>(p, a.b, lds, s);
+    return a.in_bf16 ? launch_prefill_bf16(p, a.b, a.d, lds, s) : launch_prefill_f32(p, a.b, a.d, lds, s);
 }
 
 }  // namespace dash

@@ -139,7 +139,6 @@ dash_status dash_attend_prefill(const void* Q, const void* K, const void* V, int
                                 int list_cap, void* O, int out_dtype,
                                 int b, int h_q, int h_kv, int n, int d, int B, int causal,
                                 void* ws, size_t ws_bytes, void* stream) {
-    (void)ws; (void)ws_bytes;
     if (!Q || !K || !V || !idx || !bias || !cnt || !O) return fail(DASH_ERR_NULL, "Q, K, V, idx, bias, cnt and O must be non-null");
     if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return fail(DASH_ERR_PARAM, "bad dtype");
     if (causal != 0 && causal != 1) return fail(DASH_ERR_PARAM, "causal must be 0 or 1");
@@ -153,8 +152,13 @@ dash_status dash_attend_prefill(const void* Q, const void* K, const void* V, int
     size_t lds = 0;
     dash::prefill_tiling(h_q / h_kv, B, T, d, in_dtype == DASH_BF16, &rows, &lds);
     if (rows == 0) return fail(DASH_ERR_UNSUPPORTED, "no query tiling fits LDS (g=%d, B=%d, T_c=%d)", h_q / h_kv, B, T);
+    if (in_dtype == DASH_BF16 && n > 0) {
+        const size_t need = dash::prefill_workspace_bytes(b, h_kv, n, d);
+        if (!ws || ws_bytes < need)
+            return fail(DASH_ERR_WORKSPACE, "bf16 prefill needs %zu workspace bytes, got %zu", need, ws ? ws_bytes : (size_t)0);
+    }
     dash::PrefillArgs a{Q, K, V, in_dtype == DASH_BF16, idx, bias, cnt, list_cap, O, out_dtype == DASH_BF16,
-                        b, h_q, h_kv, n, d, B, causal};
+                        b, h_q, h_kv, n, d, B, causal, ws};
     return from_hip(dash::launch_attend_prefill(a, (hipStream_t)stream), "sparse_prior_attn_kernel");
 }
 
@@ -162,7 +166,7 @@ size_t dash_workspace_bytes(int op, int b, int h_q, int h_kv, int n_or_Lcap, int
     if (b < 1 || h_q < 1 || h_kv < 1 || h_q % h_kv != 0 || n_or_Lcap < 0 || d < 1 || B < 1) return (size_t)-1;
     switch (op) {
         case DASH_OP_ROUTE: return 0;
-        case DASH_OP_PREFILL: return 0;
+        case DASH_OP_PREFILL: return dash::prefill_workspace_bytes(b, h_kv, n_or_Lcap, d);
         case DASH_OP_DECODE: {
             if (n_or_Lcap < 1) return (size_t)-1;
             return decode_layout(b, h_q, h_kv, n_or_Lcap, 1 << 30, d, B).total;

@@ -30,8 +30,13 @@ struct PrefillArgs {
     const int32_t* idx; const float* bias; const int32_t* cnt; int list_cap;
     void* O; bool out_bf16;
     int b, h_q, h_kv, n, d, B, causal;
+    void* ws;            // bf16 inputs: V transposed, prefill_workspace_bytes
 };
 hipError_t launch_attend_prefill(const PrefillArgs& a, hipStream_t s);
+// Workspace of a bf16 prefill: V transposed per (b, KV head) as [d][n_pad] bf16 with
+// n_pad = n rounded up to 64 (the pad is zero-filled).
+int prefill_n_pad(int n);
+size_t prefill_workspace_bytes(int b, int h_kv, int n, int d);
 // Rows per query tile and dynamic LDS bytes of the prefill attention kernel
 // (rows = 0 when the shape is not supported).
 void prefill_tiling(int g, int B, int T_c, int d, bool bf16, int* rows, size_t* lds_bytes);

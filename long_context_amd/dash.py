@@ -118,9 +118,13 @@ def dash_route(Q, kbar, B, alpha, gamma, sigma, causal, idx, bias, cnt, w_out=No
 
 
 def dash_attend_prefill(Q, K, V, idx, bias, cnt, O, B, causal, ws=None, stream=None):
-    """Stage 2 of a prefill into O [b,h_q,n,d] (fp32 or bf16)."""
+    """Stage 2 of a prefill into O [b,h_q,n,d] (fp32 or bf16).
+
+    bf16 inputs need a workspace (alloc_prefill_ws); one is allocated when ws is None."""
     b, h_q, n, d = Q.shape
     h_kv = K.shape[1]
+    if ws is None and Q.dtype == torch.bfloat16:
+        ws = alloc_prefill_ws(b, h_q, h_kv, n, d, B, device=Q.device)
     _check(lib.dash_attend_prefill(_ptr(Q), _ptr(K), _ptr(V), _dtype(Q), _ptr(idx), _ptr(bias),
                                    _ptr(cnt), idx.shape[-1], _ptr(O), _dtype(O), b, h_q, h_kv, n,
                                    d, B, int(causal), _ptr(ws),
@@ -157,6 +161,11 @@ def alloc_route(b, h_kv, n, T, device="cuda", with_w=False):
     cnt = torch.empty((b, h_kv, n), dtype=torch.int32, device=device)
     w = torch.empty((b, h_kv, n, cap), dtype=torch.float32, device=device) if with_w else None
     return idx, bias, cnt, w
+
+
+def alloc_prefill_ws(b, h_q, h_kv, n, d, B, device="cuda"):
+    nbytes = dash_workspace_bytes(DASH_OP_PREFILL, b, h_q, h_kv, n, d, B)
+    return torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=device)
 
 
 def alloc_decode_ws(b, h_q, h_kv, L_cap, d, B, device="cuda"):

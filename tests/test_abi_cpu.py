@@ -105,6 +105,13 @@ def test_prefill_validation(dash, kw, status):
     assert _prefill(dash, **kw) == status
 
 
+def test_prefill_bf16_needs_workspace(dash):
+    need = dash.dash_workspace_bytes(dash.DASH_OP_PREFILL, 1, 4, 2, 256, 128, 64)
+    args = (P, P, P, 1, P, P, P, 4, P, 0, 1, 4, 2, 256, 128, 64, 1)
+    assert dash.lib.dash_attend_prefill(*args, NUL, need, NUL) == dash.DASH_ERR_WORKSPACE
+    assert dash.lib.dash_attend_prefill(*args, P, need - 1, NUL) == dash.DASH_ERR_WORKSPACE
+
+
 def _decode(dash, ws_bytes, **kw):
     a = dict(Q=P, Kc=P, Vc=P, dt=1, kbar=P, sl=P, b=4, h_q=32, h_kv=2, L=131072, cap=1024,
              d=128, B=128, alpha=1.5, gamma=1.0, sigma=1.0, O=P, odt=0, idx=NUL, bias=NUL,
@@ -131,7 +138,8 @@ def test_decode_workspace_checks(dash):
 
 def test_workspace_sizes(dash):
     assert dash.dash_workspace_bytes(dash.DASH_OP_ROUTE, 1, 32, 2, 32768, 128, 64) == 0
-    assert dash.dash_workspace_bytes(dash.DASH_OP_PREFILL, 1, 32, 2, 32768, 128, 64) == 0
+    assert dash.dash_workspace_bytes(dash.DASH_OP_PREFILL, 1, 32, 2, 32768, 128, 64) == 2 * 128 * 32768 * 2
+    assert dash.dash_workspace_bytes(dash.DASH_OP_PREFILL, 1, 4, 2, 100, 64, 32) == 2 * 64 * 128 * 2
     big = dash.dash_workspace_bytes(dash.DASH_OP_DECODE, 16, 32, 2, 32768, 128, 64)
     small = dash.dash_workspace_bytes(dash.DASH_OP_DECODE, 16, 32, 2, 4096, 128, 64)
     assert big > small > 0
