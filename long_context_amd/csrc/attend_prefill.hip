@@ -212,16 +212,20 @@ static constexpr size_t kMaxLds = 160 * 1024;
 
 static int stage_bytes(int d, bool bf16, int TT) { return 2 * TT * d * (bf16 ? 2 : 4); }
 
+PrefillGeom prefill_geom_f32(int, int B) {
+    return PrefillGeom{(B % 64 == 0) ? 64 : 32, kWaves, 32 * kWaves, 2};
+}
+
 void prefill_tiling(int g, int B, int T_c, int d, bool bf16, int* rows, size_t* lds_bytes) {
     *rows = 0;
     *lds_bytes = 0;
     if (B % 32 != 0 || g < 1 || g > 16) return;
-    const int TT = (B % 64 == 0) ? 64 : 32;
-    const int st = stage_bytes(d, bf16, TT);
-    for (int m = 256; m >= 32; m >>= 1) {
+    const PrefillGeom geo = bf16 ? prefill_geom_bf16(d, B) : prefill_geom_f32(d, B);
+    const int st = stage_bytes(d, bf16, geo.TT);
+    for (int m = geo.max_pairs; m >= 32; m >>= 1) {
         const int R_t = m / g;
         if (R_t < 1 || B % R_t != 0) continue;
-        const size_t lds = (size_t)2 * st + TileTables::bytes(R_t, T_c);
+        const size_t lds = (size_t)geo.stages * st + TileTables::bytes(R_t, T_c);
         if (lds <= kMaxLds) {
             *rows = R_t;
             *lds_bytes = lds;

@@ -367,6 +367,12 @@ size_t prefill_workspace_bytes(int b, int h_kv, int n, int d) {
 constexpr int kWavesB = 8;        // wavefronts per workgroup
 constexpr int kPairBlocks = 1;    // 32-pair blocks per wavefront
 
+static int bf16_tile_tokens(int, int B) { return (B % 64 == 0) ? 64 : 32; }
+
+PrefillGeom prefill_geom_bf16(int d, int B) {
+    return PrefillGeom{bf16_tile_tokens(d, B), kWavesB, 32 * kWavesB * kPairBlocks, 2};
+}
+
 template <int D, int TT>
 static hipError_t launch_bf16_t(const PrefillParams& p, int b, size_t lds, hipStream_t s) {
     auto kern = sparse_prior_attn_bf16_kernel<D, TT, kWavesB, kPairBlocks>;
@@ -384,7 +390,7 @@ static hipError_t launch_bf16_t(const PrefillParams& p, int b, size_t lds, hipSt
 }
 
 hipError_t launch_prefill_bf16(const PrefillParams& p, int b, int d, size_t lds, hipStream_t s) {
-    const bool t64 = (p.B % 64 == 0);
+    const bool t64 = bf16_tile_tokens(d, p.B) == 64;
     if (d == 64) return t64 ? launch_bf16_t<64, 64>(p, b, lds, s) : launch_bf16_t<64, 32>(p, b, lds, s);
     return t64 ? launch_bf16_t<128, 64>(p, b, lds, s) : launch_bf16_t<128, 32>(p, b, lds, s);
 }

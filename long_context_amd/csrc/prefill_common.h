@@ -103,6 +103,12 @@ struct TileSteps {
     }
 };
 
+// Launch geometry of a prefill kernel: tokens per tile, wavefronts per workgroup,
+// the most (row, head) pairs a workgroup takes, and LDS ring stages.
+struct PrefillGeom { int TT, waves, max_pairs, stages; };
+PrefillGeom prefill_geom_f32(int d, int B);
+PrefillGeom prefill_geom_bf16(int d, int B);
+
 // fp32-input kernel (attend_prefill.hip) and bf16-input kernel with its V
 // transposition (attend_prefill_bf16.hip).
 hipError_t launch_prefill_f32(const PrefillParams& p, int b, int d, size_t lds, hipStream_t s);
