@@ -306,9 +306,12 @@ __global__ __launch_bounds__(256, 2) void decode_attn_kernel(DecodeParams p) {
             mx = fmaxf(mx, v);
         }
         mx = fmaxf(mx, shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx);
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = fast_exp2(m_run - m_use);
+        // lazy rescaling: the reference maximum moves only when the tile maximum
+        // exceeds it by more than 8 (probabilities stay <= 2^8 in between)
+        const bool grow = mx > m_run + 8.f;
+        const float alpha = grow ? fast_exp2(m_run - mx) : 1.f;
+        m_run = grow ? mx : m_run;
+        const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
         float ps = 0.f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -317,11 +320,12 @@ __global__ __launch_bounds__(256, 2) void decode_attn_kernel(DecodeParams p) {
             ps += pv;
         }
         l_run = fmaf(l_run, alpha, ps);
-        m_run = m_new;
+        if (ballot(grow) != 0) {
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db)
+            for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) o_acc[db][i] *= alpha;
+                for (int i = 0; i < 16; ++i) o_acc[db][i] *= alpha;
+        }
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             float pv8[8];
