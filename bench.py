@@ -121,6 +121,12 @@ class Prefill:
                               ws=self.ws)
         if ev: ev[3].record()
 
+    def route_bytes(self):
+        """Algorithmic HBM bytes of the last routing: Q, summaries, lists written, counts."""
+        w = self.w
+        sup = int(self.cnt.to(self.torch.int64).sum().item())
+        return (w.Q.size * 2 + w.b * w.h_kv * self.T * w.d * 4 + sup * 8 + w.b * w.h_kv * w.n * 4)
+
     def stats(self):
         """Work of the last routing (bookkeeping outside the timed region).
 
@@ -276,12 +282,16 @@ def main():
     st = pre.stats()
     t_sum, t_route, t_att = (float(np.mean(seg[:, j])) for j in range(3))
     t_pre = t_sum + t_route + t_att
+    tot = seg.sum(1)
+    route_bytes = pre.route_bytes()
     res["prefill"] = dict(ms=t_pre, stage0_ms=t_sum, stage1_ms=t_route, stage2_ms=t_att,
                           tok_s=wp.n / (t_pre * 1e-3), sparsity=st["sparsity"],
                           stage2_row_tflops=st["flops_row"] / (t_att * 1e-3) / 1e12,
                           stage2_wave_tflops=st["flops_wave"] / (t_att * 1e-3) / 1e12,
                           stage2_tile_tflops=st["flops_tile"] / (t_att * 1e-3) / 1e12,
                           inflation_wave=st["inflation_wave"], inflation_tile=st["inflation_tile"],
+                          ms_median=float(np.median(tot)), ms_min=float(tot.min()), ms_max=float(tot.max()),
+                          stage1_gbs=route_bytes / (t_route * 1e-3) / 1e9,
                           wall_s=wall)
     print(f"[bench] prefill alpha={args.alpha}: {res['prefill']}", file=sys.stderr, flush=True)
 
@@ -314,19 +324,33 @@ def main():
         del di, db, dc, Od
         print(f"[bench] dense: {dense}", file=sys.stderr, flush=True)
 
-    # --- decode at 128K ------------------------------------------------------------
-    dec = None
+    # --- decode at 128K (and 32K x 16) ----------------------------------------------
+    dec = dec32 = None
     if args.only in ("decode", "both"):
-        wd = inputs.decode_128k_b4()
-        dd = Decode(wd, torch, dash)
-        sdec, _ = time_events(torch, dd.run, 2, args.steps, args.warmup)
-        tdec = float(sdec.mean())
-        nbytes, cnt = dd.bytes_per_step()
-        dec = dict(us_per_step=tdec * 1e3, gbs=nbytes / (tdec * 1e-3) / 1e9,
-                   hbm_frac=nbytes / (tdec * 1e-3) / 1e9 / PEAK_HBM_GBS, bytes=nbytes,
-                   routed=cnt.ravel().tolist())
-        print(f"[bench] decode: {dec}", file=sys.stderr, flush=True)
+        # reading a 512 MiB buffer between timed decode steps evicts the 256 MiB
+        # Infinity Cache (a read leaves no dirty lines to write back during the
+        # step), so each step streams its KV from HBM; the read is outside the events
+        scrub = torch.ones(512 << 20, dtype=torch.uint8, device="cuda")
+
+        def time_decode(dd):
+            sfl, _ = time_events(torch, lambda ev: (scrub.max(), dd.run(ev)), 2, args.steps, args.warmup)
+            sun, _ = time_events(torch, dd.run, 2, args.steps, args.warmup)
+            nbytes, cnt = dd.bytes_per_step()
+            tfl, tun = float(np.median(sfl)), float(np.median(sun))
+            return dict(us_per_step=tfl * 1e3, us_min=float(sfl.min()) * 1e3, us_max=float(sfl.max()) * 1e3,
+                        us_per_step_unflushed=tun * 1e3, gbs=nbytes / (tfl * 1e-3) / 1e9,
+                        hbm_frac=nbytes / (tfl * 1e-3) / 1e9 / PEAK_HBM_GBS, bytes=nbytes,
+                        routed=cnt.ravel().tolist())
+
+        dd = Decode(inputs.decode_128k_b4(), torch, dash)
+        dec = time_decode(dd)
+        print(f"[bench] decode 128k: {dec}", file=sys.stderr, flush=True)
         del dd
+        dd = Decode(inputs.decode_32k_b16(), torch, dash)
+        dec32 = time_decode(dd)
+        dec32.pop("routed")
+        print(f"[bench] decode 32k x16: {dec32}", file=sys.stderr, flush=True)
+        del dd, scrub
 
     t_step = t_pre + (dec["us_per_step"] * 1e-3 if dec else 0.0)
     out.update({"value": res["prefill"]["tok_s"], "unit": "tok/s", "ms_per_step": t_step,
@@ -347,6 +371,7 @@ def main():
     out["dense_baseline"] = dense
     if dec:
         out["decode"] = dec
+        out["decode_32k_b16"] = dec32
         out["decode_roofline"] = {"bound": "hbm", "kernel": "decode (route + split-KV + combine)",
                                   "achieved": dec["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                   "frac": dec["hbm_frac"], "traffic": None}
