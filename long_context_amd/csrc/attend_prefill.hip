@@ -236,12 +236,10 @@ void prefill_tiling(int g, int B, int T_c, int d, bool bf16, int* rows, size_t* 
 
 template <int D, int TT>
 static hipError_t launch_prefill_t(const PrefillParams& p, int b, size_t lds, hipStream_t s) {
-    static bool configured = false;
-    if (!configured) {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&sparse_prior_attn_kernel<float, D, TT>),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
-        configured = true;
-    }
+    static hipError_t configured = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&sparse_prior_attn_kernel<float, D, TT>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
+    if (configured != hipSuccess) return configured;
     dim3 grid((p.n + p.R_t - 1) / p.R_t, p.h_kv, b), block(64 * kWaves);
     hipLaunchKernelGGL((sparse_prior_attn_kernel<float, D, TT>), grid, block, lds, s, p);
     return hipGetLastError();

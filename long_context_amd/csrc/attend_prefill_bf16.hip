@@ -79,9 +79,12 @@ struct BfCopier {
             }
         }
     }
-    // K rows min(tb + t, nmax); V^T columns tb .. tb+TT-1 (inside n_pad).
+    // K rows min(tb + t, nmax); V^T columns tb .. tb+TT-1 (inside n_pad). Tile bases
+    // are multiples of TT below n_pad by construction; the clamp keeps every source
+    // address inside the tensors even if a table were corrupted.
     __device__ __forceinline__ void issue(char* stage, const uint16_t* Kg, const uint16_t* Vtg, int tb,
                                           int nmax, int n_pad, int wid) const {
+        tb = min(max(tb, 0), n_pad - TT);
 #pragma unroll
         for (int i = 0; i < CPW; ++i) {
             const bool isk = wid + i * NW < S::KINSTS;     // wavefront-uniform
@@ -137,7 +140,7 @@ __global__ __launch_bounds__(64 * NW) void sparse_prior_attn_bf16_kernel(Prefill
     constexpr int NP = TT / 16;    // k16 steps of O^T
     constexpr int ND = D / 32;     // 32-wide d blocks of O^T
     extern __shared__ __attribute__((aligned(16))) char smem[];
-    char* ring = smem;
+    char* ring = smem;                                   // two tile stages
     TileTables tabs;
     tabs.carve(smem + 2 * S::STAGE, p.R_t, p.T_c);
 
@@ -376,12 +379,9 @@ PrefillGeom prefill_geom_bf16(int d, int B) {
 template <int D, int TT>
 static hipError_t launch_bf16_t(const PrefillParams& p, int b, size_t lds, hipStream_t s) {
     auto kern = sparse_prior_attn_bf16_kernel<D, TT, kWavesB, kPairBlocks>;
-    static bool configured = false;
-    if (!configured) {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-        configured = true;
-    }
+    static hipError_t configured = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (configured != hipSuccess) return configured;
     hipLaunchKernelGGL((transpose_v_kernel<D>), dim3(p.n_pad / 64, b * p.h_kv), dim3(256), 0, s,
                        static_cast<const uint16_t*>(p.V), const_cast<uint16_t*>(p.Vt), p.n, p.n_pad);
     dim3 grid((p.n + p.R_t - 1) / p.R_t, p.h_kv, b), block(64 * kWavesB);

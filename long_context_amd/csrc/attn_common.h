@@ -190,7 +190,7 @@ struct TileCopier {
         for (int i = 0; i < CPW; ++i) {
             const int j = wid + i * NW;
             const T* base = (j >= S::INSTS) ? Vg : Kg;            // wavefront-uniform
-            const T* src = base + (size_t)min(tb + row[i], nmax) * D + off[i];
+            const T* src = base + (size_t)max(min(tb + row[i], nmax), 0) * D + off[i];
             __builtin_amdgcn_global_load_lds(src, stage + dst[i], 16, 0, 0);
         }
     }

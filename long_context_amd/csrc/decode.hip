@@ -448,12 +448,9 @@ static void launch_dec_route(const DecodeParams& p, int b, hipStream_t s) {
 template <typename T, int D>
 static hipError_t launch_decode_t(const DecodeParams& p, const DecodeArgs& a, hipStream_t s) {
     constexpr size_t lds = TileGeom<T, D, kDecTT>::BYTES + 64 * 8;
-    static bool configured = false;
-    if (!configured) {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_attn_kernel<T, D>),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-        configured = true;
-    }
+    static hipError_t configured = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_attn_kernel<T, D>),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (configured != hipSuccess) return configured;
     if (p.T_route > 0) {
         dim3 g1((p.T_route + 63) / 64, p.h_kv, a.b);
         hipLaunchKernelGGL((decode_scores_kernel<D>), g1, dim3(256), 0, s, p, a.Q, a.in_bf16);

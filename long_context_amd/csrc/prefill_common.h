@@ -53,7 +53,7 @@ struct TileTables {
             const int row = row0 + j;
             if (row >= p.n) break;
             const size_t rb = bhkv * p.n + row;
-            const int cn = p.cnt[rb];
+            const int cn = min(p.cnt[rb], p.list_cap);
             for (int e = tid; e < cn; e += nthr) {
                 const int c = p.idx[rb * p.list_cap + e];
                 if (c >= 0 && c < nvis) {
