@@ -137,7 +137,7 @@ __global__ __launch_bounds__(64 * kWaves) void sparse_prior_attn_kernel(PrefillP
             for (int blk = 0; blk < TT / 32; ++blk)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[blk][i]);
-            mx = fmaxf(mx, shfl_xor(mx, 32));
+            mx = pair32_max(mx);
             const float tmax = fmaf(mx, p.scale_log2, bias2);     // -inf when nothing is visible
             // lazy rescaling: the reference maximum only moves when the tile maximum
             // exceeds it by more than 8 (probabilities stay <= 2^8 in between)
@@ -182,7 +182,7 @@ __global__ __launch_bounds__(64 * kWaves) void sparse_prior_attn_kernel(PrefillP
         __syncthreads();
     }
 
-    const float l_tot = l_run + shfl_xor(l_run, 32);
+    const float l_tot = pair32_sum(l_run);
     if (pair_ok) {
         const float inv = 1.f / l_tot;
         const size_t obase = (((size_t)bi * p.h_q + hh) * p.n + my_row) * D;

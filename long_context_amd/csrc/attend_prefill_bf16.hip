@@ -121,15 +121,6 @@ __global__ __launch_bounds__(256) void transpose_v_kernel(const uint16_t* V, uin
     }
 }
 
-__device__ __forceinline__ float half_swap_max(float v) {
-    // lanes l and l^32 hold the two token halves of one (row, head) pair
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float half_swap_sum(float v) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
 
 // NW wavefronts of PBW pair blocks (32 (row, head) pairs each).
 template <int D, int TT, int NW, int PBW>
@@ -251,7 +242,7 @@ __global__ __launch_bounds__(64 * NW) void sparse_prior_attn_bf16_kernel(Prefill
         for (int blk = 0; blk < NB; ++blk)
 #pragma unroll
             for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[blk][i]);
-        mx = half_swap_max(mx);
+        mx = pair32_max(mx);
         const float tmax = fmaf(mx, c1, bias2);              // -inf when nothing is visible
         // lazy rescaling: the reference maximum only moves when the tile maximum
         // exceeds it by more than 8 (probabilities stay <= 2^8 in between)
@@ -333,7 +324,7 @@ __global__ __launch_bounds__(64 * NW) void sparse_prior_attn_bf16_kernel(Prefill
 
 #pragma unroll
     for (int pb = 0; pb < PBW; ++pb) {
-        const float l_tot = half_swap_sum(l_run[pb]);
+        const float l_tot = pair32_sum(l_run[pb]);
         if (pok[pb]) {
             const int hh = r * g + (((wid * PBW + pb) * 32 + l32) & (g - 1));
             const float inv = 1.f / l_tot;

@@ -44,16 +44,50 @@ __device__ __forceinline__ int shfl_xor_i(int v, int mask) {
 
 __device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
 
-// Sum / max over all 64 lanes (result in every lane).
+// Sum / max of the values of lanes l and l^16 (l^32) without LDS traffic:
+// v_permlane16_swap (v_permlane32_swap) with both operands equal hands every lane
+// its own and its partner's value; sum and max are symmetric in the two, so both
+// lanes of a pair get the same, order-independent result.
+__device__ __forceinline__ float pair16_sum(float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float pair32_sum(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float pair16_max(float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair32_max(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// Value of the partner lane within a 16-lane row: xor 1, xor 2, mirror within 8
+// lanes, mirror within 16 (DPP). Applied in this order with a symmetric combine,
+// they reduce a whole row and leave the result in every lane of it.
+template <int CTRL>
+__device__ __forceinline__ float dpp_partner(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum / max over all 64 lanes (the same value in every lane): DPP within each
+// 16-lane row, then the cross-row swaps; no LDS traffic.
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += shfl_xor(v, m);
-    return v;
+    v += dpp_partner<0xB1>(v);
+    v += dpp_partner<0x4E>(v);
+    v += dpp_partner<0x141>(v);
+    v += dpp_partner<0x140>(v);
+    return pair32_sum(pair16_sum(v));
 }
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, shfl_xor(v, m));
-    return v;
+    v = fmaxf(v, dpp_partner<0xB1>(v));
+    v = fmaxf(v, dpp_partner<0x4E>(v));
+    v = fmaxf(v, dpp_partner<0x141>(v));
+    v = fmaxf(v, dpp_partner<0x140>(v));
+    return pair32_max(pair16_max(v));
 }
 
 // Load 8 consecutive elements of a row as fp32 (T = float or raw bf16 bits).

@@ -26,7 +26,10 @@
 
 namespace dash {
 
-constexpr int kDecTT = 128;          // tokens per decode tile (4 wavefronts x 32)
+constexpr int kDecTT = 64;           // tokens per decode tile (one 32-token block per wavefront)
+constexpr int kDecWaves = kDecTT / 32;
+constexpr int kDecThreads = 64 * kDecWaves;
+constexpr int kDecSlice = 512;        // stream tokens per workgroup
 
 struct DecodeParams {
     const void* Q; const void* Kc; const void* Vc;
@@ -208,7 +211,7 @@ __global__ __launch_bounds__(1024) void decode_route_kernel(DecodeParams p) {
 
 // ---------------------------------------------------------------------------------
 template <typename T, int D>
-__global__ __launch_bounds__(256, 2) void decode_attn_kernel(DecodeParams p) {
+__global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_attn_kernel(DecodeParams p) {
     typedef TileGeom<T, D, kDecTT> G;
     typedef Mfma<T> MM;
     typedef typename MM::Op Op;
@@ -233,7 +236,7 @@ __global__ __launch_bounds__(256, 2) void decode_attn_kernel(DecodeParams p) {
     if (t_begin >= t_end) return;
     const int e_first = t_begin / B;
     const int e_last = (t_end - 1) / B;
-    for (int e = e_first + tid; e <= e_last; e += 256) {
+    for (int e = e_first + tid; e <= e_last; e += kDecThreads) {
         const bool routed = e < cnt;
         s_chunk[e - e_first] = routed ? p.idx[grp * p.list_cap + e] : cq;
         s_bias[e - e_first] = routed ? p.bias[grp * p.list_cap + e] * kLog2e : 0.f;
@@ -265,17 +268,16 @@ __global__ __launch_bounds__(256, 2) void decode_attn_kernel(DecodeParams p) {
         if (tau >= t_end) return -1;
         return s_chunk[tau / B - e_first] * B + tau % B;
     };
-    int rb0, rb1, rb2, rb3;
+    int rb[kDecWaves];
     auto set_bases = [&](int tt0) {
-        rb0 = group_base(tt0); rb1 = group_base(tt0 + 32);
-        rb2 = group_base(tt0 + 64); rb3 = group_base(tt0 + 96);
+#pragma unroll
+        for (int q = 0; q < kDecWaves; ++q) rb[q] = group_base(tt0 + 32 * q);
     };
     auto row_of = [&](int t) -> int {
-        const int g4 = t >> 5;
-        const int base = g4 == 0 ? rb0 : g4 == 1 ? rb1 : g4 == 2 ? rb2 : rb3;
+        const int base = rb[t >> 5];
         return base < 0 ? 0 : min(base + (t & 31), pos);
     };
-    TileRegs<T, D, kDecTT, 256> regs;
+    TileRegs<T, D, kDecTT, kDecThreads> regs;
     set_bases(t_begin);
     regs.load(Kg, Vg, row_of, tid);
     for (int k = 0; k < ntiles; ++k) {
@@ -305,7 +307,7 @@ __global__ __launch_bounds__(256, 2) void decode_attn_kernel(DecodeParams p) {
             sacc[i] = v;
             mx = fmaxf(mx, v);
         }
-        mx = fmaxf(mx, shfl_xor(mx, 32));
+        mx = pair32_max(mx);
         // lazy rescaling: the reference maximum moves only when the tile maximum
         // exceeds it by more than 8 (probabilities stay <= 2^8 in between)
         const bool grow = mx > m_run + 8.f;
@@ -344,9 +346,9 @@ __global__ __launch_bounds__(256, 2) void decode_attn_kernel(DecodeParams p) {
     // merge the 4 wavefronts' partial softmax states in LDS
     __syncthreads();
     float* s_o = reinterpret_cast<float*>(smem);               // [4][32][D]
-    float* s_m = s_o + 4 * 32 * D;                             // [4][32]
-    float* s_l = s_m + 4 * 32;                                 // [4][32]
-    const float l_tot = l_run + shfl_xor(l_run, 32);
+    float* s_m = s_o + kDecWaves * 32 * D;                     // [waves][32]
+    float* s_l = s_m + kDecWaves * 32;                         // [waves][32]
+    const float l_tot = pair32_sum(l_run);
     if (hl == 0) { s_m[wid * 32 + l32] = m_run; s_l[wid * 32 + l32] = l_tot; }
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
@@ -357,13 +359,13 @@ __global__ __launch_bounds__(256, 2) void decode_attn_kernel(DecodeParams p) {
         }
     __syncthreads();
     float* part = p.partials + ((grp * p.max_slices + slice) * (size_t)g) * (D + 2);
-    for (int q = tid; q < g * D; q += 256) {
+    for (int q = tid; q < g * D; q += kDecThreads) {
         const int pr = q / D, d = q % D;
         float mstar = -INFINITY;
-        for (int w = 0; w < 4; ++w) mstar = fmaxf(mstar, s_m[w * 32 + pr]);
+        for (int w = 0; w < kDecWaves; ++w) mstar = fmaxf(mstar, s_m[w * 32 + pr]);
         const float mu = (mstar == -INFINITY) ? 0.f : mstar;
         float o = 0.f, l = 0.f;
-        for (int w = 0; w < 4; ++w) {
+        for (int w = 0; w < kDecWaves; ++w) {
             const float f = fast_exp2(s_m[w * 32 + pr] - mu);
             o += f * s_o[(w * 32 + pr) * D + d];
             l += f * s_l[w * 32 + pr];
@@ -428,8 +430,8 @@ void decode_geometry(int L_cap, int kbar_cap, int B, int* T_route, int* slice_to
                      int* max_slices) {
     const int tr = min((L_cap - 1) / B, kbar_cap);
     *T_route = tr;
-    *slice_tokens = 1024;
-    *max_slices = ((tr + 1) * B + 1024 - 1) / 1024;
+    *slice_tokens = kDecSlice;
+    *max_slices = ((tr + 1) * B + kDecSlice - 1) / kDecSlice;
 }
 
 int pmode_of(float alpha);
@@ -448,6 +450,7 @@ static void launch_dec_route(const DecodeParams& p, int b, hipStream_t s) {
 template <typename T, int D>
 static hipError_t launch_decode_t(const DecodeParams& p, const DecodeArgs& a, hipStream_t s) {
     constexpr size_t lds = TileGeom<T, D, kDecTT>::BYTES + 64 * 8;
+    static_assert(TileGeom<T, D, kDecTT>::BYTES >= kDecWaves * (32 * D + 64) * 4, "LDS merge space");
     static hipError_t configured = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_attn_kernel<T, D>),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (configured != hipSuccess) return configured;
@@ -457,7 +460,7 @@ static hipError_t launch_decode_t(const DecodeParams& p, const DecodeArgs& a, hi
     }
     if (p.T_route <= 256) launch_dec_route<4>(p, a.b, s);
     else launch_dec_route<16>(p, a.b, s);
-    hipLaunchKernelGGL((decode_attn_kernel<T, D>), dim3(p.max_slices, p.h_kv, a.b), dim3(256), lds, s, p);
+    hipLaunchKernelGGL((decode_attn_kernel<T, D>), dim3(p.max_slices, p.h_kv, a.b), dim3(kDecThreads), lds, s, p);
     hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(p.h_q, a.b), dim3(256),
                        (size_t)p.max_slices * sizeof(float), s, p);
     return hipGetLastError();

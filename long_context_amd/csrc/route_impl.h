@@ -83,8 +83,8 @@ __device__ __forceinline__ float solve_tau(float (&sv)[NT][4], int nt, float pex
                 for (int i = 0; i < 4; ++i) accum_pow<PM>(fmaxf(sv[t][i] - tau, 0.f), pexp, a0, a1);
             }
         }
-        a0 += shfl_xor(a0, 16); a1 += shfl_xor(a1, 16);
-        a0 += shfl_xor(a0, 32); a1 += shfl_xor(a1, 32);
+        a0 = pair32_sum(pair16_sum(a0));
+        a1 = pair32_sum(pair16_sum(a1));
         float delta;
         if (PM == 1) {
             delta = (a1 - 1.f) / a0;               // f = sum t - 1, f' = -|{t > 0}|
@@ -309,8 +309,7 @@ __global__ __launch_bounds__(512) void entmax_route_kernel(RouteParams p) {
                 }
             }
         }
-        smax = fmaxf(smax, shfl_xor(smax, 16));
-        smax = fmaxf(smax, shfl_xor(smax, 32));
+        smax = pair32_max(pair16_max(smax));
         // thresholded argument shifted by the row maximum: y = (α-1)γ(z̄ - max z̄) <= 0
 #pragma unroll
         for (int t = 0; t < NT; ++t)
