@@ -128,7 +128,7 @@ dash_status dash_route(const void* Q, int q_dtype, const float* kbar,
     const int T = n / B;
     if (kbar_cap < T) return fail(DASH_ERR_SHAPE, "kbar_cap %d < floor(n/B) = %d", kbar_cap, T);
     if (list_cap < T) return fail(DASH_ERR_SHAPE, "list_cap %d < floor(n/B) = %d", list_cap, T);
-    if (dash::route_tiles_bucket(T) == 0) return fail(DASH_ERR_UNSUPPORTED, "%d chunks exceed the router's 1024", T);
+    if (dash::route_tiles_bucket(T) == 0) return fail(DASH_ERR_UNSUPPORTED, "%d chunks exceed the router's 2048", T);
     dash::RouteArgs a{Q, q_dtype == DASH_BF16, kbar, b, h_q, h_kv, n, kbar_cap, d, B, causal, list_cap,
                       alpha, gamma, sigma, idx, bias, cnt, w_out};
     return from_hip(dash::launch_route(a, (hipStream_t)stream), "entmax_route_kernel");
@@ -193,7 +193,7 @@ dash_status dash_attend_decode(const void* Q, const void* Kc, const void* Vc, in
     if (B % 32 != 0) return fail(DASH_ERR_UNSUPPORTED, "decode attention needs B %% 32 == 0 (B = %d)", B);
     if (L_cap < 1 || kbar_cap < 0) return fail(DASH_ERR_SHAPE, "L_cap must be >= 1 and kbar_cap >= 0");
     const DecodeLayout Lo = decode_layout(b, h_q, h_kv, L_cap, kbar_cap, d, B);
-    if (Lo.T_ws > 1024) return fail(DASH_ERR_UNSUPPORTED, "%d routable chunks exceed the decode router's 1024", Lo.T_ws);
+    if (Lo.T_ws > 2048) return fail(DASH_ERR_UNSUPPORTED, "%d routable chunks exceed the decode router's 2048", Lo.T_ws);
     if (given == 3 && list_cap < Lo.T_route) return fail(DASH_ERR_SHAPE, "list_cap %d < routable chunks %d", list_cap, Lo.T_route);
     if (!ws || ws_bytes < Lo.total) return fail(DASH_ERR_WORKSPACE, "decode needs %zu workspace bytes, got %zu", Lo.total, ws ? ws_bytes : (size_t)0);
     char* w = static_cast<char*>(ws);

@@ -6,7 +6,8 @@
 //                          one wavefront per 16 chunks x the g heads of a group;
 //                          spread over many workgroups because this step is bound
 //                          by reading the fp32 summaries.
-//   decode_route_kernel    one workgroup per (b, KV group): wavefront h solves the
+//   decode_route_kernel    one workgroup per (b, KV group), up to 2048 chunks per
+//                          row: wavefront h solves the
 //                          entmax threshold of head h over all visible chunks
 //                          (Newton on the p-norm form, as in the prefill router),
 //                          the group average is taken in LDS in a fixed head order,
@@ -115,7 +116,8 @@ __device__ __forceinline__ float dec_pow(float t, float pexp) {
 template <int VPL, int PM>
 __global__ __launch_bounds__(1024) void decode_route_kernel(DecodeParams p) {
     constexpr int TMAX = VPL * 64;
-    __shared__ float wl[16][TMAX];
+    extern __shared__ float dyn_wl[];                 // [16][TMAX] per-head weights
+    auto wl = reinterpret_cast<float (*)[TMAX]>(dyn_wl);
     __shared__ float red[2][16];
     __shared__ int wcnt[16];
     const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
@@ -436,14 +438,23 @@ void decode_geometry(int L_cap, int kbar_cap, int B, int* T_route, int* slice_to
 
 int pmode_of(float alpha);
 
+template <int VPL, int PM>
+static hipError_t launch_dec_route_pm(const DecodeParams& p, int b, hipStream_t s) {
+    constexpr size_t lds = (size_t)16 * VPL * 64 * sizeof(float);
+    static hipError_t configured = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_route_kernel<VPL, PM>),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (configured != hipSuccess) return configured;
+    hipLaunchKernelGGL((decode_route_kernel<VPL, PM>), dim3(p.h_kv, b), dim3(1024), lds, s, p);
+    return hipSuccess;
+}
+
 template <int VPL>
-static void launch_dec_route(const DecodeParams& p, int b, hipStream_t s) {
-    dim3 grid(p.h_kv, b), block(1024);
+static hipError_t launch_dec_route(const DecodeParams& p, int b, hipStream_t s) {
     switch (p.pmode) {
-        case 1: hipLaunchKernelGGL((decode_route_kernel<VPL, 1>), grid, block, 0, s, p); break;
-        case 2: hipLaunchKernelGGL((decode_route_kernel<VPL, 2>), grid, block, 0, s, p); break;
-        case 4: hipLaunchKernelGGL((decode_route_kernel<VPL, 4>), grid, block, 0, s, p); break;
-        default: hipLaunchKernelGGL((decode_route_kernel<VPL, 0>), grid, block, 0, s, p); break;
+        case 1: return launch_dec_route_pm<VPL, 1>(p, b, s);
+        case 2: return launch_dec_route_pm<VPL, 2>(p, b, s);
+        case 4: return launch_dec_route_pm<VPL, 4>(p, b, s);
+        default: return launch_dec_route_pm<VPL, 0>(p, b, s);
     }
 }
 
@@ -458,8 +469,10 @@ static hipError_t launch_decode_t(const DecodeParams& p, const DecodeArgs& a, hi
         dim3 g1((p.T_route + 63) / 64, p.h_kv, a.b);
         hipLaunchKernelGGL((decode_scores_kernel<D>), g1, dim3(256), 0, s, p, a.Q, a.in_bf16);
     }
-    if (p.T_route <= 256) launch_dec_route<4>(p, a.b, s);
-    else launch_dec_route<16>(p, a.b, s);
+    const hipError_t er = p.T_route <= 256 ? launch_dec_route<4>(p, a.b, s)
+                        : p.T_route <= 1024 ? launch_dec_route<16>(p, a.b, s)
+                                            : launch_dec_route<32>(p, a.b, s);
+    if (er != hipSuccess) return er;
     hipLaunchKernelGGL((decode_attn_kernel<T, D>), dim3(p.max_slices, p.h_kv, a.b), dim3(kDecThreads), lds, s, p);
     hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(p.h_q, a.b), dim3(256),
                        (size_t)p.max_slices * sizeof(float), s, p);

@@ -21,8 +21,8 @@ struct RouteArgs {
     int32_t* idx; float* bias; int32_t* cnt; float* w_out;
 };
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
-// Number of 16-chunk tiles the routing kernels keep in registers for T chunks
-// (0 if T is beyond the supported range).
+// Number of 16-chunk tiles the routing kernels keep in registers per row group
+// for T chunks (0 if T is beyond the supported range of 2048 chunks).
 int route_tiles_bucket(int T);
 
 struct PrefillArgs {

@@ -8,7 +8,8 @@ int route_tiles_bucket(int T) {
     if (T <= 32) return 2;
     if (T <= 128) return 8;
     if (T <= 512) return 32;
-    if (T <= 1024) return 64;
+    if (T <= 1024) return 64;        // 32 tiles x 2 wavefronts per row group
+    if (T <= 2048) return 128;       // 32 tiles x 4 wavefronts per row group
     return 0;
 }
 

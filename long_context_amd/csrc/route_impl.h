@@ -5,11 +5,12 @@
 //   w^(r) = mean over the g heads of group r of ŵ^(h), S = {c : w_c > 0},
 //   μ = mean_{c in S} ln w_c, bias d_c = (ln w_c - μ)/σ.
 //
-// entmax_route_kernel: one wavefront handles 16 (row, head) pairs = 16/g rows x all
-// g heads of one KV group, so the GQA average is a reduction across lanes.
-//  * Logits: fp32 MFMA 16x16x4 with A = k̄ tile (16 chunks x d) and B = q (d x 16
-//    pairs); lane (kg, n) ends with chunks 16t+4kg+i of pair n, all visible chunks of
-//    a row stay in registers (the row is short: T_c = floor(n/B)).
+// entmax_route_kernel: a group of CW wavefronts handles 16 (row, head) pairs = 16/g
+// rows x all g heads of one KV group, so the GQA average is a reduction across lanes.
+//  * Logits: MFMA with A = k̄ tile (16 chunks x d) and B = q (d x 16 pairs); lane
+//    (kg, n) ends with chunks 16t+4kg+i of pair n. All visible chunks of a row stay in
+//    registers: up to 512 per wavefront, rows with more chunks are split over CW = 2
+//    or 4 wavefronts whose row maxima and Newton sums meet in LDS.
 //  * Threshold: work on y = (α-1)γ(z̄ - max z̄) <= 0 (exact shift by the row maximum)
 //    so τ lies in [-1, 0). Newton's method on g(τ) = ||[y - τ]_+||_p - 1 with
 //    p = 1/(α-1), started at τ = -1 where g >= 0: g is convex and decreasing, so the
@@ -127,33 +128,88 @@ struct KSplitStage {
     }
 };
 
-template <typename T, int D, int NT, int PM>
+// τ for rows whose chunks are split over CW cooperating wavefronts: every iteration
+// each wavefront sums its own chunks, the CW partial sums meet in LDS (double
+// buffered by iteration parity) and are added in a fixed order, so the CW wavefronts
+// of a row group take identical steps. The loop runs until every row of the
+// workgroup has converged (all wavefronts pass the same barriers).
+template <int NT, int PM, int CW>
+__device__ __forceinline__ float solve_tau_split(float (&sv)[NT][4], int nt, float pexp, bool active,
+                                                 float* xsum, int G, int gid, int cw, int n16, int kg) {
+    float tau = -1.f;
+    bool done = !active;
+    for (int it = 0; it < 100; ++it) {
+        float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            if (t < nt) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) accum_pow<PM>(fmaxf(sv[t][i] - tau, 0.f), pexp, a0, a1);
+            }
+        }
+        a0 = pair32_sum(pair16_sum(a0));
+        a1 = pair32_sum(pair16_sum(a1));
+        float* buf = xsum + ((size_t)((it & 1) * G + gid) * CW) * 32;   // [CW][16][2]
+        if (kg == 0) { buf[(cw * 16 + n16) * 2] = a0; buf[(cw * 16 + n16) * 2 + 1] = a1; }
+        __syncthreads();
+        a0 = 0.f; a1 = 0.f;
+#pragma unroll
+        for (int k = 0; k < CW; ++k) { a0 += buf[(k * 16 + n16) * 2]; a1 += buf[(k * 16 + n16) * 2 + 1]; }
+        float delta;
+        if (PM == 1) {
+            delta = (a1 - 1.f) / a0;
+        } else {
+            float nrm = (PM == 2) ? sqrtf(a1) : (PM == 4) ? sqrtf(sqrtf(a1)) : fast_exp2(fast_log2(a1) / pexp);
+            delta = (nrm - 1.f) * (a1 / nrm) / a0;
+        }
+        if (!(a0 > 0.f)) delta = 0.f;
+        if (!done) tau += delta;
+        done = done || !(fabsf(delta) > 1e-6f);
+        if (!__syncthreads_or(!done)) break;
+    }
+    return tau;
+}
+
+// One workgroup = G groups of 16 (row, head) pairs (16/g rows x the g heads of a
+// group each) times CW wavefronts per group: wavefront cw of a group holds chunks
+// [cw*16*NT, (cw+1)*16*NT) of its rows in registers (CW > 1 for long rows).
+template <typename T, int D, int NT, int PM, int CW>
 __global__ __launch_bounds__(512) void entmax_route_kernel(RouteParams p) {
-    constexpr int WS = NT * 16;                       // LDS floats per row of weights
+    constexpr int WSW = NT * 16;                      // chunks held by one wavefront
+    constexpr int WS = CW * WSW;                      // LDS floats per row of weights
     typedef KSplitStage<D> KS;
     typedef __bf16 b8 __attribute__((ext_vector_type(8)));
     extern __shared__ __attribute__((aligned(16))) char rsm[];
     const int W = blockDim.x >> 6;
-    const int wid = threadIdx.x >> 6;
-    const int lane = threadIdx.x & 63;
+    const int G = W / CW;
+    const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int gid = wid / CW, cw = wid % CW;
     const int n16 = lane & 15, kg = lane >> 4;
     const int g = p.g, lg = p.log2g;
-    const int R = 16 >> lg;                           // rows per wave
+    const int R = 16 >> lg;                           // rows per group
     const int r = blockIdx.y, bi = blockIdx.z;
-    // all rows of the workgroup lie in one chunk (W*R divides B): one visible range
-    const int wg_row0 = blockIdx.x * W * R;
-    const int row0 = wg_row0 + wid * R;
+    // all rows of the workgroup lie in one chunk (G*R divides B): one visible range
+    const int wg_row0 = blockIdx.x * G * R;
+    const int row0 = wg_row0 + gid * R;
     const bool wave_live = row0 < p.n;
     char* kstage = rsm;                                              // 2 stages (bf16 path)
-    float* wl = reinterpret_cast<float*>(rsm + (sizeof(T) == 2 ? 2 * KS::BYTES : 0)) + wid * R * WS;
+    float* wl_all = reinterpret_cast<float*>(rsm + (sizeof(T) == 2 ? 2 * KS::BYTES : 0));
+    float* wl = wl_all + gid * R * WS;
+    float* xred = wl_all + G * R * WS;                // [G][CW][16] row maxima of each wavefront
+    float* xsum = xred + G * CW * 16;                 // [2][G][CW][16][2] Newton partial sums
     const int nvis = p.causal ? min(wg_row0 / p.B, p.T_c) : p.T_c;
     const int my_row = row0 + (n16 >> lg);
     const int my_head = r * g + (n16 & (g - 1));
     const bool row_ok = my_row < p.n;
-    const int nt = (nvis + 15) >> 4;
+    const int c_lo = cw * WSW;                        // first chunk of this wavefront
+    const int nt = min(max((nvis - c_lo + 15) >> 4, 0), NT);   // its tiles holding visible chunks
 
     float sv[NT][4];
-    if (nvis > 0) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sv[t][i] = -INFINITY;
+    if (nvis > 0) {                                   // workgroup-uniform
         float smax = -INFINITY;
         if constexpr (sizeof(T) == 2) {
             // bf16 queries are exact in bf16; k̄ = hi + mid + lo (three bf16 terms, exact up
@@ -172,11 +228,11 @@ __global__ __launch_bounds__(512) void entmax_route_kernel(RouteParams p) {
                 }
             }
             // the workgroup loads each stage of 32 summaries once (fp32, coalesced),
-            // splits it in registers and stores it to LDS; the next stage is prefetched
+            // splits it in registers and stores it to LDS; the next stage is prefetched.
+            // Stage st holds chunks 32st..32st+31 = tiles 2st, 2st+1, which belong to
+            // wavefront cw = st / (NT/2) of every group.
             const float* kb = p.kbar + ((size_t)bi * p.h_kv + r) * (size_t)p.kbar_cap * D;
             const int nst = (nvis + KS::CH - 1) / KS::CH;
-            // one piece = 8 consecutive fp32 of one chunk; a workgroup of 8 waves covers a
-            // stage in one round (prefetched), smaller workgroups take extra rounds
             constexpr int PPT = (KS::PIECES + 511) / 512;
             f32x4 pre[PPT][2];
             auto piece_src = [&](int st, int q) {
@@ -222,50 +278,44 @@ __global__ __launch_bounds__(512) void entmax_route_kernel(RouteParams p) {
                 }
             };
             load_stage(0);
+            for (int rep = 0; rep < CW; ++rep) {
 #pragma unroll
-            for (int st = 0; st < (NT + 1) / 2; ++st) {
-                if (st < nst) {
-                    store_stage(st);
-                    __syncthreads();
-                    if (st + 1 < nst) load_stage(st + 1);
-                    const char* stg = kstage + (st & 1) * KS::BYTES;
+                for (int sl = 0; sl < NT / 2; ++sl) {
+                    const int st = rep * (NT / 2) + sl;
+                    if (st < nst) {                   // workgroup-uniform
+                        store_stage(st);
+                        __syncthreads();
+                        if (st + 1 < nst) load_stage(st + 1);
+                        // no trailing barrier: stage st+1 fills the other buffer, and the
+                        // barrier of stage st+1 orders this stage's reads before stage st+2
+                        if (rep == cw) {
+                            const char* stg = kstage + (st & 1) * KS::BYTES;
 #pragma unroll
-                    for (int tt = 0; tt < 2; ++tt) {
-                        const int t = 2 * st + tt;
-                        if (t < NT) {
-                            if (t < nt) {
-                                const int cl = 16 * tt + n16;            // chunk inside the stage
-                                f32x4 acc[3];
+                            for (int tt = 0; tt < 2; ++tt) {
+                                const int t = 2 * sl + tt;
+                                if (t < nt) {
+                                    const int cl = 16 * tt + n16;            // chunk inside the stage
+                                    f32x4 acc[3];
 #pragma unroll
-                                for (int h = 0; h < 3; ++h) {
-                                    acc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+                                    for (int h = 0; h < 3; ++h) {
+                                        acc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                                    for (int s = 0; s < D / 32; ++s) {
-                                        const b8 a = *reinterpret_cast<const b8*>(stg + KS::off(cl, h, 4 * s + kg));
-                                        acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[s], acc[h], 0, 0, 0);
+                                        for (int s = 0; s < D / 32; ++s) {
+                                            const b8 a = *reinterpret_cast<const b8*>(stg + KS::off(cl, h, 4 * s + kg));
+                                            acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[s], acc[h], 0, 0, 0);
+                                        }
+                                    }
+#pragma unroll
+                                    for (int i = 0; i < 4; ++i) {
+                                        const int ch = c_lo + t * 16 + 4 * kg + i;
+                                        const float v = acc[0][i] + (acc[1][i] + acc[2][i]);
+                                        sv[t][i] = (ch < nvis) ? v : -INFINITY;
+                                        smax = fmaxf(smax, sv[t][i]);
                                     }
                                 }
-#pragma unroll
-                                for (int i = 0; i < 4; ++i) {
-                                    const int ch = t * 16 + 4 * kg + i;
-                                    const float v = acc[0][i] + (acc[1][i] + acc[2][i]);
-                                    sv[t][i] = (ch < nvis) ? v : -INFINITY;
-                                    smax = fmaxf(smax, sv[t][i]);
-                                }
-                            } else {
-#pragma unroll
-                                for (int i = 0; i < 4; ++i) sv[t][i] = -INFINITY;
                             }
                         }
                     }
-                    // no trailing barrier: stage st+1 fills the other buffer, and the barrier
-                    // of stage st+1 orders this stage's reads before stage st+2 refills it
-                } else {
-#pragma unroll
-                    for (int tt = 0; tt < 2; ++tt)
-                        if (2 * st + tt < NT)
-#pragma unroll
-                            for (int i = 0; i < 4; ++i) sv[2 * st + tt][i] = -INFINITY;
                 }
             }
         } else {
@@ -286,7 +336,7 @@ __global__ __launch_bounds__(512) void entmax_route_kernel(RouteParams p) {
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
                 if (t < nt) {
-                    const int c = min(t * 16 + n16, nvis - 1);   // A row = chunk
+                    const int c = min(c_lo + t * 16 + n16, nvis - 1);   // A row = chunk
                     const float* krow = kb + (size_t)c * D;
                     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -299,24 +349,30 @@ __global__ __launch_bounds__(512) void entmax_route_kernel(RouteParams p) {
                     }
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const int ch = t * 16 + 4 * kg + i;
+                        const int ch = c_lo + t * 16 + 4 * kg + i;
                         sv[t][i] = (ch < nvis) ? acc[i] : -INFINITY;
                         smax = fmaxf(smax, sv[t][i]);
                     }
-                } else {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) sv[t][i] = -INFINITY;
                 }
             }
         }
         smax = pair32_max(pair16_max(smax));
+        if constexpr (CW > 1) {
+            if (kg == 0) xred[(gid * CW + cw) * 16 + n16] = smax;
+            __syncthreads();
+            smax = -INFINITY;
+#pragma unroll
+            for (int k = 0; k < CW; ++k) smax = fmaxf(smax, xred[(gid * CW + k) * 16 + n16]);
+        }
         // thresholded argument shifted by the row maximum: y = (α-1)γ(z̄ - max z̄) <= 0
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
             for (int i = 0; i < 4; ++i) sv[t][i] = p.cs * (sv[t][i] - smax);
 
-        const float tau = solve_tau<NT, PM>(sv, nt, p.pexp, row_ok && wave_live);
+        float tau;
+        if constexpr (CW == 1) tau = solve_tau<NT, PM>(sv, nt, p.pexp, row_ok && wave_live);
+        else tau = solve_tau_split<NT, PM, CW>(sv, nt, p.pexp, row_ok && wave_live, xsum, G, gid, cw, n16, kg);
         // per-head weights, then the group average across the g lanes of each row
         const float inv_g = 1.f / (float)g;
 #pragma unroll
@@ -338,18 +394,23 @@ __global__ __launch_bounds__(512) void entmax_route_kernel(RouteParams p) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) sv[t][i] = 0.f;
     }
-    if (!wave_live) return;                           // no barrier follows
     // group weights to LDS: the first lane of each row writes its chunks
-    if ((n16 & (g - 1)) == 0) {
+    if (wave_live && (n16 & (g - 1)) == 0) {
         float* wr = wl + (n16 >> lg) * WS;
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) wr[t * 16 + 4 * kg + i] = sv[t][i];
+            for (int i = 0; i < 4; ++i) wr[c_lo + t * 16 + 4 * kg + i] = sv[t][i];
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if constexpr (CW > 1) {
+        __syncthreads();                              // the rows' chunks come from CW wavefronts
+        if (cw != 0) return;
+    } else {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+    if (!wave_live) return;                           // no barrier follows
 
     // compaction: ascending chunk ids of the support, with d = (ln w - μ)/σ
     const size_t rowbase = ((size_t)bi * p.h_kv + r) * p.n;
@@ -387,29 +448,33 @@ __global__ __launch_bounds__(512) void entmax_route_kernel(RouteParams p) {
     }
 }
 
-// Waves per workgroup: up to 8; all rows of a workgroup must share one chunk, and
-// the LDS (two summary stages for bf16 queries plus the rows' weights) must fit.
-template <typename T, int D, int NT>
-inline int route_waves_per_block(int R, int B, size_t* lds) {
+// Workgroup geometry: up to 8 wavefronts = G groups x CW; all rows of a workgroup
+// must share one chunk, and the LDS (two summary stages for bf16 queries, the rows'
+// weights, the cross-wavefront partials) must fit 64 KiB.
+template <typename T, int D, int NT, int CW>
+inline int route_groups_per_block(int R, int B, size_t* lds) {
     const size_t stage = sizeof(T) == 2 ? 2 * (size_t)KSplitStage<D>::BYTES : 0;
-    int w = 8;
-    while (w > 1 && (B % (w * R) != 0 || stage + (size_t)w * R * NT * 16 * 4 > 64 * 1024)) w >>= 1;
-    *lds = stage + (size_t)w * R * NT * 16 * 4;
-    return w;
+    auto bytes = [&](int G) {
+        return stage + (size_t)G * R * CW * NT * 16 * 4 + (size_t)G * CW * 16 * 4 + (size_t)2 * G * CW * 32 * 4;
+    };
+    int G = 8 / CW;
+    while (G > 1 && (B % (G * R) != 0 || bytes(G) > 64 * 1024)) G >>= 1;
+    *lds = bytes(G);
+    return G;
 }
 
-template <typename T, int D, int NT>
+template <typename T, int D, int NT, int CW>
 static hipError_t launch_route_nt(const RouteParams& p, int b, hipStream_t s) {
     const int R = 16 / p.g;
     size_t lds = 0;
-    const int W = route_waves_per_block<T, D, NT>(R, p.B, &lds);
-    const int waves = (p.n + R - 1) / R;
-    dim3 grid((waves + W - 1) / W, p.h_kv, b), block(64 * W);
+    const int G = route_groups_per_block<T, D, NT, CW>(R, p.B, &lds);
+    const int groups = (p.n + R - 1) / R;
+    dim3 grid((groups + G - 1) / G, p.h_kv, b), block(64 * G * CW);
     switch (p.pmode) {
-        case 1: hipLaunchKernelGGL((entmax_route_kernel<T, D, NT, 1>), grid, block, lds, s, p); break;
-        case 2: hipLaunchKernelGGL((entmax_route_kernel<T, D, NT, 2>), grid, block, lds, s, p); break;
-        case 4: hipLaunchKernelGGL((entmax_route_kernel<T, D, NT, 4>), grid, block, lds, s, p); break;
-        default: hipLaunchKernelGGL((entmax_route_kernel<T, D, NT, 0>), grid, block, lds, s, p); break;
+        case 1: hipLaunchKernelGGL((entmax_route_kernel<T, D, NT, 1, CW>), grid, block, lds, s, p); break;
+        case 2: hipLaunchKernelGGL((entmax_route_kernel<T, D, NT, 2, CW>), grid, block, lds, s, p); break;
+        case 4: hipLaunchKernelGGL((entmax_route_kernel<T, D, NT, 4, CW>), grid, block, lds, s, p); break;
+        default: hipLaunchKernelGGL((entmax_route_kernel<T, D, NT, 0, CW>), grid, block, lds, s, p); break;
     }
     return hipGetLastError();
 }
@@ -417,10 +482,11 @@ static hipError_t launch_route_nt(const RouteParams& p, int b, hipStream_t s) {
 template <typename T, int D>
 static hipError_t launch_route_d(const RouteParams& p, int b, hipStream_t s) {
     switch (route_tiles_bucket(p.T_c)) {
-        case 2: return launch_route_nt<T, D, 2>(p, b, s);
-        case 8: return launch_route_nt<T, D, 8>(p, b, s);
-        case 32: return launch_route_nt<T, D, 32>(p, b, s);
-        default: return launch_route_nt<T, D, 64>(p, b, s);
+        case 2: return launch_route_nt<T, D, 2, 1>(p, b, s);
+        case 8: return launch_route_nt<T, D, 8, 1>(p, b, s);
+        case 32: return launch_route_nt<T, D, 32, 1>(p, b, s);
+        case 64: return launch_route_nt<T, D, 32, 2>(p, b, s);
+        default: return launch_route_nt<T, D, 32, 4>(p, b, s);
     }
 }
 

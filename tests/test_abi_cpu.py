@@ -61,7 +61,7 @@ def _route(dash, **kw):
     (dict(gamma=float("inf")), 3), (dict(sigma=0.0), 3), (dict(sigma=float("nan")), 3),
     (dict(qdt=7), 3), (dict(causal=2), 3),
     (dict(d=96), 4), (dict(B=24), 4), (dict(h_q=64, h_kv=2), 4), (dict(h_q=6, h_kv=2), 4),
-    (dict(n=65 * 1024, cap=1040, list_cap=1040), 4),
+    (dict(n=129 * 1024, cap=2064, list_cap=2064), 4),
 ])
 def test_route_validation(dash, kw, status):
     assert _route(dash, **kw) == status
@@ -133,7 +133,7 @@ def test_decode_workspace_checks(dash):
     assert _decode(dash, need, idx=P, bias=P, cnt=P, list_cap=10) == dash.DASH_ERR_SHAPE
     assert _decode(dash, need, alpha=0.5) == dash.DASH_ERR_PARAM
     assert _decode(dash, need, B=48) == dash.DASH_ERR_UNSUPPORTED
-    assert _decode(dash, need, L=300000) == dash.DASH_ERR_UNSUPPORTED
+    assert _decode(dash, need, L=300000) == dash.DASH_ERR_UNSUPPORTED      # 2343 chunks > 2048
 
 
 def test_workspace_sizes(dash):

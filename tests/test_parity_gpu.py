@@ -223,6 +223,45 @@ def test_decode_equals_last_prefill_row():
 
 
 # ------------------------------------------------------------------------------------
+# Rows longer than one router wavefront holds (512 chunks): the chunks of a row are
+# split over 2 or 4 cooperating wavefronts (prefill) / more values per lane (decode)
+# ------------------------------------------------------------------------------------
+
+LONG = [
+    # dtype, b, h_q, h_kv, d, n, B, alpha, gamma, sigma
+    ("bf16", 1, 32, 2, 128, 20032, 32, 1.5, 4.0, 1.0),     # 626 chunks: 2 wavefronts per row group
+    ("bf16", 1, 16, 2, 128, 40000, 32, 1.5, 6.0, 1.0),     # 1250 chunks: 4 wavefronts
+    ("f32", 1, 4, 2, 64, 24000, 32, 2.0, 5.0, 1.0),        # 750 chunks, fp32 queries: 2 wavefronts
+]
+
+
+@pytest.mark.parametrize("case", LONG, ids=[f"{c[0]}-g{c[2] // c[3]}-n{c[5]}-B{c[6]}" for c in LONG])
+def test_prefill_long_rows(case):
+    G = _gu()
+    dtype, b, h_q, h_kv, d, n, B, alpha, gamma, sigma = case
+    w = inputs.make_prefill(b=b, h_q=h_q, h_kv=h_kv, d=d, n=n, B=B, alphas=(alpha,), gamma=gamma,
+                            sigma=sigma, causal=True, dtype=dtype, seed=5)
+    _log(f"long prefill case {case}")
+    g = G.gpu_prefill(w)
+    rows = _sample_rows(w.n, w.B, 40, 9)
+    kb, rt, Oref = G.oracle_prefill_rows(w, rows)
+    nex, tot = G.compare_route(g, rt, rows, w.n // w.B)
+    err = G.compare_out(g["O"][:, :, rows].cpu().numpy(), Oref, rt["margin"] <= G.MARGIN, w.g, dtype)
+    _log(f"long prefill {case}: exempt {nex}/{tot}, output error {err:.3e}")
+
+
+@pytest.mark.parametrize("L", [40000, 35232])
+def test_decode_long_rows(L):
+    seq = [L, L - 1000]
+    w = inputs.make_decode(b=2, h_q=32, h_kv=2, d=128, L=L, B=32, alphas=(1.5,), gamma=3.0,
+                           sigma=1.0, dtype="bf16", seed=6, seq_len=seq)
+    _log(f"long decode L={L} seq={seq}")
+    g = gpu_decode(w, seq)
+    nex, err = check_decode(w, seq, g)
+    _log(f"long decode L={L}: exempt {nex}, output error {err:.3e}")
+
+
+# ------------------------------------------------------------------------------------
 # The five reference workloads at full size (sampled rows)
 # ------------------------------------------------------------------------------------
 
