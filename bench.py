@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--only", choices=["prefill", "decode", "both"], default="both")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (HBM counter calibration)")
+    ap.add_argument("--efficiency", action="store_true",
+                    help="only run the replicas of the pages' efficiency operating points")
     return ap.parse_args()
 
 
@@ -126,6 +128,14 @@ class Prefill:
         w = self.w
         sup = int(self.cnt.to(self.torch.int64).sum().item())
         return (w.Q.size * 2 + w.b * w.h_kv * self.T * w.d * 4 + sup * 8 + w.b * w.h_kv * w.n * 4)
+
+    def group_sparsity(self):
+        """Group sparsity of the last routing (rows with at least one visible chunk)."""
+        torch, w = self.torch, self.w
+        pos = torch.arange(w.n, device="cuda")
+        vis = torch.clamp(pos // w.B, max=self.T)
+        sup = self.cnt.to(torch.int64).sum().item()
+        return 1.0 - sup / max((vis.sum() * w.h_kv * w.b).item(), 1)
 
     def stats(self):
         """Work of the last routing (bookkeeping outside the timed region).
@@ -258,6 +268,95 @@ def cpu_baseline(w, rows_n):
                       f"CPUs; tok/s = rows / time"}
 
 
+# Speedups over dense FlashAttention printed at these operating points (paper
+# review section 六, 6.2 efficiency benchmarks table; other hardware, context only).
+PAGES_SPEEDUP = {("prefill", 16, 0.75): 1.34, ("prefill", 96, 0.9375): 3.09,
+                 ("decode", 96, 0.75): 1.96, ("decode", 96, 0.9375): 3.36}
+
+
+def sdpa_time(torch, q, k, v, causal, steps):
+    """Median ms of torch's fused dense attention (flash / memory-efficient kernels
+    only, bf16), the dense baseline of the efficiency table; None if neither fused
+    kernel takes these shapes."""
+    import torch.nn.functional as F
+    from torch.nn.attention import sdpa_kernel, SDPBackend
+    fused = [SDPBackend.FLASH_ATTENTION, SDPBackend.EFFICIENT_ATTENTION]
+
+    def call():
+        with sdpa_kernel(fused):
+            return F.scaled_dot_product_attention(q, k, v, is_causal=causal)
+    try:
+        call()
+    except RuntimeError as e:
+        print(f"[bench] fused SDPA unavailable: {e}", file=sys.stderr, flush=True)
+        return None
+    fn = lambda ev: (ev and ev[0].record(), call(), ev and ev[1].record())
+    return float(np.median(time_events(torch, fn, 2, steps, 1)[0]))
+
+
+def efficiency(torch, dash, inputs, steps):
+    """DashAttention at the efficiency operating points (prefill 16K / 96K at b=1,
+    decode 96K at b=24, B=64, group sparsity set through γ) against two dense
+    baselines: torch's fused attention, and these kernels with every chunk routed
+    (prefill: full lists, no routing; decode: γ≈0, routing included)."""
+    rows = []
+    for n in (16 * 1024, 96 * 1024):
+        targets = [t for t in inputs.EFFICIENCY_SPARSITY
+                   if (f"prefill_{n // 1024}k", t) in inputs.GAMMA_EFFICIENCY]
+        w = inputs.efficiency_prefill(n)
+        pre = Prefill(w, torch, dash)
+        di, db, dc = dense_lists(pre, torch)
+        Od = torch.empty_like(pre.O)
+        fn = lambda ev: (ev and ev[0].record(),
+                         dash.dash_attend_prefill(pre.Q, pre.K, pre.V, di, db, dc, Od, w.B, True, ws=pre.ws),
+                         ev and ev[1].record())
+        td = float(np.median(time_events(torch, fn, 2, steps, 1)[0]))
+        del di, db, dc, Od
+        g = w.h_q // w.h_kv                  # query head h reads KV head h // g
+        tf = sdpa_time(torch, pre.Q, pre.K.repeat_interleave(g, 1), pre.V.repeat_interleave(g, 1),
+                       True, steps)
+        torch.cuda.empty_cache()
+        for t in targets:
+            w.gamma = inputs.GAMMA_EFFICIENCY[(f"prefill_{n // 1024}k", t)]
+            seg, _ = time_events(torch, lambda ev: pre.run(1.5, ev), 4, steps, 1)
+            ts = float(np.median(seg.sum(1)))
+            st = pre.stats() if n <= 16 * 1024 else None
+            sp = st["sparsity"] if st else pre.group_sparsity()
+            rows.append(dict(mode="prefill", context=f"{n // 1024}K", batch=1, target_sparsity=t,
+                             sparsity=sp, gamma=w.gamma, ms=ts, stage1_ms=float(np.median(seg[:, 1])),
+                             stage2_ms=float(np.median(seg[:, 2])), dense_self_ms=td, dense_sdpa_ms=tf,
+                             speedup_vs_self=td / ts, speedup_vs_sdpa=tf / ts if tf else None,
+                             pages_speedup=PAGES_SPEEDUP.get(("prefill", n // 1024, t))))
+            print(f"[bench] efficiency {rows[-1]}", file=sys.stderr, flush=True)
+        del pre
+        torch.cuda.empty_cache()
+    w = inputs.efficiency_decode()
+    dd = Decode(w, torch, dash)
+    w.gamma = 1e-3                          # near-uniform weights: every chunk routed, d = 0
+    td = float(np.median(time_events(torch, dd.run, 2, steps, 1)[0]))
+    dense_cnt = dd.bytes_per_step()[1]
+    g = w.h_q // w.h_kv                      # a decode query sees every key: the g heads of
+    qg = dd.Q.view(w.b, w.h_kv, g, w.d)      # a group become g query rows of one KV head
+    tf = sdpa_time(torch, qg, dd.K, dd.V, False, steps)
+    for t in inputs.EFFICIENCY_SPARSITY:
+        key = (f"decode_{w.n // 1024}k_b{w.b}", t)
+        if key not in inputs.GAMMA_EFFICIENCY:
+            continue
+        w.gamma = inputs.GAMMA_EFFICIENCY[key]
+        tt = float(np.median(time_events(torch, dd.run, 2, steps, 1)[0]))
+        cnt = dd.bytes_per_step()[1]
+        vis = (w.seq_len - 1) // w.B
+        sp = 1.0 - cnt.sum() / (vis[:, None] * np.ones_like(cnt)).sum()
+        rows.append(dict(mode="decode", context=f"{w.n // 1024}K", batch=w.b, target_sparsity=t,
+                         sparsity=float(sp), gamma=w.gamma, us=tt * 1e3, dense_self_us=td * 1e3,
+                         dense_self_routed=int(dense_cnt.sum()),
+                         dense_sdpa_us=tf * 1e3 if tf else None,
+                         speedup_vs_self=td / tt, speedup_vs_sdpa=tf / tt if tf else None,
+                         pages_speedup=PAGES_SPEEDUP.get(("decode", w.n // 1024, t))))
+        print(f"[bench] efficiency {rows[-1]}", file=sys.stderr, flush=True)
+    return rows
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -267,6 +366,11 @@ def main():
     from long_context_amd import dash, inputs
     if args.copy_calibration:
         copy_calibration(torch)
+        return
+    if args.efficiency:
+        rows = efficiency(torch, dash, inputs, max(args.steps // 2, 3))
+        print(json.dumps({"metric": "DashAttention speedup over dense at the efficiency operating points",
+                          "n_gpus": 1, "data": "synthetic", "dtype": "bf16", "efficiency": rows}), flush=True)
         return
 
     out = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,

@@ -249,6 +249,53 @@ def decode_128k_b4(seed=0) -> Workload:
     return _finish(w)
 
 
+# --------------------------------------------------------------------------------------
+# Replicas of the pages' efficiency operating points (paper review section 五,
+# efficiency table): causal prefill of 16K and 96K tokens at batch 1 and decode at 96K
+# with batch 24, chunk size 64, group sparsity 75 / 87.5 / 93.75 % reached through γ.
+# Plain N(0,1) inputs (the pages measure trained-model activations, which are not
+# available); the γ values are frozen from the oracle's routing by
+# oracle/calibrate_gamma.py (`--efficiency`).
+# --------------------------------------------------------------------------------------
+
+EFFICIENCY_SPARSITY = (0.75, 0.875, 0.9375)
+# γ per (workload, target group sparsity), bisected by the float64 oracle on sampled
+# rows (prefill: every 64th row at 16K, every 256th at 96K; decode: all 24 queries).
+# 93.75% is out of reach at 16K on these inputs: with only up to 256 visible chunks,
+# the union over 16 query heads of near-argmax weights still leaves about 11% of the
+# chunks routed (0.889 at γ = 4096).
+GAMMA_EFFICIENCY = {
+    ("prefill_16k", 0.75): 34.52, ("prefill_16k", 0.875): 304.4,
+    ("prefill_96k", 0.75): 8.819, ("prefill_96k", 0.875): 16.35, ("prefill_96k", 0.9375): 29.34,
+    ("decode_96k_b24", 0.75): 6.583, ("decode_96k_b24", 0.875): 11.07, ("decode_96k_b24", 0.9375): 19.87,
+}
+
+
+def efficiency_prefill(n, sparsity=None, seed=0, gamma=None) -> Workload:
+    """Causal prefill, bf16, b=1, 32 query / 2 KV heads, d=128, B=64, α=1.5, N(0,1)."""
+    rng = np.random.default_rng(seed)
+    b, h_q, h_kv, d, B = 1, 32, 2, 128, 64
+    Q, K, V, qbar = _draw_qkv(rng, b, h_q, h_kv, n, n, d)
+    key = (f"prefill_{n // 1024}k", sparsity)
+    gam = float(gamma) if gamma is not None else GAMMA_EFFICIENCY.get(key, 1.0)
+    return _finish(Workload(f"efficiency_prefill_{n // 1024}k", "prefill", "bf16", b, h_q, h_kv, d, n, B,
+                            (1.5,), gam, 1.0, True, Q, K, V, qbar,
+                            notes=f"target group sparsity {sparsity}"))
+
+
+def efficiency_decode(sparsity=None, seed=0, gamma=None, b=24, L=96 * 1024) -> Workload:
+    """Decode, bf16, b=24, 32 query / 2 KV heads, d=128, L=96K, B=64, α=1.5, N(0,1)."""
+    rng = np.random.default_rng(seed)
+    h_q, h_kv, d, B = 32, 2, 128, 64
+    Q, K, V, qbar = _draw_qkv(rng, b, h_q, h_kv, 1, L, d)
+    key = (f"decode_{L // 1024}k_b{b}", sparsity)
+    gam = float(gamma) if gamma is not None else GAMMA_EFFICIENCY.get(key, 1.0)
+    sl = np.full((b,), L, np.int32)
+    return _finish(Workload(f"efficiency_decode_{L // 1024}k_b{b}", "decode", "bf16", b, h_q, h_kv, d, L, B,
+                            (1.5,), gam, 1.0, True, Q, K, V, qbar, sl,
+                            notes=f"target group sparsity {sparsity}"))
+
+
 WORKLOADS = {
     "prefill_1k_fp32": prefill_1k_fp32,
     "prefill_8k_gqa8_needles": prefill_8k_gqa8_needles,
