@@ -29,7 +29,7 @@ __global__ __launch_bounds__(64 * kWaves) void sparse_prior_attn_kernel(PrefillP
     extern __shared__ __attribute__((aligned(16))) char smem[];
     char* ring = smem;                                             // 2 stages
     TileTables tabs;
-    tabs.carve(smem + 2 * S::STAGE, p.R_t, p.T_c);
+    tabs.carve(smem + 2 * S::STAGE, p.T_c);
 
     constexpr int nthr = 64 * kWaves;
     const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
@@ -45,7 +45,6 @@ __global__ __launch_bounds__(64 * kWaves) void sparse_prior_attn_kernel(PrefillP
     const T* Kg = static_cast<const T*>(p.K) + bhkv * (size_t)p.n * D;
     const T* Vg = static_cast<const T*>(p.V) + bhkv * (size_t)p.n * D;
     const int U = tabs.build(p, bhkv, row0, nvis, tid, nthr);
-    const float* btab = tabs.btab;
     const int* ulist = tabs.ulist;
 
     // ---- this lane's (row, head) pair ----
@@ -55,6 +54,8 @@ __global__ __launch_bounds__(64 * kWaves) void sparse_prior_attn_kernel(PrefillP
     const int hh = r * g + (pair & (g - 1));
     const int my_row = row0 + j;
     const bool pair_ok = wave_active && j < R_t && my_row < p.n;
+    ListCursor lc;
+    lc.init(p, bhkv * p.n + (pair_ok ? my_row : 0), pair_ok);
     Op qf[D / 16];
     if (pair_ok) {
         const T* qrow = static_cast<const T*>(p.Q) + (((size_t)bi * p.h_q + hh) * p.n + my_row) * D + 8 * hl;
@@ -76,28 +77,34 @@ __global__ __launch_bounds__(64 * kWaves) void sparse_prior_attn_kernel(PrefillP
     st.init(p, U, cq, last_row, TT);
     const int nrouted = st.nrouted, nsteps = st.nsteps, SPC = st.SPC;
     const int nmax = p.n - 1;
-    auto tile_base = [&](int k) -> int { return st.base(ulist, k); };
     TileCopier<T, D, TT, kWaves> copier;
     copier.init(wid, lane);
-    auto issue = [&](int k) { copier.issue(ring + (k & 1) * S::STAGE, Kg, Vg, tile_base(k), nmax, wid); };
+    // the tile base and chunk of each step are read from LDS two steps ahead, so
+    // that neither the cursor nor the copies wait on an LDS read
+    int tb_cur, c_cur, tb_nxt, c_nxt;
+    st.at(ulist, 0, tb_cur, c_cur);
+    st.at(ulist, 1, tb_nxt, c_nxt);
 
-    if (nsteps > 0) issue(0);
+    if (nsteps > 0) copier.issue(ring, Kg, Vg, tb_cur, nmax, wid);
     wait_tile_copies();
     __syncthreads();
     for (int k = 0; k < nsteps; ++k) {
-        if (k + 1 < nsteps) issue(k + 1);
-        const char* ktile = ring + (k & 1) * S::STAGE;
-        const char* vtile = ktile + S::BYTES;
+        // the cursor's entry arrived during the previous tile; its next load goes
+        // out ahead of the copies
         const bool routed = k < nrouted;
         float bias2 = 0.f;
         bool run = wave_active;
         if (routed && run) {
-            const int c = ulist[k / SPC];
-            bias2 = pair_ok ? btab[j * p.T_c + c] * kLog2e : -INFINITY;
+            bias2 = lc.take(c_cur, k % SPC == SPC - 1);
             run = ballot(bias2 > -INFINITY) != 0;          // some row of this wave routes c
         }
+        if (k + 1 < nsteps) copier.issue(ring + ((k + 1) & 1) * S::STAGE, Kg, Vg, tb_nxt, nmax, wid);
+        int tb_nn, c_nn;
+        st.at(ulist, k + 2, tb_nn, c_nn);
+        const char* ktile = ring + (k & 1) * S::STAGE;
+        const char* vtile = ktile + S::BYTES;
         if (run) {
-            const int tb = tile_base(k);
+            const int tb = tb_cur;
             // S^T = K Q^T: accumulator column = this lane's pair, rows = tokens
             f32x16 sacc[TT / 32];
 #pragma unroll
@@ -180,6 +187,8 @@ __global__ __launch_bounds__(64 * kWaves) void sparse_prior_attn_kernel(PrefillP
         }
         wait_tile_copies();
         __syncthreads();
+        tb_cur = tb_nxt; c_cur = c_nxt;
+        tb_nxt = tb_nn; c_nxt = c_nn;
     }
 
     const float l_tot = pair32_sum(l_run);
@@ -225,7 +234,7 @@ void prefill_tiling(int g, int B, int T_c, int d, bool bf16, int* rows, size_t* 
     for (int m = geo.max_pairs; m >= 32; m >>= 1) {
         const int R_t = m / g;
         if (R_t < 1 || B % R_t != 0) continue;
-        const size_t lds = (size_t)geo.stages * st + TileTables::bytes(R_t, T_c);
+        const size_t lds = (size_t)geo.stages * st + TileTables::bytes(T_c);
         if (lds <= kMaxLds) {
             *rows = R_t;
             *lds_bytes = lds;

@@ -1,11 +1,9 @@
 // Stage 2 prefill kernel for bf16 inputs (the method is stated in prefill_common.h).
 //
-// sparse_prior_attn_bf16_kernel: 4 wavefronts, one per SIMD, each owning 64
-// (row, head) pairs as two 32-pair blocks.
-//   * Every K or V operand read from LDS feeds one 32x32x16 MFMA per pair block,
-//     so LDS reads per flop are half of a 32-pairs-per-wavefront layout; on gfx950
-//     LDS throughput is bounded by the number of read instructions, so every
-//     operand is one 16-byte read.
+// sparse_prior_attn_bf16_kernel: NW wavefronts, each owning PBW blocks of 32
+// (row, head) pairs.
+//   * On gfx950 LDS throughput is bounded by the number of read instructions, so
+//     every MFMA operand read from LDS is one 16-byte read.
 //   * V is transposed once per call into [d][n_pad] (transpose_v_kernel): the A
 //     operand of O^T += V^T P^T (8 consecutive tokens of one d) is then a plain
 //     16-byte read of the V^T tile.
@@ -14,13 +12,10 @@
 //     (rows 8(i/4) + 4(l/32) + i%4) then holds token 16(i/8) + 8(l/32) + i%8, which
 //     is exactly the token order k-slot (l/32, e) of a k16 step needs in the B
 //     operand P^T: P leaves the accumulator in natural token order.
-//   * Within a tile the work of the two pair blocks is staggered: the S^T MFMAs of
-//     block 1 are issued together with the softmax of block 0, and the O^T MFMAs of
-//     block 0 together with the softmax of block 1, so the matrix cores and the
-//     vector ALUs of a SIMD work at the same time.
 //   * Tiles of K and V^T are copied global->LDS asynchronously into a two-stage
 //     ring (one barrier per tile); a pair block skips a routed chunk none of its
-//     rows routes to.
+//     rows routes to. Each lane finds its row's bias by walking the row's routed
+//     list alongside the tile's union of chunks (no per-row table in LDS).
 #include "kernels.h"
 #include "prefill_common.h"
 
@@ -133,7 +128,7 @@ __global__ __launch_bounds__(64 * NW) void sparse_prior_attn_bf16_kernel(Prefill
     extern __shared__ __attribute__((aligned(16))) char smem[];
     char* ring = smem;                                   // two tile stages
     TileTables tabs;
-    tabs.carve(smem + 2 * S::STAGE, p.R_t, p.T_c);
+    tabs.carve(smem + 2 * S::STAGE, p.T_c);
 
     constexpr int nthr = 64 * NW;
     const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
@@ -153,6 +148,7 @@ __global__ __launch_bounds__(64 * NW) void sparse_prior_attn_bf16_kernel(Prefill
     // ---- the lane's (row, head) pair in each of its pair blocks ----
     int jrow[PBW], my_row[PBW];
     bool pok[PBW], live[PBW];
+    ListCursor lc[PBW];
     bf16x8 qf[PBW][NS];
 #pragma unroll
     for (int pb = 0; pb < PBW; ++pb) {
@@ -162,6 +158,7 @@ __global__ __launch_bounds__(64 * NW) void sparse_prior_attn_bf16_kernel(Prefill
         const int hh = r * g + (P & (g - 1));
         live[pb] = (wid * PBW + pb) * 32 < g * R_t;              // wavefront-uniform
         pok[pb] = live[pb] && jrow[pb] < R_t && my_row[pb] < p.n;
+        lc[pb].init(p, bhkv * p.n + (pok[pb] ? my_row[pb] : 0), pok[pb]);
         const uint16_t* qrow = static_cast<const uint16_t*>(p.Q) +
             (((size_t)bi * p.h_q + hh) * p.n + (pok[pb] ? my_row[pb] : 0)) * D + 8 * hl;
 #pragma unroll
@@ -284,24 +281,31 @@ __global__ __launch_bounds__(64 * NW) void sparse_prior_attn_bf16_kernel(Prefill
                 o_acc[pb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[s][db], pp[s], o_acc[pb][db], 0, 0, 0);
     };
 
-    if (st.nsteps > 0) cp.issue(ring, Kg, Vtg, st.base(tabs.ulist, 0), nmax, p.n_pad, wid);
+    // the tile base and chunk of each step are read from LDS two steps ahead, so
+    // that neither the cursors nor the copies wait on an LDS read
+    int tb_cur, c_cur, tb_nxt, c_nxt;
+    st.at(tabs.ulist, 0, tb_cur, c_cur);
+    st.at(tabs.ulist, 1, tb_nxt, c_nxt);
+    if (st.nsteps > 0) cp.issue(ring, Kg, Vtg, tb_cur, nmax, p.n_pad, wid);
     wait_tile_copies();
     __syncthreads();
     for (int k = 0; k < st.nsteps; ++k) {
-        if (k + 1 < st.nsteps)
-            cp.issue(ring + ((k + 1) & 1) * S::STAGE, Kg, Vtg, st.base(tabs.ulist, k + 1), nmax, p.n_pad, wid);
-        const char* kt = ring + (k & 1) * S::STAGE;
-        const char* vt = kt + S::KBYTES;
-        const int tb = st.base(tabs.ulist, k);
+        // bias of this tile's chunk per pair block; the cursors' entries arrived
+        // during the previous tile, and their next loads go out ahead of the copies
         const bool routed = k < st.nrouted;
         float bias2[PBW];
         bool run[PBW];
-        const int c = routed ? tabs.ulist[k / st.SPC] : 0;
 #pragma unroll
         for (int pb = 0; pb < PBW; ++pb) {
-            bias2[pb] = routed ? (pok[pb] ? tabs.btab[jrow[pb] * p.T_c + c] * kLog2e : -INFINITY) : 0.f;
+            bias2[pb] = routed ? lc[pb].take(c_cur, k % st.SPC == st.SPC - 1) : 0.f;
             run[pb] = live[pb] && (!routed || ballot(bias2[pb] > -INFINITY) != 0);
         }
+        if (k + 1 < st.nsteps) cp.issue(ring + ((k + 1) & 1) * S::STAGE, Kg, Vtg, tb_nxt, nmax, p.n_pad, wid);
+        int tb_nn, c_nn;
+        st.at(tabs.ulist, k + 2, tb_nn, c_nn);
+        const char* kt = ring + (k & 1) * S::STAGE;
+        const char* vt = kt + S::KBYTES;
+        const int tb = tb_cur;
 #pragma unroll
         for (int pb = 0; pb < PBW; ++pb) {
             if (run[pb]) {
@@ -320,6 +324,8 @@ __global__ __launch_bounds__(64 * NW) void sparse_prior_attn_bf16_kernel(Prefill
         }
         wait_tile_copies();
         __syncthreads();
+        tb_cur = tb_nxt; c_cur = c_nxt;
+        tb_nxt = tb_nn; c_nxt = c_nn;
     }
 
 #pragma unroll

@@ -27,39 +27,37 @@ struct PrefillParams {
     float scale_log2;    // log2(e)/sqrt(d)
 };
 
-// LDS tables of one query tile: the union of routed chunks and the bias table.
+// LDS tables of one query tile: the ascending union of the chunks its rows route.
 struct TileTables {
-    float* btab;   // [R_t][T_c] bias of chunk c for tile row j (-inf: not routed)
     int* uflag;    // [T_c] scratch flags
     int* ulist;    // [T_c] ascending union of routed chunks
     int* s_U;      // union size
-    __host__ __device__ static size_t bytes(int R_t, int T_c) {
-        return (size_t)R_t * T_c * 4 + (size_t)2 * T_c * 4 + 16;
-    }
-    __device__ __forceinline__ void carve(char* base, int R_t, int T_c) {
-        btab = reinterpret_cast<float*>(base);
-        uflag = reinterpret_cast<int*>(btab + R_t * T_c);
+    __host__ __device__ static size_t bytes(int T_c) { return (size_t)2 * T_c * 4 + 16; }
+    __device__ __forceinline__ void carve(char* base, int T_c) {
+        uflag = reinterpret_cast<int*>(base);
         ulist = uflag + T_c;
         s_U = ulist + T_c;
     }
-    // Fill the tables for rows row0 .. row0+R_t-1 of KV group bhkv (visible chunks
-    // 0..nvis-1) and return the union size. Ends with a workgroup barrier.
+    // Fill the union for rows row0 .. row0+R_t-1 of KV group bhkv (visible chunks
+    // 0..nvis-1) and return its size. Every row has nthr/R_t threads, which read its
+    // list four entries apart at a time, so all rows' loads are in flight together.
+    // Ends with a workgroup barrier.
     __device__ int build(const PrefillParams& p, size_t bhkv, int row0, int nvis, int tid, int nthr) {
-        const int R_t = p.R_t;
-        for (int i = tid; i < R_t * nvis; i += nthr) btab[(i / nvis) * p.T_c + i % nvis] = -INFINITY;
         for (int c = tid; c < nvis; c += nthr) uflag[c] = 0;
         __syncthreads();
-        for (int j = 0; j < R_t; ++j) {
-            const int row = row0 + j;
-            if (row >= p.n) break;
+        const int tpr = max(nthr / p.R_t, 1);
+        const int j = tid / tpr, sub = tid % tpr, row = row0 + j;
+        if (j < p.R_t && row < p.n) {
             const size_t rb = bhkv * p.n + row;
             const int cn = min(p.cnt[rb], p.list_cap);
-            for (int e = tid; e < cn; e += nthr) {
-                const int c = p.idx[rb * p.list_cap + e];
-                if (c >= 0 && c < nvis) {
-                    btab[j * p.T_c + c] = p.bias[rb * p.list_cap + e];
-                    uflag[c] = 1;
-                }
+            const int32_t* li = p.idx + rb * p.list_cap;
+            for (int e0 = sub; e0 < cn; e0 += 4 * tpr) {
+                int c[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) c[u] = e0 + u * tpr < cn ? li[e0 + u * tpr] : -1;
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    if (c[u] >= 0 && c[u] < nvis) uflag[c[u]] = 1;
             }
         }
         __syncthreads();
@@ -77,6 +75,39 @@ struct TileTables {
         }
         __syncthreads();
         return *s_U;
+    }
+};
+
+// A lane's walk along the routed list of its query row, in step with the tile's
+// ascending union: both are ascending, so the bias of union chunk c for this row
+// is the list's next entry when that entry is c, and the row does not route c
+// otherwise. The entry after a consumed one is loaded at once and has a whole
+// tile of work to arrive.
+struct ListCursor {
+    const int32_t* idx; const float* bias;
+    int cn, pos, next;
+    float nb;
+    __device__ __forceinline__ void fetch() {
+        next = pos < cn ? idx[pos] : 0x7fffffff;
+        nb = pos < cn ? bias[pos] : 0.f;
+    }
+    __device__ __forceinline__ void init(const PrefillParams& p, size_t rb, bool ok) {
+        idx = p.idx + rb * p.list_cap;
+        bias = p.bias + rb * p.list_cap;
+        cn = ok ? min(p.cnt[rb], p.list_cap) : 0;
+        pos = 0;
+        fetch();
+    }
+    // bias of union chunk c in log2 units (-inf: not routed); `last` marks the
+    // chunk's last token tile, after which the cursor moves past c
+    __device__ __forceinline__ float take(int c, bool last) {
+        float b = next == c ? nb * kLog2e : -INFINITY;
+        // b is fixed here, before the cursor moves: the old entry is then dead when
+        // the next one is loaded into its registers, and nothing waits on that load
+        // until the following tile
+        asm volatile("" : "+v"(b));
+        if (last && next <= c) { ++pos; fetch(); }
+        return b;
     }
 };
 
@@ -100,6 +131,11 @@ struct TileSteps {
     __device__ __forceinline__ int base(const int* ulist, int k) const {
         return k < nrouted ? ulist[k / SPC] * (SPC * TT) + (k % SPC) * TT
                            : diag_base + (k - nrouted) * TT;
+    }
+    // first token and routed chunk (0 on the diagonal) of step k; zeros past the end
+    __device__ __forceinline__ void at(const int* ulist, int k, int& tb, int& c) const {
+        c = k < nrouted ? ulist[k / SPC] : 0;
+        tb = k < nrouted ? c * (SPC * TT) + (k % SPC) * TT : k < nsteps ? diag_base + (k - nrouted) * TT : 0;
     }
 };
 

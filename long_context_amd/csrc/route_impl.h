@@ -10,7 +10,9 @@
 //  * Logits: MFMA with A = k̄ tile (16 chunks x d) and B = q (d x 16 pairs); lane
 //    (kg, n) ends with chunks 16t+4kg+i of pair n. All visible chunks of a row stay in
 //    registers: up to 512 per wavefront, rows with more chunks are split over CW = 2
-//    or 4 wavefronts whose row maxima and Newton sums meet in LDS.
+//    or 4 wavefronts whose row maxima and Newton sums meet in LDS. The split is
+//    interleaved by 16-chunk tile (wavefront cw takes tiles cw, cw + CW, ...), so the
+//    two tiles of each shared summary stage go to two different wavefronts.
 //  * Threshold: work on y = (α-1)γ(z̄ - max z̄) <= 0 (exact shift by the row maximum)
 //    so τ lies in [-1, 0). Newton's method on g(τ) = ||[y - τ]_+||_p - 1 with
 //    p = 1/(α-1), started at τ = -1 where g >= 0: g is convex and decreasing, so the
@@ -112,13 +114,13 @@ __device__ __forceinline__ void load4(const uint16_t* p, float* o) {
     o[2] = __uint_as_float(v[1] << 16); o[3] = __uint_as_float(v[1] & 0xFFFF0000u);
 }
 
-// Shared summaries of one stage (32 chunks) for bf16 queries: per chunk three rows
+// Shared summaries of one stage (CH chunks) for bf16 queries: per chunk three rows
 // (hi, mid, lo) of D bf16, i.e. 3*D/8 16-byte pieces; piece c of split h sits at
 // h*(D/8) + (c ^ (chunk mod D/8)) so that the 16 lanes reading 16 consecutive chunks
 // at one column hit distinct banks.
-template <int D>
+template <int D, int CH_>
 struct KSplitStage {
-    static constexpr int CH = 32;                     // chunks per stage
+    static constexpr int CH = CH_;                    // chunks per stage
     static constexpr int PPS = D / 8;                 // pieces per split row
     static constexpr int ROWB = 3 * D * 2;            // bytes per chunk
     static constexpr int BYTES = CH * ROWB;
@@ -170,14 +172,26 @@ __device__ __forceinline__ float solve_tau_split(float (&sv)[NT][4], int nt, flo
     return tau;
 }
 
+// Chunk layout of a row over the CW wavefronts of its group: 16-chunk tile j of the
+// row belongs to wavefront j % CW as its local tile j / CW.
+template <int CW> struct RouteSplit {
+    __device__ __forceinline__ static int tile_chunk(int t, int cw) { return 16 * (t * CW + cw); }
+    // local tiles of wavefront cw that start below nvis
+    __device__ __forceinline__ static int tiles_below(int nvis, int cw) {
+        const int rest = (nvis + 15) / 16 - cw;
+        return rest > 0 ? (rest + CW - 1) / CW : 0;
+    }
+};
+
 // One workgroup = G groups of 16 (row, head) pairs (16/g rows x the g heads of a
-// group each) times CW wavefronts per group: wavefront cw of a group holds chunks
-// [cw*16*NT, (cw+1)*16*NT) of its rows in registers (CW > 1 for long rows).
+// group each) times CW wavefronts per group; each wavefront holds NT tiles of its
+// rows' chunks in registers (CW > 1 for long rows).
 template <typename T, int D, int NT, int PM, int CW>
 __global__ __launch_bounds__(512) void entmax_route_kernel(RouteParams p) {
     constexpr int WSW = NT * 16;                      // chunks held by one wavefront
     constexpr int WS = CW * WSW;                      // LDS floats per row of weights
-    typedef KSplitStage<D> KS;
+    typedef RouteSplit<CW> RS;
+    typedef KSplitStage<D, 32> KS;
     typedef __bf16 b8 __attribute__((ext_vector_type(8)));
     extern __shared__ __attribute__((aligned(16))) char rsm[];
     const int W = blockDim.x >> 6;
@@ -201,8 +215,7 @@ __global__ __launch_bounds__(512) void entmax_route_kernel(RouteParams p) {
     const int my_row = row0 + (n16 >> lg);
     const int my_head = r * g + (n16 & (g - 1));
     const bool row_ok = my_row < p.n;
-    const int c_lo = cw * WSW;                        // first chunk of this wavefront
-    const int nt = min(max((nvis - c_lo + 15) >> 4, 0), NT);   // its tiles holding visible chunks
+    const int nt = min(RS::tiles_below(nvis, cw), NT);   // tiles holding visible chunks
 
     float sv[NT][4];
 #pragma unroll
@@ -228,13 +241,16 @@ __global__ __launch_bounds__(512) void entmax_route_kernel(RouteParams p) {
                 }
             }
             // the workgroup loads each stage of 32 summaries once (fp32, coalesced),
-            // splits it in registers and stores it to LDS; the next stage is prefetched.
-            // Stage st holds chunks 32st..32st+31 = tiles 2st, 2st+1, which belong to
-            // wavefront cw = st / (NT/2) of every group.
+            // splits it in registers and stores it to LDS; later stages are prefetched.
+            // Stage st holds the row tiles 2st and 2st+1 (chunks 32st .. 32st+31).
             const float* kb = p.kbar + ((size_t)bi * p.h_kv + r) * (size_t)p.kbar_cap * D;
             const int nst = (nvis + KS::CH - 1) / KS::CH;
             constexpr int PPT = (KS::PIECES + 511) / 512;
-            f32x4 pre[PPT][2];
+            // stages in flight: the loads of stage st + PD are issued once stage st is
+            // stored, so every load has PD stages of work to arrive (PD = 2 when the
+            // stage loop is fully unrolled, so that the register slot is static)
+            constexpr int PD = (CW == 1 && NT >= 4) ? 2 : 1;
+            f32x4 pre[PD][PPT][2];
             auto piece_src = [&](int st, int q) {
                 const int c = min(st * KS::CH + q / KS::PPS, nvis - 1);
                 return reinterpret_cast<const f32x4*>(kb + (size_t)c * D + (q % KS::PPS) * 8);
@@ -254,66 +270,88 @@ __global__ __launch_bounds__(512) void entmax_route_kernel(RouteParams p) {
                 *reinterpret_cast<b8*>(dst + KS::off(c, 1, pc)) = mv;
                 *reinterpret_cast<b8*>(dst + KS::off(c, 2, pc)) = lv;
             };
-            auto load_stage = [&](int st) {
+            auto load_stage = [&](int st, f32x4 (&pr)[PPT][2]) {
 #pragma unroll
                 for (int i = 0; i < PPT; ++i) {
                     const int q = threadIdx.x + i * blockDim.x;
                     if (q < KS::PIECES) {
                         const f32x4* src = piece_src(st, q);
-                        pre[i][0] = src[0];
-                        pre[i][1] = src[1];
+                        pr[i][0] = src[0];
+                        pr[i][1] = src[1];
                     }
                 }
             };
-            auto store_stage = [&](int st) {
+            auto store_stage = [&](int st, const f32x4 (&pr)[PPT][2]) {
                 char* dst = kstage + (st & 1) * KS::BYTES;
 #pragma unroll
                 for (int i = 0; i < PPT; ++i) {
                     const int q = threadIdx.x + i * blockDim.x;
-                    if (q < KS::PIECES) split_store(dst, q, pre[i][0], pre[i][1]);
+                    if (q < KS::PIECES) split_store(dst, q, pr[i][0], pr[i][1]);
                 }
                 for (int q = threadIdx.x + PPT * blockDim.x; q < KS::PIECES; q += blockDim.x) {
                     const f32x4* src = piece_src(st, q);
                     split_store(dst, q, src[0], src[1]);
                 }
             };
-            load_stage(0);
-            for (int rep = 0; rep < CW; ++rep) {
+            // logits of local tile t (a compile-time index once inlined) from stage
+            // tile tt: A = 16 summaries x D (three bf16 splits), B = the 16 pairs' q
+            auto tile_logits = [&](const char* stg, int tt, int t) {
+                const int cl = 16 * tt + n16;         // chunk inside the stage
+                f32x4 acc[3];
 #pragma unroll
-                for (int sl = 0; sl < NT / 2; ++sl) {
-                    const int st = rep * (NT / 2) + sl;
+                for (int h = 0; h < 3; ++h) {
+                    acc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int s = 0; s < D / 32; ++s) {
+                        const b8 a = *reinterpret_cast<const b8*>(stg + KS::off(cl, h, 4 * s + kg));
+                        acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[s], acc[h], 0, 0, 0);
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int ch = RS::tile_chunk(t, cw) + 4 * kg + i;
+                    const float v = acc[0][i] + (acc[1][i] + acc[2][i]);
+                    sv[t][i] = (ch < nvis) ? v : -INFINITY;
+                    smax = fmaxf(smax, sv[t][i]);
+                }
+            };
+            // one stage: split and store it, prefetch stage st + PD into the freed
+            // registers, then the owners of its two tiles compute their logits. No
+            // trailing barrier: stage st+1 fills the other buffer, and the barrier of
+            // stage st+1 orders this stage's reads before stage st+2 overwrites it.
+#pragma unroll
+            for (int j = 0; j < PD; ++j)
+                if (j < nst) load_stage(j, pre[j]);
+            if constexpr (CW == 1) {
+                // stage st holds local tiles 2st and 2st+1 of the single wavefront
+#pragma unroll
+                for (int st = 0; st < NT / 2; ++st) {
                     if (st < nst) {                   // workgroup-uniform
-                        store_stage(st);
+                        store_stage(st, pre[st % PD]);
                         __syncthreads();
-                        if (st + 1 < nst) load_stage(st + 1);
-                        // no trailing barrier: stage st+1 fills the other buffer, and the
-                        // barrier of stage st+1 orders this stage's reads before stage st+2
-                        if (rep == cw) {
+                        if (st + PD < nst) load_stage(st + PD, pre[st % PD]);
+                        const char* stg = kstage + (st & 1) * KS::BYTES;
+#pragma unroll
+                        for (int tt = 0; tt < 2; ++tt)
+                            if (2 * st + tt < nt) tile_logits(stg, tt, 2 * st + tt);
+                    }
+                }
+            } else {
+                // the CW/2 stages st = t*CW/2 + u hold local tile t of every wavefront:
+                // row tile 2st+tt = t*CW + 2u + tt belongs to wavefront 2u + tt
+#pragma unroll
+                for (int t = 0; t < NT; ++t) {
+#pragma unroll 1
+                    for (int u = 0; u < CW / 2; ++u) {
+                        const int st = t * (CW / 2) + u;
+                        if (st < nst) {               // workgroup-uniform
+                            store_stage(st, pre[0]);
+                            __syncthreads();
+                            if (st + 1 < nst) load_stage(st + 1, pre[0]);
                             const char* stg = kstage + (st & 1) * KS::BYTES;
 #pragma unroll
-                            for (int tt = 0; tt < 2; ++tt) {
-                                const int t = 2 * sl + tt;
-                                if (t < nt) {
-                                    const int cl = 16 * tt + n16;            // chunk inside the stage
-                                    f32x4 acc[3];
-#pragma unroll
-                                    for (int h = 0; h < 3; ++h) {
-                                        acc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                                        for (int s = 0; s < D / 32; ++s) {
-                                            const b8 a = *reinterpret_cast<const b8*>(stg + KS::off(cl, h, 4 * s + kg));
-                                            acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[s], acc[h], 0, 0, 0);
-                                        }
-                                    }
-#pragma unroll
-                                    for (int i = 0; i < 4; ++i) {
-                                        const int ch = c_lo + t * 16 + 4 * kg + i;
-                                        const float v = acc[0][i] + (acc[1][i] + acc[2][i]);
-                                        sv[t][i] = (ch < nvis) ? v : -INFINITY;
-                                        smax = fmaxf(smax, sv[t][i]);
-                                    }
-                                }
-                            }
+                            for (int tt = 0; tt < 2; ++tt)
+                                if (2 * u + tt == cw && t < nt) tile_logits(stg, tt, t);
                         }
                     }
                 }
@@ -336,7 +374,7 @@ __global__ __launch_bounds__(512) void entmax_route_kernel(RouteParams p) {
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
                 if (t < nt) {
-                    const int c = min(c_lo + t * 16 + n16, nvis - 1);   // A row = chunk
+                    const int c = min(RS::tile_chunk(t, cw) + n16, nvis - 1);   // A row = chunk
                     const float* krow = kb + (size_t)c * D;
                     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -349,7 +387,7 @@ __global__ __launch_bounds__(512) void entmax_route_kernel(RouteParams p) {
                     }
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const int ch = c_lo + t * 16 + 4 * kg + i;
+                        const int ch = RS::tile_chunk(t, cw) + 4 * kg + i;
                         sv[t][i] = (ch < nvis) ? acc[i] : -INFINITY;
                         smax = fmaxf(smax, sv[t][i]);
                     }
@@ -400,7 +438,7 @@ __global__ __launch_bounds__(512) void entmax_route_kernel(RouteParams p) {
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) wr[c_lo + t * 16 + 4 * kg + i] = sv[t][i];
+            for (int i = 0; i < 4; ++i) wr[RS::tile_chunk(t, cw) + 4 * kg + i] = sv[t][i];
     }
     if constexpr (CW > 1) {
         __syncthreads();                              // the rows' chunks come from CW wavefronts
@@ -453,7 +491,7 @@ __global__ __launch_bounds__(512) void entmax_route_kernel(RouteParams p) {
 // weights, the cross-wavefront partials) must fit 64 KiB.
 template <typename T, int D, int NT, int CW>
 inline int route_groups_per_block(int R, int B, size_t* lds) {
-    const size_t stage = sizeof(T) == 2 ? 2 * (size_t)KSplitStage<D>::BYTES : 0;
+    const size_t stage = sizeof(T) == 2 ? 2 * (size_t)KSplitStage<D, 32>::BYTES : 0;
     auto bytes = [&](int G) {
         return stage + (size_t)G * R * CW * NT * 16 * 4 + (size_t)G * CW * 16 * 4 + (size_t)2 * G * CW * 32 * 4;
     };
@@ -461,6 +499,24 @@ inline int route_groups_per_block(int R, int B, size_t* lds) {
     while (G > 1 && (B % (G * R) != 0 || bytes(G) > 64 * 1024)) G >>= 1;
     *lds = bytes(G);
     return G;
+}
+
+template <typename T, int D, int NT, int PM, int CW>
+static hipError_t launch_route_pm(const RouteParams& p, dim3 grid, dim3 block, size_t lds, hipStream_t s) {
+    auto kern = entmax_route_kernel<T, D, NT, PM, CW>;
+    if (lds > 64 * 1024) {
+        // allow dynamic LDS up to the CU's 160 KiB less the kernel's static LDS
+        static hipError_t configured = [&] {
+            hipFuncAttributes fa;
+            hipError_t e = hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(kern));
+            if (e != hipSuccess) return e;
+            return hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)(160 * 1024 - fa.sharedSizeBytes));
+        }();
+        if (configured != hipSuccess) return configured;
+    }
+    hipLaunchKernelGGL(kern, grid, block, lds, s, p);
+    return hipGetLastError();
 }
 
 template <typename T, int D, int NT, int CW>
@@ -471,12 +527,11 @@ static hipError_t launch_route_nt(const RouteParams& p, int b, hipStream_t s) {
     const int groups = (p.n + R - 1) / R;
     dim3 grid((groups + G - 1) / G, p.h_kv, b), block(64 * G * CW);
     switch (p.pmode) {
-        case 1: hipLaunchKernelGGL((entmax_route_kernel<T, D, NT, 1, CW>), grid, block, lds, s, p); break;
-        case 2: hipLaunchKernelGGL((entmax_route_kernel<T, D, NT, 2, CW>), grid, block, lds, s, p); break;
-        case 4: hipLaunchKernelGGL((entmax_route_kernel<T, D, NT, 4, CW>), grid, block, lds, s, p); break;
-        default: hipLaunchKernelGGL((entmax_route_kernel<T, D, NT, 0, CW>), grid, block, lds, s, p); break;
+        case 1: return launch_route_pm<T, D, NT, 1, CW>(p, grid, block, lds, s);
+        case 2: return launch_route_pm<T, D, NT, 2, CW>(p, grid, block, lds, s);
+        case 4: return launch_route_pm<T, D, NT, 4, CW>(p, grid, block, lds, s);
+        default: return launch_route_pm<T, D, NT, 0, CW>(p, grid, block, lds, s);
     }
-    return hipGetLastError();
 }
 
 template <typename T, int D>
