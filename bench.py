@@ -110,6 +110,7 @@ class Prefill:
         self.idx, self.bias, self.cnt, _ = dash.alloc_route(b, w.h_kv, n, self.T)
         self.O = torch.empty((b, h_q, n, d), dtype=torch.bfloat16, device="cuda")
         self.ws = dash.alloc_prefill_ws(b, h_q, w.h_kv, n, d, w.B)
+        self.rws = dash.alloc_route_ws(b, h_q, w.h_kv, n, d, w.B)
 
     def run(self, alpha, ev=None):
         d, w = self.dash, self.w
@@ -117,7 +118,7 @@ class Prefill:
         d.dash_summarize(self.K, self.qbar, self.kbar, w.B)
         if ev: ev[1].record()
         d.dash_route(self.Q, self.kbar, w.B, alpha, w.gamma, w.sigma, True, self.idx, self.bias,
-                     self.cnt)
+                     self.cnt, ws=self.rws)
         if ev: ev[2].record()
         d.dash_attend_prefill(self.Q, self.K, self.V, self.idx, self.bias, self.cnt, self.O, w.B, True,
                               ws=self.ws)

@@ -86,8 +86,13 @@ dash_status dash_summarize(const void* K, int k_dtype, const float* qbar, float*
  *   bias[b, h_kv, n, list_cap]  fp32  d = (ln w - μ)/σ of each listed chunk
  *   w_out (nullable) [b, h_kv, n, kbar_cap] fp32 dense group weights w (0 off
  *          the visible set); meant for verification.
- * list_cap >= floor(n/B) and kbar_cap >= floor(n/B). The workspace may be NULL
- * when dash_workspace_bytes(DASH_OP_ROUTE, ...) is 0.
+ * list_cap >= floor(n/B) and kbar_cap >= floor(n/B). bf16 queries need a device
+ * workspace of at least dash_workspace_bytes(DASH_OP_ROUTE, ...) bytes (the
+ * summaries split into three bf16 terms, b * h_kv * (floor(n/B) rounded up to 32)
+ * * 3 * d * 2 bytes); fp32 queries need none (ws may be NULL). Calls that share one
+ * workspace must not overlap. Shapes whose working set does not fit a compute
+ * unit's LDS (many chunks with few query heads per KV head) return
+ * DASH_ERR_UNSUPPORTED.
  */
 dash_status dash_route(const void* Q, int q_dtype, const float* kbar,
                        int b, int h_q, int h_kv, int n, int kbar_cap, int d, int B,
@@ -136,7 +141,8 @@ dash_status dash_attend_decode(const void* Q, const void* Kc, const void* Vc, in
                                void* ws, size_t ws_bytes, void* stream);
 
 /* Workspace bytes an operation needs (n_or_Lcap: n for prefill ops, L_cap for
- * decode; DASH_OP_PREFILL gives the size for bf16 inputs). Returns 0 when no
+ * decode; DASH_OP_ROUTE and DASH_OP_PREFILL give the size for bf16 inputs, which
+ * fp32 inputs do not need). Returns 0 when no
  * workspace is needed, (size_t)-1 on invalid sizes. */
 size_t dash_workspace_bytes(int op, int b, int h_q, int h_kv, int n_or_Lcap, int d, int B);
 

@@ -117,7 +117,6 @@ dash_status dash_route(const void* Q, int q_dtype, const float* kbar,
                        float alpha, float gamma, float sigma, int causal,
                        int32_t* idx, float* bias, int32_t* cnt, int list_cap,
                        float* w_out, void* ws, size_t ws_bytes, void* stream) {
-    (void)ws; (void)ws_bytes;
     if (!Q || !kbar || !idx || !bias || !cnt) return fail(DASH_ERR_NULL, "Q, kbar, idx, bias and cnt must be non-null");
     if (!valid_dtype(q_dtype)) return fail(DASH_ERR_PARAM, "bad Q dtype %d", q_dtype);
     if (causal != 0 && causal != 1) return fail(DASH_ERR_PARAM, "causal must be 0 or 1");
@@ -129,8 +128,17 @@ dash_status dash_route(const void* Q, int q_dtype, const float* kbar,
     if (kbar_cap < T) return fail(DASH_ERR_SHAPE, "kbar_cap %d < floor(n/B) = %d", kbar_cap, T);
     if (list_cap < T) return fail(DASH_ERR_SHAPE, "list_cap %d < floor(n/B) = %d", list_cap, T);
     if (dash::route_tiles_bucket(T) == 0) return fail(DASH_ERR_UNSUPPORTED, "%d chunks exceed the router's 2048", T);
+    const size_t lds = dash::route_lds_bytes(h_q / h_kv, B, T, d, q_dtype == DASH_BF16);
+    if (lds > dash::kRouteLdsLimit)
+        return fail(DASH_ERR_UNSUPPORTED, "routing %d chunks at g = %d needs %zu bytes of LDS (limit %zu)", T, h_q / h_kv,
+                    lds, dash::kRouteLdsLimit);
+    if (q_dtype == DASH_BF16 && T > 0) {
+        const size_t need = dash::route_workspace_bytes(b, h_kv, T, d);
+        if (!ws || ws_bytes < need)
+            return fail(DASH_ERR_WORKSPACE, "bf16 routing needs %zu workspace bytes, got %zu", need, ws ? ws_bytes : (size_t)0);
+    }
     dash::RouteArgs a{Q, q_dtype == DASH_BF16, kbar, b, h_q, h_kv, n, kbar_cap, d, B, causal, list_cap,
-                      alpha, gamma, sigma, idx, bias, cnt, w_out};
+                      alpha, gamma, sigma, idx, bias, cnt, w_out, ws};
     return from_hip(dash::launch_route(a, (hipStream_t)stream), "entmax_route_kernel");
 }
 
@@ -165,7 +173,7 @@ dash_status dash_attend_prefill(const void* Q, const void* K, const void* V, int
 size_t dash_workspace_bytes(int op, int b, int h_q, int h_kv, int n_or_Lcap, int d, int B) {
     if (b < 1 || h_q < 1 || h_kv < 1 || h_q % h_kv != 0 || n_or_Lcap < 0 || d < 1 || B < 1) return (size_t)-1;
     switch (op) {
-        case DASH_OP_ROUTE: return 0;
+        case DASH_OP_ROUTE: return dash::route_workspace_bytes(b, h_kv, n_or_Lcap / B, d);
         case DASH_OP_PREFILL: return dash::prefill_workspace_bytes(b, h_kv, n_or_Lcap, d);
         case DASH_OP_DECODE: {
             if (n_or_Lcap < 1) return (size_t)-1;

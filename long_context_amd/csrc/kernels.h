@@ -19,8 +19,16 @@ struct RouteArgs {
     int b, h_q, h_kv, n, kbar_cap, d, B, causal, list_cap;
     float alpha, gamma, sigma;
     int32_t* idx; float* bias; int32_t* cnt; float* w_out;
+    void* ws;            // bf16 queries: split summaries, route_workspace_bytes
 };
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
+// Workspace of a bf16-query routing: the summaries split into three bf16 terms,
+// b * h_kv * (T_c rounded up to 32) * 3 * d * 2 bytes.
+size_t route_workspace_bytes(int b, int h_kv, int T_c, int d);
+// LDS bytes the routing kernel needs for group size g, chunk size B, T_c chunks
+// (the host rejects shapes beyond what a compute unit holds).
+size_t route_lds_bytes(int g, int B, int T_c, int d, bool q_bf16);
+constexpr size_t kRouteLdsLimit = 159 * 1024;   // 160 KiB less room for static LDS
 // Number of 16-chunk tiles the routing kernels keep in registers per row group
 // for T chunks (0 if T is beyond the supported range of 2048 chunks).
 int route_tiles_bucket(int T);

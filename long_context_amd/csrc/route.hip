@@ -13,6 +13,38 @@ int route_tiles_bucket(int T) {
     return 0;
 }
 
+size_t route_workspace_bytes(int b, int h_kv, int T_c, int d) {
+    const size_t T_pad = (size_t)(T_c + 31) / 32 * 32;
+    return (size_t)b * h_kv * T_pad * 3 * d * sizeof(uint16_t);
+}
+
+template <typename T, int D>
+static size_t route_lds_d(int R, int B, int T_c) {
+    size_t lds = 0;
+    switch (route_tiles_bucket(T_c)) {
+        case 2: route_groups_per_block<T, D, 2, 1>(R, B, &lds); break;
+        case 8: route_groups_per_block<T, D, 8, 1>(R, B, &lds); break;
+        case 32: route_groups_per_block<T, D, 32, 1>(R, B, &lds); break;
+        case 64: route_groups_per_block<T, D, 32, 2>(R, B, &lds); break;
+        default: route_groups_per_block<T, D, 32, 4>(R, B, &lds); break;
+    }
+    return lds;
+}
+
+size_t route_lds_bytes(int g, int B, int T_c, int d, bool q_bf16) {
+    const int R = 16 / g;
+    if (q_bf16) return d == 64 ? route_lds_d<uint16_t, 64>(R, B, T_c) : route_lds_d<uint16_t, 128>(R, B, T_c);
+    return d == 64 ? route_lds_d<float, 64>(R, B, T_c) : route_lds_d<float, 128>(R, B, T_c);
+}
+
+template <int D>
+static hipError_t launch_ksplit(const RouteParams& p, int b, hipStream_t s) {
+    const int pieces = p.T_pad * (D / 8);
+    hipLaunchKernelGGL((ksplit_kernel<D>), dim3((pieces + 255) / 256, p.h_kv, b), dim3(256), 0, s,
+                       p.kbar, const_cast<uint8_t*>(p.ksplit), p.kbar_cap, p.T_c, p.T_pad);
+    return hipGetLastError();
+}
+
 int pmode_of(float alpha) {
     const double pe = 1.0 / ((double)alpha - 1.0);
     if (pe == 1.0) return 1;
@@ -33,8 +65,16 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
     p.pexp = (float)(1.0 / ((double)a.alpha - 1.0));
     p.pmode = pmode_of(a.alpha);
     p.inv_sigma = isinf(a.sigma) ? 0.f : (float)(1.0 / (double)a.sigma);
+    p.ksplit = static_cast<const uint8_t*>(a.ws);
+    p.T_pad = (p.T_c + 31) / 32 * 32;
     if (a.n == 0) return hipSuccess;
-    if (a.q_bf16) return a.d == 64 ? launch_route_bf16_64(p, a.b, s) : launch_route_bf16_128(p, a.b, s);
+    if (a.q_bf16) {
+        if (p.T_c > 0) {
+            const hipError_t e = a.d == 64 ? launch_ksplit<64>(p, a.b, s) : launch_ksplit<128>(p, a.b, s);
+            if (e != hipSuccess) return e;
+        }
+        return a.d == 64 ? launch_route_bf16_64(p, a.b, s) : launch_route_bf16_128(p, a.b, s);
+    }
     return a.d == 64 ? launch_route_f32_64(p, a.b, s) : launch_route_f32_128(p, a.b, s);
 }
 

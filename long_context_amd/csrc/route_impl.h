@@ -33,6 +33,8 @@ namespace dash {
 
 struct RouteParams {
     const void* Q; const float* kbar;
+    const uint8_t* ksplit;  // bf16 queries: summaries split into bf16 (hi, mid, lo), staged layout
+    int T_pad;              // chunks per (b, KV head) in ksplit: T_c rounded up to 32
     int32_t* idx; float* bias; int32_t* cnt; float* w_out;
     int h_q, h_kv, n, kbar_cap, list_cap, B, T_c, g, log2g, causal;
     float cs;           // (α-1) γ / sqrt(d)
@@ -130,6 +132,58 @@ struct KSplitStage {
     }
 };
 
+// k̄ [b, h_kv, kbar_cap, D] fp32 -> ksplit [b, h_kv, T_pad] chunks of three bf16
+// rows (hi, mid, lo; hi + mid + lo reproduces k̄ to the last bits of fp32) in the
+// swizzled order of KSplitStage, so that a stage is one contiguous block that the
+// routing kernel copies to LDS as is. Chunks T_c .. T_pad-1 are zero.
+template <int D>
+__global__ __launch_bounds__(256) void ksplit_kernel(const float* kbar, uint8_t* ksplit, int kbar_cap, int T_c,
+                                                     int T_pad) {
+    typedef KSplitStage<D, 32> KS;
+    typedef __bf16 b8 __attribute__((ext_vector_type(8)));
+    const int q = blockIdx.x * 256 + threadIdx.x;
+    const int c = q / KS::PPS, pc = q % KS::PPS;
+    if (c >= T_pad) return;
+    const size_t bh = (size_t)blockIdx.z * gridDim.y + blockIdx.y;
+    f32x4 lo4 = {0.f, 0.f, 0.f, 0.f}, hi4 = {0.f, 0.f, 0.f, 0.f};
+    if (c < T_c) {
+        const f32x4* src = reinterpret_cast<const f32x4*>(kbar + (bh * kbar_cap + c) * D + pc * 8);
+        lo4 = src[0];
+        hi4 = src[1];
+    }
+    b8 hv, mv, lv;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float x = e < 4 ? lo4[e] : hi4[e - 4];
+        const __bf16 h = (__bf16)x;
+        const float r1 = x - (float)h;
+        const __bf16 m = (__bf16)r1;
+        hv[e] = h; mv[e] = m; lv[e] = (__bf16)(r1 - (float)m);
+    }
+    uint8_t* dst = ksplit + bh * (size_t)T_pad * KS::ROWB;
+    *reinterpret_cast<b8*>(dst + KS::off(c, 0, pc)) = hv;
+    *reinterpret_cast<b8*>(dst + KS::off(c, 1, pc)) = mv;
+    *reinterpret_cast<b8*>(dst + KS::off(c, 2, pc)) = lv;
+}
+
+// s_waitcnt vmcnt(n) for the counts the summary ring needs (larger counts wait for
+// everything, which is always safe)
+__device__ __forceinline__ void wait_vm_at_most(int n) {
+    switch (n) {
+        case 1: asm volatile("s_waitcnt vmcnt(1)" ::: "memory"); break;
+        case 2: asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
+        case 3: asm volatile("s_waitcnt vmcnt(3)" ::: "memory"); break;
+        case 6: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
+        case 12: asm volatile("s_waitcnt vmcnt(12)" ::: "memory"); break;
+        case 24: asm volatile("s_waitcnt vmcnt(24)" ::: "memory"); break;
+        default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    }
+}
+
+// Stages of the summary ring in LDS: three when a row can need many stages, so the
+// copies run two stages ahead.
+template <int NT, int CW> constexpr int route_ring_stages() { return NT * CW / 2 >= 4 ? 3 : 2; }
+
 // τ for rows whose chunks are split over CW cooperating wavefronts: every iteration
 // each wavefront sums its own chunks, the CW partial sums meet in LDS (double
 // buffered by iteration parity) and are added in a fixed order, so the CW wavefronts
@@ -206,8 +260,9 @@ __global__ __launch_bounds__(512) void entmax_route_kernel(RouteParams p) {
     const int wg_row0 = blockIdx.x * G * R;
     const int row0 = wg_row0 + gid * R;
     const bool wave_live = row0 < p.n;
-    char* kstage = rsm;                                              // 2 stages (bf16 path)
-    float* wl_all = reinterpret_cast<float*>(rsm + (sizeof(T) == 2 ? 2 * KS::BYTES : 0));
+    constexpr int RSTG = route_ring_stages<NT, CW>();
+    char* kstage = rsm;                                              // RSTG stages (bf16 path)
+    float* wl_all = reinterpret_cast<float*>(rsm + (sizeof(T) == 2 ? RSTG * KS::BYTES : 0));
     float* wl = wl_all + gid * R * WS;
     float* xred = wl_all + G * R * WS;                // [G][CW][16] row maxima of each wavefront
     float* xsum = xred + G * CW * 16;                 // [2][G][CW][16][2] Newton partial sums
@@ -240,58 +295,30 @@ __global__ __launch_bounds__(512) void entmax_route_kernel(RouteParams p) {
                     if (!row_ok) qb[s] = b8{};
                 }
             }
-            // the workgroup loads each stage of 32 summaries once (fp32, coalesced),
-            // splits it in registers and stores it to LDS; later stages are prefetched.
-            // Stage st holds the row tiles 2st and 2st+1 (chunks 32st .. 32st+31).
-            const float* kb = p.kbar + ((size_t)bi * p.h_kv + r) * (size_t)p.kbar_cap * D;
+            // stages of 32 split summaries (chunks 32st .. 32st+31 = row tiles 2st and
+            // 2st+1) reach LDS by asynchronous copies from the split buffer, RSTG-1
+            // stages ahead; every wavefront issues the same number of copies per stage
             const int nst = (nvis + KS::CH - 1) / KS::CH;
-            constexpr int PPT = (KS::PIECES + 511) / 512;
-            // stages in flight: the loads of stage st + PD are issued once stage st is
-            // stored, so every load has PD stages of work to arrive (PD = 2 when the
-            // stage loop is fully unrolled, so that the register slot is static)
-            constexpr int PD = (CW == 1 && NT >= 4) ? 2 : 1;
-            f32x4 pre[PD][PPT][2];
-            auto piece_src = [&](int st, int q) {
-                const int c = min(st * KS::CH + q / KS::PPS, nvis - 1);
-                return reinterpret_cast<const f32x4*>(kb + (size_t)c * D + (q % KS::PPS) * 8);
-            };
-            auto split_store = [&](char* dst, int q, f32x4 lo4, f32x4 hi4) {
-                const int c = q / KS::PPS, pc = q % KS::PPS;
-                b8 hv, mv, lv;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float x = e < 4 ? lo4[e] : hi4[e - 4];
-                    const __bf16 h = (__bf16)x;
-                    const float r1 = x - (float)h;
-                    const __bf16 m = (__bf16)r1;
-                    hv[e] = h; mv[e] = m; lv[e] = (__bf16)(r1 - (float)m);
-                }
-                *reinterpret_cast<b8*>(dst + KS::off(c, 0, pc)) = hv;
-                *reinterpret_cast<b8*>(dst + KS::off(c, 1, pc)) = mv;
-                *reinterpret_cast<b8*>(dst + KS::off(c, 2, pc)) = lv;
-            };
-            auto load_stage = [&](int st, f32x4 (&pr)[PPT][2]) {
-#pragma unroll
-                for (int i = 0; i < PPT; ++i) {
-                    const int q = threadIdx.x + i * blockDim.x;
-                    if (q < KS::PIECES) {
-                        const f32x4* src = piece_src(st, q);
-                        pr[i][0] = src[0];
-                        pr[i][1] = src[1];
-                    }
+            constexpr int CPI = KS::BYTES / 1024;    // 1 KiB copy instructions per stage
+            const int cps = (CPI + W - 1) / W;         // per wavefront (some duplicated)
+            const uint8_t* ksrc = p.ksplit + ((size_t)bi * p.h_kv + r) * (size_t)p.T_pad * KS::ROWB;
+            auto issue = [&](int st) {                 // st may pass nst: a copy of the last
+                char* dst = kstage + (st % RSTG) * KS::BYTES;   // stage into a free slot
+                const uint8_t* src = ksrc + (size_t)min(st, nst - 1) * KS::BYTES + lane * 16;
+                for (int i = 0; i < cps; ++i) {
+                    int j = wid + i * W;
+                    if (j >= CPI) j -= CPI;
+                    __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint32_t*>(src + j * 1024),
+                                                     reinterpret_cast<uint32_t*>(dst + j * 1024), 16, 0, 0);
                 }
             };
-            auto store_stage = [&](int st, const f32x4 (&pr)[PPT][2]) {
-                char* dst = kstage + (st & 1) * KS::BYTES;
-#pragma unroll
-                for (int i = 0; i < PPT; ++i) {
-                    const int q = threadIdx.x + i * blockDim.x;
-                    if (q < KS::PIECES) split_store(dst, q, pr[i][0], pr[i][1]);
-                }
-                for (int q = threadIdx.x + PPT * blockDim.x; q < KS::PIECES; q += blockDim.x) {
-                    const f32x4* src = piece_src(st, q);
-                    split_store(dst, q, src[0], src[1]);
-                }
+            // stage st is complete once at most the (RSTG-2) newer stages' copies are
+            // outstanding; the barrier then also frees the slot of stage st-1, which
+            // the copies of stage st+RSTG-1 fill
+            auto enter_stage = [&](int st) {
+                wait_vm_at_most((RSTG - 2) * cps);
+                __syncthreads();
+                issue(st + RSTG - 1);
             };
             // logits of local tile t (a compile-time index once inlined) from stage
             // tile tt: A = 16 summaries x D (three bf16 splits), B = the 16 pairs' q
@@ -315,22 +342,15 @@ __global__ __launch_bounds__(512) void entmax_route_kernel(RouteParams p) {
                     smax = fmaxf(smax, sv[t][i]);
                 }
             };
-            // one stage: split and store it, prefetch stage st + PD into the freed
-            // registers, then the owners of its two tiles compute their logits. No
-            // trailing barrier: stage st+1 fills the other buffer, and the barrier of
-            // stage st+1 orders this stage's reads before stage st+2 overwrites it.
 #pragma unroll
-            for (int j = 0; j < PD; ++j)
-                if (j < nst) load_stage(j, pre[j]);
+            for (int j = 0; j < RSTG - 1; ++j) issue(j);
             if constexpr (CW == 1) {
                 // stage st holds local tiles 2st and 2st+1 of the single wavefront
 #pragma unroll
                 for (int st = 0; st < NT / 2; ++st) {
                     if (st < nst) {                   // workgroup-uniform
-                        store_stage(st, pre[st % PD]);
-                        __syncthreads();
-                        if (st + PD < nst) load_stage(st + PD, pre[st % PD]);
-                        const char* stg = kstage + (st & 1) * KS::BYTES;
+                        enter_stage(st);
+                        const char* stg = kstage + (st % RSTG) * KS::BYTES;
 #pragma unroll
                         for (int tt = 0; tt < 2; ++tt)
                             if (2 * st + tt < nt) tile_logits(stg, tt, 2 * st + tt);
@@ -345,10 +365,8 @@ __global__ __launch_bounds__(512) void entmax_route_kernel(RouteParams p) {
                     for (int u = 0; u < CW / 2; ++u) {
                         const int st = t * (CW / 2) + u;
                         if (st < nst) {               // workgroup-uniform
-                            store_stage(st, pre[0]);
-                            __syncthreads();
-                            if (st + 1 < nst) load_stage(st + 1, pre[0]);
-                            const char* stg = kstage + (st & 1) * KS::BYTES;
+                            enter_stage(st);
+                            const char* stg = kstage + (st % RSTG) * KS::BYTES;
 #pragma unroll
                             for (int tt = 0; tt < 2; ++tt)
                                 if (2 * u + tt == cw && t < nt) tile_logits(stg, tt, t);
@@ -356,6 +374,8 @@ __global__ __launch_bounds__(512) void entmax_route_kernel(RouteParams p) {
                     }
                 }
             }
+            // no copy may still be landing in LDS when the workgroup ends
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         } else {
             // fp32 queries: the MFMA k-slot kg of step (s, j) carries dimension 16s + 4kg + j
             // for both operands, so every dimension is summed exactly once.
@@ -487,16 +507,18 @@ __global__ __launch_bounds__(512) void entmax_route_kernel(RouteParams p) {
 }
 
 // Workgroup geometry: up to 8 wavefronts = G groups x CW; all rows of a workgroup
-// must share one chunk, and the LDS (two summary stages for bf16 queries, the rows'
-// weights, the cross-wavefront partials) must fit 64 KiB.
+// must share one chunk, and the LDS (the summary ring for bf16 queries, the rows'
+// weights, the cross-wavefront partials) must fit 96 KiB (G shrinks until it does;
+// a single group that still does not fit is rejected on the host).
+constexpr size_t kRouteMaxLds = 96 * 1024;
 template <typename T, int D, int NT, int CW>
 inline int route_groups_per_block(int R, int B, size_t* lds) {
-    const size_t stage = sizeof(T) == 2 ? 2 * (size_t)KSplitStage<D, 32>::BYTES : 0;
+    const size_t stage = sizeof(T) == 2 ? route_ring_stages<NT, CW>() * (size_t)KSplitStage<D, 32>::BYTES : 0;
     auto bytes = [&](int G) {
         return stage + (size_t)G * R * CW * NT * 16 * 4 + (size_t)G * CW * 16 * 4 + (size_t)2 * G * CW * 32 * 4;
     };
     int G = 8 / CW;
-    while (G > 1 && (B % (G * R) != 0 || bytes(G) > 64 * 1024)) G >>= 1;
+    while (G > 1 && (B % (G * R) != 0 || bytes(G) > kRouteMaxLds)) G >>= 1;
     *lds = bytes(G);
     return G;
 }

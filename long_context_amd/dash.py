@@ -107,9 +107,13 @@ def dash_summarize(K, qbar, kbar, B, chunk_begin=0, chunk_end=None, stream=None)
 
 def dash_route(Q, kbar, B, alpha, gamma, sigma, causal, idx, bias, cnt, w_out=None,
                ws=None, stream=None):
-    """Stage 1 of a prefill: routed chunk lists idx/bias [b,h_kv,n,cap] and cnt [b,h_kv,n]."""
+    """Stage 1 of a prefill: routed chunk lists idx/bias [b,h_kv,n,cap] and cnt [b,h_kv,n].
+
+    bf16 queries need a workspace (alloc_route_ws); one is allocated when ws is None."""
     b, h_q, n, d = Q.shape
     h_kv = kbar.shape[1]
+    if ws is None and Q.dtype == torch.bfloat16:
+        ws = alloc_route_ws(b, h_q, h_kv, n, d, B, device=Q.device)
     _check(lib.dash_route(_ptr(Q), _dtype(Q), _ptr(kbar), b, h_q, h_kv, n, kbar.shape[2], d, B,
                           float(alpha), float(gamma), float(sigma), int(causal),
                           _ptr(idx), _ptr(bias), _ptr(cnt), idx.shape[-1], _ptr(w_out),
@@ -161,6 +165,11 @@ def alloc_route(b, h_kv, n, T, device="cuda", with_w=False):
     cnt = torch.empty((b, h_kv, n), dtype=torch.int32, device=device)
     w = torch.empty((b, h_kv, n, cap), dtype=torch.float32, device=device) if with_w else None
     return idx, bias, cnt, w
+
+
+def alloc_route_ws(b, h_q, h_kv, n, d, B, device="cuda"):
+    nbytes = dash_workspace_bytes(DASH_OP_ROUTE, b, h_q, h_kv, n, d, B)
+    return torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=device)
 
 
 def alloc_prefill_ws(b, h_q, h_kv, n, d, B, device="cuda"):

@@ -62,10 +62,18 @@ def _route(dash, **kw):
     (dict(qdt=7), 3), (dict(causal=2), 3),
     (dict(d=96), 4), (dict(B=24), 4), (dict(h_q=64, h_kv=2), 4), (dict(h_q=6, h_kv=2), 4),
     (dict(n=129 * 1024, cap=2064, list_cap=2064), 4),
+    # one query head per KV head: 2048 chunks of 16 rows' weights do not fit LDS
+    (dict(h_q=2, h_kv=2, n=2048 * 64, cap=2048, list_cap=2048), 4),
 ])
 def test_route_validation(dash, kw, status):
     assert _route(dash, **kw) == status
     assert dash.lib.dash_last_error().decode() != ""
+
+
+def test_route_bf16_needs_workspace(dash):
+    # valid bf16 routing with no workspace: the split summaries have nowhere to go
+    assert _route(dash) == dash.DASH_ERR_WORKSPACE
+    assert "workspace" in dash.lib.dash_last_error().decode()
 
 
 def test_route_accepts_infinite_sigma_in_validation(dash):
@@ -137,7 +145,9 @@ def test_decode_workspace_checks(dash):
 
 
 def test_workspace_sizes(dash):
-    assert dash.dash_workspace_bytes(dash.DASH_OP_ROUTE, 1, 32, 2, 32768, 128, 64) == 0
+    # route: split summaries, b * h_kv * (T_c rounded up to 32) * 3 * d * 2 bytes
+    assert dash.dash_workspace_bytes(dash.DASH_OP_ROUTE, 1, 32, 2, 32768, 128, 64) == 2 * 512 * 3 * 128 * 2
+    assert dash.dash_workspace_bytes(dash.DASH_OP_ROUTE, 1, 4, 2, 100, 64, 32) == 2 * 32 * 3 * 64 * 2
     assert dash.dash_workspace_bytes(dash.DASH_OP_PREFILL, 1, 32, 2, 32768, 128, 64) == 2 * 128 * 32768 * 2
     assert dash.dash_workspace_bytes(dash.DASH_OP_PREFILL, 1, 4, 2, 100, 64, 32) == 2 * 64 * 128 * 2
     big = dash.dash_workspace_bytes(dash.DASH_OP_DECODE, 16, 32, 2, 32768, 128, 64)
