@@ -94,6 +94,9 @@ __global__ __launch_bounds__(256) void decode_scores_kernel(DecodeParams p, cons
 }
 
 // ---------------------------------------------------------------------------------
+// The Newton terms below take [y - τ]_+ as a clamp of y - τ to [0, 1]: y <= 0 and
+// τ >= -1 (the iterates rise from -1), so y - τ <= 1 and the clamp folds into the
+// subtraction.
 template <int PM>
 __device__ __forceinline__ void dec_accum(float t, float pexp, float& a0, float& a1) {
     if (PM == 1) { a0 += (t > 0.f) ? 1.f : 0.f; a1 += t; }
@@ -144,7 +147,7 @@ __global__ __launch_bounds__(1024) void decode_route_kernel(DecodeParams p) {
         for (int it = 0; it < 100; ++it) {
             float a0 = 0.f, a1 = 0.f;
 #pragma unroll
-            for (int k = 0; k < VPL; ++k) dec_accum<PM>(fmaxf(y[k] - tau, 0.f), p.pexp, a0, a1);
+            for (int k = 0; k < VPL; ++k) dec_accum<PM>(__builtin_amdgcn_fmed3f(y[k] - tau, 0.f, 1.f), p.pexp, a0, a1);
             a0 = wave_sum(a0);
             a1 = wave_sum(a1);
             float delta;
@@ -158,7 +161,7 @@ __global__ __launch_bounds__(1024) void decode_route_kernel(DecodeParams p) {
             if (!(fabsf(delta) > 1e-6f)) break;
         }
 #pragma unroll
-        for (int k = 0; k < VPL; ++k) wl[wid][lane + 64 * k] = dec_pow<PM>(fmaxf(y[k] - tau, 0.f), p.pexp);
+        for (int k = 0; k < VPL; ++k) wl[wid][lane + 64 * k] = dec_pow<PM>(__builtin_amdgcn_fmed3f(y[k] - tau, 0.f, 1.f), p.pexp);
     }
     __syncthreads();
     // group average in a fixed head order, then μ over the support
