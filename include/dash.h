@@ -37,8 +37,11 @@
  *     Device faults surface at the caller's next synchronisation.
  *   - Supported: d in {64, 128}; B a multiple of 16 (the prefill attention
  *     kernel needs B a multiple of 32); g = h_q/h_kv a power of two <= 16;
- *     Q/K/V both fp32 or all bf16; α > 1, γ > 0, σ > 0 (σ = +inf allowed);
+ *     Q/K/V both fp32 or all bf16; α >= 1, γ > 0, σ > 0 (σ = +inf allowed);
  *     at most 2048 routable chunks per row (e.g. 128K tokens at B = 64).
+ *   - α = 1 routes with softmax instead of entmax (the α -> 1 limit of the
+ *     entmax family, a dense-routing ablation): ŵ = softmax(γ z̄) per head,
+ *     every visible chunk is routed, and w, μ and d are formed as for α > 1.
  */
 #ifndef DASH_H
 #define DASH_H

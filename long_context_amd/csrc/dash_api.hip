@@ -48,7 +48,7 @@ dash_status check_common(int b, int h_q, int h_kv, int d, int B) {
 }
 
 dash_status check_params(float alpha, float gamma, float sigma) {
-    if (!(alpha > 1.0f) || isinf(alpha)) return fail(DASH_ERR_PARAM, "alpha must be finite and > 1 (got %g)", alpha);
+    if (!(alpha >= 1.0f) || isinf(alpha)) return fail(DASH_ERR_PARAM, "alpha must be finite and >= 1 (got %g)", alpha);
     if (!(gamma > 0.0f) || isinf(gamma)) return fail(DASH_ERR_PARAM, "gamma must be finite and > 0 (got %g)", gamma);
     if (!(sigma > 0.0f)) return fail(DASH_ERR_PARAM, "sigma must be > 0 or +inf (got %g)", sigma);
     return DASH_OK;

@@ -31,6 +31,7 @@ constexpr int kDecTT = 64;           // tokens per decode tile (one 32-token blo
 constexpr int kDecWaves = kDecTT / 32;
 constexpr int kDecThreads = 64 * kDecWaves;
 constexpr int kDecSlice = 512;        // stream tokens per workgroup
+constexpr int kDecSoftmax = -1;       // pmode of α = 1 (softmax routing)
 
 struct DecodeParams {
     const void* Q; const void* Kc; const void* Vc;
@@ -143,6 +144,15 @@ __global__ __launch_bounds__(1024) void decode_route_kernel(DecodeParams p) {
         mx = wave_max(mx);
 #pragma unroll
         for (int k = 0; k < VPL; ++k) y[k] = p.cs * (y[k] - mx);
+        if constexpr (PM == kDecSoftmax) {
+            // α = 1: per-head softmax, kept as log2 ŵ = y - log2 Σ 2^y
+            float se = 0.f;
+#pragma unroll
+            for (int k = 0; k < VPL; ++k) se += fast_exp2(y[k]);
+            const float lse = fast_log2(wave_sum(se));
+#pragma unroll
+            for (int k = 0; k < VPL; ++k) wl[wid][lane + 64 * k] = y[k] - lse;
+        } else {
         float tau = -1.f;
         for (int it = 0; it < 100; ++it) {
             float a0 = 0.f, a1 = 0.f;
@@ -162,23 +172,36 @@ __global__ __launch_bounds__(1024) void decode_route_kernel(DecodeParams p) {
         }
 #pragma unroll
         for (int k = 0; k < VPL; ++k) wl[wid][lane + 64 * k] = dec_pow<PM>(__builtin_amdgcn_fmed3f(y[k] - tau, 0.f, 1.f), p.pexp);
+        }
     }
     __syncthreads();
     // group average in a fixed head order, then μ over the support
     const float inv_g = 1.f / (float)g;
     float wv[TMAX / 1024 > 0 ? TMAX / 1024 : 1];
     constexpr int PER = TMAX / 1024 > 0 ? TMAX / 1024 : 1;
+    // (α = 1: wv holds log2 w = log2((1/g) Σ_h ŵ_h), taken stably, and every visible
+    // chunk is in the support)
+    constexpr bool SOFT = PM == kDecSoftmax;
     float sl = 0.f, scn = 0.f;
 #pragma unroll
     for (int q = 0; q < PER; ++q) {
         const int c = tid + 1024 * q;
-        float w = 0.f;
+        float w = SOFT ? -INFINITY : 0.f;
         if (c < nvis) {
-            for (int h = 0; h < g; ++h) w += wl[h][c];
-            w *= inv_g;
+            if (SOFT) {
+                float m = -INFINITY;
+                for (int h = 0; h < g; ++h) m = fmaxf(m, wl[h][c]);
+                float sm = 0.f;
+                for (int h = 0; h < g; ++h) sm += fast_exp2(wl[h][c] - m);
+                w = m + fast_log2(sm) - fast_log2((float)g);
+                sl += w; scn += 1.f;
+            } else {
+                for (int h = 0; h < g; ++h) w += wl[h][c];
+                w *= inv_g;
+            }
         }
         wv[q] = w;
-        if (w > 0.f) { sl += fast_log2(w); scn += 1.f; }
+        if (!SOFT && w > 0.f) { sl += fast_log2(w); scn += 1.f; }
     }
     sl = wave_sum(sl);
     scn = wave_sum(scn);
@@ -194,7 +217,7 @@ __global__ __launch_bounds__(1024) void decode_route_kernel(DecodeParams p) {
 #pragma unroll
     for (int q = 0; q < PER; ++q) {
         const int c = tid + 1024 * q;
-        const bool in = wv[q] > 0.f;
+        const bool in = SOFT ? c < nvis : wv[q] > 0.f;
         const uint64_t m = ballot(in);
         if (lane == 0) wcnt[wid] = __builtin_popcountll(m);
         __syncthreads();
@@ -205,9 +228,9 @@ __global__ __launch_bounds__(1024) void decode_route_kernel(DecodeParams p) {
         if (in) {
             const int pos = off + __builtin_popcountll(m & ((1ull << lane) - 1ull));
             idx[pos] = c;
-            bias[pos] = p.inv_sigma == 0.f ? 0.f : bscale * (fast_log2(wv[q]) - mu2);
+            bias[pos] = p.inv_sigma == 0.f ? 0.f : bscale * ((SOFT ? wv[q] : fast_log2(wv[q])) - mu2);
         }
-        if (p.w_out && c < p.T_route) p.w_out[grp * p.kbar_cap + c] = wv[q];
+        if (p.w_out && c < p.T_route) p.w_out[grp * p.kbar_cap + c] = SOFT ? fast_exp2(wv[q]) : wv[q];
         base += tot;
         __syncthreads();
     }
@@ -454,6 +477,7 @@ static hipError_t launch_dec_route_pm(const DecodeParams& p, int b, hipStream_t 
 template <int VPL>
 static hipError_t launch_dec_route(const DecodeParams& p, int b, hipStream_t s) {
     switch (p.pmode) {
+        case kDecSoftmax: return launch_dec_route_pm<VPL, kDecSoftmax>(p, b, s);
         case 1: return launch_dec_route_pm<VPL, 1>(p, b, s);
         case 2: return launch_dec_route_pm<VPL, 2>(p, b, s);
         case 4: return launch_dec_route_pm<VPL, 4>(p, b, s);
@@ -491,7 +515,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
     while ((1 << p.log2g) < p.g) ++p.log2g;
     p.T_route = a.T_route; p.list_cap = a.list_cap; p.max_slices = a.max_slices;
     p.slice_tokens = a.slice_tokens;
-    p.cs = (float)(((double)a.alpha - 1.0) * (double)a.gamma / sqrt((double)a.d));
+    p.cs = route_scale(a.alpha, a.gamma, a.d);
     p.pexp = (float)(1.0 / ((double)a.alpha - 1.0));
     p.pmode = pmode_of(a.alpha);
     p.inv_sigma = isinf(a.sigma) ? 0.f : (float)(1.0 / (double)a.sigma);

@@ -22,6 +22,8 @@ struct RouteArgs {
     void* ws;            // bf16 queries: split summaries, route_workspace_bytes
 };
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
+// Scale of the routing logits: (α-1)γ/sqrt(d) for entmax, γ log2(e)/sqrt(d) for α = 1.
+float route_scale(float alpha, float gamma, int d);
 // Workspace of a bf16-query routing: the summaries split into three bf16 terms,
 // b * h_kv * (T_c rounded up to 32) * 3 * d * 2 bytes.
 size_t route_workspace_bytes(int b, int h_kv, int T_c, int d);

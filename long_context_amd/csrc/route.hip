@@ -13,6 +13,11 @@ int route_tiles_bucket(int T) {
     return 0;
 }
 
+float route_scale(float alpha, float gamma, int d) {
+    if (alpha == 1.0f) return (float)(1.4426950408889634 * (double)gamma / sqrt((double)d));
+    return (float)(((double)alpha - 1.0) * (double)gamma / sqrt((double)d));
+}
+
 size_t route_workspace_bytes(int b, int h_kv, int T_c, int d) {
     const size_t T_pad = (size_t)(T_c + 31) / 32 * 32;
     return (size_t)b * h_kv * T_pad * 3 * d * sizeof(uint16_t);
@@ -46,6 +51,7 @@ static hipError_t launch_ksplit(const RouteParams& p, int b, hipStream_t s) {
 }
 
 int pmode_of(float alpha) {
+    if (alpha == 1.0f) return kSoftmaxRouting;
     const double pe = 1.0 / ((double)alpha - 1.0);
     if (pe == 1.0) return 1;
     if (pe == 2.0) return 2;
@@ -61,7 +67,7 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
     p.log2g = 0;
     while ((1 << p.log2g) < p.g) ++p.log2g;
     p.causal = a.causal;
-    p.cs = (float)(((double)a.alpha - 1.0) * (double)a.gamma / sqrt((double)a.d));
+    p.cs = route_scale(a.alpha, a.gamma, a.d);
     p.pexp = (float)(1.0 / ((double)a.alpha - 1.0));
     p.pmode = pmode_of(a.alpha);
     p.inv_sigma = isinf(a.sigma) ? 0.f : (float)(1.0 / (double)a.sigma);

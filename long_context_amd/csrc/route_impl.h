@@ -39,9 +39,22 @@ struct RouteParams {
     int h_q, h_kv, n, kbar_cap, list_cap, B, T_c, g, log2g, causal;
     float cs;           // (α-1) γ / sqrt(d)
     float pexp;         // 1/(α-1)
-    int pmode;          // 1, 2, 4 for integer exponents, 0 otherwise
+    int pmode;          // 1, 2, 4 for integer exponents, 0 otherwise, kSoftmaxRouting for α = 1
     float inv_sigma;    // 1/σ (0 for σ = inf)
 };
+
+// Routing with α = 1: per-head softmax weights instead of entmax (every visible chunk
+// is routed); p.cs then holds γ log2(e)/sqrt(d).
+constexpr int kSoftmaxRouting = -1;
+
+// Maximum over the lanes of a 16-lane row whose index differs only in the low `steps` bits.
+__device__ __forceinline__ float row_group_max(float v, int steps) {
+    if (steps > 0) v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
+    if (steps > 1) v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
+    if (steps > 2) v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false)));
+    if (steps > 3) v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false)));
+    return v;
+}
 
 // Sum over the lanes of a 16-lane row whose index differs only in the low `steps` bits.
 __device__ __forceinline__ float row_group_sum(float v, int steps) {
@@ -427,6 +440,7 @@ __global__ __launch_bounds__(512) void entmax_route_kernel(RouteParams p) {
             for (int k = 0; k < CW; ++k) smax = fmaxf(smax, xred[(gid * CW + k) * 16 + n16]);
         }
         // thresholded argument shifted by the row maximum: y = (α-1)γ(z̄ - max z̄) <= 0
+        // (α = 1: y = γ log2(e)(z̄ - max z̄))
 #pragma unroll
         for (int t = 0; t < NT; ++t)
             if (t < nt) {                             // later tiles are never read
@@ -434,6 +448,43 @@ __global__ __launch_bounds__(512) void entmax_route_kernel(RouteParams p) {
                 for (int i = 0; i < 4; ++i) sv[t][i] = p.cs * (sv[t][i] - smax);
             }
 
+        if constexpr (PM == kSoftmaxRouting) {
+            // per-head softmax in log2 units, log2 ŵ = y - log2 Σ 2^y, then the group
+            // weight log2 w = log2((1/g) Σ_h ŵ_h) taken stably across the g lanes
+            float se = 0.f;
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                if (t < nt) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) se += fast_exp2(sv[t][i]);
+                }
+            se = pair32_sum(pair16_sum(se));
+            if constexpr (CW > 1) {
+                float* buf = xsum + ((size_t)gid * CW) * 32;
+                if (kg == 0) buf[(cw * 16 + n16) * 2] = se;
+                __syncthreads();
+                se = 0.f;
+#pragma unroll
+                for (int k = 0; k < CW; ++k) se += buf[(k * 16 + n16) * 2];
+            }
+            const float lse = fast_log2(se);
+            const float lg_g = (float)lg;
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                if (t < nt) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float lw = sv[t][i] - lse;
+                        const float m = row_group_max(lw, lg);
+                        const float sm = row_group_sum(m == -INFINITY ? 0.f : fast_exp2(lw - m), lg);
+                        sv[t][i] = m == -INFINITY ? -INFINITY : m + fast_log2(sm) - lg_g;
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) sv[t][i] = -INFINITY;
+                }
+            }
+        } else {
         float tau;
         if constexpr (CW == 1) tau = solve_tau<NT, PM>(sv, nt, p.pexp, row_ok && wave_live);
         else tau = solve_tau_split<NT, PM, CW>(sv, nt, p.pexp, row_ok && wave_live, xsum, G, gid, cw, n16, kg);
@@ -451,6 +502,7 @@ __global__ __launch_bounds__(512) void entmax_route_kernel(RouteParams p) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) sv[t][i] = 0.f;
             }
+        }
         }
     } else {
 #pragma unroll
@@ -476,7 +528,9 @@ __global__ __launch_bounds__(512) void entmax_route_kernel(RouteParams p) {
     }
     if (!wave_live) return;                           // no barrier follows
 
-    // compaction: ascending chunk ids of the support, with d = (ln w - μ)/σ
+    // compaction: ascending chunk ids of the support, with d = (ln w - μ)/σ (with
+    // α = 1 the LDS holds log2 w and every visible chunk is in the support)
+    constexpr bool SOFT = PM == kSoftmaxRouting;
     const size_t rowbase = ((size_t)bi * p.h_kv + r) * p.n;
     for (int j = 0; j < R; ++j) {
         const int row = row0 + j;
@@ -485,7 +539,8 @@ __global__ __launch_bounds__(512) void entmax_route_kernel(RouteParams p) {
         float sl = 0.f, sc = 0.f;
         for (int c = lane; c < nvis; c += 64) {
             const float v = wr[c];
-            if (v > 0.f) { sl += fast_log2(v); sc += 1.f; }
+            if (SOFT) { sl += v; sc += 1.f; }
+            else if (v > 0.f) { sl += fast_log2(v); sc += 1.f; }
         }
         sl = wave_sum(sl);
         sc = wave_sum(sc);
@@ -497,15 +552,15 @@ __global__ __launch_bounds__(512) void entmax_route_kernel(RouteParams p) {
         int base = 0;
         for (int c0 = 0; c0 < p.T_c; c0 += 64) {
             const int c = c0 + lane;
-            const float v = (c < nvis) ? wr[c] : 0.f;
-            const bool in = v > 0.f;
+            const float v = (c < nvis) ? wr[c] : (SOFT ? -INFINITY : 0.f);
+            const bool in = SOFT ? c < nvis : v > 0.f;
             const uint64_t m = ballot(in);
             const int pre = __builtin_popcountll(m & ((1ull << lane) - 1ull));
             if (in) {
                 idx[base + pre] = c;
-                bias[base + pre] = p.inv_sigma == 0.f ? 0.f : bscale * (fast_log2(v) - mu2);
+                bias[base + pre] = p.inv_sigma == 0.f ? 0.f : bscale * ((SOFT ? v : fast_log2(v)) - mu2);
             }
-            if (wo && c < p.T_c) wo[c] = v;
+            if (wo && c < p.T_c) wo[c] = SOFT ? fast_exp2(v) : v;
             base += __builtin_popcountll(m);
         }
         if (lane == 0) p.cnt[rowbase + row] = base;
@@ -555,6 +610,7 @@ static hipError_t launch_route_nt(const RouteParams& p, int b, hipStream_t s) {
     const int groups = (p.n + R - 1) / R;
     dim3 grid((groups + G - 1) / G, p.h_kv, b), block(64 * G * CW);
     switch (p.pmode) {
+        case kSoftmaxRouting: return launch_route_pm<T, D, NT, kSoftmaxRouting, CW>(p, grid, block, lds, s);
         case 1: return launch_route_pm<T, D, NT, 1, CW>(p, grid, block, lds, s);
         case 2: return launch_route_pm<T, D, NT, 2, CW>(p, grid, block, lds, s);
         case 4: return launch_route_pm<T, D, NT, 4, CW>(p, grid, block, lds, s);

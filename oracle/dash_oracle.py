@@ -138,9 +138,11 @@ def entmax(s, alpha=1.5, valid=None):
         valid = np.ones(s.shape, bool)
     if alpha == 1.0:
         z = np.where(valid, s, -np.inf)
-        z = z - z.max(-1, keepdims=True)
+        m = z.max(-1, keepdims=True) if z.shape[-1] else np.zeros(z.shape[:-1] + (1,))
+        z = z - np.where(np.isfinite(m), m, 0.0)
         e = np.where(valid, np.exp(z), 0.0)
-        return e / e.sum(-1, keepdims=True), None, s
+        tot = e.sum(-1, keepdims=True)
+        return np.where(tot > 0, e / np.where(tot > 0, tot, 1.0), 0.0), None, s
     x = (alpha - 1.0) * s
     tau = entmax_tau(x, valid, alpha)
     t = np.clip(x - tau[..., None], 0.0, None)
@@ -191,7 +193,9 @@ def route(Qr, pos, kbar, B, alpha, gamma, sigma, causal, n_kv, keep_heads=False,
     """Stage 1 routing for query rows Qr [b, h_q, R, d] at token positions pos [b, R].
 
     For every query head h (KV group r = floor(h/g)) and row i:
-      z̄_c = <q_i, k̄_c>/sqrt(d) over visible chunks, ŵ = α-entmax(γ z̄);
+      z̄_c = <q_i, k̄_c>/sqrt(d) over visible chunks, ŵ = α-entmax(γ z̄)
+      (α = 1: ŵ = softmax(γ z̄), the α -> 1 limit, and every visible chunk is in
+      the support; log w is then formed in log space);
     then per KV group: w = mean over the group's heads of ŵ, support S = {c: w_c > 0}
     (the union of the head supports), μ = mean_{c in S} log w_c and the
     Prop. 4.1 bias d_c = (log w_c - μ)/σ on S (σ = inf gives d = 0).
@@ -217,29 +221,48 @@ def route(Qr, pos, kbar, B, alpha, gamma, sigma, causal, n_kv, keep_heads=False,
         what_all = np.zeros((b, hq, R, T))
         x_all = np.zeros((b, hq, R, T))
     valid_full = np.arange(T)[None, None, :] < vis[:, :, None]          # [b, R, T]
+    logw_soft = np.zeros((b, hkv, R, T))
     for r0 in range(0, R, row_block):
         r1 = min(R, r0 + row_block)
         for bi in range(b):
             valid = valid_full[bi, r0:r1]                                 # [rows, T]
             for r in range(hkv):
                 acc = np.zeros((r1 - r0, T))
+                lacc = np.full((r1 - r0, T), -np.inf)     # α = 1: log Σ_h ŵ_h
                 for h in range(r * g, (r + 1) * g):
                     z = (Qr[bi, h, r0:r1] @ kb[bi, r].T) / np.sqrt(d)      # [rows, T]
                     p, t, x = entmax(gamma * z, alpha, valid)
                     acc += p
-                    tau[bi, h, r0:r1] = t
-                    with np.errstate(invalid="ignore"):
-                        gap = np.where(valid, np.abs(x - t[:, None]), np.inf)
-                    if T > 0:
-                        margin[bi, r, r0:r1] = np.minimum(margin[bi, r, r0:r1], gap.min(-1))
+                    if alpha == 1.0:
+                        # softmax routing has no threshold and no support boundary
+                        # (every visible chunk is routed): keep log ŵ for a stable log w
+                        zz = np.where(valid, gamma * z, -np.inf)
+                        m = np.max(zz, -1, keepdims=True) if T else np.zeros((r1 - r0, 1))
+                        m = np.where(np.isfinite(m), m, 0.0)
+                        tot = np.exp(zz - m).sum(-1, keepdims=True)
+                        lse = np.log(np.where(tot > 0, tot, 1.0))
+                        lp = np.where(valid, zz - m - lse, -np.inf)
+                        lacc = np.logaddexp(lacc, lp)
+                    else:
+                        tau[bi, h, r0:r1] = t
+                        with np.errstate(invalid="ignore"):
+                            gap = np.where(valid, np.abs(x - t[:, None]), np.inf)
+                        if T > 0:
+                            margin[bi, r, r0:r1] = np.minimum(margin[bi, r, r0:r1], gap.min(-1))
                     if keep_heads:
                         what_all[bi, h, r0:r1] = p
                         x_all[bi, h, r0:r1] = np.where(valid, x, 0.0)
                 w[bi, r, r0:r1] = acc / g
-    support = w > 0.0
+                if alpha == 1.0:
+                    logw_soft[bi, r, r0:r1] = np.where(valid, lacc - np.log(g), 0.0)
+    if alpha == 1.0:
+        support = np.broadcast_to(valid_full[:, None], w.shape).copy()
+        logw = np.where(support, logw_soft, 0.0)
+    else:
+        support = w > 0.0
+        with np.errstate(divide="ignore"):
+            logw = np.where(support, np.log(np.where(support, w, 1.0)), 0.0)
     cnt = support.sum(-1)
-    with np.errstate(divide="ignore"):
-        logw = np.where(support, np.log(np.where(support, w, 1.0)), 0.0)
     mu = np.where(cnt > 0, logw.sum(-1) / np.maximum(cnt, 1), 0.0)
     if np.isinf(sigma):
         bias = np.zeros_like(w)

@@ -57,7 +57,7 @@ def _route(dash, **kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(Q=NUL), 1), (dict(idx=NUL), 1), (dict(cnt=NUL), 1),
     (dict(h_q=3), 2), (dict(b=0), 2), (dict(n=-1), 2), (dict(cap=3), 2), (dict(list_cap=2), 2),
-    (dict(alpha=1.0), 3), (dict(alpha=float("nan")), 3), (dict(gamma=0.0), 3),
+    (dict(alpha=0.99), 3), (dict(alpha=float("nan")), 3), (dict(gamma=0.0), 3),
     (dict(gamma=float("inf")), 3), (dict(sigma=0.0), 3), (dict(sigma=float("nan")), 3),
     (dict(qdt=7), 3), (dict(causal=2), 3),
     (dict(d=96), 4), (dict(B=24), 4), (dict(h_q=64, h_kv=2), 4), (dict(h_q=6, h_kv=2), 4),
@@ -68,6 +68,12 @@ def _route(dash, **kw):
 def test_route_validation(dash, kw, status):
     assert _route(dash, **kw) == status
     assert dash.lib.dash_last_error().decode() != ""
+
+
+def test_route_accepts_alpha_one(dash):
+    # α = 1 (softmax routing) passes parameter validation; the missing workspace of
+    # this bf16 call is what fails next
+    assert _route(dash, alpha=1.0) == dash.DASH_ERR_WORKSPACE
 
 
 def test_route_bf16_needs_workspace(dash):

@@ -373,3 +373,34 @@ def test_sequence_shorter_than_a_chunk_routes_nothing():
         torch.from_numpy(np.asarray(np.repeat(w.K, 2, axis=1), np.float64)),
         torch.from_numpy(np.asarray(np.repeat(w.V, 2, axis=1), np.float64)), is_causal=True)
     np.testing.assert_allclose(res["O"], ref.numpy(), atol=1e-13)
+
+
+def test_softmax_routing_is_the_entmax_limit():
+    """α = 1 routes with softmax, the α -> 1 limit of entmax (paper review section 三,
+    α-entmax background): its group weights, supports and biases approach those of
+    α-entmax routing as α -> 1, every visible chunk is routed, and each row's group
+    weights sum to one."""
+    w = _small()
+    kb = O.stage0_summaries(w.K, w.qbar, w.B)
+    rows = np.arange(w.n)
+    soft = O.route(w.Q, rows[None], kb, w.B, 1.0, 3.0, 1.0, True, w.n)
+    near = O.route(w.Q, rows[None], kb, w.B, 1.0 + 1e-5, 3.0, 1.0, True, w.n)
+    np.testing.assert_allclose(soft["w"], near["w"], atol=1e-5)
+    assert np.array_equal(soft["cnt"][0, 0], soft["vis"][0])
+    assert np.array_equal(soft["support"], near["support"])
+    np.testing.assert_allclose(soft["bias"], near["bias"], atol=1e-3)
+    has = soft["vis"][0] > 0
+    np.testing.assert_allclose(soft["w"].sum(-1)[..., has], 1.0, atol=1e-12)
+    assert np.isinf(soft["margin"]).all()             # no support boundary to exempt
+
+
+def test_softmax_routing_log_weights_stay_finite():
+    """Softmax routing with a huge γ: the group log-weights (and so the biases) stay
+    finite although the smallest weights underflow in floating point."""
+    w = _small()
+    kb = O.stage0_summaries(w.K, w.qbar, w.B)
+    rows = np.arange(w.n)
+    rt = O.route(w.Q, rows[None], kb, w.B, 1.0, 5000.0, 1.0, True, w.n)
+    sup = rt["support"]
+    assert np.isfinite(rt["bias"][sup]).all()
+    assert (rt["w"][sup] == 0.0).any()

@@ -80,6 +80,8 @@ SMALL = [
     ("bf16", 1, 8, 2, 128, 520, 64, 1.5, 6.0, 1.0, False),      # non-causal with a tail
     ("f32", 1, 2, 1, 128, 300, 32, 1.5, 5.0, 1.0, True),        # fp32, d = 128
     ("bf16", 1, 16, 8, 128, 48, 64, 1.5, 5.0, 1.0, True),       # n < B: no routable chunk
+    ("bf16", 1, 32, 2, 128, 900, 64, 1.0, 3.0, 1.0, True),      # α = 1: softmax routing
+    ("f32", 1, 4, 2, 64, 700, 32, 1.0, 8.0, 0.5, True),         # softmax routing, fp32
 ]
 
 
@@ -186,6 +188,7 @@ DEC = [
     ("bf16", 2, 8, 2, 64, 3000, 32, 2.0, 4.0, [3000, 33]),
     ("bf16", 2, 32, 2, 128, 2048, 64, 1.25, 2.0, [2048, 64]),
     ("f32", 2, 4, 2, 64, 1500, 64, 1.5, 3.0, [1500, 1]),
+    ("bf16", 2, 32, 2, 128, 4096, 64, 1.0, 3.0, [4096, 700]),   # α = 1: softmax routing
 ]
 
 
