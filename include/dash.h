@@ -104,6 +104,23 @@ dash_status dash_route(const void* Q, int q_dtype, const float* kbar,
                        float* w_out, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * dash_route with a fixed routing budget, for ablations against the top-k block
+ * selection the pages compare with (paper review section 二, the hierarchical
+ * sparse attention background): after the group weights w are formed, each row
+ * keeps only the top_k largest w among its routed chunks (all of them when it has
+ * at most top_k; equal weights go to the lower chunk id first), and μ and d are
+ * taken over the kept chunks. top_k = 0 is dash_route. With α = 1 (softmax
+ * routing, every visible chunk has w > 0) each row routes exactly
+ * min(top_k, visible chunks). top_k < 0 returns DASH_ERR_PARAM; everything else
+ * as dash_route.
+ */
+dash_status dash_route_topk(const void* Q, int q_dtype, const float* kbar,
+                            int b, int h_q, int h_kv, int n, int kbar_cap, int d, int B,
+                            float alpha, float gamma, float sigma, int causal,
+                            int32_t* idx, float* bias, int32_t* cnt, int list_cap,
+                            float* w_out, int top_k, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Stage 2 for a prefill (Eq. 10 in the bias form of Prop. 4.1): for every query
  * head and row, softmax over the tokens of the routed chunks (logit
  * <q,k>/sqrt(d) + bias of the chunk) and of the diagonal branch (bias 0, causal

@@ -112,14 +112,15 @@ dash_status dash_summarize(const void* K, int k_dtype, const float* qbar, float*
     return from_hip(dash::launch_summary(a, (hipStream_t)stream), "chunk_summary_kernel");
 }
 
-dash_status dash_route(const void* Q, int q_dtype, const float* kbar,
-                       int b, int h_q, int h_kv, int n, int kbar_cap, int d, int B,
-                       float alpha, float gamma, float sigma, int causal,
-                       int32_t* idx, float* bias, int32_t* cnt, int list_cap,
-                       float* w_out, void* ws, size_t ws_bytes, void* stream) {
+dash_status dash_route_topk(const void* Q, int q_dtype, const float* kbar,
+                            int b, int h_q, int h_kv, int n, int kbar_cap, int d, int B,
+                            float alpha, float gamma, float sigma, int causal,
+                            int32_t* idx, float* bias, int32_t* cnt, int list_cap,
+                            float* w_out, int top_k, void* ws, size_t ws_bytes, void* stream) {
     if (!Q || !kbar || !idx || !bias || !cnt) return fail(DASH_ERR_NULL, "Q, kbar, idx, bias and cnt must be non-null");
     if (!valid_dtype(q_dtype)) return fail(DASH_ERR_PARAM, "bad Q dtype %d", q_dtype);
     if (causal != 0 && causal != 1) return fail(DASH_ERR_PARAM, "causal must be 0 or 1");
+    if (top_k < 0) return fail(DASH_ERR_PARAM, "top_k must be >= 0 (got %d)", top_k);
     dash_status st = check_common(b, h_q, h_kv, d, B);
     if (st != DASH_OK) return st;
     if ((st = check_params(alpha, gamma, sigma)) != DASH_OK) return st;
@@ -138,8 +139,17 @@ dash_status dash_route(const void* Q, int q_dtype, const float* kbar,
             return fail(DASH_ERR_WORKSPACE, "bf16 routing needs %zu workspace bytes, got %zu", need, ws ? ws_bytes : (size_t)0);
     }
     dash::RouteArgs a{Q, q_dtype == DASH_BF16, kbar, b, h_q, h_kv, n, kbar_cap, d, B, causal, list_cap,
-                      alpha, gamma, sigma, idx, bias, cnt, w_out, ws};
+                      alpha, gamma, sigma, idx, bias, cnt, w_out, ws, top_k};
     return from_hip(dash::launch_route(a, (hipStream_t)stream), "entmax_route_kernel");
+}
+
+dash_status dash_route(const void* Q, int q_dtype, const float* kbar,
+                       int b, int h_q, int h_kv, int n, int kbar_cap, int d, int B,
+                       float alpha, float gamma, float sigma, int causal,
+                       int32_t* idx, float* bias, int32_t* cnt, int list_cap,
+                       float* w_out, void* ws, size_t ws_bytes, void* stream) {
+    return dash_route_topk(Q, q_dtype, kbar, b, h_q, h_kv, n, kbar_cap, d, B, alpha, gamma, sigma, causal, idx,
+                           bias, cnt, list_cap, w_out, 0, ws, ws_bytes, stream);
 }
 
 dash_status dash_attend_prefill(const void* Q, const void* K, const void* V, int in_dtype,

@@ -20,6 +20,7 @@ struct RouteArgs {
     float alpha, gamma, sigma;
     int32_t* idx; float* bias; int32_t* cnt; float* w_out;
     void* ws;            // bf16 queries: split summaries, route_workspace_bytes
+    int top_k;           // > 0: fixed budget of routed chunks per row
 };
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
 // Scale of the routing logits: (α-1)γ/sqrt(d) for entmax, γ log2(e)/sqrt(d) for α = 1.

@@ -41,7 +41,14 @@ struct RouteParams {
     float pexp;         // 1/(α-1)
     int pmode;          // 1, 2, 4 for integer exponents, 0 otherwise, kSoftmaxRouting for α = 1
     float inv_sigma;    // 1/σ (0 for σ = inf)
+    int top_k;          // > 0: keep only the top_k largest group weights of each row
 };
+
+// Order-preserving map of a float to an unsigned key (larger float, larger key).
+__device__ __forceinline__ uint32_t float_key(float v) {
+    const uint32_t u = __float_as_uint(v);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
 
 // Routing with α = 1: per-head softmax weights instead of entmax (every visible chunk
 // is routed); p.cs then holds γ log2(e)/sqrt(d).
@@ -529,18 +536,65 @@ __global__ __launch_bounds__(512) void entmax_route_kernel(RouteParams p) {
     if (!wave_live) return;                           // no barrier follows
 
     // compaction: ascending chunk ids of the support, with d = (ln w - μ)/σ (with
-    // α = 1 the LDS holds log2 w and every visible chunk is in the support)
+    // α = 1 the LDS holds log2 w and every visible chunk is in the support). With a
+    // top-k budget the support keeps its top_k largest weights (ties to the lower
+    // chunk): the k-th largest key is found by bisection on the key bits, counted
+    // with ballots over the row.
     constexpr bool SOFT = PM == kSoftmaxRouting;
+    constexpr int NK = (WS + 63) / 64;                // keys per lane
     const size_t rowbase = ((size_t)bi * p.h_kv + r) * p.n;
     for (int j = 0; j < R; ++j) {
         const int row = row0 + j;
         if (row >= p.n) break;
         const float* wr = wl + j * WS;
+        auto cand = [&](int c, float v) { return c < nvis && (SOFT || v > 0.f); };
+        bool limit = false;
+        uint32_t kstar = 0;
+        int need_eq = 0;
+        if (p.top_k > 0) {
+            uint32_t key[NK];
+            int ncand = 0;
+#pragma unroll
+            for (int q = 0; q < NK; ++q) {
+                const int c = lane + 64 * q;
+                const float v = c < nvis ? wr[c] : 0.f;
+                const bool in = cand(c, v);
+                key[q] = in ? float_key(v) : 0u;
+                ncand += __builtin_popcountll(ballot(in));
+            }
+            if (ncand > p.top_k) {                    // wavefront-uniform
+                limit = true;
+                uint32_t prefix = 0;
+                for (int bit = 31; bit >= 0; --bit) {
+                    const uint32_t trial = prefix | (1u << bit);
+                    int cnt = 0;
+#pragma unroll
+                    for (int q = 0; q < NK; ++q) cnt += __builtin_popcountll(ballot(key[q] >= trial));
+                    if (cnt >= p.top_k) prefix = trial;
+                }
+                kstar = prefix;
+                int gt = 0;
+#pragma unroll
+                for (int q = 0; q < NK; ++q) gt += __builtin_popcountll(ballot(key[q] > kstar));
+                need_eq = p.top_k - gt;
+            }
+        }
+        // membership of chunk c (value v) given the running count of earlier ties
+        auto selected = [&](int c, float v, int& eq_before) {
+            const bool in = cand(c, v);
+            if (!limit) return in;
+            const uint32_t k = in ? float_key(v) : 0u;
+            const uint64_t eq = ballot(in && k == kstar);
+            const int rank = eq_before + __builtin_popcountll(eq & ((1ull << lane) - 1ull));
+            eq_before += __builtin_popcountll(eq);
+            return in && (k > kstar || (k == kstar && rank < need_eq));
+        };
         float sl = 0.f, sc = 0.f;
-        for (int c = lane; c < nvis; c += 64) {
-            const float v = wr[c];
-            if (SOFT) { sl += v; sc += 1.f; }
-            else if (v > 0.f) { sl += fast_log2(v); sc += 1.f; }
+        int eqb = 0;
+        for (int c0 = 0; c0 < nvis; c0 += 64) {
+            const int c = c0 + lane;
+            const float v = c < nvis ? wr[c] : 0.f;
+            if (selected(c, v, eqb)) { sl += SOFT ? v : fast_log2(v); sc += 1.f; }
         }
         sl = wave_sum(sl);
         sc = wave_sum(sc);
@@ -550,10 +604,11 @@ __global__ __launch_bounds__(512) void entmax_route_kernel(RouteParams p) {
         float* bias = p.bias + (rowbase + row) * (size_t)p.list_cap;
         float* wo = p.w_out ? p.w_out + (rowbase + row) * (size_t)p.kbar_cap : nullptr;
         int base = 0;
+        eqb = 0;
         for (int c0 = 0; c0 < p.T_c; c0 += 64) {
             const int c = c0 + lane;
             const float v = (c < nvis) ? wr[c] : (SOFT ? -INFINITY : 0.f);
-            const bool in = SOFT ? c < nvis : v > 0.f;
+            const bool in = selected(c, v, eqb);
             const uint64_t m = ballot(in);
             const int pre = __builtin_popcountll(m & ((1ull << lane) - 1ull));
             if (in) {

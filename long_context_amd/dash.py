@@ -34,6 +34,9 @@ def _load():
     lib.dash_route.argtypes = [vp, i32, vp, i32, i32, i32, i32, i32, i32, i32, f32, f32, f32, i32,
                                vp, vp, vp, i32, vp, vp, sz, vp]
     lib.dash_route.restype = i32
+    lib.dash_route_topk.argtypes = [vp, i32, vp, i32, i32, i32, i32, i32, i32, i32, f32, f32, f32, i32,
+                                    vp, vp, vp, i32, vp, i32, vp, sz, vp]
+    lib.dash_route_topk.restype = i32
     lib.dash_attend_prefill.argtypes = [vp, vp, vp, i32, vp, vp, vp, i32, vp, i32,
                                         i32, i32, i32, i32, i32, i32, i32, vp, sz, vp]
     lib.dash_attend_prefill.restype = i32
@@ -51,7 +54,7 @@ def _load():
 
 lib = _load()
 
-SYMBOLS = ("dash_summarize", "dash_route", "dash_attend_prefill", "dash_attend_decode",
+SYMBOLS = ("dash_summarize", "dash_route", "dash_route_topk", "dash_attend_prefill", "dash_attend_decode",
            "dash_workspace_bytes", "dash_status_string", "dash_last_error")
 
 
@@ -106,19 +109,23 @@ def dash_summarize(K, qbar, kbar, B, chunk_begin=0, chunk_end=None, stream=None)
 
 
 def dash_route(Q, kbar, B, alpha, gamma, sigma, causal, idx, bias, cnt, w_out=None,
-               ws=None, stream=None):
+               ws=None, stream=None, top_k=0):
     """Stage 1 of a prefill: routed chunk lists idx/bias [b,h_kv,n,cap] and cnt [b,h_kv,n].
 
-    bf16 queries need a workspace (alloc_route_ws); one is allocated when ws is None."""
+    bf16 queries need a workspace (alloc_route_ws); one is allocated when ws is None.
+    top_k > 0 calls dash_route_topk (a fixed budget of routed chunks per row)."""
     b, h_q, n, d = Q.shape
     h_kv = kbar.shape[1]
     if ws is None and Q.dtype == torch.bfloat16:
         ws = alloc_route_ws(b, h_q, h_kv, n, d, B, device=Q.device)
-    _check(lib.dash_route(_ptr(Q), _dtype(Q), _ptr(kbar), b, h_q, h_kv, n, kbar.shape[2], d, B,
-                          float(alpha), float(gamma), float(sigma), int(causal),
-                          _ptr(idx), _ptr(bias), _ptr(cnt), idx.shape[-1], _ptr(w_out),
-                          _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
-                          _stream(stream)))
+    args = (_ptr(Q), _dtype(Q), _ptr(kbar), b, h_q, h_kv, n, kbar.shape[2], d, B,
+            float(alpha), float(gamma), float(sigma), int(causal),
+            _ptr(idx), _ptr(bias), _ptr(cnt), idx.shape[-1], _ptr(w_out))
+    tail = (_ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
+    if top_k:
+        _check(lib.dash_route_topk(*args, int(top_k), *tail))
+    else:
+        _check(lib.dash_route(*args, *tail))
 
 
 def dash_attend_prefill(Q, K, V, idx, bias, cnt, O, B, causal, ws=None, stream=None):

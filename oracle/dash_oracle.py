@@ -189,7 +189,7 @@ def visible_chunks(pos, B, T, causal):
 
 
 def route(Qr, pos, kbar, B, alpha, gamma, sigma, causal, n_kv, keep_heads=False,
-          row_block=256):
+          row_block=256, top_k=0):
     """Stage 1 routing for query rows Qr [b, h_q, R, d] at token positions pos [b, R].
 
     For every query head h (KV group r = floor(h/g)) and row i:
@@ -204,7 +204,12 @@ def route(Qr, pos, kbar, B, alpha, gamma, sigma, causal, n_kv, keep_heads=False,
       w [b,h_kv,R,T], support [b,h_kv,R,T], bias [b,h_kv,R,T] (0 off support),
       mu [b,h_kv,R], vis [b,R], tau [b,h_q,R], margin [b,h_kv,R]
       (min over the group's heads and visible chunks of |x - τ|, x = (α-1)γz̄),
+      margin_topk [b,h_kv,R] (top_k > 0: log-weight gap between the last kept and the
+      first dropped chunk, inf where nothing is dropped),
       and when keep_heads: what [b,h_q,R,T], x [b,h_q,R,T].
+    top_k > 0 keeps only the top_k largest group weights of each row's support (a
+    fixed routing budget for ablations; equal weights go to the lower chunk id), and
+    μ and d are taken over the kept chunks.
     """
     Qr = _f64(Qr)
     kbar = _f64(kbar)
@@ -262,6 +267,20 @@ def route(Qr, pos, kbar, B, alpha, gamma, sigma, causal, n_kv, keep_heads=False,
         support = w > 0.0
         with np.errstate(divide="ignore"):
             logw = np.where(support, np.log(np.where(support, w, 1.0)), 0.0)
+    margin_topk = np.full(w.shape[:-1], np.inf)
+    if top_k > 0:
+        # fixed budget: the top_k largest weights of each row's support, equal weights
+        # to the lower chunk id; margin_topk is the log-weight gap at the cut
+        for ix in np.ndindex(*w.shape[:-1]):
+            cs = np.nonzero(support[ix])[0]
+            if cs.size <= top_k:
+                continue
+            order = sorted(cs.tolist(), key=lambda c: (-logw[ix][c], c))
+            keep = np.zeros(w.shape[-1], bool)
+            keep[order[:top_k]] = True
+            margin_topk[ix] = logw[ix][order[top_k - 1]] - logw[ix][order[top_k]]
+            support[ix] = keep
+            logw[ix] = np.where(keep, logw[ix], 0.0)
     cnt = support.sum(-1)
     mu = np.where(cnt > 0, logw.sum(-1) / np.maximum(cnt, 1), 0.0)
     if np.isinf(sigma):
@@ -269,7 +288,7 @@ def route(Qr, pos, kbar, B, alpha, gamma, sigma, causal, n_kv, keep_heads=False,
     else:
         bias = np.where(support, (logw - mu[..., None]) / sigma, 0.0)
     out = dict(w=w, support=support, bias=bias, mu=mu, vis=vis, tau=tau, margin=margin,
-               cnt=cnt)
+               cnt=cnt, margin_topk=margin_topk)
     if keep_heads:
         out["what"] = what_all
         out["x"] = x_all

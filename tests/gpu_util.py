@@ -21,6 +21,7 @@ from oracle import dash_oracle as O
 MARGIN = 1e-6
 TOL_KBAR = 1e-4
 TOL_W = 1e-3
+TOPK_MARGIN = 1e-5
 TOL_F32 = 1e-4
 TOL_BF16_ROW = 2e-2
 
@@ -30,7 +31,8 @@ def to_dev(x, dtype):
     return t.to(device="cuda", dtype=torch.bfloat16 if dtype == "bf16" else torch.float32)
 
 
-def gpu_prefill(w, alpha=None, gamma=None, sigma=None, causal=None, with_w=True, out_dtype=torch.float32):
+def gpu_prefill(w, alpha=None, gamma=None, sigma=None, causal=None, with_w=True, out_dtype=torch.float32,
+                top_k=0):
     alpha = w.alpha if alpha is None else alpha
     gamma = w.gamma if gamma is None else gamma
     sigma = w.sigma if sigma is None else sigma
@@ -44,14 +46,14 @@ def gpu_prefill(w, alpha=None, gamma=None, sigma=None, causal=None, with_w=True,
     idx, bias, cnt, wo = dash.alloc_route(b, w.h_kv, n, T, with_w=with_w)
     if with_w:
         wo.zero_()
-    dash.dash_route(Q, kbar, w.B, alpha, gamma, sigma, causal, idx, bias, cnt, wo)
+    dash.dash_route(Q, kbar, w.B, alpha, gamma, sigma, causal, idx, bias, cnt, wo, top_k=top_k)
     Oo = torch.empty((b, h_q, n, d), dtype=out_dtype, device="cuda")
     dash.dash_attend_prefill(Q, K, V, idx, bias, cnt, Oo, w.B, causal)
     torch.cuda.synchronize()
     return dict(kbar=kbar, idx=idx, bias=bias, cnt=cnt, w=wo, O=Oo, T=T)
 
 
-def oracle_prefill_rows(w, rows, kbar_or=None, alpha=None, gamma=None, sigma=None, causal=None):
+def oracle_prefill_rows(w, rows, kbar_or=None, alpha=None, gamma=None, sigma=None, causal=None, top_k=0):
     alpha = w.alpha if alpha is None else alpha
     gamma = w.gamma if gamma is None else gamma
     sigma = w.sigma if sigma is None else sigma
@@ -60,16 +62,22 @@ def oracle_prefill_rows(w, rows, kbar_or=None, alpha=None, gamma=None, sigma=Non
     rows = np.asarray(rows)
     b = w.Q.shape[0]
     pos = np.broadcast_to(rows, (b, rows.size))
-    rt = O.route(w.Q[:, :, rows], pos, kb, w.B, alpha, gamma, sigma, causal, w.n)
+    rt = O.route(w.Q[:, :, rows], pos, kb, w.B, alpha, gamma, sigma, causal, w.n, top_k=top_k)
     out = O.attend(w.Q[:, :, rows], pos, w.K, w.V, rt, w.B, causal, w.n)
     return kb, rt, out
+
+
+def exempt_rows(rt):
+    """Rows whose support the float64 oracle decides within rounding distance: a chunk
+    with |x - τ| <= MARGIN, or (top-k budget) a log-weight gap <= TOPK_MARGIN at the cut."""
+    return (rt["margin"] <= MARGIN) | (rt["margin_topk"] <= TOPK_MARGIN)
 
 
 def compare_route(g, rt, rows, T):
     """Returns (n_exempt, n_rows) after asserting lists and weights."""
     cnt = g["cnt"][:, :, rows].cpu().numpy()
     idx = g["idx"][:, :, rows].cpu().numpy()
-    exempt = rt["margin"] <= MARGIN                      # [b, h_kv, R]
+    exempt = exempt_rows(rt)                             # [b, h_kv, R]
     if g.get("w") is not None and T > 0:
         wg = g["w"][:, :, rows, :T].cpu().numpy()
         dw = np.abs(wg - rt["w"]).max()

@@ -70,6 +70,24 @@ def test_route_validation(dash, kw, status):
     assert dash.lib.dash_last_error().decode() != ""
 
 
+def _route_topk(dash, top_k, **kw):
+    a = dict(Q=P, qdt=1, kbar=P, b=1, h_q=4, h_kv=2, n=256, cap=4, d=128, B=64, alpha=1.5,
+             gamma=1.0, sigma=1.0, causal=1, idx=P, bias=P, cnt=P, list_cap=4, w=NUL)
+    a.update(kw)
+    return dash.lib.dash_route_topk(a["Q"], a["qdt"], a["kbar"], a["b"], a["h_q"], a["h_kv"], a["n"],
+                                    a["cap"], a["d"], a["B"], a["alpha"], a["gamma"], a["sigma"],
+                                    a["causal"], a["idx"], a["bias"], a["cnt"], a["list_cap"], a["w"],
+                                    top_k, NUL, 0, NUL)
+
+
+def test_route_topk_validation(dash):
+    assert _route_topk(dash, -1) == dash.DASH_ERR_PARAM
+    assert "top_k" in dash.lib.dash_last_error().decode()
+    assert _route_topk(dash, 2, Q=NUL) == dash.DASH_ERR_NULL
+    assert _route_topk(dash, 2, alpha=0.5) == dash.DASH_ERR_PARAM
+    assert _route_topk(dash, 2) == dash.DASH_ERR_WORKSPACE        # valid up to the workspace
+
+
 def test_route_accepts_alpha_one(dash):
     # α = 1 (softmax routing) passes parameter validation; the missing workspace of
     # this bf16 call is what fails next

@@ -404,3 +404,39 @@ def test_softmax_routing_log_weights_stay_finite():
     sup = rt["support"]
     assert np.isfinite(rt["bias"][sup]).all()
     assert (rt["w"][sup] == 0.0).any()
+
+
+def test_topk_keeps_the_heaviest_subset():
+    """A fixed budget keeps, per row, the k-subset of the support with the largest
+    total group weight (brute force over all k-subsets on a small case), μ is the
+    mean log-weight of the kept chunks (so the kept biases average to zero), and a
+    budget at least the support size changes nothing."""
+    w = _small()
+    kb = O.stage0_summaries(w.K, w.qbar, w.B)
+    rows = np.arange(w.B, w.n, 7)
+    full = O.route(w.Q[:, :, rows], rows[None], kb, w.B, 1.5, 1.0, 1.0, True, w.n)
+    k = 3
+    rt = O.route(w.Q[:, :, rows], rows[None], kb, w.B, 1.5, 1.0, 1.0, True, w.n, top_k=k)
+    checked = 0
+    for ix in np.ndindex(*full["cnt"].shape):
+        cs = np.nonzero(full["support"][ix])[0]
+        kept = np.nonzero(rt["support"][ix])[0]
+        assert kept.size == min(k, cs.size)
+        if cs.size > k:
+            best = max(itertools.combinations(cs.tolist(), k), key=lambda sub: sum(full["w"][ix][list(sub)]))
+            assert set(kept.tolist()) == set(best)
+            checked += 1
+        np.testing.assert_allclose(rt["bias"][ix][kept].mean() if kept.size else 0.0, 0.0, atol=1e-12)
+    assert checked > 0
+    big = O.route(w.Q[:, :, rows], rows[None], kb, w.B, 1.5, 1.0, 1.0, True, w.n, top_k=10_000)
+    assert np.array_equal(big["support"], full["support"])
+    np.testing.assert_allclose(big["bias"], full["bias"], atol=0)
+
+
+def test_topk_with_softmax_routing_is_a_fixed_budget():
+    """α = 1 routes every visible chunk, so a budget k routes exactly min(k, visible)."""
+    w = _small()
+    kb = O.stage0_summaries(w.K, w.qbar, w.B)
+    rows = np.arange(w.n)
+    rt = O.route(w.Q, rows[None], kb, w.B, 1.0, 3.0, 1.0, True, w.n, top_k=4)
+    assert np.array_equal(rt["cnt"][0, 0], np.minimum(4, rt["vis"][0]))

@@ -181,6 +181,31 @@ def check_decode(w, seq_len, g):
     return nex, max(errs)
 
 
+TOPK = [
+    # dtype, b, h_q, h_kv, d, n, B, alpha, gamma, sigma, top_k
+    ("bf16", 1, 32, 2, 128, 900, 64, 1.0, 3.0, 1.0, 4),          # softmax routing, budget 4
+    ("bf16", 1, 16, 2, 128, 1000, 64, 1.5, 2.0, 1.0, 3),         # entmax routing cut to 3
+    ("f32", 1, 4, 2, 64, 700, 32, 1.5, 2.0, float("inf"), 2),    # fp32, σ = inf
+    ("bf16", 1, 16, 2, 128, 40000, 32, 1.0, 6.0, 1.0, 16),       # 1250 chunks (4 wavefronts per row)
+]
+
+
+@pytest.mark.parametrize("case", TOPK, ids=[f"{c[0]}-g{c[2] // c[3]}-n{c[5]}-a{c[7]}-k{c[10]}" for c in TOPK])
+def test_prefill_topk_matches_oracle(case):
+    G = _gu()
+    dtype, b, h_q, h_kv, d, n, B, alpha, gamma, sigma, k = case
+    w = inputs.make_prefill(b=b, h_q=h_q, h_kv=h_kv, d=d, n=n, B=B, alphas=(alpha,), gamma=gamma,
+                            sigma=sigma, causal=True, dtype=dtype, seed=11)
+    _log(f"top-k case {case}")
+    g = G.gpu_prefill(w, top_k=k)
+    rows = np.arange(n) if n <= 2048 else _sample_rows(n, B, 96, 5)
+    kb, rt, Oref = G.oracle_prefill_rows(w, rows, top_k=k)
+    nex, tot = G.compare_route(g, rt, rows, n // B)
+    assert (g["cnt"].cpu().numpy() <= k).all()
+    err = G.compare_out(g["O"][:, :, rows].cpu().numpy(), Oref, G.exempt_rows(rt), h_q // h_kv, dtype)
+    _log(f"  exempt rows {nex}/{tot}, output error {err:.3e}")
+
+
 DEC = [
     # dtype, b, h_q, h_kv, d, L, B, alpha, gamma, seq_len
     ("bf16", 3, 32, 2, 128, 4096, 64, 1.5, 1.0, [4096, 4000, 65]),
