@@ -121,6 +121,18 @@ dash_status dash_route_topk(const void* Q, int q_dtype, const float* kbar,
                             float* w_out, int top_k, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Bitpacked block mask of routed lists (the form of the routing decision in the
+ * pages' GPU kernel table: M_i in {0,1}^{T_c}, 32 chunks per 32-bit word): for every
+ * (b, r, row) of idx [b, h_kv, n, list_cap] / cnt [b, h_kv, n] (device int32, as
+ * dash_route writes them), mask [b, h_kv, n, words] (device uint32) gets bit c % 32
+ * of word c / 32 set iff chunk c (0 <= c < T_c) is listed; all other bits are zero.
+ * Requires list_cap >= T_c, T_c <= 2048 and ceil(T_c/32) <= words <= 64. List
+ * entries outside [0, T_c) and counts outside [0, list_cap] are clamped away.
+ */
+dash_status dash_route_mask(const int32_t* idx, const int32_t* cnt, int b, int h_kv, int n, int list_cap,
+                            int T_c, uint32_t* mask, int words, void* stream);
+
+/*
  * Stage 2 for a prefill (Eq. 10 in the bias form of Prop. 4.1): for every query
  * head and row, softmax over the tokens of the routed chunks (logit
  * <q,k>/sqrt(d) + bias of the chunk) and of the diagonal branch (bias 0, causal

@@ -152,6 +152,20 @@ dash_status dash_route(const void* Q, int q_dtype, const float* kbar,
                            bias, cnt, list_cap, w_out, 0, ws, ws_bytes, stream);
 }
 
+dash_status dash_route_mask(const int32_t* idx, const int32_t* cnt, int b, int h_kv, int n, int list_cap,
+                            int T_c, uint32_t* mask, int words, void* stream) {
+    if (!idx || !cnt || !mask) return fail(DASH_ERR_NULL, "idx, cnt and mask must be non-null");
+    if (b < 1 || h_kv < 1 || n < 0) return fail(DASH_ERR_SHAPE, "need b >= 1, h_kv >= 1, n >= 0");
+    if (T_c < 0 || T_c > 2048) return fail(DASH_ERR_UNSUPPORTED, "T_c must be in [0, 2048] (got %d)", T_c);
+    if (list_cap < T_c) return fail(DASH_ERR_SHAPE, "list_cap %d < T_c %d", list_cap, T_c);
+    if (words < (T_c + 31) / 32 || words > 64)
+        return fail(DASH_ERR_SHAPE, "words must be in [ceil(T_c/32), 64] (got %d for T_c %d)", words, T_c);
+    if (words == 0) return DASH_OK;
+    return from_hip(dash::launch_lists_to_mask(idx, cnt, (size_t)b * h_kv * n, list_cap, T_c, mask, words,
+                                               (hipStream_t)stream),
+                    "lists_to_mask_kernel");
+}
+
 dash_status dash_attend_prefill(const void* Q, const void* K, const void* V, int in_dtype,
                                 const int32_t* idx, const float* bias, const int32_t* cnt,
                                 int list_cap, void* O, int out_dtype,

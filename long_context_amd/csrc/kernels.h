@@ -23,6 +23,9 @@ struct RouteArgs {
     int top_k;           // > 0: fixed budget of routed chunks per row
 };
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
+// Routed lists -> bitpacked mask [rows][words] (bit c%32 of word c/32 = chunk c routed).
+hipError_t launch_lists_to_mask(const int32_t* idx, const int32_t* cnt, size_t rows, int list_cap, int T_c,
+                                uint32_t* mask, int words, hipStream_t s);
 // Scale of the routing logits: (α-1)γ/sqrt(d) for entmax, γ log2(e)/sqrt(d) for α = 1.
 float route_scale(float alpha, float gamma, int d);
 // Workspace of a bf16-query routing: the summaries split into three bf16 terms,

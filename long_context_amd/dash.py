@@ -37,6 +37,8 @@ def _load():
     lib.dash_route_topk.argtypes = [vp, i32, vp, i32, i32, i32, i32, i32, i32, i32, f32, f32, f32, i32,
                                     vp, vp, vp, i32, vp, i32, vp, sz, vp]
     lib.dash_route_topk.restype = i32
+    lib.dash_route_mask.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, i32, vp]
+    lib.dash_route_mask.restype = i32
     lib.dash_attend_prefill.argtypes = [vp, vp, vp, i32, vp, vp, vp, i32, vp, i32,
                                         i32, i32, i32, i32, i32, i32, i32, vp, sz, vp]
     lib.dash_attend_prefill.restype = i32
@@ -54,7 +56,8 @@ def _load():
 
 lib = _load()
 
-SYMBOLS = ("dash_summarize", "dash_route", "dash_route_topk", "dash_attend_prefill", "dash_attend_decode",
+SYMBOLS = ("dash_summarize", "dash_route", "dash_route_topk", "dash_route_mask", "dash_attend_prefill",
+           "dash_attend_decode",
            "dash_workspace_bytes", "dash_status_string", "dash_last_error")
 
 
@@ -126,6 +129,13 @@ def dash_route(Q, kbar, B, alpha, gamma, sigma, causal, idx, bias, cnt, w_out=No
         _check(lib.dash_route_topk(*args, int(top_k), *tail))
     else:
         _check(lib.dash_route(*args, *tail))
+
+
+def dash_route_mask(idx, cnt, T_c, mask, stream=None):
+    """Bitpacked mask [b,h_kv,n,words] (int32 storage of uint32 words) of routed lists."""
+    b, h_kv, n, cap = idx.shape
+    _check(lib.dash_route_mask(_ptr(idx), _ptr(cnt), b, h_kv, n, cap, int(T_c), _ptr(mask),
+                               mask.shape[-1], _stream(stream)))
 
 
 def dash_attend_prefill(Q, K, V, idx, bias, cnt, O, B, causal, ws=None, stream=None):

@@ -295,6 +295,18 @@ def route(Qr, pos, kbar, B, alpha, gamma, sigma, causal, n_kv, keep_heads=False,
     return out
 
 
+def route_mask(support, words):
+    """Bitpacked block mask of a routing (paper review section 三, GPU kernel table:
+    M_i in {0,1}^{T_c}, 32 chunks per 32-bit word): bit c % 32 of word c // 32 is
+    set iff chunk c is in the support. support [..., T] bool -> [..., words] uint32."""
+    support = np.asarray(support, bool)
+    T = support.shape[-1]
+    out = np.zeros(support.shape[:-1] + (words,), np.uint32)
+    for c in range(T):
+        out[..., c // 32] |= support[..., c].astype(np.uint32) << np.uint32(c % 32)
+    return out
+
+
 def diagonal_range(pos, B, T, n_kv, causal):
     """Token range [lo, hi) of the diagonal branch D for a query at `pos`."""
     if causal:

@@ -88,6 +88,17 @@ def test_route_topk_validation(dash):
     assert _route_topk(dash, 2) == dash.DASH_ERR_WORKSPACE        # valid up to the workspace
 
 
+def test_route_mask_validation(dash):
+    m = dash.lib.dash_route_mask
+    assert m(NUL, P, 1, 2, 64, 4, 4, P, 1, NUL) == dash.DASH_ERR_NULL
+    assert m(P, P, 0, 2, 64, 4, 4, P, 1, NUL) == dash.DASH_ERR_SHAPE
+    assert m(P, P, 1, 2, 64, 40, 40, P, 1, NUL) == dash.DASH_ERR_SHAPE      # 40 chunks need 2 words
+    assert m(P, P, 1, 2, 64, 4, 4, P, 65, NUL) == dash.DASH_ERR_SHAPE       # at most 64 words
+    assert m(P, P, 1, 2, 64, 2, 4, P, 1, NUL) == dash.DASH_ERR_SHAPE        # list_cap < T_c
+    assert m(P, P, 1, 2, 64, 4096, 4096, P, 64, NUL) == dash.DASH_ERR_UNSUPPORTED
+    assert m(P, P, 1, 2, 64, 0, 0, P, 0, NUL) == dash.DASH_OK                # nothing to write
+
+
 def test_route_accepts_alpha_one(dash):
     # α = 1 (softmax routing) passes parameter validation; the missing workspace of
     # this bf16 call is what fails next

@@ -440,3 +440,18 @@ def test_topk_with_softmax_routing_is_a_fixed_budget():
     rows = np.arange(w.n)
     rt = O.route(w.Q, rows[None], kb, w.B, 1.0, 3.0, 1.0, True, w.n, top_k=4)
     assert np.array_equal(rt["cnt"][0, 0], np.minimum(4, rt["vis"][0]))
+
+
+def test_route_mask_matches_little_endian_bit_packing():
+    """The oracle's bitpacked mask equals numpy's little-endian bit packing read as
+    32-bit little-endian words, and unpacks back to the support."""
+    rng = np.random.default_rng(4)
+    sup = rng.random((2, 3, 5, 70)) < 0.3
+    words = 3
+    m = O.route_mask(sup, words)
+    padded = np.zeros(sup.shape[:-1] + (words * 32,), bool)
+    padded[..., :70] = sup
+    ref = np.packbits(padded, axis=-1, bitorder="little").view("<u4")
+    assert np.array_equal(m, ref)
+    back = np.unpackbits(m.view(np.uint8), axis=-1, bitorder="little")[..., :70].astype(bool)
+    assert np.array_equal(back, sup)

@@ -206,6 +206,33 @@ def test_prefill_topk_matches_oracle(case):
     _log(f"  exempt rows {nex}/{tot}, output error {err:.3e}")
 
 
+def test_route_mask_matches_lists_and_oracle():
+    """Bitpacked mask of the GPU's routed lists: equal to the lists packed on the host
+    for every row, and to the oracle's support off the exempt rows."""
+    G = _gu()
+    from oracle import dash_oracle as O
+    from long_context_amd import dash
+    w = inputs.make_prefill(b=2, h_q=16, h_kv=2, d=128, n=2500, B=32, alphas=(1.5,), gamma=4.0,
+                            sigma=1.0, causal=True, dtype="bf16", seed=21)
+    _log("mask case bf16 g8 n2500 B32")
+    g = G.gpu_prefill(w)
+    T = 2500 // 32
+    words = (T + 31) // 32
+    mask = torch.zeros((2, 2, 2500, words), dtype=torch.int32, device="cuda")
+    dash.dash_route_mask(g["idx"], g["cnt"], T, mask)
+    got = mask.cpu().numpy().view(np.uint32)
+    idx, cnt = g["idx"].cpu().numpy(), g["cnt"].cpu().numpy()
+    sup = np.zeros((2, 2, 2500, T), bool)
+    for ix in np.ndindex(*cnt.shape):
+        sup[ix][idx[ix][:cnt[ix]]] = True
+    assert np.array_equal(got, O.route_mask(sup, words))
+    rows = _sample_rows(2500, 32, 64, 9)
+    _, rt, _ = G.oracle_prefill_rows(w, rows)
+    ref = O.route_mask(rt["support"], words)
+    keep = ~G.exempt_rows(rt)
+    assert np.array_equal(got[:, :, rows][keep], ref[keep])
+
+
 DEC = [
     # dtype, b, h_q, h_kv, d, L, B, alpha, gamma, seq_len
     ("bf16", 3, 32, 2, 128, 4096, 64, 1.5, 1.0, [4096, 4000, 65]),
