@@ -172,6 +172,29 @@ dash_status dash_attend_decode(const void* Q, const void* Kc, const void* Vc, in
                                float* w_out, int list_cap,
                                void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * Paged KV cache (serving): pages of one chunk each. Kp, Vp are
+ * [num_pages, h_kv, B, d]; chunk c of sequence b (tokens cB .. cB+B-1) lives in
+ * page pages[b * pages_per_seq + c] (device int32 table [b, pages_per_seq]), so a
+ * sequence holds at most L_cap = pages_per_seq * B tokens. Everything else is as in
+ * dash_summarize / dash_attend_decode with that L_cap (the workspace is
+ * dash_workspace_bytes(DASH_OP_DECODE, b, h_q, h_kv, pages_per_seq * B, d, B)).
+ * Page ids outside [0, num_pages) are clamped (wrong output, never a stray read).
+ */
+dash_status dash_summarize_paged(const void* Kp, int k_dtype, const float* qbar, float* kbar,
+                                 const int32_t* pages, int pages_per_seq, int num_pages,
+                                 int b, int h_kv, int kbar_cap, int d, int B,
+                                 int chunk_begin, int chunk_end, void* stream);
+dash_status dash_attend_decode_paged(const void* Q, const void* Kp, const void* Vp, int in_dtype,
+                                     const float* kbar, const int32_t* seq_len,
+                                     const int32_t* pages, int pages_per_seq, int num_pages,
+                                     int b, int h_q, int h_kv, int kbar_cap, int d, int B,
+                                     float alpha, float gamma, float sigma,
+                                     void* O, int out_dtype,
+                                     int32_t* idx_out, float* bias_out, int32_t* cnt_out,
+                                     float* w_out, int list_cap,
+                                     void* ws, size_t ws_bytes, void* stream);
+
 /* Workspace bytes an operation needs (n_or_Lcap: n for prefill ops, L_cap for
  * decode; DASH_OP_ROUTE and DASH_OP_PREFILL give the size for bf16 inputs, which
  * fp32 inputs do not need). Returns 0 when no

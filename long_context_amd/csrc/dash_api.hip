@@ -112,6 +112,24 @@ dash_status dash_summarize(const void* K, int k_dtype, const float* qbar, float*
     return from_hip(dash::launch_summary(a, (hipStream_t)stream), "chunk_summary_kernel");
 }
 
+dash_status dash_summarize_paged(const void* Kp, int k_dtype, const float* qbar, float* kbar,
+                                 const int32_t* pages, int pages_per_seq, int num_pages,
+                                 int b, int h_kv, int kbar_cap, int d, int B,
+                                 int chunk_begin, int chunk_end, void* stream) {
+    if (!Kp || !qbar || !kbar || !pages) return fail(DASH_ERR_NULL, "Kp, qbar, kbar and pages must be non-null");
+    if (!valid_dtype(k_dtype)) return fail(DASH_ERR_PARAM, "bad K dtype %d", k_dtype);
+    dash_status st = check_common(b, h_kv, h_kv, d, B);
+    if (st != DASH_OK) return st;
+    if (pages_per_seq < 1 || num_pages < 1 || kbar_cap < 0)
+        return fail(DASH_ERR_SHAPE, "pages_per_seq and num_pages must be >= 1 and kbar_cap >= 0");
+    const int lim = pages_per_seq < kbar_cap ? pages_per_seq : kbar_cap;
+    if (chunk_begin < 0 || chunk_begin > chunk_end || chunk_end > lim)
+        return fail(DASH_ERR_SHAPE, "chunk range [%d, %d) outside [0, %d]", chunk_begin, chunk_end, lim);
+    dash::SummaryArgs a{Kp, k_dtype == DASH_BF16, qbar, kbar, b, h_kv, pages_per_seq * B, kbar_cap, d, B,
+                        chunk_begin, chunk_end, pages, pages_per_seq, num_pages};
+    return from_hip(dash::launch_summary(a, (hipStream_t)stream), "chunk_summary_kernel");
+}
+
 dash_status dash_route_topk(const void* Q, int q_dtype, const float* kbar,
                             int b, int h_q, int h_kv, int n, int kbar_cap, int d, int B,
                             float alpha, float gamma, float sigma, int causal,
@@ -207,14 +225,15 @@ size_t dash_workspace_bytes(int op, int b, int h_q, int h_kv, int n_or_Lcap, int
     }
 }
 
-dash_status dash_attend_decode(const void* Q, const void* Kc, const void* Vc, int in_dtype,
-                               const float* kbar, const int32_t* seq_len,
-                               int b, int h_q, int h_kv, int L_cap, int kbar_cap, int d, int B,
-                               float alpha, float gamma, float sigma,
-                               void* O, int out_dtype,
-                               int32_t* idx_out, float* bias_out, int32_t* cnt_out,
-                               float* w_out, int list_cap,
-                               void* ws, size_t ws_bytes, void* stream) {
+static dash_status attend_decode(const void* Q, const void* Kc, const void* Vc, int in_dtype,
+                                 const float* kbar, const int32_t* seq_len,
+                                 int b, int h_q, int h_kv, int L_cap, int kbar_cap, int d, int B,
+                                 float alpha, float gamma, float sigma,
+                                 void* O, int out_dtype,
+                                 int32_t* idx_out, float* bias_out, int32_t* cnt_out,
+                                 float* w_out, int list_cap,
+                                 void* ws, size_t ws_bytes, void* stream,
+                                 const int32_t* pages, int pages_per_seq, int num_pages) {
     if (!Q || !Kc || !Vc || !kbar || !seq_len || !O) return fail(DASH_ERR_NULL, "Q, Kc, Vc, kbar, seq_len and O must be non-null");
     const int given = (idx_out != nullptr) + (bias_out != nullptr) + (cnt_out != nullptr);
     if (given != 0 && given != 3) return fail(DASH_ERR_NULL, "idx_out, bias_out and cnt_out must be all NULL or all non-null");
@@ -247,7 +266,37 @@ dash_status dash_attend_decode(const void* Q, const void* Kc, const void* Vc, in
     a.T_route = Lo.T_route;
     a.max_slices = Lo.max_slices;
     a.slice_tokens = Lo.slice_tokens;
+    a.pages = pages; a.pages_per_seq = pages_per_seq; a.num_pages = num_pages;
     return from_hip(dash::launch_decode(a, (hipStream_t)stream), "decode kernels");
+}
+
+dash_status dash_attend_decode(const void* Q, const void* Kc, const void* Vc, int in_dtype,
+                               const float* kbar, const int32_t* seq_len,
+                               int b, int h_q, int h_kv, int L_cap, int kbar_cap, int d, int B,
+                               float alpha, float gamma, float sigma,
+                               void* O, int out_dtype,
+                               int32_t* idx_out, float* bias_out, int32_t* cnt_out,
+                               float* w_out, int list_cap,
+                               void* ws, size_t ws_bytes, void* stream) {
+    return attend_decode(Q, Kc, Vc, in_dtype, kbar, seq_len, b, h_q, h_kv, L_cap, kbar_cap, d, B, alpha, gamma,
+                         sigma, O, out_dtype, idx_out, bias_out, cnt_out, w_out, list_cap, ws, ws_bytes, stream,
+                         nullptr, 0, 0);
+}
+
+dash_status dash_attend_decode_paged(const void* Q, const void* Kp, const void* Vp, int in_dtype,
+                                     const float* kbar, const int32_t* seq_len,
+                                     const int32_t* pages, int pages_per_seq, int num_pages,
+                                     int b, int h_q, int h_kv, int kbar_cap, int d, int B,
+                                     float alpha, float gamma, float sigma,
+                                     void* O, int out_dtype,
+                                     int32_t* idx_out, float* bias_out, int32_t* cnt_out,
+                                     float* w_out, int list_cap,
+                                     void* ws, size_t ws_bytes, void* stream) {
+    if (!pages) return fail(DASH_ERR_NULL, "pages must be non-null");
+    if (pages_per_seq < 1 || num_pages < 1) return fail(DASH_ERR_SHAPE, "pages_per_seq and num_pages must be >= 1");
+    return attend_decode(Q, Kp, Vp, in_dtype, kbar, seq_len, b, h_q, h_kv, pages_per_seq * B, kbar_cap, d, B, alpha,
+                         gamma, sigma, O, out_dtype, idx_out, bias_out, cnt_out, w_out, list_cap, ws, ws_bytes,
+                         stream, pages, pages_per_seq, num_pages);
 }
 
 }  // extern "C"

@@ -42,6 +42,7 @@ struct DecodeParams {
     void* O;
     int32_t* idx; float* bias; int32_t* cnt; float* w_out;
     float* scores; float* partials;
+    const int32_t* pages; int pages_per_seq, num_pages;    // paged cache (nullable)
 };
 
 __device__ __forceinline__ int seq_len_of(const DecodeParams& p, int bi) {
@@ -247,6 +248,7 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(2, 
     constexpr int MAXE = 64;                       // entry cache per slice
     int* s_chunk = reinterpret_cast<int*>(smem + G::BYTES);
     float* s_bias = reinterpret_cast<float*>(s_chunk + MAXE);
+    int* s_row0 = reinterpret_cast<int*>(s_bias + MAXE);   // first cache row of each chunk
 
     const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
     const int l32 = lane & 31, hl = lane >> 5;
@@ -264,10 +266,20 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(2, 
     if (t_begin >= t_end) return;
     const int e_first = t_begin / B;
     const int e_last = (t_end - 1) / B;
+    // contiguous cache: row of token t of chunk c = c*B + t in the (b, r) slab; paged
+    // cache: ((page * h_kv + r) * B + t) in the page array (page ids clamped)
+    const bool paged = p.pages != nullptr;
     for (int e = e_first + tid; e <= e_last; e += kDecThreads) {
         const bool routed = e < cnt;
-        s_chunk[e - e_first] = routed ? p.idx[grp * p.list_cap + e] : cq;
+        const int c = routed ? p.idx[grp * p.list_cap + e] : cq;
+        s_chunk[e - e_first] = c;
         s_bias[e - e_first] = routed ? p.bias[grp * p.list_cap + e] * kLog2e : 0.f;
+        if (paged) {
+            const int pg = min(max(p.pages[(size_t)bi * p.pages_per_seq + c], 0), p.num_pages - 1);
+            s_row0[e - e_first] = (pg * p.h_kv + r) * B;
+        } else {
+            s_row0[e - e_first] = c * B;
+        }
     }
     __syncthreads();
 
@@ -279,8 +291,8 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(2, 
 #pragma unroll
         for (int s = 0; s < D / 16; ++s) qf[s] = pair_ok ? MM::load(qrow + 16 * s) : MM::zero();
     }
-    const T* Kg = static_cast<const T*>(p.Kc) + grp * (size_t)p.L_cap * D;
-    const T* Vg = static_cast<const T*>(p.Vc) + grp * (size_t)p.L_cap * D;
+    const T* Kg = static_cast<const T*>(p.Kc) + (paged ? (size_t)0 : grp * (size_t)p.L_cap * D);
+    const T* Vg = static_cast<const T*>(p.Vc) + (paged ? (size_t)0 : grp * (size_t)p.L_cap * D);
 
     float m_run = -INFINITY, l_run = 0.f;
     f32x16 o_acc[D / 32];
@@ -290,20 +302,26 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(2, 
         for (int i = 0; i < 16; ++i) o_acc[db][i] = 0.f;
 
     const int ntiles = (t_end - t_begin + kDecTT - 1) / kDecTT;
-    // KV row of the first token of each 32-token group of a tile (a group never
-    // straddles two chunks because B % 32 == 0); -1 past the slice end
+    // cache row of the first token of each 32-token group of a tile (a group never
+    // straddles two chunks because B % 32 == 0); -1 past the slice end. Rows of the
+    // diagonal chunk are clamped to the query's own row (later tokens are masked).
     auto group_base = [&](int tau) -> int {
         if (tau >= t_end) return -1;
-        return s_chunk[tau / B - e_first] * B + tau % B;
+        return s_row0[tau / B - e_first] + tau % B;
     };
-    int rb[kDecWaves];
+    int rb[kDecWaves], rl[kDecWaves];
     auto set_bases = [&](int tt0) {
 #pragma unroll
-        for (int q = 0; q < kDecWaves; ++q) rb[q] = group_base(tt0 + 32 * q);
+        for (int q = 0; q < kDecWaves; ++q) {
+            const int tau = tt0 + 32 * q;
+            rb[q] = group_base(tau);
+            // the diagonal entry (the last one, index cnt) may hold rows past pos
+            rl[q] = (tau < t_end && tau / B >= cnt) ? s_row0[tau / B - e_first] + pos % B : 0x7fffffff;
+        }
     };
     auto row_of = [&](int t) -> int {
         const int base = rb[t >> 5];
-        return base < 0 ? 0 : min(base + (t & 31), pos);
+        return base < 0 ? 0 : min(base + (t & 31), rl[t >> 5]);
     };
     TileRegs<T, D, kDecTT, kDecThreads> regs;
     set_bases(t_begin);
@@ -487,7 +505,7 @@ static hipError_t launch_dec_route(const DecodeParams& p, int b, hipStream_t s) 
 
 template <typename T, int D>
 static hipError_t launch_decode_t(const DecodeParams& p, const DecodeArgs& a, hipStream_t s) {
-    constexpr size_t lds = TileGeom<T, D, kDecTT>::BYTES + 64 * 8;
+    constexpr size_t lds = TileGeom<T, D, kDecTT>::BYTES + 64 * 12;   // + chunk, bias, first row
     static_assert(TileGeom<T, D, kDecTT>::BYTES >= kDecWaves * (32 * D + 64) * 4, "LDS merge space");
     static hipError_t configured = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_attn_kernel<T, D>),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
@@ -523,6 +541,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
     p.out_bf16 = a.out_bf16;
     p.O = a.O; p.idx = a.idx; p.bias = a.bias; p.cnt = a.cnt; p.w_out = a.w_out;
     p.scores = a.scores; p.partials = a.partials;
+    p.pages = a.pages; p.pages_per_seq = a.pages_per_seq; p.num_pages = a.num_pages;
     if (a.in_bf16) return a.d == 64 ? launch_decode_t<uint16_t, 64>(p, a, s) : launch_decode_t<uint16_t, 128>(p, a, s);
     return a.d == 64 ? launch_decode_t<float, 64>(p, a, s) : launch_decode_t<float, 128>(p, a, s);
 }

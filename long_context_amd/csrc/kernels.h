@@ -11,6 +11,10 @@ namespace dash {
 struct SummaryArgs {
     const void* K; bool k_bf16; const float* qbar; float* kbar;
     int b, h_kv, n_kv, kbar_cap, d, B, chunk_begin, chunk_end;
+    // paged cache (pages != nullptr): K is [num_pages, h_kv, B, d] and chunk c of
+    // sequence b lives in page pages[b * pages_per_seq + c]
+    const int32_t* pages = nullptr;
+    int pages_per_seq = 0, num_pages = 0;
 };
 hipError_t launch_summary(const SummaryArgs& a, hipStream_t s);
 
@@ -67,6 +71,10 @@ struct DecodeArgs {
     int T_route;         // routable chunk capacity: min(floor((L_cap-1)/B), kbar_cap)
     int max_slices;
     int slice_tokens;
+    // paged cache (pages != nullptr): Kc/Vc are [num_pages, h_kv, B, d], chunk c of
+    // sequence b lives in page pages[b * pages_per_seq + c], L_cap = pages_per_seq * B
+    const int32_t* pages = nullptr;
+    int pages_per_seq = 0, num_pages = 0;
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 // Split-KV geometry of the decode kernels for a given cache capacity.

@@ -39,7 +39,7 @@ template <typename T, int D>
 __global__ __launch_bounds__(256) void chunk_summary_kernel(
     const T* __restrict__ K, const float* __restrict__ qbar, float* __restrict__ kbar,
     int h_kv, int n_kv, int kbar_cap, int B, int chunk_begin, int nsel, int total,
-    float scale) {
+    float scale, const int32_t* __restrict__ pages, int pages_per_seq, int num_pages) {
     constexpr int VEC = Vec16<T>::N;
     constexpr int LPR = D / VEC;        // lanes sharing one key row
     constexpr int RPI = 64 / LPR;       // key rows per wave iteration
@@ -55,7 +55,15 @@ __global__ __launch_bounds__(256) void chunk_summary_kernel(
     float q[VEC];
 #pragma unroll
     for (int v = 0; v < VEC; ++v) q[v] = qbar[r * D + col + v];
-    const T* Kc = K + ((size_t)br * n_kv + (size_t)c * B) * D + col;
+    // contiguous: rows of (b, r) from c*B; paged: the chunk's page (out-of-range page
+    // ids are clamped, so a bad table gives wrong summaries, never a stray read)
+    const T* Kc;
+    if (pages) {
+        const int pg = min(max(pages[(size_t)(br / h_kv) * pages_per_seq + c], 0), num_pages - 1);
+        Kc = K + (((size_t)pg * h_kv + r) * B) * D + col;
+    } else {
+        Kc = K + ((size_t)br * n_kv + (size_t)c * B) * D + col;
+    }
 
     float m = -INFINITY, l = 0.f, acc[VEC];
 #pragma unroll
@@ -107,7 +115,7 @@ static hipError_t launch_summary_t(const SummaryArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((chunk_summary_kernel<T, D>), grid, block, 0, s,
                        static_cast<const T*>(a.K), a.qbar, a.kbar, a.h_kv, a.n_kv, a.kbar_cap,
                        a.B, a.chunk_begin, nsel, total,
-                       (float)(1.4426950408889634 / sqrt((double)D)));
+                       (float)(1.4426950408889634 / sqrt((double)D)), a.pages, a.pages_per_seq, a.num_pages);
     return hipGetLastError();
 }
 

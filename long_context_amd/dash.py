@@ -45,6 +45,11 @@ def _load():
     lib.dash_attend_decode.argtypes = [vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                        f32, f32, f32, vp, i32, vp, vp, vp, vp, i32, vp, sz, vp]
     lib.dash_attend_decode.restype = i32
+    lib.dash_summarize_paged.argtypes = [vp, i32, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, i32, vp]
+    lib.dash_summarize_paged.restype = i32
+    lib.dash_attend_decode_paged.argtypes = [vp, vp, vp, i32, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                             i32, f32, f32, f32, vp, i32, vp, vp, vp, vp, i32, vp, sz, vp]
+    lib.dash_attend_decode_paged.restype = i32
     lib.dash_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
     lib.dash_workspace_bytes.restype = sz
     lib.dash_status_string.argtypes = [i32]
@@ -56,8 +61,8 @@ def _load():
 
 lib = _load()
 
-SYMBOLS = ("dash_summarize", "dash_route", "dash_route_topk", "dash_route_mask", "dash_attend_prefill",
-           "dash_attend_decode",
+SYMBOLS = ("dash_summarize", "dash_summarize_paged", "dash_route", "dash_route_topk", "dash_route_mask",
+           "dash_attend_prefill", "dash_attend_decode", "dash_attend_decode_paged",
            "dash_workspace_bytes", "dash_status_string", "dash_last_error")
 
 
@@ -165,6 +170,29 @@ def dash_attend_decode(Q, Kc, Vc, kbar, seq_len, B, alpha, gamma, sigma, O, ws,
                                   _ptr(idx_out), _ptr(bias_out), _ptr(cnt_out), _ptr(w_out),
                                   list_cap, _ptr(ws), ws.numel() * ws.element_size(),
                                   _stream(stream)))
+
+
+def dash_summarize_paged(Kp, qbar, kbar, pages, B, chunk_begin, chunk_end, stream=None):
+    """Stage 0 of chunks [chunk_begin, chunk_end) from a paged cache Kp [P,h_kv,B,d]."""
+    P, h_kv, _, d = Kp.shape
+    b, pps = pages.shape
+    _check(lib.dash_summarize_paged(_ptr(Kp), _dtype(Kp), _ptr(qbar), _ptr(kbar), _ptr(pages), pps, P,
+                                    b, h_kv, kbar.shape[2], d, B, chunk_begin, chunk_end, _stream(stream)))
+
+
+def dash_attend_decode_paged(Q, Kp, Vp, kbar, seq_len, pages, B, alpha, gamma, sigma, O, ws,
+                             idx_out=None, bias_out=None, cnt_out=None, w_out=None, stream=None):
+    """One decode step against a paged cache Kp/Vp [P,h_kv,B,d] with page table [b, pages_per_seq]."""
+    b, h_q, _, d = Q.shape
+    P, h_kv, _, _ = Kp.shape
+    pps = pages.shape[1]
+    list_cap = idx_out.shape[-1] if idx_out is not None else 0
+    _check(lib.dash_attend_decode_paged(_ptr(Q), _ptr(Kp), _ptr(Vp), _dtype(Q), _ptr(kbar), _ptr(seq_len),
+                                        _ptr(pages), pps, P, b, h_q, h_kv, kbar.shape[2], d, B,
+                                        float(alpha), float(gamma), float(sigma), _ptr(O), _dtype(O),
+                                        _ptr(idx_out), _ptr(bias_out), _ptr(cnt_out), _ptr(w_out),
+                                        list_cap, _ptr(ws), ws.numel() * ws.element_size(),
+                                        _stream(stream)))
 
 
 # ----------------------------------------------------------------------------------

@@ -99,6 +99,23 @@ def test_route_mask_validation(dash):
     assert m(P, P, 1, 2, 64, 0, 0, P, 0, NUL) == dash.DASH_OK                # nothing to write
 
 
+def test_paged_entry_points_validation(dash):
+    sp = dash.lib.dash_summarize_paged
+    assert sp(P, 1, P, P, NUL, 4, 8, 1, 2, 4, 128, 64, 0, 1, NUL) == dash.DASH_ERR_NULL
+    assert sp(P, 1, P, P, P, 0, 8, 1, 2, 4, 128, 64, 0, 1, NUL) == dash.DASH_ERR_SHAPE
+    assert sp(P, 1, P, P, P, 4, 8, 1, 2, 4, 128, 64, 0, 5, NUL) == dash.DASH_ERR_SHAPE   # chunk_end > pages
+    assert sp(P, 1, P, P, P, 4, 8, 1, 2, 4, 96, 64, 0, 1, NUL) == dash.DASH_ERR_UNSUPPORTED
+    dp = dash.lib.dash_attend_decode_paged
+    args = [P, P, P, 1, P, P, P, 4, 8, 1, 4, 2, 4, 128, 64, 1.5, 1.0, 1.0, P, 0, NUL, NUL, NUL, NUL, 0]
+    assert dp(*args, NUL, 0, NUL) == dash.DASH_ERR_WORKSPACE
+    bad = list(args)
+    bad[6] = NUL
+    assert dp(*bad, NUL, 0, NUL) == dash.DASH_ERR_NULL
+    bad = list(args)
+    bad[8] = 0
+    assert dp(*bad, NUL, 0, NUL) == dash.DASH_ERR_SHAPE
+
+
 def test_route_accepts_alpha_one(dash):
     # α = 1 (softmax routing) passes parameter validation; the missing workspace of
     # this bf16 call is what fails next
