@@ -361,6 +361,71 @@ def attend(Qr, pos, K, V, rt, B, causal, n_kv, row_block=64):
     return O
 
 
+def attend_backward(Qr, pos, K, V, rt, B, causal, n_kv, dO, row_block=64):
+    """Gradients of Stage 2 (Prop. 4.1 form, the support and the bias held fixed) for
+    an upstream gradient dO [b, h_q, R, d] of o_i (paper review section 三: Stage 2 is
+    an ordinary softmax attention with an additive per-chunk bias, so its backward is
+    the softmax-attention backward with that bias):
+      P = softmax(Z), Z = QK^T/sqrt(d) + L;  dV = P^T dO;  dP = dO V^T;
+      dZ = P ∘ (dP - rowsum(dP ∘ P));  dQ = dZ K/sqrt(d);  dK = dZ^T Q/sqrt(d);
+      d(bias)_{i,c} = sum over the group's heads and the tokens j of chunk c of dZ_ij.
+    Returns dQ [b,h_q,R,d], dK, dV [b,h_kv,n_kv,d], dbias [b,h_kv,R,T] (0 off the
+    support) and lse [b,h_q,R] = log sum_j exp(Z_ij), all float64.
+    """
+    Qr = _f64(Qr)
+    K = _f64(K)
+    V = _f64(V)
+    dO = _f64(dO)
+    b, hq, R, d = Qr.shape
+    hkv = K.shape[1]
+    g = hq // hkv
+    T = n_kv // B
+    pos = np.broadcast_to(np.asarray(pos), (b, R))
+    dQ = np.zeros((b, hq, R, d))
+    dK = np.zeros((b, hkv, n_kv, d))
+    dV = np.zeros((b, hkv, n_kv, d))
+    dbias = np.zeros((b, hkv, R, T))
+    lse = np.zeros((b, hq, R))
+    sc = 1.0 / np.sqrt(d)
+    for bi in range(b):
+        for r0 in range(0, R, row_block):
+            r1 = min(R, r0 + row_block)
+            p = pos[bi, r0:r1]
+            jmax = n_kv if not causal else int(p.max()) + 1
+            tok = np.arange(jmax)
+            chunk_of = tok // B
+            for r in range(hkv):
+                L = np.full((r1 - r0, jmax), -np.inf)
+                full = chunk_of < T
+                sup = rt["support"][bi, r, r0:r1][:, chunk_of[full]]
+                bia = rt["bias"][bi, r, r0:r1][:, chunk_of[full]]
+                L[:, full] = np.where(sup, bia, -np.inf)
+                routed = np.zeros((r1 - r0, jmax), bool)
+                routed[:, full] = sup
+                for k, pk in enumerate(p):
+                    lo, hi = diagonal_range(int(pk), B, T, n_kv, causal)
+                    L[k, lo:min(hi, jmax)] = 0.0
+                    routed[k, lo:min(hi, jmax)] = False
+                for h in range(r * g, (r + 1) * g):
+                    Z = (Qr[bi, h, r0:r1] @ K[bi, r, :jmax].T) * sc + L
+                    m = Z.max(-1, keepdims=True)
+                    E = np.exp(Z - m)
+                    ssum = E.sum(-1, keepdims=True)
+                    P = E / ssum
+                    lse[bi, h, r0:r1] = (m + np.log(ssum))[:, 0]
+                    g_o = dO[bi, h, r0:r1]
+                    dV[bi, r, :jmax] += P.T @ g_o
+                    dP = g_o @ V[bi, r, :jmax].T
+                    dZ = P * (dP - (dP * P).sum(-1, keepdims=True))
+                    dQ[bi, h, r0:r1] = (dZ @ K[bi, r, :jmax]) * sc
+                    dK[bi, r, :jmax] += (dZ.T @ Qr[bi, h, r0:r1]) * sc
+                    dzr = np.where(routed, dZ, 0.0)
+                    for c in range(T):
+                        dbias[bi, r, r0:r1, c] += dzr[:, c * B:(c + 1) * B].sum(-1) if c * B < jmax else 0.0
+    dbias = np.where(rt["support"], dbias, 0.0)
+    return dict(dQ=dQ, dK=dK, dV=dV, dbias=dbias, lse=lse)
+
+
 def attend_eq9(Qr, pos, K, V, rt, B, sigma, causal, n_kv):
     """Stage 2 through the prior of Eq. 9 with Eq. 11 and Eq. 12, row by row.
 

@@ -455,3 +455,71 @@ def test_route_mask_matches_little_endian_bit_packing():
     assert np.array_equal(m, ref)
     back = np.unpackbits(m.view(np.uint8), axis=-1, bitorder="little")[..., :70].astype(bool)
     assert np.array_equal(back, sup)
+
+
+def _stage2_setup(n=160, B=16, seed=5, sigma=1.0):
+    w = _small(n=n)
+    kb = O.stage0_summaries(w.K, w.qbar, B)
+    rows = np.arange(n)
+    rt = O.route(w.Q, rows[None], kb, B, 1.5, 3.0, sigma, True, n)
+    rng = np.random.default_rng(seed)
+    dO = rng.standard_normal(w.Q.shape)
+    return w, rows, rt, dO
+
+
+def test_stage2_backward_matches_finite_differences():
+    """Stage-2 gradients of <dO, O> against central differences of the forward
+    oracle in random directions, for Q, K, V and the per-chunk bias."""
+    w, rows, rt, dO = _stage2_setup()
+    n, B = w.n, 16
+    Q, K, V = (np.asarray(x, np.float64) for x in (w.Q, w.K, w.V))
+    gr = O.attend_backward(Q, rows[None], K, V, rt, B, True, n, dO)
+    rng = np.random.default_rng(8)
+    eps = 1e-6
+
+    def loss(Qx, Kx, Vx, rtx):
+        return float((dO * O.attend(Qx, rows[None], Kx, Vx, rtx, B, True, n)).sum())
+
+    for name, x in (("Q", Q), ("K", K), ("V", V)):
+        u = rng.standard_normal(x.shape)
+        args = dict(Q=Q, K=K, V=V)
+        plus = dict(args); plus[name] = x + eps * u
+        minus = dict(args); minus[name] = x - eps * u
+        fd = (loss(plus["Q"], plus["K"], plus["V"], rt) - loss(minus["Q"], minus["K"], minus["V"], rt)) / (2 * eps)
+        an = float((gr["d" + name] * u).sum())
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (name, fd, an)
+    u = np.where(rt["support"], rng.standard_normal(rt["bias"].shape), 0.0)
+    rp = dict(rt); rp["bias"] = rt["bias"] + eps * u
+    rm = dict(rt); rm["bias"] = rt["bias"] - eps * u
+    fd = (loss(Q, K, V, rp) - loss(Q, K, V, rm)) / (2 * eps)
+    an = float((gr["dbias"] * u).sum())
+    assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), ("bias", fd, an)
+
+
+def test_stage2_backward_sigma_inf_is_masked_sdpa_autograd():
+    """σ = inf (bias 0): the Stage-2 gradients are those of masked softmax attention,
+    here from torch autograd of scaled_dot_product_attention with the same mask; and
+    the log-sum-exp equals scipy's."""
+    w, rows, rt, dO = _stage2_setup(sigma=np.inf)
+    n, B, g = w.n, 16, 2
+    Q, K, V = (np.asarray(x, np.float64) for x in (w.Q, w.K, w.V))
+    gr = O.attend_backward(Q, rows[None], K, V, rt, B, True, n, dO)
+    nb = Q.shape[0]
+    mask = np.zeros((nb, 2, n, n), bool)
+    for bi in range(nb):
+        for r in range(2):
+            for i in range(n):
+                for c in np.nonzero(rt["support"][bi, r, i])[0]:
+                    mask[bi, r, i, c * B:(c + 1) * B] = True
+                mask[bi, r, i, (i // B) * B:i + 1] = True
+    mask = np.repeat(mask, g, axis=1)
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (Q, np.repeat(K, g, 1), np.repeat(V, g, 1)))
+    out = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=torch.from_numpy(mask))
+    (out * torch.from_numpy(dO)).sum().backward()
+    np.testing.assert_allclose(gr["dQ"], tq.grad.numpy(), atol=1e-10)
+    np.testing.assert_allclose(gr["dK"], tk.grad.numpy().reshape(nb, 2, g, n, -1).sum(2), atol=1e-10)
+    np.testing.assert_allclose(gr["dV"], tv.grad.numpy().reshape(nb, 2, g, n, -1).sum(2), atol=1e-10)
+    d = Q.shape[-1]
+    Z = np.einsum("bhid,bhjd->bhij", Q, np.repeat(K, g, 1)) / np.sqrt(d)
+    Z = np.where(mask, Z, -np.inf)
+    np.testing.assert_allclose(gr["lse"], scipy.special.logsumexp(Z, axis=-1), atol=1e-12)
