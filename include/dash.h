@@ -65,7 +65,7 @@ typedef enum {
 
 typedef enum { DASH_F32 = 0, DASH_BF16 = 1 } dash_dtype;
 
-typedef enum { DASH_OP_ROUTE = 0, DASH_OP_PREFILL = 1, DASH_OP_DECODE = 2 } dash_op;
+typedef enum { DASH_OP_ROUTE = 0, DASH_OP_PREFILL = 1, DASH_OP_DECODE = 2, DASH_OP_PREFILL_BWD = 3 } dash_op;
 
 /*
  * Stage 0 (Eq. 4): for every (b, r) and every chunk c in [chunk_begin, chunk_end):
@@ -150,6 +150,43 @@ dash_status dash_attend_prefill(const void* Q, const void* K, const void* V, int
                                 void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * dash_attend_prefill that also writes lse [b, h_q, n] (device fp32): the natural
+ * log of the softmax denominator of each (head, row), i.e. log sum_j exp(z_ij + d_ij)
+ * over the row's routed and diagonal tokens; -inf for a row that sees no token.
+ * lse == NULL behaves as dash_attend_prefill. This is the statistic the backward
+ * (dash_attend_prefill_backward) reuses instead of a second softmax pass.
+ */
+dash_status dash_attend_prefill_lse(const void* Q, const void* K, const void* V, int in_dtype,
+                                    const int32_t* idx, const float* bias, const int32_t* cnt,
+                                    int list_cap, void* O, int out_dtype, float* lse,
+                                    int b, int h_q, int h_kv, int n, int d, int B, int causal,
+                                    void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Stage-2 backward (the support and the per-chunk bias of Prop. 4.1 held fixed: the
+ * gradient of a softmax attention with an additive bias). Inputs: the forward's
+ * Q, K, V (in_dtype, bf16 only), idx/bias/cnt (same list_cap), its output O and the
+ * upstream gradient dO [b, h_q, n, d] (both o_dtype) and lse from
+ * dash_attend_prefill_lse. Outputs, all device fp32:
+ *   dQ [b, h_q, n, d], dK and dV [b, h_kv, n, d];
+ *   dbias [b, h_kv, n, list_cap]: entry e of a row is the gradient of bias entry e,
+ *   the sum of dZ over the tokens of chunk idx[e] and the group's g query heads;
+ *   entries at or past cnt, or naming a chunk the row cannot see, are zero.
+ * Requires B % 64 == 0, g = h_q/h_kv in {8, 16}, d in {64, 128}, n*floor(n/B) < 2^31
+ * and a device workspace of dash_workspace_bytes(DASH_OP_PREFILL_BWD, ...) bytes
+ * (grows with n^2/B: the routed lists inverted per chunk are sized for dense
+ * routing). dK and dV sum several partials with atomic adds, so their last bits
+ * may differ between runs; dQ and dbias are reproducible. Calls that share a
+ * workspace must not overlap.
+ */
+dash_status dash_attend_prefill_backward(const void* Q, const void* K, const void* V, int in_dtype,
+                                         const int32_t* idx, const float* bias, const int32_t* cnt, int list_cap,
+                                         const void* O, const void* dO, int o_dtype, const float* lse,
+                                         float* dQ, float* dK, float* dV, float* dbias,
+                                         int b, int h_q, int h_kv, int n, int d, int B, int causal,
+                                         void* ws, size_t ws_bytes, void* stream);
+
+/*
  * One decode step (Stages 1-2 for one new query per sequence, split-KV Stage 2):
  *   Q [b, h_q, 1, d]; Kc, Vc [b, h_kv, L_cap, d] hold the KV cache including the
  *   new token; seq_len [b] (device int32) = KV length L incl. the new token, so
@@ -197,7 +234,7 @@ dash_status dash_attend_decode_paged(const void* Q, const void* Kp, const void* 
 
 /* Workspace bytes an operation needs (n_or_Lcap: n for prefill ops, L_cap for
  * decode; DASH_OP_ROUTE and DASH_OP_PREFILL give the size for bf16 inputs, which
- * fp32 inputs do not need). Returns 0 when no
+ * fp32 inputs do not need; DASH_OP_PREFILL_BWD is the Stage-2 backward's). Returns 0 when no
  * workspace is needed, (size_t)-1 on invalid sizes. */
 size_t dash_workspace_bytes(int op, int b, int h_q, int h_kv, int n_or_Lcap, int d, int B);
 

@@ -1,0 +1,878 @@
+// Stage 2 backward for bf16 inputs.
+//
+// Stage 2 is a softmax attention whose logits carry a fixed additive bias per routed
+// chunk (paper review section 三, the Proposition 4.1 form). With the support and
+// the bias held fixed its gradients are those of softmax attention:
+//   P = exp(Z - lse),  dV = P^T dO,  dP = dO V^T,  dZ = P ∘ (dP - Δ),  Δ_i = <o_i, do_i>,
+//   dQ = dZ K / sqrt(d),  dK = dZ^T Q / sqrt(d),
+// and the gradient of a routed chunk's bias in row i is the sum of dZ over the
+// chunk's tokens and the query heads of the row's KV group (they share one list).
+//
+// Kernels, in launch order:
+//   bwd_prep_kernel        Δ per (row, head); Q and dO transposed per KV group to
+//                          [d][row][head], the operands of dK and dV whose
+//                          contraction runs over (row, head) pairs; dO as bf16.
+//   inv_*_kernel           the routed lists inverted into per-chunk row lists, rows
+//                          ascending (a stable counting sort over 64-row blocks).
+//   prior_attn_dq_kernel   query-major like the forward: a query tile walks the
+//                          union of its rows' routed chunks and then the diagonal,
+//                          recomputes P from the forward's lse, keeps dQ in
+//                          registers and writes each routed chunk's bias gradient.
+//   prior_attn_dkv_kernel  key-major: a workgroup holds K and V of 64 tokens of one
+//                          chunk in registers, streams the (row, head) pairs that
+//                          see them (a segment of the chunk's row list, then its
+//                          diagonal rows) and keeps dK and dV in registers.
+// dQ and the bias gradients have one writer each. dK and dV add the partials of
+// the segments of a chunk and of the two pair halves of a workgroup onto zeros
+// with atomic adds.
+#include "kernels.h"
+#include "prefill_common.h"
+
+#include <math.h>
+
+#include <algorithm>
+
+namespace dash {
+
+// ---------------------------------------------------------------------------------
+// Preparation: Δ, transposed Q and dO, bf16 dO
+// ---------------------------------------------------------------------------------
+
+struct BwdPrepParams {
+    const uint16_t* Q; const void* O; const void* dO;
+    uint16_t* Qt; uint16_t* dOt;     // [b*h_kv][D][n*g], pair index row*g + head
+    uint16_t* dOb;                   // nullable: bf16 copy of an fp32 dO
+    float* delta;                    // [b, h_q, n]
+    int h_q, h_kv, n, g, log2g;
+};
+
+// One workgroup per 64 consecutive (row, head) pairs of a KV group (g >= 8, so a
+// 16-byte piece of 8 pairs never spans two rows).
+template <int D, typename OT>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdPrepParams p) {
+    constexpr int PR = D / 8;                    // 16-byte pieces per row
+    __shared__ __attribute__((aligned(16))) uint16_t qs[64][D + 8];
+    __shared__ __attribute__((aligned(16))) uint16_t ds[64][D + 8];
+    const int tid = threadIdx.x;
+    const int hk = blockIdx.y, bi = blockIdx.z;
+    const size_t P0 = (size_t)blockIdx.x * 64;
+    const size_t npairs = (size_t)p.n * p.g;
+    for (int q = tid; q < 64 * PR; q += 256) {
+        const int t = q / PR, c = q % PR;
+        const size_t pair = P0 + t;
+        const int row = (int)(pair >> p.log2g), head = (int)(pair & (p.g - 1));
+        const bool ok = pair < npairs;
+        const size_t off = (((size_t)bi * p.h_q + (size_t)hk * p.g + head) * p.n + (ok ? row : 0)) * D + 8 * c;
+        u32x4 qv = {0u, 0u, 0u, 0u}, dv = {0u, 0u, 0u, 0u};
+        float part = 0.f;
+        if (ok) {
+            qv = *reinterpret_cast<const u32x4*>(p.Q + off);
+            float o[8], d[8];
+            Elem<OT>::load8(static_cast<const OT*>(p.O) + off, o);
+            Elem<OT>::load8(static_cast<const OT*>(p.dO) + off, d);
+            // Δ takes dO as the MFMAs of dP see it (rounded to bf16), so that Δ and
+            // the rows of dP stay consistent and dZ cancels where it should
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t lo = f32_to_bf16_bits(d[2 * e]), hi = f32_to_bf16_bits(d[2 * e + 1]);
+                dv[e] = lo | (hi << 16);
+                part = fmaf(o[2 * e], bf16_bits_to_f32(lo), part);
+                part = fmaf(o[2 * e + 1], bf16_bits_to_f32(hi), part);
+            }
+            if (p.dOb) *reinterpret_cast<u32x4*>(p.dOb + off) = dv;
+        }
+        *reinterpret_cast<u32x4*>(&qs[t][8 * c]) = qv;
+        *reinterpret_cast<u32x4*>(&ds[t][8 * c]) = dv;
+        // the PR pieces of one pair sit in PR consecutive lanes
+#pragma unroll
+        for (int m = 1; m < PR; m <<= 1) part += shfl_xor(part, m);
+        if (ok && c == 0) p.delta[(((size_t)bi * p.h_q + (size_t)hk * p.g + head) * p.n + row)] = part;
+    }
+    __syncthreads();
+    const size_t bhk = (size_t)bi * p.h_kv + hk;
+    for (int q = tid; q < D * 8; q += 256) {
+        const int d = q / 8, cp = q % 8;
+        if (P0 + 8 * cp >= npairs) continue;
+        u32x4 a, b;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            a[e] = (uint32_t)qs[8 * cp + 2 * e][d] | ((uint32_t)qs[8 * cp + 2 * e + 1][d] << 16);
+            b[e] = (uint32_t)ds[8 * cp + 2 * e][d] | ((uint32_t)ds[8 * cp + 2 * e + 1][d] << 16);
+        }
+        const size_t o = (bhk * D + d) * npairs + P0 + 8 * cp;
+        *reinterpret_cast<u32x4*>(p.Qt + o) = a;
+        *reinterpret_cast<u32x4*>(p.dOt + o) = b;
+    }
+}
+
+__global__ __launch_bounds__(256) void fill_zero_kernel(float* x, size_t n) {
+    const size_t stride = (size_t)gridDim.x * 256;
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) x[i] = 0.f;
+}
+
+// ---------------------------------------------------------------------------------
+// Inverted lists: for each (b, KV head, chunk c) the rows whose routed list holds c
+// (visible chunks only), ascending, with the bias of that entry.
+// ---------------------------------------------------------------------------------
+
+struct InvParams {
+    const int32_t* idx; const float* bias; const int32_t* cnt;
+    int32_t* hist;       // [b*h_kv][T][nblk]: rows of block k routing c, then their offsets
+    int32_t* coff;       // [b*h_kv][T+1]: start of chunk c's rows in the inverted list
+    int32_t* inv_row; float* inv_bias;   // [b*h_kv][n*T]
+    int n, B, T, nblk, list_cap, causal;
+};
+
+// Bit r of word c: row block*64 + r routes chunk c. One wavefront per 64-row block;
+// lane r walks row r's list.
+__device__ __forceinline__ void mark_block_rows(const InvParams& p, size_t bh, int blk, int lane,
+                                                unsigned long long* msk) {
+    for (int c = lane; c < p.T; c += 64) msk[c] = 0ull;
+    __syncthreads();
+    const int row = blk * 64 + lane;
+    if (row < p.n) {
+        const int nvis = p.causal ? min(row / p.B, p.T) : p.T;
+        const size_t rb = bh * p.n + row;
+        const int cn = min(p.cnt[rb], p.list_cap);
+        const int32_t* li = p.idx + rb * p.list_cap;
+        for (int e = 0; e < cn; ++e) {
+            const int c = li[e];
+            if (c >= 0 && c < nvis) atomicOr(&msk[c], 1ull << lane);
+        }
+    }
+    __syncthreads();
+}
+
+__global__ __launch_bounds__(64) void inv_hist_kernel(InvParams p) {
+    extern __shared__ unsigned long long msk[];
+    const int blk = blockIdx.x, lane = threadIdx.x;
+    const size_t bh = blockIdx.y;
+    mark_block_rows(p, bh, blk, lane, msk);
+    for (int c = lane; c < p.T; c += 64)
+        p.hist[(bh * p.T + c) * p.nblk + blk] = __builtin_popcountll(msk[c]);
+}
+
+// Exclusive prefix sum over a 256-thread workgroup (tmp: 4 ints of LDS).
+__device__ __forceinline__ int block_scan256(int v, int* tmp, int& total) {
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    int x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __builtin_amdgcn_ds_bpermute(((lane - o) & 63) << 2, x);
+        if (lane >= o) x += y;
+    }
+    if (lane == 63) tmp[wid] = x;
+    __syncthreads();
+    int off = 0;
+    for (int w = 0; w < wid; ++w) off += tmp[w];
+    total = tmp[0] + tmp[1] + tmp[2] + tmp[3];
+    __syncthreads();
+    return off + x - v;
+}
+
+// Per (chunk, b*h_kv): block counts -> exclusive offsets inside the chunk; chunk total.
+__global__ __launch_bounds__(256) void inv_scan_blocks_kernel(InvParams p) {
+    __shared__ int tmp[4];
+    const size_t bh = blockIdx.y;
+    const int c = blockIdx.x;
+    int32_t* h = p.hist + (bh * p.T + c) * p.nblk;
+    const int per = (p.nblk + 255) / 256;
+    const int k0 = min((int)threadIdx.x * per, p.nblk), k1 = min(k0 + per, p.nblk);
+    int s = 0;
+    for (int k = k0; k < k1; ++k) s += h[k];
+    int total;
+    int run = block_scan256(s, tmp, total);
+    for (int k = k0; k < k1; ++k) {
+        const int v = h[k];
+        h[k] = run;
+        run += v;
+    }
+    if (threadIdx.x == 0) p.coff[bh * (p.T + 1) + c] = total;
+}
+
+// Per b*h_kv: chunk totals -> exclusive chunk starts (entry T: the total).
+__global__ __launch_bounds__(256) void inv_scan_chunks_kernel(InvParams p) {
+    __shared__ int tmp[4];
+    const size_t bh = blockIdx.x;
+    int32_t* co = p.coff + bh * (p.T + 1);
+    const int per = (p.T + 255) / 256;
+    const int k0 = min((int)threadIdx.x * per, p.T), k1 = min(k0 + per, p.T);
+    int s = 0;
+    for (int k = k0; k < k1; ++k) s += co[k];
+    int total;
+    int run = block_scan256(s, tmp, total);
+    for (int k = k0; k < k1; ++k) {
+        const int v = co[k];
+        co[k] = run;
+        run += v;
+    }
+    if (threadIdx.x == 0) co[p.T] = total;
+}
+
+__global__ __launch_bounds__(64) void inv_scatter_kernel(InvParams p) {
+    extern __shared__ unsigned long long msk[];
+    const int blk = blockIdx.x, lane = threadIdx.x;
+    const size_t bh = blockIdx.y;
+    mark_block_rows(p, bh, blk, lane, msk);
+    const int row = blk * 64 + lane;
+    if (row >= p.n) return;
+    const int nvis = p.causal ? min(row / p.B, p.T) : p.T;
+    const size_t rb = bh * p.n + row;
+    const int cn = min(p.cnt[rb], p.list_cap);
+    const int32_t* li = p.idx + rb * p.list_cap;
+    const float* lb = p.bias + rb * p.list_cap;
+    const size_t base = bh * (size_t)p.n * p.T;
+    const unsigned long long below = (1ull << lane) - 1ull;
+    for (int e = 0; e < cn; ++e) {
+        const int c = li[e];
+        if (c < 0 || c >= nvis) continue;
+        const size_t pos = base + p.coff[bh * (p.T + 1) + c] + p.hist[(bh * p.T + c) * p.nblk + blk] +
+                           __builtin_popcountll(msk[c] & below);
+        p.inv_row[pos] = row;
+        p.inv_bias[pos] = lb[e];
+    }
+}
+
+// ---------------------------------------------------------------------------------
+// dQ and the bias gradients (query-major)
+// ---------------------------------------------------------------------------------
+
+struct DqExtra {
+    const uint16_t* Kt;              // [b*h_kv][D][n_pad]
+    const uint16_t* dO;              // bf16 [b, h_q, n, D]
+    const float* lse; const float* delta;
+    float* dQ; float* dbias;
+    float scale;                     // 1/sqrt(d)
+};
+
+// Copies of one stage: K tile [64][D], V tile [64][D] (both "K" form) and the K^T
+// tile [D][64]; wavefront w issues copy instructions w, w+NW, ...
+template <int D, int NW>
+struct DqCopier {
+    typedef BfTiles<D, 64> S;
+    static constexpr int NI = 2 * S::KINSTS + S::VINSTS;
+    static constexpr int CPW = NI / NW;
+    static_assert(CPW * NW == NI, "copies must divide evenly over the wavefronts");
+    static constexpr int STAGE = 2 * S::KBYTES + S::VBYTES;
+    int row[CPW], off[CPW], dst[CPW];
+
+    __device__ __forceinline__ void init(int wid, int lane) {
+#pragma unroll
+        for (int i = 0; i < CPW; ++i) {
+            const int j = wid + i * NW;
+            if (j < 2 * S::KINSTS) {
+                const int jj = j % S::KINSTS;
+                const int q = jj * 64 + lane, t = q / S::KPPR, cs = q % S::KPPR;
+                row[i] = t;
+                off[i] = S::kslot(t, cs) * 8;
+                dst[i] = (j < S::KINSTS ? 0 : S::KBYTES) + jj * 1024;
+            } else {
+                const int jj = j - 2 * S::KINSTS;
+                const int q = jj * 64 + lane, d = q / S::VPPR, cs = q % S::VPPR;
+                row[i] = d;
+                off[i] = S::vslot(d, cs) * 8;
+                dst[i] = 2 * S::KBYTES + jj * 1024;
+            }
+        }
+    }
+    __device__ __forceinline__ void issue(char* stage, const uint16_t* Kg, const uint16_t* Vg, const uint16_t* Ktg,
+                                          int tb, int nmax, int n_pad, int wid) const {
+        tb = min(max(tb, 0), n_pad - 64);
+#pragma unroll
+        for (int i = 0; i < CPW; ++i) {
+            const int j = wid + i * NW;               // wavefront-uniform
+            const uint16_t* src = j < S::KINSTS       ? Kg + (size_t)min(tb + row[i], nmax) * D + off[i]
+                                  : j < 2 * S::KINSTS ? Vg + (size_t)min(tb + row[i], nmax) * D + off[i]
+                                                      : Ktg + (size_t)row[i] * n_pad + tb + off[i];
+            __builtin_amdgcn_global_load_lds(src, stage + dst[i], 16, 0, 0);
+        }
+    }
+};
+
+// NW wavefronts of one 32-pair block each; the tile geometry is the forward's.
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) void prior_attn_dq_kernel(PrefillParams p, DqExtra x) {
+    typedef BfTiles<D, 64> S;
+    typedef DqCopier<D, NW> CP;
+    constexpr int TT = 64;
+    constexpr int NS = D / 16;     // k16 steps over d
+    constexpr int NB = 2;          // 32-token blocks of S^T
+    constexpr int NP = 4;          // k16 steps over the tile's tokens
+    constexpr int ND = D / 32;     // 32-wide d blocks of dQ^T
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    char* ring = smem;
+    TileTables tabs;
+    tabs.carve(smem + 2 * CP::STAGE, p.T_c);
+
+    constexpr int nthr = 64 * NW;
+    const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
+    const int l32 = lane & 31, hl = lane >> 5;
+    const int r = blockIdx.y, bi = blockIdx.z;
+    const int g = p.g, lg = p.log2g, R_t = p.R_t;
+    const int row0 = (gridDim.x - 1 - blockIdx.x) * R_t;
+    const int cq = row0 / p.B;
+    const int nvis = p.causal ? min(cq, p.T_c) : p.T_c;
+    const int last_row = min(row0 + R_t, p.n) - 1;
+    const size_t bhkv = (size_t)bi * p.h_kv + r;
+    const uint16_t* Kg = static_cast<const uint16_t*>(p.K) + bhkv * (size_t)p.n * D;
+    const uint16_t* Vg = static_cast<const uint16_t*>(p.V) + bhkv * (size_t)p.n * D;
+    const uint16_t* Ktg = x.Kt + bhkv * (size_t)D * p.n_pad;
+    const int U = tabs.build(p, bhkv, row0, nvis, tid, nthr);
+
+    // ---- the lane's (row, head) pair ----
+    const int P = wid * 32 + l32;
+    const int jrow = P >> lg, my_row = row0 + jrow;
+    const int hh = r * g + (P & (g - 1));
+    const bool live = wid * 32 < g * R_t;                     // wavefront-uniform
+    const bool pok = live && jrow < R_t && my_row < p.n;
+    ListCursor lc;
+    lc.init(p, bhkv * p.n + (pok ? my_row : 0), pok);
+    const size_t prow = ((size_t)bi * p.h_q + hh) * p.n + (pok ? my_row : 0);
+    bf16x8 qf[NS], df[NS];
+    {
+        const uint16_t* qrow = static_cast<const uint16_t*>(p.Q) + prow * D + 8 * hl;
+        const uint16_t* drow = x.dO + prow * D + 8 * hl;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            qf[s] = *reinterpret_cast<const bf16x8*>(qrow + 16 * s);
+            df[s] = *reinterpret_cast<const bf16x8*>(drow + 16 * s);
+            if (!pok) { qf[s] = bf16x8{}; df[s] = bf16x8{}; }
+        }
+    }
+    const float lse_raw = pok ? x.lse[prow] : 0.f;
+    // a row with nothing visible has lse = -inf and no gradient: P = 0 everywhere
+    const float lse2 = (lse_raw == -INFINITY) ? INFINITY : lse_raw * kLog2e;
+    const float dlt = pok ? x.delta[prow] : 0.f;
+
+    f32x16 dq[ND];
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) dq[db][i] = 0.f;
+    float dbsum = 0.f;
+
+    TileSteps st;
+    st.init(p, U, cq, last_row, TT);
+    const int nmax = p.n - 1;
+    CP cp;
+    cp.init(wid, lane);
+    const int krow = (l32 & ~12) | ((l32 & 4) << 1) | ((l32 & 8) >> 1);
+    const float c1 = p.scale_log2;
+    const int lim = p.causal ? my_row : p.n - 1;
+
+    int tb_cur, c_cur, tb_nxt, c_nxt;
+    st.at(tabs.ulist, 0, tb_cur, c_cur);
+    st.at(tabs.ulist, 1, tb_nxt, c_nxt);
+    if (st.nsteps > 0) cp.issue(ring, Kg, Vg, Ktg, tb_cur, nmax, p.n_pad, wid);
+    wait_tile_copies();
+    __syncthreads();
+    for (int k = 0; k < st.nsteps; ++k) {
+        const bool routed = k < st.nrouted;
+        const bool last = k % st.SPC == st.SPC - 1;
+        const int epos = lc.pos;                   // list position of chunk c_cur if routed
+        const float bias2 = routed ? lc.take(c_cur, last) : 0.f;
+        const bool hit = bias2 > -INFINITY;
+        const bool run = live && (!routed || ballot(hit) != 0);
+        if (k + 1 < st.nsteps)
+            cp.issue(ring + ((k + 1) & 1) * CP::STAGE, Kg, Vg, Ktg, tb_nxt, nmax, p.n_pad, wid);
+        int tb_nn, c_nn;
+        st.at(tabs.ulist, k + 2, tb_nn, c_nn);
+        const char* kt = ring + (k & 1) * CP::STAGE;
+        const char* vt = kt + S::KBYTES;
+        const char* ktt = kt + 2 * S::KBYTES;
+        const int tb = tb_cur;
+        if (run) {
+            f32x16 sacc[NB], dpacc[NB];
+#pragma unroll
+            for (int blk = 0; blk < NB; ++blk)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) { sacc[blk][i] = 0.f; dpacc[blk][i] = 0.f; }
+            // S^T = K Q^T and dP^T = V dO^T over the tile
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                bf16x8 ka[NB], va[NB];
+#pragma unroll
+                for (int blk = 0; blk < NB; ++blk) {
+                    const int t = 32 * blk + krow;
+                    const int o = t * S::KROWB + S::kslot(t, 2 * s + hl) * 16;
+                    ka[blk] = *reinterpret_cast<const bf16x8*>(kt + o);
+                    va[blk] = *reinterpret_cast<const bf16x8*>(vt + o);
+                }
+#pragma unroll
+                for (int blk = 0; blk < NB; ++blk) {
+                    sacc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[blk], qf[s], sacc[blk], 0, 0, 0);
+                    dpacc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[blk], df[s], dpacc[blk], 0, 0, 0);
+                }
+            }
+            // P from the forward's lse, dZ = P (dP - Δ); token of element e of k16
+            // step s is tb + 16 s + 8 hl + e
+            const float off = bias2 - lse2;
+            bf16x8 dz[NP];
+            float part = 0.f;
+#pragma unroll
+            for (int s = 0; s < NP; ++s)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int i = 8 * (s & 1) + e;
+                    float pv = fast_exp2(fmaf(sacc[s >> 1][i], c1, off));
+                    if (!routed && tb + 16 * s + 8 * hl + e > lim) pv = 0.f;
+                    const float z = pv * (dpacc[s >> 1][i] - dlt);
+                    part += z;
+                    dz[s][e] = (__bf16)z;
+                }
+            dbsum += part;
+            // dQ^T += K^T dZ^T
+#pragma unroll
+            for (int s = 0; s < NP; ++s) {
+                bf16x8 kta[ND];
+#pragma unroll
+                for (int db = 0; db < ND; ++db) {
+                    const int d = 32 * db + l32;
+                    kta[db] = *reinterpret_cast<const bf16x8*>(ktt + d * S::VROWB + S::vslot(d, 2 * s + hl) * 16);
+                }
+#pragma unroll
+                for (int db = 0; db < ND; ++db)
+                    dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kta[db], dz[s], dq[db], 0, 0, 0);
+            }
+            // the chunk's bias gradient: its tokens (both lane halves, all its steps)
+            // and the g heads of the row (g consecutive lanes)
+            if (routed && last) {
+                float v = pair32_sum(dbsum);
+                for (int m = 1; m < g; m <<= 1) v += shfl_xor(v, m);
+                if (pok && hit && hl == 0 && (P & (g - 1)) == 0)
+                    x.dbias[(bhkv * p.n + my_row) * p.list_cap + epos] = v;
+            }
+        }
+        if (last || !routed) dbsum = 0.f;
+        wait_tile_copies();
+        __syncthreads();
+        tb_cur = tb_nxt; c_cur = c_nxt;
+        tb_nxt = tb_nn; c_nxt = c_nn;
+    }
+
+    if (pok) {
+        const size_t obase = prow * D;
+#pragma unroll
+        for (int db = 0; db < ND; ++db)
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                const int d0 = 32 * db + 8 * a + 4 * hl;
+                f32x4 o;
+                o[0] = dq[db][4 * a] * x.scale; o[1] = dq[db][4 * a + 1] * x.scale;
+                o[2] = dq[db][4 * a + 2] * x.scale; o[3] = dq[db][4 * a + 3] * x.scale;
+                *reinterpret_cast<f32x4*>(x.dQ + obase + d0) = o;
+            }
+    }
+}
+
+// ---------------------------------------------------------------------------------
+// dK and dV (key-major)
+// ---------------------------------------------------------------------------------
+
+struct DkvParams {
+    const uint16_t* Q; const uint16_t* dO;       // bf16 [b, h_q, n, D]
+    const uint16_t* Qt; const uint16_t* dOt;     // bf16 [b*h_kv][D][n*g]
+    const uint16_t* K; const uint16_t* V;        // bf16 [b, h_kv, n, D]
+    const float* lse; const float* delta;        // [b, h_q, n]
+    const int32_t* inv_row; const float* inv_bias; const int32_t* coff;
+    float* dK; float* dV;                        // [b, h_kv, n, D], zero on entry
+    int h_q, h_kv, n, B, T_c, causal, g, log2g, seg_rows;
+    float c1, scale;                             // log2(e)/sqrt(d), 1/sqrt(d)
+};
+
+// A stage: Q and dO of 64 pairs ("K" form [64][D]), then Q^T and dO^T ("V^T" form
+// [D][64]); the pair index of a group is row_slot * g + head.
+template <int D>
+struct DkvStage {
+    typedef BfTiles<D, 64> S;
+    static constexpr int BYTES = 2 * S::KBYTES + 2 * S::VBYTES;
+    static constexpr int NI = 2 * S::KINSTS + 2 * S::VINSTS;    // wavefront copies
+};
+
+// Row of the chunk's row sequence j: the routed rows (inverted list), then the
+// diagonal rows dlo, dlo+1, ...
+struct RowSeq {
+    const int32_t* irow; const float* ibias;
+    int nrouted, dlo, j1;
+    __device__ __forceinline__ void get(int j, int& row, float& bias, bool& valid, bool& routed) const {
+        valid = j < j1;
+        routed = valid && j < nrouted;
+        row = routed ? irow[j] : (valid ? dlo + (j - nrouted) : 0);
+        bias = routed ? ibias[j] : 0.f;
+    }
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void prior_attn_dkv_kernel(DkvParams p) {
+    typedef BfTiles<D, 64> S;
+    typedef DkvStage<D> ST;
+    constexpr int NS = D / 16, ND = D / 32;
+    constexpr int CPW = ST::NI / 4;
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    char* ring = smem;
+    float* t_off = reinterpret_cast<float*>(smem + 2 * ST::BYTES);    // [2][64] bias2 - lse2
+    int* t_lim = reinterpret_cast<int*>(t_off + 128);                  // [2][64] last visible token
+    float* t_dlt = reinterpret_cast<float*>(t_lim + 128);              // [2][64] Δ
+    int* t_row = reinterpret_cast<int*>(t_dlt + 128);                  // [2][8] rows of a group
+
+    const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
+    const int l32 = lane & 31, hl = lane >> 5;
+    const int seg = blockIdx.x, cs = blockIdx.y;
+    const size_t bhk = blockIdx.z;
+    const int bi = (int)(bhk / p.h_kv), hk = (int)(bhk % p.h_kv);
+    const int T = p.T_c, SUB = p.B / 64;
+    const int c = cs / SUB, t0 = c * p.B + 64 * (cs % SUB);
+    if (t0 >= p.n) return;
+    int nrouted = 0, rbase = 0;
+    if (c < T) {
+        rbase = p.coff[bhk * (T + 1) + c];
+        nrouted = p.coff[bhk * (T + 1) + c + 1] - rbase;
+    }
+    int dlo = 0, dhi = 0;
+    if (p.causal) { dlo = t0; dhi = min(c * p.B + p.B, p.n); }
+    else if (c == T) { dlo = 0; dhi = p.n; }
+    const int nrows = nrouted + max(dhi - dlo, 0);
+    const int j0 = seg * p.seg_rows, j1 = min(nrows, j0 + p.seg_rows);
+    if (j0 >= j1) return;
+    const int g = p.g, lg = p.log2g, RG = 64 >> lg;
+    const int ngroups = (j1 - j0 + RG - 1) / RG;
+    RowSeq rs;
+    rs.irow = p.inv_row + bhk * (size_t)p.n * T + rbase;
+    rs.ibias = p.inv_bias + bhk * (size_t)p.n * T + rbase;
+    rs.nrouted = nrouted; rs.dlo = dlo; rs.j1 = j1;
+
+    // ---- K and V of the wavefront's 32 tokens as B operands (token = lane column) ----
+    const int tbk = wid & 1, half = wid >> 1;
+    const int tok = t0 + 32 * tbk + l32;
+    bf16x8 kreg[NS], vreg[NS];
+    {
+        const size_t kb = (bhk * p.n + min(tok, p.n - 1)) * D + 8 * hl;
+        const uint16_t* K = p.K;
+        const uint16_t* V = p.V;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            kreg[s] = *reinterpret_cast<const bf16x8*>(K + kb + 16 * s);
+            vreg[s] = *reinterpret_cast<const bf16x8*>(V + kb + 16 * s);
+            if (tok >= p.n) { kreg[s] = bf16x8{}; vreg[s] = bf16x8{}; }
+        }
+    }
+
+    // ---- tables: lanes 0..15 of each wavefront keep the pair 16*wid + lane ----
+    const bool TL = lane < 16;
+    const int tp = 16 * wid + (lane & 15);
+    const int tslot = tp >> lg, thead = tp & (g - 1);
+    const size_t hbase = ((size_t)bi * p.h_q + (size_t)hk * g + thead) * p.n;
+    auto pair_tables = [&](int slot, int row, float bias, bool valid, bool routed, float lse, float dl) {
+        const float l2 = (lse == -INFINITY) ? INFINITY : lse * kLog2e;
+        t_off[slot * 64 + tp] = valid ? bias * kLog2e - l2 : -INFINITY;
+        t_lim[slot * 64 + tp] = !valid ? -1 : routed ? 0x7fffffff : (p.causal ? row : p.n - 1);
+        t_dlt[slot * 64 + tp] = valid ? dl : 0.f;
+    };
+
+    // ---- copies of a group's stage ----
+    const size_t npairs = (size_t)p.n * g;
+    const uint16_t* Qg = p.Q + ((size_t)bi * p.h_q + (size_t)hk * g) * p.n * D;
+    const uint16_t* dOg = p.dO + ((size_t)bi * p.h_q + (size_t)hk * g) * p.n * D;
+    const uint16_t* Qtg = p.Qt + bhk * D * npairs;
+    const uint16_t* dOtg = p.dOt + bhk * D * npairs;
+    auto issue = [&](char* stage, const int* rows) {
+#pragma unroll
+        for (int i = 0; i < CPW; ++i) {
+            const int j = wid + 4 * i;                 // wavefront-uniform
+            const uint16_t* src;
+            int dst;
+            if (j < 2 * S::KINSTS) {
+                const int jj = j % S::KINSTS;
+                const int q = jj * 64 + lane, t = q / S::KPPR, cc = q % S::KPPR;
+                const int row = min(max(rows[t >> lg], 0), p.n - 1);
+                const size_t o = ((size_t)(t & (g - 1)) * p.n + row) * D + S::kslot(t, cc) * 8;
+                src = (j < S::KINSTS ? Qg : dOg) + o;
+                dst = (j < S::KINSTS ? 0 : S::KBYTES) + jj * 1024;
+            } else {
+                const int j2 = j - 2 * S::KINSTS;
+                const int jj = j2 % S::VINSTS;
+                const int q = jj * 64 + lane, d = q / S::VPPR, cc = q % S::VPPR;
+                const int pr = 8 * S::vslot(d, cc);
+                const int row = min(max(rows[pr >> lg], 0), p.n - 1);
+                const size_t o = (size_t)d * npairs + (size_t)row * g + (pr & (g - 1));
+                src = (j2 < S::VINSTS ? Qtg : dOtg) + o;
+                dst = 2 * S::KBYTES + (j2 < S::VINSTS ? 0 : S::VBYTES) + jj * 1024;
+            }
+            __builtin_amdgcn_global_load_lds(src, stage + dst, 16, 0, 0);
+        }
+    };
+
+    // ---- prologue: tables of group 0, rows of groups 0 and 1, copies of group 0 ----
+    int nx_row; float nx_bias; bool nx_valid, nx_routed;     // group k+1 (table lanes)
+    {
+        int row; float bias; bool valid, routed;
+        rs.get(j0 + tslot, row, bias, valid, routed);
+        rs.get(j0 + RG + tslot, nx_row, nx_bias, nx_valid, nx_routed);
+        if (TL) {
+            const float lse = valid ? p.lse[hbase + row] : 0.f;
+            const float dl = valid ? p.delta[hbase + row] : 0.f;
+            pair_tables(0, row, bias, valid, routed, lse, dl);
+            if (thead == 0) {
+                t_row[tslot] = row;
+                t_row[8 + tslot] = nx_row;
+            }
+        }
+    }
+    __syncthreads();
+    issue(ring, t_row);
+    wait_tile_copies();
+    __syncthreads();
+
+    f32x16 dk[ND], dv[ND];
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) { dk[db][i] = 0.f; dv[db][i] = 0.f; }
+    // A row l32 presents pair (bits 2 and 3 swapped): accumulator element 8s + e of a
+    // lane is then pair 16s + 8hl + e, the k-slot order of the pair contraction
+    const int prow_a = 32 * half + ((l32 & ~12) | ((l32 & 4) << 1) | ((l32 & 8) >> 1));
+    const float c1 = p.c1;
+
+    for (int k = 0; k < ngroups; ++k) {
+        // table lanes: rows of group k+2 and lse / Δ of group k+1
+        int nn_row; float nn_bias; bool nn_valid, nn_routed;
+        rs.get(j0 + (k + 2) * RG + tslot, nn_row, nn_bias, nn_valid, nn_routed);
+        float lse_n = 0.f, dlt_n = 0.f;
+        if (TL && nx_valid) {
+            lse_n = p.lse[hbase + nx_row];
+            dlt_n = p.delta[hbase + nx_row];
+        }
+        if (k + 1 < ngroups) issue(ring + ((k + 1) & 1) * ST::BYTES, t_row + ((k + 1) & 1) * 8);
+
+        const char* qt = ring + (k & 1) * ST::BYTES;
+        const char* dot = qt + S::KBYTES;
+        const char* qtt = qt + 2 * S::KBYTES;
+        const char* dott = qtt + S::VBYTES;
+        // S = Q K^T and dP = dO V^T for this wavefront's 32 pairs x 32 tokens
+        f32x16 sacc, dpacc;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) { sacc[i] = 0.f; dpacc[i] = 0.f; }
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const int o = prow_a * S::KROWB + S::kslot(prow_a, 2 * s + hl) * 16;
+            const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qt + o);
+            const bf16x8 da = *reinterpret_cast<const bf16x8*>(dot + o);
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kreg[s], sacc, 0, 0, 0);
+            dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vreg[s], dpacc, 0, 0, 0);
+        }
+        // P and dZ per pair: element 8s + e is pair 32 half + 16 s + 8 hl + e
+        const int tb = (k & 1) * 64 + 32 * half + 8 * hl;
+        bf16x8 pa[2], za[2];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const f32x4 o0 = *reinterpret_cast<const f32x4*>(t_off + tb + 16 * s);
+            const f32x4 o1 = *reinterpret_cast<const f32x4*>(t_off + tb + 16 * s + 4);
+            const u32x4 m0 = *reinterpret_cast<const u32x4*>(t_lim + tb + 16 * s);
+            const u32x4 m1 = *reinterpret_cast<const u32x4*>(t_lim + tb + 16 * s + 4);
+            const f32x4 d0 = *reinterpret_cast<const f32x4*>(t_dlt + tb + 16 * s);
+            const f32x4 d1 = *reinterpret_cast<const f32x4*>(t_dlt + tb + 16 * s + 4);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float off = e < 4 ? o0[e & 3] : o1[e & 3];
+                const int lim = (int)(e < 4 ? m0[e & 3] : m1[e & 3]);
+                const float dl = e < 4 ? d0[e & 3] : d1[e & 3];
+                float pv = fast_exp2(fmaf(sacc[8 * s + e], c1, off));
+                if (tok > lim) pv = 0.f;
+                const float z = pv * (dpacc[8 * s + e] - dl);
+                pa[s][e] = (__bf16)pv;
+                za[s][e] = (__bf16)z;
+            }
+        }
+        // dV += P^T dO and dK += dZ^T Q over the 32 pairs
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            bf16x8 ob[ND], qb[ND];
+#pragma unroll
+            for (int db = 0; db < ND; ++db) {
+                const int d = 32 * db + l32;
+                const int o = d * S::VROWB + S::vslot(d, 4 * half + 2 * s + hl) * 16;
+                ob[db] = *reinterpret_cast<const bf16x8*>(dott + o);
+                qb[db] = *reinterpret_cast<const bf16x8*>(qtt + o);
+            }
+#pragma unroll
+            for (int db = 0; db < ND; ++db) {
+                dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[s], ob[db], dv[db], 0, 0, 0);
+                dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(za[s], qb[db], dk[db], 0, 0, 0);
+            }
+        }
+
+        // tables of group k+1 (their slot was last read in step k-1) and rows of
+        // group k+2 (their slot was last read by the copies of step k-1)
+        if (TL) {
+            pair_tables((k + 1) & 1, nx_row, nx_bias, nx_valid, nx_routed, lse_n, dlt_n);
+            if (thead == 0) t_row[(k & 1) * 8 + tslot] = nn_row;
+        }
+        nx_row = nn_row; nx_bias = nn_bias; nx_valid = nn_valid; nx_routed = nn_routed;
+        wait_tile_copies();
+        __syncthreads();
+    }
+
+    // ---- add the partials: element i of lane l is token 8(i/4) + 4hl + i%4 of the
+    // wavefront's 32, column d = 32 db + l32 ----
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int t = t0 + 32 * tbk + 8 * (i >> 2) + 4 * hl + (i & 3);
+            if (t < p.n) {
+                const size_t o = (bhk * p.n + t) * D + 32 * db + l32;
+                unsafeAtomicAdd(p.dK + o, dk[db][i] * p.scale);
+                unsafeAtomicAdd(p.dV + o, dv[db][i]);
+            }
+        }
+}
+
+// ---------------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------------
+
+static constexpr int kDqWaves = 4;
+static constexpr size_t kBwdMaxLds = 160 * 1024;
+
+static size_t dq_lds_bytes(int d, int T_c) {
+    const size_t stage = d == 64 ? DqCopier<64, kDqWaves>::STAGE : DqCopier<128, kDqWaves>::STAGE;
+    return 2 * stage + TileTables::bytes(T_c);
+}
+static size_t dkv_lds_bytes(int d) {
+    const size_t stage = d == 64 ? DkvStage<64>::BYTES : DkvStage<128>::BYTES;
+    return 2 * stage + 3 * 128 * 4 + 16 * 4;
+}
+
+int backward_tile_rows(int g, int B, int T_c, int d) {
+    if ((g != 8 && g != 16) || B % 64 != 0 || (d != 64 && d != 128)) return 0;
+    if (dq_lds_bytes(d, T_c) > kBwdMaxLds) return 0;
+    return 32 * kDqWaves / g;
+}
+
+namespace {
+struct BwdLayout {
+    size_t kt, qt, dot, dob, delta, hist, coff, inv_row, inv_bias, total;
+};
+size_t up256(size_t x) { return (x + 255) / 256 * 256; }
+BwdLayout bwd_layout(int b, int h_q, int h_kv, int n, int d, int B) {
+    BwdLayout L;
+    const size_t T = (size_t)(n / B), nblk = ((size_t)n + 63) / 64;
+    size_t o = 0;
+    L.kt = o;       o += up256(prefill_workspace_bytes(b, h_kv, n, d));
+    L.qt = o;       o += up256((size_t)b * h_q * n * d * 2);
+    L.dot = o;      o += up256((size_t)b * h_q * n * d * 2);
+    L.dob = o;      o += up256((size_t)b * h_q * n * d * 2);
+    L.delta = o;    o += up256((size_t)b * h_q * n * 4);
+    L.hist = o;     o += up256((size_t)b * h_kv * T * nblk * 4);
+    L.coff = o;     o += up256((size_t)b * h_kv * (T + 1) * 4);
+    L.inv_row = o;  o += up256((size_t)b * h_kv * n * T * 4);
+    L.inv_bias = o; o += up256((size_t)b * h_kv * n * T * 4);
+    L.total = o;
+    return L;
+}
+}  // namespace
+
+size_t backward_workspace_bytes(int b, int h_q, int h_kv, int n, int d, int B) {
+    return bwd_layout(b, h_q, h_kv, n, d, B).total;
+}
+
+static hipError_t fill_zero(float* x, size_t n, hipStream_t s) {
+    if (n == 0) return hipSuccess;
+    const size_t blocks = std::min<size_t>((n + 255) / 256, 65536);
+    hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, s, x, n);
+    return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_bwd_t(const PrefillBwdArgs& a, const BwdLayout& L, hipStream_t s) {
+    char* ws = static_cast<char*>(a.ws);
+    const int g = a.h_q / a.h_kv;
+    int lg = 0;
+    while ((1 << lg) < g) ++lg;
+    const int T = a.n / a.B, n_pad = prefill_n_pad(a.n), nblk = (a.n + 63) / 64;
+    const int bh = a.b * a.h_kv;
+    uint16_t* kt = reinterpret_cast<uint16_t*>(ws + L.kt);
+    uint16_t* qt = reinterpret_cast<uint16_t*>(ws + L.qt);
+    uint16_t* dot = reinterpret_cast<uint16_t*>(ws + L.dot);
+    uint16_t* dob = a.o_bf16 ? nullptr : reinterpret_cast<uint16_t*>(ws + L.dob);
+    float* delta = reinterpret_cast<float*>(ws + L.delta);
+    const uint16_t* dO16 = a.o_bf16 ? static_cast<const uint16_t*>(a.dO) : dob;
+
+    hipError_t e;
+    if ((e = fill_zero(a.dK, (size_t)bh * a.n * D, s)) != hipSuccess) return e;
+    if ((e = fill_zero(a.dV, (size_t)bh * a.n * D, s)) != hipSuccess) return e;
+    if ((e = fill_zero(a.dbias, (size_t)bh * a.n * a.list_cap, s)) != hipSuccess) return e;
+    if ((e = launch_transpose_rows(static_cast<const uint16_t*>(a.K), kt, bh, a.n, n_pad, D, s)) != hipSuccess)
+        return e;
+
+    BwdPrepParams pp{static_cast<const uint16_t*>(a.Q), a.O, a.dO, qt, dot, dob, delta, a.h_q, a.h_kv, a.n, g, lg};
+    const dim3 pgrid((unsigned)(((size_t)a.n * g + 63) / 64), a.h_kv, a.b);
+    if (a.o_bf16) hipLaunchKernelGGL((bwd_prep_kernel<D, uint16_t>), pgrid, dim3(256), 0, s, pp);
+    else hipLaunchKernelGGL((bwd_prep_kernel<D, float>), pgrid, dim3(256), 0, s, pp);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+
+    InvParams ip{a.idx, a.bias, a.cnt,
+                 reinterpret_cast<int32_t*>(ws + L.hist), reinterpret_cast<int32_t*>(ws + L.coff),
+                 reinterpret_cast<int32_t*>(ws + L.inv_row), reinterpret_cast<float*>(ws + L.inv_bias),
+                 a.n, a.B, T, nblk, a.list_cap, a.causal};
+    if (T > 0) {
+        const size_t mlds = (size_t)T * 8;
+        hipLaunchKernelGGL(inv_hist_kernel, dim3(nblk, bh), dim3(64), mlds, s, ip);
+        hipLaunchKernelGGL(inv_scan_blocks_kernel, dim3(T, bh), dim3(256), 0, s, ip);
+        hipLaunchKernelGGL(inv_scan_chunks_kernel, dim3(bh), dim3(256), 0, s, ip);
+        hipLaunchKernelGGL(inv_scatter_kernel, dim3(nblk, bh), dim3(64), mlds, s, ip);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+
+    // dQ and the bias gradients
+    PrefillParams p;
+    p.Q = a.Q; p.K = a.K; p.V = a.V; p.Vt = nullptr;
+    p.idx = a.idx; p.bias = a.bias; p.cnt = a.cnt; p.O = nullptr; p.lse = nullptr;
+    p.out_bf16 = 0; p.h_q = a.h_q; p.h_kv = a.h_kv; p.n = a.n; p.n_pad = n_pad; p.B = a.B;
+    p.T_c = T; p.list_cap = a.list_cap; p.causal = a.causal; p.g = g; p.log2g = lg;
+    p.R_t = backward_tile_rows(g, a.B, T, D);
+    p.nw = kDqWaves;
+    p.scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
+    const float scale = (float)(1.0 / sqrt((double)D));
+    DqExtra x{kt, dO16, a.lse, delta, a.dQ, a.dbias, scale};
+    {
+        auto kern = prior_attn_dq_kernel<D, kDqWaves>;
+        static hipError_t configured = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)kBwdMaxLds);
+        if (configured != hipSuccess) return configured;
+        dim3 grid((a.n + p.R_t - 1) / p.R_t, a.h_kv, a.b);
+        hipLaunchKernelGGL(kern, grid, dim3(64 * kDqWaves), dq_lds_bytes(D, T), s, p, x);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+
+    // dK and dV
+    DkvParams q;
+    q.Q = static_cast<const uint16_t*>(a.Q); q.dO = dO16; q.Qt = qt; q.dOt = dot;
+    q.K = static_cast<const uint16_t*>(a.K); q.V = static_cast<const uint16_t*>(a.V);
+    q.lse = a.lse; q.delta = delta;
+    q.inv_row = ip.inv_row; q.inv_bias = ip.inv_bias; q.coff = ip.coff;
+    q.dK = a.dK; q.dV = a.dV;
+    q.h_q = a.h_q; q.h_kv = a.h_kv; q.n = a.n; q.B = a.B; q.T_c = T; q.causal = a.causal;
+    q.g = g; q.log2g = lg;
+    q.seg_rows = 8192 / g;
+    q.c1 = p.scale_log2; q.scale = scale;
+    {
+        auto kern = prior_attn_dkv_kernel<D>;
+        static hipError_t configured = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)kBwdMaxLds);
+        if (configured != hipSuccess) return configured;
+        const int nseg = (a.n + q.seg_rows - 1) / q.seg_rows;
+        dim3 grid(nseg, (T + 1) * (a.B / 64), bh);
+        hipLaunchKernelGGL(kern, grid, dim3(256), dkv_lds_bytes(D), s, q);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_attend_prefill_backward(const PrefillBwdArgs& a, hipStream_t s) {
+    if (a.n == 0) return hipSuccess;
+    const BwdLayout L = bwd_layout(a.b, a.h_q, a.h_kv, a.n, a.d, a.B);
+    return a.d == 64 ? launch_bwd_t<64>(a, L, s) : launch_bwd_t<128>(a, L, s);
+}
+
+}  // namespace dash

@@ -194,6 +194,9 @@ __global__ __launch_bounds__(64 * kWaves) void sparse_prior_attn_kernel(PrefillP
     const float l_tot = pair32_sum(l_run);
     if (pair_ok) {
         const float inv = 1.f / l_tot;
+        if (p.lse && hl == 0)
+            p.lse[((size_t)bi * p.h_q + hh) * p.n + my_row] =
+                (((m_run == -INFINITY) ? 0.f : m_run) + fast_log2(l_tot)) * kLn2;
         const size_t obase = (((size_t)bi * p.h_q + hh) * p.n + my_row) * D;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
@@ -263,6 +266,7 @@ hipError_t launch_prefill_f32(const PrefillParams& p, int b, int d, size_t lds, 
 hipError_t launch_attend_prefill(const PrefillArgs& a, hipStream_t s) {
     PrefillParams p;
     p.Q = a.Q; p.K = a.K; p.V = a.V; p.idx = a.idx; p.bias = a.bias; p.cnt = a.cnt; p.O = a.O;
+    p.lse = a.lse;
     p.Vt = static_cast<const uint16_t*>(a.ws);
     p.out_bf16 = a.out_bf16; p.h_q = a.h_q; p.h_kv = a.h_kv; p.n = a.n; p.B = a.B;
     p.n_pad = prefill_n_pad(a.n);

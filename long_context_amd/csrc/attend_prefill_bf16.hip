@@ -24,27 +24,6 @@
 namespace dash {
 
 
-// LDS layout of one stage: the K tile [TT][D] then the V^T tile [D][TT], both
-// unpadded, split into 16-byte pieces stored at piece slot c ^ swz(row) so that 16
-// lanes reading one piece column of 16 different rows hit 16 distinct bank groups
-// (RPB rows share one 256-byte bank row).
-template <int D, int TT>
-struct BfTiles {
-    static constexpr int KROWB = D * 2;
-    static constexpr int KPPR = KROWB / 16;
-    static constexpr int KRPB = KROWB >= 256 ? 1 : 256 / KROWB;
-    static constexpr int KBYTES = TT * KROWB;
-    static constexpr int VROWB = TT * 2;
-    static constexpr int VPPR = VROWB / 16;
-    static constexpr int VRPB = 256 / VROWB;
-    static constexpr int VBYTES = D * VROWB;
-    static constexpr int STAGE = KBYTES + VBYTES;
-    static constexpr int KINSTS = KBYTES / 1024;     // wavefront copy instructions per tile
-    static constexpr int VINSTS = VBYTES / 1024;
-    __device__ __forceinline__ static int kslot(int t, int c) { return c ^ ((t / KRPB) & (KPPR - 1)); }
-    __device__ __forceinline__ static int vslot(int d, int c) { return c ^ ((d / VRPB) & (VPPR - 1)); }
-};
-
 // Copies of one stage split over NW wavefronts: wavefront w issues copy
 // instructions w, w+NW, ...; instructions 0..KINSTS-1 copy K pieces, the rest V^T.
 template <int D, int TT, int NW>
@@ -334,6 +313,11 @@ __global__ __launch_bounds__(64 * NW) void sparse_prior_attn_bf16_kernel(Prefill
         if (pok[pb]) {
             const int hh = r * g + (((wid * PBW + pb) * 32 + l32) & (g - 1));
             const float inv = 1.f / l_tot;
+            // log-sum-exp of the row's logits: P was taken relative to 2^m (m = 0 if
+            // nothing was visible), so sum_j e^{z_j} = 2^m l
+            if (p.lse && hl == 0)
+                p.lse[((size_t)bi * p.h_q + hh) * p.n + my_row[pb]] =
+                    (((m_run[pb] == -INFINITY) ? 0.f : m_run[pb]) + fast_log2(l_tot)) * kLn2;
             const size_t obase = (((size_t)bi * p.h_q + hh) * p.n + my_row[pb]) * D;
 #pragma unroll
             for (int db = 0; db < ND; ++db)
@@ -359,6 +343,15 @@ __global__ __launch_bounds__(64 * NW) void sparse_prior_attn_bf16_kernel(Prefill
 }
 
 int prefill_n_pad(int n) { return (n + 63) / 64 * 64; }
+
+hipError_t launch_transpose_rows(const uint16_t* src, uint16_t* dst, int bh, int n, int n_pad, int d, hipStream_t s) {
+    if (n_pad == 0) return hipSuccess;
+    if (d == 64)
+        hipLaunchKernelGGL((transpose_v_kernel<64>), dim3(n_pad / 64, bh), dim3(256), 0, s, src, dst, n, n_pad);
+    else
+        hipLaunchKernelGGL((transpose_v_kernel<128>), dim3(n_pad / 64, bh), dim3(256), 0, s, src, dst, n, n_pad);
+    return hipGetLastError();
+}
 
 size_t prefill_workspace_bytes(int b, int h_kv, int n, int d) {
     return (size_t)b * h_kv * d * (size_t)prefill_n_pad(n) * sizeof(uint16_t);

@@ -184,11 +184,11 @@ dash_status dash_route_mask(const int32_t* idx, const int32_t* cnt, int b, int h
                     "lists_to_mask_kernel");
 }
 
-dash_status dash_attend_prefill(const void* Q, const void* K, const void* V, int in_dtype,
-                                const int32_t* idx, const float* bias, const int32_t* cnt,
-                                int list_cap, void* O, int out_dtype,
-                                int b, int h_q, int h_kv, int n, int d, int B, int causal,
-                                void* ws, size_t ws_bytes, void* stream) {
+dash_status dash_attend_prefill_lse(const void* Q, const void* K, const void* V, int in_dtype,
+                                    const int32_t* idx, const float* bias, const int32_t* cnt,
+                                    int list_cap, void* O, int out_dtype, float* lse,
+                                    int b, int h_q, int h_kv, int n, int d, int B, int causal,
+                                    void* ws, size_t ws_bytes, void* stream) {
     if (!Q || !K || !V || !idx || !bias || !cnt || !O) return fail(DASH_ERR_NULL, "Q, K, V, idx, bias, cnt and O must be non-null");
     if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return fail(DASH_ERR_PARAM, "bad dtype");
     if (causal != 0 && causal != 1) return fail(DASH_ERR_PARAM, "causal must be 0 or 1");
@@ -208,8 +208,48 @@ dash_status dash_attend_prefill(const void* Q, const void* K, const void* V, int
             return fail(DASH_ERR_WORKSPACE, "bf16 prefill needs %zu workspace bytes, got %zu", need, ws ? ws_bytes : (size_t)0);
     }
     dash::PrefillArgs a{Q, K, V, in_dtype == DASH_BF16, idx, bias, cnt, list_cap, O, out_dtype == DASH_BF16,
-                        b, h_q, h_kv, n, d, B, causal, ws};
+                        b, h_q, h_kv, n, d, B, causal, ws, lse};
     return from_hip(dash::launch_attend_prefill(a, (hipStream_t)stream), "sparse_prior_attn_kernel");
+}
+
+dash_status dash_attend_prefill(const void* Q, const void* K, const void* V, int in_dtype,
+                                const int32_t* idx, const float* bias, const int32_t* cnt,
+                                int list_cap, void* O, int out_dtype,
+                                int b, int h_q, int h_kv, int n, int d, int B, int causal,
+                                void* ws, size_t ws_bytes, void* stream) {
+    return dash_attend_prefill_lse(Q, K, V, in_dtype, idx, bias, cnt, list_cap, O, out_dtype, nullptr, b, h_q, h_kv,
+                                   n, d, B, causal, ws, ws_bytes, stream);
+}
+
+dash_status dash_attend_prefill_backward(const void* Q, const void* K, const void* V, int in_dtype,
+                                         const int32_t* idx, const float* bias, const int32_t* cnt, int list_cap,
+                                         const void* O, const void* dO, int o_dtype, const float* lse,
+                                         float* dQ, float* dK, float* dV, float* dbias,
+                                         int b, int h_q, int h_kv, int n, int d, int B, int causal,
+                                         void* ws, size_t ws_bytes, void* stream) {
+    if (!Q || !K || !V || !idx || !bias || !cnt || !O || !dO || !lse || !dQ || !dK || !dV || !dbias)
+        return fail(DASH_ERR_NULL, "every tensor argument of the backward must be non-null");
+    if (!valid_dtype(in_dtype) || !valid_dtype(o_dtype)) return fail(DASH_ERR_PARAM, "bad dtype");
+    if (causal != 0 && causal != 1) return fail(DASH_ERR_PARAM, "causal must be 0 or 1");
+    dash_status st = check_common(b, h_q, h_kv, d, B);
+    if (st != DASH_OK) return st;
+    if (in_dtype != DASH_BF16) return fail(DASH_ERR_UNSUPPORTED, "the Stage-2 backward takes bf16 Q, K, V");
+    if (B % 64 != 0) return fail(DASH_ERR_UNSUPPORTED, "the Stage-2 backward needs B %% 64 == 0 (B = %d)", B);
+    if (n < 0) return fail(DASH_ERR_SHAPE, "n must be >= 0");
+    const int T = n / B;
+    if (list_cap < T) return fail(DASH_ERR_SHAPE, "list_cap %d < floor(n/B) = %d", list_cap, T);
+    if (dash::backward_tile_rows(h_q / h_kv, B, T, d) == 0)
+        return fail(DASH_ERR_UNSUPPORTED, "no backward query tiling fits LDS (g=%d, B=%d, T_c=%d)", h_q / h_kv, B, T);
+    if ((int64_t)n * T >= ((int64_t)1 << 31))
+        return fail(DASH_ERR_UNSUPPORTED, "the backward needs n * floor(n/B) < 2^31 (n = %d, B = %d)", n, B);
+    if (n > 0) {
+        const size_t need = dash::backward_workspace_bytes(b, h_q, h_kv, n, d, B);
+        if (!ws || ws_bytes < need)
+            return fail(DASH_ERR_WORKSPACE, "the backward needs %zu workspace bytes, got %zu", need, ws ? ws_bytes : (size_t)0);
+    }
+    dash::PrefillBwdArgs a{Q, K, V, idx, bias, cnt, list_cap, O, dO, o_dtype == DASH_BF16, lse,
+                           dQ, dK, dV, dbias, b, h_q, h_kv, n, d, B, causal, ws};
+    return from_hip(dash::launch_attend_prefill_backward(a, (hipStream_t)stream), "sparse_prior_attn_bwd_kernel");
 }
 
 size_t dash_workspace_bytes(int op, int b, int h_q, int h_kv, int n_or_Lcap, int d, int B) {
@@ -217,6 +257,7 @@ size_t dash_workspace_bytes(int op, int b, int h_q, int h_kv, int n_or_Lcap, int
     switch (op) {
         case DASH_OP_ROUTE: return dash::route_workspace_bytes(b, h_kv, n_or_Lcap / B, d);
         case DASH_OP_PREFILL: return dash::prefill_workspace_bytes(b, h_kv, n_or_Lcap, d);
+        case DASH_OP_PREFILL_BWD: return dash::backward_workspace_bytes(b, h_q, h_kv, n_or_Lcap, d, B);
         case DASH_OP_DECODE: {
             if (n_or_Lcap < 1) return (size_t)-1;
             return decode_layout(b, h_q, h_kv, n_or_Lcap, 1 << 30, d, B).total;

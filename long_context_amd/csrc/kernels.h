@@ -49,8 +49,27 @@ struct PrefillArgs {
     void* O; bool out_bf16;
     int b, h_q, h_kv, n, d, B, causal;
     void* ws;            // bf16 inputs: V transposed, prefill_workspace_bytes
+    float* lse = nullptr;  // optional [b, h_q, n] log-sum-exp of each row's logits
 };
 hipError_t launch_attend_prefill(const PrefillArgs& a, hipStream_t s);
+
+// Stage-2 backward for bf16 inputs (attend_backward_bf16.hip).
+struct PrefillBwdArgs {
+    const void* Q; const void* K; const void* V;
+    const int32_t* idx; const float* bias; const int32_t* cnt; int list_cap;
+    const void* O; const void* dO; bool o_bf16; const float* lse;
+    float* dQ; float* dK; float* dV; float* dbias;
+    int b, h_q, h_kv, n, d, B, causal;
+    void* ws;            // K transposed, prefill_workspace_bytes
+};
+hipError_t launch_attend_prefill_backward(const PrefillBwdArgs& a, hipStream_t s);
+// Rows per backward query tile for group size g at T_c chunks (0: unsupported).
+int backward_tile_rows(int g, int B, int T_c, int d);
+// Workspace of the backward: K^T, Q^T and dO^T per KV group, a bf16 dO, Δ and the
+// inverted routed lists (sized for every row routing every visible chunk).
+size_t backward_workspace_bytes(int b, int h_q, int h_kv, int n, int d, int B);
+// V or K [b*h_kv][n][d] bf16 -> [b*h_kv][d][n_pad] (zero tokens n .. n_pad-1).
+hipError_t launch_transpose_rows(const uint16_t* src, uint16_t* dst, int bh, int n, int n_pad, int d, hipStream_t s);
 // Workspace of a bf16 prefill: V transposed per (b, KV head) as [d][n_pad] bf16 with
 // n_pad = n rounded up to 64 (the pad is zero-filled).
 int prefill_n_pad(int n);

@@ -23,6 +23,7 @@ struct PrefillParams {
     const uint16_t* Vt;  // bf16 path: V transposed per (b, KV head): [d][n_pad]
     const int32_t* idx; const float* bias; const int32_t* cnt;
     void* O;
+    float* lse;          // nullable: per (b, query head, row) log-sum-exp of the logits
     int out_bf16, h_q, h_kv, n, n_pad, B, T_c, list_cap, causal, g, log2g, R_t, nw;
     float scale_log2;    // log2(e)/sqrt(d)
 };
@@ -137,6 +138,27 @@ struct TileSteps {
         c = k < nrouted ? ulist[k / SPC] : 0;
         tb = k < nrouted ? c * (SPC * TT) + (k % SPC) * TT : k < nsteps ? diag_base + (k - nrouted) * TT : 0;
     }
+};
+
+// bf16 tiles in LDS: a row-major tile [TT][D] ("K" form) and a transposed tile
+// [D][TT] ("V^T" form), both unpadded, split into 16-byte pieces stored at piece
+// slot c ^ swz(row) so that 16 lanes reading one piece column of 16 different rows
+// hit 16 distinct bank groups (RPB rows share one 256-byte bank row).
+template <int D, int TT>
+struct BfTiles {
+    static constexpr int KROWB = D * 2;
+    static constexpr int KPPR = KROWB / 16;
+    static constexpr int KRPB = KROWB >= 256 ? 1 : 256 / KROWB;
+    static constexpr int KBYTES = TT * KROWB;
+    static constexpr int VROWB = TT * 2;
+    static constexpr int VPPR = VROWB / 16;
+    static constexpr int VRPB = 256 / VROWB;
+    static constexpr int VBYTES = D * VROWB;
+    static constexpr int STAGE = KBYTES + VBYTES;
+    static constexpr int KINSTS = KBYTES / 1024;     // wavefront copy instructions per tile
+    static constexpr int VINSTS = VBYTES / 1024;
+    __device__ __forceinline__ static int kslot(int t, int c) { return c ^ ((t / KRPB) & (KPPR - 1)); }
+    __device__ __forceinline__ static int vslot(int d, int c) { return c ^ ((d / VRPB) & (VPPR - 1)); }
 };
 
 // Launch geometry of a prefill kernel: tokens per tile, wavefronts per workgroup,

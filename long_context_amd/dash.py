@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_HERE, "libdash.so")
 DASH_OK, DASH_ERR_NULL, DASH_ERR_SHAPE, DASH_ERR_PARAM = 0, 1, 2, 3
 DASH_ERR_UNSUPPORTED, DASH_ERR_WORKSPACE, DASH_ERR_LAUNCH = 4, 5, 6
 DASH_F32, DASH_BF16 = 0, 1
-DASH_OP_ROUTE, DASH_OP_PREFILL, DASH_OP_DECODE = 0, 1, 2
+DASH_OP_ROUTE, DASH_OP_PREFILL, DASH_OP_DECODE, DASH_OP_PREFILL_BWD = 0, 1, 2, 3
 
 
 def _load():
@@ -42,6 +42,13 @@ def _load():
     lib.dash_attend_prefill.argtypes = [vp, vp, vp, i32, vp, vp, vp, i32, vp, i32,
                                         i32, i32, i32, i32, i32, i32, i32, vp, sz, vp]
     lib.dash_attend_prefill.restype = i32
+    lib.dash_attend_prefill_lse.argtypes = [vp, vp, vp, i32, vp, vp, vp, i32, vp, i32, vp,
+                                            i32, i32, i32, i32, i32, i32, i32, vp, sz, vp]
+    lib.dash_attend_prefill_lse.restype = i32
+    lib.dash_attend_prefill_backward.argtypes = [vp, vp, vp, i32, vp, vp, vp, i32, vp, vp, i32, vp,
+                                                 vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                                 vp, sz, vp]
+    lib.dash_attend_prefill_backward.restype = i32
     lib.dash_attend_decode.argtypes = [vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                        f32, f32, f32, vp, i32, vp, vp, vp, vp, i32, vp, sz, vp]
     lib.dash_attend_decode.restype = i32
@@ -62,7 +69,8 @@ def _load():
 lib = _load()
 
 SYMBOLS = ("dash_summarize", "dash_summarize_paged", "dash_route", "dash_route_topk", "dash_route_mask",
-           "dash_attend_prefill", "dash_attend_decode", "dash_attend_decode_paged",
+           "dash_attend_prefill", "dash_attend_prefill_lse", "dash_attend_prefill_backward",
+           "dash_attend_decode", "dash_attend_decode_paged",
            "dash_workspace_bytes", "dash_status_string", "dash_last_error")
 
 
@@ -158,6 +166,38 @@ def dash_attend_prefill(Q, K, V, idx, bias, cnt, O, B, causal, ws=None, stream=N
                                    _stream(stream)))
 
 
+def dash_attend_prefill_lse(Q, K, V, idx, bias, cnt, O, lse, B, causal, ws=None, stream=None):
+    """dash_attend_prefill that also writes the log-sum-exp lse [b,h_q,n] (fp32)."""
+    b, h_q, n, d = Q.shape
+    h_kv = K.shape[1]
+    if ws is None and Q.dtype == torch.bfloat16:
+        ws = alloc_prefill_ws(b, h_q, h_kv, n, d, B, device=Q.device)
+    _check(lib.dash_attend_prefill_lse(_ptr(Q), _ptr(K), _ptr(V), _dtype(Q), _ptr(idx), _ptr(bias),
+                                       _ptr(cnt), idx.shape[-1], _ptr(O), _dtype(O), _ptr(lse), b, h_q,
+                                       h_kv, n, d, B, int(causal), _ptr(ws),
+                                       0 if ws is None else ws.numel() * ws.element_size(),
+                                       _stream(stream)))
+
+
+def dash_attend_prefill_backward(Q, K, V, idx, bias, cnt, O, dO, lse, dQ, dK, dV, dbias, B, causal,
+                                 ws=None, stream=None):
+    """Stage-2 gradients dQ [b,h_q,n,d], dK/dV [b,h_kv,n,d] and dbias [b,h_kv,n,cap] (fp32).
+
+    A workspace (alloc_backward_ws) is allocated when ws is None."""
+    b, h_q, n, d = Q.shape
+    h_kv = K.shape[1]
+    if ws is None:
+        ws = alloc_backward_ws(b, h_q, h_kv, n, d, B, device=Q.device)
+    if O.dtype != dO.dtype:
+        raise TypeError("O and dO must share a dtype")
+    _check(lib.dash_attend_prefill_backward(_ptr(Q), _ptr(K), _ptr(V), _dtype(Q), _ptr(idx), _ptr(bias),
+                                            _ptr(cnt), idx.shape[-1], _ptr(O), _ptr(dO), _dtype(O), _ptr(lse),
+                                            _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(dbias), b, h_q, h_kv, n, d, B,
+                                            int(causal), _ptr(ws),
+                                            0 if ws is None else ws.numel() * ws.element_size(),
+                                            _stream(stream)))
+
+
 def dash_attend_decode(Q, Kc, Vc, kbar, seq_len, B, alpha, gamma, sigma, O, ws,
                        idx_out=None, bias_out=None, cnt_out=None, w_out=None, stream=None):
     """One decode step: Q [b,h_q,1,d] against the KV cache Kc/Vc [b,h_kv,L_cap,d]."""
@@ -219,6 +259,11 @@ def alloc_route_ws(b, h_q, h_kv, n, d, B, device="cuda"):
 
 def alloc_prefill_ws(b, h_q, h_kv, n, d, B, device="cuda"):
     nbytes = dash_workspace_bytes(DASH_OP_PREFILL, b, h_q, h_kv, n, d, B)
+    return torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=device)
+
+
+def alloc_backward_ws(b, h_q, h_kv, n, d, B, device="cuda"):
+    nbytes = dash_workspace_bytes(DASH_OP_PREFILL_BWD, b, h_q, h_kv, n, d, B)
     return torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=device)
 
 

@@ -128,6 +128,12 @@ def make_prefill(b=1, h_q=1, h_kv=1, d=64, n=1024, B=64, alphas=(1.5,), gamma=1.
                             float(gamma), float(sigma), bool(causal), Q, K, V, qbar))
 
 
+def upstream_grad(shape, seed=0, dtype="f32") -> np.ndarray:
+    """N(0,1) upstream gradient dO of a given shape (rounded to bf16 for dtype bf16)."""
+    g = np.random.default_rng(seed).standard_normal(shape, dtype=np.float32)
+    return round_bf16(g) if dtype == "bf16" else g
+
+
 def make_decode(b=2, h_q=4, h_kv=2, d=64, L=1024, B=64, alphas=(1.5,), gamma=1.0,
                 sigma=1.0, dtype="bf16", seed=0, name="decode_custom",
                 seq_len=None) -> Workload:

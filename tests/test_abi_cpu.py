@@ -207,3 +207,49 @@ def test_workspace_sizes(dash):
     assert big > small > 0
     assert dash.dash_workspace_bytes(9, 1, 1, 1, 1, 64, 64) == 2 ** 64 - 1
     assert dash.dash_workspace_bytes(0, 1, 3, 2, 1, 64, 64) == 2 ** 64 - 1
+
+
+def _backward(dash, ws_bytes=None, **kw):
+    a = dict(Q=P, K=P, V=P, dt=1, idx=P, bias=P, cnt=P, cap=4, O=P, dO=P, odt=1, lse=P, dQ=P, dK=P,
+             dV=P, dbias=P, b=1, h_q=16, h_kv=2, n=256, d=128, B=64, causal=1, ws=P)
+    a.update(kw)
+    if ws_bytes is None:
+        ws_bytes = dash.dash_workspace_bytes(dash.DASH_OP_PREFILL_BWD, a["b"], a["h_q"], a["h_kv"], a["n"],
+                                             a["d"], a["B"])
+    return dash.lib.dash_attend_prefill_backward(
+        a["Q"], a["K"], a["V"], a["dt"], a["idx"], a["bias"], a["cnt"], a["cap"], a["O"], a["dO"],
+        a["odt"], a["lse"], a["dQ"], a["dK"], a["dV"], a["dbias"], a["b"], a["h_q"], a["h_kv"], a["n"],
+        a["d"], a["B"], a["causal"], a["ws"], ws_bytes, NUL)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(lse=NUL), 1), (dict(dO=NUL), 1), (dict(dbias=NUL), 1), (dict(dK=NUL), 1),
+    (dict(odt=2), 3), (dict(causal=2), 3), (dict(cap=3), 2), (dict(h_q=15), 2),
+    (dict(dt=0), 4),                        # fp32 Q/K/V
+    (dict(B=32, cap=8), 4),                 # B % 64 != 0
+    (dict(h_q=8), 4),                       # g = 4
+    (dict(h_q=64), 4),                      # g = 32
+    (dict(ws=NUL), 5),
+])
+def test_backward_validation(dash, kw, status):
+    assert _backward(dash, **kw) == status
+
+
+def test_backward_workspace(dash):
+    need = dash.dash_workspace_bytes(dash.DASH_OP_PREFILL_BWD, 1, 16, 2, 256, 128, 64)
+    assert _backward(dash, ws_bytes=need - 1) == dash.DASH_ERR_WORKSPACE
+    up = lambda x: (x + 255) // 256 * 256
+    b, hq, hkv, n, d, B = 1, 16, 2, 256, 128, 64
+    T, nblk = n // B, (n + 63) // 64
+    expect = (up(hkv * d * 256 * 2) + 3 * up(hq * n * d * 2) + up(hq * n * 4) + up(hkv * T * nblk * 4)
+              + up(hkv * (T + 1) * 4) + 2 * up(hkv * n * T * 4))
+    assert need == expect
+    # n * floor(n/B) must stay below 2^31 (inverted list offsets are int32)
+    assert _backward(dash, n=1 << 20, B=64, cap=1 << 14, ws_bytes=1 << 62) == dash.DASH_ERR_UNSUPPORTED
+
+
+def test_prefill_lse_validation(dash):
+    args = (P, P, P, 1, P, P, P, 4, P, 0, P, 1, 4, 2, 256, 128, 64, 1)
+    assert dash.lib.dash_attend_prefill_lse(*args, NUL, 0, NUL) == dash.DASH_ERR_WORKSPACE
+    args = (P, P, P, 1, P, P, P, 3, P, 0, NUL, 1, 4, 2, 256, 128, 64, 1)
+    assert dash.lib.dash_attend_prefill_lse(*args, P, 1 << 30, NUL) == dash.DASH_ERR_SHAPE

@@ -1,0 +1,209 @@
+"""GPU parity of the Stage-2 backward (dash_attend_prefill_lse and
+dash_attend_prefill_backward through the C ABI) against the oracle's attend_backward.
+
+The routed lists come from the oracle's routing of the same inputs, so the check
+isolates Stage 2: the GPU runs its forward (for O and lse) and its backward on those
+lists, the oracle differentiates the same fixed-support attention in float64.
+
+Tolerances (bf16 Q, K, V; the MFMA operands P and dZ are rounded to bf16, each
+product term then carries a relative error up to u = 2^-9; dO goes through bf16 too):
+  * lse: max |Δ| <= 4e-3 (the forward's denominator sums bf16-rounded P);
+  * dQ, dK, dV and the routed entries of dbias, each as a whole: relative L2 error
+    ||Δ|| / ||ref|| <= 2u (rounding errors of independent terms add in quadrature,
+    so the observed ratio sits near 1.2u);
+  * per row (dQ per (head, row), dK and dV per (KV head, token), dbias per entry):
+    max |Δ| <= 5e-2 * (rms of that row + rms of the whole tensor), the largest of up
+    to ~10^6 values each near u relative to the magnitudes that meet in its sum,
+    with the tensor's rms as the floor for rows whose sum cancels;
+  * list entries at or past cnt are exactly zero.
+With a bf16 O, Δ = <o_i, do_i> also carries O's rounding, up to 2^-9 sum_d |o_d do_d|,
+which dominates rows whose true gradient nearly cancels; the full-size case therefore
+takes O in fp32, and a small case covers bf16 O and dO.
+"""
+import numpy as np
+import pytest
+import torch
+
+from long_context_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL_LSE = 4e-3
+TOL_ROW = 5e-2
+TOL_L2 = 2.0 ** -8
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu(gpu_lib):
+    yield
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+def lists_from_support(support, bias_dense, cap):
+    b, hkv, n, T = support.shape
+    idx = np.zeros((b, hkv, n, cap), np.int32)
+    bias = np.zeros((b, hkv, n, cap), np.float32)
+    cnt = np.zeros((b, hkv, n), np.int32)
+    for bi in range(b):
+        for r in range(hkv):
+            for i in range(n):
+                c = np.nonzero(support[bi, r, i])[0]
+                idx[bi, r, i, :c.size] = c
+                bias[bi, r, i, :c.size] = bias_dense[bi, r, i, c]
+                cnt[bi, r, i] = c.size
+    return idx, bias, cnt
+
+
+def run_backward(w, causal, gamma, odt, seed=7, alpha=1.5, sigma=1.0):
+    from long_context_amd import dash
+    from oracle import dash_oracle as O
+    b, hq, n, d = w.Q.shape
+    hkv, B = w.h_kv, w.B
+    T = n // B
+    cap = max(T, 1)
+    pos = np.broadcast_to(np.arange(n), (b, n))
+    kb = O.stage0_summaries(w.K, w.qbar, B)
+    rt = O.route(w.Q, pos, kb, B, alpha, gamma, sigma, causal, n)
+    bias32 = rt["bias"].astype(np.float32)
+    idx, bias, cnt = lists_from_support(rt["support"], bias32, cap)
+    rt = dict(rt, bias=bias32.astype(np.float64))
+    dO = inputs.upstream_grad((b, hq, n, d), seed=seed, dtype=odt)
+    tdt = torch.bfloat16 if odt == "bf16" else torch.float32
+    dev = lambda x, dt: torch.from_numpy(np.ascontiguousarray(x)).to("cuda", dt)
+    Qd, Kd, Vd = (dev(x, torch.bfloat16) for x in (w.Q, w.K, w.V))
+    ti, tb, tc = dev(idx, torch.int32), dev(bias, torch.float32), dev(cnt, torch.int32)
+    Og = torch.empty((b, hq, n, d), dtype=tdt, device="cuda")
+    lse = torch.full((b, hq, n), float("nan"), device="cuda")
+    dash.dash_attend_prefill_lse(Qd, Kd, Vd, ti, tb, tc, Og, lse, B, causal)
+    dQ = torch.full((b, hq, n, d), float("nan"), device="cuda")
+    dK = torch.full((b, hkv, n, d), float("nan"), device="cuda")
+    dV = torch.full((b, hkv, n, d), float("nan"), device="cuda")
+    db = torch.full((b, hkv, n, cap), float("nan"), device="cuda")
+    dash.dash_attend_prefill_backward(Qd, Kd, Vd, ti, tb, tc, Og, dev(dO, tdt), lse, dQ, dK, dV, db, B, causal)
+    torch.cuda.synchronize()
+    ref = O.attend_backward(w.Q, pos, w.K, w.V, rt, B, causal, n, dO.astype(np.float64))
+    got = dict(lse=lse.cpu().numpy(), dQ=dQ.cpu().numpy(), dK=dK.cpu().numpy(), dV=dV.cpu().numpy(),
+               dbias=db.cpu().numpy())
+    return got, ref, idx, cnt
+
+
+def check_grads(got, ref, idx, cnt, tag=""):
+    dl = np.abs(got["lse"] - ref["lse"]).max()
+    row, l2 = {}, {}
+    for name in ("dQ", "dK", "dV"):
+        g, r = got[name], ref[name]
+        assert np.isfinite(g).all(), f"{name}: non-finite values"
+        rms_all = np.sqrt((r ** 2).mean())
+        rms_row = np.sqrt((r ** 2).mean(-1))
+        e = np.abs(g - r).max(-1) / (rms_all + rms_row)
+        row[name] = e.max()
+        if e.max() > TOL_ROW:
+            _log(f"{name}: worst row at {np.unravel_index(e.argmax(), e.shape)}")
+        l2[name] = np.linalg.norm(g - r) / max(np.linalg.norm(r), 1e-30)
+    # dbias: the oracle's dense [.., T] gradient gathered at the list positions
+    e = np.arange(idx.shape[-1])
+    live = e[None, None, None, :] < cnt[..., None]
+    if ref["dbias"].shape[-1]:
+        rd = np.take_along_axis(ref["dbias"], np.where(live, idx, 0).astype(np.int64), axis=-1)
+    else:
+        rd = np.zeros(idx.shape)
+    rd = np.where(live, rd, 0.0)
+    gd = got["dbias"]
+    assert np.all(gd[~live] == 0.0), "dbias past cnt must be zero"
+    if live.any():
+        rms = np.sqrt((rd[live] ** 2).mean())
+        row["dbias"] = (np.abs(gd - rd)[live] / (rms + np.abs(rd[live]))).max()
+        l2["dbias"] = np.linalg.norm((gd - rd)[live]) / max(np.linalg.norm(rd[live]), 1e-30)
+    _log(f"{tag} lse={dl:.2e} " + " ".join(f"{k}: row {row[k]:.2e} l2 {l2[k]:.2e}" for k in row))
+    assert dl <= TOL_LSE, f"lse differs by {dl}"
+    for name in row:
+        assert row[name] <= TOL_ROW, f"{name}: per-row error {row[name]}"
+        assert l2[name] <= TOL_L2, f"{name}: relative L2 error {l2[name]}"
+
+
+BWD = [
+    # b, h_q, h_kv, d, n, B, causal, gamma, O/dO dtype
+    (1, 16, 2, 128, 300, 64, True, 6.0, "f32"),      # GQA 8, ragged tail
+    (2, 32, 2, 64, 520, 64, False, 6.0, "f32"),      # GQA 16, d 64, non-causal tail
+    (1, 16, 2, 128, 400, 128, True, 4.0, "bf16"),    # B 128: two token tiles per chunk
+    (1, 32, 2, 128, 1100, 64, False, 8.0, "f32"),    # tail seen by every row: three segments
+    (1, 16, 2, 128, 2048, 64, True, 3.0, "f32"),     # many chunks, dense early routing
+]
+
+
+@pytest.mark.parametrize("case", BWD, ids=[f"g{c[1] // c[2]}-d{c[3]}-n{c[4]}-B{c[5]}-c{int(c[6])}-{c[8]}" for c in BWD])
+def test_backward_matches_oracle(case):
+    b, hq, hkv, d, n, B, causal, gamma, odt = case
+    _log(f"backward case {case}")
+    w = inputs.make_prefill(b=b, h_q=hq, h_kv=hkv, d=d, n=n, B=B, dtype="bf16", gamma=gamma, seed=3)
+    got, ref, idx, cnt = run_backward(w, causal, gamma, odt)
+    check_grads(got, ref, idx, cnt, tag=str(case))
+
+
+def test_backward_short_sequence_no_full_chunk():
+    """n < B: no routed chunk at all, only the diagonal (causal) branch."""
+    w = inputs.make_prefill(b=1, h_q=8, h_kv=1, d=64, n=50, B=64, dtype="bf16", seed=4)
+    got, ref, idx, cnt = run_backward(w, True, 1.0, "f32")
+    check_grads(got, ref, idx, cnt, tag="n50")
+
+
+def test_backward_32k_clusters_full_size():
+    """The 32K GQA-16 clustered workload at full size (α = 1.5, the benchmark's
+    launch). Rows of the last two chunks and a sample of other rows take the oracle's
+    routed lists (the rest keep the GPU router's); the oracle then fixes lse, dQ and
+    dbias of those rows, and dK, dV of the last two chunks' tokens exactly (only rows
+    in those chunks can see them). Over the whole tensors, sum_j dV_j equals the sum
+    of dO over the group's rows and heads, since every row's P sums to one."""
+    from long_context_amd import dash
+    from oracle import dash_oracle as O
+    w = inputs.prefill_32k_clusters(alphas=(1.5,))
+    b, hq, n, d = w.Q.shape
+    hkv, B, g = w.h_kv, w.B, hq // w.h_kv
+    T = n // B
+    rng = np.random.default_rng(21)
+    rows = np.unique(np.concatenate([rng.choice(n - 2 * B, size=24, replace=False), np.arange(n - 2 * B, n),
+                                     [0, 1, B, 2 * B - 1, n // 2]]))
+    _log(f"32k backward: {rows.size} oracle rows")
+    dev = lambda x, dt: torch.from_numpy(np.ascontiguousarray(x)).to("cuda", dt)
+    Qd, Kd, Vd = (dev(x, torch.bfloat16) for x in (w.Q, w.K, w.V))
+    kbar = dash.alloc_kbar(b, hkv, T, d)
+    dash.dash_summarize(Kd, torch.from_numpy(w.qbar).cuda(), kbar, B)
+    idx, bias, cnt, _ = dash.alloc_route(b, hkv, n, T, with_w=False)
+    dash.dash_route(Qd, kbar, B, 1.5, w.gamma, w.sigma, True, idx, bias, cnt)
+    pos = np.broadcast_to(rows, (b, rows.size))
+    kb = O.stage0_summaries(w.K, w.qbar, B)
+    rt = O.route(w.Q[:, :, rows], pos, kb, B, 1.5, w.gamma, w.sigma, True, n)
+    bias32 = rt["bias"].astype(np.float32)
+    li, lb, lc = lists_from_support(rt["support"], bias32, T)
+    ri = torch.from_numpy(rows).cuda()
+    idx[:, :, ri] = dev(li, torch.int32)
+    bias[:, :, ri] = dev(lb, torch.float32)
+    cnt[:, :, ri] = dev(lc, torch.int32)
+    rt = dict(rt, bias=bias32.astype(np.float64))
+    dO = inputs.upstream_grad((b, hq, n, d), seed=22, dtype="bf16")
+    dOd = dev(dO, torch.bfloat16)
+    # fp32 O: Δ = <o_i, do_i> then carries no bf16 rounding of O, which would add up
+    # to 2^-9 sum_d |o_d do_d| to Δ and dominate rows whose gradient cancels (row 1)
+    Og = torch.empty((b, hq, n, d), dtype=torch.float32, device="cuda")
+    lse = torch.empty((b, hq, n), device="cuda")
+    dash.dash_attend_prefill_lse(Qd, Kd, Vd, idx, bias, cnt, Og, lse, B, True)
+    dQ = torch.empty((b, hq, n, d), device="cuda")
+    dK = torch.empty((b, hkv, n, d), device="cuda")
+    dV = torch.empty((b, hkv, n, d), device="cuda")
+    db = torch.empty((b, hkv, n, T), device="cuda")
+    dash.dash_attend_prefill_backward(Qd, Kd, Vd, idx, bias, cnt, Og, dOd.float(), lse, dQ, dK, dV, db, B, True)
+    torch.cuda.synchronize()
+    # Σ_j dV_j = Σ_{h in group, i} dO_{h,i}; each row's P sums to one within its rounding
+    sv = dV.double().sum(2)
+    so = dOd.double().reshape(b, hkv, g, n, d).sum((2, 3))
+    bound = 2.0 ** -8 * dOd.double().abs().reshape(b, hkv, g, n, d).sum((2, 3))
+    assert torch.all((sv - so).abs() <= bound), float(((sv - so).abs() / bound).max())
+    ref = O.attend_backward(w.Q[:, :, rows], pos, w.K, w.V, rt, B, True, n, dO[:, :, rows].astype(np.float64))
+    tail = slice(n - 2 * B, n)
+    got = dict(lse=lse[:, :, ri].cpu().numpy(), dQ=dQ[:, :, ri].cpu().numpy(),
+               dK=dK[:, :, tail].cpu().numpy(), dV=dV[:, :, tail].cpu().numpy(), dbias=db[:, :, ri].cpu().numpy())
+    ref = dict(ref, dK=ref["dK"][:, :, tail], dV=ref["dV"][:, :, tail])
+    check_grads(got, ref, li, lc, tag="32k")
