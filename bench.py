@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--only", choices=["prefill", "decode", "both"], default="both")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (HBM counter calibration)")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the Stage-2 backward at the 32K workload instead of the forward")
     ap.add_argument("--efficiency", action="store_true",
                     help="only run the replicas of the pages' efficiency operating points")
     return ap.parse_args()
@@ -358,6 +360,54 @@ def efficiency(torch, dash, inputs, steps):
     return rows
 
 
+def backward(torch, dash, inputs, alpha, steps, warmup, no_dense=False):
+    """Stage-2 backward at the 32K workload: the routed lists of the forward at α, the
+    forward's O and lse, an N(0,1) upstream gradient; the whole backward call timed
+    (Δ and transposes, list inversion, dQ/d(bias) kernel, dK/dV kernel). The same
+    kernels on the dense lists (every visible chunk, bias 0) give the 0%-sparsity
+    baseline. Algorithmic flops: the five products of a softmax-attention backward
+    (S, dP, dQ, dK, dV) over the pairs each row sees, 2.5x the forward's."""
+    wp = inputs.prefill_32k_clusters()
+    pre = Prefill(wp, torch, dash)
+    pre.run(alpha)
+    torch.cuda.synchronize()
+    st = pre.stats()
+    b, h_q, n, d = wp.Q.shape
+    B, hkv = wp.B, wp.h_kv
+    lse = torch.empty((b, h_q, n), device="cuda")
+    dO = torch.from_numpy(inputs.upstream_grad((b, h_q, n, d), seed=1, dtype="bf16")).to("cuda", torch.bfloat16)
+    dQ = torch.empty((b, h_q, n, d), device="cuda")
+    dK = torch.empty((b, hkv, n, d), device="cuda")
+    dV = torch.empty((b, hkv, n, d), device="cuda")
+    ws = dash.alloc_backward_ws(b, h_q, hkv, n, d, B)
+
+    def timed(idx, bias, cnt):
+        db = torch.empty(idx.shape, device="cuda")
+        dash.dash_attend_prefill_lse(pre.Q, pre.K, pre.V, idx, bias, cnt, pre.O, lse, B, True, ws=pre.ws)
+
+        def fn(ev):
+            if ev: ev[0].record()
+            dash.dash_attend_prefill_backward(pre.Q, pre.K, pre.V, idx, bias, cnt, pre.O, dO, lse,
+                                              dQ, dK, dV, db, B, True, ws=ws)
+            if ev: ev[1].record()
+        seg, _ = time_events(torch, fn, 2, steps, warmup)
+        return float(seg[:, 0].mean())
+
+    t = timed(pre.idx, pre.bias, pre.cnt)
+    flops = 2.5 * st["flops_row"]
+    out = dict(ms=t, tflops=flops / (t * 1e-3) / 1e12, frac=flops / (t * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+               sparsity=st["sparsity"], algorithmic_tflop=flops / 1e12)
+    print(f"[bench] backward alpha={alpha}: {out}", file=sys.stderr, flush=True)
+    if no_dense:
+        return out
+    di, dbias, dc = dense_lists(pre, torch)
+    td = timed(di, dbias, dc)
+    dense_flops = 2.5 * 4.0 * d * h_q * (n * (n + 1) / 2)
+    out["dense"] = dict(ms=td, tflops=dense_flops / (td * 1e-3) / 1e12)
+    out["speedup_vs_dense"] = td / t
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -372,6 +422,15 @@ def main():
         rows = efficiency(torch, dash, inputs, max(args.steps // 2, 3))
         print(json.dumps({"metric": "DashAttention speedup over dense at the efficiency operating points",
                           "n_gpus": 1, "data": "synthetic", "dtype": "bf16", "efficiency": rows}), flush=True)
+        return
+
+    if args.backward:
+        res = backward(torch, dash, inputs, args.alpha, args.steps, args.warmup, args.no_dense)
+        print(json.dumps({"metric": "Stage-2 backward time at the 32K prefill workload", "unit": "ms",
+                          "value": res["ms"], "higher_is_better": False, "n_gpus": 1, "steps": args.steps,
+                          "warmup": args.warmup, "dtype": "bf16", "data": "synthetic",
+                          "config": {"workload": "prefill_32k_clusters", "alpha": args.alpha},
+                          "backward": res}), flush=True)
         return
 
     out = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,

@@ -9,9 +9,7 @@
 // chunk's tokens and the query heads of the row's KV group (they share one list).
 //
 // Kernels, in launch order:
-//   bwd_prep_kernel        Δ per (row, head); Q and dO transposed per KV group to
-//                          [d][row][head], the operands of dK and dV whose
-//                          contraction runs over (row, head) pairs; dO as bf16.
+//   bwd_prep_kernel        Δ per (row, head); dO as bf16 when it comes in fp32.
 //   inv_*_kernel           the routed lists inverted into per-chunk row lists, rows
 //                          ascending (a stable counting sort over 64-row blocks).
 //   prior_attn_dq_kernel   query-major like the forward: a query tile walks the
@@ -20,8 +18,10 @@
 //                          registers and writes each routed chunk's bias gradient.
 //   prior_attn_dkv_kernel  key-major: a workgroup holds K and V of 64 tokens of one
 //                          chunk in registers, streams the (row, head) pairs that
-//                          see them (a segment of the chunk's row list, then its
-//                          diagonal rows) and keeps dK and dV in registers.
+//                          see them (a segment of the chunk's row list and its
+//                          diagonal rows) and keeps dK and dV in registers; the
+//                          pair-contiguous operands of dK and dV come from
+//                          transposing LDS reads of the row-major Q and dO tiles.
 // dQ and the bias gradients have one writer each. dK and dV add the partials of
 // the segments of a chunk and of the two pair halves of a workgroup onto zeros
 // with atomic adds.
@@ -39,20 +39,16 @@ namespace dash {
 // ---------------------------------------------------------------------------------
 
 struct BwdPrepParams {
-    const uint16_t* Q; const void* O; const void* dO;
-    uint16_t* Qt; uint16_t* dOt;     // [b*h_kv][D][n*g], pair index row*g + head
+    const void* O; const void* dO;
     uint16_t* dOb;                   // nullable: bf16 copy of an fp32 dO
     float* delta;                    // [b, h_q, n]
     int h_q, h_kv, n, g, log2g;
 };
 
-// One workgroup per 64 consecutive (row, head) pairs of a KV group (g >= 8, so a
-// 16-byte piece of 8 pairs never spans two rows).
+// One workgroup per 64 consecutive (row, head) pairs of a KV group.
 template <int D, typename OT>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdPrepParams p) {
     constexpr int PR = D / 8;                    // 16-byte pieces per row
-    __shared__ __attribute__((aligned(16))) uint16_t qs[64][D + 8];
-    __shared__ __attribute__((aligned(16))) uint16_t ds[64][D + 8];
     const int tid = threadIdx.x;
     const int hk = blockIdx.y, bi = blockIdx.z;
     const size_t P0 = (size_t)blockIdx.x * 64;
@@ -63,10 +59,9 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdPrepParams p) {
         const int row = (int)(pair >> p.log2g), head = (int)(pair & (p.g - 1));
         const bool ok = pair < npairs;
         const size_t off = (((size_t)bi * p.h_q + (size_t)hk * p.g + head) * p.n + (ok ? row : 0)) * D + 8 * c;
-        u32x4 qv = {0u, 0u, 0u, 0u}, dv = {0u, 0u, 0u, 0u};
+        u32x4 dv;
         float part = 0.f;
         if (ok) {
-            qv = *reinterpret_cast<const u32x4*>(p.Q + off);
             float o[8], d[8];
             Elem<OT>::load8(static_cast<const OT*>(p.O) + off, o);
             Elem<OT>::load8(static_cast<const OT*>(p.dO) + off, d);
@@ -81,27 +76,10 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdPrepParams p) {
             }
             if (p.dOb) *reinterpret_cast<u32x4*>(p.dOb + off) = dv;
         }
-        *reinterpret_cast<u32x4*>(&qs[t][8 * c]) = qv;
-        *reinterpret_cast<u32x4*>(&ds[t][8 * c]) = dv;
         // the PR pieces of one pair sit in PR consecutive lanes
 #pragma unroll
         for (int m = 1; m < PR; m <<= 1) part += shfl_xor(part, m);
         if (ok && c == 0) p.delta[(((size_t)bi * p.h_q + (size_t)hk * p.g + head) * p.n + row)] = part;
-    }
-    __syncthreads();
-    const size_t bhk = (size_t)bi * p.h_kv + hk;
-    for (int q = tid; q < D * 8; q += 256) {
-        const int d = q / 8, cp = q % 8;
-        if (P0 + 8 * cp >= npairs) continue;
-        u32x4 a, b;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            a[e] = (uint32_t)qs[8 * cp + 2 * e][d] | ((uint32_t)qs[8 * cp + 2 * e + 1][d] << 16);
-            b[e] = (uint32_t)ds[8 * cp + 2 * e][d] | ((uint32_t)ds[8 * cp + 2 * e + 1][d] << 16);
-        }
-        const size_t o = (bhk * D + d) * npairs + P0 + 8 * cp;
-        *reinterpret_cast<u32x4*>(p.Qt + o) = a;
-        *reinterpret_cast<u32x4*>(p.dOt + o) = b;
     }
 }
 
@@ -471,7 +449,6 @@ __global__ __launch_bounds__(64 * NW) void prior_attn_dq_kernel(PrefillParams p,
 
 struct DkvParams {
     const uint16_t* Q; const uint16_t* dO;       // bf16 [b, h_q, n, D]
-    const uint16_t* Qt; const uint16_t* dOt;     // bf16 [b*h_kv][D][n*g]
     const uint16_t* K; const uint16_t* V;        // bf16 [b, h_kv, n, D]
     const float* lse; const float* delta;        // [b, h_q, n]
     const int32_t* inv_row; const float* inv_bias; const int32_t* coff;
@@ -480,27 +457,50 @@ struct DkvParams {
     float c1, scale;                             // log2(e)/sqrt(d), 1/sqrt(d)
 };
 
-// A stage: Q and dO of 64 pairs ("K" form [64][D]), then Q^T and dO^T ("V^T" form
-// [D][64]); the pair index of a group is row_slot * g + head.
+// A stage: Q and dO of a group of 64 (row, head) pairs, both row-major [64][D] with
+// the "K" swizzle; pair index = row_slot * g + head.
 template <int D>
 struct DkvStage {
     typedef BfTiles<D, 64> S;
-    static constexpr int BYTES = 2 * S::KBYTES + 2 * S::VBYTES;
-    static constexpr int NI = 2 * S::KINSTS + 2 * S::VINSTS;    // wavefront copies
+    static constexpr int BYTES = 2 * S::KBYTES;
+    static constexpr int NI = 2 * S::KINSTS;                     // wavefront copies
+    static constexpr int NST = 3;                                // ring stages
 };
 
-// Row of the chunk's row sequence j: the routed rows (inverted list), then the
-// diagonal rows dlo, dlo+1, ...
+// The chunk's row sequence: the routed rows (inverted list, ascending), then the
+// diagonal rows dlo, dlo+1, ...; a workgroup walks its segment [j0, j1) from the
+// end, so the workgroups running at one time start on the same late rows.
 struct RowSeq {
     const int32_t* irow; const float* ibias;
-    int nrouted, dlo, j1;
-    __device__ __forceinline__ void get(int j, int& row, float& bias, bool& valid, bool& routed) const {
-        valid = j < j1;
+    int nrouted, dlo, j0, j1;
+    // the m-th row of the walk
+    __device__ __forceinline__ void get(int m, int& row, float& bias, bool& valid, bool& routed) const {
+        const int j = j1 - 1 - m;
+        valid = j >= j0;
         routed = valid && j < nrouted;
         row = routed ? irow[j] : (valid ? dlo + (j - nrouted) : 0);
         bias = routed ? ibias[j] : 0.f;
     }
 };
+
+struct RowId { int row; float bias; bool valid, routed; };
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef i16x4 __attribute__((address_space(3))) lds_i16x4;
+
+// ds_read_b64_tr_b16: within each 16-lane group, lane i receives as element k the
+// 16-bit element i % 4 of the 8 bytes that lane 4k + i/4 of the group addressed.
+__device__ __forceinline__ i16x4 lds_read_tr16(const char* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
+}
+
+// Wait until at most N vector memory operations of this wavefront are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt immediate");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 template <int D>
 __global__ __launch_bounds__(256) void prior_attn_dkv_kernel(DkvParams p) {
@@ -509,11 +509,11 @@ __global__ __launch_bounds__(256) void prior_attn_dkv_kernel(DkvParams p) {
     constexpr int NS = D / 16, ND = D / 32;
     constexpr int CPW = ST::NI / 4;
     extern __shared__ __attribute__((aligned(16))) char smem[];
-    char* ring = smem;
-    float* t_off = reinterpret_cast<float*>(smem + 2 * ST::BYTES);    // [2][64] bias2 - lse2
+    char* ring = smem;                                                  // NST stages
+    float* t_off = reinterpret_cast<float*>(smem + ST::NST * ST::BYTES);  // [2][64] bias2 - lse2
     int* t_lim = reinterpret_cast<int*>(t_off + 128);                  // [2][64] last visible token
     float* t_dlt = reinterpret_cast<float*>(t_lim + 128);              // [2][64] Δ
-    int* t_row = reinterpret_cast<int*>(t_dlt + 128);                  // [2][8] rows of a group
+    int* t_row = reinterpret_cast<int*>(t_dlt + 128);                  // [4][64] rows of a group
 
     const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
     const int l32 = lane & 31, hl = lane >> 5;
@@ -532,14 +532,15 @@ __global__ __launch_bounds__(256) void prior_attn_dkv_kernel(DkvParams p) {
     if (p.causal) { dlo = t0; dhi = min(c * p.B + p.B, p.n); }
     else if (c == T) { dlo = 0; dhi = p.n; }
     const int nrows = nrouted + max(dhi - dlo, 0);
-    const int j0 = seg * p.seg_rows, j1 = min(nrows, j0 + p.seg_rows);
-    if (j0 >= j1) return;
+    // segment 0 holds the end of the sequence
+    const int j1 = nrows - seg * p.seg_rows, j0 = max(j1 - p.seg_rows, 0);
+    if (j1 <= 0) return;
     const int g = p.g, lg = p.log2g, RG = 64 >> lg;
     const int ngroups = (j1 - j0 + RG - 1) / RG;
     RowSeq rs;
     rs.irow = p.inv_row + bhk * (size_t)p.n * T + rbase;
     rs.ibias = p.inv_bias + bhk * (size_t)p.n * T + rbase;
-    rs.nrouted = nrouted; rs.dlo = dlo; rs.j1 = j1;
+    rs.nrouted = nrouted; rs.dlo = dlo; rs.j0 = j0; rs.j1 = j1;
 
     // ---- K and V of the wavefront's 32 tokens as B operands (token = lane column) ----
     const int tbk = wid & 1, half = wid >> 1;
@@ -547,12 +548,10 @@ __global__ __launch_bounds__(256) void prior_attn_dkv_kernel(DkvParams p) {
     bf16x8 kreg[NS], vreg[NS];
     {
         const size_t kb = (bhk * p.n + min(tok, p.n - 1)) * D + 8 * hl;
-        const uint16_t* K = p.K;
-        const uint16_t* V = p.V;
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
-            kreg[s] = *reinterpret_cast<const bf16x8*>(K + kb + 16 * s);
-            vreg[s] = *reinterpret_cast<const bf16x8*>(V + kb + 16 * s);
+            kreg[s] = *reinterpret_cast<const bf16x8*>(p.K + kb + 16 * s);
+            vreg[s] = *reinterpret_cast<const bf16x8*>(p.V + kb + 16 * s);
             if (tok >= p.n) { kreg[s] = bf16x8{}; vreg[s] = bf16x8{}; }
         }
     }
@@ -562,65 +561,57 @@ __global__ __launch_bounds__(256) void prior_attn_dkv_kernel(DkvParams p) {
     const int tp = 16 * wid + (lane & 15);
     const int tslot = tp >> lg, thead = tp & (g - 1);
     const size_t hbase = ((size_t)bi * p.h_q + (size_t)hk * g + thead) * p.n;
-    auto pair_tables = [&](int slot, int row, float bias, bool valid, bool routed, float lse, float dl) {
+    auto ids = [&](int k) {
+        RowId r;
+        rs.get(k * RG + tslot, r.row, r.bias, r.valid, r.routed);
+        return r;
+    };
+    auto pair_tables = [&](int slot, const RowId& r, float lse, float dl) {
         const float l2 = (lse == -INFINITY) ? INFINITY : lse * kLog2e;
-        t_off[slot * 64 + tp] = valid ? bias * kLog2e - l2 : -INFINITY;
-        t_lim[slot * 64 + tp] = !valid ? -1 : routed ? 0x7fffffff : (p.causal ? row : p.n - 1);
-        t_dlt[slot * 64 + tp] = valid ? dl : 0.f;
+        t_off[slot * 64 + tp] = r.valid ? r.bias * kLog2e - l2 : -INFINITY;
+        t_lim[slot * 64 + tp] = !r.valid ? -1 : r.routed ? 0x7fffffff : (p.causal ? r.row : p.n - 1);
+        t_dlt[slot * 64 + tp] = r.valid ? dl : 0.f;
     };
 
-    // ---- copies of a group's stage ----
-    const size_t npairs = (size_t)p.n * g;
+    // ---- copies of a group's stage (rows from t_row) ----
     const uint16_t* Qg = p.Q + ((size_t)bi * p.h_q + (size_t)hk * g) * p.n * D;
     const uint16_t* dOg = p.dO + ((size_t)bi * p.h_q + (size_t)hk * g) * p.n * D;
-    const uint16_t* Qtg = p.Qt + bhk * D * npairs;
-    const uint16_t* dOtg = p.dOt + bhk * D * npairs;
     auto issue = [&](char* stage, const int* rows) {
 #pragma unroll
         for (int i = 0; i < CPW; ++i) {
             const int j = wid + 4 * i;                 // wavefront-uniform
-            const uint16_t* src;
-            int dst;
-            if (j < 2 * S::KINSTS) {
-                const int jj = j % S::KINSTS;
-                const int q = jj * 64 + lane, t = q / S::KPPR, cc = q % S::KPPR;
-                const int row = min(max(rows[t >> lg], 0), p.n - 1);
-                const size_t o = ((size_t)(t & (g - 1)) * p.n + row) * D + S::kslot(t, cc) * 8;
-                src = (j < S::KINSTS ? Qg : dOg) + o;
-                dst = (j < S::KINSTS ? 0 : S::KBYTES) + jj * 1024;
-            } else {
-                const int j2 = j - 2 * S::KINSTS;
-                const int jj = j2 % S::VINSTS;
-                const int q = jj * 64 + lane, d = q / S::VPPR, cc = q % S::VPPR;
-                const int pr = 8 * S::vslot(d, cc);
-                const int row = min(max(rows[pr >> lg], 0), p.n - 1);
-                const size_t o = (size_t)d * npairs + (size_t)row * g + (pr & (g - 1));
-                src = (j2 < S::VINSTS ? Qtg : dOtg) + o;
-                dst = 2 * S::KBYTES + (j2 < S::VINSTS ? 0 : S::VBYTES) + jj * 1024;
-            }
-            __builtin_amdgcn_global_load_lds(src, stage + dst, 16, 0, 0);
+            const int jj = j % S::KINSTS;
+            const int q = jj * 64 + lane, t = q / S::KPPR, cc = q % S::KPPR;
+            const int row = min(max(rows[t >> lg], 0), p.n - 1);
+            const size_t o = ((size_t)(t & (g - 1)) * p.n + row) * D + S::kslot(t, cc) * 8;
+            // source and destination as named pointers: a conditional expression
+            // inside the builtin's argument list loses the kernel's host stub
+            const uint16_t* src = (j < S::KINSTS ? Qg : dOg) + o;
+            char* dst = stage + (j < S::KINSTS ? 0 : S::KBYTES) + jj * 1024;
+            __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
         }
     };
 
-    // ---- prologue: tables of group 0, rows of groups 0 and 1, copies of group 0 ----
-    int nx_row; float nx_bias; bool nx_valid, nx_routed;     // group k+1 (table lanes)
+    // ---- prologue: tables of group 0, rows of groups 0..2, copies of groups 0 and 1 ----
+    RowId qa = ids(1), qb = ids(2);            // table lanes: groups k+1, k+2
     {
-        int row; float bias; bool valid, routed;
-        rs.get(j0 + tslot, row, bias, valid, routed);
-        rs.get(j0 + RG + tslot, nx_row, nx_bias, nx_valid, nx_routed);
+        const RowId r0 = ids(0);
         if (TL) {
-            const float lse = valid ? p.lse[hbase + row] : 0.f;
-            const float dl = valid ? p.delta[hbase + row] : 0.f;
-            pair_tables(0, row, bias, valid, routed, lse, dl);
+            const float lse = r0.valid ? p.lse[hbase + r0.row] : 0.f;
+            const float dl = r0.valid ? p.delta[hbase + r0.row] : 0.f;
+            pair_tables(0, r0, lse, dl);
             if (thead == 0) {
-                t_row[tslot] = row;
-                t_row[8 + tslot] = nx_row;
+                t_row[tslot] = r0.row;
+                t_row[64 + tslot] = qa.row;
+                t_row[128 + tslot] = qb.row;
             }
         }
     }
     __syncthreads();
     issue(ring, t_row);
-    wait_tile_copies();
+    if (ngroups > 1) issue(ring + ST::BYTES, t_row + 64);
+    else wait_vm<0>();
+    if (ngroups > 1) wait_vm<CPW>();
     __syncthreads();
 
     f32x16 dk[ND], dv[ND];
@@ -631,23 +622,28 @@ __global__ __launch_bounds__(256) void prior_attn_dkv_kernel(DkvParams p) {
     // A row l32 presents pair (bits 2 and 3 swapped): accumulator element 8s + e of a
     // lane is then pair 16s + 8hl + e, the k-slot order of the pair contraction
     const int prow_a = 32 * half + ((l32 & ~12) | ((l32 & 4) << 1) | ((l32 & 8) >> 1));
+    // transposing reads of the B operands: lane group G = lane/16 covers columns
+    // 16(G&1) .. +15 of a 32-wide d block and k-slot half hl; its lane 4k + q reads
+    // pair base + k at d offset 4q
+    const int tr_k = (lane & 15) >> 2, tr_d = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
     const float c1 = p.c1;
+    char* st_cur = ring;
+    char* st_nxt = ring + ST::BYTES;
+    char* st_nn = ring + 2 * ST::BYTES;
 
     for (int k = 0; k < ngroups; ++k) {
-        // table lanes: rows of group k+2 and lse / Δ of group k+1
-        int nn_row; float nn_bias; bool nn_valid, nn_routed;
-        rs.get(j0 + (k + 2) * RG + tslot, nn_row, nn_bias, nn_valid, nn_routed);
+        // table lanes: rows of group k+3 and lse / Δ of group k+1
+        const RowId qc = ids(k + 3);
         float lse_n = 0.f, dlt_n = 0.f;
-        if (TL && nx_valid) {
-            lse_n = p.lse[hbase + nx_row];
-            dlt_n = p.delta[hbase + nx_row];
+        if (TL && qa.valid) {
+            lse_n = p.lse[hbase + qa.row];
+            dlt_n = p.delta[hbase + qa.row];
         }
-        if (k + 1 < ngroups) issue(ring + ((k + 1) & 1) * ST::BYTES, t_row + ((k + 1) & 1) * 8);
+        const bool more = k + 2 < ngroups;
+        if (more) issue(st_nn, t_row + ((k + 2) & 3) * 64);
 
-        const char* qt = ring + (k & 1) * ST::BYTES;
+        const char* qt = st_cur;
         const char* dot = qt + S::KBYTES;
-        const char* qtt = qt + 2 * S::KBYTES;
-        const char* dott = qtt + S::VBYTES;
         // S = Q K^T and dP = dO V^T for this wavefront's 32 pairs x 32 tokens
         f32x16 sacc, dpacc;
 #pragma unroll
@@ -655,10 +651,10 @@ __global__ __launch_bounds__(256) void prior_attn_dkv_kernel(DkvParams p) {
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
             const int o = prow_a * S::KROWB + S::kslot(prow_a, 2 * s + hl) * 16;
-            const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qt + o);
-            const bf16x8 da = *reinterpret_cast<const bf16x8*>(dot + o);
-            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kreg[s], sacc, 0, 0, 0);
-            dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vreg[s], dpacc, 0, 0, 0);
+            const bf16x8 qa8 = *reinterpret_cast<const bf16x8*>(qt + o);
+            const bf16x8 da8 = *reinterpret_cast<const bf16x8*>(dot + o);
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa8, kreg[s], sacc, 0, 0, 0);
+            dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da8, vreg[s], dpacc, 0, 0, 0);
         }
         // P and dZ per pair: element 8s + e is pair 32 half + 16 s + 8 hl + e
         const int tb = (k & 1) * 64 + 32 * half + 8 * hl;
@@ -683,33 +679,44 @@ __global__ __launch_bounds__(256) void prior_attn_dkv_kernel(DkvParams p) {
                 za[s][e] = (__bf16)z;
             }
         }
-        // dV += P^T dO and dK += dZ^T Q over the 32 pairs
+        // dV += P^T dO and dK += dZ^T Q over the 32 pairs; B operands by transposing
+        // reads of the row-major tiles
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-            bf16x8 ob[ND], qb[ND];
+            bf16x8 ob[ND], qb8[ND];
 #pragma unroll
             for (int db = 0; db < ND; ++db) {
-                const int d = 32 * db + l32;
-                const int o = d * S::VROWB + S::vslot(d, 4 * half + 2 * s + hl) * 16;
-                ob[db] = *reinterpret_cast<const bf16x8*>(dott + o);
-                qb[db] = *reinterpret_cast<const bf16x8*>(qtt + o);
+                const int d = 32 * db + tr_d;
+                i16x4 x[2], y[2];
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const int pr = 32 * half + 16 * s + 8 * hl + 4 * t + tr_k;
+                    const int o = pr * S::KROWB + S::kslot(pr, d >> 3) * 16 + ((d >> 2) & 1) * 8;
+                    x[t] = lds_read_tr16(dot + o);
+                    y[t] = lds_read_tr16(qt + o);
+                }
+                ob[db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(x[0], x[1], 0, 1, 2, 3, 4, 5, 6, 7));
+                qb8[db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(y[0], y[1], 0, 1, 2, 3, 4, 5, 6, 7));
             }
 #pragma unroll
             for (int db = 0; db < ND; ++db) {
                 dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[s], ob[db], dv[db], 0, 0, 0);
-                dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(za[s], qb[db], dk[db], 0, 0, 0);
+                dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(za[s], qb8[db], dk[db], 0, 0, 0);
             }
         }
 
-        // tables of group k+1 (their slot was last read in step k-1) and rows of
-        // group k+2 (their slot was last read by the copies of step k-1)
+        // tables of group k+1 (slot last read in step k-1) and rows of group k+3
+        // (slot last read by the copies of step k-1)
         if (TL) {
-            pair_tables((k + 1) & 1, nx_row, nx_bias, nx_valid, nx_routed, lse_n, dlt_n);
-            if (thead == 0) t_row[(k & 1) * 8 + tslot] = nn_row;
+            pair_tables((k + 1) & 1, qa, lse_n, dlt_n);
+            if (thead == 0) t_row[((k + 3) & 3) * 64 + tslot] = qc.row;
         }
-        nx_row = nn_row; nx_bias = nn_bias; nx_valid = nn_valid; nx_routed = nn_routed;
-        wait_tile_copies();
+        qa = qb; qb = qc;
+        // the copies of group k+1 have landed; those of group k+2 may stay in flight
+        if (more) wait_vm<CPW>();
+        else wait_vm<0>();
         __syncthreads();
+        char* t = st_cur; st_cur = st_nxt; st_nxt = st_nn; st_nn = t;
     }
 
     // ---- add the partials: element i of lane l is token 8(i/4) + 4hl + i%4 of the
@@ -740,18 +747,18 @@ static size_t dq_lds_bytes(int d, int T_c) {
 }
 static size_t dkv_lds_bytes(int d) {
     const size_t stage = d == 64 ? DkvStage<64>::BYTES : DkvStage<128>::BYTES;
-    return 2 * stage + 3 * 128 * 4 + 16 * 4;
+    return DkvStage<128>::NST * stage + 3 * 128 * 4 + 4 * 64 * 4;
 }
 
 int backward_tile_rows(int g, int B, int T_c, int d) {
-    if ((g != 8 && g != 16) || B % 64 != 0 || (d != 64 && d != 128)) return 0;
+    if (g < 1 || g > 16 || (g & (g - 1)) != 0 || B % 64 != 0 || (d != 64 && d != 128)) return 0;
     if (dq_lds_bytes(d, T_c) > kBwdMaxLds) return 0;
-    return 32 * kDqWaves / g;
+    return std::min(32 * kDqWaves / g, 64);      // a query tile stays inside one chunk
 }
 
 namespace {
 struct BwdLayout {
-    size_t kt, qt, dot, dob, delta, hist, coff, inv_row, inv_bias, total;
+    size_t kt, dob, delta, hist, coff, inv_row, inv_bias, total;
 };
 size_t up256(size_t x) { return (x + 255) / 256 * 256; }
 BwdLayout bwd_layout(int b, int h_q, int h_kv, int n, int d, int B) {
@@ -759,8 +766,6 @@ BwdLayout bwd_layout(int b, int h_q, int h_kv, int n, int d, int B) {
     const size_t T = (size_t)(n / B), nblk = ((size_t)n + 63) / 64;
     size_t o = 0;
     L.kt = o;       o += up256(prefill_workspace_bytes(b, h_kv, n, d));
-    L.qt = o;       o += up256((size_t)b * h_q * n * d * 2);
-    L.dot = o;      o += up256((size_t)b * h_q * n * d * 2);
     L.dob = o;      o += up256((size_t)b * h_q * n * d * 2);
     L.delta = o;    o += up256((size_t)b * h_q * n * 4);
     L.hist = o;     o += up256((size_t)b * h_kv * T * nblk * 4);
@@ -792,8 +797,6 @@ static hipError_t launch_bwd_t(const PrefillBwdArgs& a, const BwdLayout& L, hipS
     const int T = a.n / a.B, n_pad = prefill_n_pad(a.n), nblk = (a.n + 63) / 64;
     const int bh = a.b * a.h_kv;
     uint16_t* kt = reinterpret_cast<uint16_t*>(ws + L.kt);
-    uint16_t* qt = reinterpret_cast<uint16_t*>(ws + L.qt);
-    uint16_t* dot = reinterpret_cast<uint16_t*>(ws + L.dot);
     uint16_t* dob = a.o_bf16 ? nullptr : reinterpret_cast<uint16_t*>(ws + L.dob);
     float* delta = reinterpret_cast<float*>(ws + L.delta);
     const uint16_t* dO16 = a.o_bf16 ? static_cast<const uint16_t*>(a.dO) : dob;
@@ -805,7 +808,7 @@ static hipError_t launch_bwd_t(const PrefillBwdArgs& a, const BwdLayout& L, hipS
     if ((e = launch_transpose_rows(static_cast<const uint16_t*>(a.K), kt, bh, a.n, n_pad, D, s)) != hipSuccess)
         return e;
 
-    BwdPrepParams pp{static_cast<const uint16_t*>(a.Q), a.O, a.dO, qt, dot, dob, delta, a.h_q, a.h_kv, a.n, g, lg};
+    BwdPrepParams pp{a.O, a.dO, dob, delta, a.h_q, a.h_kv, a.n, g, lg};
     const dim3 pgrid((unsigned)(((size_t)a.n * g + 63) / 64), a.h_kv, a.b);
     if (a.o_bf16) hipLaunchKernelGGL((bwd_prep_kernel<D, uint16_t>), pgrid, dim3(256), 0, s, pp);
     else hipLaunchKernelGGL((bwd_prep_kernel<D, float>), pgrid, dim3(256), 0, s, pp);
@@ -847,7 +850,7 @@ static hipError_t launch_bwd_t(const PrefillBwdArgs& a, const BwdLayout& L, hipS
 
     // dK and dV
     DkvParams q;
-    q.Q = static_cast<const uint16_t*>(a.Q); q.dO = dO16; q.Qt = qt; q.dOt = dot;
+    q.Q = static_cast<const uint16_t*>(a.Q); q.dO = dO16;
     q.K = static_cast<const uint16_t*>(a.K); q.V = static_cast<const uint16_t*>(a.V);
     q.lse = a.lse; q.delta = delta;
     q.inv_row = ip.inv_row; q.inv_bias = ip.inv_bias; q.coff = ip.coff;

@@ -65,8 +65,8 @@ struct PrefillBwdArgs {
 hipError_t launch_attend_prefill_backward(const PrefillBwdArgs& a, hipStream_t s);
 // Rows per backward query tile for group size g at T_c chunks (0: unsupported).
 int backward_tile_rows(int g, int B, int T_c, int d);
-// Workspace of the backward: K^T, Q^T and dO^T per KV group, a bf16 dO, Δ and the
-// inverted routed lists (sized for every row routing every visible chunk).
+// Workspace of the backward: K^T per KV head, a bf16 dO, Δ and the inverted routed
+// lists (sized for every row routing every visible chunk).
 size_t backward_workspace_bytes(int b, int h_q, int h_kv, int n, int d, int B);
 // V or K [b*h_kv][n][d] bf16 -> [b*h_kv][d][n_pad] (zero tokens n .. n_pad-1).
 hipError_t launch_transpose_rows(const uint16_t* src, uint16_t* dst, int bh, int n, int n_pad, int d, hipStream_t s);

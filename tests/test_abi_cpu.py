@@ -227,7 +227,6 @@ def _backward(dash, ws_bytes=None, **kw):
     (dict(odt=2), 3), (dict(causal=2), 3), (dict(cap=3), 2), (dict(h_q=15), 2),
     (dict(dt=0), 4),                        # fp32 Q/K/V
     (dict(B=32, cap=8), 4),                 # B % 64 != 0
-    (dict(h_q=8), 4),                       # g = 4
     (dict(h_q=64), 4),                      # g = 32
     (dict(ws=NUL), 5),
 ])
@@ -241,7 +240,7 @@ def test_backward_workspace(dash):
     up = lambda x: (x + 255) // 256 * 256
     b, hq, hkv, n, d, B = 1, 16, 2, 256, 128, 64
     T, nblk = n // B, (n + 63) // 64
-    expect = (up(hkv * d * 256 * 2) + 3 * up(hq * n * d * 2) + up(hq * n * 4) + up(hkv * T * nblk * 4)
+    expect = (up(hkv * d * 256 * 2) + up(hq * n * d * 2) + up(hq * n * 4) + up(hkv * T * nblk * 4)
               + up(hkv * (T + 1) * 4) + 2 * up(hkv * n * T * 4))
     assert need == expect
     # n * floor(n/B) must stay below 2^31 (inverted list offsets are int32)

@@ -131,6 +131,8 @@ BWD = [
     (1, 16, 2, 128, 400, 128, True, 4.0, "bf16"),    # B 128: two token tiles per chunk
     (1, 32, 2, 128, 1100, 64, False, 8.0, "f32"),    # tail seen by every row: three segments
     (1, 16, 2, 128, 2048, 64, True, 3.0, "f32"),     # many chunks, dense early routing
+    (1, 4, 4, 64, 300, 64, True, 6.0, "f32"),        # g = 1 (one head per list)
+    (2, 8, 2, 128, 333, 64, True, 5.0, "bf16"),      # g = 4
 ]
 
 
