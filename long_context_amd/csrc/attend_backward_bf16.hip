@@ -453,9 +453,82 @@ struct DkvParams {
     const float* lse; const float* delta;        // [b, h_q, n]
     const int32_t* inv_row; const float* inv_bias; const int32_t* coff;
     float* dK; float* dV;                        // [b, h_kv, n, D], zero on entry
+    const int4* items;                           // work items (b*h_kv, chunk tile, segment)
+    int32_t* counters;                           // [0] next item, [1] item count
     int h_q, h_kv, n, B, T_c, causal, g, log2g, seg_rows;
     float c1, scale;                             // log2(e)/sqrt(d), 1/sqrt(d)
 };
+
+// Rows of the row sequence of 64-token tile cs of chunk cs / (B/64) of KV group bhk:
+// the routed rows of the chunk, then its diagonal rows at or after the tile (causal;
+// non-causal: every row for the tail tile).
+struct TileRows { int c, t0, rbase, nrouted, dlo, dhi; };
+__device__ __forceinline__ TileRows tile_rows(const int32_t* coff, size_t bhk, int cs, int n, int B, int T,
+                                              int causal) {
+    TileRows r;
+    const int SUB = B / 64;
+    r.c = cs / SUB;
+    r.t0 = r.c * B + 64 * (cs % SUB);
+    r.rbase = 0; r.nrouted = 0; r.dlo = 0; r.dhi = 0;
+    if (r.t0 >= n) return r;
+    if (r.c < T) {
+        r.rbase = coff[bhk * (T + 1) + r.c];
+        r.nrouted = coff[bhk * (T + 1) + r.c + 1] - r.rbase;
+    }
+    if (causal) { r.dlo = r.t0; r.dhi = min(r.c * B + B, n); }
+    else if (r.c == T) { r.dlo = 0; r.dhi = n; }
+    return r;
+}
+
+// Exclusive prefix sum over a 1024-thread workgroup (tmp: 16 ints of LDS).
+__device__ __forceinline__ int block_scan1024(int v, int* tmp, int& total) {
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    int x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __builtin_amdgcn_ds_bpermute(((lane - o) & 63) << 2, x);
+        if (lane >= o) x += y;
+    }
+    if (lane == 63) tmp[wid] = x;
+    __syncthreads();
+    int off = 0;
+    total = 0;
+    for (int w = 0; w < 16; ++w) {
+        off += w < wid ? tmp[w] : 0;
+        total += tmp[w];
+    }
+    __syncthreads();
+    return off + x - v;
+}
+
+// The work items of the dK/dV kernel: every 64-token tile of every chunk (and the
+// tail) with its row sequence cut into segments of seg_rows rows, segment 0 at the
+// end of the sequence; tiles in ascending chunk order (under a causal mask the early
+// chunks have the longest sequences, so the largest items go first). One workgroup.
+__global__ __launch_bounds__(1024) void dkv_items_kernel(const int32_t* coff, int4* items, int32_t* counters,
+                                                         int bh, int n, int B, int T, int causal, int seg_rows) {
+    __shared__ int tmp[16];
+    const int per_bh = (T + 1) * (B / 64);
+    const int E = bh * per_bh;
+    const int per = (E + 1023) / 1024;
+    const int e0 = min((int)threadIdx.x * per, E), e1 = min(e0 + per, E);
+    auto nseg = [&](int e) {
+        const TileRows r = tile_rows(coff, (size_t)(e / per_bh), e % per_bh, n, B, T, causal);
+        if (r.t0 >= n) return 0;
+        const int rows = r.nrouted + max(r.dhi - r.dlo, 0);
+        return (rows + seg_rows - 1) / seg_rows;
+    };
+    int sum = 0;
+    for (int e = e0; e < e1; ++e) sum += nseg(e);
+    int total;
+    int o = block_scan1024(sum, tmp, total);
+    for (int e = e0; e < e1; ++e) {
+        const int k = nseg(e);
+        for (int s = 0; s < k; ++s) items[o + s] = make_int4(e / per_bh, e % per_bh, s, 0);
+        o += k;
+    }
+    if (threadIdx.x == 0) { counters[0] = 0; counters[1] = total; }
+}
 
 // A stage: Q and dO of a group of 64 (row, head) pairs, both row-major [64][D] with
 // the "K" swizzle; pair index = row_slot * g + head.
@@ -469,30 +542,67 @@ struct DkvStage {
 
 // The chunk's row sequence: the routed rows (inverted list, ascending), then the
 // diagonal rows dlo, dlo+1, ...; a workgroup walks its segment [j0, j1) from the
-// end, so the workgroups running at one time start on the same late rows.
+// end, so the workgroups running at one time start on the same late rows. Row m of
+// the walk is entry j = j1 - 1 - m.
 struct RowSeq {
     const int32_t* irow; const float* ibias;
+    const int32_t* safe_i; const float* safe_f;  // readable stand-ins when nothing is routed
     int nrouted, dlo, j0, j1;
-    // the m-th row of the walk
-    __device__ __forceinline__ void get(int m, int& row, float& bias, bool& valid, bool& routed) const {
-        const int j = j1 - 1 - m;
-        valid = j >= j0;
-        routed = valid && j < nrouted;
-        row = routed ? irow[j] : (valid ? dlo + (j - nrouted) : 0);
-        bias = routed ? ibias[j] : 0.f;
+    __device__ __forceinline__ int entry(int m) const { return j1 - 1 - m; }
+    // list slots read for entry j (clamped into the list: always a valid address)
+    __device__ __forceinline__ const int32_t* row_src(int j) const {
+        return nrouted > 0 ? irow + min(max(j, 0), nrouted - 1) : safe_i;
+    }
+    __device__ __forceinline__ const float* bias_src(int j) const {
+        return nrouted > 0 ? ibias + min(max(j, 0), nrouted - 1) : safe_f;
+    }
+    __device__ __forceinline__ bool valid(int j) const { return j >= j0; }
+    __device__ __forceinline__ bool routed(int j) const { return j >= j0 && j < nrouted; }
+    // the row of entry j given the list value loaded for it
+    __device__ __forceinline__ int row(int j, int loaded) const {
+        return routed(j) ? loaded : (valid(j) ? dlo + (j - nrouted) : 0);
     }
 };
 
-struct RowId { int row; float bias; bool valid, routed; };
-
 typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x8 __attribute__((ext_vector_type(8)));
-typedef i16x4 __attribute__((address_space(3))) lds_i16x4;
+
+// LDS byte address of a pointer into shared memory.
+__device__ __forceinline__ uint32_t lds_addr(const char* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
 
 // ds_read_b64_tr_b16: within each 16-lane group, lane i receives as element k the
 // 16-bit element i % 4 of the 8 bytes that lane 4k + i/4 of the group addressed.
-__device__ __forceinline__ i16x4 lds_read_tr16(const char* p) {
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
+// The N reads of one call go out together and are waited for inside the same asm
+// block (the compiler's own form of this read makes it wait for every copy into
+// LDS in flight first, which stalls the copy pipeline).
+template <int N>
+__device__ __forceinline__ void lds_read_tr16(const uint32_t (&a)[N], i16x4 (&r)[N]) {
+    static_assert(N == 8 || N == 16, "8 or 16 reads");
+    if constexpr (N == 16) {
+        asm volatile(
+            "ds_read_b64_tr_b16 %0, %16\n ds_read_b64_tr_b16 %1, %17\n ds_read_b64_tr_b16 %2, %18\n"
+            "ds_read_b64_tr_b16 %3, %19\n ds_read_b64_tr_b16 %4, %20\n ds_read_b64_tr_b16 %5, %21\n"
+            "ds_read_b64_tr_b16 %6, %22\n ds_read_b64_tr_b16 %7, %23\n ds_read_b64_tr_b16 %8, %24\n"
+            "ds_read_b64_tr_b16 %9, %25\n ds_read_b64_tr_b16 %10, %26\n ds_read_b64_tr_b16 %11, %27\n"
+            "ds_read_b64_tr_b16 %12, %28\n ds_read_b64_tr_b16 %13, %29\n ds_read_b64_tr_b16 %14, %30\n"
+            "ds_read_b64_tr_b16 %15, %31\n s_waitcnt lgkmcnt(0)"
+            : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]),
+              "=&v"(r[7]), "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11]), "=&v"(r[12]), "=&v"(r[13]),
+              "=&v"(r[14]), "=&v"(r[15])
+            : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]),
+              "v"(a[8]), "v"(a[9]), "v"(a[10]), "v"(a[11]), "v"(a[12]), "v"(a[13]), "v"(a[14]), "v"(a[15])
+            : "memory");
+    } else {
+        asm volatile(
+            "ds_read_b64_tr_b16 %0, %8\n ds_read_b64_tr_b16 %1, %9\n ds_read_b64_tr_b16 %2, %10\n"
+            "ds_read_b64_tr_b16 %3, %11\n ds_read_b64_tr_b16 %4, %12\n ds_read_b64_tr_b16 %5, %13\n"
+            "ds_read_b64_tr_b16 %6, %14\n ds_read_b64_tr_b16 %7, %15\n s_waitcnt lgkmcnt(0)"
+            : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]),
+              "=&v"(r[7])
+            : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+            : "memory");
+    }
 }
 
 // Wait until at most N vector memory operations of this wavefront are in flight.
@@ -502,35 +612,43 @@ __device__ __forceinline__ void wait_vm() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// Workgroup barrier after this wavefront's LDS writes and reads have completed. Unlike
+// __syncthreads() it does not also wait for the copies into LDS still in flight
+// (their landing is ordered by explicit vmcnt waits).
+__device__ __forceinline__ void barrier_lds() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n s_barrier" ::: "memory");
+}
+
+// LDS of one work item: the tile ring, the tables and the loaded-value rings.
 template <int D>
-__global__ __launch_bounds__(256) void prior_attn_dkv_kernel(DkvParams p) {
+constexpr size_t dkv_item_lds_bytes() {
+    return (size_t)DkvStage<D>::NST * DkvStage<D>::BYTES + 3 * 128 * 4 + (8 + 8 + 4 + 4) * 64 * 4;
+}
+
+// One work item: 64 tokens of one chunk (tile cs) of KV group bhk against segment
+// seg of its row sequence.
+template <int D>
+__device__ __forceinline__ void dkv_item(const DkvParams& p, size_t bhk, int cs, int seg, char* smem) {
     typedef BfTiles<D, 64> S;
     typedef DkvStage<D> ST;
     constexpr int NS = D / 16, ND = D / 32;
     constexpr int CPW = ST::NI / 4;
-    extern __shared__ __attribute__((aligned(16))) char smem[];
     char* ring = smem;                                                  // NST stages
     float* t_off = reinterpret_cast<float*>(smem + ST::NST * ST::BYTES);  // [2][64] bias2 - lse2
     int* t_lim = reinterpret_cast<int*>(t_off + 128);                  // [2][64] last visible token
     float* t_dlt = reinterpret_cast<float*>(t_lim + 128);              // [2][64] Δ
-    int* t_row = reinterpret_cast<int*>(t_dlt + 128);                  // [4][64] rows of a group
+    int* r_row = reinterpret_cast<int*>(t_dlt + 128);                  // [8][64] list rows as loaded
+    float* r_bias = reinterpret_cast<float*>(r_row + 512);             // [8][64] list biases as loaded
+    float* r_lse = r_bias + 512;                                       // [4][64] lse as loaded
+    float* r_dlt = r_lse + 256;                                        // [4][64] Δ as loaded
 
     const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
     const int l32 = lane & 31, hl = lane >> 5;
-    const int seg = blockIdx.x, cs = blockIdx.y;
-    const size_t bhk = blockIdx.z;
     const int bi = (int)(bhk / p.h_kv), hk = (int)(bhk % p.h_kv);
-    const int T = p.T_c, SUB = p.B / 64;
-    const int c = cs / SUB, t0 = c * p.B + 64 * (cs % SUB);
+    const int T = p.T_c;
+    const TileRows tr = tile_rows(p.coff, bhk, cs, p.n, p.B, T, p.causal);
+    const int t0 = tr.t0, rbase = tr.rbase, nrouted = tr.nrouted, dlo = tr.dlo, dhi = tr.dhi;
     if (t0 >= p.n) return;
-    int nrouted = 0, rbase = 0;
-    if (c < T) {
-        rbase = p.coff[bhk * (T + 1) + c];
-        nrouted = p.coff[bhk * (T + 1) + c + 1] - rbase;
-    }
-    int dlo = 0, dhi = 0;
-    if (p.causal) { dlo = t0; dhi = min(c * p.B + p.B, p.n); }
-    else if (c == T) { dlo = 0; dhi = p.n; }
     const int nrows = nrouted + max(dhi - dlo, 0);
     // segment 0 holds the end of the sequence
     const int j1 = nrows - seg * p.seg_rows, j0 = max(j1 - p.seg_rows, 0);
@@ -540,6 +658,7 @@ __global__ __launch_bounds__(256) void prior_attn_dkv_kernel(DkvParams p) {
     RowSeq rs;
     rs.irow = p.inv_row + bhk * (size_t)p.n * T + rbase;
     rs.ibias = p.inv_bias + bhk * (size_t)p.n * T + rbase;
+    rs.safe_i = p.coff; rs.safe_f = p.lse;
     rs.nrouted = nrouted; rs.dlo = dlo; rs.j0 = j0; rs.j1 = j1;
 
     // ---- K and V of the wavefront's 32 tokens as B operands (token = lane column) ----
@@ -556,33 +675,63 @@ __global__ __launch_bounds__(256) void prior_attn_dkv_kernel(DkvParams p) {
         }
     }
 
-    // ---- tables: lanes 0..15 of each wavefront keep the pair 16*wid + lane ----
+    // ---- the table pipeline ----
+    // Every value a step needs from memory besides the Q / dO tiles arrives by a copy
+    // straight into LDS, so no register waits for a load across steps. In step k:
+    //   wavefront 0 / 1 copies the list rows / biases of group k+5 (64 lanes = the
+    //   group's 64 pairs) into ring slot (k+5) % 8;
+    //   wavefront 2 / 3 copies lse / Δ of group k+3 (rows from slot (k+3) % 8) into
+    //   ring slot (k+3) % 4;
+    //   all wavefronts copy the Q / dO tiles of group k+2 (rows from slot (k+2) % 8);
+    //   lanes 0..15 of each wavefront turn the loaded values of group k+1 into its
+    //   tables (slot (k+1) % 2).
+    // Each wavefront so issues one table copy plus its tile copies per step; the wait
+    // at the end of step k leaves exactly those in flight, so everything older has
+    // landed and every read above finds its data.
+    const int pr_slot = lane >> lg, pr_head = lane & (g - 1);    // pair = lane (table copies)
+    const size_t hbase_l = ((size_t)bi * p.h_q + (size_t)hk * g + pr_head) * p.n;
+    auto table_copy = [&](int k) {
+        if (wid < 2) {
+            const int m = k + 5;
+            const int j = rs.entry(m * RG + pr_slot);
+            const void* src = wid == 0 ? (const void*)rs.row_src(j) : (const void*)rs.bias_src(j);
+            char* dst = reinterpret_cast<char*>(wid == 0 ? r_row + (m & 7) * 64 : reinterpret_cast<int*>(r_bias) + (m & 7) * 64);
+            __builtin_amdgcn_global_load_lds(src, dst, 4, 0, 0);
+        } else {
+            const int m = k + 3;
+            const int j = rs.entry(m * RG + pr_slot);
+            const int row = rs.row(j, r_row[(m & 7) * 64 + lane]);
+            const float* src = (wid == 2 ? p.lse : p.delta) + hbase_l + row;
+            char* dst = reinterpret_cast<char*>((wid == 2 ? r_lse : r_dlt) + (m & 3) * 64);
+            __builtin_amdgcn_global_load_lds(src, dst, 4, 0, 0);
+        }
+    };
     const bool TL = lane < 16;
     const int tp = 16 * wid + (lane & 15);
-    const int tslot = tp >> lg, thead = tp & (g - 1);
-    const size_t hbase = ((size_t)bi * p.h_q + (size_t)hk * g + thead) * p.n;
-    auto ids = [&](int k) {
-        RowId r;
-        rs.get(k * RG + tslot, r.row, r.bias, r.valid, r.routed);
-        return r;
-    };
-    auto pair_tables = [&](int slot, const RowId& r, float lse, float dl) {
+    const int tslot = tp >> lg;
+    auto make_tables = [&](int m) {
+        const int j = rs.entry(m * RG + tslot);
+        const int row = rs.row(j, r_row[(m & 7) * 64 + tp]);
+        const float lse = r_lse[(m & 3) * 64 + tp];
         const float l2 = (lse == -INFINITY) ? INFINITY : lse * kLog2e;
-        t_off[slot * 64 + tp] = r.valid ? r.bias * kLog2e - l2 : -INFINITY;
-        t_lim[slot * 64 + tp] = !r.valid ? -1 : r.routed ? 0x7fffffff : (p.causal ? r.row : p.n - 1);
-        t_dlt[slot * 64 + tp] = r.valid ? dl : 0.f;
+        const float bias = rs.routed(j) ? r_bias[(m & 7) * 64 + tp] : 0.f;
+        const int slot = m & 1;
+        t_off[slot * 64 + tp] = rs.valid(j) ? bias * kLog2e - l2 : -INFINITY;
+        t_lim[slot * 64 + tp] = !rs.valid(j) ? -1 : rs.routed(j) ? 0x7fffffff : (p.causal ? row : p.n - 1);
+        t_dlt[slot * 64 + tp] = rs.valid(j) ? r_dlt[(m & 3) * 64 + tp] : 0.f;
     };
 
-    // ---- copies of a group's stage (rows from t_row) ----
+    // ---- copies of a group's Q / dO stage (rows from its ring slot) ----
     const uint16_t* Qg = p.Q + ((size_t)bi * p.h_q + (size_t)hk * g) * p.n * D;
     const uint16_t* dOg = p.dO + ((size_t)bi * p.h_q + (size_t)hk * g) * p.n * D;
-    auto issue = [&](char* stage, const int* rows) {
+    auto issue = [&](char* stage, int m) {
 #pragma unroll
         for (int i = 0; i < CPW; ++i) {
             const int j = wid + 4 * i;                 // wavefront-uniform
             const int jj = j % S::KINSTS;
             const int q = jj * 64 + lane, t = q / S::KPPR, cc = q % S::KPPR;
-            const int row = min(max(rows[t >> lg], 0), p.n - 1);
+            const int e = rs.entry(m * RG + (t >> lg));
+            const int row = min(max(rs.row(e, r_row[(m & 7) * 64 + t]), 0), p.n - 1);
             const size_t o = ((size_t)(t & (g - 1)) * p.n + row) * D + S::kslot(t, cc) * 8;
             // source and destination as named pointers: a conditional expression
             // inside the builtin's argument list loses the kernel's host stub
@@ -592,26 +741,28 @@ __global__ __launch_bounds__(256) void prior_attn_dkv_kernel(DkvParams p) {
         }
     };
 
-    // ---- prologue: tables of group 0, rows of groups 0..2, copies of groups 0 and 1 ----
-    RowId qa = ids(1), qb = ids(2);            // table lanes: groups k+1, k+2
-    {
-        const RowId r0 = ids(0);
-        if (TL) {
-            const float lse = r0.valid ? p.lse[hbase + r0.row] : 0.f;
-            const float dl = r0.valid ? p.delta[hbase + r0.row] : 0.f;
-            pair_tables(0, r0, lse, dl);
-            if (thead == 0) {
-                t_row[tslot] = r0.row;
-                t_row[64 + tslot] = qa.row;
-                t_row[128 + tslot] = qb.row;
-            }
-        }
+    // ---- prologue (plain loads): list values of groups 0..4, lse / Δ of groups
+    // 0..2, tables of group 0, tiles of groups 0 and 1 ----
+    for (int x = tid; x < 5 * 64; x += 256) {
+        const int m = x >> 6, pp = x & 63;
+        const int j = rs.entry(m * RG + (pp >> lg));
+        r_row[(m & 7) * 64 + pp] = *rs.row_src(j);
+        r_bias[(m & 7) * 64 + pp] = *rs.bias_src(j);
     }
     __syncthreads();
-    issue(ring, t_row);
-    if (ngroups > 1) issue(ring + ST::BYTES, t_row + 64);
-    else wait_vm<0>();
-    if (ngroups > 1) wait_vm<CPW>();
+    for (int x = tid; x < 3 * 64; x += 256) {
+        const int m = x >> 6, pp = x & 63;
+        const int j = rs.entry(m * RG + (pp >> lg));
+        const int row = rs.row(j, r_row[(m & 7) * 64 + pp]);
+        const size_t hb = ((size_t)bi * p.h_q + (size_t)hk * g + (pp & (g - 1))) * p.n;
+        r_lse[(m & 3) * 64 + pp] = p.lse[hb + row];
+        r_dlt[(m & 3) * 64 + pp] = p.delta[hb + row];
+    }
+    __syncthreads();
+    if (TL) make_tables(0);
+    issue(ring, 0);
+    if (ngroups > 1) issue(ring + ST::BYTES, 1);
+    wait_vm<0>();
     __syncthreads();
 
     f32x16 dk[ND], dv[ND];
@@ -632,15 +783,9 @@ __global__ __launch_bounds__(256) void prior_attn_dkv_kernel(DkvParams p) {
     char* st_nn = ring + 2 * ST::BYTES;
 
     for (int k = 0; k < ngroups; ++k) {
-        // table lanes: rows of group k+3 and lse / Δ of group k+1
-        const RowId qc = ids(k + 3);
-        float lse_n = 0.f, dlt_n = 0.f;
-        if (TL && qa.valid) {
-            lse_n = p.lse[hbase + qa.row];
-            dlt_n = p.delta[hbase + qa.row];
-        }
+        table_copy(k);
         const bool more = k + 2 < ngroups;
-        if (more) issue(st_nn, t_row + ((k + 2) & 3) * 64);
+        if (more) issue(st_nn, k + 2);
 
         const char* qt = st_cur;
         const char* dot = qt + S::KBYTES;
@@ -681,22 +826,31 @@ __global__ __launch_bounds__(256) void prior_attn_dkv_kernel(DkvParams p) {
         }
         // dV += P^T dO and dK += dZ^T Q over the 32 pairs; B operands by transposing
         // reads of the row-major tiles
+        const uint32_t qt_lds = lds_addr(qt);
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-            bf16x8 ob[ND], qb8[ND];
+            // reads 0 .. 2ND-1: dO, then 2ND .. 4ND-1: Q; read 2 db + t of a tensor
+            // holds pairs base + 4t .. +3 of d block db
+            uint32_t a[4 * ND];
 #pragma unroll
             for (int db = 0; db < ND; ++db) {
                 const int d = 32 * db + tr_d;
-                i16x4 x[2], y[2];
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
                     const int pr = 32 * half + 16 * s + 8 * hl + 4 * t + tr_k;
-                    const int o = pr * S::KROWB + S::kslot(pr, d >> 3) * 16 + ((d >> 2) & 1) * 8;
-                    x[t] = lds_read_tr16(dot + o);
-                    y[t] = lds_read_tr16(qt + o);
+                    const uint32_t o = pr * S::KROWB + S::kslot(pr, d >> 3) * 16 + ((d >> 2) & 1) * 8;
+                    a[2 * db + t] = qt_lds + S::KBYTES + o;
+                    a[2 * ND + 2 * db + t] = qt_lds + o;
                 }
-                ob[db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(x[0], x[1], 0, 1, 2, 3, 4, 5, 6, 7));
-                qb8[db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(y[0], y[1], 0, 1, 2, 3, 4, 5, 6, 7));
+            }
+            i16x4 x[4 * ND];
+            lds_read_tr16<4 * ND>(a, x);
+            bf16x8 ob[ND], qb8[ND];
+#pragma unroll
+            for (int db = 0; db < ND; ++db) {
+                ob[db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(x[2 * db], x[2 * db + 1], 0, 1, 2, 3, 4, 5, 6, 7));
+                qb8[db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(x[2 * ND + 2 * db], x[2 * ND + 2 * db + 1],
+                                                                             0, 1, 2, 3, 4, 5, 6, 7));
             }
 #pragma unroll
             for (int db = 0; db < ND; ++db) {
@@ -705,19 +859,17 @@ __global__ __launch_bounds__(256) void prior_attn_dkv_kernel(DkvParams p) {
             }
         }
 
-        // tables of group k+1 (slot last read in step k-1) and rows of group k+3
-        // (slot last read by the copies of step k-1)
-        if (TL) {
-            pair_tables((k + 1) & 1, qa, lse_n, dlt_n);
-            if (thead == 0) t_row[((k + 3) & 3) * 64 + tslot] = qc.row;
-        }
-        qa = qb; qb = qc;
-        // the copies of group k+1 have landed; those of group k+2 may stay in flight
-        if (more) wait_vm<CPW>();
-        else wait_vm<0>();
-        __syncthreads();
+        // tables of group k+1 (their slot was last read in step k-1)
+        if (TL) make_tables(k + 1);
+        // everything issued before this step has landed; this step's table copy and
+        // tile copies may stay in flight
+        if (more) wait_vm<CPW + 1>();
+        else wait_vm<1>();
+        barrier_lds();
         char* t = st_cur; st_cur = st_nxt; st_nxt = st_nn; st_nn = t;
     }
+
+    wait_vm<0>();      // no copy into LDS outlives the loop
 
     // ---- add the partials: element i of lane l is token 8(i/4) + 4hl + i%4 of the
     // wavefront's 32, column d = 32 db + l32 ----
@@ -734,6 +886,23 @@ __global__ __launch_bounds__(256) void prior_attn_dkv_kernel(DkvParams p) {
         }
 }
 
+// Persistent: each workgroup takes work items from a counter until none is left.
+template <int D>
+__global__ __launch_bounds__(256) void prior_attn_dkv_kernel(DkvParams p) {
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    int* s_item = reinterpret_cast<int*>(smem + dkv_item_lds_bytes<D>());
+    const int nitems = p.counters[1];
+    for (;;) {
+        if (threadIdx.x == 0) *s_item = atomicAdd(p.counters, 1);
+        __syncthreads();
+        const int it = *s_item;
+        __syncthreads();
+        if (it >= nitems) break;
+        const int4 w = p.items[it];
+        dkv_item<D>(p, (size_t)w.x, w.y, w.z, smem);
+    }
+}
+
 // ---------------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------------
@@ -746,8 +915,7 @@ static size_t dq_lds_bytes(int d, int T_c) {
     return 2 * stage + TileTables::bytes(T_c);
 }
 static size_t dkv_lds_bytes(int d) {
-    const size_t stage = d == 64 ? DkvStage<64>::BYTES : DkvStage<128>::BYTES;
-    return DkvStage<128>::NST * stage + 3 * 128 * 4 + 4 * 64 * 4;
+    return (d == 64 ? dkv_item_lds_bytes<64>() : dkv_item_lds_bytes<128>()) + 16;
 }
 
 int backward_tile_rows(int g, int B, int T_c, int d) {
@@ -756,9 +924,19 @@ int backward_tile_rows(int g, int B, int T_c, int d) {
     return std::min(32 * kDqWaves / g, 64);      // a query tile stays inside one chunk
 }
 
+// Rows per dK/dV work item and an upper bound on the number of items: over the tiles
+// of one KV group the sequences hold each routed entry B/64 times (at most n floor(n/B)
+// entries) plus diagonal rows (at most B/64 (n + B)); every tile adds at most one
+// partial segment.
+static int dkv_seg_rows(int g) { return 8192 / g; }
+static size_t dkv_item_bound(int b, int h_q, int h_kv, int n, int B) {
+    const size_t T = (size_t)(n / B), SUB = (size_t)(B / 64), seg = (size_t)dkv_seg_rows(h_q / h_kv);
+    return (size_t)b * h_kv * ((T + 1) * SUB + (SUB * ((size_t)n * T + n + B) + seg - 1) / seg);
+}
+
 namespace {
 struct BwdLayout {
-    size_t kt, dob, delta, hist, coff, inv_row, inv_bias, total;
+    size_t kt, dob, delta, hist, coff, inv_row, inv_bias, items, counters, total;
 };
 size_t up256(size_t x) { return (x + 255) / 256 * 256; }
 BwdLayout bwd_layout(int b, int h_q, int h_kv, int n, int d, int B) {
@@ -772,6 +950,8 @@ BwdLayout bwd_layout(int b, int h_q, int h_kv, int n, int d, int B) {
     L.coff = o;     o += up256((size_t)b * h_kv * (T + 1) * 4);
     L.inv_row = o;  o += up256((size_t)b * h_kv * n * T * 4);
     L.inv_bias = o; o += up256((size_t)b * h_kv * n * T * 4);
+    L.items = o;    o += up256(dkv_item_bound(b, h_q, h_kv, n, B) * 16);
+    L.counters = o; o += 256;
     L.total = o;
     return L;
 }
@@ -857,16 +1037,25 @@ static hipError_t launch_bwd_t(const PrefillBwdArgs& a, const BwdLayout& L, hipS
     q.dK = a.dK; q.dV = a.dV;
     q.h_q = a.h_q; q.h_kv = a.h_kv; q.n = a.n; q.B = a.B; q.T_c = T; q.causal = a.causal;
     q.g = g; q.log2g = lg;
-    q.seg_rows = 8192 / g;
+    q.seg_rows = dkv_seg_rows(g);
+    q.items = reinterpret_cast<const int4*>(ws + L.items);
+    q.counters = reinterpret_cast<int32_t*>(ws + L.counters);
     q.c1 = p.scale_log2; q.scale = scale;
     {
         auto kern = prior_attn_dkv_kernel<D>;
         static hipError_t configured = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kBwdMaxLds);
         if (configured != hipSuccess) return configured;
-        const int nseg = (a.n + q.seg_rows - 1) / q.seg_rows;
-        dim3 grid(nseg, (T + 1) * (a.B / 64), bh);
-        hipLaunchKernelGGL(kern, grid, dim3(256), dkv_lds_bytes(D), s, q);
+        hipLaunchKernelGGL(dkv_items_kernel, dim3(1), dim3(1024), 0, s, ip.coff,
+                           reinterpret_cast<int4*>(ws + L.items), q.counters, bh, a.n, a.B, T, a.causal, q.seg_rows);
+        static int cus = 0;
+        if (cus == 0) {
+            int dev = 0;
+            if (hipGetDevice(&dev) != hipSuccess ||
+                hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+                cus = 256;
+        }
+        hipLaunchKernelGGL(kern, dim3(cus), dim3(256), dkv_lds_bytes(D), s, q);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     return hipSuccess;

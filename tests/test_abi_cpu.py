@@ -240,8 +240,10 @@ def test_backward_workspace(dash):
     up = lambda x: (x + 255) // 256 * 256
     b, hq, hkv, n, d, B = 1, 16, 2, 256, 128, 64
     T, nblk = n // B, (n + 63) // 64
+    seg = 8192 // (hq // hkv)
+    items = hkv * ((T + 1) + -(-(n * T + n + B) // seg))
     expect = (up(hkv * d * 256 * 2) + up(hq * n * d * 2) + up(hq * n * 4) + up(hkv * T * nblk * 4)
-              + up(hkv * (T + 1) * 4) + 2 * up(hkv * n * T * 4))
+              + up(hkv * (T + 1) * 4) + 2 * up(hkv * n * T * 4) + up(items * 16) + 256)
     assert need == expect
     # n * floor(n/B) must stay below 2^31 (inverted list offsets are int32)
     assert _backward(dash, n=1 << 20, B=64, cap=1 << 14, ws_bytes=1 << 62) == dash.DASH_ERR_UNSUPPORTED
