@@ -605,19 +605,7 @@ __device__ __forceinline__ void lds_read_tr16(const uint32_t (&a)[N], i16x4 (&r)
     }
 }
 
-// Wait until at most N vector memory operations of this wavefront are in flight.
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-    static_assert(N >= 0 && N < 64, "vmcnt immediate");
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
 
-// Workgroup barrier after this wavefront's LDS writes and reads have completed. Unlike
-// __syncthreads() it does not also wait for the copies into LDS still in flight
-// (their landing is ordered by explicit vmcnt waits).
-__device__ __forceinline__ void barrier_lds() {
-    asm volatile("s_waitcnt lgkmcnt(0)\n s_barrier" ::: "memory");
-}
 
 // LDS of one work item: the tile ring, the tables and the loaded-value rings.
 template <int D>

@@ -196,6 +196,20 @@ struct TileCopier {
     }
 };
 
+// Wait until at most N vector memory operations of this wavefront are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt immediate");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier after this wavefront's LDS writes and reads have completed. Unlike
+// __syncthreads() it does not also wait for the copies into LDS still in flight
+// (their landing is ordered by explicit vmcnt waits).
+__device__ __forceinline__ void barrier_lds() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n s_barrier" ::: "memory");
+}
+
 __device__ __forceinline__ void wait_tile_copies() {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
