@@ -267,6 +267,26 @@ struct DqCopier {
     }
 };
 
+// dZ of one 32-token half of a tile from its S^T and dP^T accumulators: P =
+// 2^(S c1 + off) with off = bias - lse in log2 units, zero past lim on the diagonal
+// (MASK; element e of k16 step u is token tk0 + 16 u + e); returns the sum of dZ.
+template <bool MASK>
+__device__ __forceinline__ float dz_half(const f32x16& sacc, const f32x16& dpacc, float c1, float off, float dlt,
+                                         int tk0, int lim, bf16x8 (&dz)[2]) {
+    float part = 0.f;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float pv = fast_exp2(fmaf(sacc[8 * u + e], c1, off));
+            if (MASK && tk0 + 16 * u + e > lim) pv = 0.f;
+            const float z = pv * (dpacc[8 * u + e] - dlt);
+            part += z;
+            dz[u][e] = (__bf16)z;
+        }
+    return part;
+}
+
 // NW wavefronts of one 32-pair block each; the tile geometry is the forward's.
 template <int D, int NW>
 __global__ __launch_bounds__(64 * NW) void prior_attn_dq_kernel(PrefillParams p, DqExtra x) {
@@ -345,6 +365,10 @@ __global__ __launch_bounds__(64 * NW) void prior_attn_dq_kernel(PrefillParams p,
     wait_tile_copies();
     __syncthreads();
     for (int k = 0; k < st.nsteps; ++k) {
+        // dQ stays in accumulation registers across steps (both sides of the
+        // step's skip branch), so no step copies it in and out
+#pragma unroll
+        for (int db = 0; db < ND; ++db) asm volatile("" : "+a"(dq[db]));
         const bool routed = k < st.nrouted;
         const bool last = k % st.SPC == st.SPC - 1;
         const int epos = lc.pos;                   // list position of chunk c_cur if routed
@@ -360,58 +384,44 @@ __global__ __launch_bounds__(64 * NW) void prior_attn_dq_kernel(PrefillParams p,
         const char* ktt = kt + 2 * S::KBYTES;
         const int tb = tb_cur;
         if (run) {
-            f32x16 sacc[NB], dpacc[NB];
-#pragma unroll
-            for (int blk = 0; blk < NB; ++blk)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) { sacc[blk][i] = 0.f; dpacc[blk][i] = 0.f; }
-            // S^T = K Q^T and dP^T = V dO^T over the tile
-#pragma unroll
-            for (int s = 0; s < NS; ++s) {
-                bf16x8 ka[NB], va[NB];
-#pragma unroll
-                for (int blk = 0; blk < NB; ++blk) {
-                    const int t = 32 * blk + krow;
-                    const int o = t * S::KROWB + S::kslot(t, 2 * s + hl) * 16;
-                    ka[blk] = *reinterpret_cast<const bf16x8*>(kt + o);
-                    va[blk] = *reinterpret_cast<const bf16x8*>(vt + o);
-                }
-#pragma unroll
-                for (int blk = 0; blk < NB; ++blk) {
-                    sacc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[blk], qf[s], sacc[blk], 0, 0, 0);
-                    dpacc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[blk], df[s], dpacc[blk], 0, 0, 0);
-                }
-            }
-            // P from the forward's lse, dZ = P (dP - Δ); token of element e of k16
-            // step s is tb + 16 s + 8 hl + e
+            // one 32-token half of the tile at a time: S^T = K Q^T and dP^T = V dO^T,
+            // then P from the forward's lse and dZ = P (dP - Δ), then dQ^T += K^T dZ^T
+            // over the half's two k16 steps (token of element e of k16 step s is
+            // tb + 16 s + 8 hl + e)
             const float off = bias2 - lse2;
-            bf16x8 dz[NP];
             float part = 0.f;
 #pragma unroll
-            for (int s = 0; s < NP; ++s)
+            for (int blk = 0; blk < NB; ++blk) {
+                f32x16 sacc, dpacc;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int i = 8 * (s & 1) + e;
-                    float pv = fast_exp2(fmaf(sacc[s >> 1][i], c1, off));
-                    if (!routed && tb + 16 * s + 8 * hl + e > lim) pv = 0.f;
-                    const float z = pv * (dpacc[s >> 1][i] - dlt);
-                    part += z;
-                    dz[s][e] = (__bf16)z;
+                for (int i = 0; i < 16; ++i) { sacc[i] = 0.f; dpacc[i] = 0.f; }
+                const int t = 32 * blk + krow;
+#pragma unroll
+                for (int s = 0; s < NS; ++s) {
+                    const int o = t * S::KROWB + S::kslot(t, 2 * s + hl) * 16;
+                    const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kt + o);
+                    const bf16x8 va = *reinterpret_cast<const bf16x8*>(vt + o);
+                    sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[s], sacc, 0, 0, 0);
+                    dpacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, df[s], dpacc, 0, 0, 0);
                 }
-            dbsum += part;
-            // dQ^T += K^T dZ^T
+                bf16x8 dz[2];
+                part += routed ? dz_half<false>(sacc, dpacc, c1, off, dlt, 0, 0, dz)
+                               : dz_half<true>(sacc, dpacc, c1, off, dlt, tb + 32 * blk + 8 * hl, lim, dz);
 #pragma unroll
-            for (int s = 0; s < NP; ++s) {
-                bf16x8 kta[ND];
+                for (int u = 0; u < 2; ++u) {
+                    const int sk = 2 * blk + u;
+                    bf16x8 kta[ND];
 #pragma unroll
-                for (int db = 0; db < ND; ++db) {
-                    const int d = 32 * db + l32;
-                    kta[db] = *reinterpret_cast<const bf16x8*>(ktt + d * S::VROWB + S::vslot(d, 2 * s + hl) * 16);
+                    for (int db = 0; db < ND; ++db) {
+                        const int d = 32 * db + l32;
+                        kta[db] = *reinterpret_cast<const bf16x8*>(ktt + d * S::VROWB + S::vslot(d, 2 * sk + hl) * 16);
+                    }
+#pragma unroll
+                    for (int db = 0; db < ND; ++db)
+                        dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kta[db], dz[u], dq[db], 0, 0, 0);
                 }
-#pragma unroll
-                for (int db = 0; db < ND; ++db)
-                    dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kta[db], dz[s], dq[db], 0, 0, 0);
             }
+            dbsum += part;
             // the chunk's bias gradient: its tokens (both lane halves, all its steps)
             // and the g heads of the row (g consecutive lanes)
             if (routed && last) {
@@ -615,6 +625,31 @@ constexpr size_t dkv_item_lds_bytes() {
 
 // One work item: 64 tokens of one chunk (tile cs) of KV group bhk against segment
 // seg of its row sequence.
+// The 16 transposing reads of k16 step s for d = 128 from two per-lane bases. In the
+// swizzled [64][128] tiles the byte offset of read (db, t) of a lane is
+//   L + 4096 s + 1024 t + 64 (db ^ (2 hl + t)),
+// and 64 (u ^ 2 hl) with u = db ^ t equals 64 u + 128 hl for u < 2 and 64 u - 128 hl
+// otherwise, so with a = L + 128 hl and b = L - 128 hl every offset is an immediate.
+// Reads 0..7: the dO tile (at +16384), 8..15: the Q tile; read 2 db + t.
+template <int S>
+__device__ __forceinline__ void tr_reads_d128(uint32_t a, uint32_t b, i16x4 (&r)[16]) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %16 offset:%18\n ds_read_b64_tr_b16 %1, %16 offset:%18+1088\n"
+        "ds_read_b64_tr_b16 %2, %16 offset:%18+64\n ds_read_b64_tr_b16 %3, %16 offset:%18+1024\n"
+        "ds_read_b64_tr_b16 %4, %17 offset:%18+128\n ds_read_b64_tr_b16 %5, %17 offset:%18+1216\n"
+        "ds_read_b64_tr_b16 %6, %17 offset:%18+192\n ds_read_b64_tr_b16 %7, %17 offset:%18+1152\n"
+        "ds_read_b64_tr_b16 %8, %16 offset:%19\n ds_read_b64_tr_b16 %9, %16 offset:%19+1088\n"
+        "ds_read_b64_tr_b16 %10, %16 offset:%19+64\n ds_read_b64_tr_b16 %11, %16 offset:%19+1024\n"
+        "ds_read_b64_tr_b16 %12, %17 offset:%19+128\n ds_read_b64_tr_b16 %13, %17 offset:%19+1216\n"
+        "ds_read_b64_tr_b16 %14, %17 offset:%19+192\n ds_read_b64_tr_b16 %15, %17 offset:%19+1152\n"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]),
+          "=&v"(r[7]), "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11]), "=&v"(r[12]), "=&v"(r[13]),
+          "=&v"(r[14]), "=&v"(r[15])
+        : "v"(a), "v"(b), "n"(16384 + 4096 * S), "n"(4096 * S)
+        : "memory");
+}
+
 template <int D>
 __device__ __forceinline__ void dkv_item(const DkvParams& p, size_t bhk, int cs, int seg, char* smem) {
     typedef BfTiles<D, 64> S;
@@ -765,12 +800,17 @@ __device__ __forceinline__ void dkv_item(const DkvParams& p, size_t bhk, int cs,
     // 16(G&1) .. +15 of a 32-wide d block and k-slot half hl; its lane 4k + q reads
     // pair base + k at d offset 4q
     const int tr_k = (lane & 15) >> 2, tr_d = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    // d = 128: the lane's offset L of read (s, db, t) = (0, 0, 0) inside a tile
+    const uint32_t tr_base = (32 * half + 8 * hl + tr_k) * 256 + 16 * ((tr_d >> 3) ^ tr_k) + 8 * (lane & 1);
     const float c1 = p.c1;
     char* st_cur = ring;
     char* st_nxt = ring + ST::BYTES;
     char* st_nn = ring + 2 * ST::BYTES;
 
     for (int k = 0; k < ngroups; ++k) {
+        // dK and dV stay in accumulation registers across groups
+#pragma unroll
+        for (int db = 0; db < ND; ++db) asm volatile("" : "+a"(dk[db]), "+a"(dv[db]));
         table_copy(k);
         const bool more = k + 2 < ngroups;
         if (more) issue(st_nn, k + 2);
@@ -819,20 +859,26 @@ __device__ __forceinline__ void dkv_item(const DkvParams& p, size_t bhk, int cs,
         for (int s = 0; s < 2; ++s) {
             // reads 0 .. 2ND-1: dO, then 2ND .. 4ND-1: Q; read 2 db + t of a tensor
             // holds pairs base + 4t .. +3 of d block db
-            uint32_t a[4 * ND];
-#pragma unroll
-            for (int db = 0; db < ND; ++db) {
-                const int d = 32 * db + tr_d;
-#pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    const int pr = 32 * half + 16 * s + 8 * hl + 4 * t + tr_k;
-                    const uint32_t o = pr * S::KROWB + S::kslot(pr, d >> 3) * 16 + ((d >> 2) & 1) * 8;
-                    a[2 * db + t] = qt_lds + S::KBYTES + o;
-                    a[2 * ND + 2 * db + t] = qt_lds + o;
-                }
-            }
             i16x4 x[4 * ND];
-            lds_read_tr16<4 * ND>(a, x);
+            if constexpr (D == 128) {
+                const uint32_t a0 = qt_lds + tr_base + 128 * hl, b0 = qt_lds + tr_base - 128 * hl;
+                if (s == 0) tr_reads_d128<0>(a0, b0, x);
+                else tr_reads_d128<1>(a0, b0, x);
+            } else {
+                uint32_t a[4 * ND];
+#pragma unroll
+                for (int db = 0; db < ND; ++db) {
+                    const int d = 32 * db + tr_d;
+#pragma unroll
+                    for (int t = 0; t < 2; ++t) {
+                        const int pr = 32 * half + 16 * s + 8 * hl + 4 * t + tr_k;
+                        const uint32_t o = pr * S::KROWB + S::kslot(pr, d >> 3) * 16 + ((d >> 2) & 1) * 8;
+                        a[2 * db + t] = qt_lds + S::KBYTES + o;
+                        a[2 * ND + 2 * db + t] = qt_lds + o;
+                    }
+                }
+                lds_read_tr16<4 * ND>(a, x);
+            }
             bf16x8 ob[ND], qb8[ND];
 #pragma unroll
             for (int db = 0; db < ND; ++db) {
