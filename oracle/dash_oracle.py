@@ -29,7 +29,10 @@ notes of this repository):
 Parity status: pinned by tests/test_oracle.py (entmax against its variational
 definition, brute-force KKT supports, sparsemax/softmax limits; Stage 0 mean
 pooling and B=1; the Eq. 9 form against the Prop. 4.1 form; σ=inf against a
-library masked SDPA; full support against library causal SDPA).
+library masked SDPA; full support against library causal SDPA). The backward
+functions (attend_backward, route_backward, summary_backward: gradients with the
+support held fixed) are pinned by central finite differences of the forward
+oracle, chained through all three stages, and by torch autograd of masked SDPA.
 """
 from __future__ import annotations
 
@@ -424,6 +427,92 @@ def attend_backward(Qr, pos, K, V, rt, B, causal, n_kv, dO, row_block=64):
                         dbias[bi, r, r0:r1, c] += dzr[:, c * B:(c + 1) * B].sum(-1) if c * B < jmax else 0.0
     dbias = np.where(rt["support"], dbias, 0.0)
     return dict(dQ=dQ, dK=dK, dV=dV, dbias=dbias, lse=lse)
+
+
+def route_backward(Qr, pos, kbar, B, alpha, gamma, sigma, causal, n_kv, dbias):
+    """Gradients of Stage 1 for an upstream gradient dbias [b, h_kv, R, T] of the
+    Prop. 4.1 bias (paper review section 三: Eq. 6 routing, the GQA average and the
+    bias of Prop. 4.1), the support S held fixed (it changes only on a set of
+    measure zero):
+      d_c = (log w_c - μ)/σ, μ = mean over S of log w
+          -> g_c = ∂L/∂log w_c = (dbias_c - mean over S of dbias)/σ on S;
+      w = (1/g) Σ_h ŵ_h                    -> ∂L/∂ŵ_h = g_c / (g w_c) on S;
+      ŵ_h = α-entmax(x_h), x_h = γ z_h, whose Jacobian is diag(s) - s sᵀ/Σ s with
+          s = ŵ_h^(2-α) on the head's support (α = 1, softmax: s = ŵ_h)
+          -> ∂L/∂x_h = s (∂L/∂ŵ_h - Σ s ∂L/∂ŵ_h / Σ s);
+      z_h = q_h k̄ᵀ/sqrt(d)                 -> dq_h = γ ∂L/∂x_h k̄/sqrt(d),
+                                              dk̄ = Σ_h γ (∂L/∂x_h)ᵀ q_h/sqrt(d).
+    Returns dQ [b, h_q, R, d] and dkbar [b, h_kv, T, d] (float64). A fixed top-k
+    budget is not covered: its kept set drops chunks the entmax normalisation still
+    couples, so the lists alone do not carry the gradient.
+    """
+    Qr = _f64(Qr)
+    kbar = _f64(kbar)
+    b, hq, R, d = Qr.shape
+    hkv = kbar.shape[1]
+    g = hq // hkv
+    T = n_kv // B
+    kb = kbar[:, :, :T]
+    rt = route(Qr, pos, kbar, B, alpha, gamma, sigma, causal, n_kv, keep_heads=True)
+    S = rt["support"]
+    dQ = np.zeros_like(Qr)
+    dkb = np.zeros((b, hkv, T, d))
+    if np.isinf(sigma) or T == 0:
+        return dict(dQ=dQ, dkbar=dkb)
+    db = np.where(S, _f64(dbias)[..., :T], 0.0)
+    cnt = S.sum(-1, keepdims=True)
+    mean = db.sum(-1, keepdims=True) / np.maximum(cnt, 1)
+    glogw = np.where(S, (db - mean) / sigma, 0.0)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        dw = np.where(S, glogw / np.where(S, rt["w"], 1.0), 0.0)       # ∂L/∂w
+    sq = np.sqrt(d)
+    for h in range(hq):
+        r = h // g
+        what = rt["what"][:, h]                                          # [b, R, T]
+        dwhat = dw[:, r] / g
+        if alpha == 1.0:
+            s_ = what
+        else:
+            with np.errstate(invalid="ignore"):
+                s_ = np.where(what > 0, np.power(np.where(what > 0, what, 1.0), 2.0 - alpha), 0.0)
+        ssum = s_.sum(-1, keepdims=True)
+        dx = s_ * (dwhat - (s_ * dwhat).sum(-1, keepdims=True) / np.where(ssum > 0, ssum, 1.0))
+        dz = gamma * dx / sq
+        for bi in range(b):
+            dQ[bi, h] = dz[bi] @ kb[bi, r]
+            dkb[bi, r] += dz[bi].T @ Qr[bi, h]
+    return dict(dQ=dQ, dkbar=dkb)
+
+
+def summary_backward(K, qbar, B, dkbar):
+    """Gradients of Stage 0 (Eq. 4: k̄_c = Σ_j π_j k_j, π = softmax_j(<q̄, k_j>/sqrt(d))
+    over the B tokens of chunk c) for dkbar [b, h_kv, T, d]:
+      ∂L/∂π_j = <dk̄_c, k_j>, ∂L/∂a_j = π_j (<dk̄_c, k_j> - <dk̄_c, k̄_c>),
+      dk_j = π_j dk̄_c + ∂L/∂a_j q̄/sqrt(d),  dq̄ = Σ_{c, j} ∂L/∂a_j k_j/sqrt(d)
+    (summed over the batch as well). Tokens past the last complete chunk get zero.
+    Returns dK [b, h_kv, n, d] and dqbar [h_kv, d] (float64).
+    """
+    K = _f64(K)
+    qbar = _f64(qbar)
+    b, hkv, n, d = K.shape
+    T = n // B
+    dkb = _f64(dkbar)[:, :, :T]
+    dK = np.zeros_like(K)
+    dq = np.zeros((hkv, d))
+    sq = np.sqrt(d)
+    for bi in range(b):
+        for r in range(hkv):
+            for c in range(T):
+                Kc = K[bi, r, c * B:(c + 1) * B]
+                a = Kc @ qbar[r] / sq
+                pi = np.exp(a - a.max())
+                pi /= pi.sum()
+                kbc = pi @ Kc
+                dp = Kc @ dkb[bi, r, c]
+                da = pi * (dp - dkb[bi, r, c] @ kbc)
+                dK[bi, r, c * B:(c + 1) * B] = pi[:, None] * dkb[bi, r, c][None, :] + da[:, None] * qbar[r][None, :] / sq
+                dq[r] += da @ Kc / sq
+    return dict(dK=dK, dqbar=dq)
 
 
 def attend_eq9(Qr, pos, K, V, rt, B, sigma, causal, n_kv):

@@ -523,3 +523,59 @@ def test_stage2_backward_sigma_inf_is_masked_sdpa_autograd():
     Z = np.einsum("bhid,bhjd->bhij", Q, np.repeat(K, g, 1)) / np.sqrt(d)
     Z = np.where(mask, Z, -np.inf)
     np.testing.assert_allclose(gr["lse"], scipy.special.logsumexp(Z, axis=-1), atol=1e-12)
+
+
+def _chain(Q, K, V, qbar, dO, B, alpha, gamma, sigma, causal):
+    """<dO, O> of the whole forward pass (Stage 0 summaries, Stage 1 routing, Stage 2)."""
+    n = Q.shape[2]
+    rows = np.arange(n)
+    kb = O.stage0_summaries(K, qbar, B)
+    rt = O.route(Q, rows[None], kb, B, alpha, gamma, sigma, causal, n)
+    out = O.attend(Q, rows[None], K, V, rt, B, causal, n)
+    return float((dO * out).sum()), kb, rt
+
+
+@pytest.mark.parametrize("alpha,causal,sigma", [(1.5, True, 1.0), (2.0, True, 0.5), (1.0, True, 1.0),
+                                                (1.25, False, 2.0)])
+def test_backward_chain_matches_finite_differences(alpha, causal, sigma):
+    """The whole backward chain (Stage 2, the bias -> group weights -> per-head entmax
+    Jacobian -> logits, and Stage 0) against central differences of the forward
+    oracle in random directions of Q, K, V and q̄; the support must not move under
+    the perturbation (it is held fixed by construction)."""
+    w = _small(n=96, seed=3)
+    B, gamma = 16, 2.0
+    Q, K, V, qbar = (np.asarray(x, np.float64) for x in (w.Q, w.K, w.V, w.qbar))
+    rng = np.random.default_rng(11)
+    dO = rng.standard_normal(Q.shape)
+    n = Q.shape[2]
+    rows = np.arange(n)
+    loss, kb, rt = _chain(Q, K, V, qbar, dO, B, alpha, gamma, sigma, causal)
+    g2 = O.attend_backward(Q, rows[None], K, V, rt, B, causal, n, dO)
+    g1 = O.route_backward(Q, rows[None], kb, B, alpha, gamma, sigma, causal, n, g2["dbias"])
+    g0 = O.summary_backward(K, qbar, B, g1["dkbar"])
+    grads = dict(Q=g2["dQ"] + g1["dQ"], K=g2["dK"] + g0["dK"], V=g2["dV"], qbar=g0["dqbar"])
+    assert np.abs(g1["dQ"]).max() > 0 and np.abs(g0["dqbar"]).max() > 0   # the routing path carries gradient
+    eps = 1e-6
+    for name in ("Q", "K", "V", "qbar"):
+        args = dict(Q=Q, K=K, V=V, qbar=qbar)
+        u = rng.standard_normal(args[name].shape)
+        lp = dict(args); lp[name] = args[name] + eps * u
+        lm = dict(args); lm[name] = args[name] - eps * u
+        fp, _, rp = _chain(lp["Q"], lp["K"], lp["V"], lp["qbar"], dO, B, alpha, gamma, sigma, causal)
+        fm, _, rm = _chain(lm["Q"], lm["K"], lm["V"], lm["qbar"], dO, B, alpha, gamma, sigma, causal)
+        assert np.array_equal(rp["support"], rt["support"]) and np.array_equal(rm["support"], rt["support"])
+        fd = (fp - fm) / (2 * eps)
+        an = float((grads[name] * u).sum())
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (name, fd, an)
+
+
+def test_route_backward_zero_at_infinite_sigma():
+    """σ = inf makes the bias identically zero: no gradient reaches the routing."""
+    w = _small(n=64, seed=4)
+    Q = np.asarray(w.Q, np.float64)
+    kb = O.stage0_summaries(w.K, w.qbar, 16)
+    rows = np.arange(64)
+    rng = np.random.default_rng(2)
+    db = rng.standard_normal((2, 2, 64, 4))
+    g = O.route_backward(Q, rows[None], kb, 16, 1.5, 2.0, np.inf, True, 64, db)
+    assert np.all(g["dQ"] == 0) and np.all(g["dkbar"] == 0)
