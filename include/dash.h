@@ -121,6 +121,47 @@ dash_status dash_route_topk(const void* Q, int q_dtype, const float* kbar,
                             float* w_out, int top_k, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * dash_route with the forward statistics the routing backward needs: stats
+ * [b, h_q, n, 2] (device fp32) gets, for every (query head, row) with a visible
+ * chunk, the largest raw logit <q, k̄_c> and the threshold of its weights (α > 1: τ of
+ * ŵ = [y - τ]_+^{1/(α-1)}; α = 1: log2 Σ_c 2^y), with y = cs (<q, k̄_c> - max) and
+ * cs = (α-1)γ/sqrt(d) (α = 1: γ log2(e)/sqrt(d)). Other arguments as dash_route.
+ */
+dash_status dash_route_stats(const void* Q, int q_dtype, const float* kbar,
+                             int b, int h_q, int h_kv, int n, int kbar_cap, int d, int B,
+                             float alpha, float gamma, float sigma, int causal,
+                             int32_t* idx, float* bias, int32_t* cnt, int list_cap,
+                             float* w_out, float* stats, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Stage-1 backward (paper review section 三: Eq. 6 routing, the GQA average and the
+ * Prop. 4.1 bias; the support held fixed): for the gradient dbias of the routed bias
+ * entries [b, h_kv, n, list_cap] (device fp32, as dash_attend_prefill_backward
+ * writes it) and the lists and statistics of dash_route_stats, ADDS to dQ
+ * [b, h_q, n, d] the routing path's query gradient and to dkbar [b, h_kv, kbar_cap, d]
+ * the summaries' gradient (both device fp32; dkbar by atomic adds, so its last bits
+ * may vary between runs). Per row: g_c = (db_c - mean db)/σ, ∂ŵ_c = g_c/Σ_h ŵ_hc,
+ * the α-entmax Jacobian diag(s) - s sᵀ/Σs with s = ŵ^(2-α) (α = 1: s = ŵ), and the
+ * chain through <q_h, k̄_c>·γ/sqrt(d). σ = +inf: no-op. List entries outside
+ * [0, floor(n/B)) are skipped. Lists of a fixed top-k budget are not supported (their
+ * kept set drops chunks the entmax normalisation couples).
+ */
+dash_status dash_route_backward(const void* Q, int q_dtype, const float* kbar, int kbar_cap,
+                                const int32_t* idx, const int32_t* cnt, const float* dbias, int list_cap,
+                                const float* stats, int b, int h_q, int h_kv, int n, int d, int B,
+                                float alpha, float gamma, float sigma, float* dQ, float* dkbar, void* stream);
+
+/*
+ * Stage-0 backward (Eq. 4: k̄_c = Σ_j π_j k_j, π = softmax_j(<q̄, k_j>/sqrt(d))): for
+ * dkbar [b, h_kv, kbar_cap, d] ADDS to dK [b, h_kv, n, d] (tokens of complete chunks)
+ * and to dqbar [h_kv, d] (device fp32; dqbar by atomic adds). K in k_dtype, q̄
+ * [h_kv, d] fp32.
+ */
+dash_status dash_summarize_backward(const void* K, int k_dtype, const float* qbar, const float* dkbar,
+                                    int b, int h_kv, int n, int kbar_cap, int d, int B,
+                                    float* dK, float* dqbar, void* stream);
+
+/*
  * Bitpacked block mask of routed lists (the form of the routing decision in the
  * pages' GPU kernel table: M_i in {0,1}^{T_c}, 32 chunks per 32-bit word): for every
  * (b, r, row) of idx [b, h_kv, n, list_cap] / cnt [b, h_kv, n] (device int32, as

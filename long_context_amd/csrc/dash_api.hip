@@ -130,11 +130,11 @@ dash_status dash_summarize_paged(const void* Kp, int k_dtype, const float* qbar,
     return from_hip(dash::launch_summary(a, (hipStream_t)stream), "chunk_summary_kernel");
 }
 
-dash_status dash_route_topk(const void* Q, int q_dtype, const float* kbar,
-                            int b, int h_q, int h_kv, int n, int kbar_cap, int d, int B,
-                            float alpha, float gamma, float sigma, int causal,
-                            int32_t* idx, float* bias, int32_t* cnt, int list_cap,
-                            float* w_out, int top_k, void* ws, size_t ws_bytes, void* stream) {
+static dash_status route_impl(const void* Q, int q_dtype, const float* kbar,
+                              int b, int h_q, int h_kv, int n, int kbar_cap, int d, int B,
+                              float alpha, float gamma, float sigma, int causal,
+                              int32_t* idx, float* bias, int32_t* cnt, int list_cap,
+                              float* w_out, int top_k, float* stats, void* ws, size_t ws_bytes, void* stream) {
     if (!Q || !kbar || !idx || !bias || !cnt) return fail(DASH_ERR_NULL, "Q, kbar, idx, bias and cnt must be non-null");
     if (!valid_dtype(q_dtype)) return fail(DASH_ERR_PARAM, "bad Q dtype %d", q_dtype);
     if (causal != 0 && causal != 1) return fail(DASH_ERR_PARAM, "causal must be 0 or 1");
@@ -157,8 +157,27 @@ dash_status dash_route_topk(const void* Q, int q_dtype, const float* kbar,
             return fail(DASH_ERR_WORKSPACE, "bf16 routing needs %zu workspace bytes, got %zu", need, ws ? ws_bytes : (size_t)0);
     }
     dash::RouteArgs a{Q, q_dtype == DASH_BF16, kbar, b, h_q, h_kv, n, kbar_cap, d, B, causal, list_cap,
-                      alpha, gamma, sigma, idx, bias, cnt, w_out, ws, top_k};
+                      alpha, gamma, sigma, idx, bias, cnt, w_out, ws, top_k, stats};
     return from_hip(dash::launch_route(a, (hipStream_t)stream), "entmax_route_kernel");
+}
+
+dash_status dash_route_topk(const void* Q, int q_dtype, const float* kbar,
+                            int b, int h_q, int h_kv, int n, int kbar_cap, int d, int B,
+                            float alpha, float gamma, float sigma, int causal,
+                            int32_t* idx, float* bias, int32_t* cnt, int list_cap,
+                            float* w_out, int top_k, void* ws, size_t ws_bytes, void* stream) {
+    return route_impl(Q, q_dtype, kbar, b, h_q, h_kv, n, kbar_cap, d, B, alpha, gamma, sigma, causal, idx, bias, cnt,
+                      list_cap, w_out, top_k, nullptr, ws, ws_bytes, stream);
+}
+
+dash_status dash_route_stats(const void* Q, int q_dtype, const float* kbar,
+                             int b, int h_q, int h_kv, int n, int kbar_cap, int d, int B,
+                             float alpha, float gamma, float sigma, int causal,
+                             int32_t* idx, float* bias, int32_t* cnt, int list_cap,
+                             float* w_out, float* stats, void* ws, size_t ws_bytes, void* stream) {
+    if (!stats) return fail(DASH_ERR_NULL, "stats must be non-null");
+    return route_impl(Q, q_dtype, kbar, b, h_q, h_kv, n, kbar_cap, d, B, alpha, gamma, sigma, causal, idx, bias, cnt,
+                      list_cap, w_out, 0, stats, ws, ws_bytes, stream);
 }
 
 dash_status dash_route(const void* Q, int q_dtype, const float* kbar,
@@ -168,6 +187,39 @@ dash_status dash_route(const void* Q, int q_dtype, const float* kbar,
                        float* w_out, void* ws, size_t ws_bytes, void* stream) {
     return dash_route_topk(Q, q_dtype, kbar, b, h_q, h_kv, n, kbar_cap, d, B, alpha, gamma, sigma, causal, idx,
                            bias, cnt, list_cap, w_out, 0, ws, ws_bytes, stream);
+}
+
+dash_status dash_route_backward(const void* Q, int q_dtype, const float* kbar, int kbar_cap,
+                                const int32_t* idx, const int32_t* cnt, const float* dbias, int list_cap,
+                                const float* stats, int b, int h_q, int h_kv, int n, int d, int B,
+                                float alpha, float gamma, float sigma, float* dQ, float* dkbar, void* stream) {
+    if (!Q || !kbar || !idx || !cnt || !dbias || !stats || !dQ || !dkbar)
+        return fail(DASH_ERR_NULL, "every tensor argument of the routing backward must be non-null");
+    if (!valid_dtype(q_dtype)) return fail(DASH_ERR_PARAM, "bad Q dtype %d", q_dtype);
+    dash_status st = check_common(b, h_q, h_kv, d, B);
+    if (st != DASH_OK) return st;
+    if ((st = check_params(alpha, gamma, sigma)) != DASH_OK) return st;
+    if (n < 0) return fail(DASH_ERR_SHAPE, "n must be >= 0");
+    const int T = n / B;
+    if (kbar_cap < T) return fail(DASH_ERR_SHAPE, "kbar_cap %d < floor(n/B) = %d", kbar_cap, T);
+    if (list_cap < T) return fail(DASH_ERR_SHAPE, "list_cap %d < floor(n/B) = %d", list_cap, T);
+    dash::RouteBwdArgs a{Q, q_dtype == DASH_BF16, kbar, kbar_cap, idx, cnt, dbias, list_cap, stats,
+                         b, h_q, h_kv, n, d, B, alpha, gamma, sigma, dQ, dkbar};
+    return from_hip(dash::launch_route_backward(a, (hipStream_t)stream), "route_backward_kernel");
+}
+
+dash_status dash_summarize_backward(const void* K, int k_dtype, const float* qbar, const float* dkbar,
+                                    int b, int h_kv, int n, int kbar_cap, int d, int B,
+                                    float* dK, float* dqbar, void* stream) {
+    if (!K || !qbar || !dkbar || !dK || !dqbar)
+        return fail(DASH_ERR_NULL, "K, qbar, dkbar, dK and dqbar must be non-null");
+    if (!valid_dtype(k_dtype)) return fail(DASH_ERR_PARAM, "bad K dtype %d", k_dtype);
+    dash_status st = check_common(b, h_kv, h_kv, d, B);
+    if (st != DASH_OK) return st;
+    if (n < 0) return fail(DASH_ERR_SHAPE, "n must be >= 0");
+    if (kbar_cap < n / B) return fail(DASH_ERR_SHAPE, "kbar_cap %d < floor(n/B) = %d", kbar_cap, n / B);
+    dash::SumBwdArgs a{K, k_dtype == DASH_BF16, qbar, dkbar, b, h_kv, n, kbar_cap, d, B, dK, dqbar};
+    return from_hip(dash::launch_summary_backward(a, (hipStream_t)stream), "summary_backward_kernel");
 }
 
 dash_status dash_route_mask(const int32_t* idx, const int32_t* cnt, int b, int h_kv, int n, int list_cap,

@@ -25,6 +25,7 @@ struct RouteArgs {
     int32_t* idx; float* bias; int32_t* cnt; float* w_out;
     void* ws;            // bf16 queries: split summaries, route_workspace_bytes
     int top_k;           // > 0: fixed budget of routed chunks per row
+    float* stats = nullptr;  // optional [b, h_q, n, 2]: max raw logit, threshold
 };
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
 // Routed lists -> bitpacked mask [rows][words] (bit c%32 of word c/32 = chunk c routed).
@@ -63,6 +64,23 @@ struct PrefillBwdArgs {
     void* ws;            // K transposed, prefill_workspace_bytes
 };
 hipError_t launch_attend_prefill_backward(const PrefillBwdArgs& a, hipStream_t s);
+// Backward of Stage 1 (route_backward.hip): dQ and dkbar accumulate (+=).
+struct RouteBwdArgs {
+    const void* Q; bool q_bf16; const float* kbar; int kbar_cap;
+    const int32_t* idx; const int32_t* cnt; const float* dbias; int list_cap; const float* stats;
+    int b, h_q, h_kv, n, d, B;
+    float alpha, gamma, sigma;
+    float* dQ; float* dkbar;
+};
+hipError_t launch_route_backward(const RouteBwdArgs& a, hipStream_t s);
+// Backward of Stage 0 (route_backward.hip): dK and dqbar accumulate (+=).
+struct SumBwdArgs {
+    const void* K; bool k_bf16; const float* qbar; const float* dkbar;
+    int b, h_kv, n, kbar_cap, d, B;
+    float* dK; float* dqbar;
+};
+hipError_t launch_summary_backward(const SumBwdArgs& a, hipStream_t s);
+
 // Rows per backward query tile for group size g at T_c chunks (0: unsupported).
 int backward_tile_rows(int g, int B, int T_c, int d);
 // Workspace of the backward: K^T per KV head, a bf16 dO, Δ and the inverted routed

@@ -73,6 +73,7 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
     p.inv_sigma = isinf(a.sigma) ? 0.f : (float)(1.0 / (double)a.sigma);
     p.ksplit = static_cast<const uint8_t*>(a.ws);
     p.top_k = a.top_k;
+    p.stats = a.stats;
     p.T_pad = (p.T_c + 31) / 32 * 32;
     if (a.n == 0) return hipSuccess;
     if (a.q_bf16) {

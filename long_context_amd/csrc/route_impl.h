@@ -42,6 +42,8 @@ struct RouteParams {
     int pmode;          // 1, 2, 4 for integer exponents, 0 otherwise, kSoftmaxRouting for α = 1
     float inv_sigma;    // 1/σ (0 for σ = inf)
     int top_k;          // > 0: keep only the top_k largest group weights of each row
+    float* stats;       // nullable [b, h_q, n, 2]: max raw logit and the threshold
+                        // (τ; α = 1: log2 Σ 2^y) of each (head, row)
 };
 
 // Order-preserving map of a float to an unsigned key (larger float, larger key).
@@ -475,6 +477,11 @@ __global__ __launch_bounds__(512) void entmax_route_kernel(RouteParams p) {
                 for (int k = 0; k < CW; ++k) se += buf[(k * 16 + n16) * 2];
             }
             const float lse = fast_log2(se);
+            if (p.stats && kg == 0 && cw == 0 && wave_live && row_ok) {
+                float* so = p.stats + 2 * (((size_t)bi * p.h_q + my_head) * p.n + my_row);
+                so[0] = smax;
+                so[1] = lse;
+            }
             const float lg_g = (float)lg;
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
@@ -495,6 +502,11 @@ __global__ __launch_bounds__(512) void entmax_route_kernel(RouteParams p) {
         float tau;
         if constexpr (CW == 1) tau = solve_tau<NT, PM>(sv, nt, p.pexp, row_ok && wave_live);
         else tau = solve_tau_split<NT, PM, CW>(sv, nt, p.pexp, row_ok && wave_live, xsum, G, gid, cw, n16, kg);
+        if (p.stats && kg == 0 && cw == 0 && wave_live && row_ok) {
+            float* so = p.stats + 2 * (((size_t)bi * p.h_q + my_head) * p.n + my_row);
+            so[0] = smax;
+            so[1] = tau;
+        }
         // per-head weights, then the group average across the g lanes of each row
         const float inv_g = 1.f / (float)g;
 #pragma unroll

@@ -37,6 +37,14 @@ def _load():
     lib.dash_route_topk.argtypes = [vp, i32, vp, i32, i32, i32, i32, i32, i32, i32, f32, f32, f32, i32,
                                     vp, vp, vp, i32, vp, i32, vp, sz, vp]
     lib.dash_route_topk.restype = i32
+    lib.dash_route_stats.argtypes = [vp, i32, vp, i32, i32, i32, i32, i32, i32, i32, f32, f32, f32, i32,
+                                     vp, vp, vp, i32, vp, vp, vp, sz, vp]
+    lib.dash_route_stats.restype = i32
+    lib.dash_route_backward.argtypes = [vp, i32, vp, i32, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32,
+                                        f32, f32, f32, vp, vp, vp]
+    lib.dash_route_backward.restype = i32
+    lib.dash_summarize_backward.argtypes = [vp, i32, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp, vp]
+    lib.dash_summarize_backward.restype = i32
     lib.dash_route_mask.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, i32, vp]
     lib.dash_route_mask.restype = i32
     lib.dash_attend_prefill.argtypes = [vp, vp, vp, i32, vp, vp, vp, i32, vp, i32,
@@ -68,7 +76,8 @@ def _load():
 
 lib = _load()
 
-SYMBOLS = ("dash_summarize", "dash_summarize_paged", "dash_route", "dash_route_topk", "dash_route_mask",
+SYMBOLS = ("dash_summarize", "dash_summarize_paged", "dash_summarize_backward", "dash_route", "dash_route_topk",
+           "dash_route_stats", "dash_route_backward", "dash_route_mask",
            "dash_attend_prefill", "dash_attend_prefill_lse", "dash_attend_prefill_backward",
            "dash_attend_decode", "dash_attend_decode_paged",
            "dash_workspace_bytes", "dash_status_string", "dash_last_error")
@@ -142,6 +151,36 @@ def dash_route(Q, kbar, B, alpha, gamma, sigma, causal, idx, bias, cnt, w_out=No
         _check(lib.dash_route_topk(*args, int(top_k), *tail))
     else:
         _check(lib.dash_route(*args, *tail))
+
+
+def dash_route_stats(Q, kbar, B, alpha, gamma, sigma, causal, idx, bias, cnt, stats, w_out=None,
+                     ws=None, stream=None):
+    """dash_route that also writes stats [b,h_q,n,2] (max raw logit, threshold)."""
+    b, h_q, n, d = Q.shape
+    h_kv = kbar.shape[1]
+    if ws is None and Q.dtype == torch.bfloat16:
+        ws = alloc_route_ws(b, h_q, h_kv, n, d, B, device=Q.device)
+    _check(lib.dash_route_stats(_ptr(Q), _dtype(Q), _ptr(kbar), b, h_q, h_kv, n, kbar.shape[2], d, B,
+                                float(alpha), float(gamma), float(sigma), int(causal),
+                                _ptr(idx), _ptr(bias), _ptr(cnt), idx.shape[-1], _ptr(w_out), _ptr(stats),
+                                _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def dash_route_backward(Q, kbar, idx, cnt, dbias, stats, B, alpha, gamma, sigma, dQ, dkbar, stream=None):
+    """Stage-1 backward: adds the routing path's gradients to dQ [b,h_q,n,d] and dkbar."""
+    b, h_q, n, d = Q.shape
+    h_kv = kbar.shape[1]
+    _check(lib.dash_route_backward(_ptr(Q), _dtype(Q), _ptr(kbar), kbar.shape[2], _ptr(idx), _ptr(cnt),
+                                   _ptr(dbias), idx.shape[-1], _ptr(stats), b, h_q, h_kv, n, d, B,
+                                   float(alpha), float(gamma), float(sigma), _ptr(dQ), _ptr(dkbar),
+                                   _stream(stream)))
+
+
+def dash_summarize_backward(K, qbar, dkbar, B, dK, dqbar, stream=None):
+    """Stage-0 backward: adds to dK [b,h_kv,n,d] and dqbar [h_kv,d] for dkbar."""
+    b, h_kv, n, d = K.shape
+    _check(lib.dash_summarize_backward(_ptr(K), _dtype(K), _ptr(qbar), _ptr(dkbar), b, h_kv, n, dkbar.shape[2],
+                                       d, B, _ptr(dK), _ptr(dqbar), _stream(stream)))
 
 
 def dash_route_mask(idx, cnt, T_c, mask, stream=None):

@@ -254,3 +254,43 @@ def test_prefill_lse_validation(dash):
     assert dash.lib.dash_attend_prefill_lse(*args, NUL, 0, NUL) == dash.DASH_ERR_WORKSPACE
     args = (P, P, P, 1, P, P, P, 3, P, 0, NUL, 1, 4, 2, 256, 128, 64, 1)
     assert dash.lib.dash_attend_prefill_lse(*args, P, 1 << 30, NUL) == dash.DASH_ERR_SHAPE
+
+
+def _route_bwd(dash, **kw):
+    a = dict(Q=P, qdt=1, kbar=P, kcap=4, idx=P, cnt=P, dbias=P, cap=4, stats=P, b=1, h_q=16, h_kv=2, n=256,
+             d=128, B=64, alpha=1.5, gamma=1.0, sigma=1.0, dQ=P, dkbar=P)
+    a.update(kw)
+    return dash.lib.dash_route_backward(a["Q"], a["qdt"], a["kbar"], a["kcap"], a["idx"], a["cnt"], a["dbias"],
+                                        a["cap"], a["stats"], a["b"], a["h_q"], a["h_kv"], a["n"], a["d"],
+                                        a["B"], a["alpha"], a["gamma"], a["sigma"], a["dQ"], a["dkbar"], NUL)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(stats=NUL), 1), (dict(dbias=NUL), 1), (dict(dkbar=NUL), 1), (dict(dQ=NUL), 1),
+    (dict(qdt=5), 3), (dict(alpha=0.5), 3), (dict(gamma=0.0), 3), (dict(sigma=-1.0), 3),
+    (dict(kcap=3), 2), (dict(cap=3), 2), (dict(n=-1), 2), (dict(h_q=15), 2),
+    (dict(h_q=64), 4), (dict(d=96), 4),
+])
+def test_route_backward_validation(dash, kw, status):
+    assert _route_bwd(dash, **kw) == status
+    assert dash.lib.dash_last_error().decode() != ""
+
+
+def _sum_bwd(dash, **kw):
+    a = dict(K=P, kdt=1, qbar=P, dkbar=P, b=1, h_kv=2, n=256, kcap=4, d=128, B=64, dK=P, dqbar=P)
+    a.update(kw)
+    return dash.lib.dash_summarize_backward(a["K"], a["kdt"], a["qbar"], a["dkbar"], a["b"], a["h_kv"], a["n"],
+                                            a["kcap"], a["d"], a["B"], a["dK"], a["dqbar"], NUL)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(K=NUL), 1), (dict(dkbar=NUL), 1), (dict(dqbar=NUL), 1), (dict(kdt=7), 3),
+    (dict(kcap=3), 2), (dict(n=-5), 2), (dict(b=0), 2), (dict(d=80), 4), (dict(B=24), 4),
+])
+def test_summarize_backward_validation(dash, kw, status):
+    assert _sum_bwd(dash, **kw) == status
+
+
+def test_route_stats_needs_stats(dash):
+    args = (P, 0, P, 1, 8, 2, 256, 4, 64, 64, 1.5, 1.0, 1.0, 1, P, P, P, 4, NUL)
+    assert dash.lib.dash_route_stats(*args, NUL, NUL, 0, NUL) == dash.DASH_ERR_NULL

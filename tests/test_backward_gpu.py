@@ -42,6 +42,11 @@ def _log(msg):
     print(msg, flush=True)
 
 
+def _gu():
+    from tests import gpu_util
+    return gpu_util
+
+
 def lists_from_support(support, bias_dense, cap):
     b, hkv, n, T = support.shape
     idx = np.zeros((b, hkv, n, cap), np.int32)
@@ -209,3 +214,222 @@ def test_backward_32k_clusters_full_size():
                dK=dK[:, :, tail].cpu().numpy(), dV=dV[:, :, tail].cpu().numpy(), dbias=db[:, :, ri].cpu().numpy())
     ref = dict(ref, dK=ref["dK"][:, :, tail], dV=ref["dV"][:, :, tail])
     check_grads(got, ref, li, lc, tag="32k")
+
+
+# ------------------------------------------------------------------------------------
+# Stage 1 and Stage 0 backward, and the whole chain
+# ------------------------------------------------------------------------------------
+# fp32 arithmetic on exact inputs: relative L2 <= 1e-4 and per row
+# max |Δ| <= 1e-3 (rms of the row + rms of the tensor) (fp32 sums of ~10^2 terms sit
+# near 1e-6 relative; the threshold ŵ = t^(1/(α-1)) amplifies the error of a small t,
+# but only on weights near zero).
+TOL_F32_L2 = 1e-4
+TOL_F32_ROW = 1e-3
+
+
+def _rel(g, r, tol_l2, tol_row, name):
+    g = np.asarray(g, np.float64)
+    r = np.asarray(r, np.float64)
+    assert np.isfinite(g).all(), f"{name}: non-finite"
+    l2 = np.linalg.norm(g - r) / max(np.linalg.norm(r), 1e-30)
+    rms_all = np.sqrt((r ** 2).mean())
+    rms_row = np.sqrt((r ** 2).mean(-1))
+    row = (np.abs(g - r).max(-1) / (rms_all + rms_row + 1e-30)).max()
+    _log(f"  {name}: l2 {l2:.2e} row {row:.2e}")
+    assert l2 <= tol_l2, f"{name}: relative L2 error {l2}"
+    assert row <= tol_row, f"{name}: per-row error {row}"
+
+
+@pytest.mark.parametrize("dtype,d,B,n", [("f32", 64, 16, 200), ("bf16", 128, 64, 520), ("bf16", 64, 32, 96)])
+def test_summary_backward_matches_oracle(dtype, d, B, n):
+    from long_context_amd import dash
+    from oracle import dash_oracle as O
+    w = inputs.make_prefill(b=2, h_q=2, h_kv=2, d=d, n=n, B=B, dtype=dtype, seed=8)
+    T = n // B
+    dkb = inputs.upstream_grad((2, 2, T + 2, d), seed=9)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    K = torch.from_numpy(w.K).to("cuda", tdt)
+    dK = torch.zeros((2, 2, n, d), device="cuda")
+    dq = torch.zeros((2, d), device="cuda")
+    dash.dash_summarize_backward(K, torch.from_numpy(w.qbar).cuda(), torch.from_numpy(dkb).cuda(), B, dK, dq)
+    torch.cuda.synchronize()
+    ref = O.summary_backward(w.K, w.qbar, B, dkb[:, :, :T])
+    _log(f"summary backward {dtype} d={d} B={B} n={n}")
+    _rel(dK.cpu().numpy(), ref["dK"], TOL_F32_L2, TOL_F32_ROW, "dK")
+    _rel(dq.cpu().numpy(), ref["dqbar"], TOL_F32_L2, TOL_F32_ROW, "dqbar")
+    assert np.all(dK[:, :, T * B:].cpu().numpy() == 0)      # the partial chunk has no summary
+
+
+ROUTE_BWD = [
+    # dtype, b, h_q, h_kv, d, n, B, alpha, gamma, sigma, causal, seed
+    ("f32", 1, 1, 1, 64, 512, 32, 1.5, 6.0, 1.0, True, 10),
+    ("bf16", 2, 16, 2, 128, 600, 64, 1.5, 8.0, 1.0, True, 10),       # GQA 8
+    ("bf16", 1, 32, 2, 128, 384, 64, 2.0, 4.0, 0.5, True, 11),       # GQA 16, sparsemax
+    ("bf16", 1, 8, 2, 64, 400, 32, 1.0, 2.0, 1.0, True, 10),         # softmax routing
+    ("f32", 1, 8, 2, 64, 448, 32, 1.25, 6.0, 2.0, False, 10),        # non-causal
+]
+
+# The routing gradient is ill-conditioned near the edge of a head's support: with
+# t = x - τ > 0 the weight is ŵ = t^(1/(α-1)) and ∂ log ŵ/∂x = 1/((α-1) t), so a row
+# whose routed chunks all sit just above the threshold turns the fp32 rounding of x
+# and τ into a large relative error of its gradient. The tolerance therefore scales
+# with the oracle's own sensitivity: per row (and for the tensor's L2), at most
+# PERTURB_FACTOR times the largest change of the float64 gradient under three random
+# relative perturbations of k̄ by 2^-23 (one fp32 unit), plus a floor of 1e-5 of the
+# row's and tensor's rms. The kernel's x comes from fp32 dot products of at most 128
+# terms and its τ from an fp32 threshold search, together well under 2^6 units.
+PERTURB_FACTOR = 64.0
+
+
+def _spread(fn, kb, reps=3):
+    ref = fn(kb)
+    rng = np.random.default_rng(1234)
+    out = {k: (np.zeros(v.shape[:-1]), 0.0) for k, v in ref.items()}
+    for _ in range(reps):
+        pr = fn(kb * (1.0 + 2.0 ** -23 * rng.standard_normal(kb.shape)))
+        for k, v in ref.items():
+            row, l2 = out[k]
+            out[k] = (np.maximum(row, np.abs(pr[k] - v).max(-1)), max(l2, np.linalg.norm(pr[k] - v)))
+    return ref, out
+
+
+def _check_cond(g, r, spread, name):
+    g = np.asarray(g, np.float64)
+    assert np.isfinite(g).all(), f"{name}: non-finite"
+    row_sp, l2_sp = spread
+    rms_all = np.sqrt((r ** 2).mean())
+    rms_row = np.sqrt((r ** 2).mean(-1))
+    err = np.abs(g - r).max(-1)
+    tol = PERTURB_FACTOR * row_sp + 1e-5 * (rms_row + rms_all)
+    l2 = np.linalg.norm(g - r)
+    l2_tol = PERTURB_FACTOR * l2_sp + 1e-5 * np.linalg.norm(r)
+    k = np.unravel_index(np.argmax(err / tol), err.shape)
+    _log(f"  {name}: worst row {k} err {err[k]:.2e} tol {tol[k]:.2e} (spread {row_sp[k]:.2e}); "
+         f"l2 {l2 / np.linalg.norm(r):.2e} tol {l2_tol / np.linalg.norm(r):.2e}")
+    assert np.all(err <= tol), f"{name}: row {k} error {err[k]} above {tol[k]}"
+    assert l2 <= l2_tol, f"{name}: L2 error {l2} above {l2_tol}"
+
+
+@pytest.mark.parametrize("case", ROUTE_BWD, ids=[f"{c[0]}-g{c[2] // c[3]}-a{c[7]}-c{int(c[10])}" for c in ROUTE_BWD])
+def test_route_backward_matches_oracle(case):
+    """Stage-1 backward through the C ABI against the oracle: the GPU's own routing
+    (lists and statistics of dash_route_stats), one dense upstream gradient of the
+    bias read at the routed entries; every row's support must agree with the oracle's
+    (no row within the exemption margin), since dk̄ sums over all rows."""
+    from long_context_amd import dash
+    from oracle import dash_oracle as O
+    G = _gu()
+    dtype, b, hq, hkv, d, n, B, alpha, gamma, sigma, causal, seed = case
+    _log(f"route backward case {case}")
+    w = inputs.make_prefill(b=b, h_q=hq, h_kv=hkv, d=d, n=n, B=B, dtype=dtype, seed=seed)
+    T = n // B
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    Q = torch.from_numpy(w.Q).to("cuda", tdt)
+    K = torch.from_numpy(w.K).to("cuda", tdt)
+    kbar = dash.alloc_kbar(b, hkv, T, d)
+    dash.dash_summarize(K, torch.from_numpy(w.qbar).cuda(), kbar, B)
+    idx, bias, cnt, _ = dash.alloc_route(b, hkv, n, T)
+    stats = torch.empty((b, hq, n, 2), device="cuda")
+    dash.dash_route_stats(Q, kbar, B, alpha, gamma, sigma, causal, idx, bias, cnt, stats)
+    torch.cuda.synchronize()
+    dense = inputs.upstream_grad((b, hkv, n, T), seed=12)
+    ii = idx.cpu().numpy().astype(np.int64)
+    cc = cnt.cpu().numpy()
+    live = np.arange(ii.shape[-1])[None, None, None, :] < cc[..., None]
+    dlist = np.where(live, np.take_along_axis(dense, np.where(live, ii, 0), -1), 0.0).astype(np.float32)
+    dQ = torch.zeros((b, hq, n, d), device="cuda")
+    dkb = torch.zeros((b, hkv, T, d), device="cuda")
+    dash.dash_route_backward(Q, kbar, idx, cnt, torch.from_numpy(dlist).cuda(), stats, B, alpha, gamma, sigma,
+                             dQ, dkb)
+    torch.cuda.synchronize()
+    pos = np.broadcast_to(np.arange(n), (b, n))
+    kb_or = O.stage0_summaries(w.K, w.qbar, B)
+    rt = O.route(w.Q, pos, kb_or, B, alpha, gamma, sigma, causal, n)
+    assert not G.exempt_rows(rt).any(), "a row sits within the exemption margin: choose another seed"
+    G.compare_route(dict(idx=idx, cnt=cnt), rt, np.arange(n), T)
+    db = np.where(rt["support"], dense, 0.0)
+    ref, spread = _spread(lambda kb: O.route_backward(w.Q, pos, kb, B, alpha, gamma, sigma, causal, n, db), kb_or)
+    _check_cond(dQ.cpu().numpy(), ref["dQ"], spread["dQ"], "dQ (routing)")
+    _check_cond(dkb.cpu().numpy(), ref["dkbar"], spread["dkbar"], "dkbar")
+
+
+# In the chain, Stage 1 takes the Stage-2 dbias with its bf16-level error, and the
+# routing Jacobian scales a chunk's gradient by 1/w (w its group weight), so a chunk
+# routed with a tiny weight magnifies that error. The chain tolerance adds the
+# propagated part: CHAIN_FACTOR times the largest change of the oracle's Stage-1 and
+# Stage-0 gradients when its dbias takes three random errors of 2^-8 (|db| + rms db)
+# per entry, the Stage-2 tolerance on dbias as a whole.
+CHAIN_FACTOR = 4.0
+
+
+@pytest.mark.parametrize("causal,alpha", [(True, 1.5), (False, 2.0)])
+def test_full_backward_chain_matches_oracle(causal, alpha):
+    """The whole backward through the C ABI (Stage 2, then Stage 1 adding to dQ and
+    dk̄, then Stage 0 adding to dK and dq̄) after the GPU forward, against the oracle's
+    chained backward on the same inputs."""
+    from long_context_amd import dash
+    from oracle import dash_oracle as O
+    G = _gu()
+    b, hq, hkv, d, n, B, gamma, sigma = 1, 16, 2, 128, 384, 64, 4.0, 1.0
+    w = inputs.make_prefill(b=b, h_q=hq, h_kv=hkv, d=d, n=n, B=B, dtype="bf16", seed=14)
+    T = n // B
+    dev = lambda x, dt: torch.from_numpy(np.ascontiguousarray(x)).to("cuda", dt)
+    Q, K, V = (dev(x, torch.bfloat16) for x in (w.Q, w.K, w.V))
+    qbar = dev(w.qbar, torch.float32)
+    kbar = dash.alloc_kbar(b, hkv, T, d)
+    dash.dash_summarize(K, qbar, kbar, B)
+    idx, bias, cnt, _ = dash.alloc_route(b, hkv, n, T)
+    stats = torch.empty((b, hq, n, 2), device="cuda")
+    dash.dash_route_stats(Q, kbar, B, alpha, gamma, sigma, causal, idx, bias, cnt, stats)
+    Og = torch.empty((b, hq, n, d), device="cuda")
+    lse = torch.empty((b, hq, n), device="cuda")
+    dash.dash_attend_prefill_lse(Q, K, V, idx, bias, cnt, Og, lse, B, causal)
+    dO = inputs.upstream_grad((b, hq, n, d), seed=15, dtype="bf16")
+    dQ = torch.empty((b, hq, n, d), device="cuda")
+    dK = torch.empty((b, hkv, n, d), device="cuda")
+    dV = torch.empty((b, hkv, n, d), device="cuda")
+    db = torch.empty(idx.shape, device="cuda")
+    dash.dash_attend_prefill_backward(Q, K, V, idx, bias, cnt, Og, dev(dO, torch.float32), lse, dQ, dK, dV, db,
+                                      B, causal)
+    dkb = torch.zeros((b, hkv, T, d), device="cuda")
+    dash.dash_route_backward(Q, kbar, idx, cnt, db, stats, B, alpha, gamma, sigma, dQ, dkb)
+    dqb = torch.zeros((hkv, d), device="cuda")
+    dash.dash_summarize_backward(K, qbar, dkb, B, dK, dqb)
+    torch.cuda.synchronize()
+    pos = np.broadcast_to(np.arange(n), (b, n))
+    kb_or = O.stage0_summaries(w.K, w.qbar, B)
+    rt = O.route(w.Q, pos, kb_or, B, alpha, gamma, sigma, causal, n)
+    assert not G.exempt_rows(rt).any(), "a row sits within the exemption margin: choose another seed"
+    G.compare_route(dict(idx=idx, cnt=cnt), rt, np.arange(n), T)
+    rt = dict(rt, bias=rt["bias"].astype(np.float32).astype(np.float64))
+    g2 = O.attend_backward(w.Q, pos, w.K, w.V, rt, B, causal, n, dO.astype(np.float64))
+    up = lambda dbias: O.route_backward(w.Q, pos, kb_or, B, alpha, gamma, sigma, causal, n, dbias)
+    g1 = up(g2["dbias"])
+    g0 = O.summary_backward(w.K, w.qbar, B, g1["dkbar"])
+    ref = dict(dQ=g2["dQ"] + g1["dQ"], dK=g2["dK"] + g0["dK"], dV=g2["dV"], dqbar=g0["dqbar"])
+    # the Stage-2 dbias error carried through Stages 1 and 0 (oracle only)
+    S = rt["support"]
+    rms_db = np.sqrt((g2["dbias"][S] ** 2).mean())
+    rng = np.random.default_rng(99)
+    spread = {k: np.zeros(v.shape) for k, v in ref.items()}
+    for _ in range(3):
+        err = 2.0 ** -8 * (np.abs(g2["dbias"]) + rms_db) * rng.standard_normal(S.shape)
+        p1 = up(np.where(S, g2["dbias"] + err, 0.0))
+        p0 = O.summary_backward(w.K, w.qbar, B, p1["dkbar"])
+        for k, v in (("dQ", p1["dQ"] - g1["dQ"]), ("dK", p0["dK"] - g0["dK"]), ("dqbar", p0["dqbar"] - g0["dqbar"])):
+            spread[k] = np.maximum(spread[k], np.abs(v))
+    _log(f"full chain causal={causal} alpha={alpha}")
+    got = dict(dQ=dQ.cpu().numpy(), dK=dK.cpu().numpy(), dV=dV.cpu().numpy(), dqbar=dqb.cpu().numpy())
+    for name in ("dQ", "dK", "dV", "dqbar"):
+        g, r, sp = got[name].astype(np.float64), ref[name], spread[name]
+        assert np.isfinite(g).all(), f"{name}: non-finite"
+        rms_all = np.sqrt((r ** 2).mean())
+        rms_row = np.sqrt((r ** 2).mean(-1))
+        e = np.abs(g - r).max(-1)
+        tol = TOL_ROW * (rms_row + rms_all) + CHAIN_FACTOR * sp.max(-1)
+        l2, l2_tol = np.linalg.norm(g - r), TOL_L2 * np.linalg.norm(r) + CHAIN_FACTOR * np.linalg.norm(sp)
+        k = np.unravel_index(np.argmax(e / tol), e.shape)
+        _log(f"  {name}: worst row {k} err/(rms) {e[k] / (rms_row[k] + rms_all):.2e} tol {tol[k] / (rms_row[k] + rms_all):.2e}; "
+             f"l2 {l2 / np.linalg.norm(r):.2e} tol {l2_tol / np.linalg.norm(r):.2e}")
+        assert np.all(e <= tol), f"{name}: row {k} error {e[k]} above {tol[k]}"
+        assert l2 <= l2_tol, f"{name}: L2 error {l2} above {l2_tol}"
