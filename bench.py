@@ -45,7 +45,7 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (HBM counter calibration)")
     ap.add_argument("--backward", action="store_true",
-                    help="time the Stage-2 backward at the 32K workload instead of the forward")
+                    help="time the backward (Stages 2, 1 and 0) at the 32K workload instead of the forward")
     ap.add_argument("--efficiency", action="store_true",
                     help="only run the replicas of the pages' efficiency operating points")
     return ap.parse_args()
@@ -361,27 +361,35 @@ def efficiency(torch, dash, inputs, steps):
 
 
 def backward(torch, dash, inputs, alpha, steps, warmup, no_dense=False):
-    """Stage-2 backward at the 32K workload: the routed lists of the forward at α, the
-    forward's O and lse, an N(0,1) upstream gradient; the whole backward call timed
-    (Δ and transposes, list inversion, dQ/d(bias) kernel, dK/dV kernel). The same
-    kernels on the dense lists (every visible chunk, bias 0) give the 0%-sparsity
-    baseline. Algorithmic flops: the five products of a softmax-attention backward
-    (S, dP, dQ, dK, dV) over the pairs each row sees, 2.5x the forward's."""
+    """The backward of the whole 32K prefill at α: the routed lists and router
+    statistics of the forward, the forward's O and lse, an N(0,1) upstream gradient;
+    timed per stage: Stage 2 (Δ and transposes, list inversion, dQ/d(bias) kernel,
+    dK/dV kernel), Stage 1 (routing backward adding to dQ, into dk̄) and Stage 0
+    (summary backward adding to dK, into dq̄). The Stage-2 kernels on the dense lists
+    (every visible chunk, bias 0) are the 0%-sparsity baseline: dense attention has
+    no routing to differentiate. Algorithmic flops of Stage 2: the five products of a
+    softmax-attention backward (S, dP, dQ, dK, dV) over the pairs each row sees,
+    2.5x the forward's."""
     wp = inputs.prefill_32k_clusters()
     pre = Prefill(wp, torch, dash)
     pre.run(alpha)
-    torch.cuda.synchronize()
-    st = pre.stats()
     b, h_q, n, d = wp.Q.shape
     B, hkv = wp.B, wp.h_kv
+    stats = torch.empty((b, h_q, n, 2), device="cuda")
+    dash.dash_route_stats(pre.Q, pre.kbar, B, alpha, wp.gamma, wp.sigma, True, pre.idx, pre.bias, pre.cnt,
+                          stats, ws=pre.rws)
+    torch.cuda.synchronize()
+    st = pre.stats()
     lse = torch.empty((b, h_q, n), device="cuda")
     dO = torch.from_numpy(inputs.upstream_grad((b, h_q, n, d), seed=1, dtype="bf16")).to("cuda", torch.bfloat16)
     dQ = torch.empty((b, h_q, n, d), device="cuda")
     dK = torch.empty((b, hkv, n, d), device="cuda")
     dV = torch.empty((b, hkv, n, d), device="cuda")
+    dkb = torch.empty((b, hkv, pre.T, d), device="cuda")
+    dqb = torch.empty((hkv, d), device="cuda")
     ws = dash.alloc_backward_ws(b, h_q, hkv, n, d, B)
 
-    def timed(idx, bias, cnt):
+    def timed(idx, bias, cnt, chain):
         db = torch.empty(idx.shape, device="cuda")
         dash.dash_attend_prefill_lse(pre.Q, pre.K, pre.V, idx, bias, cnt, pre.O, lse, B, True, ws=pre.ws)
 
@@ -390,21 +398,32 @@ def backward(torch, dash, inputs, alpha, steps, warmup, no_dense=False):
             dash.dash_attend_prefill_backward(pre.Q, pre.K, pre.V, idx, bias, cnt, pre.O, dO, lse,
                                               dQ, dK, dV, db, B, True, ws=ws)
             if ev: ev[1].record()
-        seg, _ = time_events(torch, fn, 2, steps, warmup)
-        return float(seg[:, 0].mean())
+            if chain:
+                dkb.zero_()
+                dash.dash_route_backward(pre.Q, pre.kbar, idx, cnt, db, stats, B, alpha, wp.gamma, wp.sigma,
+                                         dQ, dkb, ws=pre.rws)
+                if ev: ev[2].record()
+                dqb.zero_()
+                dash.dash_summarize_backward(pre.K, pre.qbar, dkb, B, dK, dqb)
+                if ev: ev[3].record()
+        seg, _ = time_events(torch, fn, 4 if chain else 2, steps, warmup)
+        return seg.mean(0)
 
-    t = timed(pre.idx, pre.bias, pre.cnt)
+    t2, t1, t0 = (float(x) for x in timed(pre.idx, pre.bias, pre.cnt, True))
+    t = t2 + t1 + t0
     flops = 2.5 * st["flops_row"]
-    out = dict(ms=t, tflops=flops / (t * 1e-3) / 1e12, frac=flops / (t * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-               sparsity=st["sparsity"], algorithmic_tflop=flops / 1e12)
+    out = dict(ms=t, stage2_ms=t2, stage1_ms=t1, stage0_ms=t0,
+               stage2_tflops=flops / (t2 * 1e-3) / 1e12, stage2_frac=flops / (t2 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+               sparsity=st["sparsity"], stage2_algorithmic_tflop=flops / 1e12)
     print(f"[bench] backward alpha={alpha}: {out}", file=sys.stderr, flush=True)
     if no_dense:
         return out
     di, dbias, dc = dense_lists(pre, torch)
-    td = timed(di, dbias, dc)
+    td = float(timed(di, dbias, dc, False)[0])
     dense_flops = 2.5 * 4.0 * d * h_q * (n * (n + 1) / 2)
     out["dense"] = dict(ms=td, tflops=dense_flops / (td * 1e-3) / 1e12)
     out["speedup_vs_dense"] = td / t
+    out["stage2_speedup_vs_dense"] = td / t2
     return out
 
 
@@ -426,7 +445,7 @@ def main():
 
     if args.backward:
         res = backward(torch, dash, inputs, args.alpha, args.steps, args.warmup, args.no_dense)
-        print(json.dumps({"metric": "Stage-2 backward time at the 32K prefill workload", "unit": "ms",
+        print(json.dumps({"metric": "backward time at the 32K prefill workload", "unit": "ms",
                           "value": res["ms"], "higher_is_better": False, "n_gpus": 1, "steps": args.steps,
                           "warmup": args.warmup, "dtype": "bf16", "data": "synthetic",
                           "config": {"workload": "prefill_32k_clusters", "alpha": args.alpha},

@@ -144,12 +144,17 @@ dash_status dash_route_stats(const void* Q, int q_dtype, const float* kbar,
  * the α-entmax Jacobian diag(s) - s sᵀ/Σs with s = ŵ^(2-α) (α = 1: s = ŵ), and the
  * chain through <q_h, k̄_c>·γ/sqrt(d). σ = +inf: no-op. List entries outside
  * [0, floor(n/B)) are skipped. Lists of a fixed top-k budget are not supported (their
- * kept set drops chunks the entmax normalisation couples).
+ * kept set drops chunks the entmax normalisation couples). The weights are rebuilt
+ * with the router's own arithmetic, so the support seen here is the forward's. bf16
+ * queries need a device workspace of at least dash_workspace_bytes(DASH_OP_ROUTE, ...)
+ * bytes (k̄ split into bf16 terms); fp32 queries need none (ws may be NULL). Calls
+ * that share one workspace must not overlap.
  */
 dash_status dash_route_backward(const void* Q, int q_dtype, const float* kbar, int kbar_cap,
                                 const int32_t* idx, const int32_t* cnt, const float* dbias, int list_cap,
                                 const float* stats, int b, int h_q, int h_kv, int n, int d, int B,
-                                float alpha, float gamma, float sigma, float* dQ, float* dkbar, void* stream);
+                                float alpha, float gamma, float sigma, float* dQ, float* dkbar,
+                                void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Stage-0 backward (Eq. 4: k̄_c = Σ_j π_j k_j, π = softmax_j(<q̄, k_j>/sqrt(d))): for

@@ -192,7 +192,8 @@ dash_status dash_route(const void* Q, int q_dtype, const float* kbar,
 dash_status dash_route_backward(const void* Q, int q_dtype, const float* kbar, int kbar_cap,
                                 const int32_t* idx, const int32_t* cnt, const float* dbias, int list_cap,
                                 const float* stats, int b, int h_q, int h_kv, int n, int d, int B,
-                                float alpha, float gamma, float sigma, float* dQ, float* dkbar, void* stream) {
+                                float alpha, float gamma, float sigma, float* dQ, float* dkbar,
+                                void* ws, size_t ws_bytes, void* stream) {
     if (!Q || !kbar || !idx || !cnt || !dbias || !stats || !dQ || !dkbar)
         return fail(DASH_ERR_NULL, "every tensor argument of the routing backward must be non-null");
     if (!valid_dtype(q_dtype)) return fail(DASH_ERR_PARAM, "bad Q dtype %d", q_dtype);
@@ -203,8 +204,14 @@ dash_status dash_route_backward(const void* Q, int q_dtype, const float* kbar, i
     const int T = n / B;
     if (kbar_cap < T) return fail(DASH_ERR_SHAPE, "kbar_cap %d < floor(n/B) = %d", kbar_cap, T);
     if (list_cap < T) return fail(DASH_ERR_SHAPE, "list_cap %d < floor(n/B) = %d", list_cap, T);
+    if (q_dtype == DASH_BF16 && T > 0) {
+        const size_t need = dash::route_workspace_bytes(b, h_kv, T, d);
+        if (!ws || ws_bytes < need)
+            return fail(DASH_ERR_WORKSPACE, "bf16 routing backward needs %zu workspace bytes, got %zu", need,
+                        ws ? ws_bytes : (size_t)0);
+    }
     dash::RouteBwdArgs a{Q, q_dtype == DASH_BF16, kbar, kbar_cap, idx, cnt, dbias, list_cap, stats,
-                         b, h_q, h_kv, n, d, B, alpha, gamma, sigma, dQ, dkbar};
+                         b, h_q, h_kv, n, d, B, alpha, gamma, sigma, dQ, dkbar, ws};
     return from_hip(dash::launch_route_backward(a, (hipStream_t)stream), "route_backward_kernel");
 }
 

@@ -33,6 +33,11 @@ hipError_t launch_lists_to_mask(const int32_t* idx, const int32_t* cnt, size_t r
                                 uint32_t* mask, int words, hipStream_t s);
 // Scale of the routing logits: (α-1)γ/sqrt(d) for entmax, γ log2(e)/sqrt(d) for α = 1.
 float route_scale(float alpha, float gamma, int d);
+int pmode_of(float alpha);
+// k̄ split into three bf16 terms in the routing kernel's staged layout (route.hip),
+// written to ws (route_workspace_bytes bytes).
+hipError_t launch_kbar_split(const float* kbar, void* ws, int b, int h_kv, int kbar_cap, int T_c, int d,
+                             hipStream_t s);
 // Workspace of a bf16-query routing: the summaries split into three bf16 terms,
 // b * h_kv * (T_c rounded up to 32) * 3 * d * 2 bytes.
 size_t route_workspace_bytes(int b, int h_kv, int T_c, int d);
@@ -71,6 +76,7 @@ struct RouteBwdArgs {
     int b, h_q, h_kv, n, d, B;
     float alpha, gamma, sigma;
     float* dQ; float* dkbar;
+    void* ws;           // bf16 queries: the split summaries (route_workspace_bytes)
 };
 hipError_t launch_route_backward(const RouteBwdArgs& a, hipStream_t s);
 // Backward of Stage 0 (route_backward.hip): dK and dqbar accumulate (+=).

@@ -50,6 +50,17 @@ static hipError_t launch_ksplit(const RouteParams& p, int b, hipStream_t s) {
     return hipGetLastError();
 }
 
+hipError_t launch_kbar_split(const float* kbar, void* ws, int b, int h_kv, int kbar_cap, int T_c, int d,
+                             hipStream_t s) {
+    if (T_c <= 0) return hipSuccess;
+    RouteParams p;
+    p.kbar = kbar;
+    p.ksplit = static_cast<const uint8_t*>(ws);
+    p.h_kv = h_kv; p.kbar_cap = kbar_cap; p.T_c = T_c;
+    p.T_pad = (T_c + 31) / 32 * 32;
+    return d == 64 ? launch_ksplit<64>(p, b, s) : launch_ksplit<128>(p, b, s);
+}
+
 int pmode_of(float alpha) {
     if (alpha == 1.0f) return kSoftmaxRouting;
     const double pe = 1.0 / ((double)alpha - 1.0);

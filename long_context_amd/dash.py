@@ -41,7 +41,7 @@ def _load():
                                      vp, vp, vp, i32, vp, vp, vp, sz, vp]
     lib.dash_route_stats.restype = i32
     lib.dash_route_backward.argtypes = [vp, i32, vp, i32, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32,
-                                        f32, f32, f32, vp, vp, vp]
+                                        f32, f32, f32, vp, vp, vp, sz, vp]
     lib.dash_route_backward.restype = i32
     lib.dash_summarize_backward.argtypes = [vp, i32, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp, vp]
     lib.dash_summarize_backward.restype = i32
@@ -166,13 +166,16 @@ def dash_route_stats(Q, kbar, B, alpha, gamma, sigma, causal, idx, bias, cnt, st
                                 _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
 
 
-def dash_route_backward(Q, kbar, idx, cnt, dbias, stats, B, alpha, gamma, sigma, dQ, dkbar, stream=None):
+def dash_route_backward(Q, kbar, idx, cnt, dbias, stats, B, alpha, gamma, sigma, dQ, dkbar, ws=None, stream=None):
     """Stage-1 backward: adds the routing path's gradients to dQ [b,h_q,n,d] and dkbar."""
     b, h_q, n, d = Q.shape
     h_kv = kbar.shape[1]
+    if ws is None and Q.dtype == torch.bfloat16:
+        ws = alloc_route_ws(b, h_q, h_kv, n, d, B, device=Q.device)
     _check(lib.dash_route_backward(_ptr(Q), _dtype(Q), _ptr(kbar), kbar.shape[2], _ptr(idx), _ptr(cnt),
                                    _ptr(dbias), idx.shape[-1], _ptr(stats), b, h_q, h_kv, n, d, B,
                                    float(alpha), float(gamma), float(sigma), _ptr(dQ), _ptr(dkbar),
+                                   _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
                                    _stream(stream)))
 
 

@@ -258,11 +258,12 @@ def test_prefill_lse_validation(dash):
 
 def _route_bwd(dash, **kw):
     a = dict(Q=P, qdt=1, kbar=P, kcap=4, idx=P, cnt=P, dbias=P, cap=4, stats=P, b=1, h_q=16, h_kv=2, n=256,
-             d=128, B=64, alpha=1.5, gamma=1.0, sigma=1.0, dQ=P, dkbar=P)
+             d=128, B=64, alpha=1.5, gamma=1.0, sigma=1.0, dQ=P, dkbar=P, ws=P, ws_bytes=1 << 30)
     a.update(kw)
     return dash.lib.dash_route_backward(a["Q"], a["qdt"], a["kbar"], a["kcap"], a["idx"], a["cnt"], a["dbias"],
                                         a["cap"], a["stats"], a["b"], a["h_q"], a["h_kv"], a["n"], a["d"],
-                                        a["B"], a["alpha"], a["gamma"], a["sigma"], a["dQ"], a["dkbar"], NUL)
+                                        a["B"], a["alpha"], a["gamma"], a["sigma"], a["dQ"], a["dkbar"],
+                                        a["ws"], a["ws_bytes"], NUL)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -270,6 +271,7 @@ def _route_bwd(dash, **kw):
     (dict(qdt=5), 3), (dict(alpha=0.5), 3), (dict(gamma=0.0), 3), (dict(sigma=-1.0), 3),
     (dict(kcap=3), 2), (dict(cap=3), 2), (dict(n=-1), 2), (dict(h_q=15), 2),
     (dict(h_q=64), 4), (dict(d=96), 4),
+    (dict(ws=NUL), 5), (dict(ws_bytes=1024), 5),            # bf16 queries need the split summaries
 ])
 def test_route_backward_validation(dash, kw, status):
     assert _route_bwd(dash, **kw) == status
@@ -289,6 +291,13 @@ def _sum_bwd(dash, **kw):
 ])
 def test_summarize_backward_validation(dash, kw, status):
     assert _sum_bwd(dash, **kw) == status
+
+
+def test_route_backward_workspace(dash):
+    need = dash.dash_workspace_bytes(dash.DASH_OP_ROUTE, 1, 16, 2, 256, 128, 64)
+    assert _route_bwd(dash, ws_bytes=need - 1) == dash.DASH_ERR_WORKSPACE
+    # fp32 queries need no workspace; validation then fails only on the shape given
+    assert _route_bwd(dash, qdt=0, ws=NUL, ws_bytes=0, kcap=3) == dash.DASH_ERR_SHAPE
 
 
 def test_route_stats_needs_stats(dash):
