@@ -623,33 +623,42 @@ constexpr size_t dkv_item_lds_bytes() {
     return (size_t)DkvStage<D>::NST * DkvStage<D>::BYTES + 3 * 128 * 4 + (8 + 8 + 4 + 4) * 64 * 4;
 }
 
-// One work item: 64 tokens of one chunk (tile cs) of KV group bhk against segment
-// seg of its row sequence.
-// The 16 transposing reads of k16 step s for d = 128 from two per-lane bases. In the
-// swizzled [64][128] tiles the byte offset of read (db, t) of a lane is
-//   L + 4096 s + 1024 t + 64 (db ^ (2 hl + t)),
-// and 64 (u ^ 2 hl) with u = db ^ t equals 64 u + 128 hl for u < 2 and 64 u - 128 hl
-// otherwise, so with a = L + 128 hl and b = L - 128 hl every offset is an immediate.
-// Reads 0..7: the dO tile (at +16384), 8..15: the Q tile; read 2 db + t.
+// Piece slot of the Q and dO tiles of the dK/dV kernel: 16-byte piece c of row t sits
+// at slot c ^ swz(t). At d = 128 swz swaps the two 2-bit halves of t mod 16: the 16
+// rows of a row read still fill 16 distinct slots, and the 4 rows x 4 pieces of a
+// transposing read do too (with t mod 16 itself they fold onto 4 slots, four lanes'
+// words per bank).
+template <int D>
+__device__ __forceinline__ int dkv_slot(int t, int c) {
+    if constexpr (D == 128) return c ^ (((t & 3) << 2) | ((t >> 2) & 3));
+    else return BfTiles<D, 64>::kslot(t, c);
+}
+
+// The 16 transposing reads of k16 step S at d = 128, read (db, t) from its own
+// per-lane address a[2 db + t] (the Q tile; the dO tile is 16 KiB above, step S at
+// +4096 S, both immediates). Reads 0..7: dO, 8..15: Q.
 template <int S>
-__device__ __forceinline__ void tr_reads_d128(uint32_t a, uint32_t b, i16x4 (&r)[16]) {
+__device__ __forceinline__ void tr_reads_d128_sw(const uint32_t (&a)[8], i16x4 (&r)[16]) {
     asm volatile(
-        "ds_read_b64_tr_b16 %0, %16 offset:%18\n ds_read_b64_tr_b16 %1, %16 offset:%18+1088\n"
-        "ds_read_b64_tr_b16 %2, %16 offset:%18+64\n ds_read_b64_tr_b16 %3, %16 offset:%18+1024\n"
-        "ds_read_b64_tr_b16 %4, %17 offset:%18+128\n ds_read_b64_tr_b16 %5, %17 offset:%18+1216\n"
-        "ds_read_b64_tr_b16 %6, %17 offset:%18+192\n ds_read_b64_tr_b16 %7, %17 offset:%18+1152\n"
-        "ds_read_b64_tr_b16 %8, %16 offset:%19\n ds_read_b64_tr_b16 %9, %16 offset:%19+1088\n"
-        "ds_read_b64_tr_b16 %10, %16 offset:%19+64\n ds_read_b64_tr_b16 %11, %16 offset:%19+1024\n"
-        "ds_read_b64_tr_b16 %12, %17 offset:%19+128\n ds_read_b64_tr_b16 %13, %17 offset:%19+1216\n"
-        "ds_read_b64_tr_b16 %14, %17 offset:%19+192\n ds_read_b64_tr_b16 %15, %17 offset:%19+1152\n"
+        "ds_read_b64_tr_b16 %0, %16 offset:%24\n ds_read_b64_tr_b16 %1, %17 offset:%24\n"
+        "ds_read_b64_tr_b16 %2, %18 offset:%24\n ds_read_b64_tr_b16 %3, %19 offset:%24\n"
+        "ds_read_b64_tr_b16 %4, %20 offset:%24\n ds_read_b64_tr_b16 %5, %21 offset:%24\n"
+        "ds_read_b64_tr_b16 %6, %22 offset:%24\n ds_read_b64_tr_b16 %7, %23 offset:%24\n"
+        "ds_read_b64_tr_b16 %8, %16 offset:%25\n ds_read_b64_tr_b16 %9, %17 offset:%25\n"
+        "ds_read_b64_tr_b16 %10, %18 offset:%25\n ds_read_b64_tr_b16 %11, %19 offset:%25\n"
+        "ds_read_b64_tr_b16 %12, %20 offset:%25\n ds_read_b64_tr_b16 %13, %21 offset:%25\n"
+        "ds_read_b64_tr_b16 %14, %22 offset:%25\n ds_read_b64_tr_b16 %15, %23 offset:%25\n"
         "s_waitcnt lgkmcnt(0)"
         : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]),
           "=&v"(r[7]), "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11]), "=&v"(r[12]), "=&v"(r[13]),
           "=&v"(r[14]), "=&v"(r[15])
-        : "v"(a), "v"(b), "n"(16384 + 4096 * S), "n"(4096 * S)
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]),
+          "n"(16384 + 4096 * S), "n"(4096 * S)
         : "memory");
 }
 
+// One work item: 64 tokens of one chunk (tile cs) of KV group bhk against segment
+// seg of its row sequence.
 template <int D>
 __device__ __forceinline__ void dkv_item(const DkvParams& p, size_t bhk, int cs, int seg, char* smem) {
     typedef BfTiles<D, 64> S;
@@ -755,7 +764,7 @@ __device__ __forceinline__ void dkv_item(const DkvParams& p, size_t bhk, int cs,
             const int q = jj * 64 + lane, t = q / S::KPPR, cc = q % S::KPPR;
             const int e = rs.entry(m * RG + (t >> lg));
             const int row = min(max(rs.row(e, r_row[(m & 7) * 64 + t]), 0), p.n - 1);
-            const size_t o = ((size_t)(t & (g - 1)) * p.n + row) * D + S::kslot(t, cc) * 8;
+            const size_t o = ((size_t)(t & (g - 1)) * p.n + row) * D + dkv_slot<D>(t, cc) * 8;
             // source and destination as named pointers: a conditional expression
             // inside the builtin's argument list loses the kernel's host stub
             const uint16_t* src = (j < S::KINSTS ? Qg : dOg) + o;
@@ -800,8 +809,16 @@ __device__ __forceinline__ void dkv_item(const DkvParams& p, size_t bhk, int cs,
     // 16(G&1) .. +15 of a 32-wide d block and k-slot half hl; its lane 4k + q reads
     // pair base + k at d offset 4q
     const int tr_k = (lane & 15) >> 2, tr_d = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-    // d = 128: the lane's offset L of read (s, db, t) = (0, 0, 0) inside a tile
-    const uint32_t tr_base = (32 * half + 8 * hl + tr_k) * 256 + 16 * ((tr_d >> 3) ^ tr_k) + 8 * (lane & 1);
+    // d = 128: the lane's offset of read (db, t) of k16 step 0 inside the Q tile
+    // (row 32 half + 8 hl + 4 t + tr_k, piece 4 db + tr_d / 8, slot by dkv_slot)
+    uint32_t tr_off[8];
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int pr = 32 * half + 8 * hl + 4 * t + tr_k;
+            tr_off[2 * db + t] = pr * 256 + 16 * dkv_slot<128>(pr, 4 * db + (tr_d >> 3)) + 8 * (lane & 1);
+        }
     const float c1 = p.c1;
     char* st_cur = ring;
     char* st_nxt = ring + ST::BYTES;
@@ -823,7 +840,7 @@ __device__ __forceinline__ void dkv_item(const DkvParams& p, size_t bhk, int cs,
         for (int i = 0; i < 16; ++i) { sacc[i] = 0.f; dpacc[i] = 0.f; }
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
-            const int o = prow_a * S::KROWB + S::kslot(prow_a, 2 * s + hl) * 16;
+            const int o = prow_a * S::KROWB + dkv_slot<D>(prow_a, 2 * s + hl) * 16;
             const bf16x8 qa8 = *reinterpret_cast<const bf16x8*>(qt + o);
             const bf16x8 da8 = *reinterpret_cast<const bf16x8*>(dot + o);
             sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa8, kreg[s], sacc, 0, 0, 0);
@@ -861,9 +878,11 @@ __device__ __forceinline__ void dkv_item(const DkvParams& p, size_t bhk, int cs,
             // holds pairs base + 4t .. +3 of d block db
             i16x4 x[4 * ND];
             if constexpr (D == 128) {
-                const uint32_t a0 = qt_lds + tr_base + 128 * hl, b0 = qt_lds + tr_base - 128 * hl;
-                if (s == 0) tr_reads_d128<0>(a0, b0, x);
-                else tr_reads_d128<1>(a0, b0, x);
+                uint32_t a8[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) a8[u] = qt_lds + tr_off[u];
+                if (s == 0) tr_reads_d128_sw<0>(a8, x);
+                else tr_reads_d128_sw<1>(a8, x);
             } else {
                 uint32_t a[4 * ND];
 #pragma unroll
@@ -872,7 +891,7 @@ __device__ __forceinline__ void dkv_item(const DkvParams& p, size_t bhk, int cs,
 #pragma unroll
                     for (int t = 0; t < 2; ++t) {
                         const int pr = 32 * half + 16 * s + 8 * hl + 4 * t + tr_k;
-                        const uint32_t o = pr * S::KROWB + S::kslot(pr, d >> 3) * 16 + ((d >> 2) & 1) * 8;
+                        const uint32_t o = pr * S::KROWB + dkv_slot<D>(pr, d >> 3) * 16 + ((d >> 2) & 1) * 8;
                         a[2 * db + t] = qt_lds + S::KBYTES + o;
                         a[2 * ND + 2 * db + t] = qt_lds + o;
                     }
