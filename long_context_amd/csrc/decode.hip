@@ -67,13 +67,18 @@ __global__ __launch_bounds__(256) void decode_scores_kernel(DecodeParams p, cons
     const size_t qoff = ((size_t)bi * p.h_q + hh) * D + 4 * kg;
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            float x;
-            if (q_bf16) x = bf16_bits_to_f32(static_cast<const uint16_t*>(Qv)[qoff + 16 * s + j]);
-            else x = static_cast<const float*>(Qv)[qoff + 16 * s + j];
-            qv[4 * s + j] = head_ok ? x : 0.f;
+        // 4 consecutive elements per lane and step: one 8-byte (bf16) or 16-byte load
+        float x[4];
+        if (q_bf16) {
+            const u32x2 v = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(Qv) + qoff + 16 * s);
+            x[0] = __uint_as_float(v[0] << 16); x[1] = __uint_as_float(v[0] & 0xFFFF0000u);
+            x[2] = __uint_as_float(v[1] << 16); x[3] = __uint_as_float(v[1] & 0xFFFF0000u);
+        } else {
+            const f32x4 v = *reinterpret_cast<const f32x4*>(static_cast<const float*>(Qv) + qoff + 16 * s);
+            x[0] = v[0]; x[1] = v[1]; x[2] = v[2]; x[3] = v[3];
         }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) qv[4 * s + j] = head_ok ? x[j] : 0.f;
     }
     const int c = min(c0 + n16, nvis - 1);
     const float* krow = p.kbar + (((size_t)bi * p.h_kv + r) * p.kbar_cap + c) * D + 4 * kg;
@@ -423,11 +428,16 @@ __global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(2, 
 }
 
 // ---------------------------------------------------------------------------------
+// One workgroup of 1024 threads per (head, b): slice maxima and weighted sums by
+// block reductions, then 1024/D thread groups each sum a share of the slices'
+// outputs (the work is a few loads per thread; more threads shorten the chain).
+constexpr int kCombThreads = 1024;
 template <int D>
-__global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p) {
-    constexpr int NG = 256 / D;                     // thread groups splitting the slices
+__global__ __launch_bounds__(kCombThreads) void decode_combine_kernel(DecodeParams p) {
+    constexpr int NG = kCombThreads / D;            // thread groups splitting the slices
+    constexpr int NW = kCombThreads / 64;
     extern __shared__ float s_f[];                  // [max_slices] slice factors
-    __shared__ float red[2][4];
+    __shared__ float red[2][NW];
     __shared__ float s_acc[NG][D];
     const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
     const int hh = blockIdx.x, bi = blockIdx.y;
@@ -438,14 +448,16 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p) {
     const float* base = p.partials + (grp * p.max_slices * (size_t)g + pr) * (D + 2);
     const size_t sstride = (size_t)g * (D + 2);
     float mx = -INFINITY;
-    for (int s = tid; s < nsl; s += 256) mx = fmaxf(mx, base[s * sstride]);
+    for (int s = tid; s < nsl; s += kCombThreads) mx = fmaxf(mx, base[s * sstride]);
     mx = wave_max(mx);
     if (lane == 0) red[0][wid] = mx;
     __syncthreads();
-    const float mstar = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
+    float mstar = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) mstar = fmaxf(mstar, red[0][w]);
     const float mu = (mstar == -INFINITY) ? 0.f : mstar;
     float ls = 0.f;
-    for (int s = tid; s < nsl; s += 256) {
+    for (int s = tid; s < nsl; s += kCombThreads) {
         const float f = fast_exp2(base[s * sstride] - mu);
         s_f[s] = f;
         ls += f * base[s * sstride + 1];
@@ -453,10 +465,12 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeParams p) {
     ls = wave_sum(ls);
     if (lane == 0) red[1][wid] = ls;
     __syncthreads();
-    const float l = red[1][0] + red[1][1] + red[1][2] + red[1][3];
+    float l = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) l += red[1][w];
     const int gq = tid / D, d = tid % D;
     float acc = 0.f;
-#pragma unroll 8
+#pragma unroll 4
     for (int s = gq; s < nsl; s += NG) acc += s_f[s] * base[s * sstride + 2 + d];
     s_acc[gq][d] = acc;
     __syncthreads();
@@ -519,7 +533,7 @@ static hipError_t launch_decode_t(const DecodeParams& p, const DecodeArgs& a, hi
                                             : launch_dec_route<32>(p, a.b, s);
     if (er != hipSuccess) return er;
     hipLaunchKernelGGL((decode_attn_kernel<T, D>), dim3(p.max_slices, p.h_kv, a.b), dim3(kDecThreads), lds, s, p);
-    hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(p.h_q, a.b), dim3(256),
+    hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(p.h_q, a.b), dim3(kCombThreads),
                        (size_t)p.max_slices * sizeof(float), s, p);
     return hipGetLastError();
 }
