@@ -142,8 +142,8 @@ dash_status dash_route_stats(const void* Q, int q_dtype, const float* kbar,
  * the summaries' gradient (both device fp32; dkbar by atomic adds, so its last bits
  * may vary between runs). Per row: g_c = (db_c - mean db)/σ, ∂ŵ_c = g_c/Σ_h ŵ_hc,
  * the α-entmax Jacobian diag(s) - s sᵀ/Σs with s = ŵ^(2-α) (α = 1: s = ŵ), and the
- * chain through <q_h, k̄_c>·γ/sqrt(d). σ = +inf: no-op. List entries outside
- * [0, floor(n/B)) are skipped. Lists of a fixed top-k budget are not supported (their
+ * chain through <q_h, k̄_c>·γ/sqrt(d). σ = +inf: no-op. floor(n/B) ≤ 2048 chunks (as
+ * for the router). List entries outside [0, floor(n/B)) are skipped. Lists of a fixed top-k budget are not supported (their
  * kept set drops chunks the entmax normalisation couples). The weights are rebuilt
  * with the router's own arithmetic, so the support seen here is the forward's. bf16
  * queries need a device workspace of at least dash_workspace_bytes(DASH_OP_ROUTE, ...)

@@ -204,6 +204,7 @@ dash_status dash_route_backward(const void* Q, int q_dtype, const float* kbar, i
     const int T = n / B;
     if (kbar_cap < T) return fail(DASH_ERR_SHAPE, "kbar_cap %d < floor(n/B) = %d", kbar_cap, T);
     if (list_cap < T) return fail(DASH_ERR_SHAPE, "list_cap %d < floor(n/B) = %d", list_cap, T);
+    if (dash::route_tiles_bucket(T) == 0) return fail(DASH_ERR_UNSUPPORTED, "%d chunks exceed the router's 2048", T);
     if (q_dtype == DASH_BF16 && T > 0) {
         const size_t need = dash::route_workspace_bytes(b, h_kv, T, d);
         if (!ws || ws_bytes < need)

@@ -38,193 +38,8 @@ struct RouteBwdParams {
     int T_pad;               // chunks per (b, KV head) in ksplit
     float cs;           // scale of y: (α-1)γ/sqrt(d), or γ log2(e)/sqrt(d) when soft
     float pexp;         // 1/(α-1)
-    float two_m_alpha;  // 2 - α
     float inv_sigma, dz_scale;   // 1/σ and γ/sqrt(d)
 };
-
-// max_g heads per group; entries handled 64 at a time (one per lane).
-constexpr int kMaxG = 16;
-
-template <typename T>
-__device__ __forceinline__ float load_f(const T* p, size_t i);
-template <>
-__device__ __forceinline__ float load_f<float>(const float* p, size_t i) { return p[i]; }
-template <>
-__device__ __forceinline__ float load_f<uint16_t>(const uint16_t* p, size_t i) { return bf16_bits_to_f32(p[i]); }
-
-// One wavefront per (b, KV head, row); 4 wavefronts per workgroup. LDS per
-// wavefront: the group's query rows [g][D] fp32 and dz [g][64].
-template <typename T, int D>
-__global__ __launch_bounds__(256) void route_backward_kernel(RouteBwdParams p, int rows_total) {
-    __shared__ float qs[4][kMaxG][D];
-    __shared__ float dzs[4][kMaxG][64];
-    const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int item = blockIdx.x * 4 + wid;
-    if (item >= rows_total) return;                  // wavefront-uniform; no barrier below
-    const int row = item % p.n;
-    const size_t bh = (size_t)(item / p.n);          // b * h_kv + r
-    const int bi = (int)(bh / p.h_kv), r = (int)(bh % p.h_kv);
-    const int g = p.g;
-    const size_t rb = bh * p.n + row;
-    const int cn = min(p.cnt[rb], p.list_cap);
-    if (cn <= 0) return;
-    const int32_t* li = p.idx + rb * p.list_cap;
-    const float* ldb = p.dbias + rb * p.list_cap;
-    const T* Q = static_cast<const T*>(p.Q);
-    const float* kb = p.kbar + bh * (size_t)p.kbar_cap * D;
-
-    // the group's query rows into LDS (fp32) and the heads' statistics
-    for (int x = lane; x < g * D; x += 64) {
-        const int h = x / D, dd = x % D;
-        qs[wid][h][dd] = load_f<T>(Q, (((size_t)bi * p.h_q + r * g + h) * p.n + row) * D + dd);
-    }
-    float smax[kMaxG], thr[kMaxG];
-#pragma unroll
-    for (int h = 0; h < kMaxG; ++h) {
-        if (h < g) {
-            const float* st = p.stats + 2 * (((size_t)bi * p.h_q + r * g + h) * p.n + row);
-            smax[h] = st[0];
-            thr[h] = st[1];
-        }
-    }
-    __builtin_amdgcn_wave_barrier();
-
-    // mean of the bias gradient over the list
-    float dsum = 0.f;
-    for (int e = lane; e < cn; e += 64) dsum += ldb[e];
-    const float dmean = wave_sum(dsum) / (float)cn;
-
-    // per head: Σ_c s ∂ŵ and Σ_c s over the list (first pass)
-    float A[kMaxG], Bs[kMaxG];
-#pragma unroll
-    for (int h = 0; h < kMaxG; ++h) { A[h] = 0.f; Bs[h] = 0.f; }
-    auto weights = [&](int e, float (&wh)[kMaxG], float& dwhat) {
-        const int c = li[e];
-        if ((unsigned)c >= (unsigned)p.T) {          // not a chunk: no weight, no gradient
-#pragma unroll
-            for (int h = 0; h < kMaxG; ++h) wh[h] = 0.f;
-            dwhat = 0.f;
-            return;
-        }
-        const float* kr = kb + (size_t)c * D;
-        float z[kMaxG];
-#pragma unroll
-        for (int h = 0; h < kMaxG; ++h) z[h] = 0.f;
-        for (int d0 = 0; d0 < D; d0 += 4) {
-            const f32x4 kv = *reinterpret_cast<const f32x4*>(kr + d0);
-#pragma unroll
-            for (int h = 0; h < kMaxG; ++h)
-                if (h < g)
-                    z[h] = fmaf(kv[0], qs[wid][h][d0], fmaf(kv[1], qs[wid][h][d0 + 1],
-                           fmaf(kv[2], qs[wid][h][d0 + 2], fmaf(kv[3], qs[wid][h][d0 + 3], z[h]))));
-        }
-        float wsum = 0.f;
-#pragma unroll
-        for (int h = 0; h < kMaxG; ++h) {
-            if (h < g) {
-                const float y = p.cs * (z[h] - smax[h]);
-                float v;
-                if (p.soft) v = exp2f(y - thr[h]);
-                else {
-                    const float t = fmaxf(y - thr[h], 0.f);
-                    v = t > 0.f ? powf(t, p.pexp) : 0.f;
-                }
-                wh[h] = v;
-                wsum += v;
-            } else {
-                wh[h] = 0.f;
-            }
-        }
-        // ∂L/∂ŵ, the same for every head: g_c / (g w_c) = g_c / Σ_h ŵ_hc
-        const float gc = (ldb[e] - dmean) * p.inv_sigma;
-        dwhat = wsum > 0.f ? gc / wsum : 0.f;
-    };
-    auto s_of = [&](float v) {
-        return v > 0.f ? (p.soft ? v : powf(v, p.two_m_alpha)) : 0.f;
-    };
-    for (int e0 = 0; e0 < cn; e0 += 64) {
-        const int e = e0 + lane;
-        float wh[kMaxG], dwh = 0.f;
-        if (e < cn) weights(e, wh, dwh);
-        else {
-#pragma unroll
-            for (int h = 0; h < kMaxG; ++h) wh[h] = 0.f;
-        }
-#pragma unroll
-        for (int h = 0; h < kMaxG; ++h) {
-            const float s = s_of(wh[h]);
-            A[h] += s * dwh;
-            Bs[h] += s;
-        }
-    }
-#pragma unroll
-    for (int h = 0; h < kMaxG; ++h) {
-        if (h < g) {
-            A[h] = wave_sum(A[h]);
-            Bs[h] = wave_sum(Bs[h]);
-        }
-    }
-
-    // second pass: dz per (head, entry), then dq (lanes over d) and dk̄ (atomics)
-    float dq[kMaxG][D / 64];
-#pragma unroll
-    for (int h = 0; h < kMaxG; ++h)
-#pragma unroll
-        for (int u = 0; u < D / 64; ++u) dq[h][u] = 0.f;
-    for (int e0 = 0; e0 < cn; e0 += 64) {
-        const int e = e0 + lane;
-        float wh[kMaxG], dwh = 0.f;
-        if (e < cn) weights(e, wh, dwh);
-        else {
-#pragma unroll
-            for (int h = 0; h < kMaxG; ++h) wh[h] = 0.f;
-        }
-#pragma unroll
-        for (int h = 0; h < kMaxG; ++h) {
-            if (h < g) {
-                const float s = s_of(wh[h]);
-                const float dx = Bs[h] > 0.f ? s * (dwh - A[h] / Bs[h]) : 0.f;
-                dzs[wid][h][lane] = e < cn ? dx * p.dz_scale : 0.f;
-            }
-        }
-        __builtin_amdgcn_wave_barrier();
-        const int ne = min(64, cn - e0);
-        for (int k = 0; k < ne; ++k) {
-            const int c = li[e0 + k];
-            if ((unsigned)c >= (unsigned)p.T) continue;   // wavefront-uniform
-            const float* kr = kb + (size_t)c * D;
-            float gk[D / 64];
-#pragma unroll
-            for (int u = 0; u < D / 64; ++u) gk[u] = 0.f;
-#pragma unroll
-            for (int u = 0; u < D / 64; ++u) {
-                const int dd = lane + 64 * u;
-                const float kv = kr[dd];
-#pragma unroll
-                for (int h = 0; h < kMaxG; ++h) {
-                    if (h < g) {
-                        const float dz = dzs[wid][h][k];
-                        dq[h][u] = fmaf(dz, kv, dq[h][u]);
-                        gk[u] = fmaf(dz, qs[wid][h][dd], gk[u]);
-                    }
-                }
-            }
-            float* dkr = p.dkbar + (bh * (size_t)p.kbar_cap + c) * D;
-#pragma unroll
-            for (int u = 0; u < D / 64; ++u) unsafeAtomicAdd(dkr + lane + 64 * u, gk[u]);
-        }
-        __builtin_amdgcn_wave_barrier();
-    }
-    // dQ: each (head, row) belongs to this wavefront alone
-#pragma unroll
-    for (int h = 0; h < kMaxG; ++h) {
-        if (h < g) {
-            float* out = p.dQ + (((size_t)bi * p.h_q + r * g + h) * p.n + row) * D;
-#pragma unroll
-            for (int u = 0; u < D / 64; ++u) out[lane + 64 * u] += dq[h][u];
-        }
-    }
-}
 
 // ---------------------------------------------------------------------------------
 // Stage-1 backward with dk̄ accumulated in LDS (the form used whenever one column
@@ -637,6 +452,13 @@ __global__ __launch_bounds__(512) void route_backward_lds_kernel(RouteBwdParams 
     }
 }
 
+template <typename T>
+__device__ __forceinline__ float load_f(const T* p, size_t i);
+template <>
+__device__ __forceinline__ float load_f<float>(const float* p, size_t i) { return p[i]; }
+template <>
+__device__ __forceinline__ float load_f<uint16_t>(const uint16_t* p, size_t i) { return bf16_bits_to_f32(p[i]); }
+
 struct SumBwdParams {
     const void* K; const float* qbar; const float* dkbar;
     float* dK; float* dqbar;
@@ -706,7 +528,8 @@ __global__ __launch_bounds__(64) void summary_backward_kernel(SumBwdParams p) {
 }
 
 // Widest column slice (64, 32, 16) whose LDS accumulator [T][DS + 1] fits beside the
-// transpose tiles; 0 when none does. (128 columns would not fit the registers.)
+// transpose tiles (128 columns would not fit the registers). Every chunk count the
+// router accepts (≤ 2048) fits a 16-column slice.
 static int route_bwd_slice(int d, int T) {
     for (int ds = d == 128 ? 64 : d; ds >= 16; ds /= 2)
         if ((size_t)T * (ds + 1) * 4 + (size_t)kRbWaves * kRbTr * 4 <= kRbMaxLds) return ds;
@@ -756,7 +579,6 @@ hipError_t launch_route_backward(const RouteBwdArgs& a, hipStream_t s) {
     p.pmode = pmode_of(a.alpha);
     p.cs = route_scale(a.alpha, a.gamma, a.d);
     p.pexp = p.soft ? 1.f : (float)(1.0 / ((double)a.alpha - 1.0));
-    p.two_m_alpha = 2.f - a.alpha;
     p.inv_sigma = 1.f / a.sigma;
     p.dz_scale = (float)(a.gamma / sqrt((double)a.d));
     p.ksplit = static_cast<const uint8_t*>(a.ws);
@@ -773,17 +595,7 @@ hipError_t launch_route_backward(const RouteBwdArgs& a, hipStream_t s) {
                                        : launch_rb_lds_d<uint16_t, 128>(p, bh, ds, s);
         return a.d == 64 ? launch_rb_lds_d<float, 64>(p, bh, ds, s) : launch_rb_lds_d<float, 128>(p, bh, ds, s);
     }
-    // very long sequences: one wavefront per row, dk̄ by global atomics
-    const int rows = a.b * a.h_kv * a.n;
-    const dim3 grid((rows + 3) / 4);
-    if (a.q_bf16) {
-        if (a.d == 64) hipLaunchKernelGGL((route_backward_kernel<uint16_t, 64>), grid, dim3(256), 0, s, p, rows);
-        else hipLaunchKernelGGL((route_backward_kernel<uint16_t, 128>), grid, dim3(256), 0, s, p, rows);
-    } else {
-        if (a.d == 64) hipLaunchKernelGGL((route_backward_kernel<float, 64>), grid, dim3(256), 0, s, p, rows);
-        else hipLaunchKernelGGL((route_backward_kernel<float, 128>), grid, dim3(256), 0, s, p, rows);
-    }
-    return hipGetLastError();
+    return hipErrorInvalidValue;                      // rejected by the host checks first
 }
 
 hipError_t launch_summary_backward(const SumBwdArgs& a, hipStream_t s) {

@@ -272,6 +272,7 @@ def _route_bwd(dash, **kw):
     (dict(kcap=3), 2), (dict(cap=3), 2), (dict(n=-1), 2), (dict(h_q=15), 2),
     (dict(h_q=64), 4), (dict(d=96), 4),
     (dict(ws=NUL), 5), (dict(ws_bytes=1024), 5),            # bf16 queries need the split summaries
+    (dict(n=2049 * 16, B=16, kcap=2049, cap=2049), 4),       # more chunks than the router takes
 ])
 def test_route_backward_validation(dash, kw, status):
     assert _route_bwd(dash, **kw) == status

@@ -443,49 +443,45 @@ def test_full_backward_chain_matches_oracle(causal, alpha):
         assert l2 <= l2_tol, f"{name}: L2 error {l2} above {l2_tol}"
 
 
-@pytest.mark.parametrize("alpha", [1.5, 1.25])
-def test_route_and_summary_backward_32k_full_size(alpha):
-    """Stages 1 and 0 backward on the 32K GQA-16 clustered workload at full size, in
-    the benchmark's launch (512 chunks: dk̄ in two 64-column slices). Both gradients are
-    linear in the upstream dbias, so it is nonzero only on sampled rows (the oracle's
-    routed entries of each, where its list matches the GPU router's): the oracle then
-    fixes dQ of those rows, every other row's routing gradient is exactly zero, and
-    dk̄ is the sum over the sampled rows alone. Stage 0 takes the oracle's dk̄ on both
-    sides and is checked on the whole of dK and dq̄."""
+def _route_backward_sampled(w, alpha, rows, seed):
+    """Stages 1 and 0 backward through the C ABI with the upstream dbias nonzero only on
+    the given rows (their oracle-routed entries, where the oracle's list matches the
+    GPU router's). Both gradients are linear in dbias: the oracle then fixes dQ of
+    those rows, every other row's routing gradient is exactly zero, and dk̄ is the sum
+    over the given rows alone. Stage 0 takes the oracle's dk̄ on both sides and is
+    checked on the whole of dK and dq̄."""
     from long_context_amd import dash
     from oracle import dash_oracle as O
     G = _gu()
-    w = inputs.prefill_32k_clusters(alphas=(alpha,))
     b, hq, n, d = w.Q.shape
-    hkv, B, g = w.h_kv, w.B, hq // w.h_kv
+    hkv, B = w.h_kv, w.B
     T = n // B
-    rng = np.random.default_rng(31)
-    rows = np.unique(np.concatenate([rng.choice(n, size=24, replace=False), [B, 2 * B - 1, n // 2, n - 1]]))
-    _log(f"32k routing backward alpha={alpha}: {rows.size} rows")
     dev = lambda x, dt: torch.from_numpy(np.ascontiguousarray(x)).to("cuda", dt)
-    Qd, Kd = dev(w.Q, torch.bfloat16), dev(w.K, torch.bfloat16)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    Qd, Kd = dev(w.Q, tdt), dev(w.K, tdt)
     qbar = torch.from_numpy(w.qbar).cuda()
     kbar = dash.alloc_kbar(b, hkv, T, d)
     dash.dash_summarize(Kd, qbar, kbar, B)
     idx, bias, cnt, _ = dash.alloc_route(b, hkv, n, T)
     stats = torch.empty((b, hq, n, 2), device="cuda")
-    dash.dash_route_stats(Qd, kbar, B, alpha, w.gamma, w.sigma, True, idx, bias, cnt, stats)
+    dash.dash_route_stats(Qd, kbar, B, alpha, w.gamma, w.sigma, w.causal, idx, bias, cnt, stats)
     torch.cuda.synchronize()
     pos = np.broadcast_to(rows, (b, rows.size))
     kb = O.stage0_summaries(w.K, w.qbar, B)
-    rt = O.route(w.Q[:, :, rows], pos, kb, B, alpha, w.gamma, w.sigma, True, n)
+    rt = O.route(w.Q[:, :, rows], pos, kb, B, alpha, w.gamma, w.sigma, w.causal, n)
     nex, _ = G.compare_route(dict(idx=idx, cnt=cnt), rt, rows, T)
     keep = ~G.exempt_rows(rt)                                  # [b, h_kv, R]
     _log(f"  exempt rows: {nex}")
-    up = inputs.upstream_grad((b, hkv, rows.size, T), seed=32)
+    up = inputs.upstream_grad((b, hkv, rows.size, T), seed=seed)
     dense = np.where(rt["support"] & keep[..., None], up, 0.0)  # oracle layout, sampled rows
     # the same values at the GPU's list positions of the sampled rows, zero elsewhere
-    ii = idx[:, :, torch.from_numpy(rows).cuda()].cpu().numpy().astype(np.int64)
-    cc = cnt[:, :, torch.from_numpy(rows).cuda()].cpu().numpy()
+    ri = torch.from_numpy(rows).cuda()
+    ii = idx[:, :, ri].cpu().numpy().astype(np.int64)
+    cc = cnt[:, :, ri].cpu().numpy()
     live = np.arange(ii.shape[-1])[None, None, None, :] < cc[..., None]
     dl = np.where(live, np.take_along_axis(dense, np.where(live, ii, 0), -1), 0.0).astype(np.float32)
     dlist = torch.zeros(idx.shape, device="cuda")
-    dlist[:, :, torch.from_numpy(rows).cuda()] = dev(dl, torch.float32)
+    dlist[:, :, ri] = dev(dl, torch.float32)
     dQ = torch.zeros((b, hq, n, d), device="cuda")
     dkb = torch.zeros((b, hkv, T, d), device="cuda")
     dash.dash_route_backward(Qd, kbar, idx, cnt, dlist, stats, B, alpha, w.gamma, w.sigma, dQ, dkb)
@@ -494,11 +490,10 @@ def test_route_and_summary_backward_32k_full_size(alpha):
     others = np.ones(n, bool)
     others[rows] = False
     assert np.all(gq[:, :, others] == 0.0), "rows with a zero upstream gradient must get none"
-    ref, spread = _spread(lambda k: O.route_backward(w.Q[:, :, rows], pos, k, B, alpha, w.gamma, w.sigma, True, n,
-                                                     dense), kb)
+    ref, spread = _spread(lambda k: O.route_backward(w.Q[:, :, rows], pos, k, B, alpha, w.gamma, w.sigma, w.causal,
+                                                     n, dense), kb)
     _check_cond(gq[:, :, rows], ref["dQ"], spread["dQ"], "dQ (routing, sampled rows)")
     _check_cond(dkb.cpu().numpy(), ref["dkbar"], spread["dkbar"], "dkbar")
-    # Stage 0 on the oracle's dk̄, all of dK and dq̄
     dK = torch.zeros((b, hkv, n, d), device="cuda")
     dq = torch.zeros((hkv, d), device="cuda")
     dash.dash_summarize_backward(Kd, qbar, dev(ref["dkbar"], torch.float32), B, dK, dq)
@@ -506,3 +501,27 @@ def test_route_and_summary_backward_32k_full_size(alpha):
     r0 = O.summary_backward(w.K, w.qbar, B, ref["dkbar"])
     _rel(dK.cpu().numpy(), r0["dK"], TOL_F32_L2, TOL_F32_ROW, "dK (summaries)")
     _rel(dq.cpu().numpy(), r0["dqbar"], TOL_F32_L2, TOL_F32_ROW, "dqbar")
+
+
+@pytest.mark.parametrize("alpha", [1.5, 1.25])
+def test_route_and_summary_backward_32k_full_size(alpha):
+    """Stages 1 and 0 backward on the 32K GQA-16 clustered workload at full size, in
+    the benchmark's launch (512 chunks: dk̄ in two 64-column slices), with the upstream
+    gradient on 28 sampled rows."""
+    w = inputs.prefill_32k_clusters(alphas=(alpha,))
+    n, B = w.n, w.B
+    rng = np.random.default_rng(31)
+    rows = np.unique(np.concatenate([rng.choice(n, size=24, replace=False), [B, 2 * B - 1, n // 2, n - 1]]))
+    _log(f"32k routing backward alpha={alpha}: {rows.size} rows")
+    _route_backward_sampled(w, alpha, rows, seed=32)
+
+
+def test_route_backward_1300_chunks_sampled():
+    """1300 chunks at d = 128 (B = 16, GQA 8): the dk̄ accumulator no longer fits 32
+    columns per workgroup and runs in eight 16-column slices; the router splits each
+    row over four wavefronts. Upstream gradient on sampled rows."""
+    w = inputs.make_prefill(b=1, h_q=16, h_kv=2, d=128, n=1300 * 16, B=16, dtype="bf16", seed=41, gamma=6.0)
+    rng = np.random.default_rng(42)
+    rows = np.unique(np.concatenate([rng.choice(w.n, size=20, replace=False), [16, w.n - 1]]))
+    _log(f"1300-chunk routing backward: {rows.size} rows")
+    _route_backward_sampled(w, 1.5, rows, seed=43)
