@@ -11,8 +11,10 @@
 //    (kg, n) ends with chunks 16t+4kg+i of pair n. All visible chunks of a row stay in
 //    registers: up to 512 per wavefront, rows with more chunks are split over CW = 2
 //    or 4 wavefronts whose row maxima and Newton sums meet in LDS. The split is
-//    interleaved by 16-chunk tile (wavefront cw takes tiles cw, cw + CW, ...), so the
-//    two tiles of each shared summary stage go to two different wavefronts.
+//    interleaved by 16-chunk tile (wavefront cw takes tiles cw, cw + CW, ...). bf16
+//    queries take the summaries from a buffer split into three bf16 terms: through a
+//    three-stage LDS ring when one wavefront holds a row, straight from L2 when rows
+//    are split (the ring's barriers across all wavefronts cost more than its sharing).
 //  * Threshold: work on y = (α-1)γ(z̄ - max z̄) <= 0 (exact shift by the row maximum)
 //    so τ lies in [-1, 0). Newton's method on g(τ) = ||[y - τ]_+||_p - 1 with
 //    p = 1/(α-1), started at τ = -1 where g >= 0: g is convex and decreasing, so the
@@ -209,6 +211,9 @@ __device__ __forceinline__ void wait_vm_at_most(int n) {
 // Stages of the summary ring in LDS: three when a row can need many stages, so the
 // copies run two stages ahead.
 template <int NT, int CW> constexpr int route_ring_stages() { return NT * CW / 2 >= 4 ? 3 : 2; }
+// bf16 queries stream the split summaries through an LDS ring when one wavefront
+// holds a whole row; rows split over several wavefronts read them from L2.
+template <typename T, int CW> constexpr bool route_uses_ring() { return sizeof(T) == 2 && CW == 1; }
 
 // τ for rows whose chunks are split over CW cooperating wavefronts: every iteration
 // each wavefront sums its own chunks, the CW partial sums meet in LDS (double
@@ -287,8 +292,9 @@ __global__ __launch_bounds__(512) void entmax_route_kernel(RouteParams p) {
     const int row0 = wg_row0 + gid * R;
     const bool wave_live = row0 < p.n;
     constexpr int RSTG = route_ring_stages<NT, CW>();
-    char* kstage = rsm;                                              // RSTG stages (bf16 path)
-    float* wl_all = reinterpret_cast<float*>(rsm + (sizeof(T) == 2 ? RSTG * KS::BYTES : 0));
+    constexpr bool RING = route_uses_ring<T, CW>();
+    char* kstage = rsm;                                              // RSTG stages (ring only)
+    float* wl_all = reinterpret_cast<float*>(rsm + (RING ? RSTG * KS::BYTES : 0));
     float* wl = wl_all + gid * R * WS;
     float* xred = wl_all + G * R * WS;                // [G][CW][16] row maxima of each wavefront
     float* xsum = xred + G * CW * 16;                 // [2][G][CW][16][2] Newton partial sums
@@ -368,9 +374,9 @@ __global__ __launch_bounds__(512) void entmax_route_kernel(RouteParams p) {
                     smax = fmaxf(smax, sv[t][i]);
                 }
             };
+            if constexpr (RING) {
 #pragma unroll
-            for (int j = 0; j < RSTG - 1; ++j) issue(j);
-            if constexpr (CW == 1) {
+                for (int j = 0; j < RSTG - 1; ++j) issue(j);
                 // stage st holds local tiles 2st and 2st+1 of the single wavefront
 #pragma unroll
                 for (int st = 0; st < NT / 2; ++st) {
@@ -383,20 +389,15 @@ __global__ __launch_bounds__(512) void entmax_route_kernel(RouteParams p) {
                     }
                 }
             } else {
-                // the CW/2 stages st = t*CW/2 + u hold local tile t of every wavefront:
-                // row tile 2st+tt = t*CW + 2u + tt belongs to wavefront 2u + tt
+                // rows split over CW wavefronts: each wavefront reads its own tiles of
+                // the split buffer straight from L2 (a shared ring's per-stage barriers
+                // across all wavefronts cost more than its sharing saves here)
+                const char* kglob = reinterpret_cast<const char*>(ksrc);
 #pragma unroll
                 for (int t = 0; t < NT; ++t) {
-#pragma unroll 1
-                    for (int u = 0; u < CW / 2; ++u) {
-                        const int st = t * (CW / 2) + u;
-                        if (st < nst) {               // workgroup-uniform
-                            enter_stage(st);
-                            const char* stg = kstage + (st % RSTG) * KS::BYTES;
-#pragma unroll
-                            for (int tt = 0; tt < 2; ++tt)
-                                if (2 * u + tt == cw && t < nt) tile_logits(stg, tt, t);
-                        }
+                    if (t < nt) {
+                        const int c0 = RS::tile_chunk(t, cw);
+                        tile_logits(kglob + (size_t)(c0 >> 5) * KS::BYTES, (c0 >> 4) & 1, t);
                     }
                 }
             }
@@ -641,7 +642,7 @@ __global__ __launch_bounds__(512) void entmax_route_kernel(RouteParams p) {
 constexpr size_t kRouteMaxLds = 96 * 1024;
 template <typename T, int D, int NT, int CW>
 inline int route_groups_per_block(int R, int B, size_t* lds) {
-    const size_t stage = sizeof(T) == 2 ? route_ring_stages<NT, CW>() * (size_t)KSplitStage<D, 32>::BYTES : 0;
+    const size_t stage = route_uses_ring<T, CW>() ? route_ring_stages<NT, CW>() * (size_t)KSplitStage<D, 32>::BYTES : 0;
     auto bytes = [&](int G) {
         return stage + (size_t)G * R * CW * NT * 16 * 4 + (size_t)G * CW * 16 * 4 + (size_t)2 * G * CW * 32 * 4;
     };
