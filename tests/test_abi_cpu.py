@@ -62,8 +62,9 @@ def _route(dash, **kw):
     (dict(qdt=7), 3), (dict(causal=2), 3),
     (dict(d=96), 4), (dict(B=24), 4), (dict(h_q=64, h_kv=2), 4), (dict(h_q=6, h_kv=2), 4),
     (dict(n=129 * 1024, cap=2064, list_cap=2064), 4),
-    # one query head per KV head: 2048 chunks of 16 rows' weights do not fit LDS
-    (dict(h_q=2, h_kv=2, n=2048 * 64, cap=2048, list_cap=2048), 4),
+    # one query head per KV head, 2048 chunks: fits LDS (split rows stage no summaries
+    # there), so validation goes on to the missing bf16 workspace
+    (dict(h_q=2, h_kv=2, n=2048 * 64, cap=2048, list_cap=2048), 5),
 ])
 def test_route_validation(dash, kw, status):
     assert _route(dash, **kw) == status

@@ -287,6 +287,7 @@ LONG = [
     ("bf16", 1, 32, 2, 128, 20032, 32, 1.5, 4.0, 1.0),     # 626 chunks: 2 wavefronts per row group
     ("bf16", 1, 16, 2, 128, 40000, 32, 1.5, 6.0, 1.0),     # 1250 chunks: 4 wavefronts
     ("f32", 1, 4, 2, 64, 24000, 32, 2.0, 5.0, 1.0),        # 750 chunks, fp32 queries: 2 wavefronts
+    ("bf16", 1, 2, 2, 64, 35200, 32, 1.5, 4.0, 1.0),       # g = 1, 1100 chunks: 16 rows x 4 wavefronts
 ]
 
 
