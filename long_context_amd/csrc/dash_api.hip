@@ -213,7 +213,7 @@ dash_status dash_route_backward(const void* Q, int q_dtype, const float* kbar, i
     }
     dash::RouteBwdArgs a{Q, q_dtype == DASH_BF16, kbar, kbar_cap, idx, cnt, dbias, list_cap, stats,
                          b, h_q, h_kv, n, d, B, alpha, gamma, sigma, dQ, dkbar, ws};
-    return from_hip(dash::launch_route_backward(a, (hipStream_t)stream), "route_backward_kernel");
+    return from_hip(dash::launch_route_backward(a, (hipStream_t)stream), "route_backward_lds_kernel");
 }
 
 dash_status dash_summarize_backward(const void* K, int k_dtype, const float* qbar, const float* dkbar,
