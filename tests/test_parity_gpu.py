@@ -470,3 +470,44 @@ def test_incremental_decode_loop_matches_oracle():
                                              ex[None, :, None], h_q // h_kv, "bf16"))
     assert done == (4 * B + 3 - 1) // B
     _log(f"  worst per-row relative error {worst:.3e}")
+
+
+def test_decode_graph_replay_matches_eager():
+    """A decode step captured in a HIP graph (a serving loop's form): the entry point
+    records no memset or allocation, so each replay, with new query values copied into
+    the captured buffer and eager decode work and synchronisation in between, equals
+    the eager step on the same inputs bit for bit."""
+    from long_context_amd import dash
+    seq_len = [4096, 3000, 700]
+    w = inputs.make_decode(b=3, h_q=16, h_kv=2, d=128, L=4096, B=64, alphas=(1.5,), gamma=4.0, dtype="bf16",
+                           seed=17, seq_len=seq_len)
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to("cuda", torch.bfloat16)
+    Q, K, V = dev(w.Q), dev(w.K), dev(w.V)
+    kbar = dash.alloc_kbar(3, 2, w.n // w.B, 128)
+    dash.dash_summarize(K, torch.from_numpy(w.qbar).cuda(), kbar, w.B)
+    sl = torch.tensor(seq_len, dtype=torch.int32, device="cuda")
+    ws = dash.alloc_decode_ws(3, 16, 2, w.n, 128, w.B)
+    ws_eager = dash.alloc_decode_ws(3, 16, 2, w.n, 128, w.B)
+    O = torch.empty((3, 16, 1, 128), device="cuda")
+    O_eager = torch.empty_like(O)
+    step = lambda out, wsp: dash.dash_attend_decode(Q, K, V, kbar, sl, w.B, 1.5, 4.0, 1.0, out, wsp)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(2):
+            step(O, ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(O, ws)
+    rng = np.random.default_rng(18)
+    for k in range(4):
+        Q.copy_(dev(inputs.round_bf16(rng.standard_normal(Q.shape).astype(np.float32))))
+        O.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        step(O_eager, ws_eager)                      # eager work between replays
+        torch.cuda.synchronize()
+        _log(f"graph replay {k}: max |diff| {float((O - O_eager).abs().max()):.3e}")
+        assert torch.equal(O, O_eager), f"replay {k} differs from the eager step"
