@@ -430,7 +430,7 @@ def backward(torch, dash, inputs, alpha, steps, warmup, no_dense=False):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "this benchmark runs on one GPU; --gpus must be 1 (sharding across GPUs is not implemented)"}))
         sys.exit(2)
     import torch
     from long_context_amd import dash, inputs
