@@ -442,6 +442,65 @@ def test_topk_with_softmax_routing_is_a_fixed_budget():
     assert np.array_equal(rt["cnt"][0, 0], np.minimum(4, rt["vis"][0]))
 
 
+def _one_hot_route(xs, alpha, gamma=1.0, top_k=0):
+    """Route one non-causal row whose per-head thresholded scores are exactly `xs`
+    [heads, T]: summaries k̄_c = sqrt(T) e_c make z̄_c = q_c, so q = x / ((α-1)γ)
+    (α = 1: x / γ)."""
+    heads, T = xs.shape
+    scale = gamma * (alpha - 1.0 if alpha != 1.0 else 1.0)
+    Q = (xs / scale)[None, :, None, :]                   # [1, heads, 1, d = T]
+    kb = (np.sqrt(T) * np.eye(T))[None, None]            # [1, 1, T, T]
+    return O.route(Q, np.array([[T]]), kb, 1, alpha, gamma, 1.0, False, T, keep_heads=True, top_k=top_k)
+
+
+@pytest.mark.parametrize("alpha", [1.25, 1.5, 2.0])
+def test_margin_is_the_distance_to_the_brute_force_threshold(alpha):
+    """The exemption margin of a row is min over its group's heads and visible chunks
+    of |x - τ| (the distance of a score to the unique KKT threshold): compared with τ
+    from the brute-force support enumeration, on random tiny rows."""
+    rng = np.random.default_rng(31)
+    for _ in range(6):
+        T = int(rng.integers(2, 8))
+        xs = rng.standard_normal((2, T)) * (alpha - 1.0) * 2.0
+        rt = _one_hot_route(xs, alpha)
+        ref = np.inf
+        for h in range(2):
+            found = _brute_force_tau(xs[h], alpha)
+            assert len(found) == 1
+            ref = min(ref, np.abs(xs[h] - found[0][1]).min())
+        assert abs(rt["margin"][0, 0, 0] - ref) < 1e-12
+
+
+@pytest.mark.parametrize("alpha", [1.5, 2.0])
+def test_margin_separates_planted_near_threshold_scores(alpha):
+    """A chunk planted 5e-7 below a head's τ (outside the support, so τ is unchanged)
+    makes the row exempt (margin <= 1e-6); planted 2e-6 below, it does not. The other
+    head is uniform, so its scores sit far from its own threshold."""
+    base = np.array([1.0, 0.6, 0.1, -0.3]) * (alpha - 1.0) * 2.0
+    (S, tau), = _brute_force_tau(base, alpha)
+    for gap, exempt in ((5e-7, True), (2e-6, False)):
+        xs = np.stack([np.append(base, tau - gap), np.zeros(5)])
+        (S2, tau2), = _brute_force_tau(xs[0], alpha)
+        assert set(S2) == set(S) and abs(tau2 - tau) < 1e-12
+        rt = _one_hot_route(xs, alpha)
+        assert abs(rt["margin"][0, 0, 0] - gap) < 1e-10
+        assert bool(rt["margin"][0, 0, 0] <= 1e-6) == exempt
+
+
+def test_topk_margin_is_the_log_weight_gap_at_the_cut():
+    """With softmax routing (α = 1) log w_c - log w_c' = γ (z̄_c - z̄_c') for one head,
+    so the fixed-budget margin is the logit gap between the last kept and the first
+    dropped chunk: planted gaps of 5e-6 (exempt, <= 1e-5) and 2e-5 (not exempt)."""
+    for gap, exempt in ((5e-6, True), (2e-5, False)):
+        xs = np.array([[2.0, 1.5, 1.0, 1.0 - gap, 0.0]])
+        rt = _one_hot_route(xs, 1.0, gamma=1.0, top_k=3)
+        assert np.array_equal(np.nonzero(rt["support"][0, 0, 0])[0], [0, 1, 2])
+        assert abs(rt["margin_topk"][0, 0, 0] - gap) < 1e-12
+        assert bool(rt["margin_topk"][0, 0, 0] <= 1e-5) == exempt
+    rt = _one_hot_route(np.array([[2.0, 1.0]]), 1.0, top_k=3)   # nothing dropped
+    assert rt["margin_topk"][0, 0, 0] == np.inf
+
+
 def test_route_mask_matches_little_endian_bit_packing():
     """The oracle's bitpacked mask equals numpy's little-endian bit packing read as
     32-bit little-endian words, and unpacks back to the support."""
