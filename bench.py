@@ -41,7 +41,10 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense baseline")
     ap.add_argument("--cpu-rows", type=int, default=3072, help="query rows of the oracle sample")
-    ap.add_argument("--only", choices=["prefill", "decode", "both"], default="both")
+    ap.add_argument("--only", choices=["prefill", "decode", "both", "decode128k", "decode32k"], default="both",
+                    help="decode128k / decode32k: time one decode workload alone (no prefill)")
+    ap.add_argument("--flushed-only", action="store_true",
+                    help="decode: time only the Infinity-Cache-flushed steps (one kernel mix per trace)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (HBM counter calibration)")
     ap.add_argument("--backward", action="store_true",
@@ -427,6 +430,22 @@ def backward(torch, dash, inputs, alpha, steps, warmup, no_dense=False):
     return out
 
 
+def time_decode(torch, dd, scrub, args):
+    """Median µs of a decode step with the 256 MiB Infinity Cache evicted before each
+    step by reading a 512 MiB buffer (a read leaves no dirty lines to write back
+    during the step; it sits outside the events), and unflushed for context."""
+    sfl, _ = time_events(torch, lambda ev: (scrub.max(), dd.run(ev)), 2, args.steps, args.warmup)
+    nbytes, cnt = dd.bytes_per_step()
+    tfl = float(np.median(sfl))
+    out = dict(us_per_step=tfl * 1e3, us_min=float(sfl.min()) * 1e3, us_max=float(sfl.max()) * 1e3,
+               gbs=nbytes / (tfl * 1e-3) / 1e9, hbm_frac=nbytes / (tfl * 1e-3) / 1e9 / PEAK_HBM_GBS,
+               bytes=nbytes, routed=cnt.ravel().tolist())
+    if not args.flushed_only:
+        sun, _ = time_events(torch, dd.run, 2, args.steps, args.warmup)
+        out["us_per_step_unflushed"] = float(np.median(sun)) * 1e3
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -450,6 +469,16 @@ def main():
                           "warmup": args.warmup, "dtype": "bf16", "data": "synthetic",
                           "config": {"workload": "prefill_32k_clusters", "alpha": args.alpha},
                           "backward": res}), flush=True)
+        return
+
+    if args.only in ("decode128k", "decode32k"):
+        w = inputs.decode_128k_b4() if args.only == "decode128k" else inputs.decode_32k_b16()
+        scrub = torch.ones(512 << 20, dtype=torch.uint8, device="cuda")
+        dec = time_decode(torch, Decode(w, torch, dash), scrub, args)
+        print(json.dumps({"metric": f"decode µs/step, {w.name}", "unit": "us", "value": dec["us_per_step"],
+                          "higher_is_better": False, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+                          "dtype": "bf16", "data": "synthetic", "config": {"workload": w.name},
+                          "decode": dec}), flush=True)
         return
 
     out = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -510,27 +539,13 @@ def main():
     # --- decode at 128K (and 32K x 16) ----------------------------------------------
     dec = dec32 = None
     if args.only in ("decode", "both"):
-        # reading a 512 MiB buffer between timed decode steps evicts the 256 MiB
-        # Infinity Cache (a read leaves no dirty lines to write back during the
-        # step), so each step streams its KV from HBM; the read is outside the events
         scrub = torch.ones(512 << 20, dtype=torch.uint8, device="cuda")
-
-        def time_decode(dd):
-            sfl, _ = time_events(torch, lambda ev: (scrub.max(), dd.run(ev)), 2, args.steps, args.warmup)
-            sun, _ = time_events(torch, dd.run, 2, args.steps, args.warmup)
-            nbytes, cnt = dd.bytes_per_step()
-            tfl, tun = float(np.median(sfl)), float(np.median(sun))
-            return dict(us_per_step=tfl * 1e3, us_min=float(sfl.min()) * 1e3, us_max=float(sfl.max()) * 1e3,
-                        us_per_step_unflushed=tun * 1e3, gbs=nbytes / (tfl * 1e-3) / 1e9,
-                        hbm_frac=nbytes / (tfl * 1e-3) / 1e9 / PEAK_HBM_GBS, bytes=nbytes,
-                        routed=cnt.ravel().tolist())
-
         dd = Decode(inputs.decode_128k_b4(), torch, dash)
-        dec = time_decode(dd)
+        dec = time_decode(torch, dd, scrub, args)
         print(f"[bench] decode 128k: {dec}", file=sys.stderr, flush=True)
         del dd
         dd = Decode(inputs.decode_32k_b16(), torch, dash)
-        dec32 = time_decode(dd)
+        dec32 = time_decode(torch, dd, scrub, args)
         dec32.pop("routed")
         print(f"[bench] decode 32k x16: {dec32}", file=sys.stderr, flush=True)
         del dd, scrub

