@@ -243,8 +243,9 @@ dash_status dash_attend_prefill_backward(const void* Q, const void* K, const voi
  *   Optional outputs (NULL to skip): idx_out/bias_out [b, h_kv, list_cap],
  *   cnt_out [b, h_kv], w_out [b, h_kv, kbar_cap] dense group weights.
  * ws: at least dash_workspace_bytes(DASH_OP_DECODE, b, h_q, h_kv, L_cap, d, B)
- * bytes of device memory (scores, routed lists and split-KV partials). Calls that
- * share one workspace must not overlap.
+ * bytes of device memory (scores, routed lists, per-group counters and split-KV
+ * partials); no initial contents are needed (the kernels clear what they count).
+ * Calls that share one workspace must not overlap.
  */
 dash_status dash_attend_decode(const void* Q, const void* Kc, const void* Vc, int in_dtype,
                                const float* kbar, const int32_t* seq_len,

@@ -55,24 +55,25 @@ dash_status check_params(float alpha, float gamma, float sigma) {
 }
 
 struct DecodeLayout {
-    int T_ws, T_route, slice_tokens, max_slices;
-    size_t off_scores, off_idx, off_bias, off_cnt, off_part, total;
+    int T_ws, T_route;
+    size_t off_scores, off_idx, off_bias, off_cnt, off_counters, off_ml, off_o, total;
 };
 
 DecodeLayout decode_layout(int b, int h_q, int h_kv, int L_cap, int kbar_cap, int d, int B) {
     DecodeLayout L;
     const int g = h_q / h_kv;
     L.T_ws = (L_cap - 1) / B;                       // upper bound of the routable chunks
-    int tr_dummy = 0;
-    dash::decode_geometry(L_cap, L.T_ws, B, &tr_dummy, &L.slice_tokens, &L.max_slices);
     L.T_route = kbar_cap < L.T_ws ? kbar_cap : L.T_ws;
     const size_t nT = (size_t)(L.T_ws > 0 ? L.T_ws : 1);
+    const size_t slots = (size_t)dash::decode_partial_slots(b, h_kv);
     L.off_scores = 0;
     L.off_idx = align256(L.off_scores + (size_t)b * h_q * nT * 4);
     L.off_bias = align256(L.off_idx + (size_t)b * h_kv * nT * 4);
     L.off_cnt = align256(L.off_bias + (size_t)b * h_kv * nT * 4);
-    L.off_part = align256(L.off_cnt + (size_t)b * h_kv * 4);
-    L.total = align256(L.off_part + (size_t)b * h_kv * L.max_slices * g * (d + 2) * 4);
+    L.off_counters = align256(L.off_cnt + (size_t)b * h_kv * 4);
+    L.off_ml = align256(L.off_counters + (size_t)3 * b * h_kv * 4);
+    L.off_o = align256(L.off_ml + (size_t)g * slots * 2 * 4);
+    L.total = align256(L.off_o + (size_t)g * slots * d * 4);
     return L;
 }
 
@@ -363,10 +364,10 @@ static dash_status attend_decode(const void* Q, const void* Kc, const void* Vc, 
     }
     a.w_out = w_out;
     a.scores = reinterpret_cast<float*>(w + Lo.off_scores);
-    a.partials = reinterpret_cast<float*>(w + Lo.off_part);
+    a.counters = reinterpret_cast<int32_t*>(w + Lo.off_counters);
+    a.part_ml = reinterpret_cast<float*>(w + Lo.off_ml);
+    a.part_o = reinterpret_cast<float*>(w + Lo.off_o);
     a.T_route = Lo.T_route;
-    a.max_slices = Lo.max_slices;
-    a.slice_tokens = Lo.slice_tokens;
     a.pages = pages; a.pages_per_seq = pages_per_seq; a.num_pages = num_pages;
     return from_hip(dash::launch_decode(a, (hipStream_t)stream), "decode kernels");
 }

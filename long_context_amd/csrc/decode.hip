@@ -3,23 +3,31 @@
 // kernel table), for one new query per sequence at position p = L-1.
 //
 //   decode_scores_kernel   z̄ for every (b, head, visible chunk): fp32 MFMA 16x16x4,
-//                          one wavefront per 16 chunks x the g heads of a group;
-//                          spread over many workgroups because this step is bound
-//                          by reading the fp32 summaries.
-//   decode_route_kernel    one workgroup per (b, KV group), up to 2048 chunks per
-//                          row: wavefront h solves the
-//                          entmax threshold of head h over all visible chunks
-//                          (Newton on the p-norm form, as in the prefill router),
-//                          the group average is taken in LDS in a fixed head order,
-//                          then μ, the bias, and a block-wide ballot compaction.
-//   decode_attn_kernel     split-KV Stage 2: the group's routed chunks followed by
-//                          the diagonal chunk form one token stream; each workgroup
-//                          takes a slice of it, its 4 wavefronts take 32 tokens of
-//                          every 128-token tile (K/V staged in LDS, prefetched), and
-//                          the workgroup writes one unnormalised partial
-//                          (max, sum, output) per head. HBM-bound.
-//   decode_combine_kernel  merges the partials of all slices with the usual
-//                          max-rescaled sum and normalises.
+//                          one wavefront per 16 chunks x the g heads of a group, all
+//                          summary loads issued before the first product. It also
+//                          clears the per-group arrival counters of the router.
+//   decode_route_kernel    one workgroup per (b, query head): the entmax threshold of
+//                          the head over all its visible chunks (Newton on the
+//                          p-norm form, as in the prefill router, with workgroup-wide
+//                          sums), the head's weights written back over its scores.
+//                          The last head of a group to finish (an arrival counter)
+//                          takes the group average in a fixed head order, μ, the
+//                          bias and a workgroup ballot compaction. The heads of a
+//                          group are placed on one XCD (one L2).
+//   decode_attn_kernel     split-KV Stage 2 as a balanced token stream: every group
+//                          contributes its routed chunks, then its diagonal chunk up
+//                          to the query, in 32-token units; the units of all groups
+//                          form one sequence, cut into equal contiguous ranges, one
+//                          per wavefront (no empty workgroups, whatever the routed
+//                          counts). A wavefront copies the K and V rows of its units
+//                          into its own LDS ring (asynchronous global->LDS copies,
+//                          stages ahead of the compute), runs S^T = K Q^T and
+//                          O^T = V^T P^T on MFMA with an online softmax over the g
+//                          heads of the group, and writes one unnormalised partial
+//                          (max, sum, output) per group it touches. HBM-bound.
+//   decode_combine_kernel  merges the partials of each (b, head) with the usual
+//                          max-rescaled sum and normalises; the partials of one head
+//                          are contiguous, so the merge reads them as one stream.
 #include "attn_common.h"
 #include "kernels.h"
 
@@ -27,21 +35,29 @@
 
 namespace dash {
 
-constexpr int kDecTT = 64;           // tokens per decode tile (one 32-token block per wavefront)
-constexpr int kDecWaves = kDecTT / 32;
-constexpr int kDecThreads = 64 * kDecWaves;
-constexpr int kDecSlice = 512;        // stream tokens per workgroup
+constexpr int kDecUnit = 32;          // tokens per stream unit (one 32x32 S^T block)
 constexpr int kDecSoftmax = -1;       // pmode of α = 1 (softmax routing)
+constexpr int kRouteThreads = 256;    // workgroup of the per-head router
+constexpr int kMaxStreams = 2048;     // upper bound of the attention wavefronts
+constexpr int kCombThreads = 512;
+// Attention wavefronts per compute unit: more streams add in-flight copies but also
+// partial results, which the next kernel must read back.
+constexpr int kDecStreamsPerCU = 2;
 
 struct DecodeParams {
     const void* Q; const void* Kc; const void* Vc;
     const float* kbar; const int32_t* seq_len;
-    int h_q, h_kv, L_cap, kbar_cap, B, g, log2g, T_route, list_cap, max_slices, slice_tokens;
+    int b, h_q, h_kv, L_cap, kbar_cap, B, g, log2g, T_route, list_cap, streams;
     float cs, pexp, inv_sigma, scale_log2;
     int pmode, out_bf16;
     void* O;
     int32_t* idx; float* bias; int32_t* cnt; float* w_out;
-    float* scores; float* partials;
+    float* scores;       // [b, h_q, T_route]: raw logits, then each head's weights
+    int32_t* counters;   // [b * h_kv]: head workgroups of a group that have finished
+    int32_t* ranges;     // [b * h_kv][2]: first and last partial slot of each group
+    float* part_ml;      // [g][slots][2]: running max and sum of a stream segment
+    float* part_o;       // [g][slots][D]: its unnormalised output
+    int slots;           // kMaxStreams + b * h_kv
     const int32_t* pages; int pages_per_seq, num_pages;    // paged cache (nullable)
 };
 
@@ -58,16 +74,23 @@ __global__ __launch_bounds__(256) void decode_scores_kernel(DecodeParams p, cons
     const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int n16 = lane & 15, kg = lane >> 4;
     const int r = blockIdx.y, bi = blockIdx.z;
+    // the router's arrival counters start every call at zero (this kernel runs first)
+    if (blockIdx.x == 0 && threadIdx.x == 0) p.counters[bi * p.h_kv + r] = 0;
     const int c0 = (blockIdx.x * 4 + wid) * 16;
     const int nvis = visible_of(p, seq_len_of(p, bi));
     if (c0 >= nvis) return;
     const bool head_ok = n16 < p.g;
     const int hh = r * p.g + (head_ok ? n16 : 0);
+    // every load of the wavefront is issued before the first product
+    const int c = min(c0 + n16, nvis - 1);
+    const float* krow = p.kbar + (((size_t)bi * p.h_kv + r) * p.kbar_cap + c) * D + 4 * kg;
+    f32x4 a[D / 16];
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) a[s] = *reinterpret_cast<const f32x4*>(krow + 16 * s);
     float qv[D / 4];
     const size_t qoff = ((size_t)bi * p.h_q + hh) * D + 4 * kg;
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
-        // 4 consecutive elements per lane and step: one 8-byte (bf16) or 16-byte load
         float x[4];
         if (q_bf16) {
             const u32x2 v = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(Qv) + qoff + 16 * s);
@@ -80,16 +103,12 @@ __global__ __launch_bounds__(256) void decode_scores_kernel(DecodeParams p, cons
 #pragma unroll
         for (int j = 0; j < 4; ++j) qv[4 * s + j] = head_ok ? x[j] : 0.f;
     }
-    const int c = min(c0 + n16, nvis - 1);
-    const float* krow = p.kbar + (((size_t)bi * p.h_kv + r) * p.kbar_cap + c) * D + 4 * kg;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-        const f32x4 a = *reinterpret_cast<const f32x4*>(krow + 16 * s);
+    for (int s = 0; s < D / 16; ++s)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], qv[4 * s + j], acc, 0, 0, 0);
-    }
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s][j], qv[4 * s + j], acc, 0, 0, 0);
     if (head_ok) {
         float* out = p.scores + ((size_t)bi * p.h_q + hh) * p.T_route;
 #pragma unroll
@@ -123,430 +142,600 @@ __device__ __forceinline__ float dec_pow(float t, float pexp) {
     return t > 0.f ? fast_exp2(pexp * fast_log2(t)) : 0.f;
 }
 
-template <int VPL, int PM>
-__global__ __launch_bounds__(1024) void decode_route_kernel(DecodeParams p) {
-    constexpr int TMAX = VPL * 64;
-    extern __shared__ float dyn_wl[];                 // [16][TMAX] per-head weights
-    auto wl = reinterpret_cast<float (*)[TMAX]>(dyn_wl);
-    __shared__ float red[2][16];
-    __shared__ int wcnt[16];
-    const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
-    const int r = blockIdx.x, bi = blockIdx.y;
-    const int g = p.g;
-    const int nvis = visible_of(p, seq_len_of(p, bi));
-    const size_t grp = (size_t)bi * p.h_kv + r;
+// Inclusive prefix sum and total of one int per lane over the wavefront.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(v, o);
+        if (lane >= o) v += y;
+    }
+    return v;
+}
+__device__ __forceinline__ int wave_sum_int(int v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
 
-    if (wid < g && nvis > 0) {
-        const int hh = r * g + wid;
-        const float* sc = p.scores + ((size_t)bi * p.h_q + hh) * p.T_route;
-        float y[VPL];
+// Workgroup sum / max of one value per thread (4 wavefronts), the same result in every
+// thread; `buf` holds 4 floats and is reused after a barrier.
+__device__ __forceinline__ float block4_sum(float v, float* buf) {
+    v = wave_sum(v);
+    const int wid = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) buf[wid] = v;
+    __syncthreads();
+    const float r = (buf[0] + buf[1]) + (buf[2] + buf[3]);
+    __syncthreads();
+    return r;
+}
+__device__ __forceinline__ float block4_max(float v, float* buf) {
+    v = wave_max(v);
+    const int wid = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) buf[wid] = v;
+    __syncthreads();
+    const float r = fmaxf(fmaxf(buf[0], buf[1]), fmaxf(buf[2], buf[3]));
+    __syncthreads();
+    return r;
+}
+
+// Hand-off between workgroups of one launch without an agent-scope release fence (on
+// gfx950 it writes back the whole L2, and those write-backs serialise across
+// workgroups): the data goes out through agent-scope relaxed atomic stores, which
+// write through the non-coherent caches (sc1), and the arrival on a counter comes
+// after every store of the workgroup has completed.
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// All threads call it; returns (through *last, in LDS) whether this workgroup is the
+// n-th and last to arrive on the counter. The last one then invalidates its caches
+// (an agent-scope acquire: no write-back), so plain loads see what the others stored.
+__device__ __forceinline__ void arrive_last(int32_t* counter, int n, int* last) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");      // this thread's stores are done
+    __syncthreads();                                      // ... and every thread's
+    if (threadIdx.x == 0)
+        *last = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == n - 1;
+    __syncthreads();
+    if (*last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+}
+
+// Workgroups of the router are numbered so that the g heads of a group get ids of
+// equal residue mod 8: consecutive workgroup ids go round-robin to the 8 XCDs, so the
+// heads of a group share an L2 (the summaries they read, the weights the last one
+// gathers).
+__device__ __forceinline__ void route_block_of(int id, int g, int& grp, int& h) {
+    const int x = id & 7, j = id >> 3;
+    grp = (j / g) * 8 + x;
+    h = j % g;
+}
+
+template <int VPT, int PM>
+__global__ __launch_bounds__(kRouteThreads) void decode_route_kernel(DecodeParams p, int ngroups) {
+    constexpr bool SOFT = PM == kDecSoftmax;
+    __shared__ float red[4];
+    __shared__ float nsum[2][4][2];                 // Newton partial sums, by step parity
+    __shared__ int s_last, wcnt[4];
+    const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
+    int grp, h;
+    route_block_of(blockIdx.x, p.g, grp, h);
+    if (grp >= ngroups) return;
+    const int g = p.g;
+    const int bi = grp / p.h_kv, r = grp % p.h_kv;
+    const int nvis = visible_of(p, seq_len_of(p, bi));
+    float* row = p.scores + ((size_t)bi * p.h_q + r * g + h) * p.T_route;
+
+    if (nvis > 0) {                                   // workgroup-uniform
+        float y[VPT];
         float mx = -INFINITY;
 #pragma unroll
-        for (int k = 0; k < VPL; ++k) {
-            const int c = lane + 64 * k;
-            y[k] = c < nvis ? sc[c] : -INFINITY;
+        for (int k = 0; k < VPT; ++k) {
+            const int c = VPT * tid + k;
+            y[k] = c < nvis ? row[c] : -INFINITY;
             mx = fmaxf(mx, y[k]);
         }
-        mx = wave_max(mx);
+        mx = block4_max(mx, red);
 #pragma unroll
-        for (int k = 0; k < VPL; ++k) y[k] = p.cs * (y[k] - mx);
-        if constexpr (PM == kDecSoftmax) {
+        for (int k = 0; k < VPT; ++k) y[k] = p.cs * (y[k] - mx);
+        if constexpr (SOFT) {
             // α = 1: per-head softmax, kept as log2 ŵ = y - log2 Σ 2^y
             float se = 0.f;
 #pragma unroll
-            for (int k = 0; k < VPL; ++k) se += fast_exp2(y[k]);
-            const float lse = fast_log2(wave_sum(se));
+            for (int k = 0; k < VPT; ++k) se += fast_exp2(y[k]);
+            const float lse = fast_log2(block4_sum(se, red));
 #pragma unroll
-            for (int k = 0; k < VPL; ++k) wl[wid][lane + 64 * k] = y[k] - lse;
-        } else {
-        float tau = -1.f;
-        for (int it = 0; it < 100; ++it) {
-            float a0 = 0.f, a1 = 0.f;
-#pragma unroll
-            for (int k = 0; k < VPL; ++k) dec_accum<PM>(__builtin_amdgcn_fmed3f(y[k] - tau, 0.f, 1.f), p.pexp, a0, a1);
-            a0 = wave_sum(a0);
-            a1 = wave_sum(a1);
-            float delta;
-            if (PM == 1) delta = (a1 - 1.f) / a0;
-            else {
-                const float nrm = (PM == 2) ? sqrtf(a1) : (PM == 4) ? sqrtf(sqrtf(a1)) : fast_exp2(fast_log2(a1) / p.pexp);
-                delta = (nrm - 1.f) * (a1 / nrm) / a0;
+            for (int k = 0; k < VPT; ++k) {
+                const int c = VPT * tid + k;
+                if (c < nvis) store_coherent(row + c, y[k] - lse);
             }
-            if (!(a0 > 0.f)) delta = 0.f;
-            tau += delta;
-            if (!(fabsf(delta) > 1e-6f)) break;
-        }
+        } else {
+            // Newton from τ = -1 (every thread takes the same steps: the partial sums
+            // of the 4 wavefronts are added in a fixed order)
+            float tau = -1.f;
+            for (int it = 0; it < 100; ++it) {
+                float a0 = 0.f, a1 = 0.f;
 #pragma unroll
-        for (int k = 0; k < VPL; ++k) wl[wid][lane + 64 * k] = dec_pow<PM>(__builtin_amdgcn_fmed3f(y[k] - tau, 0.f, 1.f), p.pexp);
+                for (int k = 0; k < VPT; ++k)
+                    dec_accum<PM>(__builtin_amdgcn_fmed3f(y[k] - tau, 0.f, 1.f), p.pexp, a0, a1);
+                a0 = wave_sum(a0);
+                a1 = wave_sum(a1);
+                if (lane == 0) { nsum[it & 1][wid][0] = a0; nsum[it & 1][wid][1] = a1; }
+                __syncthreads();
+                a0 = (nsum[it & 1][0][0] + nsum[it & 1][1][0]) + (nsum[it & 1][2][0] + nsum[it & 1][3][0]);
+                a1 = (nsum[it & 1][0][1] + nsum[it & 1][1][1]) + (nsum[it & 1][2][1] + nsum[it & 1][3][1]);
+                float delta;
+                if (PM == 1) delta = (a1 - 1.f) / a0;
+                else {
+                    const float nrm = (PM == 2) ? sqrtf(a1) : (PM == 4) ? sqrtf(sqrtf(a1)) : fast_exp2(fast_log2(a1) / p.pexp);
+                    delta = (nrm - 1.f) * (a1 / nrm) / a0;
+                }
+                if (!(a0 > 0.f)) delta = 0.f;
+                tau += delta;
+                if (!(fabsf(delta) > 1e-6f)) break;
+            }
+#pragma unroll
+            for (int k = 0; k < VPT; ++k) {
+                const int c = VPT * tid + k;
+                if (c < nvis) store_coherent(row + c, dec_pow<PM>(__builtin_amdgcn_fmed3f(y[k] - tau, 0.f, 1.f), p.pexp));
+            }
         }
     }
-    __syncthreads();
-    // group average in a fixed head order, then μ over the support
+    // publish this head's weights; the last head of the group to arrive goes on
+    arrive_last(&p.counters[grp], g, &s_last);
+    if (!s_last) return;
+
+    // group average in a fixed head order (α = 1: log2 w = log2((1/g) Σ_h ŵ_h), taken
+    // stably, and every visible chunk is in the support), then μ over the support.
+    // Every head's weights are loaded before any is used (g <= 16 slots, unrolled).
+    const float* rows = p.scores + ((size_t)bi * p.h_q + r * g) * p.T_route;
     const float inv_g = 1.f / (float)g;
-    float wv[TMAX / 1024 > 0 ? TMAX / 1024 : 1];
-    constexpr int PER = TMAX / 1024 > 0 ? TMAX / 1024 : 1;
-    // (α = 1: wv holds log2 w = log2((1/g) Σ_h ŵ_h), taken stably, and every visible
-    // chunk is in the support)
-    constexpr bool SOFT = PM == kDecSoftmax;
+    float hv[VPT][16];
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+        const int c = min(VPT * tid + k, max(nvis - 1, 0));
+#pragma unroll
+        for (int hh = 0; hh < 16; ++hh) hv[k][hh] = hh < g ? rows[(size_t)hh * p.T_route + c] : (SOFT ? -INFINITY : 0.f);
+    }
+    float wv[VPT];
     float sl = 0.f, scn = 0.f;
 #pragma unroll
-    for (int q = 0; q < PER; ++q) {
-        const int c = tid + 1024 * q;
+    for (int k = 0; k < VPT; ++k) {
+        const int c = VPT * tid + k;
         float w = SOFT ? -INFINITY : 0.f;
         if (c < nvis) {
             if (SOFT) {
                 float m = -INFINITY;
-                for (int h = 0; h < g; ++h) m = fmaxf(m, wl[h][c]);
+#pragma unroll
+                for (int hh = 0; hh < 16; ++hh) m = fmaxf(m, hv[k][hh]);
                 float sm = 0.f;
-                for (int h = 0; h < g; ++h) sm += fast_exp2(wl[h][c] - m);
+#pragma unroll
+                for (int hh = 0; hh < 16; ++hh) sm += hh < g ? fast_exp2(hv[k][hh] - m) : 0.f;
                 w = m + fast_log2(sm) - fast_log2((float)g);
                 sl += w; scn += 1.f;
             } else {
-                for (int h = 0; h < g; ++h) w += wl[h][c];
+#pragma unroll
+                for (int hh = 0; hh < 16; ++hh) w += hv[k][hh];
                 w *= inv_g;
+                if (w > 0.f) { sl += fast_log2(w); scn += 1.f; }
             }
         }
-        wv[q] = w;
-        if (!SOFT && w > 0.f) { sl += fast_log2(w); scn += 1.f; }
+        wv[k] = w;
     }
-    sl = wave_sum(sl);
-    scn = wave_sum(scn);
-    if (lane == 0) { red[0][wid] = sl; red[1][wid] = scn; }
-    __syncthreads();
-    float tsl = 0.f, tsc = 0.f;
-    for (int w = 0; w < 16; ++w) { tsl += red[0][w]; tsc += red[1][w]; }
+    const float tsl = block4_sum(sl, red);
+    const float tsc = block4_sum(scn, red);
     const float mu2 = tsc > 0.f ? tsl / tsc : 0.f;
     const float bscale = kLn2 * p.inv_sigma;
-    int32_t* idx = p.idx + grp * p.list_cap;
-    float* bias = p.bias + grp * p.list_cap;
-    int base = 0;
+    int32_t* idx = p.idx + (size_t)grp * p.list_cap;
+    float* bias = p.bias + (size_t)grp * p.list_cap;
+    // compaction: thread tid holds chunks VPT*tid .. VPT*tid+VPT-1, so a chunk's list
+    // position is the workgroup's exclusive prefix of the per-thread counts plus its
+    // rank inside the thread
+    bool in[VPT];
+    int mine = 0;
 #pragma unroll
-    for (int q = 0; q < PER; ++q) {
-        const int c = tid + 1024 * q;
-        const bool in = SOFT ? c < nvis : wv[q] > 0.f;
-        const uint64_t m = ballot(in);
-        if (lane == 0) wcnt[wid] = __builtin_popcountll(m);
-        __syncthreads();
-        int off = base;
-        for (int w = 0; w < wid; ++w) off += wcnt[w];
-        int tot = 0;
-        for (int w = 0; w < 16; ++w) tot += wcnt[w];
-        if (in) {
-            const int pos = off + __builtin_popcountll(m & ((1ull << lane) - 1ull));
+    for (int k = 0; k < VPT; ++k) {
+        const int c = VPT * tid + k;
+        in[k] = SOFT ? c < nvis : wv[k] > 0.f;
+        mine += in[k] ? 1 : 0;
+    }
+    const int incl = wave_incl_scan(mine);
+    if (lane == 63) wcnt[wid] = incl;
+    __syncthreads();
+    int pos = incl - mine;
+    for (int w = 0; w < wid; ++w) pos += wcnt[w];
+    const int base = (wcnt[0] + wcnt[1]) + (wcnt[2] + wcnt[3]);
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+        const int c = VPT * tid + k;
+        if (in[k]) {
             idx[pos] = c;
-            bias[pos] = p.inv_sigma == 0.f ? 0.f : bscale * ((SOFT ? wv[q] : fast_log2(wv[q])) - mu2);
+            bias[pos] = p.inv_sigma == 0.f ? 0.f : bscale * ((SOFT ? wv[k] : fast_log2(wv[k])) - mu2);
+            ++pos;
         }
-        if (p.w_out && c < p.T_route) p.w_out[grp * p.kbar_cap + c] = SOFT ? fast_exp2(wv[q]) : wv[q];
-        base += tot;
-        __syncthreads();
+        if (p.w_out && c < p.T_route) p.w_out[(size_t)grp * p.kbar_cap + c] = SOFT ? fast_exp2(wv[k]) : wv[k];
     }
     if (tid == 0) p.cnt[grp] = base;
 }
 
 // ---------------------------------------------------------------------------------
-template <typename T, int D>
-__global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_attn_kernel(DecodeParams p) {
-    typedef TileGeom<T, D, kDecTT> G;
+// The decode token stream. Group grp = b * h_kv + r contributes units_of(grp) units
+// of 32 tokens: cnt * B/32 for its routed chunks, then the diagonal chunk up to the
+// query. The units of all groups, in group order, form one sequence of W units; the
+// P = min(streams, W) wavefronts take the ranges [blk*W/P, (blk+1)*W/P).
+__device__ __forceinline__ int units_of(const DecodeParams& p, int grp) {
+    const int pos = seq_len_of(p, grp / p.h_kv) - 1;
+    return p.cnt[grp] * (p.B / kDecUnit) + (pos % p.B) / kDecUnit + 1;
+}
+__device__ __forceinline__ int first_unit_of(long long blk, long long W, long long P) {
+    return (int)(blk * W / P);
+}
+// the range that holds unit x
+__device__ __forceinline__ int range_of(long long x, long long W, long long P) {
+    return (int)(((x + 1) * P + W - 1) / W) - 1;
+}
+__device__ __forceinline__ int stream_units(const DecodeParams& p, int ngroups) {
+    int W = 0;
+    for (int base = 0; base < ngroups; base += 64) {
+        const int grp = base + (threadIdx.x & 63);
+        W += wave_sum_int(grp < ngroups ? units_of(p, grp) : 0);
+    }
+    return W;
+}
+
+template <int CPW>
+__device__ __forceinline__ void wait_copies_behind(int n) {
+    // at most n units' copies (CPW instructions each) still in flight
+    if (n <= 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    else if (n == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(CPW) : "memory");
+    else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * CPW) : "memory");
+}
+
+template <typename T, int D, int NST>
+__global__ __launch_bounds__(64) void decode_attn_kernel(DecodeParams p, int ngroups) {
+    typedef SwzTile<T, D, kDecUnit> S;
+    typedef TileCopier<T, D, kDecUnit, 1> CP;
     typedef Mfma<T> MM;
     typedef typename MM::Op Op;
-    extern __shared__ __attribute__((aligned(16))) char smem[];
-    constexpr int MAXE = 64;                       // entry cache per slice
-    int* s_chunk = reinterpret_cast<int*>(smem + G::BYTES);
-    float* s_bias = reinterpret_cast<float*>(s_chunk + MAXE);
-    int* s_row0 = reinterpret_cast<int*>(s_bias + MAXE);   // first cache row of each chunk
-
-    const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
-    const int l32 = lane & 31, hl = lane >> 5;
-    const int slice = blockIdx.x, r = blockIdx.y, bi = blockIdx.z;
-    const int g = p.g, B = p.B;
-    const size_t grp = (size_t)bi * p.h_kv + r;
-    const int L = seq_len_of(p, bi);
-    const int pos = L - 1;
-    const int cq = pos / B;
-    const int cnt = p.cnt[grp];
-    const int E = cnt + 1;                          // routed chunks, then the diagonal
-    const int ST = p.slice_tokens;
-    const int t_begin = slice * ST;
-    const int t_end = min(t_begin + ST, E * B);
-    if (t_begin >= t_end) return;
-    const int e_first = t_begin / B;
-    const int e_last = (t_end - 1) / B;
-    // contiguous cache: row of token t of chunk c = c*B + t in the (b, r) slab; paged
-    // cache: ((page * h_kv + r) * B + t) in the page array (page ids clamped)
+    static_assert(NST >= 2 && NST <= 3, "two or three ring stages");
+    static_assert(CP::CPW * (NST - 1) < 64, "vmcnt range");
+    extern __shared__ __attribute__((aligned(16))) char ring[];   // NST stages of K, V
+    const int lane = threadIdx.x & 63, l32 = lane & 31, hl = lane >> 5;
+    const int blk = blockIdx.x;
+    const int W = stream_units(p, ngroups);
+    const int P = min(p.streams, W);
+    if (blk >= P) return;
+    const int u_begin = first_unit_of(blk, W, P), u_end = first_unit_of(blk + 1, W, P);
+    const int upc = p.B / kDecUnit;                   // units per chunk
+    const int g = p.g;
     const bool paged = p.pages != nullptr;
-    for (int e = e_first + tid; e <= e_last; e += kDecThreads) {
-        const bool routed = e < cnt;
-        const int c = routed ? p.idx[grp * p.list_cap + e] : cq;
-        s_chunk[e - e_first] = c;
-        s_bias[e - e_first] = routed ? p.bias[grp * p.list_cap + e] * kLog2e : 0.f;
-        if (paged) {
-            const int pg = min(max(p.pages[(size_t)bi * p.pages_per_seq + c], 0), p.num_pages - 1);
-            s_row0[e - e_first] = (pg * p.h_kv + r) * B;
-        } else {
-            s_row0[e - e_first] = c * B;
-        }
-    }
-    __syncthreads();
+    CP cp;
+    cp.init(0, lane);
 
-    const bool pair_ok = l32 < g;
-    const int hh = r * g + (pair_ok ? l32 : 0);
-    Op qf[D / 16];
-    {
-        const T* qrow = static_cast<const T*>(p.Q) + ((size_t)bi * p.h_q + hh) * D + 8 * hl;
+    int S0 = 0;                                       // first unit of the current round's groups
+    for (int base = 0; base < ngroups && S0 < u_end; base += 64) {
+        const int mg = base + lane;
+        const int mu = mg < ngroups ? units_of(p, mg) : 0;
+        const int incl = wave_incl_scan(mu);
+        const int mstart = S0 + incl - mu;
+        uint64_t hit = ballot(mg < ngroups && mstart < u_end && mstart + mu > u_begin);
+        S0 += __shfl(incl, 63);
+        while (hit) {
+            const int k = __builtin_ctzll(hit);
+            hit &= hit - 1;
+            // ---- one segment: the units [s0, s1) of group grp (relative to the group)
+            const int grp = base + k;
+            const int gS = __shfl(mstart, k), gU = __shfl(mu, k);
+            const int s0 = max(u_begin, gS) - gS, s1 = min(u_end, gS + gU) - gS;
+            const int bi = grp / p.h_kv, r = grp % p.h_kv;
+            const int pos = seq_len_of(p, bi) - 1;
+            const int cq = pos / p.B;
+            const int cnt = p.cnt[grp];
+            const bool pair_ok = l32 < g;
+            if (s0 == 0 && lane == 0) {           // this wavefront holds the group's first unit
+                p.ranges[2 * grp] = blk + grp;
+                p.ranges[2 * grp + 1] = range_of(gS + gU - 1, W, P) + grp;
+            }
+            Op qf[D / 16];
+            {
+                const int hh = r * g + (pair_ok ? l32 : 0);
+                const T* qrow = static_cast<const T*>(p.Q) + ((size_t)bi * p.h_q + hh) * D + 8 * hl;
 #pragma unroll
-        for (int s = 0; s < D / 16; ++s) qf[s] = pair_ok ? MM::load(qrow + 16 * s) : MM::zero();
-    }
-    const T* Kg = static_cast<const T*>(p.Kc) + (paged ? (size_t)0 : grp * (size_t)p.L_cap * D);
-    const T* Vg = static_cast<const T*>(p.Vc) + (paged ? (size_t)0 : grp * (size_t)p.L_cap * D);
-
-    float m_run = -INFINITY, l_run = 0.f;
-    f32x16 o_acc[D / 32];
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o_acc[db][i] = 0.f;
-
-    const int ntiles = (t_end - t_begin + kDecTT - 1) / kDecTT;
-    // cache row of the first token of each 32-token group of a tile (a group never
-    // straddles two chunks because B % 32 == 0); -1 past the slice end. Rows of the
-    // diagonal chunk are clamped to the query's own row (later tokens are masked).
-    auto group_base = [&](int tau) -> int {
-        if (tau >= t_end) return -1;
-        return s_row0[tau / B - e_first] + tau % B;
-    };
-    int rb[kDecWaves], rl[kDecWaves];
-    auto set_bases = [&](int tt0) {
-#pragma unroll
-        for (int q = 0; q < kDecWaves; ++q) {
-            const int tau = tt0 + 32 * q;
-            rb[q] = group_base(tau);
-            // the diagonal entry (the last one, index cnt) may hold rows past pos
-            rl[q] = (tau < t_end && tau / B >= cnt) ? s_row0[tau / B - e_first] + pos % B : 0x7fffffff;
-        }
-    };
-    auto row_of = [&](int t) -> int {
-        const int base = rb[t >> 5];
-        return base < 0 ? 0 : min(base + (t & 31), rl[t >> 5]);
-    };
-    TileRegs<T, D, kDecTT, kDecThreads> regs;
-    set_bases(t_begin);
-    regs.load(Kg, Vg, row_of, tid);
-    for (int k = 0; k < ntiles; ++k) {
-        const int tt0 = t_begin + k * kDecTT;
-        __syncthreads();
-        regs.store(smem, tid);
-        __syncthreads();
-        if (k + 1 < ntiles) {
-            set_bases(tt0 + kDecTT);
-            regs.load(Kg, Vg, row_of, tid);
-        }
-        const int wt0 = tt0 + 32 * wid;            // this wavefront's 32 stream tokens
-        if (wt0 >= t_end) continue;
-        const int e = wt0 / B;
-        const bool diag = e >= cnt;
-        const float bias2 = s_bias[e - e_first];
-        const int kv0 = s_chunk[e - e_first] * B + wt0 % B;   // KV position of token 0
-        f32x16 sacc1[1];
-        score_blocks<T, D, 1, G::KROW>(sacc1, smem + (32 * wid + l32) * G::KROW + 8 * hl * G::ES, qf);
-        f32x16 sacc = sacc1[0];
-        float mx = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int toff = 8 * (i >> 2) + 4 * hl + (i & 3);
-            float v = fmaf(sacc[i], p.scale_log2, bias2);
-            if ((diag && kv0 + toff > pos) || wt0 + toff >= t_end) v = -INFINITY;
-            sacc[i] = v;
-            mx = fmaxf(mx, v);
-        }
-        mx = pair32_max(mx);
-        // lazy rescaling: the reference maximum moves only when the tile maximum
-        // exceeds it by more than 8 (probabilities stay <= 2^8 in between)
-        const bool grow = mx > m_run + 8.f;
-        const float alpha = grow ? fast_exp2(m_run - mx) : 1.f;
-        m_run = grow ? mx : m_run;
-        const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-        float ps = 0.f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const float pv = fast_exp2(sacc[i] - m_use);
-            sacc[i] = pv;
-            ps += pv;
-        }
-        l_run = fmaf(l_run, alpha, ps);
-        if (ballot(grow) != 0) {
+                for (int s = 0; s < D / 16; ++s) qf[s] = pair_ok ? MM::load(qrow + 16 * s) : MM::zero();
+            }
+            float m_run = -INFINITY, l_run = 0.f;
+            f32x16 o_acc[D / 32];
 #pragma unroll
             for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) o_acc[db][i] *= alpha;
+                for (int i = 0; i < 16; ++i) o_acc[db][i] = 0.f;
+
+            for (int w0 = s0; w0 < s1;) {
+                // ---- a window of up to 64 list entries (chunks): lane e holds the first
+                // cache row of entry e_lo + e, its last valid row and its bias
+                const int e_lo = w0 / upc;
+                const int e_hi = min((s1 - 1) / upc, e_lo + 63);
+                const int w1 = min(s1, (e_hi + 1) * upc);
+                int row0 = 0, rowmax = 0;
+                float bias2 = 0.f;
+                {
+                    const int e = e_lo + lane;
+                    if (e <= e_hi) {
+                        const bool routed = e < cnt;
+                        // a routed chunk is one of the query's visible chunks (< cq)
+                        const int c = routed ? min(max(p.idx[(size_t)grp * p.list_cap + e], 0), max(cq - 1, 0)) : cq;
+                        bias2 = routed ? p.bias[(size_t)grp * p.list_cap + e] * kLog2e : 0.f;
+                        if (paged) {
+                            const int pg = min(max(p.pages[(size_t)bi * p.pages_per_seq + c], 0), p.num_pages - 1);
+                            row0 = (pg * p.h_kv + r) * p.B;
+                        } else {
+                            row0 = (grp * p.L_cap) + c * p.B;
+                        }
+                        // the diagonal chunk: rows past the query are never read
+                        rowmax = row0 + (routed ? p.B - 1 : pos % p.B);
+                    }
+                }
+                const int nu = w1 - w0;
+                auto issue = [&](int j) {                // unit w0 + j into its stage
+                    const int u = w0 + j;
+                    const int e = u / upc - e_lo;
+                    const int tb = __builtin_amdgcn_readlane(row0, e) + (u % upc) * kDecUnit;
+                    const int nmax = __builtin_amdgcn_readlane(rowmax, e);
+                    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // stage reads done
+                    cp.issue(ring + (j % NST) * S::STAGE, static_cast<const T*>(p.Kc),
+                             static_cast<const T*>(p.Vc), tb, nmax, 0);
+                };
+#pragma unroll
+                for (int j = 0; j < NST - 1; ++j)
+                    if (j < nu) issue(j);
+                for (int j = 0; j < nu; ++j) {
+                    if (j + NST - 1 < nu) issue(j + NST - 1);
+                    wait_copies_behind<CP::CPW>(min(nu - 1 - j, NST - 1));
+                    const char* kt = ring + (j % NST) * S::STAGE;
+                    const char* vt = kt + S::BYTES;
+                    const int u = w0 + j;
+                    const int e = u / upc - e_lo;
+                    const float b2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bias2), e));
+                    const int lim = __builtin_amdgcn_readlane(rowmax, e) - __builtin_amdgcn_readlane(row0, e);
+                    const int toff0 = (u % upc) * kDecUnit;       // token offset of the unit in its chunk
+                    // S^T = K Q^T for the unit's 32 tokens
+                    Op ka[D / 16];
+#pragma unroll
+                    for (int s = 0; s < D / 16; ++s) ka[s] = load_k_op<T, D, kDecUnit>(kt, l32, 16 * s + 8 * hl);
+                    f32x16 sacc;
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
+#pragma unroll
+                    for (int s = 0; s < D / 16; ++s) sacc = MM::mma(ka[s], qf[s], sacc);
+                    float mx = -INFINITY;
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int toff = toff0 + 8 * (i >> 2) + 4 * hl + (i & 3);
+                        const float v = fmaf(sacc[i], p.scale_log2, b2);
+                        sacc[i] = toff > lim ? -INFINITY : v;
+                        mx = fmaxf(mx, sacc[i]);
+                    }
+                    mx = pair32_max(mx);
+                    // lazy rescaling: the reference maximum moves only when the unit's
+                    // maximum exceeds it by more than 8 (probabilities stay <= 2^8)
+                    const bool grow = mx > m_run + 8.f;
+                    const float alpha = grow ? fast_exp2(m_run - mx) : 1.f;
+                    m_run = grow ? mx : m_run;
+                    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+                    float ps = 0.f;
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const float pv = fast_exp2(sacc[i] - m_use);
+                        sacc[i] = pv;
+                    }
+                    Op pb[2];
+#pragma unroll
+                    for (int s2 = 0; s2 < 2; ++s2) {
+                        float pv8[8];
+#pragma unroll
+                        for (int e8 = 0; e8 < 8; ++e8) pv8[e8] = sacc[8 * s2 + e8];
+                        pb[s2] = MM::pack(pv8);
+                        ps = MM::sum(pb[s2], pv8, ps);            // the denominator sums what the MFMA sees
+                    }
+                    l_run = fmaf(l_run, alpha, ps);
+                    if (ballot(grow) != 0) {
+#pragma unroll
+                        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                            for (int i = 0; i < 16; ++i) o_acc[db][i] *= alpha;
+                    }
+#pragma unroll
+                    for (int s2 = 0; s2 < 2; ++s2) {
+                        Op va[D / 32];
+#pragma unroll
+                        for (int db = 0; db < D / 32; ++db) va[db] = load_vt_op<T, D, kDecUnit>(vt, s2, db, lane);
+#pragma unroll
+                        for (int db = 0; db < D / 32; ++db) o_acc[db] = MM::mma(va[db], pb[s2], o_acc[db]);
+                    }
+                }
+                w0 = w1;
+            }
+            // ---- the segment's partial, per head: running max, sum, unnormalised output
+            const float l_tot = pair32_sum(l_run);
+            if (pair_ok) {
+                const size_t slot = (size_t)blk + grp;
+                if (hl == 0) {
+                    float* ml = p.part_ml + ((size_t)l32 * p.slots + slot) * 2;
+                    ml[0] = m_run;
+                    ml[1] = l_tot;
+                }
+                float* po = p.part_o + ((size_t)l32 * p.slots + slot) * D;
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                    for (int a = 0; a < 4; ++a) {
+                        f32x4 o;
+                        o[0] = o_acc[db][4 * a]; o[1] = o_acc[db][4 * a + 1];
+                        o[2] = o_acc[db][4 * a + 2]; o[3] = o_acc[db][4 * a + 3];
+                        *reinterpret_cast<f32x4*>(po + 32 * db + 8 * a + 4 * hl) = o;
+                    }
+            }
         }
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            float pv8[8];
-#pragma unroll
-            for (int e8 = 0; e8 < 8; ++e8) pv8[e8] = sacc[8 * s + e8];
-            const Op pb = MM::pack(pv8);
-            Op va[D / 32];
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db)
-                va[db] = MM::load(reinterpret_cast<const T*>(smem + G::KBYTES + (32 * db + l32) * G::VROW) + 32 * wid + 16 * s + 8 * hl);
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db) o_acc[db] = MM::mma(va[db], pb, o_acc[db]);
-        }
-    }
-    // merge the 4 wavefronts' partial softmax states in LDS
-    __syncthreads();
-    float* s_o = reinterpret_cast<float*>(smem);               // [4][32][D]
-    float* s_m = s_o + kDecWaves * 32 * D;                     // [waves][32]
-    float* s_l = s_m + kDecWaves * 32;                         // [waves][32]
-    const float l_tot = pair32_sum(l_run);
-    if (hl == 0) { s_m[wid * 32 + l32] = m_run; s_l[wid * 32 + l32] = l_tot; }
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int d = 32 * db + 8 * (i >> 2) + 4 * hl + (i & 3);
-            s_o[(wid * 32 + l32) * D + d] = o_acc[db][i];
-        }
-    __syncthreads();
-    float* part = p.partials + ((grp * p.max_slices + slice) * (size_t)g) * (D + 2);
-    for (int q = tid; q < g * D; q += kDecThreads) {
-        const int pr = q / D, d = q % D;
-        float mstar = -INFINITY;
-        for (int w = 0; w < kDecWaves; ++w) mstar = fmaxf(mstar, s_m[w * 32 + pr]);
-        const float mu = (mstar == -INFINITY) ? 0.f : mstar;
-        float o = 0.f, l = 0.f;
-        for (int w = 0; w < kDecWaves; ++w) {
-            const float f = fast_exp2(s_m[w * 32 + pr] - mu);
-            o += f * s_o[(w * 32 + pr) * D + d];
-            l += f * s_l[w * 32 + pr];
-        }
-        float* pp = part + (size_t)pr * (D + 2);
-        if (d == 0) { pp[0] = mstar; pp[1] = l; }
-        pp[2 + d] = o;
     }
 }
 
 // ---------------------------------------------------------------------------------
-// One workgroup of 1024 threads per (head, b): slice maxima and weighted sums by
-// block reductions, then 1024/D thread groups each sum a share of the slices'
-// outputs (the work is a few loads per thread; more threads shorten the chain).
-constexpr int kCombThreads = 1024;
+// One workgroup per (b, query head, quarter of d): the partial slots of the head's
+// group (first .. last, written by the attention kernel) sit contiguously in part_o
+// for one head, D floats apart. Threads split them into slot lanes x column quads;
+// each thread merges its slots with a running maximum (its loads of a batch issued
+// together), then the slot lanes are merged in LDS.
+constexpr int kCombParts = 4;
 template <int D>
 __global__ __launch_bounds__(kCombThreads) void decode_combine_kernel(DecodeParams p) {
-    constexpr int NG = kCombThreads / D;            // thread groups splitting the slices
-    constexpr int NW = kCombThreads / 64;
-    extern __shared__ float s_f[];                  // [max_slices] slice factors
-    __shared__ float red[2][NW];
-    __shared__ float s_acc[NG][D];
-    const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
-    const int hh = blockIdx.x, bi = blockIdx.y;
+    constexpr int DQ = D / 4 / kCombParts;         // column quads of this workgroup
+    constexpr int SL = kCombThreads / DQ;          // slot lanes
+    constexpr int NB = 8;                          // slots per thread and batch
+    __shared__ float s_m[SL][DQ], s_l[SL][DQ];
+    __shared__ f32x4 s_acc[SL][DQ];
+    const int tid = threadIdx.x;
+    const int hh = blockIdx.x, bi = blockIdx.y, part = blockIdx.z;
     const int g = p.g, r = hh / g, pr = hh % g;
-    const size_t grp = (size_t)bi * p.h_kv + r;
-    const int E = p.cnt[grp] + 1;
-    const int nsl = (E * p.B + p.slice_tokens - 1) / p.slice_tokens;
-    const float* base = p.partials + (grp * p.max_slices * (size_t)g + pr) * (D + 2);
-    const size_t sstride = (size_t)g * (D + 2);
-    float mx = -INFINITY;
-    for (int s = tid; s < nsl; s += kCombThreads) mx = fmaxf(mx, base[s * sstride]);
-    mx = wave_max(mx);
-    if (lane == 0) red[0][wid] = mx;
-    __syncthreads();
-    float mstar = -INFINITY;
+    const int grp = bi * p.h_kv + r;
+    const int first = p.ranges[2 * grp], n = p.ranges[2 * grp + 1] - first + 1;
+    const int sl = tid / DQ, dq = tid % DQ;
+    const int d0 = part * (D / kCombParts) + 4 * dq;
+    const float* ml = p.part_ml + ((size_t)pr * p.slots + first) * 2;
+    const float* po = p.part_o + ((size_t)pr * p.slots + first) * D + d0;
+    float m_t = -INFINITY, l_t = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int j0 = sl; j0 < n; j0 += NB * SL) {
+        f32x4 v[NB];
+        float mj[NB], lj[NB];
 #pragma unroll
-    for (int w = 0; w < NW; ++w) mstar = fmaxf(mstar, red[0][w]);
-    const float mu = (mstar == -INFINITY) ? 0.f : mstar;
-    float ls = 0.f;
-    for (int s = tid; s < nsl; s += kCombThreads) {
-        const float f = fast_exp2(base[s * sstride] - mu);
-        s_f[s] = f;
-        ls += f * base[s * sstride + 1];
+        for (int u = 0; u < NB; ++u) {
+            const int j = j0 + u * SL;
+            const bool ok = j < n;
+            v[u] = ok ? *reinterpret_cast<const f32x4*>(po + (size_t)j * D) : f32x4{0.f, 0.f, 0.f, 0.f};
+            mj[u] = ok ? ml[2 * j] : -INFINITY;
+            lj[u] = ok ? ml[2 * j + 1] : 0.f;
+        }
+        float mb = m_t;
+#pragma unroll
+        for (int u = 0; u < NB; ++u) mb = fmaxf(mb, mj[u]);
+        const float sc = m_t == -INFINITY ? 0.f : fast_exp2(m_t - mb);
+        acc *= sc;
+        l_t *= sc;
+#pragma unroll
+        for (int u = 0; u < NB; ++u) {
+            const float f = mj[u] == -INFINITY ? 0.f : fast_exp2(mj[u] - mb);
+            acc[0] = fmaf(f, v[u][0], acc[0]); acc[1] = fmaf(f, v[u][1], acc[1]);
+            acc[2] = fmaf(f, v[u][2], acc[2]); acc[3] = fmaf(f, v[u][3], acc[3]);
+            l_t = fmaf(f, lj[u], l_t);
+        }
+        m_t = mb;
     }
-    ls = wave_sum(ls);
-    if (lane == 0) red[1][wid] = ls;
-    __syncthreads();
-    float l = 0.f;
+    s_m[sl][dq] = m_t;
+    s_l[sl][dq] = l_t;
+    s_acc[sl][dq] = acc;
+    // merge the slot lanes pairwise (fixed tree order)
 #pragma unroll
-    for (int w = 0; w < NW; ++w) l += red[1][w];
-    const int gq = tid / D, d = tid % D;
-    float acc = 0.f;
-#pragma unroll 4
-    for (int s = gq; s < nsl; s += NG) acc += s_f[s] * base[s * sstride + 2 + d];
-    s_acc[gq][d] = acc;
+    for (int half = SL / 2; half >= 1; half >>= 1) {
+        __syncthreads();
+        if (sl < half) {
+            const float ma = s_m[sl][dq], mb = s_m[sl + half][dq];
+            const float M = fmaxf(ma, mb);
+            const float fa = ma == -INFINITY ? 0.f : fast_exp2(ma - M);
+            const float fb = mb == -INFINITY ? 0.f : fast_exp2(mb - M);
+            s_m[sl][dq] = M;
+            s_l[sl][dq] = fa * s_l[sl][dq] + fb * s_l[sl + half][dq];
+            s_acc[sl][dq] = fa * s_acc[sl][dq] + fb * s_acc[sl + half][dq];
+        }
+    }
     __syncthreads();
-    if (gq == 0) {
-        float o = 0.f;
-#pragma unroll
-        for (int k = 0; k < NG; ++k) o += s_acc[k][d];
-        const float val = o / l;
-        const size_t oi = ((size_t)bi * p.h_q + hh) * D + d;
-        if (p.out_bf16) static_cast<uint16_t*>(p.O)[oi] = f32_to_bf16_bits(val);
-        else static_cast<float*>(p.O)[oi] = val;
+    if (tid < DQ) {
+        const float L = s_l[0][tid];
+        const f32x4 o = s_acc[0][tid];
+        const float inv = 1.f / L;
+        const size_t oi = ((size_t)bi * p.h_q + hh) * D + part * (D / kCombParts) + 4 * tid;
+        if (p.out_bf16) {
+            u32x2 ob;
+            ob[0] = (uint32_t)f32_to_bf16_bits(o[0] * inv) | ((uint32_t)f32_to_bf16_bits(o[1] * inv) << 16);
+            ob[1] = (uint32_t)f32_to_bf16_bits(o[2] * inv) | ((uint32_t)f32_to_bf16_bits(o[3] * inv) << 16);
+            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.O) + oi) = ob;
+        } else {
+            *reinterpret_cast<f32x4*>(static_cast<float*>(p.O) + oi) = o * inv;
+        }
     }
 }
 
 // ---------------------------------------------------------------------------------
-void decode_geometry(int L_cap, int kbar_cap, int B, int* T_route, int* slice_tokens,
-                     int* max_slices) {
-    const int tr = min((L_cap - 1) / B, kbar_cap);
-    *T_route = tr;
-    *slice_tokens = kDecSlice;
-    *max_slices = ((tr + 1) * B + kDecSlice - 1) / kDecSlice;
-}
+int decode_partial_slots(int b, int h_kv) { return kMaxStreams + b * h_kv; }
 
 int pmode_of(float alpha);
 
-template <int VPL, int PM>
-static hipError_t launch_dec_route_pm(const DecodeParams& p, int b, hipStream_t s) {
-    constexpr size_t lds = (size_t)16 * VPL * 64 * sizeof(float);
-    static hipError_t configured = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_route_kernel<VPL, PM>),
-                                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (configured != hipSuccess) return configured;
-    hipLaunchKernelGGL((decode_route_kernel<VPL, PM>), dim3(p.h_kv, b), dim3(1024), lds, s, p);
+template <int VPT, int PM>
+static hipError_t launch_dec_route_pm(const DecodeParams& p, int ngroups, hipStream_t s) {
+    const int nblk = (ngroups + 7) / 8 * 8 * p.g;
+    hipLaunchKernelGGL((decode_route_kernel<VPT, PM>), dim3(nblk), dim3(kRouteThreads), 0, s, p, ngroups);
     return hipSuccess;
 }
 
-template <int VPL>
-static hipError_t launch_dec_route(const DecodeParams& p, int b, hipStream_t s) {
+template <int VPT>
+static hipError_t launch_dec_route(const DecodeParams& p, int ngroups, hipStream_t s) {
     switch (p.pmode) {
-        case kDecSoftmax: return launch_dec_route_pm<VPL, kDecSoftmax>(p, b, s);
-        case 1: return launch_dec_route_pm<VPL, 1>(p, b, s);
-        case 2: return launch_dec_route_pm<VPL, 2>(p, b, s);
-        case 4: return launch_dec_route_pm<VPL, 4>(p, b, s);
-        default: return launch_dec_route_pm<VPL, 0>(p, b, s);
+        case kDecSoftmax: return launch_dec_route_pm<VPT, kDecSoftmax>(p, ngroups, s);
+        case 1: return launch_dec_route_pm<VPT, 1>(p, ngroups, s);
+        case 2: return launch_dec_route_pm<VPT, 2>(p, ngroups, s);
+        case 4: return launch_dec_route_pm<VPT, 4>(p, ngroups, s);
+        default: return launch_dec_route_pm<VPT, 0>(p, ngroups, s);
     }
 }
 
+// Ring stages and wavefronts resident per CU of the attention kernel.
+template <typename T, int D> struct DecAttnCfg {
+    static constexpr int NST = sizeof(T) == 2 ? 2 : 2;
+    static constexpr size_t LDS = (size_t)NST * SwzTile<T, D, kDecUnit>::STAGE;
+};
+
+static int device_cus() {
+    static int cus = [] {
+        int dev = 0, n = 0;
+        if (hipGetDevice(&dev) != hipSuccess) return 256;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 256;
+        return n;
+    }();
+    return cus;
+}
+
 template <typename T, int D>
-static hipError_t launch_decode_t(const DecodeParams& p, const DecodeArgs& a, hipStream_t s) {
-    constexpr size_t lds = TileGeom<T, D, kDecTT>::BYTES + 64 * 12;   // + chunk, bias, first row
-    static_assert(TileGeom<T, D, kDecTT>::BYTES >= kDecWaves * (32 * D + 64) * 4, "LDS merge space");
-    static hipError_t configured = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_attn_kernel<T, D>),
-                                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+static hipError_t launch_decode_t(DecodeParams p, const DecodeArgs& a, hipStream_t s) {
+    typedef DecAttnCfg<T, D> C;
+    auto attn = decode_attn_kernel<T, D, C::NST>;
+    static hipError_t configured = hipFuncSetAttribute(reinterpret_cast<const void*>(attn),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::LDS);
     if (configured != hipSuccess) return configured;
-    if (p.T_route > 0) {
-        dim3 g1((p.T_route + 63) / 64, p.h_kv, a.b);
-        hipLaunchKernelGGL((decode_scores_kernel<D>), g1, dim3(256), 0, s, p, a.Q, a.in_bf16);
-    }
-    const hipError_t er = p.T_route <= 256 ? launch_dec_route<4>(p, a.b, s)
-                        : p.T_route <= 1024 ? launch_dec_route<16>(p, a.b, s)
-                                            : launch_dec_route<32>(p, a.b, s);
+    static int per_cu = [&] {
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(attn), 64, C::LDS) != hipSuccess || n < 1)
+            return 1;
+        return n;
+    }();
+    const int ngroups = a.b * a.h_kv;
+    p.streams = min(kMaxStreams, device_cus() * min(per_cu, kDecStreamsPerCU));
+    dim3 g1(max((p.T_route + 63) / 64, 1), p.h_kv, a.b);
+    hipLaunchKernelGGL((decode_scores_kernel<D>), g1, dim3(256), 0, s, p, a.Q, a.in_bf16);
+    const hipError_t er = p.T_route <= 256 ? launch_dec_route<1>(p, ngroups, s)
+                        : p.T_route <= 512 ? launch_dec_route<2>(p, ngroups, s)
+                        : p.T_route <= 1024 ? launch_dec_route<4>(p, ngroups, s)
+                                            : launch_dec_route<8>(p, ngroups, s);
     if (er != hipSuccess) return er;
-    hipLaunchKernelGGL((decode_attn_kernel<T, D>), dim3(p.max_slices, p.h_kv, a.b), dim3(kDecThreads), lds, s, p);
-    hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(p.h_q, a.b), dim3(kCombThreads),
-                       (size_t)p.max_slices * sizeof(float), s, p);
+    hipLaunchKernelGGL(attn, dim3(p.streams), dim3(64), C::LDS, s, p, ngroups);
+    hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(p.h_q, a.b, kCombParts), dim3(kCombThreads), 0, s, p);
     return hipGetLastError();
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
     DecodeParams p;
     p.Q = a.Q; p.Kc = a.Kc; p.Vc = a.Vc; p.kbar = a.kbar; p.seq_len = a.seq_len;
-    p.h_q = a.h_q; p.h_kv = a.h_kv; p.L_cap = a.L_cap; p.kbar_cap = a.kbar_cap; p.B = a.B;
+    p.b = a.b; p.h_q = a.h_q; p.h_kv = a.h_kv; p.L_cap = a.L_cap; p.kbar_cap = a.kbar_cap; p.B = a.B;
     p.g = a.h_q / a.h_kv;
     p.log2g = 0;
     while ((1 << p.log2g) < p.g) ++p.log2g;
-    p.T_route = a.T_route; p.list_cap = a.list_cap; p.max_slices = a.max_slices;
-    p.slice_tokens = a.slice_tokens;
+    p.T_route = a.T_route; p.list_cap = a.list_cap;
     p.cs = route_scale(a.alpha, a.gamma, a.d);
     p.pexp = (float)(1.0 / ((double)a.alpha - 1.0));
     p.pmode = pmode_of(a.alpha);
@@ -554,7 +743,9 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
     p.scale_log2 = (float)(1.4426950408889634 / sqrt((double)a.d));
     p.out_bf16 = a.out_bf16;
     p.O = a.O; p.idx = a.idx; p.bias = a.bias; p.cnt = a.cnt; p.w_out = a.w_out;
-    p.scores = a.scores; p.partials = a.partials;
+    p.scores = a.scores; p.counters = a.counters; p.ranges = a.counters + a.b * a.h_kv; p.part_ml = a.part_ml; p.part_o = a.part_o;
+    p.slots = decode_partial_slots(a.b, a.h_kv);
+    p.streams = kMaxStreams;
     p.pages = a.pages; p.pages_per_seq = a.pages_per_seq; p.num_pages = a.num_pages;
     if (a.in_bf16) return a.d == 64 ? launch_decode_t<uint16_t, 64>(p, a, s) : launch_decode_t<uint16_t, 128>(p, a, s);
     return a.d == 64 ? launch_decode_t<float, 64>(p, a, s) : launch_decode_t<float, 128>(p, a, s);

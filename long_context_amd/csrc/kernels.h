@@ -110,18 +110,19 @@ struct DecodeArgs {
     void* O; bool out_bf16;
     int32_t* idx; float* bias; int32_t* cnt; float* w_out; int list_cap;
     float* scores;       // [b, h_q, T_route] workspace
-    float* partials;     // [b, h_kv, max_slices, g, d + 2] workspace
+    int32_t* counters;   // [3, b, h_kv] workspace: arrival counters (cleared by the
+                         // kernels), then each group's first and last partial slot
+    float* part_ml;      // [g, decode_partial_slots, 2] workspace
+    float* part_o;       // [g, decode_partial_slots, d] workspace
     int T_route;         // routable chunk capacity: min(floor((L_cap-1)/B), kbar_cap)
-    int max_slices;
-    int slice_tokens;
     // paged cache (pages != nullptr): Kc/Vc are [num_pages, h_kv, B, d], chunk c of
     // sequence b lives in page pages[b * pages_per_seq + c], L_cap = pages_per_seq * B
     const int32_t* pages = nullptr;
     int pages_per_seq = 0, num_pages = 0;
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
-// Split-KV geometry of the decode kernels for a given cache capacity.
-void decode_geometry(int L_cap, int kbar_cap, int B, int* T_route, int* slice_tokens,
-                     int* max_slices);
+// Partial-result slots of the split-KV decode: one per (attention wavefront, group it
+// touches), at most the wavefront count bound plus b * h_kv.
+int decode_partial_slots(int b, int h_kv);
 
 }  // namespace dash
