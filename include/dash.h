@@ -257,6 +257,28 @@ dash_status dash_attend_decode(const void* Q, const void* Kc, const void* Vc, in
                                void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * For callers that cannot allocate (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): dash_attend_decode without a workspace
+ * argument. The kernels' scratch (scores, routed lists, counters, split-KV
+ * partials) lives in a library-owned device array of DASH_NOALLOC_SCRATCH_BYTES
+ * that each GPU the library runs on holds until the process ends; the call makes
+ * no allocation of any kind. Shapes whose decode workspace
+ * (dash_workspace_bytes(DASH_OP_DECODE, ...)) exceeds it return DASH_ERR_WORKSPACE
+ * before anything is enqueued. Every call on one GPU shares that GPU's array and
+ * leaves its contents behind (the kernels clear what they count), so calls that
+ * overlap on one GPU (other streams, other threads) race. Arguments and outputs are
+ * otherwise those of dash_attend_decode.
+ */
+#define DASH_NOALLOC_SCRATCH_BYTES (32u << 20)
+dash_status dash_attend_decode_noalloc(const void* Q, const void* Kc, const void* Vc, int in_dtype,
+                                       const float* kbar, const int32_t* seq_len,
+                                       int b, int h_q, int h_kv, int L_cap, int kbar_cap, int d, int B,
+                                       float alpha, float gamma, float sigma,
+                                       void* O, int out_dtype,
+                                       int32_t* idx_out, float* bias_out, int32_t* cnt_out,
+                                       float* w_out, int list_cap, void* stream);
+
+/*
  * Paged KV cache (serving): pages of one chunk each. Kp, Vp are
  * [num_pages, h_kv, B, d]; chunk c of sequence b (tokens cB .. cB+B-1) lives in
  * page pages[b * pages_per_seq + c] (device int32 table [b, pages_per_seq]), so a

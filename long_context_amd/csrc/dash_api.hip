@@ -10,6 +10,8 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
+
 namespace {
 
 thread_local char g_err[512] = "";
@@ -75,6 +77,32 @@ DecodeLayout decode_layout(int b, int h_q, int h_kv, int L_cap, int kbar_cap, in
     L.off_o = align256(L.off_ml + (size_t)g * slots * 2 * 4);
     L.total = align256(L.off_o + (size_t)g * slots * d * 4);
     return L;
+}
+
+// Device scratch of dash_attend_decode_noalloc: a file-scope array that every GPU the
+// library runs on holds until the process ends. Host code never passes the array's
+// name to a kernel (on the host it is only a stand-in for the symbol): it asks each
+// device once for the array's address there and keeps that pointer per device.
+static __device__ __align__(256) unsigned char scratch[DASH_NOALLOC_SCRATCH_BYTES];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+dash_status scratch_of_current_device(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(DASH_ERR_LAUNCH, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(DASH_ERR_UNSUPPORTED, "device %d beyond the scratch table", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr)
+            return fail(DASH_ERR_LAUNCH, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return DASH_OK;
 }
 
 }  // namespace
@@ -383,6 +411,27 @@ dash_status dash_attend_decode(const void* Q, const void* Kc, const void* Vc, in
     return attend_decode(Q, Kc, Vc, in_dtype, kbar, seq_len, b, h_q, h_kv, L_cap, kbar_cap, d, B, alpha, gamma,
                          sigma, O, out_dtype, idx_out, bias_out, cnt_out, w_out, list_cap, ws, ws_bytes, stream,
                          nullptr, 0, 0);
+}
+
+dash_status dash_attend_decode_noalloc(const void* Q, const void* Kc, const void* Vc, int in_dtype,
+                                       const float* kbar, const int32_t* seq_len,
+                                       int b, int h_q, int h_kv, int L_cap, int kbar_cap, int d, int B,
+                                       float alpha, float gamma, float sigma,
+                                       void* O, int out_dtype,
+                                       int32_t* idx_out, float* bias_out, int32_t* cnt_out,
+                                       float* w_out, int list_cap, void* stream) {
+    if (b >= 1 && h_kv >= 1 && h_q >= h_kv && h_q % h_kv == 0 && L_cap >= 1 && B >= 1 && d >= 1) {
+        const size_t need = decode_layout(b, h_q, h_kv, L_cap, kbar_cap < 0 ? 0 : kbar_cap, d, B).total;
+        if (need > DASH_NOALLOC_SCRATCH_BYTES)
+            return fail(DASH_ERR_WORKSPACE, "decode needs %zu scratch bytes; the no-allocation scratch holds %zu",
+                        need, (size_t)DASH_NOALLOC_SCRATCH_BYTES);
+    }
+    void* ws = nullptr;
+    const dash_status st = scratch_of_current_device(&ws);
+    if (st != DASH_OK) return st;
+    return attend_decode(Q, Kc, Vc, in_dtype, kbar, seq_len, b, h_q, h_kv, L_cap, kbar_cap, d, B, alpha, gamma,
+                         sigma, O, out_dtype, idx_out, bias_out, cnt_out, w_out, list_cap, ws,
+                         DASH_NOALLOC_SCRATCH_BYTES, stream, nullptr, 0, 0);
 }
 
 dash_status dash_attend_decode_paged(const void* Q, const void* Kp, const void* Vp, int in_dtype,

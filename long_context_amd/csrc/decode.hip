@@ -38,7 +38,7 @@ namespace dash {
 constexpr int kDecUnit = 32;          // tokens per stream unit (one 32x32 S^T block)
 constexpr int kDecSoftmax = -1;       // pmode of α = 1 (softmax routing)
 constexpr int kRouteThreads = 256;    // workgroup of the per-head router
-constexpr int kMaxStreams = 2048;     // upper bound of the attention wavefronts
+constexpr int kMaxStreams = 1024;     // upper bound of the attention wavefronts
 constexpr int kCombThreads = 512;
 // Attention wavefronts per compute unit: more streams add in-flight copies but also
 // partial results, which the next kernel must read back.

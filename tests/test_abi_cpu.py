@@ -197,6 +197,17 @@ def test_decode_workspace_checks(dash):
     assert _decode(dash, need, L=300000) == dash.DASH_ERR_UNSUPPORTED      # 2343 chunks > 2048
 
 
+def test_decode_noalloc_rejects_shapes_beyond_its_scratch(dash):
+    """The entry point without a workspace refuses, before touching any device, a
+    shape whose decode workspace exceeds the library's scratch (32 MiB)."""
+    b, h_q, h_kv, d, L, B = 512, 32, 2, 128, 131072, 128
+    assert dash.dash_workspace_bytes(dash.DASH_OP_DECODE, b, h_q, h_kv, L, d, B) > (32 << 20)
+    st = dash.lib.dash_attend_decode_noalloc(P, P, P, dash.DASH_BF16, P, P, b, h_q, h_kv, L, L // B, d, B,
+                                             1.5, 1.0, 1.0, P, dash.DASH_BF16, NUL, NUL, NUL, NUL, 0, NUL)
+    assert st == dash.DASH_ERR_WORKSPACE
+    assert b"scratch" in dash.lib.dash_last_error()
+
+
 def test_workspace_sizes(dash):
     # route: split summaries, b * h_kv * (T_c rounded up to 32) * 3 * d * 2 bytes
     assert dash.dash_workspace_bytes(dash.DASH_OP_ROUTE, 1, 32, 2, 32768, 128, 64) == 2 * 512 * 3 * 128 * 2
