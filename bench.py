@@ -54,27 +54,29 @@ def parse():
     return ap.parse_args()
 
 
-# Files that define the Stage-2 prefill kernel: a traffic figure measured with
-# hardware counters is reported only while they are unchanged.
-KERNEL_SOURCES = ["long_context_amd/csrc/attend_prefill_bf16.hip", "long_context_amd/csrc/prefill_common.h",
-                  "long_context_amd/csrc/attn_common.h", "long_context_amd/csrc/common.h"]
+# Counter summaries (profiles/): an HBM traffic figure measured with hardware
+# counters is reported only while the sources of the kernels it covers are unchanged.
+COMMON_SOURCES = ["long_context_amd/csrc/attn_common.h", "long_context_amd/csrc/common.h"]
+STAGE2_SOURCES = ["long_context_amd/csrc/attend_prefill_bf16.hip", "long_context_amd/csrc/prefill_common.h"] + COMMON_SOURCES
+DECODE_SOURCES = ["long_context_amd/csrc/decode.hip"] + COMMON_SOURCES
 TRAFFIC_FILE = "profiles/sparse_prior_attn_bf16_kernel_prefill_32k_traffic.txt"
+DECODE_TRAFFIC_FILE = "profiles/decode_128k_b4_traffic.txt"
 
 
-def kernel_source_hash():
+def kernel_source_hash(files=STAGE2_SOURCES):
     import hashlib
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in files:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
 
-def measured_traffic():
-    """HBM bytes per launch of the Stage-2 kernel from the committed counter summary
-    (FETCH_SIZE + WRITE_SIZE scaled by a plain copy's readings), or None when the
-    summary is missing or the kernel sources changed since it was taken."""
-    path = os.path.join(ROOT, TRAFFIC_FILE)
+def measured_traffic(path=TRAFFIC_FILE, sources=STAGE2_SOURCES, key="traffic_bytes_per_launch"):
+    """HBM bytes per launch (or step) from a committed counter summary (FETCH_SIZE +
+    WRITE_SIZE scaled by a plain copy's readings), or None when the summary is missing
+    or the kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, path)
     if not os.path.exists(path):
         return None
     vals = {}
@@ -82,10 +84,10 @@ def measured_traffic():
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
-    if vals.get("source_sha256") != kernel_source_hash():
+    if vals.get("source_sha256") != kernel_source_hash(sources):
         return None
     try:
-        return float(vals["traffic_bytes_per_launch"])
+        return float(vals[key])
     except (KeyError, ValueError):
         return None
 
@@ -572,7 +574,9 @@ def main():
         out["decode_32k_b16"] = dec32
         out["decode_roofline"] = {"bound": "hbm", "kernel": "decode (route + split-KV + combine)",
                                   "achieved": dec["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                                  "frac": dec["hbm_frac"], "traffic": None}
+                                  "frac": dec["hbm_frac"],
+                                  "traffic": measured_traffic(DECODE_TRAFFIC_FILE, DECODE_SOURCES,
+                                                              "traffic_bytes_per_step")}
     del pre
     torch.cuda.empty_cache()
     if not args.no_cpu:
