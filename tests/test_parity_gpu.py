@@ -524,3 +524,38 @@ def test_decode_graph_replay_matches_eager():
         torch.cuda.synchronize()
         _log(f"graph replay {k}: max |diff| {float((O - O_eager).abs().max()):.3e}")
         assert torch.equal(O, O_eager), f"replay {k} differs from the eager step"
+
+
+# ------------------------------------------------------------------------------------
+# The pages' efficiency operating points (paper review section 六, 6.2 efficiency
+# table): 96K-token prefill and decode at batch 24, B = 64, 32 query / 2 KV heads,
+# γ calibrated to the stated group sparsity; the benchmark's launch, sampled rows.
+# ------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("sparsity", [0.75, 0.9375])
+def test_efficiency_prefill_96k_sampled_rows(sparsity):
+    """1536 chunks per row group: the router splits every row over four wavefronts."""
+    G = _gu()
+    w = inputs.efficiency_prefill(96 * 1024, sparsity)
+    _log(f"efficiency prefill 96K sparsity {sparsity} gamma {w.gamma}")
+    g = G.gpu_prefill(w)
+    rows = _sample_rows(w.n, w.B, 30, 13)
+    kb, rt, Oref = G.oracle_prefill_rows(w, rows)
+    assert np.abs(g["kbar"].cpu().numpy() - kb).max() <= G.TOL_KBAR
+    nex, tot = G.compare_route(g, rt, rows, w.n // w.B)
+    err = G.compare_out(g["O"][:, :, rows].cpu().numpy(), Oref, rt["margin"] <= G.MARGIN, w.g, "bf16")
+    from oracle import dash_oracle as O
+    _log(f"efficiency prefill 96K: exempt {nex}/{tot}, row error {err:.3e}, "
+         f"sampled-row group sparsity {O.group_sparsity(rt):.3f}")
+
+
+@pytest.mark.parametrize("sparsity", [0.75, 0.9375])
+def test_efficiency_decode_96k_b24(sparsity):
+    w = inputs.efficiency_decode(sparsity)
+    _log(f"efficiency decode 96K b24 sparsity {sparsity} gamma {w.gamma}")
+    g = gpu_decode(w, w.seq_len)
+    nex, err = check_decode(w, w.seq_len, g)
+    cnt = g["cnt"].cpu().numpy()
+    vis = (w.seq_len - 1) // w.B
+    _log(f"efficiency decode 96K: exempt groups {nex}, row error {err:.3e}, "
+         f"group sparsity {1.0 - cnt.sum() / (vis[:, None] * np.ones_like(cnt)).sum():.3f}")
