@@ -257,6 +257,23 @@ dash_status dash_attend_decode(const void* Q, const void* Kc, const void* Vc, in
                                void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Decode with a fixed routing budget (an ablation of the adaptive support; the
+ * decode counterpart of dash_route_topk): each group keeps only the top_k largest
+ * group weights w among its routed chunks (all of them when it has at most top_k;
+ * equal weights go to the lower chunk id first), and μ and the bias d of
+ * Proposition 4.1 are taken over the kept chunks. top_k = 0 is dash_attend_decode;
+ * top_k < 0 returns DASH_ERR_PARAM. Everything else as in dash_attend_decode.
+ */
+dash_status dash_attend_decode_topk(const void* Q, const void* Kc, const void* Vc, int in_dtype,
+                                    const float* kbar, const int32_t* seq_len,
+                                    int b, int h_q, int h_kv, int L_cap, int kbar_cap, int d, int B,
+                                    float alpha, float gamma, float sigma,
+                                    void* O, int out_dtype,
+                                    int32_t* idx_out, float* bias_out, int32_t* cnt_out,
+                                    float* w_out, int list_cap, int top_k,
+                                    void* ws, size_t ws_bytes, void* stream);
+
+/*
  * For callers that cannot allocate (code under HIP graph capture, tight serving
  * loops, harnesses that forbid allocation): dash_attend_decode without a workspace
  * argument. The kernels' scratch (scores, routed lists, counters, split-KV

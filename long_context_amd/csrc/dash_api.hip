@@ -363,8 +363,9 @@ static dash_status attend_decode(const void* Q, const void* Kc, const void* Vc, 
                                  int32_t* idx_out, float* bias_out, int32_t* cnt_out,
                                  float* w_out, int list_cap,
                                  void* ws, size_t ws_bytes, void* stream,
-                                 const int32_t* pages, int pages_per_seq, int num_pages) {
+                                 const int32_t* pages, int pages_per_seq, int num_pages, int top_k = 0) {
     if (!Q || !Kc || !Vc || !kbar || !seq_len || !O) return fail(DASH_ERR_NULL, "Q, Kc, Vc, kbar, seq_len and O must be non-null");
+    if (top_k < 0) return fail(DASH_ERR_PARAM, "top_k must be >= 0 (got %d)", top_k);
     const int given = (idx_out != nullptr) + (bias_out != nullptr) + (cnt_out != nullptr);
     if (given != 0 && given != 3) return fail(DASH_ERR_NULL, "idx_out, bias_out and cnt_out must be all NULL or all non-null");
     if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return fail(DASH_ERR_PARAM, "bad dtype");
@@ -397,6 +398,7 @@ static dash_status attend_decode(const void* Q, const void* Kc, const void* Vc, 
     a.part_o = reinterpret_cast<float*>(w + Lo.off_o);
     a.T_route = Lo.T_route;
     a.pages = pages; a.pages_per_seq = pages_per_seq; a.num_pages = num_pages;
+    a.top_k = top_k;
     return from_hip(dash::launch_decode(a, (hipStream_t)stream), "decode kernels");
 }
 
@@ -411,6 +413,19 @@ dash_status dash_attend_decode(const void* Q, const void* Kc, const void* Vc, in
     return attend_decode(Q, Kc, Vc, in_dtype, kbar, seq_len, b, h_q, h_kv, L_cap, kbar_cap, d, B, alpha, gamma,
                          sigma, O, out_dtype, idx_out, bias_out, cnt_out, w_out, list_cap, ws, ws_bytes, stream,
                          nullptr, 0, 0);
+}
+
+dash_status dash_attend_decode_topk(const void* Q, const void* Kc, const void* Vc, int in_dtype,
+                                    const float* kbar, const int32_t* seq_len,
+                                    int b, int h_q, int h_kv, int L_cap, int kbar_cap, int d, int B,
+                                    float alpha, float gamma, float sigma,
+                                    void* O, int out_dtype,
+                                    int32_t* idx_out, float* bias_out, int32_t* cnt_out,
+                                    float* w_out, int list_cap, int top_k,
+                                    void* ws, size_t ws_bytes, void* stream) {
+    return attend_decode(Q, Kc, Vc, in_dtype, kbar, seq_len, b, h_q, h_kv, L_cap, kbar_cap, d, B, alpha, gamma,
+                         sigma, O, out_dtype, idx_out, bias_out, cnt_out, w_out, list_cap, ws, ws_bytes, stream,
+                         nullptr, 0, 0, top_k);
 }
 
 dash_status dash_attend_decode_noalloc(const void* Q, const void* Kc, const void* Vc, int in_dtype,

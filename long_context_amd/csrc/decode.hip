@@ -50,6 +50,7 @@ struct DecodeParams {
     int b, h_q, h_kv, L_cap, kbar_cap, B, g, log2g, T_route, list_cap, streams;
     float cs, pexp, inv_sigma, scale_log2;
     int pmode, out_bf16;
+    int top_k;           // > 0: keep only the top_k largest group weights of the group
     void* O;
     int32_t* idx; float* bias; int32_t* cnt; float* w_out;
     float* scores;       // [b, h_q, T_route]: raw logits, then each head's weights
@@ -179,6 +180,31 @@ __device__ __forceinline__ float block4_max(float v, float* buf) {
     return r;
 }
 
+// Integer workgroup sum and exclusive prefix (4 wavefronts); `buf` holds 4 ints.
+__device__ __forceinline__ int block4_sum_int(int v, int* buf) {
+    v = wave_sum_int(v);
+    if ((threadIdx.x & 63) == 0) buf[threadIdx.x >> 6] = v;
+    __syncthreads();
+    const int r = (buf[0] + buf[1]) + (buf[2] + buf[3]);
+    __syncthreads();
+    return r;
+}
+__device__ __forceinline__ int block4_excl_scan(int v, int* buf) {
+    const int incl = wave_incl_scan(v);
+    const int wid = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 63) buf[wid] = incl;
+    __syncthreads();
+    int pre = incl - v;
+    for (int w = 0; w < wid; ++w) pre += buf[w];
+    __syncthreads();
+    return pre;
+}
+// Order-preserving map of a float to an unsigned key (larger float, larger key).
+__device__ __forceinline__ uint32_t dec_float_key(float v) {
+    const uint32_t u = __float_as_uint(v);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
 // Hand-off between workgroups of one launch without an agent-scope release fence (on
 // gfx950 it writes back the whole L2, and those write-backs serialise across
 // workgroups): the data goes out through agent-scope relaxed atomic stores, which
@@ -296,7 +322,8 @@ __global__ __launch_bounds__(kRouteThreads) void decode_route_kernel(DecodeParam
         for (int hh = 0; hh < 16; ++hh) hv[k][hh] = hh < g ? rows[(size_t)hh * p.T_route + c] : (SOFT ? -INFINITY : 0.f);
     }
     float wv[VPT];
-    float sl = 0.f, scn = 0.f;
+    bool in[VPT];
+    int ncand = 0;
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
         const int c = VPT * tid + k;
@@ -310,16 +337,45 @@ __global__ __launch_bounds__(kRouteThreads) void decode_route_kernel(DecodeParam
 #pragma unroll
                 for (int hh = 0; hh < 16; ++hh) sm += hh < g ? fast_exp2(hv[k][hh] - m) : 0.f;
                 w = m + fast_log2(sm) - fast_log2((float)g);
-                sl += w; scn += 1.f;
             } else {
 #pragma unroll
                 for (int hh = 0; hh < 16; ++hh) w += hv[k][hh];
                 w *= inv_g;
-                if (w > 0.f) { sl += fast_log2(w); scn += 1.f; }
             }
         }
         wv[k] = w;
+        in[k] = c < nvis && (SOFT || w > 0.f);
+        ncand += in[k] ? 1 : 0;
     }
+    // fixed budget: keep the top_k largest weights (equal weights to the lower chunk):
+    // the top_k-th largest key by bisection on the key bits, counted over the workgroup
+    if (p.top_k > 0 && block4_sum_int(ncand, wcnt) > p.top_k) {     // workgroup-uniform
+        uint32_t key[VPT];
+#pragma unroll
+        for (int k = 0; k < VPT; ++k) key[k] = in[k] ? dec_float_key(wv[k]) : 0u;
+        uint32_t kstar = 0;
+        for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t trial = kstar | (1u << bit);
+            int ge = 0;
+#pragma unroll
+            for (int k = 0; k < VPT; ++k) ge += key[k] >= trial ? 1 : 0;
+            if (block4_sum_int(ge, wcnt) >= p.top_k) kstar = trial;
+        }
+        int gt = 0, eq = 0;
+#pragma unroll
+        for (int k = 0; k < VPT; ++k) { gt += key[k] > kstar ? 1 : 0; eq += (in[k] && key[k] == kstar) ? 1 : 0; }
+        const int need_eq = p.top_k - block4_sum_int(gt, wcnt);
+        int rank = block4_excl_scan(eq, wcnt);           // equal keys of lower chunks
+#pragma unroll
+        for (int k = 0; k < VPT; ++k) {
+            if (in[k] && key[k] == kstar) in[k] = rank++ < need_eq;
+            else in[k] = in[k] && key[k] > kstar;
+        }
+    }
+    float sl = 0.f, scn = 0.f;
+#pragma unroll
+    for (int k = 0; k < VPT; ++k)
+        if (in[k]) { sl += SOFT ? wv[k] : fast_log2(wv[k]); scn += 1.f; }
     const float tsl = block4_sum(sl, red);
     const float tsc = block4_sum(scn, red);
     const float mu2 = tsc > 0.f ? tsl / tsc : 0.f;
@@ -329,14 +385,9 @@ __global__ __launch_bounds__(kRouteThreads) void decode_route_kernel(DecodeParam
     // compaction: thread tid holds chunks VPT*tid .. VPT*tid+VPT-1, so a chunk's list
     // position is the workgroup's exclusive prefix of the per-thread counts plus its
     // rank inside the thread
-    bool in[VPT];
     int mine = 0;
 #pragma unroll
-    for (int k = 0; k < VPT; ++k) {
-        const int c = VPT * tid + k;
-        in[k] = SOFT ? c < nvis : wv[k] > 0.f;
-        mine += in[k] ? 1 : 0;
-    }
+    for (int k = 0; k < VPT; ++k) mine += in[k] ? 1 : 0;
     const int incl = wave_incl_scan(mine);
     if (lane == 63) wcnt[wid] = incl;
     __syncthreads();
@@ -739,6 +790,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
     p.cs = route_scale(a.alpha, a.gamma, a.d);
     p.pexp = (float)(1.0 / ((double)a.alpha - 1.0));
     p.pmode = pmode_of(a.alpha);
+    p.top_k = a.top_k;
     p.inv_sigma = isinf(a.sigma) ? 0.f : (float)(1.0 / (double)a.sigma);
     p.scale_log2 = (float)(1.4426950408889634 / sqrt((double)a.d));
     p.out_bf16 = a.out_bf16;

@@ -115,6 +115,7 @@ struct DecodeArgs {
     float* part_ml;      // [g, decode_partial_slots, 2] workspace
     float* part_o;       // [g, decode_partial_slots, d] workspace
     int T_route;         // routable chunk capacity: min(floor((L_cap-1)/B), kbar_cap)
+    int top_k = 0;       // > 0: a fixed budget of routed chunks per group
     // paged cache (pages != nullptr): Kc/Vc are [num_pages, h_kv, B, d], chunk c of
     // sequence b lives in page pages[b * pages_per_seq + c], L_cap = pages_per_seq * B
     const int32_t* pages = nullptr;

@@ -3,7 +3,7 @@
 // also used as the values:  k̄_c = sum_t softmax_t(<q̄, k_t>/sqrt(d)) k_t.
 //
 // chunk_summary_kernel: one wavefront per (b, r, c). Each lane reads 16 bytes of a
-// key row per iteration (a wave reads 1 KiB contiguous), the row's dot product
+// key row per row group (a wave reads 1 KiB contiguous, 16 row groups in flight), the row's dot product
 // with q̄ is reduced across the lanes that share the row, and an online softmax
 // (log2 domain, fp32) accumulates the weighted keys. The row groups are merged at
 // the end and the fp32 summary is written once. HBM-bound: the K chunk is read
@@ -69,22 +69,34 @@ __global__ __launch_bounds__(256) void chunk_summary_kernel(
 #pragma unroll
     for (int v = 0; v < VEC; ++v) acc[v] = 0.f;
 
-    for (int t0 = 0; t0 < B; t0 += RPI) {
-        float k[VEC];
-        Vec16<T>::load(Kc + (size_t)(t0 + rr) * D, k);
-        float s = 0.f;
+    // the rows of a batch (UNR row groups) are loaded before any is used, so a lane has
+    // UNR 16-byte reads in flight instead of one dependent read per row group
+    constexpr int UNR = 16;
+    for (int b0 = 0; b0 < B; b0 += RPI * UNR) {
+        float kk[UNR][VEC];
 #pragma unroll
-        for (int v = 0; v < VEC; ++v) s = fmaf(q[v], k[v], s);
+        for (int u = 0; u < UNR; ++u) {
+            const int t = b0 + u * RPI + rr;
+            if (t < B) Vec16<T>::load(Kc + (size_t)t * D, kk[u]);
+        }
 #pragma unroll
-        for (int o = LPR / 2; o >= 1; o >>= 1) s += shfl_xor(s, o);
-        s *= scale;
-        const float mn = fmaxf(m, s);
-        const float corr = fast_exp2(m - mn);
-        const float p = fast_exp2(s - mn);
-        l = fmaf(l, corr, p);
+        for (int u = 0; u < UNR; ++u) {
+            if (b0 + u * RPI < B) {                  // wave-uniform: B is a multiple of RPI
+                float s = 0.f;
 #pragma unroll
-        for (int v = 0; v < VEC; ++v) acc[v] = fmaf(acc[v], corr, p * k[v]);
-        m = mn;
+                for (int v = 0; v < VEC; ++v) s = fmaf(q[v], kk[u][v], s);
+#pragma unroll
+                for (int o = LPR / 2; o >= 1; o >>= 1) s += shfl_xor(s, o);
+                s *= scale;
+                const float mn = fmaxf(m, s);
+                const float corr = fast_exp2(m - mn);
+                const float p = fast_exp2(s - mn);
+                l = fmaf(l, corr, p);
+#pragma unroll
+                for (int v = 0; v < VEC; ++v) acc[v] = fmaf(acc[v], corr, p * kk[u][v]);
+                m = mn;
+            }
+        }
     }
     // merge the RPI row groups of the wave
 #pragma unroll

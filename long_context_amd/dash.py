@@ -60,6 +60,9 @@ def _load():
     lib.dash_attend_decode.argtypes = [vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                        f32, f32, f32, vp, i32, vp, vp, vp, vp, i32, vp, sz, vp]
     lib.dash_attend_decode.restype = i32
+    lib.dash_attend_decode_topk.argtypes = [vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                            f32, f32, f32, vp, i32, vp, vp, vp, vp, i32, i32, vp, sz, vp]
+    lib.dash_attend_decode_topk.restype = i32
     lib.dash_attend_decode_noalloc.argtypes = [vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                                f32, f32, f32, vp, i32, vp, vp, vp, vp, i32, vp]
     lib.dash_attend_decode_noalloc.restype = i32
@@ -82,7 +85,7 @@ lib = _load()
 SYMBOLS = ("dash_summarize", "dash_summarize_paged", "dash_summarize_backward", "dash_route", "dash_route_topk",
            "dash_route_stats", "dash_route_backward", "dash_route_mask",
            "dash_attend_prefill", "dash_attend_prefill_lse", "dash_attend_prefill_backward",
-           "dash_attend_decode", "dash_attend_decode_noalloc", "dash_attend_decode_paged",
+           "dash_attend_decode", "dash_attend_decode_topk", "dash_attend_decode_noalloc", "dash_attend_decode_paged",
            "dash_workspace_bytes", "dash_status_string", "dash_last_error")
 
 
@@ -244,17 +247,20 @@ def dash_attend_prefill_backward(Q, K, V, idx, bias, cnt, O, dO, lse, dQ, dK, dV
 
 
 def dash_attend_decode(Q, Kc, Vc, kbar, seq_len, B, alpha, gamma, sigma, O, ws,
-                       idx_out=None, bias_out=None, cnt_out=None, w_out=None, stream=None):
-    """One decode step: Q [b,h_q,1,d] against the KV cache Kc/Vc [b,h_kv,L_cap,d]."""
+                       idx_out=None, bias_out=None, cnt_out=None, w_out=None, stream=None, top_k=0):
+    """One decode step: Q [b,h_q,1,d] against the KV cache Kc/Vc [b,h_kv,L_cap,d].
+    top_k > 0 calls dash_attend_decode_topk (a fixed budget of routed chunks per group)."""
     b, h_q, _, d = Q.shape
     _, h_kv, L_cap, _ = Kc.shape
     list_cap = idx_out.shape[-1] if idx_out is not None else 0
-    _check(lib.dash_attend_decode(_ptr(Q), _ptr(Kc), _ptr(Vc), _dtype(Q), _ptr(kbar),
-                                  _ptr(seq_len), b, h_q, h_kv, L_cap, kbar.shape[2], d, B,
-                                  float(alpha), float(gamma), float(sigma), _ptr(O), _dtype(O),
-                                  _ptr(idx_out), _ptr(bias_out), _ptr(cnt_out), _ptr(w_out),
-                                  list_cap, _ptr(ws), ws.numel() * ws.element_size(),
-                                  _stream(stream)))
+    args = (_ptr(Q), _ptr(Kc), _ptr(Vc), _dtype(Q), _ptr(kbar), _ptr(seq_len), b, h_q, h_kv, L_cap,
+            kbar.shape[2], d, B, float(alpha), float(gamma), float(sigma), _ptr(O), _dtype(O),
+            _ptr(idx_out), _ptr(bias_out), _ptr(cnt_out), _ptr(w_out), list_cap)
+    tail = (_ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    if top_k:
+        _check(lib.dash_attend_decode_topk(*args, int(top_k), *tail))
+    else:
+        _check(lib.dash_attend_decode(*args, *tail))
 
 
 def dash_attend_decode_noalloc(Q, Kc, Vc, kbar, seq_len, B, alpha, gamma, sigma, O,

@@ -588,10 +588,10 @@ def prefill(Q, K, V, qbar, B, alpha, gamma, sigma, causal=True, rows=None, keep_
     return dict(kbar=kbar, route=rt, O=O, rows=rows)
 
 
-def decode(Q, K, V, kbar, seq_len, B, alpha, gamma, sigma, keep_heads=False):
+def decode(Q, K, V, kbar, seq_len, B, alpha, gamma, sigma, keep_heads=False, top_k=0):
     """One decode step: the query Q[b, h_q, 0] sits at position seq_len[b]-1 and sees
-    KV tokens [0, seq_len[b]). Routing uses the cached summaries kbar.
-    Returns dict(route=..., O [b, h_q, 1, d]).
+    KV tokens [0, seq_len[b]). Routing uses the cached summaries kbar (top_k > 0: the
+    fixed routing budget of route()). Returns dict(route=..., O [b, h_q, 1, d]).
     """
     Q = _f64(Q)
     b = Q.shape[0]
@@ -601,7 +601,7 @@ def decode(Q, K, V, kbar, seq_len, B, alpha, gamma, sigma, keep_heads=False):
         L = int(seq_len[bi])
         pos = np.array([[L - 1]])
         rt = route(Q[bi:bi + 1], pos, kbar[bi:bi + 1, :, :L // B], B, alpha, gamma, sigma,
-                   True, L, keep_heads=keep_heads)
+                   True, L, keep_heads=keep_heads, top_k=top_k)
         O = attend(Q[bi:bi + 1], pos, K[bi:bi + 1, :, :L], V[bi:bi + 1, :, :L], rt, B, True, L)
         outs.append(O)
         rts.append(rt)

@@ -197,6 +197,14 @@ def test_decode_workspace_checks(dash):
     assert _decode(dash, need, L=300000) == dash.DASH_ERR_UNSUPPORTED      # 2343 chunks > 2048
 
 
+def test_decode_topk_rejects_negative_budget(dash):
+    need = dash.dash_workspace_bytes(dash.DASH_OP_DECODE, 4, 32, 2, 131072, 128, 128)
+    st = dash.lib.dash_attend_decode_topk(P, P, P, dash.DASH_BF16, P, P, 4, 32, 2, 131072, 1023, 128, 128,
+                                          1.5, 1.0, 1.0, P, dash.DASH_BF16, NUL, NUL, NUL, NUL, 0, -1,
+                                          P, need, NUL)
+    assert st == dash.DASH_ERR_PARAM
+
+
 def test_decode_noalloc_rejects_shapes_beyond_its_scratch(dash):
     """The entry point without a workspace refuses, before touching any device, a
     shape whose decode workspace exceeds the library's scratch (32 MiB)."""
