@@ -80,6 +80,22 @@ dash_status dash_summarize(const void* K, int k_dtype, const float* qbar, float*
                            int chunk_begin, int chunk_end, void* stream);
 
 /*
+ * Ragged batches (sequences of different lengths padded to one n): seq_len [b]
+ * (device int32) gives the tokens of each sequence, clamped to [0, n]. The pages
+ * define every stage per sequence (Eq. 4, Eq. 6 and Eq. 10 see only the
+ * sequence's own tokens), so a ragged batch is the per-sequence computation on
+ * each sequence's first seq_len[b] rows, with T_b = floor(seq_len[b]/B) complete
+ * chunks. Padding rows of Q, K and V are never read and may hold anything.
+ *
+ * dash_summarize_varlen: dash_summarize restricted to chunks c < T_b of each
+ * sequence (the chunk range still applies); k̄ rows of later chunks are not
+ * written. seq_len == NULL returns DASH_ERR_NULL (use dash_summarize).
+ */
+dash_status dash_summarize_varlen(const void* K, int k_dtype, const float* qbar, float* kbar,
+                                  const int32_t* seq_len, int b, int h_kv, int n_kv, int kbar_cap, int d, int B,
+                                  int chunk_begin, int chunk_end, void* stream);
+
+/*
  * Stage 1 for a prefill (Eq. 6, the GQA paragraph, Prop. 4.1's μ and d): every
  * query row i (position i) of Q [b, h_q, n, d] (q_dtype) is routed against
  * k̄ [b, h_kv, kbar_cap, d] (chunks 0..floor(n/B)-1 must be summarised).
@@ -119,6 +135,20 @@ dash_status dash_route_topk(const void* Q, int q_dtype, const float* kbar,
                             float alpha, float gamma, float sigma, int causal,
                             int32_t* idx, float* bias, int32_t* cnt, int list_cap,
                             float* w_out, int top_k, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * dash_route_topk over a ragged batch (seq_len as for dash_summarize_varlen): row i
+ * < seq_len[b] of sequence b is routed against that sequence's chunks c < T_b only
+ * (causal: c < min(floor(i/B), T_b)); k̄ rows of later chunks are not read. Padding
+ * rows i >= seq_len[b] get cnt = 0, and their idx, bias and w_out rows are not
+ * written. w_out of a routed row is 0 for chunks >= T_b. Everything else,
+ * including the workspace (sized by n), as dash_route_topk.
+ */
+dash_status dash_route_varlen(const void* Q, int q_dtype, const float* kbar, const int32_t* seq_len,
+                              int b, int h_q, int h_kv, int n, int kbar_cap, int d, int B,
+                              float alpha, float gamma, float sigma, int causal,
+                              int32_t* idx, float* bias, int32_t* cnt, int list_cap,
+                              float* w_out, int top_k, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * dash_route with the forward statistics the routing backward needs: stats
@@ -207,6 +237,21 @@ dash_status dash_attend_prefill_lse(const void* Q, const void* K, const void* V,
                                     int list_cap, void* O, int out_dtype, float* lse,
                                     int b, int h_q, int h_kv, int n, int d, int B, int causal,
                                     void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * dash_attend_prefill_lse over a ragged batch (seq_len as for dash_summarize_varlen;
+ * idx/bias/cnt as dash_route_varlen writes them): row i < seq_len[b] attends to its
+ * routed chunks and to its diagonal branch inside the sequence (causal: its own
+ * chunk up to i; non-causal: the sequence's tokens from T_b*B on), never to a
+ * token >= seq_len[b]. Rows i >= seq_len[b] of O and lse (nullable) are not
+ * written. The Stage-2 backward has no ragged form. Workspace as
+ * dash_attend_prefill (sized by n).
+ */
+dash_status dash_attend_prefill_varlen(const void* Q, const void* K, const void* V, int in_dtype,
+                                       const int32_t* seq_len, const int32_t* idx, const float* bias,
+                                       const int32_t* cnt, int list_cap, void* O, int out_dtype, float* lse,
+                                       int b, int h_q, int h_kv, int n, int d, int B, int causal,
+                                       void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Stage-2 backward (the support and the per-chunk bias of Prop. 4.1 held fixed: the

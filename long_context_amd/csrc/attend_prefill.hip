@@ -38,13 +38,17 @@ __global__ __launch_bounds__(64 * kWaves) void sparse_prior_attn_kernel(PrefillP
     const int g = p.g, lg = p.log2g, R_t = p.R_t;
     // causal tiles near the end of the sequence carry the most work: launch them first
     const int row0 = (gridDim.x - 1 - blockIdx.x) * R_t;
+    // ragged batch: the sequence's own tokens and complete chunks; a tile past them
+    // has nothing to do (workgroup-uniform, before any barrier)
+    const int nb = seq_tokens(p, bi), Tb = nb / p.B;
+    if (row0 >= nb) return;
     const int cq = row0 / p.B;
-    const int nvis = p.causal ? min(cq, p.T_c) : p.T_c;
-    const int last_row = min(row0 + R_t, p.n) - 1;
+    const int nvis = p.causal ? min(cq, Tb) : Tb;
+    const int last_row = min(row0 + R_t, nb) - 1;
     const size_t bhkv = (size_t)bi * p.h_kv + r;
     const T* Kg = static_cast<const T*>(p.K) + bhkv * (size_t)p.n * D;
     const T* Vg = static_cast<const T*>(p.V) + bhkv * (size_t)p.n * D;
-    const int U = tabs.build(p, bhkv, row0, nvis, tid, nthr);
+    const int U = tabs.build(p, bhkv, row0, nvis, tid, nthr, nb);
     const int* ulist = tabs.ulist;
 
     // ---- this lane's (row, head) pair ----
@@ -53,7 +57,7 @@ __global__ __launch_bounds__(64 * kWaves) void sparse_prior_attn_kernel(PrefillP
     const int j = pair >> lg;
     const int hh = r * g + (pair & (g - 1));
     const int my_row = row0 + j;
-    const bool pair_ok = wave_active && j < R_t && my_row < p.n;
+    const bool pair_ok = wave_active && j < R_t && my_row < nb;
     ListCursor lc;
     lc.init(p, bhkv * p.n + (pair_ok ? my_row : 0), pair_ok);
     Op qf[D / 16];
@@ -74,9 +78,9 @@ __global__ __launch_bounds__(64 * kWaves) void sparse_prior_attn_kernel(PrefillP
         for (int i = 0; i < 16; ++i) o_acc[db][i] = 0.f;
 
     TileSteps st;
-    st.init(p, U, cq, last_row, TT);
+    st.init(p, U, cq, last_row, TT, nb, Tb);
     const int nrouted = st.nrouted, nsteps = st.nsteps, SPC = st.SPC;
-    const int nmax = p.n - 1;
+    const int nmax = nb - 1;
     TileCopier<T, D, TT, kWaves> copier;
     copier.init(wid, lane);
     // the tile base and chunk of each step are read from LDS two steps ahead, so
@@ -128,7 +132,7 @@ __global__ __launch_bounds__(64 * kWaves) void sparse_prior_attn_kernel(PrefillP
             }
             // mask the diagonal tile on the raw scores (selects, no branches)
             if (!routed) {
-                const int lim = p.causal ? my_row : p.n - 1;
+                const int lim = p.causal ? my_row : nb - 1;
                 const int tk0 = tb + 4 * hl;
 #pragma unroll
                 for (int blk = 0; blk < TT / 32; ++blk)
@@ -275,6 +279,7 @@ hipError_t launch_attend_prefill(const PrefillArgs& a, hipStream_t s) {
     p.log2g = 0;
     while ((1 << p.log2g) < p.g) ++p.log2g;
     p.scale_log2 = (float)(1.4426950408889634 / sqrt((double)a.d));
+    p.seq_len = a.seq_len;
     size_t lds = 0;
     prefill_tiling(p.g, a.B, p.T_c, a.d, a.in_bf16, &p.R_t, &lds);
     if (p.R_t == 0) return hipErrorInvalidValue;

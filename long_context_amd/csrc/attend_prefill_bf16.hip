@@ -69,19 +69,22 @@ struct BfCopier {
     }
 };
 
-// V [b, h_kv, n, D] -> Vt [b, h_kv, D, n_pad], tokens n .. n_pad-1 zero.
+// V [b, h_kv, n, D] -> Vt [b, h_kv, D, n_pad], tokens n .. n_pad-1 zero (in a ragged
+// batch, tokens from seq_len[b] on: padding rows may hold anything).
 template <int D>
-__global__ __launch_bounds__(256) void transpose_v_kernel(const uint16_t* V, uint16_t* Vt, int n, int n_pad) {
+__global__ __launch_bounds__(256) void transpose_v_kernel(const uint16_t* V, uint16_t* Vt, int n, int n_pad,
+                                                          const int32_t* seq_len = nullptr, int h_kv = 1) {
     __shared__ __attribute__((aligned(16))) uint16_t tile[64][D + 8];
     const int t0 = blockIdx.x * 64;
     const size_t bh = blockIdx.y;
+    const int nv = seq_len ? min(max(seq_len[bh / h_kv], 0), n) : n;   // tokens copied
     const uint16_t* src = V + bh * (size_t)n * D;
     uint16_t* dst = Vt + bh * (size_t)D * n_pad;
     constexpr int PR = D / 8;                          // 16-byte pieces per V row
     for (int q = threadIdx.x; q < 64 * PR; q += 256) {
         const int t = q / PR, c = q % PR;
         u32x4 v = {0u, 0u, 0u, 0u};
-        if (t0 + t < n) v = *reinterpret_cast<const u32x4*>(src + (size_t)(t0 + t) * D + 8 * c);
+        if (t0 + t < nv) v = *reinterpret_cast<const u32x4*>(src + (size_t)(t0 + t) * D + 8 * c);
         *reinterpret_cast<u32x4*>(&tile[t][8 * c]) = v;
     }
     __syncthreads();
@@ -116,13 +119,17 @@ __global__ __launch_bounds__(64 * NW) void sparse_prior_attn_bf16_kernel(Prefill
     const int g = p.g, lg = p.log2g, R_t = p.R_t;
     // causal tiles near the end of the sequence carry the most work: launch them first
     const int row0 = (gridDim.x - 1 - blockIdx.x) * R_t;
+    // ragged batch: the sequence's own tokens and complete chunks; a tile past them
+    // has nothing to do (workgroup-uniform, before any barrier)
+    const int nb = seq_tokens(p, bi), Tb = nb / p.B;
+    if (row0 >= nb) return;
     const int cq = row0 / p.B;
-    const int nvis = p.causal ? min(cq, p.T_c) : p.T_c;
-    const int last_row = min(row0 + R_t, p.n) - 1;
+    const int nvis = p.causal ? min(cq, Tb) : Tb;
+    const int last_row = min(row0 + R_t, nb) - 1;
     const size_t bhkv = (size_t)bi * p.h_kv + r;
     const uint16_t* Kg = static_cast<const uint16_t*>(p.K) + bhkv * (size_t)p.n * D;
     const uint16_t* Vtg = p.Vt + bhkv * (size_t)D * p.n_pad;
-    const int U = tabs.build(p, bhkv, row0, nvis, tid, nthr);
+    const int U = tabs.build(p, bhkv, row0, nvis, tid, nthr, nb);
 
     // ---- the lane's (row, head) pair in each of its pair blocks ----
     int jrow[PBW], my_row[PBW];
@@ -136,7 +143,7 @@ __global__ __launch_bounds__(64 * NW) void sparse_prior_attn_bf16_kernel(Prefill
         my_row[pb] = row0 + jrow[pb];
         const int hh = r * g + (P & (g - 1));
         live[pb] = (wid * PBW + pb) * 32 < g * R_t;              // wavefront-uniform
-        pok[pb] = live[pb] && jrow[pb] < R_t && my_row[pb] < p.n;
+        pok[pb] = live[pb] && jrow[pb] < R_t && my_row[pb] < nb;
         lc[pb].init(p, bhkv * p.n + (pok[pb] ? my_row[pb] : 0), pok[pb]);
         const uint16_t* qrow = static_cast<const uint16_t*>(p.Q) +
             (((size_t)bi * p.h_q + hh) * p.n + (pok[pb] ? my_row[pb] : 0)) * D + 8 * hl;
@@ -160,8 +167,8 @@ __global__ __launch_bounds__(64 * NW) void sparse_prior_attn_bf16_kernel(Prefill
     }
 
     TileSteps st;
-    st.init(p, U, cq, last_row, TT);
-    const int nmax = p.n - 1;
+    st.init(p, U, cq, last_row, TT, nb, Tb);
+    const int nmax = nb - 1;
     BfCopier<D, TT, NW> cp;
     cp.init(wid, lane);
     // tile row presented by A row l32 of a 32-token block: bits 2 and 3 swapped
@@ -204,7 +211,7 @@ __global__ __launch_bounds__(64 * NW) void sparse_prior_attn_bf16_kernel(Prefill
     auto softmax = [&](int pb, bool diag, int tb, float bias2, f32x16 (&sacc)[NB], bf16x8 (&pp)[NP],
                        bool& grow) -> float {
         if (diag) {
-            const int lim = p.causal ? my_row[pb] : p.n - 1;
+            const int lim = p.causal ? my_row[pb] : nb - 1;
 #pragma unroll
             for (int blk = 0; blk < NB; ++blk)
 #pragma unroll
@@ -373,7 +380,8 @@ static hipError_t launch_bf16_t(const PrefillParams& p, int b, size_t lds, hipSt
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (configured != hipSuccess) return configured;
     hipLaunchKernelGGL((transpose_v_kernel<D>), dim3(p.n_pad / 64, b * p.h_kv), dim3(256), 0, s,
-                       static_cast<const uint16_t*>(p.V), const_cast<uint16_t*>(p.Vt), p.n, p.n_pad);
+                       static_cast<const uint16_t*>(p.V), const_cast<uint16_t*>(p.Vt), p.n, p.n_pad, p.seq_len,
+                       p.h_kv);
     dim3 grid((p.n + p.R_t - 1) / p.R_t, p.h_kv, b), block(64 * kWavesB);
     hipLaunchKernelGGL(kern, grid, block, lds, s, p);
     return hipGetLastError();

@@ -141,6 +141,25 @@ dash_status dash_summarize(const void* K, int k_dtype, const float* qbar, float*
     return from_hip(dash::launch_summary(a, (hipStream_t)stream), "chunk_summary_kernel");
 }
 
+dash_status dash_summarize_varlen(const void* K, int k_dtype, const float* qbar, float* kbar,
+                                  const int32_t* seq_len, int b, int h_kv, int n_kv, int kbar_cap, int d, int B,
+                                  int chunk_begin, int chunk_end, void* stream) {
+    if (!seq_len) return fail(DASH_ERR_NULL, "seq_len must be non-null");
+    if (!K || !qbar || !kbar) return fail(DASH_ERR_NULL, "K, qbar and kbar must be non-null");
+    if (!valid_dtype(k_dtype)) return fail(DASH_ERR_PARAM, "bad K dtype %d", k_dtype);
+    dash_status st = check_common(b, h_kv, h_kv, d, B);
+    if (st != DASH_OK) return st;
+    if (n_kv < 0 || kbar_cap < 0) return fail(DASH_ERR_SHAPE, "n_kv and kbar_cap must be >= 0");
+    const int T = n_kv / B;
+    const int lim = T < kbar_cap ? T : kbar_cap;
+    if (chunk_begin < 0 || chunk_begin > chunk_end || chunk_end > lim)
+        return fail(DASH_ERR_SHAPE, "chunk range [%d, %d) outside [0, %d]", chunk_begin, chunk_end, lim);
+    dash::SummaryArgs a{K, k_dtype == DASH_BF16, qbar, kbar, b, h_kv, n_kv, kbar_cap, d, B,
+                        chunk_begin, chunk_end};
+    a.seq_len = seq_len;
+    return from_hip(dash::launch_summary(a, (hipStream_t)stream), "chunk_summary_kernel");
+}
+
 dash_status dash_summarize_paged(const void* Kp, int k_dtype, const float* qbar, float* kbar,
                                  const int32_t* pages, int pages_per_seq, int num_pages,
                                  int b, int h_kv, int kbar_cap, int d, int B,
@@ -163,7 +182,8 @@ static dash_status route_impl(const void* Q, int q_dtype, const float* kbar,
                               int b, int h_q, int h_kv, int n, int kbar_cap, int d, int B,
                               float alpha, float gamma, float sigma, int causal,
                               int32_t* idx, float* bias, int32_t* cnt, int list_cap,
-                              float* w_out, int top_k, float* stats, void* ws, size_t ws_bytes, void* stream) {
+                              float* w_out, int top_k, float* stats, void* ws, size_t ws_bytes, void* stream,
+                              const int32_t* seq_len = nullptr) {
     if (!Q || !kbar || !idx || !bias || !cnt) return fail(DASH_ERR_NULL, "Q, kbar, idx, bias and cnt must be non-null");
     if (!valid_dtype(q_dtype)) return fail(DASH_ERR_PARAM, "bad Q dtype %d", q_dtype);
     if (causal != 0 && causal != 1) return fail(DASH_ERR_PARAM, "causal must be 0 or 1");
@@ -186,7 +206,7 @@ static dash_status route_impl(const void* Q, int q_dtype, const float* kbar,
             return fail(DASH_ERR_WORKSPACE, "bf16 routing needs %zu workspace bytes, got %zu", need, ws ? ws_bytes : (size_t)0);
     }
     dash::RouteArgs a{Q, q_dtype == DASH_BF16, kbar, b, h_q, h_kv, n, kbar_cap, d, B, causal, list_cap,
-                      alpha, gamma, sigma, idx, bias, cnt, w_out, ws, top_k, stats};
+                      alpha, gamma, sigma, idx, bias, cnt, w_out, ws, top_k, stats, seq_len};
     return from_hip(dash::launch_route(a, (hipStream_t)stream), "entmax_route_kernel");
 }
 
@@ -197,6 +217,16 @@ dash_status dash_route_topk(const void* Q, int q_dtype, const float* kbar,
                             float* w_out, int top_k, void* ws, size_t ws_bytes, void* stream) {
     return route_impl(Q, q_dtype, kbar, b, h_q, h_kv, n, kbar_cap, d, B, alpha, gamma, sigma, causal, idx, bias, cnt,
                       list_cap, w_out, top_k, nullptr, ws, ws_bytes, stream);
+}
+
+dash_status dash_route_varlen(const void* Q, int q_dtype, const float* kbar, const int32_t* seq_len,
+                              int b, int h_q, int h_kv, int n, int kbar_cap, int d, int B,
+                              float alpha, float gamma, float sigma, int causal,
+                              int32_t* idx, float* bias, int32_t* cnt, int list_cap,
+                              float* w_out, int top_k, void* ws, size_t ws_bytes, void* stream) {
+    if (!seq_len) return fail(DASH_ERR_NULL, "seq_len must be non-null");
+    return route_impl(Q, q_dtype, kbar, b, h_q, h_kv, n, kbar_cap, d, B, alpha, gamma, sigma, causal, idx, bias, cnt,
+                      list_cap, w_out, top_k, nullptr, ws, ws_bytes, stream, seq_len);
 }
 
 dash_status dash_route_stats(const void* Q, int q_dtype, const float* kbar,
@@ -273,11 +303,11 @@ dash_status dash_route_mask(const int32_t* idx, const int32_t* cnt, int b, int h
                     "lists_to_mask_kernel");
 }
 
-dash_status dash_attend_prefill_lse(const void* Q, const void* K, const void* V, int in_dtype,
-                                    const int32_t* idx, const float* bias, const int32_t* cnt,
-                                    int list_cap, void* O, int out_dtype, float* lse,
-                                    int b, int h_q, int h_kv, int n, int d, int B, int causal,
-                                    void* ws, size_t ws_bytes, void* stream) {
+static dash_status attend_prefill(const void* Q, const void* K, const void* V, int in_dtype,
+                                  const int32_t* idx, const float* bias, const int32_t* cnt,
+                                  int list_cap, void* O, int out_dtype, float* lse,
+                                  int b, int h_q, int h_kv, int n, int d, int B, int causal,
+                                  void* ws, size_t ws_bytes, void* stream, const int32_t* seq_len) {
     if (!Q || !K || !V || !idx || !bias || !cnt || !O) return fail(DASH_ERR_NULL, "Q, K, V, idx, bias, cnt and O must be non-null");
     if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return fail(DASH_ERR_PARAM, "bad dtype");
     if (causal != 0 && causal != 1) return fail(DASH_ERR_PARAM, "causal must be 0 or 1");
@@ -297,8 +327,27 @@ dash_status dash_attend_prefill_lse(const void* Q, const void* K, const void* V,
             return fail(DASH_ERR_WORKSPACE, "bf16 prefill needs %zu workspace bytes, got %zu", need, ws ? ws_bytes : (size_t)0);
     }
     dash::PrefillArgs a{Q, K, V, in_dtype == DASH_BF16, idx, bias, cnt, list_cap, O, out_dtype == DASH_BF16,
-                        b, h_q, h_kv, n, d, B, causal, ws, lse};
+                        b, h_q, h_kv, n, d, B, causal, ws, lse, seq_len};
     return from_hip(dash::launch_attend_prefill(a, (hipStream_t)stream), "sparse_prior_attn_kernel");
+}
+
+dash_status dash_attend_prefill_lse(const void* Q, const void* K, const void* V, int in_dtype,
+                                    const int32_t* idx, const float* bias, const int32_t* cnt,
+                                    int list_cap, void* O, int out_dtype, float* lse,
+                                    int b, int h_q, int h_kv, int n, int d, int B, int causal,
+                                    void* ws, size_t ws_bytes, void* stream) {
+    return attend_prefill(Q, K, V, in_dtype, idx, bias, cnt, list_cap, O, out_dtype, lse, b, h_q, h_kv, n, d, B,
+                          causal, ws, ws_bytes, stream, nullptr);
+}
+
+dash_status dash_attend_prefill_varlen(const void* Q, const void* K, const void* V, int in_dtype,
+                                       const int32_t* seq_len, const int32_t* idx, const float* bias,
+                                       const int32_t* cnt, int list_cap, void* O, int out_dtype, float* lse,
+                                       int b, int h_q, int h_kv, int n, int d, int B, int causal,
+                                       void* ws, size_t ws_bytes, void* stream) {
+    if (!seq_len) return fail(DASH_ERR_NULL, "seq_len must be non-null");
+    return attend_prefill(Q, K, V, in_dtype, idx, bias, cnt, list_cap, O, out_dtype, lse, b, h_q, h_kv, n, d, B,
+                          causal, ws, ws_bytes, stream, seq_len);
 }
 
 dash_status dash_attend_prefill(const void* Q, const void* K, const void* V, int in_dtype,

@@ -15,6 +15,9 @@ struct SummaryArgs {
     // sequence b lives in page pages[b * pages_per_seq + c]
     const int32_t* pages = nullptr;
     int pages_per_seq = 0, num_pages = 0;
+    // ragged batch (nullable): sequence b holds seq_len[b] tokens; chunks past its
+    // last complete one are skipped
+    const int32_t* seq_len = nullptr;
 };
 hipError_t launch_summary(const SummaryArgs& a, hipStream_t s);
 
@@ -26,6 +29,8 @@ struct RouteArgs {
     void* ws;            // bf16 queries: split summaries, route_workspace_bytes
     int top_k;           // > 0: fixed budget of routed chunks per row
     float* stats = nullptr;  // optional [b, h_q, n, 2]: max raw logit, threshold
+    const int32_t* seq_len = nullptr;  // ragged batch (nullable): rows of sequence b past
+                                       // seq_len[b] get an empty list
 };
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
 // Routed lists -> bitpacked mask [rows][words] (bit c%32 of word c/32 = chunk c routed).
@@ -56,6 +61,8 @@ struct PrefillArgs {
     int b, h_q, h_kv, n, d, B, causal;
     void* ws;            // bf16 inputs: V transposed, prefill_workspace_bytes
     float* lse = nullptr;  // optional [b, h_q, n] log-sum-exp of each row's logits
+    const int32_t* seq_len = nullptr;  // ragged batch (nullable): sequence b holds
+                                       // seq_len[b] tokens; later rows are not written
 };
 hipError_t launch_attend_prefill(const PrefillArgs& a, hipStream_t s);
 

@@ -26,7 +26,13 @@ struct PrefillParams {
     float* lse;          // nullable: per (b, query head, row) log-sum-exp of the logits
     int out_bf16, h_q, h_kv, n, n_pad, B, T_c, list_cap, causal, g, log2g, R_t, nw;
     float scale_log2;    // log2(e)/sqrt(d)
+    const int32_t* seq_len = nullptr;  // ragged batch (nullable): tokens of each sequence
 };
+
+// Tokens of sequence bi: seq_len[bi] clamped to [0, n] in a ragged batch, else n.
+__device__ __forceinline__ int seq_tokens(const PrefillParams& p, int bi) {
+    return p.seq_len ? min(max(p.seq_len[bi], 0), p.n) : p.n;
+}
 
 // LDS tables of one query tile: the ascending union of the chunks its rows route.
 struct TileTables {
@@ -43,12 +49,13 @@ struct TileTables {
     // 0..nvis-1) and return its size. Every row has nthr/R_t threads, which read its
     // list four entries apart at a time, so all rows' loads are in flight together.
     // Ends with a workgroup barrier.
-    __device__ int build(const PrefillParams& p, size_t bhkv, int row0, int nvis, int tid, int nthr) {
+    __device__ int build(const PrefillParams& p, size_t bhkv, int row0, int nvis, int tid, int nthr, int nb = -1) {
+        if (nb < 0) nb = p.n;
         for (int c = tid; c < nvis; c += nthr) uflag[c] = 0;
         __syncthreads();
         const int tpr = max(nthr / p.R_t, 1);
         const int j = tid / tpr, sub = tid % tpr, row = row0 + j;
-        if (j < p.R_t && row < p.n) {
+        if (j < p.R_t && row < nb) {
             const size_t rb = bhkv * p.n + row;
             const int cn = min(p.cnt[rb], p.list_cap);
             const int32_t* li = p.idx + rb * p.list_cap;
@@ -116,15 +123,18 @@ struct ListCursor {
 // diagonal branch.
 struct TileSteps {
     int SPC, nrouted, ndiag, nsteps, diag_base, TT;
-    __device__ __forceinline__ void init(const PrefillParams& p, int U, int cq, int last_row, int tt) {
+    // nb, Tb: the sequence's tokens and complete chunks (a ragged batch), else n and T_c
+    __device__ __forceinline__ void init(const PrefillParams& p, int U, int cq, int last_row, int tt,
+                                         int nb = -1, int Tb = -1) {
+        if (nb < 0) { nb = p.n; Tb = p.T_c; }
         TT = tt;
         SPC = p.B / TT;
         if (p.causal) {
             diag_base = cq * p.B;
             ndiag = (last_row - diag_base) / TT + 1;
         } else {
-            diag_base = p.T_c * p.B;
-            ndiag = (p.n - diag_base + TT - 1) / TT;
+            diag_base = Tb * p.B;
+            ndiag = (nb - diag_base + TT - 1) / TT;
         }
         nrouted = U * SPC;
         nsteps = nrouted + ndiag;

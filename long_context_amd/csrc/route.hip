@@ -75,6 +75,7 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
     p.Q = a.Q; p.kbar = a.kbar; p.idx = a.idx; p.bias = a.bias; p.cnt = a.cnt; p.w_out = a.w_out;
     p.h_q = a.h_q; p.h_kv = a.h_kv; p.n = a.n; p.kbar_cap = a.kbar_cap; p.list_cap = a.list_cap;
     p.B = a.B; p.T_c = a.n / a.B; p.g = a.h_q / a.h_kv;
+    p.seq_len = a.seq_len;
     p.log2g = 0;
     while ((1 << p.log2g) < p.g) ++p.log2g;
     p.causal = a.causal;

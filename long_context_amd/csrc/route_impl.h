@@ -46,6 +46,7 @@ struct RouteParams {
     int top_k;          // > 0: keep only the top_k largest group weights of each row
     float* stats;       // nullable [b, h_q, n, 2]: max raw logit and the threshold
                         // (τ; α = 1: log2 Σ 2^y) of each (head, row)
+    const int32_t* seq_len = nullptr;  // nullable: ragged batch, sequence b holds seq_len[b] rows
 };
 
 // Order-preserving map of a float to an unsigned key (larger float, larger key).
@@ -291,6 +292,9 @@ __global__ __launch_bounds__(512) void entmax_route_kernel(RouteParams p) {
     const int wg_row0 = blockIdx.x * G * R;
     const int row0 = wg_row0 + gid * R;
     const bool wave_live = row0 < p.n;
+    // ragged batch: the sequence's own tokens and complete chunks
+    const int nb = p.seq_len ? min(max(p.seq_len[bi], 0), p.n) : p.n;
+    const int Tb = nb / p.B;
     constexpr int RSTG = route_ring_stages<NT, CW>();
     constexpr bool RING = route_uses_ring<T, CW>();
     char* kstage = rsm;                                              // RSTG stages (ring only)
@@ -298,10 +302,10 @@ __global__ __launch_bounds__(512) void entmax_route_kernel(RouteParams p) {
     float* wl = wl_all + gid * R * WS;
     float* xred = wl_all + G * R * WS;                // [G][CW][16] row maxima of each wavefront
     float* xsum = xred + G * CW * 16;                 // [2][G][CW][16][2] Newton partial sums
-    const int nvis = p.causal ? min(wg_row0 / p.B, p.T_c) : p.T_c;
+    const int nvis = p.causal ? min(wg_row0 / p.B, Tb) : Tb;
     const int my_row = row0 + (n16 >> lg);
     const int my_head = r * g + (n16 & (g - 1));
-    const bool row_ok = my_row < p.n;
+    const bool row_ok = my_row < nb;
     const int nt = min(RS::tiles_below(nvis, cw), NT);   // tiles holding visible chunks
 
     float sv[NT][4];
@@ -559,6 +563,10 @@ __global__ __launch_bounds__(512) void entmax_route_kernel(RouteParams p) {
     for (int j = 0; j < R; ++j) {
         const int row = row0 + j;
         if (row >= p.n) break;
+        if (row >= nb) {                              // a padding row of a ragged batch
+            if (lane == 0) p.cnt[rowbase + row] = 0;
+            continue;
+        }
         const float* wr = wl + j * WS;
         auto cand = [&](int c, float v) { return c < nvis && (SOFT || v > 0.f); };
         bool limit = false;

@@ -39,7 +39,8 @@ template <typename T, int D>
 __global__ __launch_bounds__(256) void chunk_summary_kernel(
     const T* __restrict__ K, const float* __restrict__ qbar, float* __restrict__ kbar,
     int h_kv, int n_kv, int kbar_cap, int B, int chunk_begin, int nsel, int total,
-    float scale, const int32_t* __restrict__ pages, int pages_per_seq, int num_pages) {
+    float scale, const int32_t* __restrict__ pages, int pages_per_seq, int num_pages,
+    const int32_t* __restrict__ seq_len) {
     constexpr int VEC = Vec16<T>::N;
     constexpr int LPR = D / VEC;        // lanes sharing one key row
     constexpr int RPI = 64 / LPR;       // key rows per wave iteration
@@ -49,6 +50,8 @@ __global__ __launch_bounds__(256) void chunk_summary_kernel(
     const int c = chunk_begin + wave % nsel;
     const int br = wave / nsel;         // b * h_kv + r
     const int r = br % h_kv;
+    // ragged batch: only the complete chunks of the sequence's own tokens
+    if (seq_len && c >= min(max(seq_len[br / h_kv], 0), n_kv) / B) return;
     const int rr = lane / LPR;
     const int col = (lane % LPR) * VEC;
 
@@ -127,7 +130,8 @@ static hipError_t launch_summary_t(const SummaryArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((chunk_summary_kernel<T, D>), grid, block, 0, s,
                        static_cast<const T*>(a.K), a.qbar, a.kbar, a.h_kv, a.n_kv, a.kbar_cap,
                        a.B, a.chunk_begin, nsel, total,
-                       (float)(1.4426950408889634 / sqrt((double)D)), a.pages, a.pages_per_seq, a.num_pages);
+                       (float)(1.4426950408889634 / sqrt((double)D)), a.pages, a.pages_per_seq, a.num_pages,
+                       a.seq_len);
     return hipGetLastError();
 }
 

@@ -31,12 +31,17 @@ def _load():
     vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.dash_summarize.argtypes = [vp, i32, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, vp]
     lib.dash_summarize.restype = i32
+    lib.dash_summarize_varlen.argtypes = [vp, i32, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, vp]
+    lib.dash_summarize_varlen.restype = i32
     lib.dash_route.argtypes = [vp, i32, vp, i32, i32, i32, i32, i32, i32, i32, f32, f32, f32, i32,
                                vp, vp, vp, i32, vp, vp, sz, vp]
     lib.dash_route.restype = i32
     lib.dash_route_topk.argtypes = [vp, i32, vp, i32, i32, i32, i32, i32, i32, i32, f32, f32, f32, i32,
                                     vp, vp, vp, i32, vp, i32, vp, sz, vp]
     lib.dash_route_topk.restype = i32
+    lib.dash_route_varlen.argtypes = [vp, i32, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, f32, f32, i32,
+                                      vp, vp, vp, i32, vp, i32, vp, sz, vp]
+    lib.dash_route_varlen.restype = i32
     lib.dash_route_stats.argtypes = [vp, i32, vp, i32, i32, i32, i32, i32, i32, i32, f32, f32, f32, i32,
                                      vp, vp, vp, i32, vp, vp, vp, sz, vp]
     lib.dash_route_stats.restype = i32
@@ -53,6 +58,9 @@ def _load():
     lib.dash_attend_prefill_lse.argtypes = [vp, vp, vp, i32, vp, vp, vp, i32, vp, i32, vp,
                                             i32, i32, i32, i32, i32, i32, i32, vp, sz, vp]
     lib.dash_attend_prefill_lse.restype = i32
+    lib.dash_attend_prefill_varlen.argtypes = [vp, vp, vp, i32, vp, vp, vp, vp, i32, vp, i32, vp,
+                                               i32, i32, i32, i32, i32, i32, i32, vp, sz, vp]
+    lib.dash_attend_prefill_varlen.restype = i32
     lib.dash_attend_prefill_backward.argtypes = [vp, vp, vp, i32, vp, vp, vp, i32, vp, vp, i32, vp,
                                                  vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                                  vp, sz, vp]
@@ -82,9 +90,10 @@ def _load():
 
 lib = _load()
 
-SYMBOLS = ("dash_summarize", "dash_summarize_paged", "dash_summarize_backward", "dash_route", "dash_route_topk",
-           "dash_route_stats", "dash_route_backward", "dash_route_mask",
-           "dash_attend_prefill", "dash_attend_prefill_lse", "dash_attend_prefill_backward",
+SYMBOLS = ("dash_summarize", "dash_summarize_varlen", "dash_summarize_paged", "dash_summarize_backward",
+           "dash_route", "dash_route_topk", "dash_route_varlen", "dash_route_stats", "dash_route_backward",
+           "dash_route_mask", "dash_attend_prefill", "dash_attend_prefill_lse", "dash_attend_prefill_varlen",
+           "dash_attend_prefill_backward",
            "dash_attend_decode", "dash_attend_decode_topk", "dash_attend_decode_noalloc", "dash_attend_decode_paged",
            "dash_workspace_bytes", "dash_status_string", "dash_last_error")
 
@@ -137,6 +146,28 @@ def dash_summarize(K, qbar, kbar, B, chunk_begin=0, chunk_end=None, stream=None)
         chunk_end = n // B
     _check(lib.dash_summarize(_ptr(K), _dtype(K), _ptr(qbar), _ptr(kbar), b, h_kv, n,
                               kbar.shape[2], d, B, chunk_begin, chunk_end, _stream(stream)))
+
+
+def dash_summarize_varlen(K, qbar, kbar, seq_len, B, chunk_begin=0, chunk_end=None, stream=None):
+    """dash_summarize over a ragged batch: only chunks below seq_len[b] // B of each sequence."""
+    b, h_kv, n, d = K.shape
+    if chunk_end is None:
+        chunk_end = min(n // B, kbar.shape[2])
+    _check(lib.dash_summarize_varlen(_ptr(K), _dtype(K), _ptr(qbar), _ptr(kbar), _ptr(seq_len), b, h_kv, n,
+                                     kbar.shape[2], d, B, chunk_begin, chunk_end, _stream(stream)))
+
+
+def dash_route_varlen(Q, kbar, seq_len, B, alpha, gamma, sigma, causal, idx, bias, cnt, w_out=None,
+                      ws=None, stream=None, top_k=0):
+    """dash_route over a ragged batch (seq_len [b] int32): padding rows get cnt 0."""
+    b, h_q, n, d = Q.shape
+    h_kv = kbar.shape[1]
+    if ws is None and Q.dtype == torch.bfloat16:
+        ws = alloc_route_ws(b, h_q, h_kv, n, d, B, device=Q.device)
+    _check(lib.dash_route_varlen(_ptr(Q), _dtype(Q), _ptr(kbar), _ptr(seq_len), b, h_q, h_kv, n, kbar.shape[2], d,
+                                 B, float(alpha), float(gamma), float(sigma), int(causal),
+                                 _ptr(idx), _ptr(bias), _ptr(cnt), idx.shape[-1], _ptr(w_out), int(top_k),
+                                 _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def dash_route(Q, kbar, B, alpha, gamma, sigma, causal, idx, bias, cnt, w_out=None,
@@ -225,6 +256,19 @@ def dash_attend_prefill_lse(Q, K, V, idx, bias, cnt, O, lse, B, causal, ws=None,
                                        h_kv, n, d, B, int(causal), _ptr(ws),
                                        0 if ws is None else ws.numel() * ws.element_size(),
                                        _stream(stream)))
+
+
+def dash_attend_prefill_varlen(Q, K, V, seq_len, idx, bias, cnt, O, B, causal, lse=None, ws=None, stream=None):
+    """dash_attend_prefill over a ragged batch: rows at or past seq_len[b] are not written."""
+    b, h_q, n, d = Q.shape
+    h_kv = K.shape[1]
+    if ws is None and Q.dtype == torch.bfloat16:
+        ws = alloc_prefill_ws(b, h_q, h_kv, n, d, B, device=Q.device)
+    _check(lib.dash_attend_prefill_varlen(_ptr(Q), _ptr(K), _ptr(V), _dtype(Q), _ptr(seq_len), _ptr(idx),
+                                          _ptr(bias), _ptr(cnt), idx.shape[-1], _ptr(O), _dtype(O), _ptr(lse),
+                                          b, h_q, h_kv, n, d, B, int(causal), _ptr(ws),
+                                          0 if ws is None else ws.numel() * ws.element_size(),
+                                          _stream(stream)))
 
 
 def dash_attend_prefill_backward(Q, K, V, idx, bias, cnt, O, dO, lse, dQ, dK, dV, dbias, B, causal,

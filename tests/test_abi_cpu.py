@@ -324,3 +324,32 @@ def test_route_backward_workspace(dash):
 def test_route_stats_needs_stats(dash):
     args = (P, 0, P, 1, 8, 2, 256, 4, 64, 64, 1.5, 1.0, 1.0, 1, P, P, P, 4, NUL)
     assert dash.lib.dash_route_stats(*args, NUL, NUL, 0, NUL) == dash.DASH_ERR_NULL
+
+
+def test_varlen_entry_points_validation(dash):
+    """The ragged-batch entry points need seq_len and otherwise validate as their
+    dense counterparts (the checks come before any launch)."""
+    L = dash.lib
+    s = L.dash_summarize_varlen
+    assert s(P, 1, P, P, NUL, 1, 2, 256, 4, 128, 64, 0, 4, NUL) == dash.DASH_ERR_NULL
+    assert "seq_len" in L.dash_last_error().decode()
+    assert s(P, 1, P, P, P, 1, 2, 256, 4, 128, 64, 0, 5, NUL) == dash.DASH_ERR_SHAPE
+    assert s(P, 1, P, P, P, 1, 2, 256, 4, 128, 8, 0, 4, NUL) == dash.DASH_ERR_UNSUPPORTED
+    r = L.dash_route_varlen
+    args = [P, 1, P, P, 1, 4, 2, 256, 4, 128, 64, 1.5, 1.0, 1.0, 1, P, P, P, 4, NUL, 0]
+    assert r(*args, NUL, 0, NUL) == dash.DASH_ERR_WORKSPACE          # valid up to the workspace
+    bad = list(args)
+    bad[3] = NUL
+    assert r(*bad, NUL, 0, NUL) == dash.DASH_ERR_NULL
+    bad = list(args)
+    bad[20] = -1
+    assert r(*bad, NUL, 0, NUL) == dash.DASH_ERR_PARAM              # negative budget
+    p = L.dash_attend_prefill_varlen
+    args = [P, P, P, 1, P, P, P, P, 4, P, 0, NUL, 1, 4, 2, 256, 128, 64, 1]
+    assert p(*args, NUL, 0, NUL) == dash.DASH_ERR_WORKSPACE
+    bad = list(args)
+    bad[4] = NUL
+    assert p(*bad, NUL, 0, NUL) == dash.DASH_ERR_NULL
+    bad = list(args)
+    bad[17] = 48
+    assert p(*bad, NUL, 0, NUL) == dash.DASH_ERR_UNSUPPORTED        # B % 32 != 0
