@@ -31,6 +31,8 @@
 
 #include <math.h>
 
+#include <algorithm>
+
 namespace dash {
 
 struct RouteParams {
@@ -47,6 +49,7 @@ struct RouteParams {
     float* stats;       // nullable [b, h_q, n, 2]: max raw logit and the threshold
                         // (τ; α = 1: log2 Σ 2^y) of each (head, row)
     const int32_t* seq_len = nullptr;  // nullable: ragged batch, sequence b holds seq_len[b] rows
+    int redo = 0;       // 1: route only the row groups the candidate kernel marked (cnt -1)
 };
 
 // Order-preserving map of a float to an unsigned key (larger float, larger key).
@@ -269,6 +272,99 @@ template <int CW> struct RouteSplit {
     }
 };
 
+// Compaction of the rows row0 .. row0+R-1 of one row group by one wavefront: the
+// group weights of row j are wl[j * WS + c] (α = 1: log2 w) for the visible chunks
+// c < nvis. Writes ascending chunk ids of the support with d = (ln w - μ)/σ, the
+// counts and (optionally) the dense weights. With a top-k budget the support keeps
+// its top_k largest weights (ties to the lower chunk): the k-th largest key is found
+// by bisection on the key bits, counted with ballots over the row. NK >= WS/64.
+template <bool SOFT, int NK>
+__device__ __forceinline__ void route_compact(const RouteParams& p, const float* wl, int WS, int R, int row0, int nb,
+                                              int nvis, int bi, int r, int lane) {
+    const size_t rowbase = ((size_t)bi * p.h_kv + r) * p.n;
+    for (int j = 0; j < R; ++j) {
+        const int row = row0 + j;
+        if (row >= p.n) break;
+        if (row >= nb) {                              // a padding row of a ragged batch
+            if (lane == 0) p.cnt[rowbase + row] = 0;
+            continue;
+        }
+        const float* wr = wl + j * WS;
+        auto cand = [&](int c, float v) { return c < nvis && (SOFT || v > 0.f); };
+        bool limit = false;
+        uint32_t kstar = 0;
+        int need_eq = 0;
+        if (p.top_k > 0) {
+            uint32_t key[NK];
+            int ncand = 0;
+#pragma unroll
+            for (int q = 0; q < NK; ++q) {
+                const int c = lane + 64 * q;
+                const float v = c < nvis ? wr[c] : 0.f;
+                const bool in = cand(c, v);
+                key[q] = in ? float_key(v) : 0u;
+                ncand += __builtin_popcountll(ballot(in));
+            }
+            if (ncand > p.top_k) {                    // wavefront-uniform
+                limit = true;
+                uint32_t prefix = 0;
+                for (int bit = 31; bit >= 0; --bit) {
+                    const uint32_t trial = prefix | (1u << bit);
+                    int cnt = 0;
+#pragma unroll
+                    for (int q = 0; q < NK; ++q) cnt += __builtin_popcountll(ballot(key[q] >= trial));
+                    if (cnt >= p.top_k) prefix = trial;
+                }
+                kstar = prefix;
+                int gt = 0;
+#pragma unroll
+                for (int q = 0; q < NK; ++q) gt += __builtin_popcountll(ballot(key[q] > kstar));
+                need_eq = p.top_k - gt;
+            }
+        }
+        // membership of chunk c (value v) given the running count of earlier ties
+        auto selected = [&](int c, float v, int& eq_before) {
+            const bool in = cand(c, v);
+            if (!limit) return in;
+            const uint32_t k = in ? float_key(v) : 0u;
+            const uint64_t eq = ballot(in && k == kstar);
+            const int rank = eq_before + __builtin_popcountll(eq & ((1ull << lane) - 1ull));
+            eq_before += __builtin_popcountll(eq);
+            return in && (k > kstar || (k == kstar && rank < need_eq));
+        };
+        float sl = 0.f, sc = 0.f;
+        int eqb = 0;
+        for (int c0 = 0; c0 < nvis; c0 += 64) {
+            const int c = c0 + lane;
+            const float v = c < nvis ? wr[c] : 0.f;
+            if (selected(c, v, eqb)) { sl += SOFT ? v : fast_log2(v); sc += 1.f; }
+        }
+        sl = wave_sum(sl);
+        sc = wave_sum(sc);
+        const float mu2 = sc > 0.f ? sl / sc : 0.f;            // μ in log2 units
+        const float bscale = kLn2 * p.inv_sigma;
+        int32_t* idx = p.idx + (rowbase + row) * (size_t)p.list_cap;
+        float* bias = p.bias + (rowbase + row) * (size_t)p.list_cap;
+        float* wo = p.w_out ? p.w_out + (rowbase + row) * (size_t)p.kbar_cap : nullptr;
+        int base = 0;
+        eqb = 0;
+        for (int c0 = 0; c0 < p.T_c; c0 += 64) {
+            const int c = c0 + lane;
+            const float v = (c < nvis) ? wr[c] : (SOFT ? -INFINITY : 0.f);
+            const bool in = selected(c, v, eqb);
+            const uint64_t m = ballot(in);
+            const int pre = __builtin_popcountll(m & ((1ull << lane) - 1ull));
+            if (in) {
+                idx[base + pre] = c;
+                bias[base + pre] = p.inv_sigma == 0.f ? 0.f : bscale * ((SOFT ? v : fast_log2(v)) - mu2);
+            }
+            if (wo && c < p.T_c) wo[c] = SOFT ? fast_exp2(v) : v;
+            base += __builtin_popcountll(m);
+        }
+        if (lane == 0) p.cnt[rowbase + row] = base;
+    }
+}
+
 // One workgroup = G groups of 16 (row, head) pairs (16/g rows x the g heads of a
 // group each) times CW wavefronts per group; each wavefront holds NT tiles of its
 // rows' chunks in registers (CW > 1 for long rows).
@@ -291,10 +387,17 @@ __global__ __launch_bounds__(512) void entmax_route_kernel(RouteParams p) {
     // all rows of the workgroup lie in one chunk (G*R divides B): one visible range
     const int wg_row0 = blockIdx.x * G * R;
     const int row0 = wg_row0 + gid * R;
-    const bool wave_live = row0 < p.n;
     // ragged batch: the sequence's own tokens and complete chunks
     const int nb = p.seq_len ? min(max(p.seq_len[bi], 0), p.n) : p.n;
     const int Tb = nb / p.B;
+    // second pass after the candidate router: only the row groups it marked (count -1)
+    // are routed here; a workgroup without one leaves at once (before any barrier)
+    bool marked = true;
+    if (p.redo) {
+        marked = row0 < nb && p.cnt[((size_t)bi * p.h_kv + r) * p.n + row0] == -1;
+        if (!__syncthreads_or(marked)) return;
+    }
+    const bool wave_live = row0 < p.n && marked;
     constexpr int RSTG = route_ring_stages<NT, CW>();
     constexpr bool RING = route_uses_ring<T, CW>();
     char* kstage = rsm;                                              // RSTG stages (ring only)
@@ -558,89 +661,240 @@ __global__ __launch_bounds__(512) void entmax_route_kernel(RouteParams p) {
     // chunk): the k-th largest key is found by bisection on the key bits, counted
     // with ballots over the row.
     constexpr bool SOFT = PM == kSoftmaxRouting;
-    constexpr int NK = (WS + 63) / 64;                // keys per lane
-    const size_t rowbase = ((size_t)bi * p.h_kv + r) * p.n;
-    for (int j = 0; j < R; ++j) {
-        const int row = row0 + j;
-        if (row >= p.n) break;
-        if (row >= nb) {                              // a padding row of a ragged batch
-            if (lane == 0) p.cnt[rowbase + row] = 0;
-            continue;
-        }
-        const float* wr = wl + j * WS;
-        auto cand = [&](int c, float v) { return c < nvis && (SOFT || v > 0.f); };
-        bool limit = false;
-        uint32_t kstar = 0;
-        int need_eq = 0;
-        if (p.top_k > 0) {
-            uint32_t key[NK];
-            int ncand = 0;
+    route_compact<SOFT, (WS + 63) / 64>(p, wl, WS, R, row0, nb, nvis, bi, r, lane);
+}
+
+// ---------------------------------------------------------------------------------
+// Candidate router for long rows (bf16 queries, α > 1): the same routing as
+// entmax_route_kernel, without keeping a row's logits in registers.
+//  * One wavefront per group of 16 (row, head) pairs; the W groups of a workgroup
+//    share one stream of split summaries through the LDS ring, so a workgroup reads
+//    the summaries once for W·16/g rows.
+//  * While the logits stream by, a lane keeps in LDS only its chunks whose logit can
+//    still reach the support: since τ >= -1 on y = cs(z̄ - max z̄), a chunk with
+//    z̄ <= max - 1/cs never enters it, and the lane's running maximum is a lower
+//    bound of the row maximum. When a lane's list fills up, Newton's iterate on the
+//    kept chunks gives a lower bound θ of the threshold (the root of a sum over fewer
+//    terms lies left of the full root), and chunks below θ are dropped.
+//  * The kept chunks then give τ (Newton from the left, as in the register kernel),
+//    the group weights w_c = mean_h ŵ_hc are summed into an LDS row by LDS atomic
+//    adds issued in a fixed order by one wavefront, and the rows are compacted by
+//    route_compact. A group whose lists overflow writes count -1 on its rows, and a
+//    second launch of entmax_route_kernel (redo) routes those rows.
+constexpr int kCandCap = 24;            // kept chunks per lane
+constexpr float kCandMargin = 1.0f / 1024.0f;  // slack on every bound, in units of y
+
+template <int PM>
+__device__ __forceinline__ float cand_newton(const float (&cv)[kCandCap], int n, float m, float cs, float pexp,
+                                             bool active, float tau) {
+    bool done = !active;
+    for (int it = 0; it < 100; ++it) {
+        float a0 = 0.f, a1 = 0.f;
 #pragma unroll
-            for (int q = 0; q < NK; ++q) {
-                const int c = lane + 64 * q;
-                const float v = c < nvis ? wr[c] : 0.f;
-                const bool in = cand(c, v);
-                key[q] = in ? float_key(v) : 0u;
-                ncand += __builtin_popcountll(ballot(in));
-            }
-            if (ncand > p.top_k) {                    // wavefront-uniform
-                limit = true;
-                uint32_t prefix = 0;
-                for (int bit = 31; bit >= 0; --bit) {
-                    const uint32_t trial = prefix | (1u << bit);
-                    int cnt = 0;
-#pragma unroll
-                    for (int q = 0; q < NK; ++q) cnt += __builtin_popcountll(ballot(key[q] >= trial));
-                    if (cnt >= p.top_k) prefix = trial;
-                }
-                kstar = prefix;
-                int gt = 0;
-#pragma unroll
-                for (int q = 0; q < NK; ++q) gt += __builtin_popcountll(ballot(key[q] > kstar));
-                need_eq = p.top_k - gt;
-            }
+        for (int j = 0; j < kCandCap; ++j)
+            if (j < n) accum_pow<PM>(pos_part(cs * (cv[j] - m) - tau), pexp, a0, a1);
+        a0 = pair32_sum(pair16_sum(a0));
+        a1 = pair32_sum(pair16_sum(a1));
+        float delta;
+        if (PM == 1) {
+            delta = (a1 - 1.f) / a0;
+        } else {
+            const float nrm = (PM == 2) ? sqrtf(a1) : (PM == 4) ? sqrtf(sqrtf(a1)) : fast_exp2(fast_log2(a1) / pexp);
+            delta = (nrm - 1.f) * (a1 / nrm) / a0;
         }
-        // membership of chunk c (value v) given the running count of earlier ties
-        auto selected = [&](int c, float v, int& eq_before) {
-            const bool in = cand(c, v);
-            if (!limit) return in;
-            const uint32_t k = in ? float_key(v) : 0u;
-            const uint64_t eq = ballot(in && k == kstar);
-            const int rank = eq_before + __builtin_popcountll(eq & ((1ull << lane) - 1ull));
-            eq_before += __builtin_popcountll(eq);
-            return in && (k > kstar || (k == kstar && rank < need_eq));
-        };
-        float sl = 0.f, sc = 0.f;
-        int eqb = 0;
-        for (int c0 = 0; c0 < nvis; c0 += 64) {
-            const int c = c0 + lane;
-            const float v = c < nvis ? wr[c] : 0.f;
-            if (selected(c, v, eqb)) { sl += SOFT ? v : fast_log2(v); sc += 1.f; }
-        }
-        sl = wave_sum(sl);
-        sc = wave_sum(sc);
-        const float mu2 = sc > 0.f ? sl / sc : 0.f;            // μ in log2 units
-        const float bscale = kLn2 * p.inv_sigma;
-        int32_t* idx = p.idx + (rowbase + row) * (size_t)p.list_cap;
-        float* bias = p.bias + (rowbase + row) * (size_t)p.list_cap;
-        float* wo = p.w_out ? p.w_out + (rowbase + row) * (size_t)p.kbar_cap : nullptr;
-        int base = 0;
-        eqb = 0;
-        for (int c0 = 0; c0 < p.T_c; c0 += 64) {
-            const int c = c0 + lane;
-            const float v = (c < nvis) ? wr[c] : (SOFT ? -INFINITY : 0.f);
-            const bool in = selected(c, v, eqb);
-            const uint64_t m = ballot(in);
-            const int pre = __builtin_popcountll(m & ((1ull << lane) - 1ull));
-            if (in) {
-                idx[base + pre] = c;
-                bias[base + pre] = p.inv_sigma == 0.f ? 0.f : bscale * ((SOFT ? v : fast_log2(v)) - mu2);
-            }
-            if (wo && c < p.T_c) wo[c] = SOFT ? fast_exp2(v) : v;
-            base += __builtin_popcountll(m);
-        }
-        if (lane == 0) p.cnt[rowbase + row] = base;
+        if (!(a0 > 0.f)) delta = 0.f;
+        if (!done) tau += delta;
+        done = done || !(fabsf(delta) > 1e-6f);
+        if (ballot(!done) == 0) break;
     }
+    return tau;
+}
+
+template <int D> constexpr int cand_ring_stages() { return 3; }
+
+template <int D, int PM, int TB>
+__global__ __launch_bounds__(512) void entmax_route_cand_kernel(RouteParams p) {
+    typedef KSplitStage<D, 32> KS;
+    typedef __bf16 b8 __attribute__((ext_vector_type(8)));
+    constexpr int RSTG = cand_ring_stages<D>();
+    constexpr int CAP = kCandCap;
+    extern __shared__ __attribute__((aligned(16))) char rsm[];
+    const int W = blockDim.x >> 6;
+    const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int n16 = lane & 15, kg = lane >> 4;
+    const int g = p.g, lg = p.log2g;
+    const int R = 16 >> lg;
+    const int r = blockIdx.y, bi = blockIdx.z;
+    const int wg_row0 = blockIdx.x * W * R;
+    const int row0 = wg_row0 + wid * R;
+    const bool wave_live = row0 < p.n;
+    const int nb = p.seq_len ? min(max(p.seq_len[bi], 0), p.n) : p.n;
+    const int Tb = nb / p.B;
+    const int nvis = p.causal ? min(wg_row0 / p.B, Tb) : Tb;
+    const int my_row = row0 + (n16 >> lg);
+    const int my_head = r * g + (n16 & (g - 1));
+    const bool row_ok = wave_live && my_row < nb;
+    // LDS: the summary ring, later the rows' weights; then the lanes' kept chunks
+    const size_t region = max((size_t)RSTG * KS::BYTES, (size_t)W * R * TB * 4);
+    char* kstage = rsm;
+    float* cval = reinterpret_cast<float*>(rsm + region);               // [W][CAP][64]
+    uint16_t* cidx = reinterpret_cast<uint16_t*>(cval + (size_t)W * CAP * 64);   // [W][CAP][64]
+    auto slot = [&](int j) { return ((size_t)wid * CAP + j) * 64 + lane; };
+
+    const float cs = p.cs, inv_cs = 1.f / p.cs;
+    float mlane = -INFINITY;     // the lane's running maximum of z̄
+    float theta = -INFINITY;     // lower bound of the threshold on z̄ (the same in a pair's lanes)
+    int ncand = 0;
+    bool ovf = false;
+
+    if (nvis > 0) {                                   // workgroup-uniform
+        b8 qb[D / 32];
+        {
+            const uint16_t* qrow = static_cast<const uint16_t*>(p.Q) +
+                (((size_t)bi * p.h_q + my_head) * p.n + (row_ok ? my_row : 0)) * D + 8 * kg;
+#pragma unroll
+            for (int s = 0; s < D / 32; ++s) {
+                qb[s] = *reinterpret_cast<const b8*>(qrow + 32 * s);
+                if (!row_ok) qb[s] = b8{};
+            }
+        }
+        const int nst = (nvis + KS::CH - 1) / KS::CH;
+        constexpr int CPI = KS::BYTES / 1024;
+        const int cps = (CPI + W - 1) / W;
+        const uint8_t* ksrc = p.ksplit + ((size_t)bi * p.h_kv + r) * (size_t)p.T_pad * KS::ROWB;
+        // the lane's A-operand offsets inside a stage, the same for every stage
+        int aoff[2][3][D / 32];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int h = 0; h < 3; ++h)
+#pragma unroll
+                for (int s = 0; s < D / 32; ++s) aoff[tt][h][s] = KS::off(16 * tt + n16, h, 4 * s + kg);
+        auto issue = [&](int st) {
+            char* dst = kstage + (st % RSTG) * KS::BYTES;
+            const uint8_t* src = ksrc + (size_t)min(st, nst - 1) * KS::BYTES + lane * 16;
+            for (int i = 0; i < cps; ++i) {
+                int j = wid + i * W;
+                if (j >= CPI) j -= CPI;
+                __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint32_t*>(src + j * 1024),
+                                                 reinterpret_cast<uint32_t*>(dst + j * 1024), 16, 0, 0);
+            }
+        };
+        // drop the kept chunks below the bound that Newton's iterate on them gives
+        auto prune = [&]() {
+            float cv[CAP];
+#pragma unroll
+            for (int j = 0; j < CAP; ++j) cv[j] = j < ncand ? cval[slot(j)] : -INFINITY;
+            const float m = pair32_max(pair16_max(mlane));
+            // θ is below the root over the kept chunks (their set only grew above θ),
+            // so Newton may start there
+            const float tau0 = fmaxf(-1.f, cs * (theta - m));
+            const float tau = cand_newton<PM>(cv, ncand, m, cs, p.pexp, row_ok && m > -INFINITY, tau0);
+            if (row_ok && m > -INFINITY) theta = fmaxf(theta, m + (tau - kCandMargin) * inv_cs);
+            int k = 0;
+#pragma unroll
+            for (int j = 0; j < CAP; ++j) {
+                if (j < ncand && cv[j] > theta) {
+                    const uint16_t c = cidx[slot(j)];
+                    cval[slot(k)] = cv[j];
+                    cidx[slot(k)] = c;
+                    ++k;
+                }
+            }
+            ncand = k;
+        };
+        for (int j = 0; j < RSTG - 1; ++j) issue(j);
+        for (int st = 0; st < nst; ++st) {
+            wait_vm_at_most((RSTG - 2) * cps);
+            __syncthreads();
+            issue(st + RSTG - 1);
+            const char* stg = kstage + (st % RSTG) * KS::BYTES;
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+                const int cb = KS::CH * st + 16 * tt;
+                if (cb < nvis) {                      // workgroup-uniform
+                    f32x4 acc[3];
+#pragma unroll
+                    for (int h = 0; h < 3; ++h) {
+                        acc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int s = 0; s < D / 32; ++s) {
+                            const b8 a = *reinterpret_cast<const b8*>(stg + aoff[tt][h][s]);
+                            acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[s], acc[h], 0, 0, 0);
+                        }
+                    }
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int c = cb + 4 * kg + i;
+                        const float x = acc[0][i] + (acc[1][i] + acc[2][i]);
+                        const bool valid = row_ok && c < nvis;
+                        if (valid) mlane = fmaxf(mlane, x);
+                        const float lim = fmaxf(theta, mlane - (1.f + kCandMargin) * inv_cs);
+                        if (valid && x > lim) {
+                            if (ncand < CAP) {
+                                cval[slot(ncand)] = x;
+                                cidx[slot(ncand)] = (uint16_t)c;
+                                ++ncand;
+                            } else {
+                                ovf = true;
+                            }
+                        }
+                    }
+                }
+            }
+            // the pair's lanes share their maxima: a tighter bound for the next stage
+            mlane = pair32_max(pair16_max(mlane));
+            if (ballot(ncand > CAP - 8) != 0) prune();
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    __syncthreads();                                  // the ring is free: it holds the weights now
+    if (!wave_live) return;                           // no barrier follows
+    const size_t rowbase = ((size_t)bi * p.h_kv + r) * p.n;
+    if (ballot(ovf) != 0) {
+        // this group's lists overflowed: its rows are routed by the second pass
+        if (lane < R && row0 + lane < nb) p.cnt[rowbase + row0 + lane] = -1;
+        else if (lane < R && row0 + lane < p.n) p.cnt[rowbase + row0 + lane] = 0;
+        return;
+    }
+    float cv[CAP];
+    int cc[CAP];
+#pragma unroll
+    for (int j = 0; j < CAP; ++j) {
+        cv[j] = j < ncand ? cval[slot(j)] : -INFINITY;
+        cc[j] = j < ncand ? cidx[slot(j)] : 0;
+    }
+    const float m = pair32_max(pair16_max(mlane));
+    const bool active = row_ok && m > -INFINITY;
+    const float tau = cand_newton<PM>(cv, ncand, m, cs, p.pexp, active, fmaxf(-1.f, cs * (theta - m)));
+    if (p.stats && kg == 0 && row_ok) {
+        float* so = p.stats + 2 * (((size_t)bi * p.h_q + my_head) * p.n + my_row);
+        so[0] = m;
+        so[1] = tau;
+    }
+    // group weights: zero the rows' visible chunks, then every head adds its weight
+    // over g (exact: g is a power of two) by LDS atomic adds issued in a fixed order
+    // within this wavefront
+    float* wlw = reinterpret_cast<float*>(rsm) + (size_t)wid * R * TB;
+    const int nz = (nvis + 63) & ~63;
+    for (int j = 0; j < R; ++j)
+        for (int c = lane; c < nz; c += 64) wlw[j * TB + c] = 0.f;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    float* wr = wlw + (size_t)(n16 >> lg) * TB;
+    const float inv_g = 1.f / (float)g;
+#pragma unroll
+    for (int j = 0; j < CAP; ++j) {
+        if (active && j < ncand) {
+            const float v = pow_p<PM>(pos_part(cs * (cv[j] - m) - tau), p.pexp);
+            if (v > 0.f) atomicAdd(wr + cc[j], v * inv_g);
+        }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    route_compact<false, TB / 64>(p, wlw, TB, R, row0, nb, nvis, bi, r, lane);
 }
 
 // Workgroup geometry: up to 8 wavefronts = G groups x CW; all rows of a workgroup
@@ -678,6 +932,33 @@ static hipError_t launch_route_pm(const RouteParams& p, dim3 grid, dim3 block, s
     return hipGetLastError();
 }
 
+// Candidate router geometry: W wavefronts (one group of 16 pairs each) with W·R | B
+// and the LDS (ring or weight rows, plus the kept chunks) within 160 KiB; 0 if none.
+template <int D, int TB>
+inline int cand_waves(int R, int B, size_t* lds) {
+    for (int W = 8; W >= 1; W >>= 1) {
+        if (B % (W * R) != 0) continue;
+        const size_t region = std::max((size_t)cand_ring_stages<D>() * KSplitStage<D, 32>::BYTES,
+                                       (size_t)W * R * TB * 4);
+        const size_t bytes = region + (size_t)W * kCandCap * 64 * 6;
+        if (bytes <= 160 * 1024) {
+            *lds = bytes;
+            return W;
+        }
+    }
+    return 0;
+}
+
+template <int D, int PM, int TB>
+static hipError_t launch_cand_pm(const RouteParams& p, dim3 grid, dim3 block, size_t lds, hipStream_t s) {
+    auto kern = entmax_route_cand_kernel<D, PM, TB>;
+    static hipError_t configured = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (configured != hipSuccess) return configured;
+    hipLaunchKernelGGL(kern, grid, block, lds, s, p);
+    return hipGetLastError();
+}
+
 template <typename T, int D, int NT, int CW>
 static hipError_t launch_route_nt(const RouteParams& p, int b, hipStream_t s) {
     const int R = 16 / p.g;
@@ -694,14 +975,47 @@ static hipError_t launch_route_nt(const RouteParams& p, int b, hipStream_t s) {
     }
 }
 
+// Long rows with bf16 queries and α > 1: the candidate router, then the register
+// kernel on the row groups it could not finish. Returns hipErrorNotSupported when
+// the candidate router does not apply (the caller runs the register kernel alone).
+template <int D, int NT, int CW, int TB>
+static hipError_t launch_route_cand(const RouteParams& p, int b, hipStream_t s) {
+    const int R = 16 / p.g;
+    size_t lds = 0;
+    const int W = cand_waves<D, TB>(R, p.B, &lds);
+    if (W < 4 || p.pmode == kSoftmaxRouting) return hipErrorNotSupported;
+    dim3 grid((p.n + W * R - 1) / (W * R), p.h_kv, b), block(64 * W);
+    hipError_t e;
+    switch (p.pmode) {
+        case 1: e = launch_cand_pm<D, 1, TB>(p, grid, block, lds, s); break;
+        case 2: e = launch_cand_pm<D, 2, TB>(p, grid, block, lds, s); break;
+        case 4: e = launch_cand_pm<D, 4, TB>(p, grid, block, lds, s); break;
+        default: e = launch_cand_pm<D, 0, TB>(p, grid, block, lds, s); break;
+    }
+    if (e != hipSuccess) return e;
+    RouteParams q = p;
+    q.redo = 1;
+    return launch_route_nt<uint16_t, D, NT, CW>(q, b, s);
+}
+
 template <typename T, int D>
 static hipError_t launch_route_d(const RouteParams& p, int b, hipStream_t s) {
     switch (route_tiles_bucket(p.T_c)) {
         case 2: return launch_route_nt<T, D, 2, 1>(p, b, s);
         case 8: return launch_route_nt<T, D, 8, 1>(p, b, s);
         case 32: return launch_route_nt<T, D, 32, 1>(p, b, s);
-        case 64: return launch_route_nt<T, D, 32, 2>(p, b, s);
-        default: return launch_route_nt<T, D, 32, 4>(p, b, s);
+        case 64:
+            if constexpr (sizeof(T) == 2) {
+                const hipError_t e = launch_route_cand<D, 32, 2, 1024>(p, b, s);
+                if (e != hipErrorNotSupported) return e;
+            }
+            return launch_route_nt<T, D, 32, 2>(p, b, s);
+        default:
+            if constexpr (sizeof(T) == 2) {
+                const hipError_t e = launch_route_cand<D, 32, 4, 2048>(p, b, s);
+                if (e != hipErrorNotSupported) return e;
+            }
+            return launch_route_nt<T, D, 32, 4>(p, b, s);
     }
 }
 
