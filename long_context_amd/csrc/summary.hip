@@ -3,11 +3,11 @@
 // also used as the values:  k̄_c = sum_t softmax_t(<q̄, k_t>/sqrt(d)) k_t.
 //
 // chunk_summary_kernel: one wavefront per (b, r, c). Each lane reads 16 bytes of a
-// key row per row group (a wave reads 1 KiB contiguous, 16 row groups in flight), the row's dot product
-// with q̄ is reduced across the lanes that share the row, and an online softmax
-// (log2 domain, fp32) accumulates the weighted keys. The row groups are merged at
-// the end and the fp32 summary is written once. HBM-bound: the K chunk is read
-// exactly once.
+// key row per row group (a wave reads 1 KiB contiguous, 16 row groups in flight), the
+// rows' dot products with q̄ are reduced across the lanes that share a row (DPP), and
+// a softmax in the log2 domain (fp32) accumulates the weighted keys, one batch of 16
+// row groups at a time. The row groups are merged at the end and the fp32 summary is
+// written once. HBM-bound: the K chunk is read exactly once.
 #include "common.h"
 #include "kernels.h"
 
@@ -34,6 +34,19 @@ template <> struct Vec16<uint16_t> {
         }
     }
 };
+
+// Sum over aligned groups of LPR lanes (8, 16 or 32), the same result in every lane of
+// a group: DPP xor 1, xor 2, the 8-lane mirror and the 16-lane mirror with a symmetric
+// combine, then the swap of 16-lane rows.
+template <int LPR>
+__device__ __forceinline__ float lane_group_sum(float v) {
+    v += dpp_partner<0xB1>(v);
+    v += dpp_partner<0x4E>(v);
+    v += dpp_partner<0x141>(v);
+    if constexpr (LPR >= 16) v += dpp_partner<0x140>(v);
+    if constexpr (LPR >= 32) v = pair16_sum(v);
+    return v;
+}
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void chunk_summary_kernel(
@@ -73,7 +86,8 @@ __global__ __launch_bounds__(256) void chunk_summary_kernel(
     for (int v = 0; v < VEC; ++v) acc[v] = 0.f;
 
     // the rows of a batch (UNR row groups) are loaded before any is used, so a lane has
-    // UNR 16-byte reads in flight instead of one dependent read per row group
+    // UNR 16-byte reads in flight; their UNR logits are independent (row sums by DPP
+    // within the lanes of a row), and the batch enters the running softmax once
     constexpr int UNR = 16;
     for (int b0 = 0; b0 < B; b0 += RPI * UNR) {
         float kk[UNR][VEC];
@@ -82,24 +96,34 @@ __global__ __launch_bounds__(256) void chunk_summary_kernel(
             const int t = b0 + u * RPI + rr;
             if (t < B) Vec16<T>::load(Kc + (size_t)t * D, kk[u]);
         }
+        float sc[UNR];
+        float bm = -INFINITY;
 #pragma unroll
         for (int u = 0; u < UNR; ++u) {
+            sc[u] = -INFINITY;
             if (b0 + u * RPI < B) {                  // wave-uniform: B is a multiple of RPI
-                float s = 0.f;
+                float sd = 0.f;
 #pragma unroll
-                for (int v = 0; v < VEC; ++v) s = fmaf(q[v], kk[u][v], s);
-#pragma unroll
-                for (int o = LPR / 2; o >= 1; o >>= 1) s += shfl_xor(s, o);
-                s *= scale;
-                const float mn = fmaxf(m, s);
-                const float corr = fast_exp2(m - mn);
-                const float p = fast_exp2(s - mn);
-                l = fmaf(l, corr, p);
-#pragma unroll
-                for (int v = 0; v < VEC; ++v) acc[v] = fmaf(acc[v], corr, p * kk[u][v]);
-                m = mn;
+                for (int v = 0; v < VEC; ++v) sd = fmaf(q[v], kk[u][v], sd);
+                sc[u] = lane_group_sum<LPR>(sd) * scale;
+                bm = fmaxf(bm, sc[u]);
             }
         }
+        const float mn = fmaxf(m, bm);
+        const float corr = fast_exp2(m - mn);
+        l *= corr;
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) acc[v] *= corr;
+#pragma unroll
+        for (int u = 0; u < UNR; ++u) {
+            if (b0 + u * RPI < B) {
+                const float pu = fast_exp2(sc[u] - mn);
+                l += pu;
+#pragma unroll
+                for (int v = 0; v < VEC; ++v) acc[v] = fmaf(pu, kk[u][v], acc[v]);
+            }
+        }
+        m = mn;
     }
     // merge the RPI row groups of the wave
 #pragma unroll
