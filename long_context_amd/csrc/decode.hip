@@ -14,6 +14,11 @@
 //                          takes the group average in a fixed head order, μ, the
 //                          bias and a workgroup ballot compaction. The heads of a
 //                          group are placed on one XCD (one L2).
+//   decode_group_route_kernel  instead of the two above, for bf16 queries over more
+//                          than 1024 chunks: one workgroup per group computes the g
+//                          heads' logits (k̄ split into three bf16 terms on load),
+//                          one wavefront per head solves τ, and the group step reads
+//                          the heads' weights from LDS.
 //   decode_attn_kernel     split-KV Stage 2 as a balanced token stream: every group
 //                          contributes its routed chunks, then its diagonal chunk up
 //                          to the query, in 32-token units; the units of all groups
@@ -408,6 +413,263 @@ __global__ __launch_bounds__(kRouteThreads) void decode_route_kernel(DecodeParam
 }
 
 // ---------------------------------------------------------------------------------
+// Routing of a whole group in one workgroup (bf16 queries): decode_group_route_kernel
+// computes the g heads' logits itself, so no score buffer, arrival counter or second
+// kernel is involved, and the group average reads the heads' weights from LDS.
+//  * Logits: 16-chunk tiles over the 8 wavefronts; each k̄ row is split on load into
+//    three bf16 terms (hi + mid + lo reproduces the fp32 value), so three 16x16x32
+//    bf16 MFMA chains against the exact bf16 q give the fp32 products; lane (kg, n)
+//    ends with chunks 16t + 4kg + i of head n (the prefill router's arithmetic).
+//  * Threshold: one wavefront per head, Newton from τ = -1 with wavefront sums only.
+//  * Group step as in decode_route_kernel, with the workgroup's 8 wavefronts.
+constexpr int kGroupThreads = 512;
+constexpr int kGroupWaves = kGroupThreads / 64;
+
+__device__ __forceinline__ float blockg_sum(float v, float* buf) {
+    v = wave_sum(v);
+    const int wid = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) buf[wid] = v;
+    __syncthreads();
+    float r = 0.f;
+#pragma unroll
+    for (int w = 0; w < kGroupWaves; ++w) r += buf[w];
+    __syncthreads();
+    return r;
+}
+__device__ __forceinline__ int blockg_sum_int(int v, int* buf) {
+    v = wave_sum_int(v);
+    if ((threadIdx.x & 63) == 0) buf[threadIdx.x >> 6] = v;
+    __syncthreads();
+    int r = 0;
+#pragma unroll
+    for (int w = 0; w < kGroupWaves; ++w) r += buf[w];
+    __syncthreads();
+    return r;
+}
+__device__ __forceinline__ int blockg_excl_scan(int v, int* buf) {
+    const int incl = wave_incl_scan(v);
+    const int wid = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 63) buf[wid] = incl;
+    __syncthreads();
+    int pre = incl - v;
+    for (int w = 0; w < wid; ++w) pre += buf[w];
+    __syncthreads();
+    return pre;
+}
+
+// LDS of the group router: 16 head rows of NV * 64 floats.
+template <int NV> constexpr size_t dec_group_lds() { return (size_t)16 * NV * 64 * sizeof(float); }
+
+template <int D, int PM, int NV>
+__global__ __launch_bounds__(kGroupThreads) void decode_group_route_kernel(DecodeParams p, const uint16_t* Q,
+                                                                           int ngroups) {
+    constexpr bool SOFT = PM == kDecSoftmax;
+    constexpr int VPT = NV * 64 / kGroupThreads;      // chunks per thread in the group step
+    typedef __bf16 b8 __attribute__((ext_vector_type(8)));
+    extern __shared__ __attribute__((aligned(16))) float hw[];    // [16][TS]
+    __shared__ float red[kGroupWaves];
+    __shared__ int ired[kGroupWaves];
+    const int grp = blockIdx.x;
+    if (grp >= ngroups) return;
+    const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
+    const int n16 = lane & 15, kg = lane >> 4;
+    const int g = p.g;
+    const int bi = grp / p.h_kv, r = grp % p.h_kv;
+    const int nvis = visible_of(p, seq_len_of(p, bi));
+    constexpr int TS = NV * 64;
+
+    if (nvis > 0) {                                   // workgroup-uniform
+        // logits of 16-chunk tiles; wavefront w takes tiles w, w + 8, ..., four at a time
+        const bool head_ok = n16 < g;
+        b8 qb[D / 32];
+        {
+            const uint16_t* qrow = Q + ((size_t)bi * p.h_q + r * g + (head_ok ? n16 : 0)) * D + 8 * kg;
+#pragma unroll
+            for (int s = 0; s < D / 32; ++s) {
+                qb[s] = *reinterpret_cast<const b8*>(qrow + 32 * s);
+                if (!head_ok) qb[s] = b8{};
+            }
+        }
+        const float* kb = p.kbar + (size_t)grp * p.kbar_cap * D + 8 * kg;
+        const int ntile = (nvis + 15) / 16;
+        constexpr int TPR = 4;                        // tiles of a wavefront in flight
+        for (int t0 = wid; t0 < ntile; t0 += kGroupWaves * TPR) {
+            f32x4 raw[TPR][D / 32][2];
+#pragma unroll
+            for (int u = 0; u < TPR; ++u) {
+                const int t = min(t0 + u * kGroupWaves, ntile - 1);
+                const float* krow = kb + (size_t)min(16 * t + n16, nvis - 1) * D;
+#pragma unroll
+                for (int s = 0; s < D / 32; ++s) {
+                    raw[u][s][0] = *reinterpret_cast<const f32x4*>(krow + 32 * s);
+                    raw[u][s][1] = *reinterpret_cast<const f32x4*>(krow + 32 * s + 4);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < TPR; ++u) {
+                const int t = t0 + u * kGroupWaves;
+                if (t < ntile) {                      // wavefront-uniform
+                    f32x4 acc[3];
+#pragma unroll
+                    for (int h = 0; h < 3; ++h) acc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int s = 0; s < D / 32; ++s) {
+                        b8 hv, mv, lv;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const float x = raw[u][s][e >> 2][e & 3];
+                            const __bf16 hb = (__bf16)x;
+                            const float r1 = x - (float)hb;
+                            const __bf16 mb = (__bf16)r1;
+                            hv[e] = hb; mv[e] = mb; lv[e] = (__bf16)(r1 - (float)mb);
+                        }
+                        acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hv, qb[s], acc[0], 0, 0, 0);
+                        acc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mv, qb[s], acc[1], 0, 0, 0);
+                        acc[2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lv, qb[s], acc[2], 0, 0, 0);
+                    }
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int ch = 16 * t + 4 * kg + i;
+                        if (head_ok && ch < nvis) hw[n16 * TS + ch] = acc[0][i] + (acc[1][i] + acc[2][i]);
+                    }
+                }
+            }
+        }
+    }
+    __syncthreads();
+    if (nvis > 0) {
+        // per head: y = cs (z - max z) <= 0, then τ (α > 1) or log2 Σ 2^y (α = 1); the
+        // head's weights replace its logits
+        for (int h = wid; h < g; h += kGroupWaves) {
+            float* row = hw + h * TS;
+            float y[NV];
+            float mx = -INFINITY;
+#pragma unroll
+            for (int k = 0; k < NV; ++k) {
+                const int c = 64 * k + lane;
+                y[k] = c < nvis ? row[c] : -INFINITY;
+                mx = fmaxf(mx, y[k]);
+            }
+            mx = wave_max(mx);
+#pragma unroll
+            for (int k = 0; k < NV; ++k) y[k] = p.cs * (y[k] - mx);
+            if constexpr (SOFT) {
+                float se = 0.f;
+#pragma unroll
+                for (int k = 0; k < NV; ++k) se += fast_exp2(y[k]);
+                const float lse = fast_log2(wave_sum(se));
+#pragma unroll
+                for (int k = 0; k < NV; ++k) {
+                    const int c = 64 * k + lane;
+                    if (c < nvis) row[c] = y[k] - lse;
+                }
+            } else {
+                float tau = -1.f;
+                for (int it = 0; it < 100; ++it) {
+                    float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+                    for (int k = 0; k < NV; ++k)
+                        dec_accum<PM>(__builtin_amdgcn_fmed3f(y[k] - tau, 0.f, 1.f), p.pexp, a0, a1);
+                    a0 = wave_sum(a0);
+                    a1 = wave_sum(a1);
+                    float delta;
+                    if (PM == 1) delta = (a1 - 1.f) / a0;
+                    else {
+                        const float nrm = (PM == 2) ? sqrtf(a1) : (PM == 4) ? sqrtf(sqrtf(a1)) : fast_exp2(fast_log2(a1) / p.pexp);
+                        delta = (nrm - 1.f) * (a1 / nrm) / a0;
+                    }
+                    if (!(a0 > 0.f)) delta = 0.f;
+                    tau += delta;
+                    if (!(fabsf(delta) > 1e-6f)) break;
+                }
+#pragma unroll
+                for (int k = 0; k < NV; ++k) {
+                    const int c = 64 * k + lane;
+                    if (c < nvis) row[c] = dec_pow<PM>(__builtin_amdgcn_fmed3f(y[k] - tau, 0.f, 1.f), p.pexp);
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    // group average in a fixed head order, then the fixed budget, μ and the compaction
+    // (thread tid holds chunks VPT*tid .. VPT*tid+VPT-1)
+    const float inv_g = 1.f / (float)g;
+    float wv[VPT];
+    bool in[VPT];
+    int ncand = 0;
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+        const int c = VPT * tid + k;
+        float w = SOFT ? -INFINITY : 0.f;
+        if (c < nvis) {
+            if (SOFT) {
+                float m = -INFINITY;
+                for (int h = 0; h < g; ++h) m = fmaxf(m, hw[h * TS + c]);
+                float sm = 0.f;
+                for (int h = 0; h < g; ++h) sm += fast_exp2(hw[h * TS + c] - m);
+                w = m + fast_log2(sm) - fast_log2((float)g);
+            } else {
+                for (int h = 0; h < g; ++h) w += hw[h * TS + c];
+                w *= inv_g;
+            }
+        }
+        wv[k] = w;
+        in[k] = c < nvis && (SOFT || w > 0.f);
+        ncand += in[k] ? 1 : 0;
+    }
+    if (p.top_k > 0 && blockg_sum_int(ncand, ired) > p.top_k) {     // workgroup-uniform
+        uint32_t key[VPT];
+#pragma unroll
+        for (int k = 0; k < VPT; ++k) key[k] = in[k] ? dec_float_key(wv[k]) : 0u;
+        uint32_t kstar = 0;
+        for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t trial = kstar | (1u << bit);
+            int ge = 0;
+#pragma unroll
+            for (int k = 0; k < VPT; ++k) ge += key[k] >= trial ? 1 : 0;
+            if (blockg_sum_int(ge, ired) >= p.top_k) kstar = trial;
+        }
+        int gt = 0, eq = 0;
+#pragma unroll
+        for (int k = 0; k < VPT; ++k) { gt += key[k] > kstar ? 1 : 0; eq += (in[k] && key[k] == kstar) ? 1 : 0; }
+        const int need_eq = p.top_k - blockg_sum_int(gt, ired);
+        int rank = blockg_excl_scan(eq, ired);
+#pragma unroll
+        for (int k = 0; k < VPT; ++k) {
+            if (in[k] && key[k] == kstar) in[k] = rank++ < need_eq;
+            else in[k] = in[k] && key[k] > kstar;
+        }
+    }
+    float sl = 0.f, scn = 0.f;
+#pragma unroll
+    for (int k = 0; k < VPT; ++k)
+        if (in[k]) { sl += SOFT ? wv[k] : fast_log2(wv[k]); scn += 1.f; }
+    const float tsl = blockg_sum(sl, red);
+    const float tsc = blockg_sum(scn, red);
+    const float mu2 = tsc > 0.f ? tsl / tsc : 0.f;
+    const float bscale = kLn2 * p.inv_sigma;
+    int32_t* idx = p.idx + (size_t)grp * p.list_cap;
+    float* bias = p.bias + (size_t)grp * p.list_cap;
+    int mine = 0;
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) mine += in[k] ? 1 : 0;
+    int pos = blockg_excl_scan(mine, ired);
+    const int base = blockg_sum_int(mine, ired);
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+        const int c = VPT * tid + k;
+        if (in[k]) {
+            idx[pos] = c;
+            bias[pos] = p.inv_sigma == 0.f ? 0.f : bscale * ((SOFT ? wv[k] : fast_log2(wv[k])) - mu2);
+            ++pos;
+        }
+        if (p.w_out && c < p.T_route) p.w_out[(size_t)grp * p.kbar_cap + c] = SOFT ? fast_exp2(wv[k]) : wv[k];
+    }
+    if (tid == 0) p.cnt[grp] = base;
+}
+
+// ---------------------------------------------------------------------------------
 // The decode token stream. Group grp = b * h_kv + r contributes units_of(grp) units
 // of 32 tokens: cnt * B/32 for its routed chunks, then the diagonal chunk up to the
 // query. The units of all groups, in group order, form one sequence of W units; the
@@ -736,6 +998,37 @@ static hipError_t launch_dec_route(const DecodeParams& p, int ngroups, hipStream
     }
 }
 
+template <int D, int PM, int NV>
+static hipError_t launch_dec_group_pm(const DecodeParams& p, const void* Q, int ngroups, hipStream_t s) {
+    auto kern = decode_group_route_kernel<D, PM, NV>;
+    static hipError_t configured = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, 150 * 1024);
+    if (configured != hipSuccess) return configured;
+    hipLaunchKernelGGL(kern, dim3(ngroups), dim3(kGroupThreads), dec_group_lds<NV>(), s, p,
+                       static_cast<const uint16_t*>(Q), ngroups);
+    return hipGetLastError();
+}
+
+template <int D, int NV>
+static hipError_t launch_dec_group_nv(const DecodeParams& p, const void* Q, int ngroups, hipStream_t s) {
+    switch (p.pmode) {
+        case kDecSoftmax: return launch_dec_group_pm<D, kDecSoftmax, NV>(p, Q, ngroups, s);
+        case 1: return launch_dec_group_pm<D, 1, NV>(p, Q, ngroups, s);
+        case 2: return launch_dec_group_pm<D, 2, NV>(p, Q, ngroups, s);
+        case 4: return launch_dec_group_pm<D, 4, NV>(p, Q, ngroups, s);
+        default: return launch_dec_group_pm<D, 0, NV>(p, Q, ngroups, s);
+    }
+}
+
+// bf16 queries: the whole routing in decode_group_route_kernel (NV chunks of 64 per
+// head row: the group step's threads hold NV/8 chunks each).
+template <int D>
+static hipError_t launch_dec_group(const DecodeParams& p, const void* Q, int ngroups, hipStream_t s) {
+    if (p.T_route <= 512) return launch_dec_group_nv<D, 8>(p, Q, ngroups, s);
+    if (p.T_route <= 1024) return launch_dec_group_nv<D, 16>(p, Q, ngroups, s);
+    return launch_dec_group_nv<D, 32>(p, Q, ngroups, s);
+}
+
 // Ring stages and wavefronts resident per CU of the attention kernel.
 template <typename T, int D> struct DecAttnCfg {
     static constexpr int NST = sizeof(T) == 2 ? 2 : 2;
@@ -767,13 +1060,23 @@ static hipError_t launch_decode_t(DecodeParams p, const DecodeArgs& a, hipStream
     }();
     const int ngroups = a.b * a.h_kv;
     p.streams = min(kMaxStreams, device_cus() * min(per_cu, kDecStreamsPerCU));
-    dim3 g1(max((p.T_route + 63) / 64, 1), p.h_kv, a.b);
-    hipLaunchKernelGGL((decode_scores_kernel<D>), g1, dim3(256), 0, s, p, a.Q, a.in_bf16);
-    const hipError_t er = p.T_route <= 256 ? launch_dec_route<1>(p, ngroups, s)
-                        : p.T_route <= 512 ? launch_dec_route<2>(p, ngroups, s)
-                        : p.T_route <= 1024 ? launch_dec_route<4>(p, ngroups, s)
-                                            : launch_dec_route<8>(p, ngroups, s);
+    // bf16 queries over more than 1024 chunks: the whole routing in one workgroup per
+    // group (at 96K with 48 groups the logits and per-head router take 15 + 48 µs, the
+    // group router 37); otherwise logits over many workgroups, then the per-head router
+    // (at 128K with 8 groups 6 + 11 µs, where eight group workgroups take longer)
+    hipError_t er;
+    if (a.in_bf16 && p.T_route > 1024) {
+        er = launch_dec_group<D>(p, a.Q, ngroups, s);
+    } else {
+        dim3 g1(max((p.T_route + 63) / 64, 1), p.h_kv, a.b);
+        hipLaunchKernelGGL((decode_scores_kernel<D>), g1, dim3(256), 0, s, p, a.Q, a.in_bf16);
+        er = p.T_route <= 256 ? launch_dec_route<1>(p, ngroups, s)
+           : p.T_route <= 512 ? launch_dec_route<2>(p, ngroups, s)
+           : p.T_route <= 1024 ? launch_dec_route<4>(p, ngroups, s)
+                               : launch_dec_route<8>(p, ngroups, s);
+    }
     if (er != hipSuccess) return er;
+
     hipLaunchKernelGGL(attn, dim3(p.streams), dim3(64), C::LDS, s, p, ngroups);
     hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(p.h_q, a.b, kCombParts), dim3(kCombThreads), 0, s, p);
     return hipGetLastError();
