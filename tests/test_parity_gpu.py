@@ -269,6 +269,28 @@ def test_decode_small_matches_oracle(case):
     assert torch.equal(g["O"], g2["O"])
 
 
+DEC_GROUP = [
+    # beyond 1024 chunks with bf16 queries the group router routes (one workgroup per
+    # group); dtype, b, h_q, h_kv, d, L, B, alpha, gamma, seq_len
+    ("bf16", 3, 32, 2, 64, 36000, 32, 1.75, 3.0, [36000, 33000, 40]),    # d = 64, p non-integer, a short row
+    ("bf16", 2, 16, 2, 128, 70000, 64, 1.25, 2.0, [70000, 65600]),       # g = 8, p = 4
+    ("bf16", 2, 32, 2, 128, 40000, 32, 2.0, 4.0, [40000, 1]),            # sparsemax; L = 1 routes nothing
+    ("bf16", 2, 32, 2, 128, 36000, 32, 1.0, 3.0, [36000, 35000]),        # softmax routing
+]
+
+
+@pytest.mark.parametrize("case", DEC_GROUP, ids=[f"g{c[2] // c[3]}-d{c[4]}-L{c[5]}-a{c[7]}" for c in DEC_GROUP])
+def test_decode_group_router_matches_oracle(case):
+    dtype, b, h_q, h_kv, d, L, B, alpha, gamma, seq_len = case
+    _log(f"decode group-router case {case}")
+    w = inputs.make_decode(b=b, h_q=h_q, h_kv=h_kv, d=d, L=L, B=B, alphas=(alpha,), gamma=gamma,
+                           dtype=dtype, seed=62, seq_len=seq_len)
+    assert (L - 1) // B > 1024
+    g = gpu_decode(w, seq_len)
+    nex, err = check_decode(w, np.asarray(seq_len), g)
+    _log(f"  exempt groups {nex}, output error {err:.3e}, counts {g['cnt'].cpu().numpy().ravel().tolist()}")
+
+
 DEC_TOPK = [
     # dtype, b, h_q, h_kv, d, L, B, alpha, gamma, seq_len, top_k
     ("bf16", 3, 32, 2, 128, 4096, 64, 1.0, 3.0, [4096, 3000, 700], 8),     # softmax routing: exactly 8
