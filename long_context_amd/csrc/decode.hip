@@ -32,7 +32,9 @@
 //                          (max, sum, output) per group it touches. HBM-bound.
 //   decode_combine_kernel  merges the partials of each (b, head) with the usual
 //                          max-rescaled sum and normalises; the partials of one head
-//                          are contiguous, so the merge reads them as one stream.
+//                          are contiguous, so the merge reads them as one stream (one
+//                          wavefront per (b, head, quarter of d) when there are many
+//                          groups, eight when a few groups own many partials each).
 #include "attn_common.h"
 #include "kernels.h"
 
@@ -44,7 +46,7 @@ constexpr int kDecUnit = 32;          // tokens per stream unit (one 32x32 S^T b
 constexpr int kDecSoftmax = -1;       // pmode of α = 1 (softmax routing)
 constexpr int kRouteThreads = 256;    // workgroup of the per-head router
 constexpr int kMaxStreams = 1024;     // upper bound of the attention wavefronts
-constexpr int kCombThreads = 512;
+constexpr int kCombThreads = 512;     // combine workgroup when groups are few
 // Attention wavefronts per compute unit: more streams add in-flight copies but also
 // partial results, which the next kernel must read back.
 constexpr int kDecStreamsPerCU = 2;
@@ -897,13 +899,11 @@ __global__ __launch_bounds__(64) void decode_attn_kernel(DecodeParams p, int ngr
 // each thread merges its slots with a running maximum (its loads of a batch issued
 // together), then the slot lanes are merged in LDS.
 constexpr int kCombParts = 4;
-template <int D>
-__global__ __launch_bounds__(kCombThreads) void decode_combine_kernel(DecodeParams p) {
+template <int D, int NT>
+__global__ __launch_bounds__(NT) void decode_combine_kernel(DecodeParams p) {
     constexpr int DQ = D / 4 / kCombParts;         // column quads of this workgroup
-    constexpr int SL = kCombThreads / DQ;          // slot lanes
+    constexpr int SL = NT / DQ;                    // slot lanes
     constexpr int NB = 8;                          // slots per thread and batch
-    __shared__ float s_m[SL][DQ], s_l[SL][DQ];
-    __shared__ f32x4 s_acc[SL][DQ];
     const int tid = threadIdx.x;
     const int hh = blockIdx.x, bi = blockIdx.y, part = blockIdx.z;
     const int g = p.g, r = hh / g, pr = hh % g;
@@ -941,36 +941,59 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine_kernel(DecodePara
         }
         m_t = mb;
     }
-    s_m[sl][dq] = m_t;
-    s_l[sl][dq] = l_t;
-    s_acc[sl][dq] = acc;
-    // merge the slot lanes pairwise (fixed tree order)
+    // merge the slot lanes pairwise in a fixed order: within the wavefront by a
+    // butterfly over the slot bits of the lane (both lanes of a pair combine the same
+    // operands in the same order), across wavefronts through LDS
 #pragma unroll
-    for (int half = SL / 2; half >= 1; half >>= 1) {
+    for (int o = DQ; o < 64 && o < NT; o <<= 1) {
+        const float mo = shfl_xor(m_t, o), lo = shfl_xor(l_t, o);
+        f32x4 ao;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ao[e] = shfl_xor(acc[e], o);
+        const bool lower = (tid & o) == 0;
+        const float ma = lower ? m_t : mo, mb2 = lower ? mo : m_t;
+        const float la = lower ? l_t : lo, lb = lower ? lo : l_t;
+        const f32x4 aa = lower ? acc : ao, ab = lower ? ao : acc;
+        const float M = fmaxf(ma, mb2);
+        const float fa = ma == -INFINITY ? 0.f : fast_exp2(ma - M);
+        const float fb = mb2 == -INFINITY ? 0.f : fast_exp2(mb2 - M);
+        m_t = M;
+        l_t = fa * la + fb * lb;
+        acc = fa * aa + fb * ab;
+    }
+    if constexpr (NT > 64) {
+        constexpr int NW = NT / 64;
+        __shared__ float s_m[NW][DQ], s_l[NW][DQ];
+        __shared__ f32x4 s_acc[NW][DQ];
+        const int wid = tid >> 6;
+        if ((tid & 63) < DQ) {
+            s_m[wid][dq] = m_t;
+            s_l[wid][dq] = l_t;
+            s_acc[wid][dq] = acc;
+        }
         __syncthreads();
-        if (sl < half) {
-            const float ma = s_m[sl][dq], mb = s_m[sl + half][dq];
-            const float M = fmaxf(ma, mb);
-            const float fa = ma == -INFINITY ? 0.f : fast_exp2(ma - M);
-            const float fb = mb == -INFINITY ? 0.f : fast_exp2(mb - M);
-            s_m[sl][dq] = M;
-            s_l[sl][dq] = fa * s_l[sl][dq] + fb * s_l[sl + half][dq];
-            s_acc[sl][dq] = fa * s_acc[sl][dq] + fb * s_acc[sl + half][dq];
+        if (tid < DQ) {
+            for (int w = 1; w < NW; ++w) {
+                const float mb2 = s_m[w][dq];
+                const float M = fmaxf(m_t, mb2);
+                const float fa = m_t == -INFINITY ? 0.f : fast_exp2(m_t - M);
+                const float fb = mb2 == -INFINITY ? 0.f : fast_exp2(mb2 - M);
+                m_t = M;
+                l_t = fa * l_t + fb * s_l[w][dq];
+                acc = fa * acc + fb * s_acc[w][dq];
+            }
         }
     }
-    __syncthreads();
     if (tid < DQ) {
-        const float L = s_l[0][tid];
-        const f32x4 o = s_acc[0][tid];
-        const float inv = 1.f / L;
+        const float inv = 1.f / l_t;
         const size_t oi = ((size_t)bi * p.h_q + hh) * D + part * (D / kCombParts) + 4 * tid;
         if (p.out_bf16) {
             u32x2 ob;
-            ob[0] = (uint32_t)f32_to_bf16_bits(o[0] * inv) | ((uint32_t)f32_to_bf16_bits(o[1] * inv) << 16);
-            ob[1] = (uint32_t)f32_to_bf16_bits(o[2] * inv) | ((uint32_t)f32_to_bf16_bits(o[3] * inv) << 16);
+            ob[0] = (uint32_t)f32_to_bf16_bits(acc[0] * inv) | ((uint32_t)f32_to_bf16_bits(acc[1] * inv) << 16);
+            ob[1] = (uint32_t)f32_to_bf16_bits(acc[2] * inv) | ((uint32_t)f32_to_bf16_bits(acc[3] * inv) << 16);
             *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.O) + oi) = ob;
         } else {
-            *reinterpret_cast<f32x4*>(static_cast<float*>(p.O) + oi) = o * inv;
+            *reinterpret_cast<f32x4*>(static_cast<float*>(p.O) + oi) = acc * inv;
         }
     }
 }
@@ -1078,7 +1101,12 @@ static hipError_t launch_decode_t(DecodeParams p, const DecodeArgs& a, hipStream
     if (er != hipSuccess) return er;
 
     hipLaunchKernelGGL(attn, dim3(p.streams), dim3(64), C::LDS, s, p, ngroups);
-    hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(p.h_q, a.b, kCombParts), dim3(kCombThreads), 0, s, p);
+    // few groups own many partials each (wide merge); many groups own few (one wavefront)
+    if (ngroups >= 16)
+        hipLaunchKernelGGL((decode_combine_kernel<D, 64>), dim3(p.h_q, a.b, kCombParts), dim3(64), 0, s, p);
+    else
+        hipLaunchKernelGGL((decode_combine_kernel<D, kCombThreads>), dim3(p.h_q, a.b, kCombParts),
+                           dim3(kCombThreads), 0, s, p);
     return hipGetLastError();
 }
 
