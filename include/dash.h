@@ -254,6 +254,25 @@ dash_status dash_attend_prefill_varlen(const void* Q, const void* K, const void*
                                        void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Stage 2 of a prefill over a paged KV cache (the layout of dash_attend_decode_paged:
+ * Kp, Vp [num_pages, h_kv, B, d], chunk c of sequence b in page
+ * pages[b * pages_per_seq + c], device int32 [b, pages_per_seq]); Q stays contiguous
+ * [b, h_q, n, d]. seq_len (nullable) gives a ragged batch as for
+ * dash_attend_prefill_varlen; otherwise every sequence holds n tokens. Requires
+ * pages_per_seq * B >= n and a cache of fewer than 2^31 rows. Page ids outside
+ * [0, num_pages) are clamped (wrong output, never a stray read). The summaries come
+ * from dash_summarize_paged, the lists from dash_route or dash_route_varlen. Output,
+ * lse (nullable) and workspace as dash_attend_prefill_lse; the result equals the
+ * contiguous entry point's on the same tokens.
+ */
+dash_status dash_attend_prefill_paged(const void* Q, const void* Kp, const void* Vp, int in_dtype,
+                                      const int32_t* pages, int pages_per_seq, int num_pages,
+                                      const int32_t* seq_len, const int32_t* idx, const float* bias,
+                                      const int32_t* cnt, int list_cap, void* O, int out_dtype, float* lse,
+                                      int b, int h_q, int h_kv, int n, int d, int B, int causal,
+                                      void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Stage-2 backward (the support and the per-chunk bias of Prop. 4.1 held fixed: the
  * gradient of a softmax attention with an additive bias). Inputs: the forward's
  * Q, K, V (in_dtype, bf16 only), idx/bias/cnt (same list_cap), its output O and the

@@ -21,7 +21,7 @@ namespace dash {
 
 constexpr int kWaves = 8;                 // wavefronts per workgroup (256 pairs)
 
-template <typename T, int D, int TT>
+template <typename T, int D, int TT, bool PAGED>
 __global__ __launch_bounds__(64 * kWaves) void sparse_prior_attn_kernel(PrefillParams p) {
     typedef SwzTile<T, D, TT> S;
     typedef Mfma<T> MM;
@@ -46,8 +46,11 @@ __global__ __launch_bounds__(64 * kWaves) void sparse_prior_attn_kernel(PrefillP
     const int nvis = p.causal ? min(cq, Tb) : Tb;
     const int last_row = min(row0 + R_t, nb) - 1;
     const size_t bhkv = (size_t)bi * p.h_kv + r;
-    const T* Kg = static_cast<const T*>(p.K) + bhkv * (size_t)p.n * D;
-    const T* Vg = static_cast<const T*>(p.V) + bhkv * (size_t)p.n * D;
+    // K and V rows: the sequence's own rows, or (paged) the whole cache with per-chunk
+    // row offsets
+    const T* Kg = static_cast<const T*>(p.K) + (PAGED ? 0 : bhkv * (size_t)p.n * D);
+    const T* Vg = static_cast<const T*>(p.V) + (PAGED ? 0 : bhkv * (size_t)p.n * D);
+    auto krow0 = [&](int t) { return PAGED ? paged_row0(p, bi, r, t) : 0; };
     const int U = tabs.build(p, bhkv, row0, nvis, tid, nthr, nb);
     const int* ulist = tabs.ulist;
 
@@ -89,7 +92,11 @@ __global__ __launch_bounds__(64 * kWaves) void sparse_prior_attn_kernel(PrefillP
     st.at(ulist, 0, tb_cur, c_cur);
     st.at(ulist, 1, tb_nxt, c_nxt);
 
-    if (nsteps > 0) copier.issue(ring, Kg, Vg, tb_cur, nmax, wid);
+    int ko_nxt = krow0(tb_nxt);
+    if (nsteps > 0) {
+        const int ko = krow0(tb_cur);
+        copier.issue(ring, Kg, Vg, ko + tb_cur, ko + nmax, wid);
+    }
     wait_tile_copies();
     __syncthreads();
     for (int k = 0; k < nsteps; ++k) {
@@ -102,7 +109,7 @@ __global__ __launch_bounds__(64 * kWaves) void sparse_prior_attn_kernel(PrefillP
             bias2 = lc.take(c_cur, k % SPC == SPC - 1);
             run = ballot(bias2 > -INFINITY) != 0;          // some row of this wave routes c
         }
-        if (k + 1 < nsteps) copier.issue(ring + ((k + 1) & 1) * S::STAGE, Kg, Vg, tb_nxt, nmax, wid);
+        if (k + 1 < nsteps) copier.issue(ring + ((k + 1) & 1) * S::STAGE, Kg, Vg, ko_nxt + tb_nxt, ko_nxt + nmax, wid);
         int tb_nn, c_nn;
         st.at(ulist, k + 2, tb_nn, c_nn);
         const char* ktile = ring + (k & 1) * S::STAGE;
@@ -193,6 +200,7 @@ __global__ __launch_bounds__(64 * kWaves) void sparse_prior_attn_kernel(PrefillP
         __syncthreads();
         tb_cur = tb_nxt; c_cur = c_nxt;
         tb_nxt = tb_nn; c_nxt = c_nn;
+        ko_nxt = krow0(tb_nxt);
     }
 
     const float l_tot = pair32_sum(l_run);
@@ -250,15 +258,31 @@ void prefill_tiling(int g, int B, int T_c, int d, bool bf16, int* rows, size_t* 
     }
 }
 
-template <int D, int TT>
-static hipError_t launch_prefill_t(const PrefillParams& p, int b, size_t lds, hipStream_t s) {
+// Both K/V layouts of every (d, tile) pair are instantiated explicitly: when one
+// dispatcher names the two, hipcc emits the host handle of only the first.
+#define DASH_PREFILL_F32_INST(D, TT)                                                   \
+    template __global__ void sparse_prior_attn_kernel<float, D, TT, false>(PrefillParams); \
+    template __global__ void sparse_prior_attn_kernel<float, D, TT, true>(PrefillParams);
+DASH_PREFILL_F32_INST(64, 32)
+DASH_PREFILL_F32_INST(64, 64)
+DASH_PREFILL_F32_INST(128, 32)
+DASH_PREFILL_F32_INST(128, 64)
+#undef DASH_PREFILL_F32_INST
+
+template <int D, int TT, bool PAGED>
+static hipError_t launch_prefill_paged(const PrefillParams& p, int b, size_t lds, hipStream_t s) {
     static hipError_t configured = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&sparse_prior_attn_kernel<float, D, TT>),
+        reinterpret_cast<const void*>(&sparse_prior_attn_kernel<float, D, TT, PAGED>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
     if (configured != hipSuccess) return configured;
     dim3 grid((p.n + p.R_t - 1) / p.R_t, p.h_kv, b), block(64 * kWaves);
-    hipLaunchKernelGGL((sparse_prior_attn_kernel<float, D, TT>), grid, block, lds, s, p);
+    hipLaunchKernelGGL((sparse_prior_attn_kernel<float, D, TT, PAGED>), grid, block, lds, s, p);
     return hipGetLastError();
+}
+
+template <int D, int TT>
+static hipError_t launch_prefill_t(const PrefillParams& p, int b, size_t lds, hipStream_t s) {
+    return p.pages ? launch_prefill_paged<D, TT, true>(p, b, lds, s) : launch_prefill_paged<D, TT, false>(p, b, lds, s);
 }
 
 hipError_t launch_prefill_f32(const PrefillParams& p, int b, int d, size_t lds, hipStream_t s) {
@@ -280,6 +304,7 @@ hipError_t launch_attend_prefill(const PrefillArgs& a, hipStream_t s) {
     while ((1 << p.log2g) < p.g) ++p.log2g;
     p.scale_log2 = (float)(1.4426950408889634 / sqrt((double)a.d));
     p.seq_len = a.seq_len;
+    p.pages = a.pages; p.pages_per_seq = a.pages_per_seq; p.num_pages = a.num_pages;
     size_t lds = 0;
     prefill_tiling(p.g, a.B, p.T_c, a.d, a.in_bf16, &p.R_t, &lds);
     if (p.R_t == 0) return hipErrorInvalidValue;

@@ -53,16 +53,17 @@ struct BfCopier {
             }
         }
     }
-    // K rows min(tb + t, nmax); V^T columns tb .. tb+TT-1 (inside n_pad). Tile bases
-    // are multiples of TT below n_pad by construction; the clamp keeps every source
-    // address inside the tensors even if a table were corrupted.
-    __device__ __forceinline__ void issue(char* stage, const uint16_t* Kg, const uint16_t* Vtg, int tb,
+    // K rows ko + min(tb + t, nmax) (ko: 0, or the paged cache's row offset of the tile's
+    // chunk); V^T columns tb .. tb+TT-1 (inside n_pad). Tile bases are multiples of TT
+    // below n_pad by construction; the clamp keeps every source address inside the
+    // tensors even if a table were corrupted.
+    __device__ __forceinline__ void issue(char* stage, const uint16_t* Kg, int ko, const uint16_t* Vtg, int tb,
                                           int nmax, int n_pad, int wid) const {
         tb = min(max(tb, 0), n_pad - TT);
 #pragma unroll
         for (int i = 0; i < CPW; ++i) {
             const bool isk = wid + i * NW < S::KINSTS;     // wavefront-uniform
-            const uint16_t* src = isk ? Kg + (size_t)min(tb + row[i], nmax) * D + off[i]
+            const uint16_t* src = isk ? Kg + (size_t)(ko + min(tb + row[i], nmax)) * D + off[i]
                                       : Vtg + (size_t)row[i] * n_pad + tb + off[i];
             __builtin_amdgcn_global_load_lds(src, stage + dst[i], 16, 0, 0);
         }
@@ -71,20 +72,31 @@ struct BfCopier {
 
 // V [b, h_kv, n, D] -> Vt [b, h_kv, D, n_pad], tokens n .. n_pad-1 zero (in a ragged
 // batch, tokens from seq_len[b] on: padding rows may hold anything).
+// A paged V (pages != nullptr) is [num_pages, h_kv, B, D] with chunk c of sequence b in
+// page pages[b * pages_per_seq + c].
 template <int D>
 __global__ __launch_bounds__(256) void transpose_v_kernel(const uint16_t* V, uint16_t* Vt, int n, int n_pad,
-                                                          const int32_t* seq_len = nullptr, int h_kv = 1) {
+                                                          const int32_t* seq_len = nullptr, int h_kv = 1,
+                                                          const int32_t* pages = nullptr, int pages_per_seq = 0,
+                                                          int num_pages = 0, int B = 1) {
     __shared__ __attribute__((aligned(16))) uint16_t tile[64][D + 8];
     const int t0 = blockIdx.x * 64;
     const size_t bh = blockIdx.y;
     const int nv = seq_len ? min(max(seq_len[bh / h_kv], 0), n) : n;   // tokens copied
-    const uint16_t* src = V + bh * (size_t)n * D;
     uint16_t* dst = Vt + bh * (size_t)D * n_pad;
+    // V row of token t
+    auto vrow = [&](int t) -> const uint16_t* {
+        if (pages) {
+            const int pg = min(max(pages[(bh / h_kv) * pages_per_seq + t / B], 0), num_pages - 1);
+            return V + (((size_t)pg * h_kv + bh % h_kv) * B + t % B) * D;
+        }
+        return V + (bh * (size_t)n + t) * D;
+    };
     constexpr int PR = D / 8;                          // 16-byte pieces per V row
     for (int q = threadIdx.x; q < 64 * PR; q += 256) {
         const int t = q / PR, c = q % PR;
         u32x4 v = {0u, 0u, 0u, 0u};
-        if (t0 + t < nv) v = *reinterpret_cast<const u32x4*>(src + (size_t)(t0 + t) * D + 8 * c);
+        if (t0 + t < nv) v = *reinterpret_cast<const u32x4*>(vrow(t0 + t) + 8 * c);
         *reinterpret_cast<u32x4*>(&tile[t][8 * c]) = v;
     }
     __syncthreads();
@@ -99,8 +111,9 @@ __global__ __launch_bounds__(256) void transpose_v_kernel(const uint16_t* V, uin
 }
 
 
-// NW wavefronts of PBW pair blocks (32 (row, head) pairs each).
-template <int D, int TT, int NW, int PBW>
+// NW wavefronts of PBW pair blocks (32 (row, head) pairs each); PAGED: K read through
+// the page table.
+template <int D, int TT, int NW, int PBW, bool PAGED>
 __global__ __launch_bounds__(64 * NW) void sparse_prior_attn_bf16_kernel(PrefillParams p) {
     typedef BfTiles<D, TT> S;
     constexpr int NS = D / 16;     // k16 steps of S^T
@@ -127,7 +140,9 @@ __global__ __launch_bounds__(64 * NW) void sparse_prior_attn_bf16_kernel(Prefill
     const int nvis = p.causal ? min(cq, Tb) : Tb;
     const int last_row = min(row0 + R_t, nb) - 1;
     const size_t bhkv = (size_t)bi * p.h_kv + r;
-    const uint16_t* Kg = static_cast<const uint16_t*>(p.K) + bhkv * (size_t)p.n * D;
+    // K rows: the sequence's own rows, or (paged) the whole cache with per-chunk offsets
+    const uint16_t* Kg = static_cast<const uint16_t*>(p.K) + (PAGED ? 0 : bhkv * (size_t)p.n * D);
+    auto krow0 = [&](int t) { return PAGED ? paged_row0(p, bi, r, t) : 0; };
     const uint16_t* Vtg = p.Vt + bhkv * (size_t)D * p.n_pad;
     const int U = tabs.build(p, bhkv, row0, nvis, tid, nthr, nb);
 
@@ -272,7 +287,8 @@ __global__ __launch_bounds__(64 * NW) void sparse_prior_attn_bf16_kernel(Prefill
     int tb_cur, c_cur, tb_nxt, c_nxt;
     st.at(tabs.ulist, 0, tb_cur, c_cur);
     st.at(tabs.ulist, 1, tb_nxt, c_nxt);
-    if (st.nsteps > 0) cp.issue(ring, Kg, Vtg, tb_cur, nmax, p.n_pad, wid);
+    int ko_nxt = krow0(tb_nxt);
+    if (st.nsteps > 0) cp.issue(ring, Kg, krow0(tb_cur), Vtg, tb_cur, nmax, p.n_pad, wid);
     wait_tile_copies();
     __syncthreads();
     for (int k = 0; k < st.nsteps; ++k) {
@@ -286,9 +302,10 @@ __global__ __launch_bounds__(64 * NW) void sparse_prior_attn_bf16_kernel(Prefill
             bias2[pb] = routed ? lc[pb].take(c_cur, k % st.SPC == st.SPC - 1) : 0.f;
             run[pb] = live[pb] && (!routed || ballot(bias2[pb] > -INFINITY) != 0);
         }
-        if (k + 1 < st.nsteps) cp.issue(ring + ((k + 1) & 1) * S::STAGE, Kg, Vtg, tb_nxt, nmax, p.n_pad, wid);
+        if (k + 1 < st.nsteps) cp.issue(ring + ((k + 1) & 1) * S::STAGE, Kg, ko_nxt, Vtg, tb_nxt, nmax, p.n_pad, wid);
         int tb_nn, c_nn;
         st.at(tabs.ulist, k + 2, tb_nn, c_nn);
+        const int ko_nn = krow0(tb_nn);      // (paged) a page-table load with two tiles to arrive
         const char* kt = ring + (k & 1) * S::STAGE;
         const char* vt = kt + S::KBYTES;
         const int tb = tb_cur;
@@ -312,6 +329,7 @@ __global__ __launch_bounds__(64 * NW) void sparse_prior_attn_bf16_kernel(Prefill
         __syncthreads();
         tb_cur = tb_nxt; c_cur = c_nxt;
         tb_nxt = tb_nn; c_nxt = c_nn;
+        ko_nxt = ko_nn;
     }
 
 #pragma unroll
@@ -373,18 +391,34 @@ PrefillGeom prefill_geom_bf16(int d, int B) {
     return PrefillGeom{bf16_tile_tokens(d, B), kWavesB, 32 * kWavesB * kPairBlocks, 2};
 }
 
-template <int D, int TT>
-static hipError_t launch_bf16_t(const PrefillParams& p, int b, size_t lds, hipStream_t s) {
-    auto kern = sparse_prior_attn_bf16_kernel<D, TT, kWavesB, kPairBlocks>;
+// Both K/V layouts of every (d, tile) pair are instantiated explicitly: when one
+// dispatcher names the two, hipcc emits the host handle of only the first.
+#define DASH_PREFILL_BF16_INST(D, TT)                                                                   \
+    template __global__ void sparse_prior_attn_bf16_kernel<D, TT, kWavesB, kPairBlocks, false>(PrefillParams); \
+    template __global__ void sparse_prior_attn_bf16_kernel<D, TT, kWavesB, kPairBlocks, true>(PrefillParams);
+DASH_PREFILL_BF16_INST(64, 32)
+DASH_PREFILL_BF16_INST(64, 64)
+DASH_PREFILL_BF16_INST(128, 32)
+DASH_PREFILL_BF16_INST(128, 64)
+#undef DASH_PREFILL_BF16_INST
+
+template <int D, int TT, bool PAGED>
+static hipError_t launch_bf16_paged(const PrefillParams& p, int b, size_t lds, hipStream_t s) {
+    auto kern = sparse_prior_attn_bf16_kernel<D, TT, kWavesB, kPairBlocks, PAGED>;
     static hipError_t configured = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (configured != hipSuccess) return configured;
     hipLaunchKernelGGL((transpose_v_kernel<D>), dim3(p.n_pad / 64, b * p.h_kv), dim3(256), 0, s,
                        static_cast<const uint16_t*>(p.V), const_cast<uint16_t*>(p.Vt), p.n, p.n_pad, p.seq_len,
-                       p.h_kv);
+                       p.h_kv, p.pages, p.pages_per_seq, p.num_pages, p.B);
     dim3 grid((p.n + p.R_t - 1) / p.R_t, p.h_kv, b), block(64 * kWavesB);
     hipLaunchKernelGGL(kern, grid, block, lds, s, p);
     return hipGetLastError();
+}
+
+template <int D, int TT>
+static hipError_t launch_bf16_t(const PrefillParams& p, int b, size_t lds, hipStream_t s) {
+    return p.pages ? launch_bf16_paged<D, TT, true>(p, b, lds, s) : launch_bf16_paged<D, TT, false>(p, b, lds, s);
 }
 
 hipError_t launch_prefill_bf16(const PrefillParams& p, int b, int d, size_t lds, hipStream_t s) {

@@ -307,7 +307,8 @@ static dash_status attend_prefill(const void* Q, const void* K, const void* V, i
                                   const int32_t* idx, const float* bias, const int32_t* cnt,
                                   int list_cap, void* O, int out_dtype, float* lse,
                                   int b, int h_q, int h_kv, int n, int d, int B, int causal,
-                                  void* ws, size_t ws_bytes, void* stream, const int32_t* seq_len) {
+                                  void* ws, size_t ws_bytes, void* stream, const int32_t* seq_len,
+                                  const int32_t* pages = nullptr, int pages_per_seq = 0, int num_pages = 0) {
     if (!Q || !K || !V || !idx || !bias || !cnt || !O) return fail(DASH_ERR_NULL, "Q, K, V, idx, bias, cnt and O must be non-null");
     if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return fail(DASH_ERR_PARAM, "bad dtype");
     if (causal != 0 && causal != 1) return fail(DASH_ERR_PARAM, "causal must be 0 or 1");
@@ -328,6 +329,7 @@ static dash_status attend_prefill(const void* Q, const void* K, const void* V, i
     }
     dash::PrefillArgs a{Q, K, V, in_dtype == DASH_BF16, idx, bias, cnt, list_cap, O, out_dtype == DASH_BF16,
                         b, h_q, h_kv, n, d, B, causal, ws, lse, seq_len};
+    a.pages = pages; a.pages_per_seq = pages_per_seq; a.num_pages = num_pages;
     return from_hip(dash::launch_attend_prefill(a, (hipStream_t)stream), "sparse_prior_attn_kernel");
 }
 
@@ -338,6 +340,23 @@ dash_status dash_attend_prefill_lse(const void* Q, const void* K, const void* V,
                                     void* ws, size_t ws_bytes, void* stream) {
     return attend_prefill(Q, K, V, in_dtype, idx, bias, cnt, list_cap, O, out_dtype, lse, b, h_q, h_kv, n, d, B,
                           causal, ws, ws_bytes, stream, nullptr);
+}
+
+dash_status dash_attend_prefill_paged(const void* Q, const void* Kp, const void* Vp, int in_dtype,
+                                      const int32_t* pages, int pages_per_seq, int num_pages,
+                                      const int32_t* seq_len, const int32_t* idx, const float* bias,
+                                      const int32_t* cnt, int list_cap, void* O, int out_dtype, float* lse,
+                                      int b, int h_q, int h_kv, int n, int d, int B, int causal,
+                                      void* ws, size_t ws_bytes, void* stream) {
+    if (!pages) return fail(DASH_ERR_NULL, "pages must be non-null");
+    if (pages_per_seq < 1 || num_pages < 1)
+        return fail(DASH_ERR_SHAPE, "pages_per_seq and num_pages must be >= 1");
+    if (n > 0 && (long long)pages_per_seq * B < n)
+        return fail(DASH_ERR_SHAPE, "pages_per_seq * B = %lld < n = %d", (long long)pages_per_seq * B, n);
+    if ((long long)num_pages * h_kv * B > 0x7fffffffLL)
+        return fail(DASH_ERR_UNSUPPORTED, "the cache holds more than 2^31 rows");
+    return attend_prefill(Q, Kp, Vp, in_dtype, idx, bias, cnt, list_cap, O, out_dtype, lse, b, h_q, h_kv, n, d, B,
+                          causal, ws, ws_bytes, stream, seq_len, pages, pages_per_seq, num_pages);
 }
 
 dash_status dash_attend_prefill_varlen(const void* Q, const void* K, const void* V, int in_dtype,

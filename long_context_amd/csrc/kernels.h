@@ -63,6 +63,10 @@ struct PrefillArgs {
     float* lse = nullptr;  // optional [b, h_q, n] log-sum-exp of each row's logits
     const int32_t* seq_len = nullptr;  // ragged batch (nullable): sequence b holds
                                        // seq_len[b] tokens; later rows are not written
+    // paged K/V (nullable): K and V are [num_pages, h_kv, B, d], chunk c of sequence b
+    // in page pages[b * pages_per_seq + c]
+    const int32_t* pages = nullptr;
+    int pages_per_seq = 0, num_pages = 0;
 };
 hipError_t launch_attend_prefill(const PrefillArgs& a, hipStream_t s);
 

@@ -27,7 +27,20 @@ struct PrefillParams {
     int out_bf16, h_q, h_kv, n, n_pad, B, T_c, list_cap, causal, g, log2g, R_t, nw;
     float scale_log2;    // log2(e)/sqrt(d)
     const int32_t* seq_len = nullptr;  // ragged batch (nullable): tokens of each sequence
+    // paged K/V (nullable): K and V are [num_pages, h_kv, B, D] and chunk c of sequence b
+    // lives in page pages[b * pages_per_seq + c]
+    const int32_t* pages = nullptr;
+    int pages_per_seq = 0, num_pages = 0;
 };
+
+// Paged K/V: the row of token t of sequence bi, KV head r, is paged_row0(p, bi, r, t) + t
+// in the cache viewed as [num_pages * h_kv * B, D] (page ids outside the cache are
+// clamped: a bad table gives wrong output, never a stray read).
+__device__ __forceinline__ int paged_row0(const PrefillParams& p, int bi, int r, int t) {
+    const int c = t / p.B;
+    const int pg = min(max(p.pages[(size_t)bi * p.pages_per_seq + c], 0), p.num_pages - 1);
+    return (pg * p.h_kv + r) * p.B - c * p.B;
+}
 
 // Tokens of sequence bi: seq_len[bi] clamped to [0, n] in a ragged batch, else n.
 __device__ __forceinline__ int seq_tokens(const PrefillParams& p, int bi) {

@@ -61,6 +61,9 @@ def _load():
     lib.dash_attend_prefill_varlen.argtypes = [vp, vp, vp, i32, vp, vp, vp, vp, i32, vp, i32, vp,
                                                i32, i32, i32, i32, i32, i32, i32, vp, sz, vp]
     lib.dash_attend_prefill_varlen.restype = i32
+    lib.dash_attend_prefill_paged.argtypes = [vp, vp, vp, i32, vp, i32, i32, vp, vp, vp, vp, i32, vp, i32, vp,
+                                              i32, i32, i32, i32, i32, i32, i32, vp, sz, vp]
+    lib.dash_attend_prefill_paged.restype = i32
     lib.dash_attend_prefill_backward.argtypes = [vp, vp, vp, i32, vp, vp, vp, i32, vp, vp, i32, vp,
                                                  vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                                  vp, sz, vp]
@@ -93,6 +96,7 @@ lib = _load()
 SYMBOLS = ("dash_summarize", "dash_summarize_varlen", "dash_summarize_paged", "dash_summarize_backward",
            "dash_route", "dash_route_topk", "dash_route_varlen", "dash_route_stats", "dash_route_backward",
            "dash_route_mask", "dash_attend_prefill", "dash_attend_prefill_lse", "dash_attend_prefill_varlen",
+           "dash_attend_prefill_paged",
            "dash_attend_prefill_backward",
            "dash_attend_decode", "dash_attend_decode_topk", "dash_attend_decode_noalloc", "dash_attend_decode_paged",
            "dash_workspace_bytes", "dash_status_string", "dash_last_error")
@@ -269,6 +273,22 @@ def dash_attend_prefill_varlen(Q, K, V, seq_len, idx, bias, cnt, O, B, causal, l
                                           b, h_q, h_kv, n, d, B, int(causal), _ptr(ws),
                                           0 if ws is None else ws.numel() * ws.element_size(),
                                           _stream(stream)))
+
+
+def dash_attend_prefill_paged(Q, Kp, Vp, pages, idx, bias, cnt, O, B, causal, n=None, seq_len=None, lse=None,
+                              ws=None, stream=None):
+    """Stage 2 of a prefill over a paged cache Kp, Vp [num_pages, h_kv, B, d]; pages
+    [b, pages_per_seq] int32; seq_len (optional) for a ragged batch."""
+    b, h_q, nq, d = Q.shape
+    n = nq if n is None else n
+    h_kv = Kp.shape[1]
+    if ws is None and Q.dtype == torch.bfloat16:
+        ws = alloc_prefill_ws(b, h_q, h_kv, n, d, B, device=Q.device)
+    _check(lib.dash_attend_prefill_paged(_ptr(Q), _ptr(Kp), _ptr(Vp), _dtype(Q), _ptr(pages), pages.shape[1],
+                                         Kp.shape[0], _ptr(seq_len), _ptr(idx), _ptr(bias), _ptr(cnt),
+                                         idx.shape[-1], _ptr(O), _dtype(O), _ptr(lse), b, h_q, h_kv, n, d, B,
+                                         int(causal), _ptr(ws),
+                                         0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def dash_attend_prefill_backward(Q, K, V, idx, bias, cnt, O, dO, lse, dQ, dK, dV, dbias, B, causal,

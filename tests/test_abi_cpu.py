@@ -353,3 +353,18 @@ def test_varlen_entry_points_validation(dash):
     bad = list(args)
     bad[17] = 48
     assert p(*bad, NUL, 0, NUL) == dash.DASH_ERR_UNSUPPORTED        # B % 32 != 0
+
+
+def test_paged_prefill_validation(dash):
+    p = dash.lib.dash_attend_prefill_paged
+    args = [P, P, P, 1, P, 16, 40, NUL, P, P, P, 16, P, 0, NUL, 1, 4, 2, 1024, 128, 64, 1]
+    assert p(*args, NUL, 0, NUL) == dash.DASH_ERR_WORKSPACE          # valid up to the workspace
+    bad = list(args)
+    bad[4] = NUL
+    assert p(*bad, NUL, 0, NUL) == dash.DASH_ERR_NULL               # no page table
+    bad = list(args)
+    bad[5] = 15
+    assert p(*bad, NUL, 0, NUL) == dash.DASH_ERR_SHAPE              # 15 pages of 64 < 1024 tokens
+    bad = list(args)
+    bad[6] = 0
+    assert p(*bad, NUL, 0, NUL) == dash.DASH_ERR_SHAPE

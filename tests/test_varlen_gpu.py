@@ -147,3 +147,81 @@ def test_varlen_full_lengths_equal_the_dense_entry_points():
         listed = torch.arange(a["idx"].shape[-1], device="cuda") < a["cnt"][..., None]
         assert torch.equal(a["idx"][listed], v["idx"][listed])
         assert torch.equal(a["bias"][listed], v["bias"][listed])
+
+
+# ------------------------------------------------------------------------------------
+# Paged K/V in prefill (the serving layout of dash_attend_decode_paged)
+# ------------------------------------------------------------------------------------
+
+def _pages_of(X, B, perm, fill=float("nan")):
+    """[b, h_kv, n, d] -> [P, h_kv, B, d] with chunk c of sequence b in page
+    perm[b * pps + c] (pps = ceil(n / B)); rows past n and unused pages hold NaN."""
+    b, h_kv, n, d = X.shape
+    pps = (n + B - 1) // B
+    Xp = torch.full((b, h_kv, pps * B, d), fill, device=X.device).to(X.dtype)
+    Xp[:, :, :n] = X
+    P = int(perm.max()) + 1 + 2
+    pages = torch.full((P, h_kv, B, d), fill, device=X.device).to(X.dtype)
+    src = Xp.reshape(b, h_kv, pps, B, d).permute(0, 2, 1, 3, 4).reshape(b * pps, h_kv, B, d)
+    pages[torch.from_numpy(perm).to(X.device).long()] = src
+    return pages
+
+
+PAGED = [
+    # dtype, b, h_q, h_kv, d, n, B, causal, lengths (None: all n)
+    ("bf16", 2, 16, 2, 128, 1000, 64, True, None),
+    ("bf16", 2, 8, 2, 128, 520, 64, False, None),
+    ("bf16", 3, 16, 2, 128, 900, 128, True, [900, 517, 33]),
+    ("f32", 2, 2, 1, 64, 700, 32, True, [700, 301]),
+    ("bf16", 1, 32, 2, 128, 4096, 32, True, None),
+]
+
+
+@pytest.mark.parametrize("case", PAGED, ids=[f"{c[0]}-g{c[2] // c[3]}-n{c[5]}-B{c[6]}-c{int(c[7])}-{'ragged' if c[8] else 'full'}"
+                                             for c in PAGED])
+def test_paged_prefill_equals_contiguous(case):
+    """Stage 2 reading K and V through a page table (pages in random order, NaN in
+    every row outside the sequences) gives the contiguous entry points' O and lse bit
+    for bit; the summaries of dash_summarize_paged equal dash_summarize's."""
+    from long_context_amd import dash
+    G = _gu()
+    dtype, b, h_q, h_kv, d, n, B, causal, lengths = case
+    print(f"paged prefill case {case}", flush=True)
+    w = inputs.make_prefill(b=b, h_q=h_q, h_kv=h_kv, d=d, n=n, B=B, alphas=(1.5,), gamma=6.0,
+                            causal=causal, dtype=dtype, seed=31)
+    Q, K, V = G.to_dev(w.Q, dtype), G.to_dev(w.K, dtype), G.to_dev(w.V, dtype)
+    T = n // B
+    pps = (n + B - 1) // B
+    perm = np.random.default_rng(5).permutation(b * pps + 3)[:b * pps].astype(np.int32)
+    Kp, Vp = _pages_of(K, B, perm), _pages_of(V, B, perm)
+    pages = torch.from_numpy(perm.reshape(b, pps)).cuda()
+    qbar = torch.from_numpy(w.qbar).cuda()
+    kbar = dash.alloc_kbar(b, h_kv, T, d)
+    dash.dash_summarize(K, qbar, kbar, B)
+    if T > 0:
+        kbp = torch.full_like(kbar, float("nan"))
+        dash.dash_summarize_paged(Kp, qbar, kbp, pages, B, 0, T)
+        assert torch.equal(kbp, kbar)
+    idx, bias, cnt, _ = dash.alloc_route(b, h_kv, n, T)
+    sl = None if lengths is None else torch.tensor(lengths, dtype=torch.int32, device="cuda")
+    if sl is None:
+        dash.dash_route(Q, kbar, B, w.alpha, w.gamma, w.sigma, causal, idx, bias, cnt)
+    else:
+        dash.dash_route_varlen(Q, kbar, sl, B, w.alpha, w.gamma, w.sigma, causal, idx, bias, cnt)
+    O1 = torch.full((b, h_q, n, d), float("nan"), device="cuda")
+    O2 = torch.full_like(O1, float("nan"))
+    l1 = torch.full((b, h_q, n), float("nan"), device="cuda")
+    l2 = torch.full_like(l1, float("nan"))
+    if sl is None:
+        dash.dash_attend_prefill_lse(Q, K, V, idx, bias, cnt, O1, l1, B, causal)
+    else:
+        dash.dash_attend_prefill_varlen(Q, K, V, sl, idx, bias, cnt, O1, B, causal, lse=l1)
+    dash.dash_attend_prefill_paged(Q, Kp, Vp, pages, idx, bias, cnt, O2, B, causal, seq_len=sl, lse=l2)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.nan_to_num(O1, nan=7.0), torch.nan_to_num(O2, nan=7.0))
+    assert torch.equal(torch.nan_to_num(l1, nan=7.0), torch.nan_to_num(l2, nan=7.0))
+    valid = torch.ones((b, n), dtype=torch.bool, device="cuda")
+    if lengths is not None:
+        for bi, L in enumerate(lengths):
+            valid[bi, L:] = False
+    assert torch.isfinite(O2.permute(0, 2, 1, 3)[valid]).all()
