@@ -2,12 +2,13 @@
 // is local attention of the learned query q̄ over the chunk's keys, with the keys
 // also used as the values:  k̄_c = sum_t softmax_t(<q̄, k_t>/sqrt(d)) k_t.
 //
-// chunk_summary_kernel: one wavefront per (b, r, c). Each lane reads 16 bytes of a
-// key row per row group (a wave reads 1 KiB contiguous, 16 row groups in flight), the
-// rows' dot products with q̄ are reduced across the lanes that share a row (DPP), and
-// a softmax in the log2 domain (fp32) accumulates the weighted keys, one batch of 16
-// row groups at a time. The row groups are merged at the end and the fp32 summary is
-// written once. HBM-bound: the K chunk is read exactly once.
+// chunk_summary_kernel: one workgroup of four wavefronts per (b, r, c); batches of 16
+// key rows go round-robin to the wavefronts. Each lane reads 16 bytes of a key row
+// (a wavefront reads 1 KiB contiguous per load, a whole batch in flight), the rows'
+// dot products with q̄ are reduced across the lanes that share a row (DPP), and a
+// softmax in the log2 domain (fp32) accumulates the weighted keys. The row groups of
+// a wavefront, then the four wavefronts (through LDS, in a fixed order), are merged
+// and the fp32 summary is written once. HBM-bound: the K chunk is read exactly once.
 #include "common.h"
 #include "kernels.h"
 
@@ -48,8 +49,10 @@ __device__ __forceinline__ float lane_group_sum(float v) {
     return v;
 }
 
+constexpr int kSumWaves = 4;            // wavefronts per chunk
+
 template <typename T, int D>
-__global__ __launch_bounds__(256) void chunk_summary_kernel(
+__global__ __launch_bounds__(64 * kSumWaves) void chunk_summary_kernel(
     const T* __restrict__ K, const float* __restrict__ qbar, float* __restrict__ kbar,
     int h_kv, int n_kv, int kbar_cap, int B, int chunk_begin, int nsel, int total,
     float scale, const int32_t* __restrict__ pages, int pages_per_seq, int num_pages,
@@ -57,13 +60,17 @@ __global__ __launch_bounds__(256) void chunk_summary_kernel(
     constexpr int VEC = Vec16<T>::N;
     constexpr int LPR = D / VEC;        // lanes sharing one key row
     constexpr int RPI = 64 / LPR;       // key rows per wave iteration
-    const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (wave >= total) return;
-    const int lane = threadIdx.x & 63;
-    const int c = chunk_begin + wave % nsel;
-    const int br = wave / nsel;         // b * h_kv + r
+    constexpr int UNR = 16 / RPI;       // row groups per batch: 16 rows
+    constexpr int ROWS = RPI * UNR;
+    __shared__ float s_m[kSumWaves], s_l[kSumWaves], s_acc[kSumWaves][D];
+    const int item = blockIdx.x;        // one chunk per workgroup
+    if (item >= total) return;
+    const int ws = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int c = chunk_begin + item % nsel;
+    const int br = item / nsel;         // b * h_kv + r
     const int r = br % h_kv;
     // ragged batch: only the complete chunks of the sequence's own tokens
+    // (workgroup-uniform, before the barrier)
     if (seq_len && c >= min(max(seq_len[br / h_kv], 0), n_kv) / B) return;
     const int rr = lane / LPR;
     const int col = (lane % LPR) * VEC;
@@ -85,16 +92,18 @@ __global__ __launch_bounds__(256) void chunk_summary_kernel(
 #pragma unroll
     for (int v = 0; v < VEC; ++v) acc[v] = 0.f;
 
-    // the rows of a batch (UNR row groups) are loaded before any is used, so a lane has
-    // UNR 16-byte reads in flight; their UNR logits are independent (row sums by DPP
-    // within the lanes of a row), and the batch enters the running softmax once
-    constexpr int UNR = 16;
-    for (int b0 = 0; b0 < B; b0 += RPI * UNR) {
+    // batches of 16 rows go round-robin to the wavefronts of the workgroup. The rows of
+    // a batch (UNR row groups) are loaded before any is used; their UNR logits are
+    // independent (row sums by DPP within the lanes of a row), and the batch enters
+    // the wavefront's running softmax once
+    for (int b0 = ws * ROWS; b0 < B; b0 += kSumWaves * ROWS) {
         float kk[UNR][VEC];
+        // rows past the chunk (a batch longer than B) re-read its last row: no branch, so
+        // all UNR loads are in flight together; those rows are skipped below
 #pragma unroll
         for (int u = 0; u < UNR; ++u) {
-            const int t = b0 + u * RPI + rr;
-            if (t < B) Vec16<T>::load(Kc + (size_t)t * D, kk[u]);
+            const int t = min(b0 + u * RPI + rr, B - 1);
+            Vec16<T>::load(Kc + (size_t)t * D, kk[u]);
         }
         float sc[UNR];
         float bm = -INFINITY;
@@ -137,11 +146,25 @@ __global__ __launch_bounds__(256) void chunk_summary_kernel(
         for (int v = 0; v < VEC; ++v) acc[v] = acc[v] * a + shfl_xor(acc[v], o) * bsc;
         m = mn;
     }
-    if (lane < LPR) {
-        const float inv = 1.f / l;
-        float* out = kbar + ((size_t)br * kbar_cap + c) * D + col;
+    // merge the wavefronts that have rows (the first nw; B is a multiple of 16, so
+    // each of them has whole batches) in a fixed order
+    const int nw = min(kSumWaves, B / ROWS);
+    if (ws < nw && lane < LPR) {
 #pragma unroll
-        for (int v = 0; v < VEC; ++v) out[v] = acc[v] * inv;
+        for (int v = 0; v < VEC; ++v) s_acc[ws][col + v] = acc[v];
+        if (lane == 0) { s_m[ws] = m; s_l[ws] = l; }
+    }
+    __syncthreads();
+    for (int d = threadIdx.x; d < D; d += blockDim.x) {
+        float mt = s_m[0];
+        for (int w = 1; w < nw; ++w) mt = fmaxf(mt, s_m[w]);
+        float lt = 0.f, at = 0.f;
+        for (int w = 0; w < nw; ++w) {
+            const float f = fast_exp2(s_m[w] - mt);
+            lt = fmaf(s_l[w], f, lt);
+            at = fmaf(s_acc[w][d], f, at);
+        }
+        kbar[((size_t)br * kbar_cap + c) * D + d] = at / lt;
     }
 }
 
@@ -150,7 +173,7 @@ static hipError_t launch_summary_t(const SummaryArgs& a, hipStream_t s) {
     const int nsel = a.chunk_end - a.chunk_begin;
     const int total = a.b * a.h_kv * nsel;
     if (total == 0) return hipSuccess;
-    dim3 grid((total + 3) / 4), block(256);
+    dim3 grid(total), block(64 * kSumWaves);
     hipLaunchKernelGGL((chunk_summary_kernel<T, D>), grid, block, 0, s,
                        static_cast<const T*>(a.K), a.qbar, a.kbar, a.h_kv, a.n_kv, a.kbar_cap,
                        a.B, a.chunk_begin, nsel, total,

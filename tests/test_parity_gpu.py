@@ -32,7 +32,8 @@ def _log(msg):
 
 @pytest.mark.parametrize("dtype,d,B,n", [("f32", 64, 64, 1024), ("bf16", 128, 64, 1000),
                                          ("bf16", 64, 16, 200), ("f32", 128, 128, 640),
-                                         ("bf16", 128, 32, 96)])
+                                         ("bf16", 128, 32, 96), ("f32", 64, 48, 480),
+                                         ("bf16", 128, 256, 1024)])
 def test_summaries_match_oracle(dtype, d, B, n):
     G = _gu()
     from oracle import dash_oracle as O
