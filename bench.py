@@ -34,8 +34,8 @@ PEAK_HBM_GBS = 8000.0              # MI355X HBM3E
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--alpha", type=float, default=1.5)
     ap.add_argument("--no-sweep", action="store_true", help="skip the alpha sweep")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
