@@ -254,9 +254,11 @@ dash_status dash_attend_prefill_varlen(const void* Q, const void* K, const void*
                                        void* ws, size_t ws_bytes, void* stream);
 
 /*
- * Stage 2 of a prefill over a paged KV cache (the layout of dash_attend_decode_paged:
- * Kp, Vp [num_pages, h_kv, B, d], chunk c of sequence b in page
- * pages[b * pages_per_seq + c], device int32 [b, pages_per_seq]); Q stays contiguous
+ * Stage 2 of a prefill (Eq. 9-12 via Prop. 4.1, as dash_attend_prefill) whose K and
+ * V live in a paged KV cache, so that prefill and incremental decoding (the
+ * gist.science summary, "Efficient GPU Implementation") share one cache. Layout of
+ * dash_attend_decode_paged: Kp, Vp [num_pages, h_kv, B, d], chunk c of sequence b in page
+ * pages[b * pages_per_seq + c] (device int32 [b, pages_per_seq]); Q stays contiguous
  * [b, h_q, n, d]. seq_len (nullable) gives a ragged batch as for
  * dash_attend_prefill_varlen; otherwise every sequence holds n tokens. Requires
  * pages_per_seq * B >= n and a cache of fewer than 2^31 rows. Page ids outside
