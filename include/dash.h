@@ -284,7 +284,8 @@ dash_status dash_attend_prefill_paged(const void* Q, const void* Kp, const void*
  *   dbias [b, h_kv, n, list_cap]: entry e of a row is the gradient of bias entry e,
  *   the sum of dZ over the tokens of chunk idx[e] and the group's g query heads;
  *   entries at or past cnt, or naming a chunk the row cannot see, are zero.
- * Requires B % 64 == 0, g = h_q/h_kv <= 16, d in {64, 128}, n*floor(n/B) < 2^31
+ * Requires B % 32 == 0 (a 32-token chunk takes a 64-token tile of the dK/dV pass,
+ * half of it computed and discarded), g = h_q/h_kv <= 16, d in {64, 128}, n*floor(n/B) < 2^31
  * and a device workspace of dash_workspace_bytes(DASH_OP_PREFILL_BWD, ...) bytes
  * (grows with n^2/B: the routed lists inverted per chunk are sized for dense
  * routing). dK and dV sum several partials with atomic adds, so their last bits

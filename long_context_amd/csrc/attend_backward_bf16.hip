@@ -223,11 +223,11 @@ struct DqExtra {
     float scale;                     // 1/sqrt(d)
 };
 
-// Copies of one stage: K tile [64][D], V tile [64][D] (both "K" form) and the K^T
-// tile [D][64]; wavefront w issues copy instructions w, w+NW, ...
-template <int D, int NW>
+// Copies of one stage: K tile [TT][D], V tile [TT][D] (both "K" form) and the K^T
+// tile [D][TT]; wavefront w issues copy instructions w, w+NW, ...
+template <int D, int TT, int NW>
 struct DqCopier {
-    typedef BfTiles<D, 64> S;
+    typedef BfTiles<D, TT> S;
     static constexpr int NI = 2 * S::KINSTS + S::VINSTS;
     static constexpr int CPW = NI / NW;
     static_assert(CPW * NW == NI, "copies must divide evenly over the wavefronts");
@@ -255,7 +255,7 @@ struct DqCopier {
     }
     __device__ __forceinline__ void issue(char* stage, const uint16_t* Kg, const uint16_t* Vg, const uint16_t* Ktg,
                                           int tb, int nmax, int n_pad, int wid) const {
-        tb = min(max(tb, 0), n_pad - 64);
+        tb = min(max(tb, 0), n_pad - TT);
 #pragma unroll
         for (int i = 0; i < CPW; ++i) {
             const int j = wid + i * NW;               // wavefront-uniform
@@ -287,15 +287,14 @@ __device__ __forceinline__ float dz_half(const f32x16& sacc, const f32x16& dpacc
     return part;
 }
 
-// NW wavefronts of one 32-pair block each; the tile geometry is the forward's.
-template <int D, int NW>
+// NW wavefronts of one 32-pair block each; the tile geometry is the forward's
+// (TT = 64 tokens when B is a multiple of 64, else 32).
+template <int D, int TT, int NW>
 __global__ __launch_bounds__(64 * NW) void prior_attn_dq_kernel(PrefillParams p, DqExtra x) {
-    typedef BfTiles<D, 64> S;
-    typedef DqCopier<D, NW> CP;
-    constexpr int TT = 64;
+    typedef BfTiles<D, TT> S;
+    typedef DqCopier<D, TT, NW> CP;
     constexpr int NS = D / 16;     // k16 steps over d
-    constexpr int NB = 2;          // 32-token blocks of S^T
-    constexpr int NP = 4;          // k16 steps over the tile's tokens
+    constexpr int NB = TT / 32;    // 32-token blocks of S^T
     constexpr int ND = D / 32;     // 32-wide d blocks of dQ^T
     extern __shared__ __attribute__((aligned(16))) char smem[];
     char* ring = smem;
@@ -469,16 +468,21 @@ struct DkvParams {
     float c1, scale;                             // log2(e)/sqrt(d), 1/sqrt(d)
 };
 
-// Rows of the row sequence of 64-token tile cs of chunk cs / (B/64) of KV group bhk:
-// the routed rows of the chunk, then its diagonal rows at or after the tile (causal;
-// non-causal: every row for the tail tile).
-struct TileRows { int c, t0, rbase, nrouted, dlo, dhi; };
+// 64-token tiles per chunk: B/64, or one (half used) for B = 32
+__host__ __device__ __forceinline__ int tiles_per_chunk(int B) { return B >= 64 ? B / 64 : 1; }
+
+// Rows of the row sequence of 64-token tile cs of chunk cs / SUB of KV group bhk
+// (SUB = tiles_per_chunk(B)): the routed rows of the chunk, then its diagonal rows at
+// or after the tile (causal; non-causal: every row for the tail tile). The tile's
+// tokens are t0 .. tend-1 (tend - t0 < 64 for a 32-token chunk or the tail).
+struct TileRows { int c, t0, tend, rbase, nrouted, dlo, dhi; };
 __device__ __forceinline__ TileRows tile_rows(const int32_t* coff, size_t bhk, int cs, int n, int B, int T,
                                               int causal) {
     TileRows r;
-    const int SUB = B / 64;
+    const int SUB = tiles_per_chunk(B);
     r.c = cs / SUB;
     r.t0 = r.c * B + 64 * (cs % SUB);
+    r.tend = min(min(r.t0 + 64, r.c * B + B), n);
     r.rbase = 0; r.nrouted = 0; r.dlo = 0; r.dhi = 0;
     if (r.t0 >= n) return r;
     if (r.c < T) {
@@ -518,7 +522,7 @@ __device__ __forceinline__ int block_scan1024(int v, int* tmp, int& total) {
 __global__ __launch_bounds__(1024) void dkv_items_kernel(const int32_t* coff, int4* items, int32_t* counters,
                                                          int bh, int n, int B, int T, int causal, int seg_rows) {
     __shared__ int tmp[16];
-    const int per_bh = (T + 1) * (B / 64);
+    const int per_bh = (T + 1) * tiles_per_chunk(B);
     const int E = bh * per_bh;
     const int per = (E + 1023) / 1024;
     const int e0 = min((int)threadIdx.x * per, E), e1 = min(e0 + per, E);
@@ -657,8 +661,9 @@ __device__ __forceinline__ void tr_reads_d128_sw(const uint32_t (&a)[8], i16x4 (
         : "memory");
 }
 
-// One work item: 64 tokens of one chunk (tile cs) of KV group bhk against segment
-// seg of its row sequence.
+// One work item: up to 64 tokens of one chunk (tile cs) of KV group bhk against
+// segment seg of its row sequence. Tokens from tend on (a 32-token chunk's second
+// half, the sequence end) are computed on and never written.
 template <int D>
 __device__ __forceinline__ void dkv_item(const DkvParams& p, size_t bhk, int cs, int seg, char* smem) {
     typedef BfTiles<D, 64> S;
@@ -679,7 +684,7 @@ __device__ __forceinline__ void dkv_item(const DkvParams& p, size_t bhk, int cs,
     const int bi = (int)(bhk / p.h_kv), hk = (int)(bhk % p.h_kv);
     const int T = p.T_c;
     const TileRows tr = tile_rows(p.coff, bhk, cs, p.n, p.B, T, p.causal);
-    const int t0 = tr.t0, rbase = tr.rbase, nrouted = tr.nrouted, dlo = tr.dlo, dhi = tr.dhi;
+    const int t0 = tr.t0, tend = tr.tend, rbase = tr.rbase, nrouted = tr.nrouted, dlo = tr.dlo, dhi = tr.dhi;
     if (t0 >= p.n) return;
     const int nrows = nrouted + max(dhi - dlo, 0);
     // segment 0 holds the end of the sequence
@@ -931,7 +936,7 @@ __device__ __forceinline__ void dkv_item(const DkvParams& p, size_t bhk, int cs,
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int t = t0 + 32 * tbk + 8 * (i >> 2) + 4 * hl + (i & 3);
-            if (t < p.n) {
+            if (t < tend) {
                 const size_t o = (bhk * p.n + t) * D + 32 * db + l32;
                 unsafeAtomicAdd(p.dK + o, dk[db][i] * p.scale);
                 unsafeAtomicAdd(p.dV + o, dv[db][i]);
@@ -963,8 +968,10 @@ __global__ __launch_bounds__(256) void prior_attn_dkv_kernel(DkvParams p) {
 static constexpr int kDqWaves = 4;
 static constexpr size_t kBwdMaxLds = 160 * 1024;
 
-static size_t dq_lds_bytes(int d, int T_c) {
-    const size_t stage = d == 64 ? DqCopier<64, kDqWaves>::STAGE : DqCopier<128, kDqWaves>::STAGE;
+static size_t dq_lds_bytes(int d, int B, int T_c) {
+    const bool t64 = B % 64 == 0;
+    const size_t stage = d == 64 ? (t64 ? DqCopier<64, 64, kDqWaves>::STAGE : DqCopier<64, 32, kDqWaves>::STAGE)
+                                 : (t64 ? DqCopier<128, 64, kDqWaves>::STAGE : DqCopier<128, 32, kDqWaves>::STAGE);
     return 2 * stage + TileTables::bytes(T_c);
 }
 static size_t dkv_lds_bytes(int d) {
@@ -972,18 +979,18 @@ static size_t dkv_lds_bytes(int d) {
 }
 
 int backward_tile_rows(int g, int B, int T_c, int d) {
-    if (g < 1 || g > 16 || (g & (g - 1)) != 0 || B % 64 != 0 || (d != 64 && d != 128)) return 0;
-    if (dq_lds_bytes(d, T_c) > kBwdMaxLds) return 0;
-    return std::min(32 * kDqWaves / g, 64);      // a query tile stays inside one chunk
+    if (g < 1 || g > 16 || (g & (g - 1)) != 0 || B % 32 != 0 || (d != 64 && d != 128)) return 0;
+    if (dq_lds_bytes(d, B, T_c) > kBwdMaxLds) return 0;
+    return std::min(32 * kDqWaves / g, std::min(B, 64));      // a query tile stays inside one chunk
 }
 
 // Rows per dK/dV work item and an upper bound on the number of items: over the tiles
-// of one KV group the sequences hold each routed entry B/64 times (at most n floor(n/B)
-// entries) plus diagonal rows (at most B/64 (n + B)); every tile adds at most one
-// partial segment.
+// of one KV group the sequences hold each routed entry SUB = tiles_per_chunk(B) times
+// (at most n floor(n/B) entries) plus diagonal rows (at most SUB (n + B)); every tile
+// adds at most one partial segment.
 static int dkv_seg_rows(int g) { return 8192 / g; }
 static size_t dkv_item_bound(int b, int h_q, int h_kv, int n, int B) {
-    const size_t T = (size_t)(n / B), SUB = (size_t)(B / 64), seg = (size_t)dkv_seg_rows(h_q / h_kv);
+    const size_t T = (size_t)(n / B), SUB = (size_t)tiles_per_chunk(B), seg = (size_t)dkv_seg_rows(h_q / h_kv);
     return (size_t)b * h_kv * ((T + 1) * SUB + (SUB * ((size_t)n * T + n + B) + seg - 1) / seg);
 }
 
@@ -1018,6 +1025,17 @@ static hipError_t fill_zero(float* x, size_t n, hipStream_t s) {
     if (n == 0) return hipSuccess;
     const size_t blocks = std::min<size_t>((n + 255) / 256, 65536);
     hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, s, x, n);
+    return hipGetLastError();
+}
+
+template <int D, int TT>
+static hipError_t launch_dq(const PrefillParams& p, const DqExtra& x, const PrefillBwdArgs& a, int T, hipStream_t s) {
+    auto kern = prior_attn_dq_kernel<D, TT, kDqWaves>;
+    static hipError_t configured = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kBwdMaxLds);
+    if (configured != hipSuccess) return configured;
+    dim3 grid((a.n + p.R_t - 1) / p.R_t, a.h_kv, a.b);
+    hipLaunchKernelGGL(kern, grid, dim3(64 * kDqWaves), dq_lds_bytes(D, a.B, T), s, p, x);
     return hipGetLastError();
 }
 
@@ -1071,15 +1089,8 @@ static hipError_t launch_bwd_t(const PrefillBwdArgs& a, const BwdLayout& L, hipS
     p.scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
     const float scale = (float)(1.0 / sqrt((double)D));
     DqExtra x{kt, dO16, a.lse, delta, a.dQ, a.dbias, scale};
-    {
-        auto kern = prior_attn_dq_kernel<D, kDqWaves>;
-        static hipError_t configured = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)kBwdMaxLds);
-        if (configured != hipSuccess) return configured;
-        dim3 grid((a.n + p.R_t - 1) / p.R_t, a.h_kv, a.b);
-        hipLaunchKernelGGL(kern, grid, dim3(64 * kDqWaves), dq_lds_bytes(D, T), s, p, x);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
+    if ((e = a.B % 64 == 0 ? launch_dq<D, 64>(p, x, a, T, s) : launch_dq<D, 32>(p, x, a, T, s)) != hipSuccess)
+        return e;
 
     // dK and dV
     DkvParams q;

@@ -391,7 +391,7 @@ dash_status dash_attend_prefill_backward(const void* Q, const void* K, const voi
     dash_status st = check_common(b, h_q, h_kv, d, B);
     if (st != DASH_OK) return st;
     if (in_dtype != DASH_BF16) return fail(DASH_ERR_UNSUPPORTED, "the Stage-2 backward takes bf16 Q, K, V");
-    if (B % 64 != 0) return fail(DASH_ERR_UNSUPPORTED, "the Stage-2 backward needs B %% 64 == 0 (B = %d)", B);
+    if (B % 32 != 0) return fail(DASH_ERR_UNSUPPORTED, "the Stage-2 backward needs B %% 32 == 0 (B = %d)", B);
     if (n < 0) return fail(DASH_ERR_SHAPE, "n must be >= 0");
     const int T = n / B;
     if (list_cap < T) return fail(DASH_ERR_SHAPE, "list_cap %d < floor(n/B) = %d", list_cap, T);

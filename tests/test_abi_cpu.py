@@ -246,7 +246,7 @@ def _backward(dash, ws_bytes=None, **kw):
     (dict(lse=NUL), 1), (dict(dO=NUL), 1), (dict(dbias=NUL), 1), (dict(dK=NUL), 1),
     (dict(odt=2), 3), (dict(causal=2), 3), (dict(cap=3), 2), (dict(h_q=15), 2),
     (dict(dt=0), 4),                        # fp32 Q/K/V
-    (dict(B=32, cap=8), 4),                 # B % 64 != 0
+    (dict(B=48, cap=8), 4),                 # B % 32 != 0
     (dict(h_q=64), 4),                      # g = 32
     (dict(ws=NUL), 5),
 ])
@@ -265,6 +265,13 @@ def test_backward_workspace(dash):
     expect = (up(hkv * d * 256 * 2) + up(hq * n * d * 2) + up(hq * n * 4) + up(hkv * T * nblk * 4)
               + up(hkv * (T + 1) * 4) + 2 * up(hkv * n * T * 4) + up(items * 16) + 256)
     assert need == expect
+    # 32-token chunks: one (half used) 64-token dK/dV tile per chunk
+    B = 32
+    T = n // B
+    items32 = hkv * ((T + 1) + -(-(n * T + n + B) // seg))
+    expect32 = (up(hkv * d * 256 * 2) + up(hq * n * d * 2) + up(hq * n * 4) + up(hkv * T * nblk * 4)
+                + up(hkv * (T + 1) * 4) + 2 * up(hkv * n * T * 4) + up(items32 * 16) + 256)
+    assert dash.dash_workspace_bytes(dash.DASH_OP_PREFILL_BWD, 1, hq, hkv, n, d, B) == expect32
     # n * floor(n/B) must stay below 2^31 (inverted list offsets are int32)
     assert _backward(dash, n=1 << 20, B=64, cap=1 << 14, ws_bytes=1 << 62) == dash.DASH_ERR_UNSUPPORTED
 
