@@ -31,6 +31,8 @@
  *     of each listed chunk alongside.
  *   - `stream` is a hipStream_t (NULL = the null stream). Calls only enqueue
  *     work; they never synchronise.
+ *   - n = 0 (empty sequences) is a valid call of the prefill-side entry points: the
+ *     arguments are validated as usual (pointers non-null) and nothing is launched.
  *   - Every argument is validated on the host before anything is enqueued; on
  *     error nothing is launched, outputs are untouched, and a detail string is
  *     available from dash_last_error() (per thread). The library never aborts.

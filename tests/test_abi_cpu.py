@@ -375,3 +375,15 @@ def test_paged_prefill_validation(dash):
     bad = list(args)
     bad[6] = 0
     assert p(*bad, NUL, 0, NUL) == dash.DASH_ERR_SHAPE
+
+
+def test_empty_sequence_is_a_no_op(dash):
+    """n = 0 (a batch of empty sequences) is a valid call of every prefill-side entry
+    point: validation passes and nothing is launched (there is no GPU here, so any
+    launch would come back as DASH_ERR_LAUNCH)."""
+    assert _summ(dash, n=0, cap=1, c0=0, c1=0) == dash.DASH_OK
+    assert _route(dash, n=0, cap=1, list_cap=1) == dash.DASH_OK
+    assert _prefill(dash, n=0) == dash.DASH_OK
+    assert _prefill(dash, n=0, dt=1, odt=1) == dash.DASH_OK
+    assert _backward(dash, n=0, ws_bytes=0) == dash.DASH_OK
+    assert _route_bwd(dash, n=0, ws_bytes=0) == dash.DASH_OK
