@@ -1,6 +1,6 @@
-"""The oracle's α-entmax against hand-derived closed forms stored in
-tests/golden/entmax_closed_forms.txt (each line carries its derivation from the
-α-entmax definition of the paper review, section 三 background)."""
+"""The oracle against hand-derived closed forms stored under tests/golden/ (each line
+carries its derivation): α-entmax (the paper review, section 三 background formula) and
+the Stage-0 summaries (section 三, Eq. 4)."""
 import os
 
 import numpy as np
@@ -38,3 +38,27 @@ def test_entmax_closed_form(case):
     assert abs(p[0].sum() - 1.0) <= 1e-12
     if tau_ref is not None:
         assert abs(float(tau[0]) - tau_ref) <= 1e-12, why
+
+
+def _stage0_cases():
+    out = []
+    for line in open(os.path.join(HERE, "golden", "stage0_closed_forms.txt")):
+        if not line.strip() or line.startswith("#"):
+            continue
+        d, B, keys, qbar, kbar, why = [f.strip() for f in line.split("|")]
+        K = np.array([[float(v) for v in row.split(",")] for row in keys.split(";")])
+        out.append((int(d), int(B), K, np.array([float(v) for v in qbar.split(",")]),
+                    np.array([float(v) for v in kbar.split(",")]), why))
+    return out
+
+
+S0 = _stage0_cases()
+
+
+@pytest.mark.parametrize("case", S0, ids=[f"s0-{i}" for i in range(len(S0))])
+def test_stage0_closed_form(case):
+    d, B, K, qbar, kbar_ref, why = case
+    assert K.shape == (B, d)
+    kb = O.stage0_summaries(K[None, None], qbar[None], B)          # [1, 1, 1, d]
+    assert kb.shape == (1, 1, 1, d)
+    assert np.abs(kb[0, 0, 0] - kbar_ref).max() <= 1e-12, why
