@@ -62,3 +62,29 @@ def test_stage0_closed_form(case):
     kb = O.stage0_summaries(K[None, None], qbar[None], B)          # [1, 1, 1, d]
     assert kb.shape == (1, 1, 1, d)
     assert np.abs(kb[0, 0, 0] - kbar_ref).max() <= 1e-12, why
+
+
+def _ra_cases():
+    import json
+    f = json.load(open(os.path.join(HERE, "golden", "route_attend_closed_forms.json")))
+    return f["common"], f["cases"]
+
+
+RA_COMMON, RA = _ra_cases()
+
+
+@pytest.mark.parametrize("case", RA, ids=[c["name"].replace(" ", "_") for c in RA])
+def test_route_attend_closed_form(case):
+    c = RA_COMMON
+    Q = np.array(case["Q"], dtype=np.float64)[None, :, None, :]            # [1, h_q, 1, d]
+    kbar = np.array(case["kbar"], dtype=np.float64)[None, None]            # [1, 1, T, d]
+    pos = np.array([[c["pos"]]])
+    rt = O.route(Q, pos, kbar, c["B"], c["alpha"], c["gamma"], c["sigma"], c["causal"], c["n_kv"])
+    tv = len(case["w"])                                  # visible chunks; the rest is the query's own
+    assert np.abs(rt["w"][0, 0, 0, :tv] - np.array(case["w"])).max() <= 1e-12, case["derivation"]
+    assert rt["support"][0, 0, 0, :tv].all() and not rt["support"][0, 0, 0, tv:].any()
+    assert np.abs(rt["bias"][0, 0, 0, :tv] - np.array(case["bias"])).max() <= 1e-12, case["derivation"]
+    K = np.array(c["K"], dtype=np.float64)[None, None]
+    V = np.array(c["V"], dtype=np.float64)[None, None]
+    out = O.attend(Q, pos, K, V, rt, c["B"], c["causal"], c["n_kv"])
+    assert np.abs(out[0, :, 0] - np.array(case["O"])).max() <= 1e-12, case["derivation"]
