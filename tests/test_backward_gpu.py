@@ -209,6 +209,7 @@ BWD = [
     (1, 16, 2, 128, 300, 32, True, 6.0, "f32"),      # B 32: 32-token dQ tiles, half-used dK/dV tiles
     (2, 8, 2, 64, 250, 32, False, 5.0, "bf16"),      # B 32, d 64, non-causal tail of 26 tokens
     (1, 2, 2, 64, 200, 32, True, 4.0, "f32"),        # B 32, g = 1 (query tiles of 32 rows)
+    (1, 32, 2, 128, 260, 32, True, 6.0, "bf16"),     # B 32, GQA 16 (query tiles of 8 rows)
 ]
 
 
