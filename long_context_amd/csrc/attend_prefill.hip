@@ -249,7 +249,8 @@ void prefill_tiling(int g, int B, int T_c, int d, bool bf16, int* rows, size_t* 
     for (int m = geo.max_pairs; m >= 32; m >>= 1) {
         const int R_t = m / g;
         if (R_t < 1 || B % R_t != 0) continue;
-        const size_t lds = (size_t)geo.stages * st + TileTables::bytes(T_c);
+        const int stages = bf16 ? prefill_bf16_stages(d, B, T_c) : geo.stages;
+        const size_t lds = (size_t)stages * st + TileTables::bytes(T_c);
         if (lds <= kMaxLds) {
             *rows = R_t;
             *lds_bytes = lds;

@@ -112,8 +112,8 @@ __global__ __launch_bounds__(256) void transpose_v_kernel(const uint16_t* V, uin
 
 
 // NW wavefronts of PBW pair blocks (32 (row, head) pairs each); PAGED: K read through
-// the page table.
-template <int D, int TT, int NW, int PBW, bool PAGED>
+// the page table; PS tiles per barrier.
+template <int D, int TT, int NW, int PBW, bool PAGED, int PS>
 __global__ __launch_bounds__(64 * NW) void sparse_prior_attn_bf16_kernel(PrefillParams p) {
     typedef BfTiles<D, TT> S;
     constexpr int NS = D / 16;     // k16 steps of S^T
@@ -121,9 +121,9 @@ __global__ __launch_bounds__(64 * NW) void sparse_prior_attn_bf16_kernel(Prefill
     constexpr int NP = TT / 16;    // k16 steps of O^T
     constexpr int ND = D / 32;     // 32-wide d blocks of O^T
     extern __shared__ __attribute__((aligned(16))) char smem[];
-    char* ring = smem;                                   // two tile stages
+    char* ring = smem;                                   // two stages of PS tiles
     TileTables tabs;
-    tabs.carve(smem + 2 * S::STAGE, p.T_c);
+    tabs.carve(smem + 2 * PS * S::STAGE, p.T_c);
 
     constexpr int nthr = 64 * NW;
     const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
@@ -282,54 +282,76 @@ __global__ __launch_bounds__(64 * NW) void sparse_prior_attn_bf16_kernel(Prefill
                 o_acc[pb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[s][db], pp[s], o_acc[pb][db], 0, 0, 0);
     };
 
-    // the tile base and chunk of each step are read from LDS two steps ahead, so
-    // that neither the cursors nor the copies wait on an LDS read
-    int tb_cur, c_cur, tb_nxt, c_nxt;
-    st.at(tabs.ulist, 0, tb_cur, c_cur);
-    st.at(tabs.ulist, 1, tb_nxt, c_nxt);
-    int ko_nxt = krow0(tb_nxt);
-    if (st.nsteps > 0) cp.issue(ring, Kg, krow0(tb_cur), Vtg, tb_cur, nmax, p.n_pad, wid);
+    // PS steps per barrier: ring stage j & 1 holds the PS tiles of group j, and a
+    // wavefront takes the tiles of the group it has rows for one after the other (a
+    // wavefront idle on a tile no longer waits at a barrier of that tile's own). The
+    // tile bases and chunks are read from LDS two groups ahead, so that neither the
+    // cursors nor the copies wait on an LDS read.
+    const int npairs = (st.nsteps + PS - 1) / PS;
+    int tb_cur[PS], c_cur[PS], tb_nxt[PS], c_nxt[PS], ko_nxt[PS];
+#pragma unroll
+    for (int u = 0; u < PS; ++u) {
+        st.at(tabs.ulist, u, tb_cur[u], c_cur[u]);
+        st.at(tabs.ulist, PS + u, tb_nxt[u], c_nxt[u]);
+        ko_nxt[u] = krow0(tb_nxt[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < PS; ++u)
+        if (u < st.nsteps) cp.issue(ring + u * S::STAGE, Kg, krow0(tb_cur[u]), Vtg, tb_cur[u], nmax, p.n_pad, wid);
     wait_tile_copies();
     __syncthreads();
-    for (int k = 0; k < st.nsteps; ++k) {
-        // bias of this tile's chunk per pair block; the cursors' entries arrived
-        // during the previous tile, and their next loads go out ahead of the copies
-        const bool routed = k < st.nrouted;
-        float bias2[PBW];
-        bool run[PBW];
+    for (int j = 0; j < npairs; ++j) {
+        const int k0 = PS * j;
 #pragma unroll
-        for (int pb = 0; pb < PBW; ++pb) {
-            bias2[pb] = routed ? lc[pb].take(c_cur, k % st.SPC == st.SPC - 1) : 0.f;
-            run[pb] = live[pb] && (!routed || ballot(bias2[pb] > -INFINITY) != 0);
+        for (int u = 0; u < PS; ++u)
+            if (k0 + PS + u < st.nsteps)
+                cp.issue(ring + (((j + 1) & 1) * PS + u) * S::STAGE, Kg, ko_nxt[u], Vtg, tb_nxt[u], nmax, p.n_pad, wid);
+        int tb_nn[PS], c_nn[PS], ko_nn[PS];
+#pragma unroll
+        for (int u = 0; u < PS; ++u) {
+            st.at(tabs.ulist, k0 + 2 * PS + u, tb_nn[u], c_nn[u]);
+            ko_nn[u] = krow0(tb_nn[u]);      // (paged) a page-table load with a group to arrive
         }
-        if (k + 1 < st.nsteps) cp.issue(ring + ((k + 1) & 1) * S::STAGE, Kg, ko_nxt, Vtg, tb_nxt, nmax, p.n_pad, wid);
-        int tb_nn, c_nn;
-        st.at(tabs.ulist, k + 2, tb_nn, c_nn);
-        const int ko_nn = krow0(tb_nn);      // (paged) a page-table load with two tiles to arrive
-        const char* kt = ring + (k & 1) * S::STAGE;
-        const char* vt = kt + S::KBYTES;
-        const int tb = tb_cur;
 #pragma unroll
-        for (int pb = 0; pb < PBW; ++pb) {
-            if (run[pb]) {
-                bf16x8 ka[NB][NS];
-                load_k(kt, ka);
-                f32x16 sacc[NB];
-                scores(pb, ka, sacc);
-                bf16x8 pp[NP];
-                bool grow;
-                const float alpha = softmax(pb, !routed, tb, bias2[pb], sacc, pp, grow);
-                rescale(pb, grow, alpha);
-                bf16x8 va[NP][ND];
-                load_v(vt, va);
-                pv(pb, va, pp);
+        for (int u = 0; u < PS; ++u) {
+            const int k = k0 + u;
+            if (k >= st.nsteps) break;
+            const bool routed = k < st.nrouted;
+            float bias2[PBW];
+            bool run[PBW];
+#pragma unroll
+            for (int pb = 0; pb < PBW; ++pb) {
+                bias2[pb] = routed ? lc[pb].take(c_cur[u], k % st.SPC == st.SPC - 1) : 0.f;
+                run[pb] = live[pb] && (!routed || ballot(bias2[pb] > -INFINITY) != 0);
+            }
+            const char* kt = ring + ((j & 1) * PS + u) * S::STAGE;
+            const char* vt = kt + S::KBYTES;
+            const int tb = tb_cur[u];
+#pragma unroll
+            for (int pb = 0; pb < PBW; ++pb) {
+                if (run[pb]) {
+                    bf16x8 ka[NB][NS];
+                    load_k(kt, ka);
+                    f32x16 sacc[NB];
+                    scores(pb, ka, sacc);
+                    bf16x8 pp[NP];
+                    bool grow;
+                    const float alpha = softmax(pb, !routed, tb, bias2[pb], sacc, pp, grow);
+                    rescale(pb, grow, alpha);
+                    bf16x8 va[NP][ND];
+                    load_v(vt, va);
+                    pv(pb, va, pp);
+                }
             }
         }
         wait_tile_copies();
         __syncthreads();
-        tb_cur = tb_nxt; c_cur = c_nxt;
-        tb_nxt = tb_nn; c_nxt = c_nn;
-        ko_nxt = ko_nn;
+#pragma unroll
+        for (int u = 0; u < PS; ++u) {
+            tb_cur[u] = tb_nxt[u]; c_cur[u] = c_nxt[u];
+            tb_nxt[u] = tb_nn[u]; c_nxt[u] = c_nn[u];
+            ko_nxt[u] = ko_nn[u];
+        }
     }
 
 #pragma unroll
@@ -391,20 +413,33 @@ PrefillGeom prefill_geom_bf16(int d, int B) {
     return PrefillGeom{bf16_tile_tokens(d, B), kWavesB, 32 * kWavesB * kPairBlocks, 2};
 }
 
-// Both K/V layouts of every (d, tile) pair are instantiated explicitly: when one
-// dispatcher names the two, hipcc emits the host handle of only the first.
-#define DASH_PREFILL_BF16_INST(D, TT)                                                                   \
-    template __global__ void sparse_prior_attn_bf16_kernel<D, TT, kWavesB, kPairBlocks, false>(PrefillParams); \
-    template __global__ void sparse_prior_attn_bf16_kernel<D, TT, kWavesB, kPairBlocks, true>(PrefillParams);
-DASH_PREFILL_BF16_INST(64, 32)
-DASH_PREFILL_BF16_INST(64, 64)
-DASH_PREFILL_BF16_INST(128, 32)
-DASH_PREFILL_BF16_INST(128, 64)
+// Ring stages of tiles: two groups of two tiles (two steps per barrier) when they and
+// the tile tables fit LDS, else two single tiles (contexts of more than about 4K chunks
+// at d = 128 and 64-token tiles).
+int prefill_bf16_stages(int d, int B, int T_c) {
+    const size_t stage = (size_t)2 * bf16_tile_tokens(d, B) * d * 2;     // K and V^T tiles
+    return 4 * stage + TileTables::bytes(T_c) <= (size_t)160 * 1024 ? 4 : 2;
+}
+
+// Every (d, tile, K/V layout, tiles per barrier) combination is instantiated
+// explicitly: when one dispatcher names two, hipcc emits the host handle of only the
+// first.
+#define DASH_PREFILL_BF16_INST(D, TT, PS)                                                                   \
+    template __global__ void sparse_prior_attn_bf16_kernel<D, TT, kWavesB, kPairBlocks, false, PS>(PrefillParams); \
+    template __global__ void sparse_prior_attn_bf16_kernel<D, TT, kWavesB, kPairBlocks, true, PS>(PrefillParams);
+DASH_PREFILL_BF16_INST(64, 32, 1)
+DASH_PREFILL_BF16_INST(64, 64, 1)
+DASH_PREFILL_BF16_INST(128, 32, 1)
+DASH_PREFILL_BF16_INST(128, 64, 1)
+DASH_PREFILL_BF16_INST(64, 32, 2)
+DASH_PREFILL_BF16_INST(64, 64, 2)
+DASH_PREFILL_BF16_INST(128, 32, 2)
+DASH_PREFILL_BF16_INST(128, 64, 2)
 #undef DASH_PREFILL_BF16_INST
 
-template <int D, int TT, bool PAGED>
+template <int D, int TT, bool PAGED, int PS>
 static hipError_t launch_bf16_paged(const PrefillParams& p, int b, size_t lds, hipStream_t s) {
-    auto kern = sparse_prior_attn_bf16_kernel<D, TT, kWavesB, kPairBlocks, PAGED>;
+    auto kern = sparse_prior_attn_bf16_kernel<D, TT, kWavesB, kPairBlocks, PAGED, PS>;
     static hipError_t configured = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (configured != hipSuccess) return configured;
@@ -416,9 +451,15 @@ static hipError_t launch_bf16_paged(const PrefillParams& p, int b, size_t lds, h
     return hipGetLastError();
 }
 
+template <int D, int TT, int PS>
+static hipError_t launch_bf16_ps(const PrefillParams& p, int b, size_t lds, hipStream_t s) {
+    return p.pages ? launch_bf16_paged<D, TT, true, PS>(p, b, lds, s) : launch_bf16_paged<D, TT, false, PS>(p, b, lds, s);
+}
+
 template <int D, int TT>
 static hipError_t launch_bf16_t(const PrefillParams& p, int b, size_t lds, hipStream_t s) {
-    return p.pages ? launch_bf16_paged<D, TT, true>(p, b, lds, s) : launch_bf16_paged<D, TT, false>(p, b, lds, s);
+    return prefill_bf16_stages(D, p.B, p.T_c) == 4 ? launch_bf16_ps<D, TT, 2>(p, b, lds, s)
+                                                   : launch_bf16_ps<D, TT, 1>(p, b, lds, s);
 }
 
 hipError_t launch_prefill_bf16(const PrefillParams& p, int b, int d, size_t lds, hipStream_t s) {

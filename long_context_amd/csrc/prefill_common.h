@@ -189,6 +189,8 @@ struct BfTiles {
 struct PrefillGeom { int TT, waves, max_pairs, stages; };
 PrefillGeom prefill_geom_f32(int d, int B);
 PrefillGeom prefill_geom_bf16(int d, int B);
+// LDS tile stages of the bf16 kernel (4: two tiles per barrier; 2: one), by context length
+int prefill_bf16_stages(int d, int B, int T_c);
 
 // fp32-input kernel (attend_prefill.hip) and bf16-input kernel with its V
 // transposition (attend_prefill_bf16.hip).

@@ -605,3 +605,54 @@ def test_efficiency_decode_96k_b24(sparsity):
     vis = (w.seq_len - 1) // w.B
     _log(f"efficiency decode 96K: exempt groups {nex}, row error {err:.3e}, "
          f"group sparsity {1.0 - cnt.sum() / (vis[:, None] * np.ones_like(cnt)).sum():.3f}")
+
+
+def test_prefill_stage2_beyond_4k_chunks():
+    """Stage 2 over 4097 chunks (d = 128, 64-token tiles): the tile tables no longer fit
+    LDS beside two groups of two tiles, so the kernel takes one tile per barrier. The
+    router stops at 2048 chunks, so the lists are made here (the first, middle and
+    last visible chunk of each row, random biases) and the oracle's attention
+    (Prop. 4.1 form) runs on the same lists for sampled rows."""
+    from long_context_amd import dash
+    from oracle import dash_oracle as O
+    G = _gu()
+    B, d, T = 64, 128, 4097
+    n = T * B
+    _log(f"stage-2 case n={n} T={T} (one tile per barrier)")
+    rng = np.random.default_rng(21)
+    Qh = rng.standard_normal((1, 1, n, d), dtype=np.float32)
+    Kh = rng.standard_normal((1, 1, n, d), dtype=np.float32)
+    Vh = rng.standard_normal((1, 1, n, d), dtype=np.float32)
+    Q, K, V = (G.to_dev(x, "bf16") for x in (Qh, Kh, Vh))
+    Qr, Kr, Vr = (x.float().cpu().numpy() for x in (Q, K, V))      # the bf16 values both sides use
+    vis = np.arange(n) // B
+    cnt = np.minimum(vis, 3).astype(np.int32)
+    idx = np.zeros((n, 3), np.int32)
+    idx[:, 1] = np.where(cnt == 3, vis // 2, np.maximum(vis - 1, 0))
+    idx[:, 2] = np.maximum(vis - 1, 0)
+    bias = rng.uniform(-1.0, 1.0, (n, 3)).astype(np.float32)
+    # the lists are sized for every visible chunk (list_cap >= T); only the first three
+    # entries of a row are filled
+    idx_d = torch.zeros((1, 1, n, T), dtype=torch.int32, device="cuda")
+    bias_d = torch.zeros((1, 1, n, T), device="cuda")
+    idx_d[0, 0, :, :3] = torch.from_numpy(idx).cuda()
+    bias_d[0, 0, :, :3] = torch.from_numpy(bias).cuda()
+    O_gpu = torch.full((1, 1, n, d), float("nan"), device="cuda")
+    dash.dash_attend_prefill(Q, K, V, idx_d, bias_d, torch.from_numpy(cnt[None, None]).cuda(), O_gpu, B, True)
+    torch.cuda.synchronize()
+    rows = _sample_rows(n, B, 24, 5)
+    rows = np.unique(np.concatenate([rows, [2 * B, 3 * B + 5]]))
+    R = rows.size
+    support = np.zeros((1, 1, R, T), bool)
+    bmat = np.zeros((1, 1, R, T))
+    for k, i in enumerate(rows):
+        for e in range(cnt[i]):
+            support[0, 0, k, idx[i, e]] = True
+            bmat[0, 0, k, idx[i, e]] = bias[i, e]
+    rt = dict(support=support, bias=bmat)
+    ref = O.attend(Qr[:, :, rows], rows[None], Kr, Vr, rt, B, True, n)
+    got = O_gpu[0, 0, torch.from_numpy(rows).cuda()].cpu().numpy().astype(np.float64)
+    err = np.abs(got - ref[0, 0]).max(-1) / np.sqrt((ref[0, 0] ** 2).mean(-1))
+    _log(f"  rows {R}, worst per-row relative error {err.max():.2e}")
+    assert np.isfinite(got).all()
+    assert err.max() <= G.TOL_BF16_ROW
