@@ -32,6 +32,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <type_traits>
 
 namespace dash {
 
@@ -106,6 +107,38 @@ __device__ __forceinline__ float pow_p(float t, float pexp) {
     return t > 0.f ? fast_exp2(pexp * fast_log2(t)) : 0.f;
 }
 
+// Tiles of a row are visited in groups of four, one uniform branch per group: a tile
+// at or past nt holds y = -inf, so [y - τ]_+ = 0 and it adds exact zeros to every sum
+// below. (One branch per tile made the compiler keep 32 loop-invariant conditions live
+// across the Newton loop, spilling them and re-testing each through vector registers.)
+template <int NT> constexpr int tile_group() { return NT < 4 ? NT : 4; }
+
+// The (wavefront-uniform) tile count laundered through an empty asm statement, so that
+// the group tests are evaluated where they stand instead of being hoisted out of the
+// enclosing loop.
+__device__ __forceinline__ int fresh_count(int nt) {
+    nt = __builtin_amdgcn_readfirstlane(nt);
+    asm volatile("" : "+s"(nt));
+    return nt;
+}
+
+// Newton sums a0 = sum t^{p-1}, a1 = sum t^p over the lane's chunks, t = [y - τ]_+.
+template <int NT, int PM>
+__device__ __forceinline__ void newton_sums(const float (&sv)[NT][4], int nt, float tau, float pexp,
+                                            float& a0, float& a1) {
+    constexpr int TG = tile_group<NT>();
+    const int ntl = fresh_count(nt);
+#pragma unroll
+    for (int t4 = 0; t4 < NT; t4 += TG) {
+        if (t4 < ntl) {
+#pragma unroll
+            for (int t = t4; t < t4 + TG; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) accum_pow<PM>(pos_part(sv[t][i] - tau), pexp, a0, a1);
+        }
+    }
+}
+
 // Newton iterations on the wave's 16 pairs; sv holds y (-inf on invalid chunks).
 template <int NT, int PM>
 __device__ __forceinline__ float solve_tau(float (&sv)[NT][4], int nt, float pexp, bool active) {
@@ -113,13 +146,7 @@ __device__ __forceinline__ float solve_tau(float (&sv)[NT][4], int nt, float pex
     bool done = !active;
     for (int it = 0; it < 100; ++it) {
         float a0 = 0.f, a1 = 0.f;
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            if (t < nt) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) accum_pow<PM>(pos_part(sv[t][i] - tau), pexp, a0, a1);
-            }
-        }
+        newton_sums<NT, PM>(sv, nt, tau, pexp, a0, a1);
         a0 = pair32_sum(pair16_sum(a0));
         a1 = pair32_sum(pair16_sum(a1));
         float delta;
@@ -135,6 +162,58 @@ __device__ __forceinline__ float solve_tau(float (&sv)[NT][4], int nt, float pex
         if (ballot(!done) == 0) break;
     }
     return tau;
+}
+
+// Group weights w_c = (1/g) sum_h ŵ_hc of the lane's chunks in place of y: the per-head
+// weights first, then the sum over the g = 2^lg lanes of each row one DPP level at a
+// time over all chunks (the additions row_group_sum makes per value, in its order), so
+// each level is tested once instead of once per value.
+template <int CTRL, int NT>
+__device__ __forceinline__ void dpp_level(float (&sv)[NT][4], int nt) {
+    constexpr int TG = tile_group<NT>();
+    const int ntl = fresh_count(nt);
+#pragma unroll
+    for (int t4 = 0; t4 < NT; t4 += TG) {
+        if (t4 < ntl) {
+#pragma unroll
+            for (int t = t4; t < t4 + TG; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    sv[t][i] += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(sv[t][i]), CTRL, 0xF, 0xF, false));
+        }
+    }
+}
+template <int NT, int PM>
+__device__ __forceinline__ void group_weights(float (&sv)[NT][4], int nt, float tau, float pexp, bool row_ok,
+                                              int lg, float inv_g) {
+    constexpr int TG = tile_group<NT>();
+    {
+        const int ntl = fresh_count(nt);
+#pragma unroll
+        for (int t4 = 0; t4 < NT; t4 += TG) {
+            if (t4 < ntl) {
+#pragma unroll
+                for (int t = t4; t < t4 + TG; ++t)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float wv = pow_p<PM>(pos_part(sv[t][i] - tau), pexp);
+                        sv[t][i] = row_ok ? wv : 0.f;
+                    }
+            }
+        }
+    }
+    if (lg > 0) dpp_level<0xB1>(sv, nt);     // xor 1
+    if (lg > 1) dpp_level<0x4E>(sv, nt);     // xor 2
+    if (lg > 2) dpp_level<0x141>(sv, nt);    // half-row mirror
+    if (lg > 3) dpp_level<0x140>(sv, nt);    // row mirror
+    const int ntl = fresh_count(nt);
+#pragma unroll
+    for (int t4 = 0; t4 < NT; t4 += TG) {
+#pragma unroll
+        for (int t = t4; t < t4 + TG; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sv[t][i] = t4 < ntl ? sv[t][i] * inv_g : 0.f;
+    }
 }
 
 // Load 4 consecutive elements of a row as fp32.
@@ -231,13 +310,7 @@ __device__ __forceinline__ float solve_tau_split(float (&sv)[NT][4], int nt, flo
     bool done = !active;
     for (int it = 0; it < 100; ++it) {
         float a0 = 0.f, a1 = 0.f;
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            if (t < nt) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) accum_pow<PM>(pos_part(sv[t][i] - tau), pexp, a0, a1);
-            }
-        }
+        newton_sums<NT, PM>(sv, nt, tau, pexp, a0, a1);
         a0 = pair32_sum(pair16_sum(a0));
         a1 = pair32_sum(pair16_sum(a1));
         float* buf = xsum + ((size_t)((it & 1) * G + gid) * CW) * 32;   // [CW][16][2]
@@ -463,16 +536,24 @@ __global__ __launch_bounds__(512) void entmax_route_kernel(RouteParams p) {
             // tile tt: A = 16 summaries x D (three bf16 splits), B = the 16 pairs' q
             auto tile_logits = [&](const char* stg, int tt, int t) {
                 const int cl = 16 * tt + n16;         // chunk inside the stage
+                // every operand read of the tile is issued before the first product
+                b8 a[3][D / 32];
+#pragma unroll
+                for (int h = 0; h < 3; ++h)
+#pragma unroll
+                    for (int s = 0; s < D / 32; ++s) a[h][s] = *reinterpret_cast<const b8*>(stg + KS::off(cl, h, 4 * s + kg));
                 f32x4 acc[3];
 #pragma unroll
                 for (int h = 0; h < 3; ++h) {
                     acc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int s = 0; s < D / 32; ++s) {
-                        const b8 a = *reinterpret_cast<const b8*>(stg + KS::off(cl, h, 4 * s + kg));
-                        acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[s], acc[h], 0, 0, 0);
-                    }
+                    for (int s = 0; s < D / 32; ++s)
+                        acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[h][s], qb[s], acc[h], 0, 0, 0);
                 }
+                // keep the reads together ahead of the products (the scheduler otherwise
+                // pairs each product with its own read and waits for it)
+                __builtin_amdgcn_sched_group_barrier(0x100, 3 * D / 32, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 3 * D / 32, 0);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int ch = RS::tile_chunk(t, cw) + 4 * kg + i;
@@ -616,20 +697,7 @@ __global__ __launch_bounds__(512) void entmax_route_kernel(RouteParams p) {
             so[1] = tau;
         }
         // per-head weights, then the group average across the g lanes of each row
-        const float inv_g = 1.f / (float)g;
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            if (t < nt) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float wv = row_ok ? pow_p<PM>(pos_part(sv[t][i] - tau), p.pexp) : 0.f;
-                    sv[t][i] = row_group_sum(wv, lg) * inv_g;
-                }
-            } else {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) sv[t][i] = 0.f;
-            }
-        }
+        group_weights<NT, PM>(sv, nt, tau, p.pexp, row_ok, lg, 1.f / (float)g);
         }
     } else {
 #pragma unroll
