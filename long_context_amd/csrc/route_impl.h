@@ -292,8 +292,15 @@ __device__ __forceinline__ void wait_vm_at_most(int n) {
 }
 
 // Stages of the summary ring in LDS: three when a row can need many stages, so the
-// copies run two stages ahead.
-template <int NT, int CW> constexpr int route_ring_stages() { return NT * CW / 2 >= 4 ? 3 : 2; }
+// copies run two stages ahead; two for rows of up to 512 chunks in one wavefront, whose
+// workgroups are halved so that two share a compute unit (one streams summaries while
+// the other solves τ; at 32K, 0.77 -> 0.72 ms against one workgroup with three stages).
+template <int NT, int CW> constexpr int route_ring_stages() {
+    return (NT >= 32 && CW == 1) ? 2 : NT * CW / 2 >= 4 ? 3 : 2;
+}
+template <typename T, int NT, int CW> constexpr int route_max_groups() {
+    return (sizeof(T) == 2 && NT >= 32 && CW == 1) ? 4 : 8 / CW;
+}
 // bf16 queries stream the split summaries through an LDS ring when one wavefront
 // holds a whole row; rows split over several wavefronts read them from L2.
 template <typename T, int CW> constexpr bool route_uses_ring() { return sizeof(T) == 2 && CW == 1; }
@@ -976,7 +983,7 @@ inline int route_groups_per_block(int R, int B, size_t* lds) {
     auto bytes = [&](int G) {
         return stage + (size_t)G * R * CW * NT * 16 * 4 + (size_t)G * CW * 16 * 4 + (size_t)2 * G * CW * 32 * 4;
     };
-    int G = 8 / CW;
+    int G = route_max_groups<T, NT, CW>();
     while (G > 1 && (B % (G * R) != 0 || bytes(G) > kRouteMaxLds)) G >>= 1;
     *lds = bytes(G);
     return G;
