@@ -347,6 +347,12 @@ LONG = [
     ("bf16", 1, 16, 2, 128, 40000, 32, 1.5, 6.0, 1.0),     # 1250 chunks: 4 wavefronts
     ("f32", 1, 4, 2, 64, 24000, 32, 2.0, 5.0, 1.0),        # 750 chunks, fp32 queries: 2 wavefronts
     ("bf16", 1, 2, 2, 64, 35200, 32, 1.5, 4.0, 1.0),       # g = 1, 1100 chunks: 16 rows x 4 wavefronts
+    # 129-512 chunks in one wavefront per row group (four-wavefront workgroups), g < 16:
+    # fewer DPP levels in the group average and several rows per group of 16 pairs
+    ("bf16", 1, 16, 2, 128, 12000, 32, 1.5, 4.0, 1.0),     # g = 8, 375 chunks, 2 rows per group
+    ("bf16", 1, 8, 2, 64, 10000, 64, 1.25, 3.0, 1.0),      # g = 4, 156 chunks, 4 rows per group
+    ("bf16", 1, 4, 4, 64, 9000, 32, 2.0, 5.0, 1.0),        # g = 1, 281 chunks, 16 rows: workgroup of two groups
+    ("bf16", 1, 16, 2, 128, 10000, 32, 1.0, 3.0, 1.0),     # α = 1 (softmax routing), g = 8, 312 chunks
 ]
 
 
