@@ -32,7 +32,6 @@
 #include <math.h>
 
 #include <algorithm>
-#include <type_traits>
 
 namespace dash {
 
@@ -428,7 +427,10 @@ __device__ __forceinline__ void route_compact(const RouteParams& p, const float*
         float* wo = p.w_out ? p.w_out + (rowbase + row) * (size_t)p.kbar_cap : nullptr;
         int base = 0;
         eqb = 0;
-        for (int c0 = 0; c0 < p.T_c; c0 += 64) {
+        // chunks past the visible ones are never routed: walk them only to write the
+        // dense weights
+        const int cend = wo ? p.T_c : nvis;
+        for (int c0 = 0; c0 < cend; c0 += 64) {
             const int c = c0 + lane;
             const float v = (c < nvis) ? wr[c] : (SOFT ? -INFINITY : 0.f);
             const bool in = selected(c, v, eqb);
@@ -543,24 +545,16 @@ __global__ __launch_bounds__(512) void entmax_route_kernel(RouteParams p) {
             // tile tt: A = 16 summaries x D (three bf16 splits), B = the 16 pairs' q
             auto tile_logits = [&](const char* stg, int tt, int t) {
                 const int cl = 16 * tt + n16;         // chunk inside the stage
-                // every operand read of the tile is issued before the first product
-                b8 a[3][D / 32];
-#pragma unroll
-                for (int h = 0; h < 3; ++h)
-#pragma unroll
-                    for (int s = 0; s < D / 32; ++s) a[h][s] = *reinterpret_cast<const b8*>(stg + KS::off(cl, h, 4 * s + kg));
                 f32x4 acc[3];
 #pragma unroll
                 for (int h = 0; h < 3; ++h) {
                     acc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int s = 0; s < D / 32; ++s)
-                        acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[h][s], qb[s], acc[h], 0, 0, 0);
+                    for (int s = 0; s < D / 32; ++s) {
+                        const b8 a = *reinterpret_cast<const b8*>(stg + KS::off(cl, h, 4 * s + kg));
+                        acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[s], acc[h], 0, 0, 0);
+                    }
                 }
-                // keep the reads together ahead of the products (the scheduler otherwise
-                // pairs each product with its own read and waits for it)
-                __builtin_amdgcn_sched_group_barrier(0x100, 3 * D / 32, 0);
-                __builtin_amdgcn_sched_group_barrier(0x008, 3 * D / 32, 0);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int ch = RS::tile_chunk(t, cw) + 4 * kg + i;
