@@ -12,9 +12,9 @@
 //    registers: up to 512 per wavefront, rows with more chunks are split over CW = 2
 //    or 4 wavefronts whose row maxima and Newton sums meet in LDS. The split is
 //    interleaved by 16-chunk tile (wavefront cw takes tiles cw, cw + CW, ...). bf16
-//    queries take the summaries from a buffer split into three bf16 terms: through a
-//    three-stage LDS ring when one wavefront holds a row, straight from L2 when rows
-//    are split (the ring's barriers across all wavefronts cost more than its sharing).
+//    queries take the summaries from a buffer split into three bf16 terms: through an
+//    LDS ring when one wavefront holds a row, straight from L2 when rows are split
+//    (the ring's barriers across all wavefronts cost more than its sharing).
 //  * Threshold: work on y = (α-1)γ(z̄ - max z̄) <= 0 (exact shift by the row maximum)
 //    so τ lies in [-1, 0). Newton's method on g(τ) = ||[y - τ]_+||_p - 1 with
 //    p = 1/(α-1), started at τ = -1 where g >= 0: g is convex and decreasing, so the
@@ -24,6 +24,10 @@
 //  * GQA average with DPP row permutations (within 16-lane rows), then the group
 //    weights go to LDS and each row is compacted with a ballot/prefix count into an
 //    ascending chunk list with its bias.
+//  * A wave64 VALU instruction takes four cycles on the 16-lane SIMD, and Newton and
+//    the weights are bound by their instruction count: the row's tiles are visited in
+//    groups of four with one uniform test per group, and the DPP levels of the group
+//    average are tested once per level, not per value.
 #pragma once
 
 #include "common.h"
