@@ -759,9 +759,9 @@ constexpr float kCandMargin = 1.0f / 1024.0f;  // slack on every bound, in units
 
 template <int PM>
 __device__ __forceinline__ float cand_newton(const float (&cv)[kCandCap], int n, float m, float cs, float pexp,
-                                             bool active, float tau) {
+                                             bool active, float tau, int max_it = 100) {
     bool done = !active;
-    for (int it = 0; it < 100; ++it) {
+    for (int it = 0; it < max_it; ++it) {
         float a0 = 0.f, a1 = 0.f;
 #pragma unroll
         for (int j = 0; j < kCandCap; ++j)
@@ -860,9 +860,12 @@ __global__ __launch_bounds__(512) void entmax_route_cand_kernel(RouteParams p) {
             for (int j = 0; j < CAP; ++j) cv[j] = j < ncand ? cval[slot(j)] : -INFINITY;
             const float m = pair32_max(pair16_max(mlane));
             // θ is below the root over the kept chunks (their set only grew above θ),
-            // so Newton may start there
+            // so Newton may start there. Every iterate from the left is a lower bound of
+            // that root, so two steps suffice for a bound: at 96K they take the routing
+            // from 9.4 / 7.7 / 5.9 to 8.2 / 7.0 / 5.8 ms at 75 / 87.5 / 93.75% group
+            // sparsity (one step: the same; three: 8.6 / 7.3 / 5.8)
             const float tau0 = fmaxf(-1.f, cs * (theta - m));
-            const float tau = cand_newton<PM>(cv, ncand, m, cs, p.pexp, row_ok && m > -INFINITY, tau0);
+            const float tau = cand_newton<PM>(cv, ncand, m, cs, p.pexp, row_ok && m > -INFINITY, tau0, 2);
             if (row_ok && m > -INFINITY) theta = fmaxf(theta, m + (tau - kCandMargin) * inv_cs);
             int k = 0;
 #pragma unroll
